@@ -1,0 +1,166 @@
+"""Float64 CPU oracle for causal linear attention (phi = elu + 1).
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with
+the HIP path.  The arithmetic lives in ``la_oracle.c`` (plain C, float64,
+token by token); this module only builds that file, marshals numpy arrays to
+float64 and back, and says which routine follows which equation.
+
+Sources: "Transformers are RNNs -- part 2/3" eq. 7-20; the reading notes on
+the same paper, section 3.2 eq. 4-6 and appendix A; "Linear Attention/zh",
+kernel reformulation and recurrent form.
+
+Every routine here is pinned by the tests in ``tests/test_oracle_pins.py``
+(brute force of the quadratic masked definition, a hand-derived worked
+example, closed forms, invariants and finite differences).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+_LIB = os.path.join(_HERE, "liblaoracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile la_oracle.c into liblaoracle.so with gcc (OpenMP over heads)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    dp = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.orc_phi.restype = ctypes.c_double
+    lib.orc_phi.argtypes = [ctypes.c_double]
+    lib.orc_dphi.restype = ctypes.c_double
+    lib.orc_dphi.argtypes = [ctypes.c_double]
+    lib.orc_forward_causal.argtypes = [dp] * 9 + [L] * 5
+    lib.orc_forward_causal_parallel.argtypes = [dp] * 5 + [L] * 5
+    lib.orc_forward_noncausal.argtypes = [dp] * 4 + [L] * 5
+    lib.orc_numerator_backward.argtypes = [dp] * 7 + [L] * 3
+    lib.orc_backward_causal.argtypes = [dp] * 9 + [L] * 5
+    lib.orc_decode_step.argtypes = [dp] * 6 + [L] * 4
+    lib.orc_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def phi(x: float) -> float:
+    """eq. 7 with elu's alpha = 1."""
+    return float(_load().orc_phi(float(x)))
+
+
+def dphi(x: float) -> float:
+    return float(_load().orc_dphi(float(x)))
+
+
+def forward_causal(q, k, v, s0=None, z0=None):
+    """Recurrent form, eq. 10-12.  Returns (O, den, S_N, Z_N) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    if (s0 is None) != (z0 is None):
+        raise ValueError("s0 and z0 go together")
+    s0 = None if s0 is None else _f64(s0)
+    z0 = None if z0 is None else _f64(z0)
+    o = np.empty((B, H, N, M))
+    den = np.empty((B, H, N))
+    s = np.empty((B, H, D, M))
+    z = np.empty((B, H, D))
+    _load().orc_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(s0), _ptr(z0), _ptr(o), _ptr(den),
+                               _ptr(s), _ptr(z), B, H, N, D, M)
+    return o, den, s, z
+
+
+def forward_causal_parallel(q, k, v):
+    """Quadratic masked form of eq. 9.  Returns (O, den)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    o = np.empty((B, H, N, M))
+    den = np.empty((B, H, N))
+    _load().orc_forward_causal_parallel(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), B, H, N, D, M)
+    return o, den
+
+
+def forward_noncausal(q, k, v):
+    """eq. 5-6: S and Z summed over the whole sequence, reused by every query."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    o = np.empty((B, H, N, M))
+    _load().orc_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M)
+    return o
+
+
+def numerator_backward(p, kf, vb, g):
+    """eq. 13-15 for one head on feature-mapped inputs: returns (dP, dKf, dVb)."""
+    p, kf, vb, g = _f64(p), _f64(kf), _f64(vb), _f64(g)
+    N, C = p.shape
+    Mb = vb.shape[1]
+    dp_ = np.empty((N, C))
+    dk = np.empty((N, C))
+    dv = np.empty((N, Mb))
+    _load().orc_numerator_backward(_ptr(p), _ptr(kf), _ptr(vb), _ptr(g), _ptr(dp_), _ptr(dk), _ptr(dv),
+                                   N, C, Mb)
+    return dp_, dk, dv
+
+
+def backward_causal(q, k, v, do, s0=None, z0=None):
+    """Gradients of sum(dO * O) w.r.t. raw Q, K, V.  Returns (dQ, dK, dV)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    s0 = None if s0 is None else _f64(s0)
+    z0 = None if z0 is None else _f64(z0)
+    dq = np.empty((B, H, N, D))
+    dk = np.empty((B, H, N, D))
+    dv = np.empty((B, H, N, M))
+    _load().orc_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dq), _ptr(dk),
+                                _ptr(dv), B, H, N, D, M)
+    return dq, dk, dv
+
+
+def decode_step(q, k, v, s, z):
+    """eq. 18-20 (attention part).  Returns (y, S_new, Z_new); inputs untouched."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s = np.array(s, dtype=np.float64, copy=True, order="C")
+    z = np.array(z, dtype=np.float64, copy=True, order="C")
+    B, H, D = q.shape
+    M = v.shape[-1]
+    y = np.empty((B, H, M))
+    _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(y), B, H, D, M)
+    return y, s, z

@@ -1,0 +1,348 @@
+/*
+ * la_oracle.c -- float64 CPU oracle for causal linear attention with
+ * phi(x) = elu(x) + 1.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file: only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * Every routine is the plain definition written out, in float64, one token
+ * at a time; there is no chunking, blocking or fusion.  Parallelism is only
+ * across independent (batch, head) pairs (heads never interact: Transformer
+ * Family v2, multi-head attention section).
+ *
+ * Sources, cited by page title and equation:
+ *  [TaR]  "Transformers are RNNs: Fast Autoregressive Transformers with
+ *         Linear Attention -- part 2/3": eq. 7 (feature map), eq. 8-12
+ *         (causal masking), eq. 13-15 (gradient of the numerator), eq. 16-20
+ *         (the RNN form).
+ *  [TaRn] reading notes "Transformers are RNNs" (papercache): section 3.2
+ *         eq. 4-6 (non-causal linearised attention), appendix A (the
+ *         denominator's gradient left to automatic differentiation).
+ *  [LA]   "Linear Attention/zh": kernel reformulation (S, z summed once and
+ *         reused), recurrent form (S_t, z_t updates).
+ *
+ * Readings where the pages leave a step open:
+ *  - elu's alpha is 1 (the Clevert et al. default the pages cite), so
+ *    phi(x) = x + 1 for x > 0 and exp(x) otherwise; phi'(x) = 1 for x > 0
+ *    and exp(x) otherwise.
+ *  - no epsilon in the denominator.
+ *  - causal masking is inclusive (j <= i), as eq. 8 states.
+ *  - the gradient of the denominator and of the fraction, left by the pages
+ *    to autograd, is the quotient rule: with num_i and den_i the numerator
+ *    and denominator of eq. 12 and dO_i the upstream gradient,
+ *      d num_i = dO_i / den_i,   d den_i = -(dO_i . O_i) / den_i.
+ *    The denominator of eq. 12 is the numerator with V replaced by a column
+ *    of ones, so both are handled by the numerator gradient of eq. 13-15
+ *    applied to V-bar = [V, 1] with upstream [d num, d den].
+ *  - gradients are returned with respect to the raw Q, K, V (chain rule
+ *    through phi').
+ *
+ * All pins of these routines are structural (the pages print no tensor
+ * values); they live in the test-suite.
+ *
+ * Layout: row-major, Q and K [B,H,N,D]; V, O, dO [B,H,N,M]; den [B,H,N];
+ * S [B,H,D,M] with S[d][m] = sum_j phi(K_j)[d] V_j[m]; Z [B,H,D].
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* [TaR] eq. 7 with alpha = 1. */
+double orc_phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* Derivative of eq. 7: 1 for x > 0, exp(x) otherwise (both sides give 1 at 0). */
+double orc_dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/*
+ * Causal forward, recurrent form ([TaR] eq. 10-12, eq. 16-19 without the
+ * projections):  S_i = S_{i-1} + phi(K_i) V_i^T,  Z_i = Z_{i-1} + phi(K_i),
+ * den_i = phi(Q_i) . Z_i,  O_i = phi(Q_i)^T S_i / den_i.
+ * S0/Z0 (both or neither, may be NULL) are the state before token 1.
+ * den, S_out, Z_out may be NULL.
+ */
+void orc_forward_causal(const double *Q, const double *K, const double *V,
+                        const double *S0, const double *Z0, double *O,
+                        double *den, double *S_out, double *Z_out, long B,
+                        long H, long N, long D, long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+    double *Z = (double *)calloc((size_t)D, sizeof(double));
+    double *pq = (double *)malloc((size_t)D * sizeof(double));
+    double *pk = (double *)malloc((size_t)D * sizeof(double));
+    if (S0) memcpy(S, S0 + bh * D * M, (size_t)(D * M) * sizeof(double));
+    if (Z0) memcpy(Z, Z0 + bh * D, (size_t)D * sizeof(double));
+    for (long i = 0; i < N; ++i) {
+      const double *q = Q + (bh * N + i) * D;
+      const double *k = K + (bh * N + i) * D;
+      const double *v = V + (bh * N + i) * M;
+      for (long d = 0; d < D; ++d) {
+        pq[d] = orc_phi(q[d]);
+        pk[d] = orc_phi(k[d]);
+      }
+      /* state update first: the mask is inclusive (eq. 8, j <= i) */
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) S[d * M + m] += pk[d] * v[m];
+        Z[d] += pk[d];
+      }
+      double dn = 0.0;
+      for (long d = 0; d < D; ++d) dn += pq[d] * Z[d];
+      double *o = O + (bh * N + i) * M;
+      for (long m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (long d = 0; d < D; ++d) num += pq[d] * S[d * M + m];
+        o[m] = num / dn;
+      }
+      if (den) den[bh * N + i] = dn;
+    }
+    if (S_out) memcpy(S_out + bh * D * M, S, (size_t)(D * M) * sizeof(double));
+    if (Z_out) memcpy(Z_out + bh * D, Z, (size_t)D * sizeof(double));
+    free(S);
+    free(Z);
+    free(pq);
+    free(pk);
+  }
+}
+
+/*
+ * Causal forward, parallel (quadratic) form ([TaR] eq. 9 read as matrices):
+ * A = phi(Q) phi(K)^T with the inclusive lower-triangular mask,
+ * O = (A V) / (A 1) row-wise.  Cross-check for the recurrent form; O(N^2).
+ */
+void orc_forward_causal_parallel(const double *Q, const double *K,
+                                 const double *V, double *O, double *den,
+                                 long B, long H, long N, long D, long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    double *pq = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *pk = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *arow = (double *)malloc((size_t)N * sizeof(double));
+    for (long t = 0; t < N * D; ++t) {
+      pq[t] = orc_phi(Q[bh * N * D + t]);
+      pk[t] = orc_phi(K[bh * N * D + t]);
+    }
+    for (long i = 0; i < N; ++i) {
+      double rowsum = 0.0;
+      for (long j = 0; j <= i; ++j) {
+        double a = 0.0;
+        for (long d = 0; d < D; ++d) a += pq[i * D + d] * pk[j * D + d];
+        arow[j] = a;
+        rowsum += a;
+      }
+      double *o = O + (bh * N + i) * M;
+      for (long m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (long j = 0; j <= i; ++j) acc += arow[j] * V[(bh * N + j) * M + m];
+        o[m] = acc / rowsum;
+      }
+      if (den) den[bh * N + i] = rowsum;
+    }
+    free(pq);
+    free(pk);
+    free(arow);
+  }
+}
+
+/*
+ * Non-causal forward ([TaRn] section 3.2, eq. 5-6; [LA] kernel
+ * reformulation): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) are formed
+ * once per head and reused for every query: O_i = phi(Q_i)^T S / phi(Q_i).Z.
+ */
+void orc_forward_noncausal(const double *Q, const double *K, const double *V,
+                           double *O, long B, long H, long N, long D, long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+    double *Z = (double *)calloc((size_t)D, sizeof(double));
+    double *pq = (double *)malloc((size_t)D * sizeof(double));
+    for (long j = 0; j < N; ++j) {
+      const double *k = K + (bh * N + j) * D;
+      const double *v = V + (bh * N + j) * M;
+      for (long d = 0; d < D; ++d) {
+        double pk = orc_phi(k[d]);
+        for (long m = 0; m < M; ++m) S[d * M + m] += pk * v[m];
+        Z[d] += pk;
+      }
+    }
+    for (long i = 0; i < N; ++i) {
+      const double *q = Q + (bh * N + i) * D;
+      for (long d = 0; d < D; ++d) pq[d] = orc_phi(q[d]);
+      double dn = 0.0;
+      for (long d = 0; d < D; ++d) dn += pq[d] * Z[d];
+      double *o = O + (bh * N + i) * M;
+      for (long m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (long d = 0; d < D; ++d) num += pq[d] * S[d * M + m];
+        o[m] = num / dn;
+      }
+    }
+    free(S);
+    free(Z);
+    free(pq);
+  }
+}
+
+/*
+ * Gradient of the causal numerator ([TaR] eq. 13-15) for one head.
+ * Inputs are already feature-mapped, as the pages' appendix allows
+ * ("without loss of generality Q and K already hold phi-mapped vectors"):
+ *   P = phi(Q) [N,C], Kf = phi(K) [N,C], Vb [N,Mb], G = dL/dVbar [N,Mb]
+ * where Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j.
+ *   eq. 13: dP_i  = S_i G_i,      S_i = sum_{j<=i} Kf_j Vb_j^T   (forward sum)
+ *   eq. 14: dKf_i = R_i Vb_i,     R_i = sum_{j>=i} P_j G_j^T     (reverse sum)
+ *   eq. 15: dVb_i = R_i^T Kf_i.
+ * The two sums are accumulated token by token in opposite directions.
+ */
+void orc_numerator_backward(const double *P, const double *Kf, const double *Vb,
+                            const double *G, double *dP, double *dKf,
+                            double *dVb, long N, long C, long Mb) {
+  double *S = (double *)calloc((size_t)(C * Mb), sizeof(double));
+  double *R = (double *)calloc((size_t)(C * Mb), sizeof(double));
+  for (long i = 0; i < N; ++i) { /* forward cumulative sum, eq. 13 */
+    for (long c = 0; c < C; ++c)
+      for (long m = 0; m < Mb; ++m) S[c * Mb + m] += Kf[i * C + c] * Vb[i * Mb + m];
+    for (long c = 0; c < C; ++c) {
+      double acc = 0.0;
+      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m];
+      dP[i * C + c] = acc;
+    }
+  }
+  for (long i = N - 1; i >= 0; --i) { /* reverse cumulative sum, eq. 14-15 */
+    for (long c = 0; c < C; ++c)
+      for (long m = 0; m < Mb; ++m) R[c * Mb + m] += P[i * C + c] * G[i * Mb + m];
+    for (long c = 0; c < C; ++c) {
+      double acc = 0.0;
+      for (long m = 0; m < Mb; ++m) acc += R[c * Mb + m] * Vb[i * Mb + m];
+      dKf[i * C + c] = acc;
+    }
+    for (long m = 0; m < Mb; ++m) {
+      double acc = 0.0;
+      for (long c = 0; c < C; ++c) acc += R[c * Mb + m] * Kf[i * C + c];
+      dVb[i * Mb + m] = acc;
+    }
+  }
+  free(S);
+  free(R);
+}
+
+/*
+ * Full causal backward: gradients of L = sum(dO * O) with respect to the raw
+ * Q, K, V, where O is the causal forward of eq. 12 started from (S0, Z0)
+ * (both may be NULL: zero state).  Steps:
+ *  1. forward recurrence (eq. 10-12) for den_i and O_i;
+ *  2. quotient rule: d num_i = dO_i / den_i, d den_i = -(dO_i . O_i) / den_i;
+ *  3. eq. 13-15 on the augmented values Vbar = [V, 1] with upstream
+ *     [d num, d den] (the denominator is the numerator of a ones column);
+ *     an initial state contributes S0 G_i to the phi(Q) gradient (it is the
+ *     j = 0 term of the forward sum of eq. 13);
+ *  4. chain rule through phi: dQ = dphiQ * phi'(Q), dK = dphiK * phi'(K).
+ */
+void orc_backward_causal(const double *Q, const double *K, const double *V,
+                         const double *dO, const double *S0, const double *Z0,
+                         double *dQ, double *dK, double *dV, long B, long H,
+                         long N, long D, long M) {
+  long BH = B * H;
+  long Mb = M + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    const double *q = Q + bh * N * D, *k = K + bh * N * D, *v = V + bh * N * M;
+    const double *go = dO + bh * N * M;
+    double *O = (double *)malloc((size_t)(N * M) * sizeof(double));
+    double *den = (double *)malloc((size_t)N * sizeof(double));
+    double *P = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *Kf = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *Vb = (double *)malloc((size_t)(N * Mb) * sizeof(double));
+    double *G = (double *)malloc((size_t)(N * Mb) * sizeof(double));
+    double *dP = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *dKf = (double *)malloc((size_t)(N * D) * sizeof(double));
+    double *dVb = (double *)malloc((size_t)(N * Mb) * sizeof(double));
+    /* 1. forward pass of this head */
+    orc_forward_causal(q, k, v, S0 ? S0 + bh * D * M : NULL,
+                       Z0 ? Z0 + bh * D : NULL, O, den, NULL, NULL, 1, 1, N, D, M);
+    /* 2. quotient rule, 3. augmented numerator */
+    for (long i = 0; i < N; ++i) {
+      for (long d = 0; d < D; ++d) {
+        P[i * D + d] = orc_phi(q[i * D + d]);
+        Kf[i * D + d] = orc_phi(k[i * D + d]);
+      }
+      double dot = 0.0;
+      for (long m = 0; m < M; ++m) {
+        Vb[i * Mb + m] = v[i * M + m];
+        G[i * Mb + m] = go[i * M + m] / den[i];
+        dot += go[i * M + m] * O[i * M + m];
+      }
+      Vb[i * Mb + M] = 1.0;
+      G[i * Mb + M] = -dot / den[i];
+    }
+    orc_numerator_backward(P, Kf, Vb, G, dP, dKf, dVb, N, D, Mb);
+    if (S0 || Z0) { /* initial state: the j = 0 term of eq. 13's sum */
+      for (long i = 0; i < N; ++i)
+        for (long d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (long m = 0; m < M; ++m)
+            acc += (S0 ? S0[bh * D * M + d * M + m] : 0.0) * G[i * Mb + m];
+          acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];
+          dP[i * D + d] += acc;
+        }
+    }
+    /* 4. chain rule through phi */
+    for (long i = 0; i < N; ++i) {
+      for (long d = 0; d < D; ++d) {
+        dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_dphi(q[i * D + d]);
+        dK[(bh * N + i) * D + d] = dKf[i * D + d] * orc_dphi(k[i * D + d]);
+      }
+      for (long m = 0; m < M; ++m) dV[(bh * N + i) * M + m] = dVb[i * Mb + m];
+    }
+    free(O);
+    free(den);
+    free(P);
+    free(Kf);
+    free(Vb);
+    free(G);
+    free(dP);
+    free(dKf);
+    free(dVb);
+  }
+}
+
+/*
+ * One RNN decode step ([TaR] eq. 18-20, attention part; [LA] recurrent
+ * form): S += phi(k) v^T, Z += phi(k), then y = phi(q)^T S / phi(q).Z.
+ * S [B,H,D,M] and Z [B,H,D] are updated in place; y [B,H,M].
+ */
+void orc_decode_step(const double *q, const double *k, const double *v,
+                     double *S, double *Z, double *y, long B, long H, long D,
+                     long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(static)
+  for (long bh = 0; bh < BH; ++bh) {
+    double *s = S + bh * D * M, *z = Z + bh * D;
+    for (long d = 0; d < D; ++d) {
+      double pk = orc_phi(k[bh * D + d]);
+      for (long m = 0; m < M; ++m) s[d * M + m] += pk * v[bh * M + m];
+      z[d] += pk;
+    }
+    double dn = 0.0;
+    for (long d = 0; d < D; ++d) dn += orc_phi(q[bh * D + d]) * z[d];
+    for (long m = 0; m < M; ++m) {
+      double num = 0.0;
+      for (long d = 0; d < D; ++d) num += orc_phi(q[bh * D + d]) * s[d * M + m];
+      y[bh * M + m] = num / dn;
+    }
+  }
+}
+
+/* Threads the OpenMP runtime will use (1 when built without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

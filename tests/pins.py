@@ -1,0 +1,80 @@
+"""Independent reference computations used to pin the oracle.
+
+Nothing here calls the oracle or the HIP library.  phi comes from PyTorch's
+library ``elu`` (alpha = 1) plus one, and the attention is the quadratic
+masked definition of "Transformers are RNNs -- part 2/3" eq. 8 (non-causal:
+eq. 3 of the reading notes) evaluated in float64 with numpy.
+"""
+from __future__ import annotations
+
+import fractions
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def phi_lib(x: np.ndarray) -> np.ndarray:
+    """elu(x) + 1 via torch.nn.functional.elu (a library routine), float64."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return (torch.nn.functional.elu(t, alpha=1.0) + 1.0).numpy()
+
+
+def brute_causal(q, k, v):
+    """eq. 8 with sim(q, k) = phi(q) . phi(k): O_i = sum_{j<=i} s_ij V_j / sum_{j<=i} s_ij."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, H, N, _ = q.shape
+    out = np.empty(v.shape)
+    den = np.empty((B, H, N))
+    mask = np.tril(np.ones((N, N)))
+    for b in range(B):
+        for h in range(H):
+            sim = (phi_lib(q[b, h]) @ phi_lib(k[b, h]).T) * mask
+            den[b, h] = sim.sum(axis=1)
+            out[b, h] = (sim @ v[b, h]) / den[b, h][:, None]
+    return out, den
+
+
+def brute_noncausal(q, k, v):
+    """Unmasked form (reading notes eq. 3 with the same sim)."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    out = np.empty(v.shape)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            sim = phi_lib(q[b, h]) @ phi_lib(k[b, h]).T
+            out[b, h] = (sim @ v[b, h]) / sim.sum(axis=1)[:, None]
+    return out
+
+
+def brute_numerator(p, kf, vb):
+    """Numerator of eq. 9 on feature-mapped inputs: Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j."""
+    n = p.shape[0]
+    return (np.tril(np.ones((n, n))) * (p @ kf.T)) @ vb
+
+
+def load_golden(name: str = "worked_example.txt"):
+    """Parse the hand-derived worked examples: {key: list of Fractions}."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rhs = line.partition("=")
+            out[key.strip()] = [fractions.Fraction(tok) for tok in rhs.split()]
+    return out
+
+
+def golden_array(g, key, shape):
+    return np.array([float(x) for x in g[key]], dtype=np.float64).reshape(shape)
+
+
+def rel_err(x, y):
+    """max |x - y| / max |y| (tensor-wide), 0 when both are zero."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    scale = np.max(np.abs(y)) if y.size else 0.0
+    diff = np.max(np.abs(x - y)) if y.size else 0.0
+    return diff / scale if scale > 0 else diff

@@ -1,0 +1,86 @@
+"""Planted mistakes in a copy of the oracle must fail at least one pin.
+
+Each case copies oracle/la_oracle.c, applies one textual mutation of the kind
+a transcription of the pages could plausibly contain (a dropped term, a wrong
+sign, a wrong or transposed operand, an off-by-one mask), builds it with gcc
+into a temporary directory, swaps it in for the real oracle and runs the pin
+tests.  Everything happens on the CPU; the real oracle is never modified.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "la_oracle.c")
+
+MUTATIONS = {
+    "phi drops the +1": ("x > 0.0 ? x + 1.0 : exp(x)", "x > 0.0 ? x : exp(x)"),
+    "phi' wrong for x<=0": ("x > 0.0 ? 1.0 : exp(x)", "x > 0.0 ? 1.0 : 1.0"),
+    "state update uses phi(Q)": ("S[d * M + m] += pk[d] * v[m];", "S[d * M + m] += pq[d] * v[m];"),
+    "normaliser uses phi(Q)": ("        Z[d] += pk[d];\n      }\n      double dn", "        Z[d] += pq[d];\n      }\n      double dn"),
+    "parallel form sees one future token": ("for (long j = 0; j <= i; ++j) {\n        double a",
+                                             "for (long j = 0; j <= i + (i + 1 < N); ++j) {\n        double a"),
+    "denominator gradient sign": ("G[i * Mb + M] = -dot / den[i];", "G[i * Mb + M] = dot / den[i];"),
+    "chain rule uses phi not phi'": ("dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_dphi(q[i * D + d]);",
+                                     "dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_phi(q[i * D + d]);"),
+    "eq. 15 transposed operand": ("acc += R[c * Mb + m] * Kf[i * C + c];", "acc += R[c * Mb + m] * P[i * C + c];"),
+    "eq. 14 reverse sum of wrong factor": ("R[c * Mb + m] += P[i * C + c] * G[i * Mb + m];",
+                                           "R[c * Mb + m] += Kf[i * C + c] * G[i * Mb + m];"),
+    "eq. 13 forward sum off by one": ("    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m];\n      dP[i * C + c] = acc;\n    }\n  }",
+                                      "    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m] * (i > 0);\n      dP[i * C + c] = acc;\n    }\n  }"),
+    "non-causal drops phi on keys": ("double pk = orc_phi(k[d]);\n        for", "double pk = k[d];\n        for"),
+    "decode normaliser ignores keys": ("      z[d] += pk;", "      z[d] += 1.0;"),
+    "initial state ignored in backward": ("acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];",
+                                          "acc += 0.0 * G[i * Mb + M];"),
+}
+
+PIN_CALLS = [
+    P.test_phi_closed_forms,
+    P.test_dphi_finite_difference,
+    P.test_worked_example_forward,
+    P.test_worked_example_backward,
+    lambda: P.test_recurrent_equals_bruteforce_eq8((2, 3, 17, 5, 3)),
+    lambda: P.test_parallel_form_equals_recurrent((2, 3, 17, 5, 3)),
+    lambda: P.test_noncausal_equals_bruteforce((2, 3, 17, 5, 3)),
+    P.test_final_state_definition,
+    P.test_constant_values_give_constant_output,
+    P.test_first_row_is_first_value,
+    P.test_zero_queries_and_keys_give_running_mean,
+    P.test_decode_steps_equal_bruteforce,
+    lambda: P.test_backward_finite_differences(3, 3, False),
+    lambda: P.test_backward_finite_differences(4, 8, True),
+    P.test_numerator_gradient_finite_differences,
+    P.test_euler_identities,
+]
+
+
+def _count_failures():
+    failed = 0
+    for call in PIN_CALLS:
+        try:
+            call()
+        except (AssertionError, ZeroDivisionError, FloatingPointError, ValueError):
+            failed += 1
+    return failed
+
+
+def test_pins_pass_on_real_oracle():
+    assert _count_failures() == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name!r} must match exactly once"
+    mutated = tmp_path / "mut.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-o", str(so), str(mutated), "-lm"], check=True)
+    lib = oracle._configure(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    assert _count_failures() > 0, f"no pin caught the planted mistake {name!r}"

@@ -1,0 +1,351 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each test cites the passage it follows.  None of these compares the oracle
+with a retyped copy of its own formula: the references are the quadratic
+masked definition (eq. 8) built on PyTorch's library elu, hand-derived
+fractions, closed forms, invariants and finite differences.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_rnn_layers_amd import inputs
+from tests import pins
+
+RNG_SHAPES = [  # (B, H, N, D, M)
+    (1, 1, 1, 4, 4),
+    (2, 3, 17, 5, 3),
+    (1, 2, 40, 8, 6),
+    (2, 1, 33, 3, 9),
+]
+
+
+def _qkv(shape, seed, sigma=1.0):
+    B, H, N, D, M = shape
+    q = inputs.gaussian((B, H, N, D), seed, sigma)
+    k = inputs.gaussian((B, H, N, D), seed + 1, sigma)
+    v = inputs.gaussian((B, H, N, M), seed + 2, sigma)
+    return q, k, v
+
+
+# ---------------------------------------------------------------- eq. 7 (phi)
+def test_phi_closed_forms():
+    """eq. 7 with alpha = 1: phi(x) = x + 1 (x > 0), exp(x) (x <= 0); phi(0) = 1."""
+    assert oracle.phi(0.0) == 1.0
+    assert oracle.phi(1.0) == 2.0
+    assert oracle.phi(2.5) == 3.5
+    assert oracle.phi(-1.0) == pytest.approx(math.exp(-1.0), rel=1e-15)
+    assert oracle.phi(-30.0) == pytest.approx(math.exp(-30.0), rel=1e-15)
+    xs = np.linspace(-6, 6, 97)
+    lib = pins.phi_lib(xs)
+    mine = np.array([oracle.phi(x) for x in xs])
+    # elu(x) + 1 = expm1(x) + 1 cancels for x << 0, hence the 1e-13 bound
+    assert np.max(np.abs(mine - lib) / lib) < 1e-13
+    assert np.all(mine > 0)  # positive similarity, as the pages require
+
+
+def test_dphi_finite_difference():
+    """phi' = 1 for x > 0, exp(x) for x <= 0; continuous at 0 (phi is C1)."""
+    for x in np.linspace(-5, 5, 41):
+        if abs(x) < 1e-3:
+            continue
+        h = 1e-6
+        fd = (oracle.phi(x + h) - oracle.phi(x - h)) / (2 * h)
+        assert oracle.dphi(x) == pytest.approx(fd, rel=1e-8, abs=1e-10)
+    assert oracle.dphi(0.0) == 1.0
+    assert oracle.dphi(1e-12) == 1.0
+
+
+# ------------------------------------------------------- worked examples
+def test_worked_example_forward():
+    """Hand-derived fractions from eq. 8 / eq. 10-12 and eq. 5-6 (tests/golden)."""
+    g = pins.load_golden()
+    shp = [int(x) for x in g["A.shape"]]
+    B, H, N, D, M = shp
+    q = pins.golden_array(g, "A.Q", (B, H, N, D))
+    k = pins.golden_array(g, "A.K", (B, H, N, D))
+    v = pins.golden_array(g, "A.V", (B, H, N, M))
+    o, den, s, z = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(o, pins.golden_array(g, "A.O_causal", o.shape), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(den, pins.golden_array(g, "A.den_causal", den.shape), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(s, pins.golden_array(g, "A.S_final", s.shape), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(z, pins.golden_array(g, "A.Z_final", z.shape), rtol=0, atol=1e-13)
+    o2, den2 = oracle.forward_causal_parallel(q, k, v)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-15)
+    onc = oracle.forward_noncausal(q, k, v)
+    np.testing.assert_allclose(onc, pins.golden_array(g, "A.O_noncausal", onc.shape), rtol=0, atol=1e-15)
+
+
+def test_worked_example_backward():
+    """Hand-derived gradients for N = 2, D = M = 1 (quotient rule on eq. 12)."""
+    g = pins.load_golden()
+    B, H, N, D, M = [int(x) for x in g["B.shape"]]
+    q = pins.golden_array(g, "B.Q", (B, H, N, D))
+    k = pins.golden_array(g, "B.K", (B, H, N, D))
+    v = pins.golden_array(g, "B.V", (B, H, N, M))
+    do = pins.golden_array(g, "B.dO", (B, H, N, M))
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(o, pins.golden_array(g, "B.O_causal", o.shape), atol=1e-15)
+    dq, dk, dv = oracle.backward_causal(q, k, v, do)
+    np.testing.assert_allclose(dq, pins.golden_array(g, "B.dQ", dq.shape), atol=1e-15)
+    np.testing.assert_allclose(dk, pins.golden_array(g, "B.dK", dk.shape), atol=1e-15)
+    np.testing.assert_allclose(dv, pins.golden_array(g, "B.dV", dv.shape), atol=1e-15)
+
+
+# ------------------------------------------------- brute force of eq. 8 (P1)
+@pytest.mark.parametrize("shape", RNG_SHAPES)
+def test_recurrent_equals_bruteforce_eq8(shape):
+    """eq. 9-12 (recurrent) equal eq. 8 computed quadratically."""
+    q, k, v = _qkv(shape, 11)
+    o, den, _, _ = oracle.forward_causal(q, k, v)
+    ob, denb = pins.brute_causal(q, k, v)
+    assert pins.rel_err(o, ob) < 1e-12
+    assert pins.rel_err(den, denb) < 1e-12
+
+
+def test_small_workload_against_bruteforce():
+    """The B=1 H=1 N=64 D=M=32 float32 workload, in full."""
+    w = inputs.SMALL
+    q, k, v = w.qkv()
+    o, den, _, _ = oracle.forward_causal(q, k, v)
+    ob, denb = pins.brute_causal(q, k, v)
+    assert pins.rel_err(o, ob) < 1e-12
+    assert pins.rel_err(den, denb) < 1e-12
+
+
+def test_mnist_shape_against_bruteforce_subset():
+    """N = 784 (MNIST-shaped sequence), two heads, against eq. 8."""
+    w = inputs.MNIST
+    q, k, v = w.qkv()
+    q, k, v = q[:1, :2], k[:1, :2], v[:1, :2]
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    ob, _ = pins.brute_causal(q, k, v)
+    assert pins.rel_err(o, ob) < 1e-12
+    onc = oracle.forward_noncausal(q, k, v)
+    assert pins.rel_err(onc, pins.brute_noncausal(q, k, v)) < 1e-12
+
+
+@pytest.mark.parametrize("shape", RNG_SHAPES)
+def test_parallel_form_equals_recurrent(shape):
+    """eq. 9 (masked matrix form) and eq. 12 (recurrence) agree (P2)."""
+    q, k, v = _qkv(shape, 21)
+    o, den, _, _ = oracle.forward_causal(q, k, v)
+    o2, den2 = oracle.forward_causal_parallel(q, k, v)
+    assert pins.rel_err(o2, o) < 1e-12
+    assert pins.rel_err(den2, den) < 1e-12
+
+
+@pytest.mark.parametrize("shape", RNG_SHAPES)
+def test_noncausal_equals_bruteforce(shape):
+    """eq. 5-6 equal the unmasked quadratic form."""
+    q, k, v = _qkv(shape, 31)
+    assert pins.rel_err(oracle.forward_noncausal(q, k, v), pins.brute_noncausal(q, k, v)) < 1e-12
+
+
+def test_final_state_definition():
+    """S_N = sum_j phi(K_j) V_j^T and Z_N = sum_j phi(K_j) (eq. 10-11)."""
+    q, k, v = _qkv((2, 2, 19, 5, 7), 41)
+    _, _, s, z = oracle.forward_causal(q, k, v)
+    pk = pins.phi_lib(k)
+    np.testing.assert_allclose(s, np.einsum("bhnd,bhnm->bhdm", pk, v), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(z, pk.sum(axis=2), rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------- closed forms (P3-P7)
+def test_constant_values_give_constant_output():
+    """Weights are positive and sum to one, so V_j = v for all j gives O = v (P3)."""
+    B, H, N, D, M = 2, 2, 25, 6, 4
+    q, k, _ = _qkv((B, H, N, D, M), 51)
+    v = np.broadcast_to(np.arange(1, M + 1, dtype=np.float64) - 2.5, (B, H, N, M)).copy()
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.forward_noncausal(q, k, v), v, rtol=0, atol=1e-14)
+    # O no longer depends on Q or K, so their gradients vanish
+    do = inputs.gaussian((B, H, N, M), 52)
+    dq, dk, dv = oracle.backward_causal(q, k, v, do)
+    assert np.max(np.abs(dq)) < 1e-13 and np.max(np.abs(dk)) < 1e-13
+
+
+def test_first_row_is_first_value():
+    """Causal O_1 = V_1 and dQ_1 = 0 for any Q, K (P4)."""
+    q, k, v = _qkv((2, 3, 9, 5, 4), 61)
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=0, atol=1e-15)
+    do = inputs.gaussian(v.shape, 62)
+    dq, _, _ = oracle.backward_causal(q, k, v, do)
+    assert np.max(np.abs(dq[:, :, 0])) < 1e-14
+
+
+def test_last_causal_row_equals_noncausal():
+    """With all N tokens visible, the last causal row is the non-causal row (P5)."""
+    q, k, v = _qkv((2, 2, 30, 6, 5), 71)
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    onc = oracle.forward_noncausal(q, k, v)
+    np.testing.assert_allclose(o[:, :, -1], onc[:, :, -1], rtol=1e-13, atol=1e-14)
+
+
+def test_zero_queries_and_keys_give_running_mean():
+    """Q = K = 0 gives phi = 1, so O_i = mean(V_1..V_i); non-causal: global mean (P6)."""
+    B, H, N, D, M = 1, 2, 37, 4, 3
+    v = inputs.gaussian((B, H, N, M), 81)
+    z = np.zeros((B, H, N, D))
+    o, den, _, _ = oracle.forward_causal(z, z, v)
+    running = np.cumsum(v.astype(np.float64), axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, running, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(den, np.broadcast_to(D * np.arange(1, N + 1.0), den.shape), rtol=1e-15)
+    onc = oracle.forward_noncausal(z, z, v)
+    np.testing.assert_allclose(onc, np.broadcast_to(v.astype(np.float64).mean(axis=2, keepdims=True), v.shape), rtol=1e-13,
+                               atol=1e-14)
+
+
+def test_convexity():
+    """O_i is a convex combination of V_1..V_i (P7)."""
+    q, k, v = _qkv((2, 2, 50, 4, 5), 91)
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    vmin = np.minimum.accumulate(v.astype(np.float64), axis=2)
+    vmax = np.maximum.accumulate(v.astype(np.float64), axis=2)
+    assert np.all(o >= vmin - 1e-12) and np.all(o <= vmax + 1e-12)
+
+
+def test_noncausal_permutation():
+    """Self-attention is a set operation: invariant to permuting (K, V) rows jointly,
+    equivariant to permuting Q rows (P8)."""
+    q, k, v = _qkv((1, 2, 23, 5, 4), 101)
+    o = oracle.forward_noncausal(q, k, v)
+    perm = np.random.Generator(np.random.PCG64(7)).permutation(23)
+    np.testing.assert_allclose(oracle.forward_noncausal(q, k[:, :, perm], v[:, :, perm]), o, rtol=1e-13)
+    np.testing.assert_allclose(oracle.forward_noncausal(q[:, :, perm], k, v), o[:, :, perm], rtol=1e-13)
+
+
+# ------------------------------------------------- state continuation (P11)
+def test_split_sequence_with_initial_state():
+    """Running the second half from the first half's (S, Z) equals the whole run."""
+    q, k, v = _qkv((2, 2, 31, 5, 3), 111)
+    o, den, s, z = oracle.forward_causal(q, k, v)
+    o1, d1, s1, z1 = oracle.forward_causal(q[:, :, :12], k[:, :, :12], v[:, :, :12])
+    o2, d2, s2, z2 = oracle.forward_causal(q[:, :, 12:], k[:, :, 12:], v[:, :, 12:], s1, z1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([d1, d2], axis=2), den, rtol=1e-13)
+    np.testing.assert_allclose(s2, s, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(z2, z, rtol=1e-13)
+
+
+def test_decode_steps_equal_bruteforce():
+    """T decode steps from zero state (eq. 16-20) reproduce eq. 8 row by row."""
+    B, H, T, D, M = 2, 3, 13, 5, 4
+    q, k, v = _qkv((B, H, T, D, M), 121)
+    s = np.zeros((B, H, D, M))
+    z = np.zeros((B, H, D))
+    ys = []
+    for t in range(T):
+        y, s, z = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, z)
+        ys.append(y)
+    ob, _ = pins.brute_causal(q, k, v)
+    assert pins.rel_err(np.stack(ys, axis=2), ob) < 1e-12
+    pk = pins.phi_lib(k)
+    np.testing.assert_allclose(s, np.einsum("bhnd,bhnm->bhdm", pk, v), rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_then_decode_equals_forward():
+    """A prefill's final state continued by decode steps equals one forward pass."""
+    B, H, N, D, M = 1, 2, 20, 4, 4
+    q, k, v = _qkv((B, H, N, D, M), 131)
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    _, _, s, z = oracle.forward_causal(q[:, :, :15], k[:, :, :15], v[:, :, :15])
+    for t in range(15, N):
+        y, s, z = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, z)
+        np.testing.assert_allclose(y, o[:, :, t], rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------- gradients (P9, P10)
+def _loss(q, k, v, do, s0=None, z0=None):
+    o, _, _, _ = oracle.forward_causal(q, k, v, s0, z0)
+    return float(np.sum(do * o))
+
+
+def _nudge(x, eps=1e-3):
+    """Move entries within eps of 0 away from the kink of phi'' at 0."""
+    x = np.array(x, dtype=np.float64)
+    small = np.abs(x) < eps
+    x[small] = np.where(x[small] >= 0, eps, -eps)
+    return x
+
+
+@pytest.mark.parametrize("D,M", [(3, 3), (4, 8), (8, 4)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_backward_finite_differences(D, M, with_state):
+    """Central differences of L = sum(dO * O) agree with the oracle's gradients (P10)."""
+    N = 7
+    q, k, v = _qkv((1, 1, N, D, M), 141 + D + M)
+    q, k, v = _nudge(q), _nudge(k), np.asarray(v, np.float64)
+    do = inputs.gaussian((1, 1, N, M), 149).astype(np.float64)
+    s0 = z0 = None
+    if with_state:
+        s0 = np.abs(inputs.gaussian((1, 1, D, M), 150)).astype(np.float64)
+        z0 = np.abs(inputs.gaussian((1, 1, D), 151)).astype(np.float64) + 0.5
+    dq, dk, dv = oracle.backward_causal(q, k, v, do, s0, z0)
+    h = 1e-6
+    for name, x, g in (("Q", q, dq), ("K", k, dk), ("V", v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"Q": (xp, k, v), "K": (q, xp, v), "V": (q, k, xp)}[name]
+            args_m = {"Q": (xm, k, v), "K": (q, xm, v), "V": (q, k, xm)}[name]
+            fd[idx] = (_loss(*args_p, do, s0, z0) - _loss(*args_m, do, s0, z0)) / (2 * h)
+        scale = max(np.max(np.abs(fd)), 1e-12)
+        assert np.max(np.abs(fd - g)) / scale < 1e-6, name
+
+
+def test_numerator_gradient_finite_differences():
+    """eq. 13-15 are the gradient of the trilinear numerator sum(G * Vbar) (P10)."""
+    N, C, Mb = 6, 4, 5
+    p = np.abs(inputs.gaussian((N, C), 161)).astype(np.float64) + 0.1
+    kf = np.abs(inputs.gaussian((N, C), 162)).astype(np.float64) + 0.1
+    vb = inputs.gaussian((N, Mb), 163).astype(np.float64)
+    gg = inputs.gaussian((N, Mb), 164).astype(np.float64)
+    dp, dkf, dvb = oracle.numerator_backward(p, kf, vb, gg)
+
+    def L(p_, k_, v_):
+        return float(np.sum(gg * pins.brute_numerator(p_, k_, v_)))
+
+    h = 1e-6
+    for x, g, which in ((p, dp, 0), (kf, dkf, 1), (vb, dvb, 2)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p = [p, kf, vb]
+            args_m = [p, kf, vb]
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[which] = xp
+            args_m[which] = xm
+            fd[idx] = (L(*args_p) - L(*args_m)) / (2 * h)
+        assert np.max(np.abs(fd - g)) / np.max(np.abs(fd)) < 1e-7
+    # trilinear Euler identity: each factor carries the whole sum
+    total = float(np.sum(gg * pins.brute_numerator(p, kf, vb)))
+    for x, g in ((p, dp), (kf, dkf), (vb, dvb)):
+        assert float(np.sum(x * g)) == pytest.approx(total, rel=1e-12)
+
+
+def test_euler_identities():
+    """O_i is 0-homogeneous in phi(Q_i) and (per head) in phi(K); 1-homogeneous in V (P9)."""
+    q, k, v = _qkv((2, 2, 40, 6, 5), 171)
+    do = inputs.gaussian(v.shape, 172)
+    dq, dk, dv = oracle.backward_causal(q, k, v, do)
+    q64, k64 = q.astype(np.float64), k.astype(np.float64)
+    # raw-gradient form: sum_d dQ_id * phi(Q_id)/phi'(Q_id) = 0 per row
+    rho_q = np.where(q64 > 0, q64 + 1.0, 1.0)
+    rho_k = np.where(k64 > 0, k64 + 1.0, 1.0)
+    row = np.sum(dq * rho_q, axis=-1)
+    assert np.max(np.abs(row)) < 1e-12 * max(1.0, np.max(np.abs(dq)))
+    head = np.sum(dk * rho_k, axis=(2, 3))
+    assert np.max(np.abs(head)) < 1e-11 * max(1.0, np.max(np.abs(dk)))
+    o, _, _, _ = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(np.sum(dv * v, axis=(2, 3)), np.sum(do * o, axis=(2, 3)), rtol=1e-12,
+                               atol=1e-12)
