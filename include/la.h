@@ -1,0 +1,189 @@
+/*
+ * la.h -- C ABI of the causal linear attention library (phi = elu + 1) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: "Transformers are RNNs: Fast Autoregressive Transformers with
+ * Linear Attention -- part 2/3".  With phi(x) = elu(x) + 1 (eq. 7, alpha = 1),
+ *   S_i = sum_{j<=i} phi(K_j) V_j^T,   Z_i = sum_{j<=i} phi(K_j)   (eq. 10-11)
+ *   O_i = phi(Q_i)^T S_i / phi(Q_i)^T Z_i                           (eq. 12)
+ * i.e. the causal masked attention of eq. 8 with sim(q,k) = phi(q).phi(k).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are device pointers owned by the caller, contiguous, row-major:
+ *      Q, K      [B, H, N, D]      V, O, dO  [B, H, N, M]
+ *      den       [B, H, N]   float32
+ *      S         [B, H, D, M] float32, S[d][m] = sum_j phi(K_j)[d] V_j[m]
+ *      Z         [B, H, D]    float32
+ *    Q, K, V, O, dO, dQ, dK, dV (and decode q, k, v, y) share one storage
+ *    type `dtype` (LA_F32 or LA_BF16); states, den and checkpoints are float32.
+ *    Arithmetic is float32 throughout (bf16 values are widened exactly).
+ *  - Heads are independent; B*H is a batch axis (Transformer Family v2,
+ *    multi-head attention).
+ *  - Supported sizes: B, H >= 1; N >= 0 (N = 0 is a no-op returning LA_OK);
+ *    D, M in {32, 64}.  Every pointer must be 16-byte aligned.
+ *  - Outputs must not overlap inputs (decode's S and Z are updated in place
+ *    by design).  Overlaps are rejected with LA_ERR_ALIAS.
+ *  - Scratch memory is the caller's `ws` of `ws_bytes` bytes, at least
+ *    la_workspace_size(...) (which may be 0; then ws may be NULL).  The
+ *    library never allocates device memory.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream).  No host synchronisation, no other streams.
+ *  - All arguments are validated before any launch; on error nothing is
+ *    launched and a status is returned (la_last_error() gives details).  A
+ *    failed launch returns LA_ERR_HIP with the HIP message.  No C++
+ *    exception crosses this interface.  The library holds no device state.
+ *  - phi is applied inside the kernels; gradients are with respect to the
+ *    raw Q, K, V.  No epsilon is added to the denominator: phi > 0 keeps it
+ *    positive for inputs above about -80 (below that exp underflows in fp32).
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL */
+  LA_ERR_SHAPE = 2,       /* B, H < 1, N < 0, or sizes overflow */
+  LA_ERR_DTYPE = 3,       /* dtype not LA_F32 / LA_BF16 */
+  LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  LA_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  LA_ERR_WORKSPACE = 6,   /* ws_bytes < la_workspace_size(...) or ws NULL */
+  LA_ERR_UNSUPPORTED = 7, /* D or M not in {32, 64} */
+  LA_ERR_HIP = 8,         /* a HIP launch failed */
+  LA_ERR_ARG = 9          /* inconsistent optional arguments */
+} la_status;
+
+typedef enum {
+  LA_OP_FWD_CAUSAL = 0,
+  LA_OP_FWD_NONCAUSAL = 1,
+  LA_OP_BWD_CAUSAL = 2,
+  LA_OP_DECODE = 3
+} la_op;
+
+/* Library version, as 10000*major + 100*minor + patch. */
+int la_version(void);
+
+/* Bytes of scratch memory the operation `op` needs for these sizes
+ * (0 when none).  Returns 0 for invalid arguments. */
+size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype);
+
+/* Bytes of the segment-state checkpoint written by la_forward_causal and
+ * read by la_backward_causal: the float32 state (S, Z) before every segment
+ * of the sequence and after the last one.  The sequence is cut into
+ * segments of a fixed length chosen from (B, H, N, D, M) only, so a
+ * checkpoint is valid for any call with the same sizes.  Its size is
+ * O(N * D * M / segment) per head, well inside the pages' linear-memory
+ * bound; no per-token state S_i is ever stored ("Transformers are RNNs --
+ * part 2/3", section 3.3.1). */
+size_t la_checkpoint_size(int B, int H, int N, int D, int M);
+
+/* Sequence segment length (tokens) used for these sizes. */
+int la_segment_length(int B, int H, int N, int D, int M);
+
+/* Process-wide override of the segment length, in 64-token chunks (0 =
+ * automatic, the default).  Results do not depend on it beyond rounding;
+ * it exists to test that and to tune.  A checkpoint must be consumed under
+ * the same setting it was written with.  Returns the previous value, or -1
+ * for a negative argument. */
+int la_set_segment_chunks(int chunks);
+
+/*
+ * Causal forward, eq. 9-12 ("Transformers are RNNs -- part 2/3", section 3.3).
+ *   Q, K, V     inputs.
+ *   O           output [B,H,N,M] in `dtype` (float32 values rounded to
+ *               nearest even for bf16).
+ *   den         optional output [B,H,N] float32: phi(Q_i)^T Z_i (needed by
+ *               la_backward_causal).  NULL to skip.
+ *   S0, Z0      optional initial state (both or neither): the state before
+ *               token 1, so a sequence can be continued (eq. 16-19 with a
+ *               non-zero s_0, z_0).
+ *   S_out,Z_out optional final state S_N, Z_N (both or neither).
+ *   ckpt        optional output of la_checkpoint_size(...) bytes: segment
+ *               boundary states for la_backward_causal.  NULL to skip.
+ */
+int la_forward_causal(const void *Q, const void *K, const void *V, void *O,
+                      float *den, const float *S0, const float *Z0,
+                      float *S_out, float *Z_out, float *ckpt, int B, int H,
+                      int N, int D, int M, int dtype, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
+ * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
+ * eq. 5-6): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) are formed once
+ * per head and reused for every query, O_i = phi(Q_i)^T S / phi(Q_i)^T Z.
+ */
+int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
+                         int B, int H, int N, int D, int M, int dtype,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Causal backward: gradients of a scalar loss with respect to the raw Q, K,
+ * V given dO = dL/dO, by the cumulative sums of eq. 13-15 ("Transformers are
+ * RNNs -- part 2/3", section 3.3.1): a forward-running sum of phi(K) V^T for
+ * the query gradient and a backward-running sum of phi(Q) (dL/dnum)^T for
+ * the key and value gradients, in linear time without any per-token state.
+ * The denominator's share (left by the pages to automatic differentiation)
+ * is the quotient rule: dL/dnum_i = dO_i / den_i, dL/dden_i =
+ * -(dO_i . O_i) / den_i.
+ *   O, den      the forward's O and den (required).
+ *   S0, Z0      the initial state the forward started from (both or neither).
+ *   ckpt        the forward's checkpoint (same sizes) or NULL: then the
+ *               segment states are recomputed into `ws`.
+ *   dQ, dK, dV  outputs in `dtype`.
+ * The gradient with respect to S0/Z0 is not produced.
+ */
+int la_backward_causal(const void *Q, const void *K, const void *V,
+                       const void *O, const float *den, const void *dO,
+                       const float *S0, const float *Z0, const float *ckpt,
+                       void *dQ, void *dK, void *dV, int B, int H, int N,
+                       int D, int M, int dtype, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/*
+ * One RNN step of the attention ("Transformers are RNNs -- part 2/3",
+ * section 3.4, eq. 18-20 without the projections, f_l and residual):
+ *   S += phi(k) v^T;  Z += phi(k);  y = phi(q)^T S / phi(q)^T Z.
+ *   q, k [B,H,D], v [B,H,M], y [B,H,M] in `dtype`; S [B,H,D,M] and Z [B,H,D]
+ *   float32, updated in place (the update comes first: masking is
+ *   inclusive).  Calls on one stream are ordered; overlapping calls on
+ *   different streams that share S/Z race.
+ */
+int la_decode_step(const void *q, const void *k, const void *v, float *S,
+                   float *Z, void *y, int B, int H, int D, int M, int dtype,
+                   void *stream);
+
+/* Name of a status code. */
+const char *la_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *la_last_error(void);
+
+/*
+ * Kernel timing hooks for measurement.  la_prof_select(name) makes every
+ * later launch of the kernel `name` (see la_kernel_names) be bracketed by a
+ * pair of HIP events recorded on the launch stream; NULL or "" stops it.
+ * la_prof_collect waits for the recorded events, returns the summed
+ * duration in milliseconds and the number of launches, and clears the
+ * record.  Up to 65536 launches are recorded; later ones are counted in
+ * `dropped`.  Not thread-safe with concurrent launches of the selected
+ * kernel on several host threads.
+ */
+int la_prof_select(const char *kernel_name);
+int la_prof_collect(double *total_ms, int *launches, int *dropped);
+
+/* Comma-separated names of the kernels the library launches. */
+const char *la_kernel_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

@@ -1,0 +1,259 @@
+"""Thin ctypes binding of the C ABI in include/la.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  There is
+no CPU path: if the library or a GPU is missing, calls raise.
+
+The ``la_*`` functions mirror the C entry points one to one (tensors in
+place of pointers, sizes inferred from the tensors).  The functions without
+the prefix allocate outputs and workspace and return them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+LA_F32, LA_BF16 = 0, 1
+LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_DECODE = 0, 1, 2, 3
+ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
+                "la_forward_noncausal", "la_backward_causal", "la_decode_step", "la_status_string", "la_last_error",
+                "la_prof_select", "la_prof_collect", "la_kernel_names", "la_set_segment_chunks")
+
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        lib = load()
+        name = lib.la_status_string(status).decode()
+        detail = lib.la_last_error().decode()
+        super().__init__(f"{func} failed: {name} ({status}): {detail}")
+        self.status = status
+
+
+def load(path: str | None = None):
+    """Load the in-tree library (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or _build.ensure_built()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} not found")
+    lib = ctypes.CDLL(path)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.la_version.restype = i
+    lib.la_workspace_size.restype = sz
+    lib.la_workspace_size.argtypes = [i] * 7
+    lib.la_checkpoint_size.restype = sz
+    lib.la_checkpoint_size.argtypes = [i] * 5
+    lib.la_segment_length.restype = i
+    lib.la_segment_length.argtypes = [i] * 5
+    lib.la_forward_causal.restype = i
+    lib.la_forward_causal.argtypes = [vp] * 10 + [i] * 6 + [vp, sz, vp]
+    lib.la_forward_noncausal.restype = i
+    lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_causal.restype = i
+    lib.la_backward_causal.argtypes = [vp] * 12 + [i] * 6 + [vp, sz, vp]
+    lib.la_decode_step.restype = i
+    lib.la_decode_step.argtypes = [vp] * 6 + [i] * 5 + [vp]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_status_string.argtypes = [i]
+    lib.la_last_error.restype = ctypes.c_char_p
+    lib.la_prof_select.restype = i
+    lib.la_prof_select.argtypes = [ctypes.c_char_p]
+    lib.la_prof_collect.restype = i
+    lib.la_prof_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.la_kernel_names.restype = ctypes.c_char_p
+    lib.la_set_segment_chunks.restype = i
+    lib.la_set_segment_chunks.argtypes = [i]
+    if path is None or _lib is None:
+        _lib = lib
+    return lib
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return LA_F32
+    if dt == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported dtype {dt}: use torch.float32 or torch.bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        raise LAError(status, func)
+
+
+def _sizes(q, v):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected Q/K [B,H,N,D] and V [B,H,N,M]")
+    B, H, N, D = q.shape
+    return B, H, N, D, v.shape[-1]
+
+
+def workspace_size(op: int, B, H, N, D, M, dtype: int) -> int:
+    return int(load().la_workspace_size(op, B, H, N, D, M, dtype))
+
+
+def checkpoint_size(B, H, N, D, M) -> int:
+    return int(load().la_checkpoint_size(B, H, N, D, M))
+
+
+def segment_length(B, H, N, D, M) -> int:
+    return int(load().la_segment_length(B, H, N, D, M))
+
+
+def set_segment_chunks(chunks: int) -> int:
+    """Force the segment length to `chunks` 64-token chunks (0 = automatic); returns the previous value."""
+    prev = int(load().la_set_segment_chunks(int(chunks)))
+    if prev < 0:
+        raise ValueError("chunks must be >= 0")
+    return prev
+
+
+def alloc_workspace(op: int, B, H, N, D, M, dtype: int, device) -> torch.Tensor:
+    n = workspace_size(op, B, H, N, D, M, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------- one-to-one calls
+def la_forward_causal(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=None, ckpt=None, ws=None,
+                      stream=None):
+    B, H, N, D, M = _sizes(Q, V)
+    dt = dtype_code(Q.dtype)
+    nb = ws.numel() if ws is not None else 0
+    st = load().la_forward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(den), _ptr(S0), _ptr(Z0), _ptr(S_out),
+                                  _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, _ptr(ws), nb, _stream(stream))
+    _check(st, "la_forward_causal")
+
+
+def la_forward_noncausal(Q, K, V, O, ws=None, stream=None):
+    B, H, N, D, M = _sizes(Q, V)
+    nb = ws.numel() if ws is not None else 0
+    st = load().la_forward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, N, D, M, dtype_code(Q.dtype),
+                                     _ptr(ws), nb, _stream(stream))
+    _check(st, "la_forward_noncausal")
+
+
+def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, ws=None, stream=None):
+    B, H, N, D, M = _sizes(Q, V)
+    nb = ws.numel() if ws is not None else 0
+    st = load().la_backward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(den), _ptr(dO), _ptr(S0), _ptr(Z0),
+                                   _ptr(ckpt), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, D, M, dtype_code(Q.dtype),
+                                   _ptr(ws), nb, _stream(stream))
+    _check(st, "la_backward_causal")
+
+
+def la_decode_step(q, k, v, S, Z, y, stream=None):
+    if q.dim() != 3:
+        raise ValueError("decode expects q, k [B,H,D], v [B,H,M]")
+    B, H, D = q.shape
+    M = v.shape[-1]
+    st = load().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(Z), _ptr(y), B, H, D, M,
+                               dtype_code(q.dtype), _stream(stream))
+    _check(st, "la_decode_step")
+
+
+# ------------------------------------------------------ allocating helpers
+def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=True):
+    """Causal forward.  Returns dict(o, den, ckpt[, s, z])."""
+    B, H, N, D, M = _sizes(q, v)
+    dev = q.device
+    o = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ck = torch.empty(checkpoint_size(B, H, N, D, M) // 4, dtype=torch.float32, device=dev) if checkpoint else None
+    s = z = None
+    if return_state:
+        s = torch.empty((B, H, D, M), dtype=torch.float32, device=dev)
+        z = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    ws = alloc_workspace(LA_OP_FWD_CAUSAL, B, H, N, D, M, dtype_code(q.dtype), dev)
+    la_forward_causal(q, k, v, o, den, s0, z0, s, z, ck, ws)
+    out = {"o": o, "den": den, "ckpt": ck}
+    if return_state:
+        out["s"], out["z"] = s, z
+    return out
+
+
+def forward_noncausal(q, k, v):
+    B, H, N, D, M = _sizes(q, v)
+    o = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    ws = alloc_workspace(LA_OP_FWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
+    la_forward_noncausal(q, k, v, o, ws)
+    return o
+
+
+def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None):
+    B, H, N, D, M = _sizes(q, v)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = alloc_workspace(LA_OP_BWD_CAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
+    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ws)
+    return dq, dk, dv
+
+
+def decode_step(q, k, v, s, z, y=None):
+    """One RNN step: updates s, z in place and returns y."""
+    if y is None:
+        y = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    la_decode_step(q, k, v, s, z, y)
+    return y
+
+
+class CausalLinearAttention(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out = forward_causal(q, k, v)
+        ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"])
+        return out["o"]
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, den, ck = ctx.saved_tensors
+        return backward_causal(q, k, v, o, den, do.contiguous(), ckpt=ck)
+
+
+def causal_linear_attention(q, k, v):
+    return CausalLinearAttention.apply(q, k, v)
+
+
+# ------------------------------------------------------------- timing hooks
+def prof_select(name: str | None):
+    _check(load().la_prof_select(name.encode() if name else None), "la_prof_select")
+
+
+def prof_collect():
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    dropped = ctypes.c_int()
+    _check(load().la_prof_collect(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(dropped)), "la_prof_collect")
+    return ms.value, n.value, dropped.value
+
+
+def kernel_names():
+    return load().la_kernel_names().decode().split(",")

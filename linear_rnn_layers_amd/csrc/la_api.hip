@@ -1,0 +1,475 @@
+// la_api.hip -- the C ABI of include/la.h: argument validation, sequence
+// planning, workspace layout, kernel dispatch and timing hooks.
+//
+// Nothing here allocates device memory or synchronises the stream (except
+// la_prof_collect, which waits for its own events by design).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/la.h"
+#include "la_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const std::string& msg) {
+  g_err = msg;
+  return status;
+}
+
+// ------------------------------------------------------------------ plan
+// The sequence of each head is cut into segments of L tokens, a multiple of
+// the 64-token chunk, so that about 1024 workgroups (four per compute unit)
+// exist even when B*H is small.  The plan depends on the sizes only.
+struct Plan {
+  long BH = 0;
+  int L = 0;
+  int nseg = 0;
+  int SV = 0;  // floats per state vector: D*M + D
+};
+
+std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
+
+Plan make_plan(int B, int H, int N, int D, int M) {
+  Plan p;
+  p.BH = (long)B * H;
+  p.SV = D * M + D;
+  const long nchunks = ((long)N + la::CH - 1) / la::CH;
+  if (N <= 0) {
+    p.L = la::CH;
+    p.nseg = 0;
+    return p;
+  }
+  const long target = 1024;
+  long segs = (target + p.BH - 1) / p.BH;
+  if (segs > nchunks) segs = nchunks;
+  if (segs < 1) segs = 1;
+  long cps = (nchunks + segs - 1) / segs;
+  const int forced = g_seg_chunks.load(std::memory_order_relaxed);
+  if (forced > 0) cps = forced < nchunks ? forced : nchunks;
+  p.L = (int)(cps * la::CH);
+  p.nseg = (int)(((long)N + p.L - 1) / p.L);
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH * entries * p.SV * sizeof(float)); }
+
+// Workspace regions (bytes) per operation.
+struct WsLayout {
+  size_t agg = 0, ckpt = 0, ragg = 0, rck = 0, total = 0;
+  size_t bytes() const { return agg + ckpt + ragg + rck + total; }
+};
+
+WsLayout ws_layout(int op, const Plan& p) {
+  WsLayout w;
+  switch (op) {
+    case LA_OP_FWD_CAUSAL:
+      w.agg = state_bytes(p, p.nseg);
+      w.ckpt = state_bytes(p, p.nseg + 1);
+      break;
+    case LA_OP_FWD_NONCAUSAL:
+      w.agg = state_bytes(p, p.nseg);
+      w.total = state_bytes(p, 1);
+      break;
+    case LA_OP_BWD_CAUSAL:
+      w.agg = state_bytes(p, p.nseg);
+      w.ckpt = state_bytes(p, p.nseg + 1);
+      w.ragg = state_bytes(p, p.nseg);
+      w.rck = state_bytes(p, p.nseg);
+      break;
+    default:
+      break;
+  }
+  if (p.nseg == 0) w = WsLayout{};
+  return w;
+}
+
+// -------------------------------------------------------------- validation
+bool dims_ok(int D, int M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
+
+int check_sizes(int B, int H, int N, int D, int M, int dtype) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_DTYPE, "dtype must be LA_F32 (0) or LA_BF16 (1)");
+  if (B < 1 || H < 1 || N < 0) return fail(LA_ERR_SHAPE, "need B >= 1, H >= 1, N >= 0");
+  if (!dims_ok(D, M)) return fail(LA_ERR_UNSUPPORTED, "D and M must each be 32 or 64");
+  const double elems = (double)B * H * (double)N * (D > M ? D : M);
+  if (elems > 4.0e18 || (double)B * H * (N > 0 ? N : 1) > 2.0e9) return fail(LA_ERR_SHAPE, "sizes overflow");
+  return LA_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+  bool output;
+};
+
+int check_ptrs(const std::vector<Range>& rs) {
+  for (const Range& r : rs) {
+    if (r.lo == 0) continue;
+    if (r.lo % 16) return fail(LA_ERR_ALIGN, std::string(r.name) + " is not 16-byte aligned");
+  }
+  for (size_t a = 0; a < rs.size(); ++a) {
+    if (!rs[a].output || rs[a].lo == 0 || rs[a].hi <= rs[a].lo) continue;
+    for (size_t b = 0; b < rs.size(); ++b) {
+      if (a == b || rs[b].lo == 0 || rs[b].hi <= rs[b].lo) continue;
+      if (rs[a].lo < rs[b].hi && rs[b].lo < rs[a].hi)
+        return fail(LA_ERR_ALIAS, std::string(rs[a].name) + " overlaps " + rs[b].name);
+    }
+  }
+  return LA_OK;
+}
+
+Range rng(const char* name, const void* p, size_t bytes, bool out) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, lo ? lo + bytes : 0, out};
+}
+
+// ------------------------------------------------------------- profiling
+struct Prof {
+  std::mutex mu;
+  std::string sel;
+  std::vector<hipEvent_t> ev;  // pairs
+  size_t used = 0;             // pairs recorded
+  int dropped = 0;
+  static constexpr size_t kMax = 65536;
+};
+Prof& prof() {
+  static Prof* p = new Prof();  // never destroyed: events outlive static teardown order
+  return *p;
+}
+
+int prof_begin(const char* name, hipStream_t s) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  if (P.sel.empty() || P.sel != name) return -1;
+  if (P.used >= Prof::kMax) {
+    ++P.dropped;
+    return -1;
+  }
+  if (P.ev.size() < 2 * (P.used + 1)) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return -1;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return -1;
+    }
+    P.ev.push_back(a);
+    P.ev.push_back(b);
+  }
+  const int idx = (int)P.used++;
+  (void)hipEventRecord(P.ev[2 * idx], s);
+  return idx;
+}
+
+void prof_end(int idx, hipStream_t s) {
+  if (idx < 0) return;
+  Prof& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  (void)hipEventRecord(P.ev[2 * idx + 1], s);
+}
+
+template <typename Kern, typename... Args>
+int launch(const char* name, Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LA_OK;
+  const int idx = prof_begin(name, s);
+  hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
+  const hipError_t e = hipGetLastError();
+  prof_end(idx, s);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e));
+  return LA_OK;
+}
+
+// ------------------------------------------------------------- dispatch
+#define LA_DISPATCH(dtype, D, M, FN, ...)                                                        \
+  do {                                                                                           \
+    if ((dtype) == LA_F32) {                                                                     \
+      if ((D) == 32 && (M) == 32) return FN<float, 32, 32>(__VA_ARGS__);                         \
+      if ((D) == 32 && (M) == 64) return FN<float, 32, 64>(__VA_ARGS__);                         \
+      if ((D) == 64 && (M) == 32) return FN<float, 64, 32>(__VA_ARGS__);                         \
+      return FN<float, 64, 64>(__VA_ARGS__);                                                     \
+    } else {                                                                                     \
+      if ((D) == 32 && (M) == 32) return FN<la::bf16_t, 32, 32>(__VA_ARGS__);                    \
+      if ((D) == 32 && (M) == 64) return FN<la::bf16_t, 32, 64>(__VA_ARGS__);                    \
+      if ((D) == 64 && (M) == 32) return FN<la::bf16_t, 64, 32>(__VA_ARGS__);                    \
+      return FN<la::bf16_t, 64, 64>(__VA_ARGS__);                                                \
+    }                                                                                            \
+  } while (0)
+
+char* region(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Segment states (agg -> ckpt) for the causal passes.
+template <typename T, int D, int M>
+int run_states(const Plan& p, int N, const void* K, const void* V, const float* S0, const float* Z0, float* agg,
+               float* ckpt, float* S_out, float* Z_out, hipStream_t s) {
+  int st = LA_OK;
+  if (p.nseg > 0) {
+    st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+    if (st) return st;
+  }
+  return launch("scan_fwd", la::k_scan_fwd<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
+                dim3(la::NT), s, (const float*)agg, S0, Z0, ckpt, S_out, Z_out, (float*)nullptr, p.nseg);
+}
+
+template <typename T, int D, int M>
+int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
+                    const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, hipStream_t s) {
+  const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
+  const bool need_states = p.nseg > 1 || ckpt != nullptr || p.nseg == 0;
+  if (!need_states) {
+    // one segment, no checkpoint: the chunk kernel starts from S0/Z0 and
+    // writes the final state itself
+    return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)p.BH), dim3(la::NT), s, (const T*)Q,
+                  (const T*)K, (const T*)V, (T*)O, den, S0, Z0, (long)D * M, 0L, (long)D, 0L, S_out, Z_out, N, p.L,
+                  1);
+  }
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  float* ck = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
+  int st = run_states<T, D, M>(p, N, K, V, S0, Z0, agg, ck, S_out, Z_out, s);
+  if (st || p.nseg == 0) return st;
+  const long sv = p.SV;
+  return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, (const float*)ck, (const float*)(ck + D * M),
+                (long)(p.nseg + 1) * sv, sv, (long)(p.nseg + 1) * sv, sv, (float*)nullptr, (float*)nullptr, N, p.L,
+                p.nseg);
+}
+
+template <typename T, int D, int M>
+int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, int N, void* ws,
+                       hipStream_t s) {
+  if (p.nseg == 0) return LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_FWD_NONCAUSAL, p);
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  float* tot = reinterpret_cast<float*>(region(ws, wl.agg));
+  int st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                  (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+  if (st) return st;
+  st = launch("scan_fwd", la::k_scan_fwd<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
+              dim3(la::NT), s, (const float*)agg, (const float*)nullptr, (const float*)nullptr, (float*)nullptr,
+              (float*)nullptr, (float*)nullptr, tot, p.nseg);
+  if (st) return st;
+  const long sv = p.SV;
+  return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, (const float*)tot,
+                (const float*)(tot + D * M), sv, 0L, sv, 0L, (float*)nullptr, (float*)nullptr, N, p.L, p.nseg);
+}
+
+template <typename T, int D, int M>
+int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* O, const float* den,
+                    const void* dO, const float* S0, const float* Z0, const float* ckpt, void* dQ, void* dK,
+                    void* dV, int N, void* ws, hipStream_t s) {
+  if (p.nseg == 0) return LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_BWD_CAUSAL, p);
+  int st = LA_OK;
+  const float* ck = ckpt;
+  if (!ck) {
+    float* agg = reinterpret_cast<float*>(region(ws, 0));
+    float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
+    st = run_states<T, D, M>(p, N, K, V, S0, Z0, agg, ckw, nullptr, nullptr, s);
+    if (st) return st;
+    ck = ckw;
+  }
+  float* rck = nullptr;
+  if (p.nseg > 1) {
+    float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
+    rck = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+    st = launch("seg_rstate", la::k_seg_rstate<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg);
+    if (st) return st;
+    st = launch("scan_rev", la::k_scan_rev<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
+                dim3(la::NT), s, (const float*)ragg, rck, p.nseg);
+    if (st) return st;
+  }
+  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s, (const T*)Q,
+                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)rck, (T*)dQ, (T*)dK, (T*)dV, N, p.L,
+                p.nseg);
+}
+
+template <typename T, int D, int M>
+int decode_impl(long BH, const void* q, const void* k, const void* v, float* S, float* Z, void* y, hipStream_t s) {
+  return launch("decode", la::k_decode<T, D, M>, dim3((unsigned)((BH + 3) / 4)), dim3(la::NT), s, (const T*)q,
+                (const T*)k, (const T*)v, S, Z, (T*)y, (int)BH);
+}
+
+size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int la_version(void) { return 100; }
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL: return "LA_ERR_NULL";
+    case LA_ERR_SHAPE: return "LA_ERR_SHAPE";
+    case LA_ERR_DTYPE: return "LA_ERR_DTYPE";
+    case LA_ERR_ALIGN: return "LA_ERR_ALIGN";
+    case LA_ERR_ALIAS: return "LA_ERR_ALIAS";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+    case LA_ERR_ARG: return "LA_ERR_ARG";
+    default: return "LA_ERR_UNKNOWN";
+  }
+}
+
+const char* la_last_error(void) { return g_err.c_str(); }
+
+const char* la_kernel_names(void) {
+  return "seg_state,scan_fwd,fwd_causal,fwd_noncausal,seg_rstate,scan_rev,bwd_causal,decode";
+}
+
+size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
+  if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
+  if (op < LA_OP_FWD_CAUSAL || op > LA_OP_DECODE) return 0;
+  return ws_layout(op, make_plan(B, H, N, D, M)).bytes();
+}
+
+size_t la_checkpoint_size(int B, int H, int N, int D, int M) {
+  if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
+  const Plan p = make_plan(B, H, N, D, M);
+  return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float);
+}
+
+int la_segment_length(int B, int H, int N, int D, int M) {
+  if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
+  return make_plan(B, H, N, D, M).L;
+}
+
+int la_set_segment_chunks(int chunks) {
+  if (chunks < 0) return -1;
+  return g_seg_chunks.exchange(chunks);
+}
+
+int la_forward_causal(const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
+                      const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H, int N, int D, int M,
+                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
+  if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
+  if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
+  const Plan p = make_plan(B, H, N, D, M);
+  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const size_t need = ws_layout(LA_OP_FWD_CAUSAL, p).bytes();
+  const bool uses_ws = p.nseg != 1 || ckpt != nullptr;
+  if (uses_ws && need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
+                   rng("V", V, bh * N * M * es, false), rng("S0", S0, bh * D * M * 4, false),
+                   rng("Z0", Z0, bh * D * 4, false), rng("O", O, bh * N * M * es, true),
+                   rng("den", den, bh * N * 4, true), rng("S_out", S_out, bh * D * M * 4, true),
+                   rng("Z_out", Z_out, bh * D * 4, true),
+                   rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), true),
+                   rng("ws", uses_ws ? ws : nullptr, need, true)});
+  if (st) return st;
+  if (N == 0 && !S_out && !ckpt) return LA_OK;
+  LA_DISPATCH(dtype, D, M, fwd_causal_impl, p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
+              (hipStream_t)stream);
+}
+
+int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int D, int M,
+                         int dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  if (N == 0) return LA_OK;
+  if (!Q || !K || !V || !O) return fail(LA_ERR_NULL, "Q, K, V and O are required");
+  const Plan p = make_plan(B, H, N, D, M);
+  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const size_t need = ws_layout(LA_OP_FWD_NONCAUSAL, p).bytes();
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
+                   rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, true),
+                   rng("ws", ws, need, true)});
+  if (st) return st;
+  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, N, ws, (hipStream_t)stream);
+}
+
+int la_backward_causal(const void* Q, const void* K, const void* V, const void* O, const float* den,
+                       const void* dO, const float* S0, const float* Z0, const float* ckpt, void* dQ, void* dK,
+                       void* dV, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
+  if (N == 0) return LA_OK;
+  if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
+    return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
+  const Plan p = make_plan(B, H, N, D, M);
+  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const size_t need = ws_layout(LA_OP_BWD_CAUSAL, p).bytes();
+  const bool uses_ws = ckpt == nullptr || p.nseg > 1;
+  if (uses_ws && need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
+                   rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, false),
+                   rng("den", den, bh * N * 4, false), rng("dO", dO, bh * N * M * es, false),
+                   rng("S0", S0, bh * D * M * 4, false), rng("Z0", Z0, bh * D * 4, false),
+                   rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), false),
+                   rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
+                   rng("dV", dV, bh * N * M * es, true), rng("ws", uses_ws ? ws : nullptr, need, true)});
+  if (st) return st;
+  LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dQ, dK, dV, N, ws,
+              (hipStream_t)stream);
+}
+
+int la_decode_step(const void* q, const void* k, const void* v, float* S, float* Z, void* y, int B, int H, int D,
+                   int M, int dtype, void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, 1, D, M, dtype);
+  if (st) return st;
+  if (!q || !k || !v || !S || !Z || !y) return fail(LA_ERR_NULL, "q, k, v, S, Z and y are required");
+  const size_t es = esize(dtype), bh = (size_t)B * H;
+  st = check_ptrs({rng("q", q, bh * D * es, false), rng("k", k, bh * D * es, false), rng("v", v, bh * M * es, false),
+                   rng("S", S, bh * D * M * 4, true), rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
+  if (st) return st;
+  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, S, Z, y, (hipStream_t)stream);
+}
+
+int la_prof_select(const char* kernel_name) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.sel = kernel_name ? kernel_name : "";
+  P.used = 0;
+  P.dropped = 0;
+  return LA_OK;
+}
+
+int la_prof_collect(double* total_ms, int* launches, int* dropped) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  double sum = 0.0;
+  for (size_t i = 0; i < P.used; ++i) {
+    if (hipEventSynchronize(P.ev[2 * i + 1]) != hipSuccess)
+      return fail(LA_ERR_HIP, "hipEventSynchronize failed in la_prof_collect");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]) != hipSuccess)
+      return fail(LA_ERR_HIP, "hipEventElapsedTime failed in la_prof_collect");
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int)P.used;
+  if (dropped) *dropped = P.dropped;
+  P.used = 0;
+  P.dropped = 0;
+  return LA_OK;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports what include/la.h declares, and rejects bad
+arguments before launching anything.  CPU only: no call here reaches a kernel
+(fake device addresses are never dereferenced by the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_rnn_layers_amd import binding
+from linear_rnn_layers_amd import build as labuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, UNSUPPORTED, HIP, ARG = range(10)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in la.h but not exported"
+    assert sorted(binding.ENTRY_POINTS) == names
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", labuild.LIB], capture_output=True, text=True, check=True)
+    exported = sorted({ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln})
+    assert exported == declared_functions()
+
+
+def test_version_and_strings(lib):
+    assert lib.la_version() >= 100
+    assert lib.la_status_string(0) == b"LA_OK"
+    assert lib.la_status_string(WORKSPACE) == b"LA_ERR_WORKSPACE"
+    assert lib.la_status_string(99) == b"LA_ERR_UNKNOWN"
+    names = binding.kernel_names()
+    assert "fwd_causal" in names and "bwd_causal" in names and "decode" in names
+
+
+# Fake, 256-aligned, non-overlapping device addresses (never dereferenced).
+BASE = 0x7F0000000000
+
+
+def addr(i):
+    return ctypes.c_void_p(BASE + i * (1 << 32))
+
+
+def fwd(lib, B=2, H=2, N=100, D=32, M=32, dtype=0, ws=True, **over):
+    args = dict(Q=addr(1), K=addr(2), V=addr(3), O=addr(4), den=addr(5), S0=None, Z0=None, S_out=None, Z_out=None,
+                ckpt=None)
+    args.update(over)
+    need = lib.la_workspace_size(0, B, H, N, D, M, dtype)
+    wsp = addr(20) if ws else None
+    nb = need if ws else 0
+    if "ws_bytes" in over:
+        nb = over.pop("ws_bytes")
+        args.pop("ws_bytes")
+    return lib.la_forward_causal(args["Q"], args["K"], args["V"], args["O"], args["den"], args["S0"], args["Z0"],
+                                 args["S_out"], args["Z_out"], args["ckpt"], B, H, N, D, M, dtype, wsp, nb, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, dtype=2) == DTYPE
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, H=-1) == SHAPE
+    assert fwd(lib, N=-5) == SHAPE
+    assert fwd(lib, D=48) == UNSUPPORTED
+    assert fwd(lib, M=128) == UNSUPPORTED
+    assert fwd(lib, Q=None) == NULL
+    assert fwd(lib, O=None) == NULL
+    assert fwd(lib, S0=addr(6)) == ARG  # S0 without Z0
+    assert fwd(lib, S_out=addr(7)) == ARG  # S_out without Z_out
+    assert fwd(lib, K=ctypes.c_void_p(BASE + 2 * (1 << 32) + 8)) == ALIGN
+    assert fwd(lib, O=addr(1)) == ALIAS  # output on top of Q
+    assert fwd(lib, den=ctypes.c_void_p(BASE + 4 * (1 << 32) + 64)) == ALIAS  # den inside O
+    assert fwd(lib, ws=False) == WORKSPACE
+    assert fwd(lib, ws_bytes=16) == WORKSPACE
+    assert b"workspace" in lib.la_last_error()
+
+
+def test_noncausal_and_backward_validation(lib):
+    ws = lib.la_workspace_size(1, 1, 1, 64, 64, 64, 1)
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), None, 1, 1, 64, 64, 64, 1, addr(20), ws, None) == NULL
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), 1, 1, 64, 64, 64, 1, None, 0, None) == WORKSPACE
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(3), 1, 1, 64, 64, 64, 1, addr(20), ws,
+                                    None) == ALIAS
+    # N = 0 is a no-op
+    assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, None, 0, None) == OK
+    wsb = lib.la_workspace_size(2, 2, 2, 100, 32, 32, 0)
+    args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), None, None, None, addr(7), addr(8), addr(9)]
+    a = list(args)
+    a[4] = None  # den is required
+    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == NULL
+    a = list(args)
+    a[9] = addr(6)  # dQ on top of dO
+    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == ALIAS
+    a = list(args)
+    a[6] = addr(10)  # S0 without Z0
+    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == ARG
+    assert lib.la_backward_causal(*args, 2, 2, 100, 32, 32, 0, addr(20), wsb - 1, None) == WORKSPACE
+    assert lib.la_backward_causal(*args, 2, 2, 0, 32, 32, 0, None, 0, None) == OK
+
+
+def test_decode_validation(lib):
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), None, 2, 2, 64, 64, 1, None) == NULL
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, None) == ALIAS
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), 2, 2, 16, 64, 1, None) == UNSUPPORTED
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, None) == SHAPE
+
+
+def _plan(B, H, N):
+    """The segment plan, restated: about 1024 workgroups, segments of whole 64-token chunks."""
+    bh = B * H
+    nch = -(-N // 64)
+    segs = max(1, min(nch, -(-1024 // bh)))
+    L = -(-nch // segs) * 64
+    return L, -(-N // L)
+
+
+@pytest.mark.parametrize("B,H,N,D,M", [(1, 1, 64, 32, 32), (16, 8, 784, 32, 32), (4, 8, 3072, 32, 32),
+                                        (1, 16, 65536, 64, 64), (3, 5, 1000, 64, 32), (1, 1, 1, 32, 64)])
+def test_plan_and_sizes(lib, B, H, N, D, M):
+    L, nseg = _plan(B, H, N)
+    assert lib.la_segment_length(B, H, N, D, M) == L
+    sv = D * M + D
+    assert lib.la_checkpoint_size(B, H, N, D, M) == B * H * (nseg + 1) * sv * 4
+    # linear-memory bound: the checkpoint never exceeds B*H*N*max(D,M) floats by more than one state per head
+    assert lib.la_checkpoint_size(B, H, N, D, M) <= 4 * B * H * (N * max(D, M) + 2 * sv)
+    assert lib.la_workspace_size(3, B, H, N, D, M, 1) == 0
+    assert lib.la_workspace_size(0, B, H, N, D, M, 0) >= B * H * (2 * nseg + 1) * sv * 4
+    assert lib.la_workspace_size(9, B, H, N, D, M, 0) == 0

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element.
+
+Gate (per output tensor): rowerr <= 1e-4 for float32 storage and <= 2e-2
+for bf16 storage (tests/gpu_util.py defines rowerr).  Every call goes through
+the C ABI via the ctypes binding; the oracle runs on the host CPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_rnn_layers_amd import binding, inputs
+from tests import pins
+from tests.gpu_util import TOL, dev, dev32, host, rowerr
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = inputs.F32, inputs.BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    binding.load()
+    binding.set_segment_chunks(0)
+    yield
+    binding.set_segment_chunks(0)
+
+
+def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
+    q = inputs.gaussian((B, H, N, D), seed, sigma, dtype)
+    k = inputs.gaussian((B, H, N, D), seed + 1, sigma, dtype)
+    v = inputs.gaussian((B, H, N, M), seed + 2, sigma, dtype)
+    return q, k, v
+
+
+def gpu_forward(q, k, v, dtype, s0=None, z0=None):
+    out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
+                                 s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                 return_state=True, checkpoint=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_forward(q, k, v, dtype, s0=None, z0=None, tol=None):
+    tol = TOL[dtype] if tol is None else tol
+    out = gpu_forward(q, k, v, dtype, s0, z0)
+    o, den, s, z = oracle.forward_causal(q, k, v, s0, z0)
+    errs = {"O": rowerr(host(out["o"]), o), "den": rowerr(host(out["den"]), den, False),
+            "S_N": rowerr(host(out["s"]), s), "Z_N": rowerr(host(out["z"]), z, False)}
+    assert max(errs.values()) <= tol, errs
+    return out
+
+
+SWEEP_N = [1, 2, 15, 16, 17, 63, 64, 65, 129, 784]
+DM = [(32, 32), (64, 64), (32, 64), (64, 32)]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", SWEEP_N)
+def test_forward_causal_sweep(N, D, M, dtype):
+    q, k, v = _qkv(2, 3, N, D, M, dtype, 1000 + N)
+    check_forward(q, k, v, dtype)
+
+
+def test_small_workload_forward():
+    """B=1 H=1 N=64 D=M=32 float32, against the oracle and the quadratic eq. 8."""
+    w = inputs.SMALL
+    q, k, v = w.qkv()
+    out = check_forward(q, k, v, F32)
+    ob, denb = pins.brute_causal(q, k, v)
+    assert rowerr(host(out["o"]), ob) <= 1e-4
+    assert rowerr(host(out["den"]), denb, False) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_forward_initial_state_and_split(dtype):
+    """Continuing from (S0, Z0) matches the oracle and the unsplit sequence."""
+    B, H, N, D, M = 2, 2, 300, 64, 32
+    q, k, v = _qkv(B, H, N, D, M, dtype, 2000)
+    _, _, s0, z0 = oracle.forward_causal(q[:, :, :111], k[:, :, :111], v[:, :, :111])
+    check_forward(q[:, :, 111:], k[:, :, 111:], v[:, :, 111:], dtype, s0, z0)
+
+
+@pytest.mark.parametrize("chunks", [1, 2, 3, 5])
+def test_segment_length_invariance(chunks):
+    """Results do not depend on how the sequence is cut into segments."""
+    B, H, N, D, M = 2, 2, 784, 32, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 3000)
+    do = inputs.gaussian((B, H, N, M), 3004)
+    prev = binding.set_segment_chunks(chunks)
+    try:
+        assert binding.segment_length(B, H, N, D, M) == 64 * chunks
+        out = check_forward(q, k, v, F32)
+        dq, dk, dv = binding.backward_causal(dev(q), dev(k), dev(v), out["o"], out["den"], dev(do), ckpt=out["ckpt"])
+        torch.cuda.synchronize()
+    finally:
+        binding.set_segment_chunks(prev)
+    rq, rk, rv = oracle.backward_causal(q, k, v, do)
+    errs = [rowerr(host(dq), rq, row_floor=CANCEL_FLOOR * dq_cancel_scale(q, k, v, do)), rowerr(host(dk), rk),
+            rowerr(host(dv), rv)]
+    assert max(errs) <= 1e-4, errs
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 17, 64, 200, 784])
+def test_forward_noncausal_sweep(N, D, M, dtype):
+    q, k, v = _qkv(2, 3, N, D, M, dtype, 4000 + N)
+    o = binding.forward_noncausal(dev(q, dtype), dev(k, dtype), dev(v, dtype))
+    torch.cuda.synchronize()
+    assert rowerr(host(o), oracle.forward_noncausal(q, k, v)) <= TOL[dtype]
+
+
+# The query gradient of eq. 13 with the denominator's share,
+#   dphiQ_i = S_i g_i + c_i Z_i,
+# is a cancellation: its first term S_i g_i is removed along Z_i, exactly so
+# for token 1 (pin P4: O_1 = V_1 whatever Q, K are) and nearly so for rows
+# that happen to be small.  A relative error of such a row is limited by the
+# working precision of the terms it cancels, so each dQ row is measured
+# against the largest of |row|, 1e-3 x its head's largest row, and
+# CANCEL_FLOOR x |S_i g_i * phi'(Q_i)| (the oracle's eq. 13 first term).  At
+# the float32 gate this allows 1e-6 of the cancelled terms, i.e. about 16
+# float32 ulps.
+CANCEL_FLOOR = 1e-2
+
+
+def dq_cancel_scale(q, k, v, do, s0=None, z0=None):
+    """Per-row |S_i g_i * phi'(Q_i)|_inf from the oracle (eq. 13's first term, g_i = dO_i / den_i)."""
+    _, den, _, _ = oracle.forward_causal(q, k, v, s0, z0)
+    pq, pk = pins.phi_lib(q), pins.phi_lib(k)
+    g = do.astype(np.float64) / den[..., None]
+    u = np.empty(q.shape)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            u[b, h] = oracle.numerator_backward(pq[b, h], pk[b, h], v[b, h], g[b, h])[0]
+    if s0 is not None:
+        u += np.einsum("bhdm,bhnm->bhnd", s0, g)
+    return np.abs(u * np.minimum(pq, 1.0)).max(-1)
+
+
+def check_backward(q, k, v, do, dtype, s0=None, z0=None, use_ckpt=True, tol=None):
+    tol = TOL[dtype] if tol is None else tol
+    out = gpu_forward(q, k, v, dtype, s0, z0)
+    Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    dq, dk, dv = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, dtype),
+                                         s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                         ckpt=out["ckpt"] if use_ckpt else None)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_causal(q, k, v, do, s0, z0)
+    dq, dk, dv = host(dq), host(dk), host(dv)
+    errs = {"dV": rowerr(dv, rv),
+            "dQ": rowerr(dq, rq, row_floor=CANCEL_FLOOR * dq_cancel_scale(q, k, v, do, s0, z0))}
+    if s0 is None and q.shape[2] == 1:
+        # N = 1: dK_1 = phi(Q_1) g_1.(V_1 - O_1) is an exact zero too; terms of size |phi(Q_1)| |g_1.V_1|
+        pq, pk = pins.phi_lib(q[:, :, 0]), pins.phi_lib(k[:, :, 0])
+        scale = np.abs((v[:, :, 0].astype(np.float64) * do[:, :, 0]).sum(-1)) / (pq * pk).sum(-1) * pq.max(-1)
+        errs["dK"] = float((np.abs(dk[:, :, 0]).max(-1) / (CANCEL_FLOOR * scale)).max())
+    else:
+        errs["dK"] = rowerr(dk, rk)
+    assert max(errs.values()) <= tol, errs
+    return dq, dk, dv
+
+
+def test_first_token_query_gradient_vanishes():
+    """Pin P4 on the GPU path: dQ of token 1 is zero to working precision of the cancelled terms."""
+    for dtype, kappa in ((F32, 1e-5), (BF16, 1e-3)):
+        q, k, v = _qkv(3, 4, 40, 64, 32, dtype, 7100)
+        do = inputs.gaussian((3, 4, 40, 32), 7104, 1.0, dtype)
+        dq, _, _ = check_backward(q, k, v, do, dtype)
+        scale = dq_cancel_scale(q, k, v, do)[:, :, 0]
+        assert (np.abs(dq[:, :, 0]).max(-1) / scale).max() <= kappa
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 65, 200, 784])
+def test_backward_causal_sweep(N, D, M, dtype):
+    q, k, v = _qkv(2, 3, N, D, M, dtype, 5000 + N)
+    do = inputs.gaussian((2, 3, N, M), 5999, 1.0, dtype)
+    check_backward(q, k, v, do, dtype)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("use_ckpt", [True, False])
+def test_backward_with_initial_state(dtype, use_ckpt):
+    B, H, N, D, M = 2, 2, 333, 32, 64
+    q, k, v = _qkv(B, H, N, D, M, dtype, 6000)
+    do = inputs.gaussian((B, H, N, M), 6003, 1.0, dtype)
+    _, _, s0, z0 = oracle.forward_causal(*_qkv(B, H, 50, D, M, dtype, 6100))
+    check_backward(q, k, v, do, dtype, s0, z0, use_ckpt)
+
+
+def test_backward_first_row_and_euler_identity():
+    """sum_d dQ_id rho(Q_id) = 0 per row (phi-homogeneity of O_i in phi(Q_i)), on GPU outputs."""
+    B, H, N, D, M = 2, 2, 256, 32, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 7000)
+    do = inputs.gaussian((B, H, N, M), 7003)
+    dq, _, _ = check_backward(q, k, v, do, F32)
+    scale = np.abs(dq).max()
+    rho = np.where(q > 0, q + 1.0, 1.0)
+    assert np.abs((dq * rho).sum(-1)).max() <= 1e-5 * scale * D
+
+
+def test_determinism():
+    """Two runs of forward + backward give bit-identical results."""
+    B, H, N, D, M = 4, 4, 1000, 64, 64
+    q, k, v = _qkv(B, H, N, D, M, BF16, 8000)
+    do = inputs.gaussian((B, H, N, M), 8003, 1.0, BF16)
+    Q, K, V, dO = dev(q, BF16), dev(k, BF16), dev(v, BF16), dev(do, BF16)
+    res = []
+    for _ in range(2):
+        out = binding.forward_causal(Q, K, V)
+        grads = binding.backward_causal(Q, K, V, out["o"], out["den"], dO, ckpt=out["ckpt"])
+        torch.cuda.synchronize()
+        res.append([out["o"].clone(), out["den"].clone()] + [g.clone() for g in grads])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ decode steps
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+def test_decode_steps(D, M, dtype):
+    B, H, T = 3, 5, 20
+    q, k, v = _qkv(B, H, T, D, M, dtype, 9000 + D + M)
+    s = torch.zeros((B, H, D, M), device="cuda")
+    z = torch.zeros((B, H, D), device="cuda")
+    ys = []
+    for t in range(T):
+        y = binding.decode_step(dev(q[:, :, t], dtype), dev(k[:, :, t], dtype), dev(v[:, :, t], dtype), s, z)
+        ys.append(host(y))
+    torch.cuda.synchronize()
+    o, _, so, zo = oracle.forward_causal(q, k, v)
+    assert rowerr(np.stack(ys, axis=2), o) <= TOL[dtype]
+    assert rowerr(host(s), so) <= 1e-4 and rowerr(host(z), zo, False) <= 1e-4
+
+
+def test_prefill_then_decode_equals_forward():
+    """A GPU prefill's final state continued by GPU decode steps matches the oracle's one-pass forward."""
+    B, H, N, D, M, P = 2, 3, 100, 64, 64, 70
+    q, k, v = _qkv(B, H, N, D, M, BF16, 9500)
+    out = gpu_forward(q[:, :, :P], k[:, :, :P], v[:, :, :P], BF16)
+    s, z = out["s"], out["z"]
+    o, _, so, zo = oracle.forward_causal(q, k, v)
+    for t in range(P, N):
+        y = binding.decode_step(dev(q[:, :, t], BF16), dev(k[:, :, t], BF16), dev(v[:, :, t], BF16), s, z)
+        assert rowerr(host(y), o[:, :, t]) <= 2e-2
+    assert rowerr(host(s), so) <= 1e-4
+
+
+# --------------------------------------------------------- full workloads
+def test_mnist_workload():
+    """B=16 H=8 N=784 D=M=32 float32: causal forward + backward and non-causal forward."""
+    w = inputs.MNIST
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    check_backward(q, k, v, do, F32)
+    o = binding.forward_noncausal(dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert rowerr(host(o), oracle.forward_noncausal(q, k, v)) <= 1e-4
+
+
+@pytest.mark.parametrize("layer", [0, 15])
+def test_cifar_workload_layer(layer):
+    """B=4 H=8 N=3072 D=M=32 bf16, sigma = 0.5: forward + backward of one layer of the stack."""
+    w = inputs.CIFAR
+    q, k, v = w.qkv(layer)
+    do = w.grad_out(layer)
+    check_forward(q, k, v, BF16)
+    check_backward(q, k, v, do, BF16)
+
+
+def test_long_workload():
+    """B=1 H=16 N=65536 D=M=64 bf16, inputs scaled by 1/sqrt(D): forward + backward, all heads."""
+    w = inputs.LONG
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    check_backward(q, k, v, do, BF16)
+
+
+def test_decode_workload_sampled():
+    """Batch 256, 16 heads, D=M=64, bf16 I/O: a 512-token prefill then 512 decode steps; every step's y and
+    the final state are checked on 32 sampled heads (the oracle follows those heads only)."""
+    w = inputs.DECODE
+    steps = 512
+    B, H, D, M = w.B, w.H, w.D, w.M
+    q, k, v = w.qkv()
+    out = gpu_forward(q, k, v, BF16)
+    s, z = out["s"], out["z"]
+    rng = np.random.Generator(np.random.PCG64(77))
+    flat = np.sort(rng.choice(B * H, size=32, replace=False))
+    bi, hi = flat // H, flat % H
+    _, _, so, zo = oracle.forward_causal(q[bi, hi][None], k[bi, hi][None], v[bi, hi][None])
+    assert rowerr(host(s)[bi, hi][None], so) <= 1e-4
+    ys = torch.empty((steps, len(flat), M), device="cuda", dtype=torch.bfloat16)
+    idx_b = torch.from_numpy(bi).cuda()
+    idx_h = torch.from_numpy(hi).cuda()
+    qs, ks, vs = [], [], []
+    for t in range(steps):
+        qt, kt, vt = w.decode_step_inputs(t)
+        y = binding.decode_step(dev(qt, BF16), dev(kt, BF16), dev(vt, BF16), s, z)
+        ys[t] = y[idx_b, idx_h]
+        qs.append(qt[bi, hi])
+        ks.append(kt[bi, hi])
+        vs.append(vt[bi, hi])
+    torch.cuda.synchronize()
+    qn, kn, vn = (np.stack(a, axis=1)[None] for a in (qs, ks, vs))  # [1, 32, steps, D]
+    yo, _, sn, zn = oracle.forward_causal(qn, kn, vn, so, zo)
+    assert rowerr(host(ys).transpose(1, 0, 2)[None], yo) <= 2e-2
+    assert rowerr(host(s)[bi, hi][None], sn) <= 1e-4
+    assert rowerr(host(z)[bi, hi][None], zn, False) <= 1e-4
