@@ -1,0 +1,471 @@
+"""Benchmark of the causal linear attention library on one MI355X.
+
+Default workload (the one the headline metric is quoted on): an MNIST-shaped
+attention layer, B=16 H=8 N=784 D=M=32, float32 storage.  One step is the
+whole hot path over one batch: causal forward (phi prologue, intra-chunk
+blocks, state carry, epilogue), causal backward, and the non-causal forward
+at the same shape.  Other workloads (--workload): cifar (16 independent layers
+of B=4 H=8 N=3072 D=M=32, bf16, sigma 0.5, forward + backward each), long
+(B=1 H=16 N=65536 D=M=64, bf16, sigma 1/8, forward + backward), decode (one
+step = one la_decode_step on B=256 H=16 D=M=64 after a 512-token prefill),
+small (B=1 H=1 N=64 D=M=32 float32 causal forward).
+
+Prints one JSON line: throughput, the roofline of the dominant kernel (its
+duration measured with HIP events recorded by the library around every
+launch of that kernel inside the timed region), and the float64 oracle timed
+on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "decode", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (traffic-counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="CSV", help="write profiles/<label>_kernels.md from a "
+                    "rocprofv3 --kernel-trace --stats kernel_stats.csv")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<kernel>_<label>.json/.md from rocprofv3 --pmc counter CSVs")
+    ap.add_argument("--label", default="mnist")
+    ap.add_argument("--command", default="", help="the command that produced the CSVs (recorded in the summary)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ steps
+class Step:
+    """Inputs resident in HBM, outputs preallocated, one callable per step."""
+
+    def __init__(self, args):
+        import torch
+
+        from linear_rnn_layers_amd import binding, inputs
+
+        self.torch, self.b, self.inputs = torch, binding, inputs
+        self.args = args
+        wl = args.workload
+        self.w = {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "decode": inputs.DECODE,
+                  "small": inputs.SMALL}[wl]
+        w = self.w
+        dt = torch.float32 if w.dtype == inputs.F32 else torch.bfloat16
+        self.dt = dt
+        dev = lambda x: torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa: E731
+        B, H, N, D, M = w.B, w.H, w.N, w.D, w.M
+        code = binding.dtype_code(dt)
+        self.sets = []
+        if wl == "decode":
+            self._init_decode(dev)
+            return
+        if wl == "cifar":
+            nsets = w.layers  # one independent input set per layer
+        elif wl == "mnist":
+            nsets = 6  # rotate batches so successive steps do not hit the 256 MB last-level cache
+        else:
+            nsets = 1
+        for i in range(nsets):
+            if wl == "cifar":
+                q, k, v = w.qkv(layer=i)
+                do = w.grad_out(layer=i)
+            elif i == 0:
+                q, k, v = w.qkv()
+                do = w.grad_out()
+            else:
+                q, k, v, do = self._extra_set(i)
+            self.sets.append(tuple(dev(a) for a in (q, k, v, do)))
+        self.o = torch.empty((B, H, N, M), dtype=dt, device="cuda")
+        self.onc = torch.empty((B, H, N, M), dtype=dt, device="cuda")
+        self.den = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        self.ck = torch.empty(binding.checkpoint_size(B, H, N, D, M) // 4, dtype=torch.float32, device="cuda")
+        self.dq = torch.empty((B, H, N, D), dtype=dt, device="cuda")
+        self.dk = torch.empty((B, H, N, D), dtype=dt, device="cuda")
+        self.dv = torch.empty((B, H, N, M), dtype=dt, device="cuda")
+        self.ws_f = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, code, "cuda")
+        self.ws_b = binding.alloc_workspace(binding.LA_OP_BWD_CAUSAL, B, H, N, D, M, code, "cuda")
+        self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+        self.i = 0
+
+    def _extra_set(self, i):
+        w, inputs = self.w, self.inputs
+        base = 100_000 * i
+        sh = (w.B, w.H, w.N)
+        return (inputs.gaussian(sh + (w.D,), w.seeds[0] + base, w.sigma, w.dtype),
+                inputs.gaussian(sh + (w.D,), w.seeds[1] + base, w.sigma, w.dtype),
+                inputs.gaussian(sh + (w.M,), w.seeds[2] + base, w.sigma, w.dtype),
+                inputs.gaussian(sh + (w.M,), w.seeds[3] + base, 1.0, w.dtype))
+
+    def _init_decode(self, dev):
+        torch, b, w = self.torch, self.b, self.w
+        B, H, D, M = w.B, w.H, w.D, w.M
+        q, k, v = w.qkv()  # 512-token prefill (seeded numpy recipe)
+        out = b.forward_causal(dev(q), dev(k), dev(v), return_state=True, checkpoint=False)
+        self.S, self.Z = out["s"], out["z"]
+        pool = 4096  # distinct per-step inputs, drawn on the GPU (Philox, seed 5000000), N(0,1) in bf16
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(5_000_000)
+        self.pool_q = torch.randn((pool, B, H, D), generator=gen, device="cuda").to(self.dt)
+        self.pool_k = torch.randn((pool, B, H, D), generator=gen, device="cuda").to(self.dt)
+        self.pool_v = torch.randn((pool, B, H, M), generator=gen, device="cuda").to(self.dt)
+        self.y = torch.empty((B, H, M), dtype=self.dt, device="cuda")
+        import ctypes
+
+        lib = b.load()
+        self._call = lib.la_decode_step
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        code = b.dtype_code(self.dt)
+        qs, ks, vs = self.pool_q.stride(0) * 2, self.pool_k.stride(0) * 2, self.pool_v.stride(0) * 2
+        self._args = [(ctypes.c_void_p(self.pool_q.data_ptr() + i * qs), ctypes.c_void_p(self.pool_k.data_ptr() + i * ks),
+                       ctypes.c_void_p(self.pool_v.data_ptr() + i * vs), ctypes.c_void_p(self.S.data_ptr()),
+                       ctypes.c_void_p(self.Z.data_ptr()), ctypes.c_void_p(self.y.data_ptr()), B, H, D, M, code, stream)
+                      for i in range(pool)]
+        self.i = 0
+
+    def __call__(self):
+        wl, b = self.args.workload, self.b
+        if wl == "decode":
+            a = self._args[self.i % len(self._args)]
+            self.i += 1
+            st = self._call(*a)
+            if st != 0:
+                raise b.LAError(st, "la_decode_step")
+            return
+        if wl == "cifar":
+            for (q, k, v, do) in self.sets:
+                self._fwd_bwd(q, k, v, do)
+            return
+        q, k, v, do = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        if wl == "small":
+            b.la_forward_causal(q, k, v, self.o, self.den, ws=self.ws_f)
+            return
+        self._fwd_bwd(q, k, v, do)
+        if wl == "mnist":
+            b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n)
+
+    def _fwd_bwd(self, q, k, v, do):
+        b = self.b
+        b.la_forward_causal(q, k, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f)
+        b.la_backward_causal(q, k, v, self.o, self.den, do, self.dq, self.dk, self.dv, ckpt=self.ck, ws=self.ws_b)
+
+
+# ---------------------------------------------------- algorithmic figures
+def kernel_bytes(name, w, s):
+    """Algorithmic HBM bytes per launch: the tensors the kernel must read or write by its function
+    (per token-head: the survey's forward (2D+2M)s+4 and backward figures split over the kernels)."""
+    D, M = w.D, w.M
+    th = w.B * w.H * w.N
+    per_th = {
+        "fwd_causal": (2 * D + 2 * M) * s + 4,   # read Q, K, V; write O, den
+        "seg_state": (D + M) * s,                # read K, V
+        "fwd_noncausal": (D + M) * s,            # read Q; write O
+        "seg_rstate": (D + 2 * M) * s + 4,       # read Q, O, dO, den
+        "bwd_causal": (4 * D + 3 * M) * s,       # read Q, K, V, dO; write dQ, dK, dV
+    }
+    if name == "decode":
+        return w.B * w.H * (2 * D * M * 4 + 2 * D * 4 + (2 * D + 2 * M) * s)
+    if name in per_th:
+        return th * per_th[name]
+    return None
+
+
+def kernel_flops(name, w):
+    D, M = w.D, w.M
+    th = w.B * w.H * w.N
+    if name == "fwd_causal":
+        return th * (4 * D * M + 5 * D + M)
+    if name == "bwd_causal":
+        return th * (10 * D * M + 9 * D + 3 * M)
+    if name == "decode":
+        return w.B * w.H * (4 * D * M + 5 * D + M)
+    return None
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("la_device.h", "la_kernels.h", "la_api.hip"):
+        with open(os.path.join(ROOT, "linear_rnn_layers_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from committed counter summaries, if they match the current kernels."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------ profile summaries
+KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_seg_state<", "seg_state"),
+               ("k_scan_fwd<", "scan_fwd"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
+               ("k_fwd_fused<", "fwd_causal"))
+
+
+def kernel_tag(full_name):
+    if "k_fwd<" in full_name:
+        return "fwd_noncausal" if "false>" in full_name else "fwd_causal"
+    for key, tag in KERNEL_TAGS:
+        if key in full_name:
+            return tag
+    return full_name.split("(")[0][:60]
+
+
+def summarize_stats(args):
+    import csv
+
+    rows = list(csv.DictReader(open(args.summarize_stats)))
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"{args.label}_kernels.md")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics: {args.label} workload\n\n")
+        f.write(f"Command (run from the repository root on one MI355X):\n\n    {args.command}\n\n")
+        f.write(f"Kernel sources: sha256[:16] = {source_hash()}\n\n")
+        f.write("| kernel | template | calls | average us | min us | max us | share of GPU time |\n|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"]
+            tmpl = name.split("(")[0].replace("void ", "")
+            f.write(f"| {kernel_tag(name)} | `{tmpl}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |\n")
+    print(path)
+
+
+def _counter_means(path, counter):
+    import csv
+
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+
+
+def summarize_traffic(args):
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.summarize_traffic
+    fetch, nf = _counter_means(fetch_csv, "FETCH_SIZE")
+    write, _ = _counter_means(write_csv, "WRITE_SIZE")
+    cf, _ = _counter_means(cfetch_csv, "FETCH_SIZE")
+    cw, _ = _counter_means(cwrite_csv, "WRITE_SIZE")
+    copy_key = [k for k in cf if "copyBuffer" in k][0]
+    copy_bytes = 1024 * (1 << 20)  # bench.py --copy-only 1024: 1 GiB read and 1 GiB written per launch
+    f_read = copy_bytes / (cf[copy_key] * 1024.0)
+    f_write = copy_bytes / (cw[copy_key] * 1024.0)
+    wl = {"mnist": "MNIST", "cifar": "CIFAR", "long": "LONG", "decode": "DECODE", "small": "SMALL"}[args.label]
+    from linear_rnn_layers_amd import inputs
+
+    w = getattr(inputs, wl)
+    s = 4 if w.dtype == "f32" else 2
+    os.makedirs(PROFILES, exist_ok=True)
+    md = os.path.join(PROFILES, f"{args.label}_traffic.md")
+    with open(md, "w") as f:
+        f.write(f"# HBM traffic per launch from rocprofv3 counters: {args.label} workload\n\n")
+        f.write(f"Commands (run from the repository root on one MI355X):\n\n    {args.command}\n\n")
+        f.write(f"Kernel sources: sha256[:16] = {source_hash()}\n\n")
+        f.write(f"Calibration with a plain 1 GiB device copy (bench.py --copy-only 1024): FETCH_SIZE reads "
+                f"{cf[copy_key]:.0f} KiB and WRITE_SIZE {cw[copy_key]:.0f} KiB per copy, so bytes = "
+                f"FETCH_SIZE x 1024 x {f_read:.4f} and WRITE_SIZE x 1024 x {f_write:.4f}.\n\n")
+        f.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) | algorithmic bytes | ratio |\n")
+        f.write("|---|---|---|---|---|---|---|\n")
+        for k in sorted(fetch, key=lambda x: -fetch[x]):
+            tag = kernel_tag(k)
+            if "la::" not in k:
+                continue
+            byts = fetch[k] * 1024 * f_read + write.get(k, 0.0) * 1024 * f_write
+            alg = kernel_bytes(tag, w, s)
+            ratio = f"{byts / alg:.2f}" if alg else "-"
+            f.write(f"| {tag} | {nf[k]} | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | {byts:.4g} | "
+                    f"{alg if alg else '-'} | {ratio} |\n")
+            rec = {"kernel": tag, "workload": args.label, "source_hash": source_hash(), "bytes_per_launch": byts,
+                   "fetch_kib": fetch[k], "write_kib": write.get(k, 0.0), "read_scale": f_read,
+                   "write_scale": f_write, "algorithmic_bytes": alg, "command": args.command}
+            with open(os.path.join(PROFILES, f"traffic_{tag}_{args.label}.json"), "w") as fj:
+                json.dump(rec, fj, indent=1)
+    print(md)
+
+
+# ------------------------------------------------------------ cpu baseline
+def cpu_baseline(args, w):
+    import numpy as np
+
+    import oracle
+
+    oracle.build()
+    wl = args.workload
+    if wl == "decode":
+        nheads = 64  # bounded sample: 64 of the 4096 heads, 512 steps each
+        steps = 512
+        s = np.zeros((1, nheads, w.D, w.M))
+        z = np.zeros((1, nheads, w.D))
+        rng = np.random.Generator(np.random.PCG64(5))
+        qs = rng.standard_normal((steps, 1, nheads, w.D))
+        ks = rng.standard_normal((steps, 1, nheads, w.D))
+        vs = rng.standard_normal((steps, 1, nheads, w.M))
+        t = time.perf_counter()
+        for i in range(steps):
+            _, s, z = oracle.decode_step(qs[i], ks[i], vs[i], s, z)
+        el = time.perf_counter() - t
+        value = steps / el * nheads / (w.B * w.H)
+        return {"value": value, "unit": "decode steps/s (all B*H heads)", "cores": oracle.num_threads(),
+                "kind": "oracle", "sample": f"{steps} steps on {nheads} of {w.B * w.H} heads, scaled to all heads"}
+    # token workloads: run the oracle's passes of one step on a subset of heads until >= 10 s
+    B, H, N = w.B, w.H, w.N
+    nb = {"mnist": 4, "cifar": 1, "long": 1, "small": 1}[wl]
+    nh = {"mnist": H, "cifar": 8, "long": 2, "small": 1}[wl]
+    n = {"mnist": N, "cifar": N, "long": 16384, "small": N}[wl]
+    q, k, v = (a[:nb, :nh, :n] for a in w.qkv(n=n))
+    do = w.grad_out(n=n)[:nb, :nh, :n]
+    reps = 0
+    t = time.perf_counter()
+    while True:
+        oracle.forward_causal(q, k, v)
+        if wl != "small":
+            oracle.backward_causal(q, k, v, do)
+        if wl == "mnist":
+            oracle.forward_noncausal(q, k, v)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= 10.0 or reps >= 1000:
+            break
+    head_tokens_per_s = reps * nb * nh * n / el
+    layers = w.layers if wl == "cifar" else 1
+    value = head_tokens_per_s / (H * layers)  # model tokens/s: every token goes through H heads (x layers)
+    return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} x one step's passes on {nb}x{nh} of {B}x{H} sequences, {n} of {N} tokens"
+                      f"{', scaled to 16 layers' if wl == 'cifar' else ''}"}
+
+
+# -------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.summarize_stats:
+        summarize_stats(args)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; heads are independent, so more GPUs "
+                                   "shard B*H with no communication (see DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    if args.copy_only:
+        n = args.copy_only * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(max(1, args.steps)):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": max(1, args.steps)}))
+        return
+
+    from linear_rnn_layers_amd import binding
+
+    step = Step(args)
+    w = step.w
+    s = 4 if w.dtype == "f32" else 2
+    names = binding.kernel_names()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel durations over a few untimed steps, to find the dominant kernel
+    probe = {}
+    nprobe = 5 if args.workload != "decode" else 50
+    for name in names:
+        binding.prof_select(name)
+        for _ in range(nprobe):
+            step()
+        ms, n, _ = binding.prof_collect()
+        if n:
+            probe[name] = {"ms_per_step": ms / nprobe, "launches_per_step": n / nprobe}
+    binding.prof_select(None)
+    dominant = max(probe, key=lambda k: probe[k]["ms_per_step"])
+
+    # timed region: exactly `steps` steps between synchronisations; the library records a pair of
+    # HIP events on the launch stream around every launch of the dominant kernel
+    if not args.no_kernel_events:
+        binding.prof_select(dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms, kn, dropped = binding.prof_collect()
+    binding.prof_select(None)
+    el = t1 - t0
+    ms_per_step = el * 1e3 / args.steps
+
+    if args.workload == "decode":
+        metric, unit = "decode steps/s", "steps/s"
+        value = args.steps / el
+    else:
+        metric, unit = "causal linear-attn fwd+bwd tokens/s", "tokens/s"
+        value = w.B * w.N * args.steps / el
+
+    roof = None
+    if kn:
+        avg_s = kms / kn / 1e3
+        byts = kernel_bytes(dominant, w, s)
+        achieved = byts / avg_s / 1e9 if byts else None
+        traffic = traffic_from_profiles(dominant, args.workload)
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS if achieved else None, "traffic": traffic,
+                "algorithmic_bytes_per_launch": byts, "avg_launch_us": avg_s * 1e6, "launches": kn}
+        fl = kernel_flops(dominant, w)
+        if fl:
+            roof["useful_tflops"] = fl / avg_s / 1e12
+
+    breakdown = {k: {"us_per_step": round(v["ms_per_step"] * 1e3, 2),
+                     "launches_per_step": v["launches_per_step"]} for k, v in probe.items()}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w)
+
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M, "gpus": 1}
+    if args.workload == "mnist":
+        cfg["step"] = "causal forward + causal backward + non-causal forward"
+    elif args.workload == "cifar":
+        cfg["step"] = "16 layers x (causal forward + backward)"
+        cfg["layers"] = 16
+    elif args.workload == "long":
+        cfg["step"] = "causal forward + backward"
+    elif args.workload == "decode":
+        cfg["step"] = "one decode step of all B*H heads after a 512-token prefill"
+    else:
+        cfg["step"] = "causal forward"
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32" if s == 4 else "bf16", "data": "synthetic", "config": cfg,
+           "roofline": roof, "cpu_baseline": cpu, "kernels_us_per_step": breakdown,
+           "kernel_events_in_timed_region": not args.no_kernel_events, "events_dropped": dropped}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
