@@ -27,8 +27,9 @@ int fail(int status, const std::string& msg) {
 
 // ------------------------------------------------------------------ plan
 // The sequence of each head is cut into segments of L tokens, a multiple of
-// the 64-token chunk, so that about 1024 workgroups (four per compute unit)
-// exist even when B*H is small.  The plan depends on the sizes only.
+// 64, so that about 256 workgroups (one per compute unit) exist even when
+// B*H is small; each workgroup then pipelines its chunks.  The plan depends
+// on the sizes only.
 struct Plan {
   long BH = 0;
   int L = 0;
@@ -48,7 +49,7 @@ Plan make_plan(int B, int H, int N, int D, int M) {
     p.nseg = 0;
     return p;
   }
-  const long target = 1024;
+  const long target = 256;
   long segs = (target + p.BH - 1) / p.BH;
   if (segs > nchunks) segs = nchunks;
   if (segs < 1) segs = 1;
@@ -66,31 +67,28 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 
 // Workspace regions (bytes) per operation.
 struct WsLayout {
-  size_t agg = 0, ckpt = 0, ragg = 0, rck = 0, total = 0;
-  size_t bytes() const { return agg + ckpt + ragg + rck + total; }
+  size_t agg = 0, ckpt = 0, ragg = 0;
+  size_t bytes() const { return agg + ckpt + ragg; }
 };
 
 WsLayout ws_layout(int op, const Plan& p) {
   WsLayout w;
+  if (p.nseg == 0) return w;
   switch (op) {
     case LA_OP_FWD_CAUSAL:
-      w.agg = state_bytes(p, p.nseg);
-      w.ckpt = state_bytes(p, p.nseg + 1);
+      if (p.nseg > 1) w.agg = state_bytes(p, p.nseg);
       break;
     case LA_OP_FWD_NONCAUSAL:
       w.agg = state_bytes(p, p.nseg);
-      w.total = state_bytes(p, 1);
       break;
     case LA_OP_BWD_CAUSAL:
-      w.agg = state_bytes(p, p.nseg);
-      w.ckpt = state_bytes(p, p.nseg + 1);
-      w.ragg = state_bytes(p, p.nseg);
-      w.rck = state_bytes(p, p.nseg);
+      w.agg = state_bytes(p, p.nseg);       // checkpoint recomputation only
+      w.ckpt = state_bytes(p, p.nseg + 1);  // checkpoint recomputation only
+      if (p.nseg > 1) w.ragg = state_bytes(p, p.nseg);
       break;
     default:
       break;
   }
-  if (p.nseg == 0) w = WsLayout{};
   return w;
 }
 
@@ -206,61 +204,36 @@ int launch(const char* name, Kern kern, dim3 grid, dim3 block, hipStream_t s, Ar
 
 char* region(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
-// Segment states (agg -> ckpt) for the causal passes.
-template <typename T, int D, int M>
-int run_states(const Plan& p, int N, const void* K, const void* V, const float* S0, const float* Z0, float* agg,
-               float* ckpt, float* S_out, float* Z_out, hipStream_t s) {
-  int st = LA_OK;
-  if (p.nseg > 0) {
-    st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
-    if (st) return st;
-  }
-  return launch("scan_fwd", la::k_scan_fwd<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
-                dim3(la::NT), s, (const float*)agg, S0, Z0, ckpt, S_out, Z_out, (float*)nullptr, p.nseg);
-}
-
 template <typename T, int D, int M>
 int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
                     const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, hipStream_t s) {
-  const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
-  const bool need_states = p.nseg > 1 || ckpt != nullptr || p.nseg == 0;
-  if (!need_states) {
-    // one segment, no checkpoint: the chunk kernel starts from S0/Z0 and
-    // writes the final state itself
-    return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)p.BH), dim3(la::NT), s, (const T*)Q,
-                  (const T*)K, (const T*)V, (T*)O, den, S0, Z0, (long)D * M, 0L, (long)D, 0L, S_out, Z_out, N, p.L,
-                  1);
+  if (p.nseg == 0)
+    return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
+                  Z_out);
+  float* agg = nullptr;
+  if (p.nseg > 1) {
+    agg = reinterpret_cast<float*>(region(ws, 0));
+    const int st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                          (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+    if (st) return st;
   }
-  float* agg = reinterpret_cast<float*>(region(ws, 0));
-  float* ck = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
-  int st = run_states<T, D, M>(p, N, K, V, S0, Z0, agg, ck, S_out, Z_out, s);
-  if (st || p.nseg == 0) return st;
-  const long sv = p.SV;
   return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, (const float*)ck, (const float*)(ck + D * M),
-                (long)(p.nseg + 1) * sv, sv, (long)(p.nseg + 1) * sv, sv, (float*)nullptr, (float*)nullptr, N, p.L,
-                p.nseg);
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, (const float*)agg, S0, Z0, ckpt, S_out, Z_out, N,
+                p.L, p.nseg);
 }
 
 template <typename T, int D, int M>
 int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, int N, void* ws,
                        hipStream_t s) {
   if (p.nseg == 0) return LA_OK;
-  const WsLayout wl = ws_layout(LA_OP_FWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
-  float* tot = reinterpret_cast<float*>(region(ws, wl.agg));
   int st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                   (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
   if (st) return st;
-  st = launch("scan_fwd", la::k_scan_fwd<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
-              dim3(la::NT), s, (const float*)agg, (const float*)nullptr, (const float*)nullptr, (float*)nullptr,
-              (float*)nullptr, (float*)nullptr, tot, p.nseg);
-  if (st) return st;
-  const long sv = p.SV;
   return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, (const float*)tot,
-                (const float*)(tot + D * M), sv, 0L, sv, 0L, (float*)nullptr, (float*)nullptr, N, p.L, p.nseg);
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, (const float*)agg,
+                (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, (float*)nullptr, N,
+                p.L, p.nseg);
 }
 
 template <typename T, int D, int M>
@@ -271,26 +244,27 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   const WsLayout wl = ws_layout(LA_OP_BWD_CAUSAL, p);
   int st = LA_OK;
   const float* ck = ckpt;
-  if (!ck) {
+  if (!ck) {  // recompute the segment states: aggregates, then their scan
     float* agg = reinterpret_cast<float*>(region(ws, 0));
     float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
-    st = run_states<T, D, M>(p, N, K, V, S0, Z0, agg, ckw, nullptr, nullptr, s);
+    st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+    if (st) return st;
+    st = launch("scan_states", la::k_scan_states<D, M>,
+                dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)), dim3(la::NT), s, (const float*)agg,
+                S0, Z0, ckw, p.nseg);
     if (st) return st;
     ck = ckw;
   }
-  float* rck = nullptr;
+  float* ragg = nullptr;
   if (p.nseg > 1) {
-    float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
-    rck = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+    ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
     st = launch("seg_rstate", la::k_seg_rstate<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg);
     if (st) return st;
-    st = launch("scan_rev", la::k_scan_rev<D, M>, dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)),
-                dim3(la::NT), s, (const float*)ragg, rck, p.nseg);
-    if (st) return st;
   }
   return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s, (const T*)Q,
-                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)rck, (T*)dQ, (T*)dK, (T*)dV, N, p.L,
+                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N, p.L,
                 p.nseg);
 }
 
@@ -328,7 +302,7 @@ const char* la_status_string(int status) {
 const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
-  return "seg_state,scan_fwd,fwd_causal,fwd_noncausal,seg_rstate,scan_rev,bwd_causal,decode";
+  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,decode,scan_states,state_copy";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
@@ -365,8 +339,8 @@ int la_forward_causal(const void* Q, const void* K, const void* V, void* O, floa
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_FWD_CAUSAL, p).bytes();
-  const bool uses_ws = p.nseg != 1 || ckpt != nullptr;
-  if (uses_ws && need > 0 && (ws == nullptr || ws_bytes < need))
+  const bool uses_ws = need > 0;
+  if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
                    rng("V", V, bh * N * M * es, false), rng("S0", S0, bh * D * M * 4, false),
@@ -414,8 +388,8 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const void* 
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_BWD_CAUSAL, p).bytes();
-  const bool uses_ws = ckpt == nullptr || p.nseg > 1;
-  if (uses_ws && need > 0 && (ws == nullptr || ws_bytes < need))
+  const bool uses_ws = need > 0 && (ckpt == nullptr || p.nseg > 1);
+  if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
                    rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, false),
