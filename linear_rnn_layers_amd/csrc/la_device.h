@@ -13,6 +13,15 @@
 // k = 4g + e (e < 4), 16 + 4g + (e - 4) (e >= 4), under which the accumulators
 // of two stacked 16x16 tiles are directly a B-fragment of the next product.
 //
+// Every operand is staged token-major ([token][feature], features contiguous).
+// A contraction over features reads fragments along a row (one 16-byte or two
+// 8-byte LDS reads per plane); a contraction over tokens reads them down a
+// column with the transposing LDS read of gfx950 (ds_read_b64_tr_b16): in
+// each group of 16 lanes, lane t receives element t % 4 of the 8-byte rows
+// addressed by lanes t / 4 + 4e, e = 0..3.  So if lane a of group g addresses
+// row k(g, a / 4) at column n0 + 4 (a % 4), lane t gets X[k(g, e)][n0 + t] --
+// a fragment of column n0 + r16 with no transposed copy in LDS.
+//
 // Split precision.  A float32 operand x is staged as NP bf16 "planes"
 // x = x0 + x1 (+ x2) + residual, each plane the bf16 rounding of what the
 // previous ones leave (residual about 2^-8, 2^-16, 2^-24 of |x| for NP = 1,
@@ -21,7 +30,7 @@
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation: (1,1) is a plain bf16
 // product, (2,2) is accurate to about 2^-16 with 3 MFMAs, (3,3) to float32
 // level with 6 MFMAs -- 2.7x faster than eight v_mfma_f32_16x16x4_f32.
-// Operands that are exact in bf16 (bf16 inputs, a 0/1 mask) need one plane.
+// Operands that are exact in bf16 (bf16 inputs, 0/1 masks) need one plane.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,19 +40,33 @@ namespace la {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // bfloat16 storage (upper half of a float32)
 
 constexpr int NT = 256;  // threads per workgroup: four wavefronts
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  __bf16 h = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32)
+  __bf16 h = (__bf16)f;  // round to nearest even
   return __builtin_bit_cast(bf16_t, h);
 }
+// two floats rounded to bf16 (nearest even) in one 32-bit word, a in the low half
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float lo2f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi2f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Feature map of "Transformers are RNNs -- part 2/3" eq. 7 with elu's alpha = 1.
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// Feature map of "Transformers are RNNs -- part 2/3" eq. 7 with elu's alpha = 1:
+// x + 1 for x > 0, exp(x) otherwise, exp taken as 2^(x log2 e) on the
+// hardware exponential (relative error about |x| 2^-24 plus one ulp).
+__device__ __forceinline__ float phi(float x) {
+  return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
 // Its derivative is 1 for x > 0 and exp(x) otherwise, i.e. min(phi(x), 1).
 __device__ __forceinline__ float dphi_from_phi(float p) { return fminf(p, 1.f); }
 
@@ -54,14 +77,23 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& 
 }
 
 // ------------------------------------------------------------- splitting
-template <int NP>
-__device__ __forceinline__ void split(float x, bf16_t* out) {
-  float r = x;
+// NP planes of 2W consecutive floats, each plane packed in W 32-bit words.
+template <int NP, int W>
+__device__ __forceinline__ void split_pk(const float* x, uint32_t (*out)[W]) {
+  float r[2 * W];
+#pragma unroll
+  for (int e = 0; e < 2 * W; ++e) r[e] = x[e];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const __bf16 h = (__bf16)r;
-    out[p] = __builtin_bit_cast(bf16_t, h);
-    if (p + 1 < NP) r -= (float)h;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const uint32_t w = pk2(r[2 * i], r[2 * i + 1]);
+      out[p][i] = w;
+      if (p + 1 < NP) {
+        r[2 * i] -= lo2f(w);
+        r[2 * i + 1] -= hi2f(w);
+      }
+    }
   }
 }
 
@@ -73,17 +105,11 @@ struct Frag {
 // Fragment of 8 float32 values split into N planes.
 template <int N>
 __device__ __forceinline__ Frag<N> split8(const float* v) {
+  uint32_t u[N][4];
+  split_pk<N, 4>(v, u);
   Frag<N> f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float r = v[e];
-#pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const __bf16 h = (__bf16)r;
-      f.p[p][e] = h;
-      if (p + 1 < N) r -= (float)h;
-    }
-  }
+  for (int p = 0; p < N; ++p) f.p[p] = __builtin_bit_cast(bf16x8_t, make_uint4(u[p][0], u[p][1], u[p][2], u[p][3]));
   return f;
 }
 
@@ -92,6 +118,15 @@ template <int N>
 __device__ __forceinline__ Frag<N> acc2frag(const f32x4_t& a0, const f32x4_t& a1) {
   const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
   return split8<N>(v);
+}
+
+// The all-ones fragment (exact in bf16): as an A operand it sums a B operand
+// over k into every row of the tile; as a B operand, into every column.
+__device__ __forceinline__ Frag<1> ones_frag() {
+  Frag<1> f;
+  const __bf16 one = (__bf16)1.0f;
+  f.p[0] = bf16x8_t{one, one, one, one, one, one, one, one};
+  return f;
 }
 
 // acc += A B keeping the terms a_i b_j, i + j < max(NA, NB), smallest first.
@@ -109,57 +144,70 @@ __device__ __forceinline__ void mmaf(f32x4_t& acc, const Frag<FA>& a, const Frag
   }
 }
 
-// ---------------------------------------------------------- LDS planes
-// NP bf16 planes of a ROWS x COLS matrix; every row padded by 8 elements so
-// rows are 16-byte aligned and consecutive rows start in different banks.
-template <int NP, int ROWS, int COLS>
-struct Planes {
-  static constexpr int P = COLS + 8;
-  bf16_t v[NP][ROWS][P];
+// ------------------------------------------------------ transposed read
+__device__ __forceinline__ bf16x4_t lds_read_tr4(const bf16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4_t, r);
+}
 
-  __device__ __forceinline__ void put(int r, int c, float x) {
-    bf16_t h[NP];
-    split<NP>(x, h);
+__device__ __forceinline__ bf16x8_t cat44(const bf16x4_t& lo, const bf16x4_t& hi) {
+  return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------- LDS planes
+// NP bf16 planes of a ROWS x COLS row-major matrix; rows padded by PAD
+// elements (rows stay 16-byte aligned and consecutive rows start in
+// different banks).
+template <int NP, int ROWS, int COLS, int PAD = 8>
+struct Planes {
+  static constexpr int P = COLS + PAD;
+  static_assert(P % 8 == 0, "rows must stay 16-byte aligned");
+  alignas(16) bf16_t v[NP][ROWS][P];
+
+  // 8 (or 4) consecutive values of one row, split into the planes
+  __device__ __forceinline__ void put8(int r, int c, const float* x) {
+    uint32_t u[NP][4];
+    split_pk<NP, 4>(x, u);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) v[p][r][c] = h[p];
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<uint4*>(&v[p][r][c]) = make_uint4(u[p][0], u[p][1], u[p][2], u[p][3]);
   }
-  // E consecutive columns (E a multiple of 4) from one row
+  __device__ __forceinline__ void put4(int r, int c, const float* x) {
+    uint32_t u[NP][2];
+    split_pk<NP, 2>(x, u);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<uint2*>(&v[p][r][c]) = make_uint2(u[p][0], u[p][1]);
+  }
   template <int E>
-  __device__ __forceinline__ void putrow(int r, int c, const float* x) {
+  __device__ __forceinline__ void put(int r, int c, const float* x) {
+    static_assert(E == 4 || E == 8, "4 or 8 values");
+    if constexpr (E == 8)
+      put8(r, c, x);
+    else
+      put4(r, c, x);
+  }
+  // one value (all planes)
+  __device__ __forceinline__ void put1(int r, int c, float x) {
 #pragma unroll
-    for (int i = 0; i < E; i += 4) {
-      bf16_t h[4][NP];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split<NP>(x[i + q], h[q]);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        uint2 u;
-        u.x = (uint32_t)h[0][p] | ((uint32_t)h[1][p] << 16);
-        u.y = (uint32_t)h[2][p] | ((uint32_t)h[3][p] << 16);
-        *reinterpret_cast<uint2*>(&v[p][r][c + i]) = u;
-      }
+    for (int p = 0; p < NP; ++p) {
+      const __bf16 h = (__bf16)x;
+      v[p][r][c] = __builtin_bit_cast(bf16_t, h);
+      if (p + 1 < NP) x -= (float)h;
     }
   }
-  // value represented by the planes
-  __device__ __forceinline__ float get(int r, int c) const {
-    float s = 0.f;
-#pragma unroll
-    for (int p = NP - 1; p >= 0; --p) s += bf2f(v[p][r][c]);
-    return s;
-  }
-  // four consecutive values of one row
+  // four consecutive values of one row (sum of the planes)
   __device__ __forceinline__ void get4(int r, int c, float* o) const {
     o[0] = o[1] = o[2] = o[3] = 0.f;
 #pragma unroll
     for (int p = NP - 1; p >= 0; --p) {
       const uint2 u = *reinterpret_cast<const uint2*>(&v[p][r][c]);
-      o[0] += __uint_as_float(u.x << 16);
-      o[1] += __uint_as_float(u.x & 0xffff0000u);
-      o[2] += __uint_as_float(u.y << 16);
-      o[3] += __uint_as_float(u.y & 0xffff0000u);
+      o[0] += lo2f(u.x);
+      o[1] += hi2f(u.x);
+      o[2] += lo2f(u.y);
+      o[3] += hi2f(u.y);
     }
   }
-  // standard map along a row: v[.][row][k0 + 8g + e]
+  // row fragment, standard map: v[.][row][k0 + 8g + e]
   template <int N>
   __device__ __forceinline__ Frag<N> frag(int row, int k0, int g) const {
     static_assert(N <= NP, "not enough planes");
@@ -168,29 +216,33 @@ struct Planes {
     for (int p = 0; p < N; ++p) f.p[p] = *reinterpret_cast<const bf16x8_t*>(&v[p][row][k0 + 8 * g]);
     return f;
   }
-  // accumulator map along a row
+  // column fragment, standard map: v[.][k0 + 8g + e][n0 + r16]  (a = r16)
   template <int N>
-  __device__ __forceinline__ Frag<N> frag_acc(int row, int k0, int g) const {
+  __device__ __forceinline__ Frag<N> tfrag(int k0, int n0, int g, int a) const {
     static_assert(N <= NP, "not enough planes");
+    const int r = k0 + 8 * g + (a >> 2), c = n0 + 4 * (a & 3);
     Frag<N> f;
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(&v[p][row][k0 + 4 * g]);
-      const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(&v[p][row][k0 + 16 + 4 * g]);
-      f.p[p] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    for (int p = 0; p < N; ++p) f.p[p] = cat44(lds_read_tr4(&v[p][r][c]), lds_read_tr4(&v[p][r + 4][c]));
     return f;
   }
-  // standard map down a column: v[.][k0 + 8g + e][col]
+  // column fragment, accumulator map
   template <int N>
-  __device__ __forceinline__ Frag<N> frag_col(int col, int k0, int g) const {
+  __device__ __forceinline__ Frag<N> tfrag_acc(int k0, int n0, int g, int a) const {
     static_assert(N <= NP, "not enough planes");
+    const int r = k0 + 4 * g + (a >> 2), c = n0 + 4 * (a & 3);
     Frag<N> f;
 #pragma unroll
-    for (int p = 0; p < N; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f.p[p][e] = __builtin_bit_cast(__bf16, v[p][k0 + 8 * g + e][col]);
+    for (int p = 0; p < N; ++p) f.p[p] = cat44(lds_read_tr4(&v[p][r][c]), lds_read_tr4(&v[p][r + 16][c]));
     return f;
+  }
+  // zero columns [c0, c1) of every row and plane (cooperative, whole workgroup)
+  __device__ __forceinline__ void zero_cols(int c0, int c1) {
+    const int w = c1 - c0;
+    for (int i = threadIdx.x; i < NP * ROWS * w; i += NT) {
+      const int p = i / (ROWS * w), rem = i % (ROWS * w);
+      v[p][rem / w][c0 + rem % w] = 0;
+    }
   }
 };
 
@@ -214,7 +266,6 @@ struct IO<float> {
   __device__ static __forceinline__ void unpack(const raw& a, float* x) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   }
-  __device__ static __forceinline__ void load(const float* p, float* x) { unpack(load_raw(p), x); }
   __device__ static __forceinline__ void store4(float* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   }
@@ -228,16 +279,12 @@ struct IO<bf16_t> {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      x[2 * i] = lo2f(w[i]);
+      x[2 * i + 1] = hi2f(w[i]);
     }
   }
-  __device__ static __forceinline__ void load(const bf16_t* p, float* x) { unpack(load_raw(p), x); }
   __device__ static __forceinline__ void store4(bf16_t* p, const float* x) {
-    uint2 u;
-    u.x = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
-    u.y = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
   }
 };
 
@@ -274,6 +321,38 @@ struct RowBuf {
       float x[E];
       IO<T>::unpack(r[i], x);
       f(row, c0, x, row < nvalid);
+    }
+  }
+  // Stage values that are exact in bf16 into a one-plane matrix: bf16 input
+  // is copied as it is; float32 input is split into the planes.
+  template <int NP, int ROWS, int PC, int PAD>
+  __device__ __forceinline__ void stage_values(Planes<NP, ROWS, PC, PAD>& dst) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int v = threadIdx.x + i * NT;
+      const int row = v / PR, c0 = (v % PR) * E;
+      if constexpr (sizeof(T) == 2 && NP == 1) {
+        *reinterpret_cast<uint4*>(&dst.v[0][row][c0]) = r[i];
+      } else {
+        float x[E];
+        IO<T>::unpack(r[i], x);
+        dst.template put<E>(row, c0, x);
+      }
+    }
+  }
+  // Stage phi of the values (rows past `nvalid` are zero).
+  template <int NP, int ROWS, int PC, int PAD>
+  __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid) const {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+      const int v = threadIdx.x + i * NT;
+      const int row = v / PR, c0 = (v % PR) * E;
+      float x[E];
+      IO<T>::unpack(r[i], x);
+      const bool ok = row < nvalid;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = ok ? phi(x[e]) : 0.f;
+      dst.template put<E>(row, c0, x);
     }
   }
 };

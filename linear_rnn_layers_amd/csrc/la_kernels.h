@@ -11,14 +11,17 @@
 // tokens (a multiple of 64); one workgroup of four wavefronts owns one (head,
 // segment) and walks its chunks in order, carrying the state (S, Z) -- in the
 // backward also the reverse state (R, r) -- in registers, with the chunk's
-// operands staged once per chunk in LDS as bf16 planes (la_device.h) while
-// the next chunk's global reads are in flight.  A segment's start state is the
-// sum, in a fixed order, of the aggregates of the segments before it (after
-// it, for the reverse state), written by a separate aggregate pass: results
-// are bitwise reproducible and no workgroup waits for another.
+// operands staged once per chunk in LDS, token-major, as bf16 planes
+// (la_device.h) while the next chunk's global reads are in flight.  A
+// segment's start state is the sum, in a fixed order, of the aggregates of
+// the segments before it (after it, for the reverse state), written by a
+// separate aggregate pass: results are bitwise reproducible and no workgroup
+// waits for another.
 //
 // Inside a chunk every contraction is a 16x16 MFMA tile product; wave w owns
-// the 16 tokens 16w..16w+15 of a 64-token chunk.
+// the 16 tokens 16w..16w+15 of a 64-token chunk.  Sums over tokens of a single
+// vector (the normaliser Z, the reverse normaliser r) are MFMA products with
+// an all-ones operand, the form of eq. 14-15 on [V, 1].
 #include "la_device.h"
 
 namespace la {
@@ -35,19 +38,21 @@ template <typename T>
 struct Prec;
 template <>
 struct Prec<bf16_t> {
-  // forward: phi(Q) tok, phi(K) tok, phi(K) feat, V feat, S^T, A (accumulators)
-  static constexpr int FQ = 1, FK = 1, FKF = 2, FV = 1, FS = 1, FA = 1;
-  // backward staging
-  static constexpr int BQT = 2, BQF = 2, BKT = 2, BKF = 2, BVT = 1, BDO = 1, BG = 2, BS = 2, BR = 2;
+  // forward: phi(Q), phi(K) in A^T, phi(K) in the state update, V, S^T, A,
+  // Z (the denominator feeds the reverse-state aggregates, where errors of
+  // many tokens add up, so Z keeps two planes)
+  static constexpr int FQ = 1, FK = 1, FKF = 2, FV = 1, FS = 1, FA = 1, FZ = 2;
+  // backward staging: phi(Q), phi(K), V, dO, g, S, R
+  static constexpr int NQ = 2, NK = 2, NV = 1, NDO = 1, NG = 2, NS = 2, NR = 2;
   // backward products
   static constexpr int dS_a = 1, dS_b = 2, Bt = 1, U1_a = 2, U1_b = 1, U2 = 2, Zc = 2, dR = 2, At = 2, Wt = 1,
                        dK = 2, KR_a = 2, KR_b = 1, dV = 2, VR = 2;
 };
 template <>
 struct Prec<float> {
-  static constexpr int FQ = 2, FK = 2, FKF = 3, FV = 3, FS = 2, FA = 2;
-  static constexpr int BQT = 3, BQF = 3, BKT = 2, BKF = 3, BVT = 3, BDO = 3, BG = 2, BS = 3, BR = 2;
-  // g_i.V_j + c_i cancels where V_j = O_i, so dO.V and its product with
+  static constexpr int FQ = 2, FK = 2, FKF = 3, FV = 3, FS = 2, FA = 2, FZ = 2;
+  static constexpr int NQ = 3, NK = 3, NV = 3, NDO = 3, NG = 2, NS = 3, NR = 2;
+  // g_i.V_j - O_i.dO_i cancels where V_j = O_i, so dO.V and its product with
   // phi(Q) are taken at float32 level too (bf16 inputs make dO.V exact).
   static constexpr int dS_a = 3, dS_b = 3, Bt = 3, U1_a = 3, U1_b = 3, U2 = 3, Zc = 3, dR = 2, At = 2, Wt = 3,
                        dK = 3, KR_a = 2, KR_b = 2, dV = 2, VR = 2;
@@ -55,18 +60,46 @@ struct Prec<float> {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Backward chunk: 64 tokens, or 32 when float32 I/O with a 64-wide dimension
-// would not fit the planes in LDS.
+// Backward chunk: 64 tokens, or 32 when float32 planes of two 64-wide
+// dimensions would not fit in LDS.
 template <typename T, int D, int M>
 struct BwdChunk {
-  static constexpr int value = (sizeof(T) == 4 && (D == 64 || M == 64)) ? 32 : 64;
+  static constexpr int value = (sizeof(T) == 4 && D == 64 && M == 64) ? 32 : 64;
 };
 
-// Sum of state vectors in tile layout: lane holds S^T[16mb + 4g + r][16db + r16]
-// of tile t = w + 4k; reads S[d][m] row-major states base + p * stride, p in [p0, p1).
+// State tiles.  Tile t = w + 4k of wave w covers feature block db = t % DB
+// (the same for all of the wave's tiles, since DB divides 4) and value block
+// mb = t / DB.  Two register layouts are used:
+//   S layout:  acc[k][r] = S[16db + 4g + r][16mb + r16]
+//   S^T layout: acc[k][r] = S[16db + r16][16mb + 4g + r]
+// for a row-major D x M state S in global memory.
 template <int D, int M, int NTW>
-__device__ __forceinline__ void sum_states_tiles(f32x4_t* acc, const float* base, long stride, int p0, int p1,
-                                                 int w, int r16, int g) {
+__device__ __forceinline__ void add_S_tiles(f32x4_t* acc, const float* base, long stride, int p0, int p1, int w,
+                                            int r16, int g) {
+  constexpr int DB = D / 16;
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) {
+    const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    const float* e = base + (16 * db + 4 * g) * M + 16 * mb + r16;
+    for (int p = p0; p < p1; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[k][r] += e[(long)p * stride + r * M];
+  }
+}
+template <int D, int M, int NTW>
+__device__ __forceinline__ void store_S_tiles(float* dst, const f32x4_t* acc, int w, int r16, int g) {
+  constexpr int DB = D / 16;
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) {
+    const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    float* e = dst + (16 * db + 4 * g) * M + 16 * mb + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) e[r * M] = acc[k][r];
+  }
+}
+template <int D, int M, int NTW>
+__device__ __forceinline__ void add_ST_tiles(f32x4_t* acc, const float* base, long stride, int p0, int p1, int w,
+                                             int r16, int g) {
   constexpr int DB = D / 16;
 #pragma unroll
   for (int k = 0; k < NTW; ++k) {
@@ -78,6 +111,20 @@ __device__ __forceinline__ void sum_states_tiles(f32x4_t* acc, const float* base
     }
   }
 }
+template <int D, int M, int NTW>
+__device__ __forceinline__ void store_ST_tiles(float* dst, const f32x4_t* acc, int w, int r16, int g) {
+  constexpr int DB = D / 16;
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) {
+    const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    *reinterpret_cast<float4*>(dst + (16 * db + r16) * M + 16 * mb + 4 * g) =
+        make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
+  }
+}
+
+__device__ __forceinline__ void acc_to4(const f32x4_t& a, float* o) {
+  o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+}
 
 // ===================================================================== F1
 // Segment aggregates: agg[bh][seg] = ( sum_j phi(K_j) V_j^T  [D][M],
@@ -88,81 +135,65 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
                                                    float* __restrict__ agg, int N, int L, int nseg) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
-  constexpr int NKF = P::FKF, NVF = cmax(P::FV, 1);
-  __shared__ Planes<NKF, D, CH> kf;
-  __shared__ Planes<NVF, M, CH> vf;
-  __shared__ float zpart[4][D];
+  __shared__ Planes<P::FKF, CH, D> kt;
+  __shared__ Planes<P::FV, CH, M> vt;
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * M;
+  const Frag<1> ones = ones_frag();
 
-  f32x4_t acc[NTW];
+  f32x4_t acc[NTW], accZ = zero4();  // S layout; accZ[r] = Z[16db + 4g + r]
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = zero4();
-  float z = 0.f;
 
   RowBuf<T, CH, D> bk;
   RowBuf<T, CH, M> bv;
   bk.load(Kh + (size_t)t0 * D, min(CH, t1 - t0));
   bv.load(Vh + (size_t)t0 * M, min(CH, t1 - t0));
   for (int c0 = t0; c0 < t1; c0 += CH) {
-    const int nv = min(CH, t1 - c0);
+    const int nv = min(CH, t1 - c0), nn = min(CH, t1 - c0 - CH);
     __syncthreads();
-    bk.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-#pragma unroll
-      for (int e = 0; e < IO<T>::E; ++e) kf.put(c + e, r, ok ? phi(x[e]) : 0.f);
-    });
-    bv.for_each(nv, [&](int r, int c, const float* x, bool) {
-#pragma unroll
-      for (int e = 0; e < IO<T>::E; ++e) vf.put(c + e, r, x[e]);
-    });
-    if (c0 + CH < t1) {
-      bk.load(Kh + (size_t)(c0 + CH) * D, min(CH, t1 - c0 - CH));
-      bv.load(Vh + (size_t)(c0 + CH) * M, min(CH, t1 - c0 - CH));
+    bk.stage_phi(kt, nv);
+    bv.stage_values(vt);
+    if (nn > 0) {
+      bk.load(Kh + (size_t)(c0 + CH) * D, nn);
+      bv.load(Vh + (size_t)(c0 + CH) * M, nn);
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    for (int s = 0; s < CH / 32; ++s) {
+      const Frag<P::FKF> ka = kt.template tfrag<P::FKF>(32 * s, 16 * db, g, r16);
 #pragma unroll
-      for (int s = 0; s < CH / 32; ++s)
-        mmaf<P::FV, P::FKF>(acc[k], vf.template frag<P::FV>(16 * mb + r16, 32 * s, g),
-                            kf.template frag<P::FKF>(16 * db + r16, 32 * s, g));
-    }
-    {  // Z: each wave sums 16 of the chunk's tokens for every feature
-      for (int d = l; d < D; d += 64) {
-        float zs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) zs += kf.get(d, 16 * w + j);
-        z += zs;
+      for (int k = 0; k < NTW; ++k) {
+        const int mb = (w + 4 * k) / DB;
+        mmaf<P::FKF, P::FV>(acc[k], ka, vt.template tfrag<P::FV>(32 * s, 16 * mb, g, r16));
       }
+      if (zw) mmaf<P::FKF, 1>(accZ, ka, ones);
     }
   }
-  if (l < D) zpart[w][l] = z;
-  __syncthreads();
   float* out = agg + ((size_t)bh * nseg + seg) * SV;
-#pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    const int t = w + 4 * k, mb = t / DB, db = t % DB;
-    *reinterpret_cast<float4*>(out + (16 * db + r16) * M + 16 * mb + 4 * g) =
-        make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
-  }
-  if (tid < D) out[D * M + tid] = zpart[0][tid] + zpart[1][tid] + zpart[2][tid] + zpart[3][tid];
+  store_S_tiles<D, M, NTW>(out, acc, w, r16, g);
+  if (zw && r16 == 0)
+    *reinterpret_cast<float4*>(out + D * M + 16 * db + 4 * g) = make_float4(accZ[0], accZ[1], accZ[2], accZ[3]);
 }
 
 // ===================================================================== F3
 // Chunked forward over one segment.
 //   causal: for each chunk, A^T = phi(K) phi(Q)^T masked to j <= i (eq. 8),
-//     num^T = V^T A^T + S^T phi(Q)^T, den = rowsum(A) + phi(Q).Z, O = num/den
-//     (eq. 9-12), then S += phi(K)^T V, Z += colsum phi(K) (eq. 10-11).
-//     The start state is (S0, Z0) plus the aggregates of the earlier
-//     segments; it is written to the checkpoint, and the last segment writes
-//     the final state (checkpoint entry nseg, S_out/Z_out).
-//   non-causal: num^T = S^T phi(Q)^T with S, Z the sum of all segment
-//     aggregates (eq. 5-6).
+//     num^T = V^T A^T + S^T phi(Q)^T and den = rowsum(A) + phi(Q) Z,
+//     O = num / den (eq. 9-12), then S += phi(K)^T V, Z += phi(K)^T 1
+//     (eq. 10-11).  The start state is (S0, Z0) plus the aggregates of the
+//     earlier segments; it is written to the checkpoint, and the last segment
+//     writes the final state (checkpoint entry nseg, S_out/Z_out).
+//   non-causal: num^T = S^T phi(Q)^T, den = Z^T phi(Q)^T with S, Z the sum of
+//     all segment aggregates (eq. 5-6).
+// Z is staged as 16 identical rows, so phi(Q) Z is one more MFMA output tile
+// whose every row holds the denominators of the wave's tokens.
 template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __restrict__ K,
                                              const T* __restrict__ V, T* __restrict__ O, float* __restrict__ den_out,
@@ -172,22 +203,23 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
                                              int nseg) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
-  constexpr int KR = CAUSAL ? CH : 1, KD = CAUSAL ? D : 1, KM = CAUSAL ? M : 1;
+  constexpr int KR = CAUSAL ? CH : 1, KD = CAUSAL ? D : 8, KM = CAUSAL ? M : 8;
   __shared__ Planes<P::FQ, CH, D> qt;
-  __shared__ Planes<P::FK, KR, KD> kt;
-  __shared__ Planes<P::FKF, KD, KR> kf;
-  __shared__ Planes<P::FV, KM, KR> vf;
-  __shared__ Planes<P::FS, M, D> st;  // S^T
-  __shared__ float sZ[D];
-  __shared__ float zpart[4][D];
+  __shared__ Planes<P::FKF, KR, KD> kt;
+  __shared__ Planes<P::FV, KR, KM> vt;
+  __shared__ Planes<P::FS, M, D> st;       // S^T
+  __shared__ Planes<P::FZ, 16, D> zr;      // 16 copies of Z
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
   const T* Qh = Q + (size_t)bh * N * D;
   const T* Kh = K + (size_t)bh * N * D;
   const T* Vh = V + (size_t)bh * N * M;
   T* Oh = O + (size_t)bh * N * M;
+  const Frag<1> ones = ones_frag();
 
   RowBuf<T, CH, D> bq, bk;
   RowBuf<T, CH, M> bv;
@@ -197,62 +229,56 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
     bv.load(Vh + (size_t)t0 * M, min(CH, t1 - t0));
   }
 
-  // ---- start state
-  f32x4_t accS[NTW];
+  // ---- start state (S layout), Z for the wave's feature block
+  f32x4_t accS[NTW], accZ = zero4();
 #pragma unroll
   for (int k = 0; k < NTW; ++k) accS[k] = zero4();
   const float* aggh = agg ? agg + (size_t)bh * nseg * SV : nullptr;
   const int pend = CAUSAL ? seg : nseg;
-  if (S0) sum_states_tiles<D, M, NTW>(accS, S0 + (size_t)bh * D * M, 0, 0, 1, w, r16, g);
-  if (aggh) sum_states_tiles<D, M, NTW>(accS, aggh, SV, 0, pend, w, r16, g);
-  if (tid < D) {
-    float z = Z0 ? Z0[(size_t)bh * D + tid] : 0.f;
-    if (aggh)
-      for (int p = 0; p < pend; ++p) z += aggh[(size_t)p * SV + D * M + tid];
-    sZ[tid] = z;
+  if (S0) add_S_tiles<D, M, NTW>(accS, S0 + (size_t)bh * D * M, 0, 0, 1, w, r16, g);
+  if (aggh) add_S_tiles<D, M, NTW>(accS, aggh, SV, 0, pend, w, r16, g);
+  if (zw) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 16 * db + 4 * g + r;
+      float z = Z0 ? Z0[(size_t)bh * D + d] : 0.f;
+      if (aggh)
+        for (int p = 0; p < pend; ++p) z += aggh[(size_t)p * SV + D * M + d];
+      accZ[r] = z;
+    }
   }
-  if (CAUSAL && ckpt) {
-    float* ck = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
+  auto write_state = [&](float* dS, float* dZ) {
+    store_S_tiles<D, M, NTW>(dS, accS, w, r16, g);
+    if (zw && r16 == 0)
+      *reinterpret_cast<float4*>(dZ + 16 * db + 4 * g) = make_float4(accZ[0], accZ[1], accZ[2], accZ[3]);
+  };
+  auto stage_state = [&]() {
+    float v4[4];
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
-      *reinterpret_cast<float4*>(ck + (16 * db + r16) * M + 16 * mb + 4 * g) =
-          make_float4(accS[k][0], accS[k][1], accS[k][2], accS[k][3]);
+      acc_to4(accS[k], v4);
+      st.put4(16 * ((w + 4 * k) / DB) + r16, 16 * db + 4 * g, v4);
     }
-    if (tid < D) ck[D * M + tid] = sZ[tid];
+    if (zw) {
+      acc_to4(accZ, v4);
+      zr.put4(r16, 16 * db + 4 * g, v4);
+    }
+  };
+  if (CAUSAL && ckpt) {
+    float* ck = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
+    write_state(ck, ck + D * M);
   }
-#pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    const int t = w + 4 * k, mb = t / DB, db = t % DB;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.put(16 * mb + 4 * g + r, 16 * db + r16, accS[k][r]);
-  }
+  stage_state();
 
   for (int c0 = t0; c0 < t1; c0 += CH) {
     const int nv = min(CH, t1 - c0);
     const int nn = min(CH, t1 - c0 - CH);  // rows of the next chunk (<= 0: none)
     __syncthreads();
-    bq.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-      float p[IO<T>::E];
-#pragma unroll
-      for (int e = 0; e < IO<T>::E; ++e) p[e] = ok ? phi(x[e]) : 0.f;
-      qt.template putrow<IO<T>::E>(r, c, p);
-    });
+    bq.stage_phi(qt, nv);
     if (nn > 0) bq.load(Qh + (size_t)(c0 + CH) * D, nn);
     if constexpr (CAUSAL) {
-      bk.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-        float p[IO<T>::E];
-#pragma unroll
-        for (int e = 0; e < IO<T>::E; ++e) {
-          p[e] = ok ? phi(x[e]) : 0.f;
-          kf.put(c + e, r, p[e]);
-        }
-        kt.template putrow<IO<T>::E>(r, c, p);
-      });
-      bv.for_each(nv, [&](int r, int c, const float* x, bool) {
-#pragma unroll
-        for (int e = 0; e < IO<T>::E; ++e) vf.put(c + e, r, x[e]);
-      });
+      bk.stage_phi(kt, nv);
+      bv.stage_values(vt);
       if (nn > 0) {
         bk.load(Kh + (size_t)(c0 + CH) * D, nn);
         bv.load(Vh + (size_t)(c0 + CH) * M, nn);
@@ -265,8 +291,8 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) qf[s] = qt.template frag<P::FQ>(il, 32 * s, g);
 
-    float dp = 0.f;
     Frag<P::FA> af[2];
+    float dp = 0.f;  // row sum of the masked A, float32
     if constexpr (CAUSAL) {
       f32x4_t accA[4];
 #pragma unroll
@@ -287,16 +313,13 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p) af[p] = acc2frag<P::FA>(accA[2 * p], accA[2 * p + 1]);
+      dp = sum_over_g(dp);
     }
+    f32x4_t dn = zero4();
 #pragma unroll
-    for (int dd = 0; dd < D / 4; dd += 4) {
-      float qv[4];
-      qt.get4(il, g * (D / 4) + dd, qv);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dp += qv[q] * sZ[g * (D / 4) + dd + q];
-    }
-    dp = sum_over_g(dp);
-    const float inv = 1.f / dp;
+    for (int s = 0; s < D / 32; ++s) mmaf<P::FZ, P::FQ>(dn, zr.template frag<P::FZ>(r16, 32 * s, g), qf[s]);
+    const float den = dp + dn[0];  // every row of the Z tile holds phi(Q_i).Z, i = il
+    const float inv = 1.f / den;
     const bool row_ok = il < nv;
 
 #pragma unroll
@@ -305,7 +328,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
       if constexpr (CAUSAL) {
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-          if (2 * p <= w) mmaf<P::FV, P::FA>(acc, vf.template frag_acc<P::FV>(16 * mb + r16, 32 * p, g), af[p]);
+          if (2 * p <= w) mmaf<P::FV, P::FA>(acc, vt.template tfrag_acc<P::FV>(32 * p, 16 * mb, g, r16), af[p]);
       }
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mmaf<P::FS, P::FQ>(acc, st.template frag<P::FS>(16 * mb + r16, 32 * s, g), qf[s]);
@@ -316,49 +339,30 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
         IO<T>::store4(Oh + (size_t)(c0 + il) * M + 16 * mb + 4 * g, o);
       }
     }
-    if (den_out && g == 0 && row_ok) den_out[(size_t)bh * N + c0 + il] = dp;
+    if (den_out && g == 0 && row_ok) den_out[(size_t)bh * N + c0 + il] = den;
 
     if constexpr (CAUSAL) {
 #pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int t = w + 4 * k, mb = t / DB, db = t % DB;
+      for (int s = 0; s < CH / 32; ++s) {
+        const Frag<P::FKF> ka = kt.template tfrag<P::FKF>(32 * s, 16 * db, g, r16);
 #pragma unroll
-        for (int s = 0; s < CH / 32; ++s)
-          mmaf<P::FV, P::FKF>(accS[k], vf.template frag<P::FV>(16 * mb + r16, 32 * s, g),
-                              kf.template frag<P::FKF>(16 * db + r16, 32 * s, g));
-      }
-      for (int d = l; d < D; d += 64) {
-        float zs = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) zs += kf.get(d, 16 * w + j);
-        zpart[w][d] = zs;
+        for (int k = 0; k < NTW; ++k) {
+          const int mb = (w + 4 * k) / DB;
+          mmaf<P::FKF, P::FV>(accS[k], ka, vt.template tfrag<P::FV>(32 * s, 16 * mb, g, r16));
+        }
+        if (zw) mmaf<P::FKF, 1>(accZ, ka, ones);
       }
       __syncthreads();
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int t = w + 4 * k, mb = t / DB, db = t % DB;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.put(16 * mb + 4 * g + r, 16 * db + r16, accS[k][r]);
-      }
-      if (tid < D) sZ[tid] += zpart[0][tid] + zpart[1][tid] + zpart[2][tid] + zpart[3][tid];
+      stage_state();
     }
   }
   if constexpr (CAUSAL) {
-    if (seg == nseg - 1 && (S_out || ckpt)) {
-      __syncthreads();
-      float* ck = ckpt ? ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV : nullptr;
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int t = w + 4 * k, mb = t / DB, db = t % DB;
-        const float4 v4 = make_float4(accS[k][0], accS[k][1], accS[k][2], accS[k][3]);
-        const int off = (16 * db + r16) * M + 16 * mb + 4 * g;
-        if (S_out) *reinterpret_cast<float4*>(S_out + (size_t)bh * D * M + off) = v4;
-        if (ck) *reinterpret_cast<float4*>(ck + off) = v4;
+    if (seg == nseg - 1) {
+      if (ckpt) {
+        float* ck = ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV;
+        write_state(ck, ck + D * M);
       }
-      if (tid < D) {
-        if (Z_out) Z_out[(size_t)bh * D + tid] = sZ[tid];
-        if (ck) ck[D * M + tid] = sZ[tid];
-      }
+      if (S_out) write_state(S_out + (size_t)bh * D * M, Z_out + (size_t)bh * D);
     }
   }
 }
@@ -409,7 +413,8 @@ __global__ __launch_bounds__(NT) void k_state_copy(const float* __restrict__ S0,
 //   ( R = sum_i phi(Q_i) g_i^T [D][M],  r = sum_i c_i phi(Q_i) [D] )
 // i.e. the backward-running sums of eq. 14-15 over one segment, with the
 // upstream [g, c] of the numerator and the denominator (g_i = dO_i / den_i,
-// c_i = -(dO_i . O_i) / den_i), taken from the forward's O and den.
+// c_i = -(dO_i . O_i) / den_i), taken from the forward's O and den.  g is
+// staged with c as an extra column, so r is one more tile of R^T.
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, const T* __restrict__ O,
                                                     const float* __restrict__ den, const T* __restrict__ dO,
@@ -417,23 +422,23 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   constexpr int E = IO<T>::E, PRM = M / E;
-  __shared__ Planes<P::dR, D, CH> qf;  // phi(Q), feature-major
-  __shared__ Planes<P::dR, M, CH> gf;  // g, feature-major
-  __shared__ float sC[CH];
-  __shared__ float rpart[4][D];
+  __shared__ Planes<P::dR, CH, D> qt;       // phi(Q)
+  __shared__ Planes<P::dR, CH, M + 16> gt;  // [g | c | 0]
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
   const T* Qh = Q + (size_t)bh * N * D;
   const T* Oh = O + (size_t)bh * N * M;
   const T* dOh = dO + (size_t)bh * N * M;
   const float* denh = den + (size_t)bh * N;
+  gt.zero_cols(M + 1, M + 16);
 
-  f32x4_t acc[NTW];  // R^T tiles: [16mb + 4g + r][16db + r16]
+  f32x4_t acc[NTW], accr = zero4();  // R^T layout; accr[0] on lanes g = 0 is r[16db + r16]
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = zero4();
-  float rr = 0.f;
 
   RowBuf<T, CH, D> bq;
   RowBuf<T, CH, M> bo, bd;
@@ -444,10 +449,7 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
     const int nv = min(CH, t1 - c0);
     const int nn = min(CH, t1 - c0 - CH);
     __syncthreads();
-    bq.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) qf.put(c + e, r, ok ? phi(x[e]) : 0.f);
-    });
+    bq.stage_phi(qt, nv);
     // g and c need den (per row) and dO . O (a row reduction over PRM lanes)
 #pragma unroll
     for (int i = 0; i < RowBuf<T, CH, M>::CNT; ++i) {
@@ -456,16 +458,17 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
       float xo[E], xd[E];
       IO<T>::unpack(bo.r[i], xo);
       IO<T>::unpack(bd.r[i], xd);
-      const float dn = r < nv ? denh[c0 + r] : 1.f;
+      const float inv = r < nv ? 1.f / denh[c0 + r] : 0.f;
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) part += xd[e] * xo[e];
+      for (int e = 0; e < E; ++e) {
+        part += xd[e] * xo[e];
+        xd[e] *= inv;
+      }
 #pragma unroll
       for (int off = PRM / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-      const float inv = 1.f / dn;
-#pragma unroll
-      for (int e = 0; e < E; ++e) gf.put(c + e, r, xd[e] * inv);
-      if (c == 0) sC[r] = -part * inv;
+      gt.template put<E>(r, c, xd);
+      if (c == 0) gt.put1(r, M, -part * inv);
     }
     if (nn > 0) {
       bq.load(Qh + (size_t)(c0 + CH) * D, nn);
@@ -474,30 +477,19 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    for (int s = 0; s < CH / 32; ++s) {
+      const Frag<P::dR> qb = qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16);
 #pragma unroll
-      for (int s = 0; s < CH / 32; ++s)
-        mmaf<P::dR, P::dR>(acc[k], gf.template frag<P::dR>(16 * mb + r16, 32 * s, g),
-                           qf.template frag<P::dR>(16 * db + r16, 32 * s, g));
-    }
-    for (int d = l; d < D; d += 64) {
-      float s_ = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s_ += sC[16 * w + i] * qf.get(d, 16 * w + i);
-      rr += s_;
+      for (int k = 0; k < NTW; ++k) {
+        const int mb = (w + 4 * k) / DB;
+        mmaf<P::dR, P::dR>(acc[k], gt.template tfrag<P::dR>(32 * s, 16 * mb, g, r16), qb);
+      }
+      if (zw) mmaf<P::dR, P::dR>(accr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
     }
   }
-  if (l < D) rpart[w][l] = rr;
-  __syncthreads();
   float* out = ragg + ((size_t)bh * nseg + seg) * SV;
-#pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    const int t = w + 4 * k, mb = t / DB, db = t % DB;
-    *reinterpret_cast<float4*>(out + (16 * db + r16) * M + 16 * mb + 4 * g) =
-        make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
-  }
-  if (tid < D) out[D * M + tid] = rpart[0][tid] + rpart[1][tid] + rpart[2][tid] + rpart[3][tid];
+  store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
+  if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
 }
 
 // ===================================================================== B3
@@ -513,11 +505,11 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 //     here), dphiQ_i = (u_i - Z_i (O_i.dO_i)) / den_i, which is eq. 13's
 //     S_i g_i plus the denominator's share c_i Z_i (g_i = dO_i / den_i,
 //     c_i = -(O_i.dO_i) / den_i);
-//   dK, dV: dphiK_j = sum_{i>=j} phi(Q_i)(g_i.V_j + c_i) + R V_j + r,
-//     dV_j = sum_{i>=j} g_i (phi(Q_i).phi(K_j)) + R^T phi(K_j)
+//   dK, dV: dphiK_j = sum_{i>=j} phi(Q_i)(dO_i.V_j - O_i.dO_i) / den_i
+//     + R V_j + r, dV_j = sum_{i>=j} g_i (phi(Q_i).phi(K_j)) + R^T phi(K_j)
 //     (eq. 14-15 on [V, 1] with upstream [g, c]);
 // and the chain rule through phi.  The stored O and den are not read: the
-// recomputed den_i and O_i.dO_i are exact to float32, so g_i.V_j + c_i
+// recomputed den_i and O_i.dO_i are exact to float32, so dO_i.V_j - O_i.dO_i
 // cancels exactly where V_j = O_i even for bf16 storage.
 // With 64-token chunks wave w handles both gradients of tokens 16w..; with
 // 32-token chunks waves 0-1 produce dQ and waves 2-3 dK, dV.
@@ -531,25 +523,42 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
   constexpr int CB = BwdChunk<T, D, M>::value;
   constexpr int RB = CB / 16, NPAIR = CB / 32;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
-  __shared__ Planes<P::BQT, CB, D> qt;  // phi(Q), token-major
-  __shared__ Planes<P::BQF, D, CB> qf;  // phi(Q), feature-major
-  __shared__ Planes<P::BKT, CB, D> kt;  // phi(K), token-major
-  __shared__ Planes<P::BKF, D, CB> kf;  // phi(K), feature-major
-  __shared__ Planes<P::BVT, CB, M> vt;  // V, token-major
-  __shared__ Planes<P::BDO, CB, M> ot;  // dO, token-major
-  __shared__ Planes<P::BG, M, CB> gf;   // g = dO / den, feature-major
-  __shared__ Planes<P::BS, D, M> sp;    // S before this chunk, [d][m]
-  __shared__ Planes<P::BR, D, M> rp;    // R after this chunk, [d][m]
-  __shared__ float sZ[D], sr[D], sDen[CB], sC[CB];
-  __shared__ float zpart[4][D];
+  __shared__ Planes<P::NQ, CB, D> qt;       // phi(Q)
+  __shared__ Planes<P::NK, CB, D> kt;       // phi(K)
+  __shared__ Planes<P::NV, CB, M> vt;       // V
+  __shared__ Planes<P::NDO, CB, M> ot;      // dO
+  __shared__ Planes<P::NG, CB, M + 16> gt;  // [g | c | 0], g = dO / den
+  __shared__ Planes<P::NS, D, M> sp;        // S before this chunk, [d][m]
+  __shared__ Planes<P::NR, D, M> rp;        // R after this chunk, [d][m]
+  __shared__ alignas(16) float sZ[D];       // Z before this chunk
+  __shared__ alignas(16) float sr[D];       // r after this chunk
+  __shared__ alignas(16) float sInv[CB];    // 1 / den_i (0 past the end)
+  __shared__ alignas(16) float sOdo[CB];    // O_i . dO_i (0 past the end)
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
   const bool has_q = RB == 4 || w < 2;
   const bool has_kv = RB == 4 || w >= 2;
   const int qrb = w, kvrb = RB == 4 ? w : w - 2;
+  const Frag<1> ones = ones_frag();
+  gt.zero_cols(M + 1, M + 16);
+
+  // 0/1 masks j <= i of the query rows, under the accumulator map
+  Frag<1> onef[NPAIR];
+  {
+    const int il = 16 * qrb + r16;
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      bool on[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) on[e] = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) <= il;
+      onef[p] = mask_frag(on);
+    }
+  }
 
   const float* st_start = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
   const float* st_end = st_start + SV;
@@ -565,27 +574,32 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     bd.load(dO + offM + (size_t)c0 * M, nv);
   }
 
-  f32x4_t accS[NTW], accR[NTW];  // S^T and R^T tiles: [16mb + 4g + r][16db + r16]
+  f32x4_t accS[NTW], accR[NTW];  // S^T layout
 #pragma unroll
   for (int k = 0; k < NTW; ++k) {
     accS[k] = zero4();
     accR[k] = zero4();
   }
-  sum_states_tiles<D, M, NTW>(accS, st_end, 0, 0, 1, w, r16, g);
+  add_ST_tiles<D, M, NTW>(accS, st_end, 0, 0, 1, w, r16, g);
   const float* raggh = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
-  if (raggh) sum_states_tiles<D, M, NTW>(accR, raggh, SV, seg + 1, nseg, w, r16, g);
+  if (raggh) add_ST_tiles<D, M, NTW>(accR, raggh, SV, seg + 1, nseg, w, r16, g);
+  auto stage_R = [&]() {
+    float v4[4];
 #pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    const int t = w + 4 * k, mb = t / DB, db = t % DB;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rp.put(16 * db + r16, 16 * mb + 4 * g + r, accR[k][r]);
-  }
+    for (int k = 0; k < NTW; ++k) {
+      acc_to4(accR[k], v4);
+      rp.put4(16 * db + r16, 16 * ((w + 4 * k) / DB) + 4 * g, v4);
+    }
+  };
+  stage_R();
+  // zcur, rcur: Z and r of feature 16 db + r16 (waves w < DB)
   float zcur = 0.f, rcur = 0.f;
-  if (tid < D) {
-    zcur = st_end[D * M + tid];
+  if (zw) {
+    const int d = 16 * db + r16;
+    zcur = st_end[D * M + d];
     if (raggh)
-      for (int p = seg + 1; p < nseg; ++p) rcur += raggh[(size_t)p * SV + D * M + tid];
-    sr[tid] = rcur;
+      for (int p = seg + 1; p < nseg; ++p) rcur += raggh[(size_t)p * SV + D * M + d];
+    if (g == 0) sr[d] = rcur;
   }
 
   for (int ci = nchunk - 1; ci >= 0; --ci) {
@@ -593,30 +607,10 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     const int nv = min(CB, t1 - c0);
     // ---- stage this chunk from registers, then start reading the previous one
     __syncthreads();
-    bq.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-      float p[IO<T>::E];
-#pragma unroll
-      for (int e = 0; e < IO<T>::E; ++e) {
-        p[e] = ok ? phi(x[e]) : 0.f;
-        qf.put(c + e, r, p[e]);
-      }
-      qt.template putrow<IO<T>::E>(r, c, p);
-    });
-    bk.for_each(nv, [&](int r, int c, const float* x, bool ok) {
-      float p[IO<T>::E];
-#pragma unroll
-      for (int e = 0; e < IO<T>::E; ++e) {
-        p[e] = ok ? phi(x[e]) : 0.f;
-        kf.put(c + e, r, p[e]);
-      }
-      kt.template putrow<IO<T>::E>(r, c, p);
-    });
-    bv.for_each(nv, [&](int r, int c, const float* x, bool) { vt.template putrow<IO<T>::E>(r, c, x); });
-    bd.for_each(nv, [&](int r, int c, const float* x, bool) { ot.template putrow<IO<T>::E>(r, c, x); });
-    if (tid < CB) {  // rows past the end keep den = 1, c = 0; valid rows are set below
-      sDen[tid] = 1.f;
-      sC[tid] = 0.f;
-    }
+    bq.stage_phi(qt, nv);
+    bk.stage_phi(kt, nv);
+    bv.stage_values(vt);
+    bd.stage_values(ot);
     if (ci > 0) {
       const int p0 = c0 - CB;
       bq.load(Q + offD + (size_t)p0 * D, CB);
@@ -626,48 +620,51 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     }
     __syncthreads();
 
-    // ---- S before this chunk
+    // ---- S and Z before this chunk
+    if (ci == 0) {
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
-      if (ci == 0) {
-        const float4 a = *reinterpret_cast<const float4*>(st_start + (16 * db + r16) * M + 16 * mb + 4 * g);
-        accS[k] = f32x4_t{a.x, a.y, a.z, a.w};
-      } else {
-        f32x4_t ds = zero4();
+      for (int k = 0; k < NTW; ++k) accS[k] = zero4();
+      add_ST_tiles<D, M, NTW>(accS, st_start, 0, 0, 1, w, r16, g);
+      if (zw) zcur = st_start[D * M + 16 * db + r16];
+    } else {
+      f32x4_t ds[NTW], dz = zero4();
 #pragma unroll
-        for (int s = 0; s < CB / 32; ++s)
-          mmaf<P::dS_a, P::dS_b>(ds, vt.template frag_col<P::dS_a>(16 * mb + r16, 32 * s, g),
-                                 kf.template frag<P::dS_b>(16 * db + r16, 32 * s, g));
-        accS[k] -= ds;
+      for (int k = 0; k < NTW; ++k) ds[k] = zero4();
+#pragma unroll
+      for (int s = 0; s < CB / 32; ++s) {
+        constexpr int NKB = cmax(P::dS_b, P::Zc);
+        const Frag<NKB> kb = kt.template tfrag<NKB>(32 * s, 16 * db, g, r16);
+#pragma unroll
+        for (int k = 0; k < NTW; ++k) {
+          const int mb = (w + 4 * k) / DB;
+          mmaf<P::dS_a, P::dS_b>(ds[k], vt.template tfrag<P::dS_a>(32 * s, 16 * mb, g, r16), kb);
+        }
+        if (zw) mmaf<1, P::Zc>(dz, ones, kb);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp.put(16 * db + r16, 16 * mb + 4 * g + r, accS[k][r]);
+      for (int k = 0; k < NTW; ++k) accS[k] -= ds[k];
+      zcur -= dz[0];
     }
-    for (int d = l; d < D; d += 64) {
-      float zs = 0.f;
-      if (16 * w < CB) {
+    {
+      float v4[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) zs += kf.get(d, 16 * w + j);
+      for (int k = 0; k < NTW; ++k) {
+        acc_to4(accS[k], v4);
+        sp.put4(16 * db + r16, 16 * ((w + 4 * k) / DB) + 4 * g, v4);
       }
-      zpart[w][d] = zs;
     }
-    __syncthreads();
-    if (tid < D) {
-      zcur = ci == 0 ? st_start[D * M + tid] : zcur - (zpart[0][tid] + zpart[1][tid] + zpart[2][tid] + zpart[3][tid]);
-      sZ[tid] = zcur;
-    }
+    if (zw && g == 0) sZ[16 * db + r16] = zcur;
     __syncthreads();
 
     // ---- dQ for query rows 16 qrb + r16
     if (has_q) {
       const int ib = qrb, il = 16 * ib + r16;
+      const bool row_ok = il < nv;
       constexpr int NO = cmax(P::Bt, P::U1_b);
       Frag<NO> dof[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
       Frag<P::U2> btf[NPAIR];
-      Frag<1> onef[NPAIR];
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
         f32x4_t bt[2];
@@ -688,88 +685,81 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
           bt[h] = a;
         }
         btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
-        bool on[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) on[e] = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) <= il;
-        onef[p] = mask_frag(on);
       }
       f32x4_t U[DB], ZC[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int d0 = 0; d0 < DB; ++d0) {
         f32x4_t u = zero4(), zc = zero4();
 #pragma unroll
         for (int s = 0; s < M / 32; ++s)
-          mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * db + r16, 32 * s, g), dof[s]);
+          mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p) {
           if (2 * p <= ib) {
-            constexpr int NK = cmax(P::U2, P::Zc);
-            const Frag<NK> kfr = kf.template frag_acc<NK>(16 * db + r16, 32 * p, g);
-            mmaf<P::U2, P::U2>(u, kfr, btf[p]);
-            mmaf<P::Zc, 1>(zc, kfr, onef[p]);
+            constexpr int NKA = cmax(P::U2, P::Zc);
+            const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
+            mmaf<P::U2, P::U2>(u, kfa, btf[p]);
+            mmaf<P::Zc, 1>(zc, kfa, onef[p]);
           }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) zc[r] += sZ[16 * db + 4 * g + r];
-        U[db] = u;    // S_i dO_i
-        ZC[db] = zc;  // Z_i
+        const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
+        zc += f32x4_t{z4.x, z4.y, z4.z, z4.w};
+        U[d0] = u;    // S_i dO_i   [d][i]
+        ZC[d0] = zc;  // Z_i        [d][i]
       }
       float pu = 0.f, pz = 0.f;
       float qv[DB][4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        qt.get4(il, 16 * db + 4 * g, qv[db]);
+      for (int d0 = 0; d0 < DB; ++d0) {
+        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pu += qv[db][r] * U[db][r];
-          pz += qv[db][r] * ZC[db][r];
+          pu += qv[d0][r] * U[d0][r];
+          pz += qv[d0][r] * ZC[d0][r];
         }
       }
       pu = sum_over_g(pu);  // phi(Q_i)^T S_i dO_i = num_i . dO_i
       pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
-      const float invz = 1.f / pz;
-      const float odo = pu * invz;  // O_i . dO_i
-      if (il < nv) {
-        if (g == 0) {
-          sC[il] = -odo * invz;
-          sDen[il] = pz;
-        }
+      const float invz = row_ok ? 1.f / pz : 0.f;
+      const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
+      if (g == 0) {
+        sInv[il] = invz;
+        sOdo[il] = odo;
+      }
+      if (row_ok) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int d0 = 0; d0 < DB; ++d0) {
           float o[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (U[db][r] - ZC[db][r] * odo) * invz * dphi_from_phi(qv[db][r]);
-          IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * db + 4 * g, o);
+          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dphi_from_phi(qv[d0][r]);
+          IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
         }
       }
-      // g_i = dO_i / den_i, feature-major, for this row's quarter of the features
+      // row i of [g | c]: g_i = dO_i / den_i over this lane's quarter of the features
 #pragma unroll
       for (int mm = 0; mm < M / 4; mm += 4) {
         float dv[4];
         ot.get4(il, g * (M / 4) + mm, dv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gf.put(g * (M / 4) + mm + q, il, il < nv ? dv[q] * invz : 0.f);
+        for (int q = 0; q < 4; ++q) dv[q] *= invz;
+        gt.put4(il, g * (M / 4) + mm, dv);
       }
+      if (g == 0) gt.put1(il, M, -odo * invz);
     }
     __syncthreads();
 
-    // ---- reverse-state increment of this chunk (applied after the chunk)
-    //      R^T += g^T phi(Q),  r += sum_i c_i phi(Q_i)
+    // ---- reverse-state increment of this chunk (applied after the chunk):
+    //      R^T += g^T phi(Q), and r += phi(Q)^T c as the extra tile
+    f32x4_t dr = zero4();
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    for (int s = 0; s < CB / 32; ++s) {
+      const Frag<P::dR> qb = qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16);
 #pragma unroll
-      for (int s = 0; s < CB / 32; ++s)
-        mmaf<P::dR, P::dR>(accR[k], gf.template frag<P::dR>(16 * mb + r16, 32 * s, g),
-                           qf.template frag<P::dR>(16 * db + r16, 32 * s, g));
-    }
-    for (int d = l; d < D; d += 64) {
-      float s_ = 0.f;
-      if (16 * w < CB) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s_ += sC[16 * w + i] * qf.get(d, 16 * w + i);
+      for (int k = 0; k < NTW; ++k) {
+        const int mb = (w + 4 * k) / DB;
+        mmaf<P::dR, P::dR>(accR[k], gt.template tfrag<P::dR>(32 * s, 16 * mb, g, r16), qb);
       }
-      zpart[w][d] = s_;
+      if (zw) mmaf<P::dR, P::dR>(dr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
     }
 
     // ---- dK, dV for key rows 16 kvrb + r16
@@ -799,10 +789,12 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
 #pragma unroll
             for (int s = 0; s < M / 32; ++s)
               mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
+            const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
+            const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
+            const float ivr[4] = {iv.x, iv.y, iv.z, iv.w}, odr[4] = {od.x, od.y, od.z, od.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int i = 16 * ib + 4 * g + r;
-              b[r] = b[r] / sDen[i] + sC[i];  // g_i . V_j + c_i
+              b[r] = (b[r] - odr[r]) * ivr[r];  // (dO_i . V_j - O_i . dO_i) / den_i
               if (ib == jb && 4 * g + r < r16) {
                 a[r] = 0.f;
                 b[r] = 0.f;
@@ -817,20 +809,22 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
       }
       const bool row_ok = jl < nv;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int d0 = 0; d0 < DB; ++d0) {
         f32x4_t acc = zero4();
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(acc, qf.template frag_acc<P::dK>(16 * db + r16, 32 * p, g), wfr[p]);
+          if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(acc, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
 #pragma unroll
         for (int s = 0; s < M / 32; ++s)
-          mmaf<P::KR_a, P::KR_b>(acc, rp.template frag<P::KR_a>(16 * db + r16, 32 * s, g), vfr[s]);
+          mmaf<P::KR_a, P::KR_b>(acc, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
         if (row_ok) {
           float kv[4], o[4];
-          kt.get4(jl, 16 * db + 4 * g, kv);
+          kt.get4(jl, 16 * d0 + 4 * g, kv);
+          const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
+          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (acc[r] + sr[16 * db + 4 * g + r]) * dphi_from_phi(kv[r]);
-          IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * db + 4 * g, o);
+          for (int r = 0; r < 4; ++r) o[r] = (acc[r] + rr[r]) * dphi_from_phi(kv[r]);
+          IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
         }
       }
 #pragma unroll
@@ -838,10 +832,10 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
         f32x4_t acc = zero4();
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dV, P::dV>(acc, gf.template frag_acc<P::dV>(16 * mb + r16, 32 * p, g), afr[p]);
+          if (2 * p + 1 >= jb) mmaf<P::dV, P::dV>(acc, gt.template tfrag_acc<P::dV>(32 * p, 16 * mb, g, r16), afr[p]);
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
-          mmaf<P::VR, P::VR>(acc, rp.template frag_col<P::VR>(16 * mb + r16, 32 * s, g), kfr[s]);
+          mmaf<P::VR, P::VR>(acc, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
         if (row_ok) {
           float o[4] = {acc[0], acc[1], acc[2], acc[3]};
           IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
@@ -849,16 +843,11 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
       }
     }
     __syncthreads();
-    // ---- R for the next (earlier) chunk
-#pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int t = w + 4 * k, mb = t / DB, db = t % DB;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rp.put(16 * db + r16, 16 * mb + 4 * g + r, accR[k][r]);
-    }
-    if (tid < D) {
-      rcur += zpart[0][tid] + zpart[1][tid] + zpart[2][tid] + zpart[3][tid];
-      sr[tid] = rcur;
+    // ---- R and r for the next (earlier) chunk
+    stage_R();
+    if (zw) {
+      rcur += dr[0];
+      if (g == 0) sr[16 * db + r16] = rcur;
     }
   }
 }
