@@ -220,7 +220,7 @@ def traffic_from_profiles(kernel, workload):
 
 # ------------------------------------------------------ profile summaries
 KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_seg_state<", "seg_state"),
-               ("k_scan_fwd<", "scan_fwd"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
+               ("k_scan_states<", "scan_states"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
                ("k_fwd_fused<", "fwd_causal"))
 
 

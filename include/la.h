@@ -85,7 +85,9 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype);
  * part 2/3", section 3.3.1). */
 size_t la_checkpoint_size(int B, int H, int N, int D, int M);
 
-/* Sequence segment length (tokens) used for these sizes. */
+/* Sequence segment length (tokens) used for these sizes: the spacing of
+ * the checkpoint entries.  About 1024 segments are planned over all heads,
+ * each a whole number of 64-token chunks. */
 int la_segment_length(int B, int H, int N, int D, int M);
 
 /* Process-wide override of the segment length, in 64-token chunks (0 =

@@ -2,7 +2,9 @@
 
 One translation unit (csrc/la_api.hip, which includes the kernels) compiled
 with hipcc for gfx950 only.  Packed-FP32 instruction selection is disabled
-for all device code.
+for all device code, and MFMA results are kept in ordinary VGPRs (the
+accumulators are read by vector code after every product, which the AGPR
+form would turn into copies).
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ def hipcc() -> str:
 
 def command(out: str = LIB) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC", "-fvisibility=hidden",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-o", out, SRC]
 
 

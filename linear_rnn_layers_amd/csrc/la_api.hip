@@ -27,15 +27,22 @@ int fail(int status, const std::string& msg) {
 
 // ------------------------------------------------------------------ plan
 // The sequence of each head is cut into segments of L tokens, a multiple of
-// 64, so that about 256 workgroups (one per compute unit) exist even when
-// B*H is small; each workgroup then pipelines its chunks.  The plan depends
-// on the sizes only.
+// 64, so that about 1024 workgroups exist (four per compute unit) even when
+// B*H is small: the aggregate, forward and reverse-aggregate kernels keep
+// several workgroups resident per compute unit to hide their memory and LDS
+// latency.  Segment boundaries are the checkpoint entries.  The backward,
+// whose workgroup fills most of a compute unit's LDS, walks coarser segments
+// of kb consecutive segments (chosen at launch from its occupancy).  The
+// segment plan depends on the sizes only.
 struct Plan {
   long BH = 0;
   int L = 0;
   int nseg = 0;
   int SV = 0;  // floats per state vector: D*M + D
 };
+
+constexpr long kCUs = 256;        // compute units of one MI355X
+constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels
 
 std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
 
@@ -49,8 +56,7 @@ Plan make_plan(int B, int H, int N, int D, int M) {
     p.nseg = 0;
     return p;
   }
-  const long target = 256;
-  long segs = (target + p.BH - 1) / p.BH;
+  long segs = (kFineTarget + p.BH - 1) / p.BH;
   if (segs > nchunks) segs = nchunks;
   if (segs < 1) segs = 1;
   long cps = (nchunks + segs - 1) / segs;
@@ -59,6 +65,23 @@ Plan make_plan(int B, int H, int N, int D, int M) {
   p.L = (int)(cps * la::CH);
   p.nseg = (int)(((long)N + p.L - 1) / p.L);
   return p;
+}
+
+// The consumers of segment aggregates need prefix (or suffix) sums over
+// them.  When the aggregates are small, every consumer workgroup sums the
+// ones it needs (reading on average nseg / 2 of them, all of its threads
+// with many loads in flight); beyond about 64 KiB per workgroup a separate
+// scan kernel forms all prefix sums once.
+bool use_scan(const Plan& p) { return (size_t)p.nseg * p.SV * sizeof(float) / 2 > (64u << 10); }
+
+// Checkpoint segments per backward segment: about kCUs x (resident backward
+// workgroups per compute unit) backward workgroups in all.
+int backward_group(const Plan& p, int resident) {
+  const long target = kCUs * (resident > 0 ? resident : 1);
+  long kb = (p.BH * p.nseg + target / 2) / target;
+  if (kb < 1) kb = 1;
+  if (kb > p.nseg) kb = p.nseg;
+  return (int)kb;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,15 +94,26 @@ struct WsLayout {
   size_t bytes() const { return agg + ckpt + ragg; }
 };
 
+// fwd causal: aggregates and prefix states when there is more than one
+//   segment (the prefix states go to the caller's checkpoint when given and
+//   are only formed by the scan kernel);
+// fwd non-causal: aggregates and their scan (its last entry is the total);
+// bwd: aggregates and prefix states to recompute a missing checkpoint, and
+//   the reverse aggregates (scanned in place) when there is more than one
+//   segment.
 WsLayout ws_layout(int op, const Plan& p) {
   WsLayout w;
   if (p.nseg == 0) return w;
   switch (op) {
     case LA_OP_FWD_CAUSAL:
-      if (p.nseg > 1) w.agg = state_bytes(p, p.nseg);
+      if (p.nseg > 1) {
+        w.agg = state_bytes(p, p.nseg);
+        w.ckpt = state_bytes(p, p.nseg + 1);
+      }
       break;
     case LA_OP_FWD_NONCAUSAL:
       w.agg = state_bytes(p, p.nseg);
+      w.ckpt = state_bytes(p, p.nseg + 1);
       break;
     case LA_OP_BWD_CAUSAL:
       w.agg = state_bytes(p, p.nseg);       // checkpoint recomputation only
@@ -204,36 +238,76 @@ int launch(const char* name, Kern kern, dim3 grid, dim3 block, hipStream_t s, Ar
 
 char* region(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+dim3 scan_grid(const Plan& p) { return dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)); }
+
+template <typename T, int D, int M>
+int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, hipStream_t s) {
+  return launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+}
+
+template <int D, int M>
+int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z0, float* pref, hipStream_t s) {
+  return launch("scan_states", la::k_scan_states<D, M>, scan_grid(p), dim3(la::NT), s, agg, S0, Z0, pref, p.nseg);
+}
+
 template <typename T, int D, int M>
 int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
                     const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, hipStream_t s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
+  const float* pref = nullptr;
   float* agg = nullptr;
+  float* ckw = ckpt;  // checkpoint written by the forward itself unless the scan forms it
   if (p.nseg > 1) {
+    const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
     agg = reinterpret_cast<float*>(region(ws, 0));
-    const int st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                          (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+    int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
     if (st) return st;
+    if (use_scan(p)) {
+      float* pr = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
+      st = scan_prefix<D, M>(p, agg, S0, Z0, pr, s);
+      if (st) return st;
+      pref = pr;
+      ckw = nullptr;
+    }
   }
   return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, (const float*)agg, S0, Z0, ckpt, S_out, Z_out, N,
-                p.L, p.nseg);
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, pref, (const float*)agg, S0, Z0, ckw, S_out,
+                Z_out, N, p.L, p.nseg);
 }
 
 template <typename T, int D, int M>
 int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, int N, void* ws,
                        hipStream_t s) {
   if (p.nseg == 0) return LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_FWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
-  int st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                  (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
   if (st) return st;
+  const float* pref = nullptr;
+  if (use_scan(p)) {
+    float* pr = reinterpret_cast<float*>(region(ws, wl.agg));
+    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pr, s);
+    if (st) return st;
+    pref = pr;
+  }
   return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, (const float*)agg,
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, pref, (const float*)agg,
                 (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, (float*)nullptr, N,
                 p.L, p.nseg);
+}
+
+// backward workgroups resident per compute unit (LDS and registers)
+template <typename T, int D, int M>
+int backward_resident() {
+  static const int n = [] {
+    int r = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, la::k_bwd<T, D, M>, la::NT, 0) != hipSuccess || r < 1) r = 1;
+    return r;
+  }();
+  return n;
 }
 
 template <typename T, int D, int M>
@@ -244,28 +318,32 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   const WsLayout wl = ws_layout(LA_OP_BWD_CAUSAL, p);
   int st = LA_OK;
   const float* ck = ckpt;
-  if (!ck) {  // recompute the segment states: aggregates, then their scan
+  if (!ck) {  // recompute the checkpoint: aggregates, then their scan
     float* agg = reinterpret_cast<float*>(region(ws, 0));
     float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
-    st = launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+    st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
     if (st) return st;
-    st = launch("scan_states", la::k_scan_states<D, M>,
-                dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)), dim3(la::NT), s, (const float*)agg,
-                S0, Z0, ckw, p.nseg);
+    st = scan_prefix<D, M>(p, agg, S0, Z0, ckw, s);
     if (st) return st;
     ck = ckw;
   }
   float* ragg = nullptr;
+  const int scanned = p.nseg > 1 && use_scan(p) ? 1 : 0;
   if (p.nseg > 1) {
     ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
     st = launch("seg_rstate", la::k_seg_rstate<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg);
     if (st) return st;
+    if (scanned) {
+      st = launch("scan_rev", la::k_scan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, p.nseg);
+      if (st) return st;
+    }
   }
-  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s, (const T*)Q,
-                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N, p.L,
-                p.nseg);
+  const int kb = backward_group(p, backward_resident<T, D, M>());
+  const int nsegb = (p.nseg + kb - 1) / kb;
+  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::NT), s, (const T*)Q,
+                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N,
+                p.L * kb, nsegb, kb, p.nseg, scanned);
 }
 
 template <typename T, int D, int M>
@@ -302,7 +380,7 @@ const char* la_status_string(int status) {
 const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
-  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,decode,scan_states,state_copy";
+  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,decode,scan_states,scan_rev,state_copy";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {

@@ -195,16 +195,14 @@ struct Planes {
       if (p + 1 < NP) x -= (float)h;
     }
   }
-  // four consecutive values of one row (sum of the planes)
+  // four consecutive values of one row (sum of the planes, smallest first)
   __device__ __forceinline__ void get4(int r, int c, float* o) const {
-    o[0] = o[1] = o[2] = o[3] = 0.f;
 #pragma unroll
     for (int p = NP - 1; p >= 0; --p) {
       const uint2 u = *reinterpret_cast<const uint2*>(&v[p][r][c]);
-      o[0] += lo2f(u.x);
-      o[1] += hi2f(u.x);
-      o[2] += lo2f(u.y);
-      o[3] += hi2f(u.y);
+      const float x[4] = {lo2f(u.x), hi2f(u.x), lo2f(u.y), hi2f(u.y)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = p == NP - 1 ? x[q] : o[q] + x[q];
     }
   }
   // row fragment, standard map: v[.][row][k0 + 8g + e]
@@ -290,9 +288,11 @@ struct IO<bf16_t> {
 
 // Register buffer for one chunk (CH rows) of a [rows, COLS] tensor: the
 // 16-byte vectors this thread owns.  load() issues the global reads (rows at
-// or past `nvalid` are zero); for_each() hands them over for staging.  Each
-// wavefront owns whole rows as COLS/E consecutive lanes, so cross-lane
-// reductions over groups of COLS/E lanes inside for_each are safe.
+// or past `nvalid` are zero); the stage_* calls write them to LDS planes.
+// Each wavefront owns whole rows as COLS/E consecutive lanes, so cross-lane
+// reductions over groups of COLS/E lanes are safe.  A full chunk is read
+// from a uniform base plus this thread's fixed 32-bit byte offsets, with no
+// per-row test; only a partial chunk takes the masked path.
 template <typename T, int CH, int COLS>
 struct RowBuf {
   static constexpr int E = IO<T>::E;
@@ -301,36 +301,35 @@ struct RowBuf {
   static_assert((CH * PR) % NT == 0, "row visit must be uniform over the workgroup");
   typename IO<T>::raw r[CNT];
 
-  __device__ __forceinline__ void load(const T* base, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < CNT; ++i) {
-      const int v = threadIdx.x + i * NT;
-      const int row = v / PR, c0 = (v % PR) * E;
-      if (row < nvalid)
-        r[i] = IO<T>::load_raw(base + (size_t)row * COLS + c0);
-      else
-        r[i] = typename IO<T>::raw{};
-    }
+  __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x + i * NT) / PR; }
+  __device__ static __forceinline__ int col_of(int i) { return ((threadIdx.x + i * NT) % PR) * E; }
+  __device__ static __forceinline__ uint32_t byte_off(int i) {
+    return (uint32_t)(row_of(i) * COLS + col_of(i)) * (uint32_t)sizeof(T);
   }
-  template <typename F>
-  __device__ __forceinline__ void for_each(int nvalid, F&& f) const {
+
+  __device__ __forceinline__ void load(const T* base, int nvalid) {
+    const char* b = reinterpret_cast<const char*>(base);
+    if (nvalid >= CH) {
 #pragma unroll
-    for (int i = 0; i < CNT; ++i) {
-      const int v = threadIdx.x + i * NT;
-      const int row = v / PR, c0 = (v % PR) * E;
-      float x[E];
-      IO<T>::unpack(r[i], x);
-      f(row, c0, x, row < nvalid);
+      for (int i = 0; i < CNT; ++i) r[i] = *reinterpret_cast<const typename IO<T>::raw*>(b + byte_off(i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < CNT; ++i) {
+        if (row_of(i) < nvalid)
+          r[i] = *reinterpret_cast<const typename IO<T>::raw*>(b + byte_off(i));
+        else
+          r[i] = typename IO<T>::raw{};
+      }
     }
   }
   // Stage values that are exact in bf16 into a one-plane matrix: bf16 input
-  // is copied as it is; float32 input is split into the planes.
+  // is copied as it is; float32 input is split into the planes.  (Rows past
+  // the end were loaded as zeros.)
   template <int NP, int ROWS, int PC, int PAD>
   __device__ __forceinline__ void stage_values(Planes<NP, ROWS, PC, PAD>& dst) const {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int v = threadIdx.x + i * NT;
-      const int row = v / PR, c0 = (v % PR) * E;
+      const int row = row_of(i), c0 = col_of(i);
       if constexpr (sizeof(T) == 2 && NP == 1) {
         *reinterpret_cast<uint4*>(&dst.v[0][row][c0]) = r[i];
       } else {
@@ -340,19 +339,30 @@ struct RowBuf {
       }
     }
   }
-  // Stage phi of the values (rows past `nvalid` are zero).
-  template <int NP, int ROWS, int PC, int PAD>
-  __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid) const {
+  // Stage phi of the values (rows past `nvalid` are zero), optionally also
+  // as float32 into a [CH][F32C] array.
+  template <int NP, int ROWS, int PC, int PAD, int F32C = 0>
+  __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid, float* f32 = nullptr) const {
+    const bool full = nvalid >= CH;
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
-      const int v = threadIdx.x + i * NT;
-      const int row = v / PR, c0 = (v % PR) * E;
+      const int row = row_of(i), c0 = col_of(i);
       float x[E];
       IO<T>::unpack(r[i], x);
-      const bool ok = row < nvalid;
+      if (full) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = ok ? phi(x[e]) : 0.f;
+        for (int e = 0; e < E; ++e) x[e] = phi(x[e]);
+      } else {
+        const bool ok = row < nvalid;
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = ok ? phi(x[e]) : 0.f;
+      }
       dst.template put<E>(row, c0, x);
+      if constexpr (F32C > 0) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<float4*>(f32 + row * F32C + c0 + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+      }
     }
   }
 };

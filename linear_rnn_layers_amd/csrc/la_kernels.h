@@ -122,6 +122,36 @@ __device__ __forceinline__ void store_ST_tiles(float* dst, const f32x4_t* acc, i
   }
 }
 
+// sb[e] = init[e] + sum over p in [p0, p1), in order, of base[p * SV + e] for
+// the D*M + D floats of a state (S then Z; init from S0/Z0 or zero).  The
+// whole workgroup sums: each thread owns float4 columns and keeps a batch of
+// independent loads in flight.  The caller synchronises before reading sb.
+template <int D, int M>
+__device__ __forceinline__ void sum_states(float* sb, const float* S0, const float* Z0, const float* base, int p0,
+                                           int p1) {
+  constexpr int SV = D * M + D, BT = 8;
+  for (int e = 4 * threadIdx.x; e < SV; e += 4 * NT) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* init = e < D * M ? (S0 ? S0 + e : nullptr) : (Z0 ? Z0 + (e - D * M) : nullptr);
+    if (init) acc = *reinterpret_cast<const float4*>(init);
+    for (int p = p0; p < p1; p += BT) {
+      float4 v[BT];
+#pragma unroll
+      for (int j = 0; j < BT; ++j)
+        v[j] = p + j < p1 ? *reinterpret_cast<const float4*>(base + (size_t)(p + j) * SV + e)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < BT; ++j) {
+        acc.x += v[j].x;
+        acc.y += v[j].y;
+        acc.z += v[j].z;
+        acc.w += v[j].w;
+      }
+    }
+    *reinterpret_cast<float4*>(sb + e) = acc;
+  }
+}
+
 __device__ __forceinline__ void acc_to4(const f32x4_t& a, float* o) {
   o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
 }
@@ -151,19 +181,23 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = zero4();
 
-  RowBuf<T, CH, D> bk;
-  RowBuf<T, CH, M> bv;
-  bk.load(Kh + (size_t)t0 * D, min(CH, t1 - t0));
-  bv.load(Vh + (size_t)t0 * M, min(CH, t1 - t0));
-  for (int c0 = t0; c0 < t1; c0 += CH) {
-    const int nv = min(CH, t1 - c0), nn = min(CH, t1 - c0 - CH);
-    __syncthreads();
-    bk.stage_phi(kt, nv);
-    bv.stage_values(vt);
-    if (nn > 0) {
-      bk.load(Kh + (size_t)(c0 + CH) * D, nn);
-      bv.load(Vh + (size_t)(c0 + CH) * M, nn);
+  // two chunks of global reads in flight: the buffer of a chunk is refilled
+  // with the chunk two ahead as soon as it has been staged
+  RowBuf<T, CH, D> bk[2];
+  RowBuf<T, CH, M> bv[2];
+  auto fetch = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    if (nv > 0) {
+      k_.load(Kh + (size_t)c0 * D, nv);
+      v_.load(Vh + (size_t)c0 * M, nv);
     }
+  };
+  auto chunk = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    __syncthreads();
+    k_.stage_phi(kt, nv);
+    v_.stage_values(vt);
+    fetch(k_, v_, c0 + 2 * CH);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
@@ -175,6 +209,12 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
       }
       if (zw) mmaf<P::FKF, 1>(accZ, ka, ones);
     }
+  };
+  fetch(bk[0], bv[0], t0);
+  fetch(bk[1], bv[1], t0 + CH);
+  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
+    chunk(bk[0], bv[0], c0);
+    if (c0 + CH < t1) chunk(bk[1], bv[1], c0 + CH);
   }
   float* out = agg + ((size_t)bh * nseg + seg) * SV;
   store_S_tiles<D, M, NTW>(out, acc, w, r16, g);
@@ -187,18 +227,22 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
 //   causal: for each chunk, A^T = phi(K) phi(Q)^T masked to j <= i (eq. 8),
 //     num^T = V^T A^T + S^T phi(Q)^T and den = rowsum(A) + phi(Q) Z,
 //     O = num / den (eq. 9-12), then S += phi(K)^T V, Z += phi(K)^T 1
-//     (eq. 10-11).  The start state is (S0, Z0) plus the aggregates of the
-//     earlier segments; it is written to the checkpoint, and the last segment
-//     writes the final state (checkpoint entry nseg, S_out/Z_out).
-//   non-causal: num^T = S^T phi(Q)^T, den = Z^T phi(Q)^T with S, Z the sum of
-//     all segment aggregates (eq. 5-6).
+//     (eq. 10-11).  The start state is entry seg of the prefix states `pref`
+//     ([bh][nseg + 1][S | Z], written by k_scan_states) when given, else
+//     (S0, Z0) plus the aggregates `agg` of the earlier segments, summed in
+//     segment order here; in that case the start state goes to checkpoint
+//     entry seg and the last segment writes entry nseg.  The last segment
+//     writes the final state to S_out/Z_out.
+//   non-causal: num^T = S^T phi(Q)^T, den = Z^T phi(Q)^T with S, Z the total:
+//     entry nseg of `pref`, or the sum of all aggregates (eq. 5-6).
 // Z is staged as 16 identical rows, so phi(Q) Z is one more MFMA output tile
 // whose every row holds the denominators of the wave's tokens.
 template <typename T, int D, int M, bool CAUSAL>
 __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __restrict__ K,
                                              const T* __restrict__ V, T* __restrict__ O, float* __restrict__ den_out,
-                                             const float* __restrict__ agg, const float* __restrict__ S0,
-                                             const float* __restrict__ Z0, float* __restrict__ ckpt,
+                                             const float* __restrict__ pref, const float* __restrict__ agg,
+                                             const float* __restrict__ S0, const float* __restrict__ Z0,
+                                             float* __restrict__ ckpt,
                                              float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
                                              int nseg) {
   using P = Prec<T>;
@@ -209,6 +253,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   __shared__ Planes<P::FV, KR, KM> vt;
   __shared__ Planes<P::FS, M, D> st;       // S^T
   __shared__ Planes<P::FZ, 16, D> zr;      // 16 copies of Z
+  __shared__ alignas(16) float sbuf[SV];   // start state summed from the aggregates
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
@@ -221,30 +266,47 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   T* Oh = O + (size_t)bh * N * M;
   const Frag<1> ones = ones_frag();
 
-  RowBuf<T, CH, D> bq, bk;
-  RowBuf<T, CH, M> bv;
-  bq.load(Qh + (size_t)t0 * D, min(CH, t1 - t0));
-  if constexpr (CAUSAL) {
-    bk.load(Kh + (size_t)t0 * D, min(CH, t1 - t0));
-    bv.load(Vh + (size_t)t0 * M, min(CH, t1 - t0));
-  }
+  // two chunks of global reads in flight (see k_seg_state)
+  RowBuf<T, CH, D> bq[2], bk[2];
+  RowBuf<T, CH, M> bv[2];
+  auto fetch = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    if (nv > 0) {
+      q_.load(Qh + (size_t)c0 * D, nv);
+      if constexpr (CAUSAL) {
+        k_.load(Kh + (size_t)c0 * D, nv);
+        v_.load(Vh + (size_t)c0 * M, nv);
+      }
+    }
+  };
+  fetch(bq[0], bk[0], bv[0], t0);
+  fetch(bq[1], bk[1], bv[1], t0 + CH);
 
   // ---- start state (S layout), Z for the wave's feature block
   f32x4_t accS[NTW], accZ = zero4();
 #pragma unroll
   for (int k = 0; k < NTW; ++k) accS[k] = zero4();
-  const float* aggh = agg ? agg + (size_t)bh * nseg * SV : nullptr;
-  const int pend = CAUSAL ? seg : nseg;
-  if (S0) add_S_tiles<D, M, NTW>(accS, S0 + (size_t)bh * D * M, 0, 0, 1, w, r16, g);
-  if (aggh) add_S_tiles<D, M, NTW>(accS, aggh, SV, 0, pend, w, r16, g);
-  if (zw) {
+  if (pref) {
+    const float* st0 = pref + ((size_t)bh * (nseg + 1) + (CAUSAL ? seg : nseg)) * SV;
+    add_S_tiles<D, M, NTW>(accS, st0, 0, 0, 1, w, r16, g);
+    if (zw) {
+      const float4 z4 = *reinterpret_cast<const float4*>(st0 + D * M + 16 * db + 4 * g);
+      accZ = f32x4_t{z4.x, z4.y, z4.z, z4.w};
+    }
+  } else {
+    const int pend = agg ? (CAUSAL ? seg : nseg) : 0;
+    sum_states<D, M>(sbuf, S0 ? S0 + (size_t)bh * D * M : nullptr, Z0 ? Z0 + (size_t)bh * D : nullptr,
+                     agg ? agg + (size_t)bh * nseg * SV : nullptr, 0, pend);
+    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = 16 * db + 4 * g + r;
-      float z = Z0 ? Z0[(size_t)bh * D + d] : 0.f;
-      if (aggh)
-        for (int p = 0; p < pend; ++p) z += aggh[(size_t)p * SV + D * M + d];
-      accZ[r] = z;
+    for (int k = 0; k < NTW; ++k) {
+      const int mb = (w + 4 * k) / DB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accS[k][r] = sbuf[(16 * db + 4 * g + r) * M + 16 * mb + r16];
+    }
+    if (zw) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accZ[r] = sbuf[D * M + 16 * db + 4 * g + r];
     }
   }
   auto write_state = [&](float* dS, float* dZ) {
@@ -270,20 +332,15 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   }
   stage_state();
 
-  for (int c0 = t0; c0 < t1; c0 += CH) {
+  auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
     const int nv = min(CH, t1 - c0);
-    const int nn = min(CH, t1 - c0 - CH);  // rows of the next chunk (<= 0: none)
     __syncthreads();
-    bq.stage_phi(qt, nv);
-    if (nn > 0) bq.load(Qh + (size_t)(c0 + CH) * D, nn);
+    q_.stage_phi(qt, nv);
     if constexpr (CAUSAL) {
-      bk.stage_phi(kt, nv);
-      bv.stage_values(vt);
-      if (nn > 0) {
-        bk.load(Kh + (size_t)(c0 + CH) * D, nn);
-        bv.load(Vh + (size_t)(c0 + CH) * M, nn);
-      }
+      k_.stage_phi(kt, nv);
+      v_.stage_values(vt);
     }
+    fetch(q_, k_, v_, c0 + 2 * CH);
     __syncthreads();
 
     const int il = 16 * w + r16;
@@ -355,6 +412,10 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
       __syncthreads();
       stage_state();
     }
+  };
+  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
+    chunk(bq[0], bk[0], bv[0], c0);
+    if (c0 + CH < t1) chunk(bq[1], bk[1], bv[1], c0 + CH);
   }
   if constexpr (CAUSAL) {
     if (seg == nseg - 1) {
@@ -367,12 +428,15 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   }
 }
 
-// Checkpoint from segment aggregates (used when the backward is called without
-// the forward's checkpoint): ckpt[bh][s] = init + sum_{t<s} agg[bh][t], s = 0..nseg.
+// Prefix states from segment aggregates: pref[bh][s] = init + sum_{t<s}
+// agg[bh][t], s = 0..nseg (init = (S0, Z0) or zero), summed in segment
+// order.  One thread per state element; the aggregates are read in batches
+// so that many loads are in flight.
 template <int D, int M>
 __global__ __launch_bounds__(NT) void k_scan_states(const float* __restrict__ agg, const float* __restrict__ S0,
-                                                     const float* __restrict__ Z0, float* __restrict__ ckpt, int nseg) {
-  constexpr int SV = D * M + D;
+                                                     const float* __restrict__ Z0, float* __restrict__ pref,
+                                                     int nseg) {
+  constexpr int SV = D * M + D, BT = 16;
   const int bh = blockIdx.x;
   const int e = blockIdx.y * NT + threadIdx.x;
   if (e >= SV) return;
@@ -382,11 +446,46 @@ __global__ __launch_bounds__(NT) void k_scan_states(const float* __restrict__ ag
   } else {
     if (Z0) run = Z0[(size_t)bh * D + (e - D * M)];
   }
-  for (int s = 0; s < nseg; ++s) {
-    ckpt[((size_t)bh * (nseg + 1) + s) * SV + e] = run;
-    run += agg[((size_t)bh * nseg + s) * SV + e];
+  const float* a = agg + (size_t)bh * nseg * SV + e;
+  float* o = pref + (size_t)bh * (nseg + 1) * SV + e;
+  for (int s0 = 0; s0 < nseg; s0 += BT) {
+    float v[BT];
+#pragma unroll
+    for (int j = 0; j < BT; ++j) v[j] = s0 + j < nseg ? a[(size_t)(s0 + j) * SV] : 0.f;
+#pragma unroll
+    for (int j = 0; j < BT; ++j) {
+      if (s0 + j < nseg) {
+        o[(size_t)(s0 + j) * SV] = run;
+        run += v[j];
+      }
+    }
   }
-  ckpt[((size_t)bh * (nseg + 1) + nseg) * SV + e] = run;
+  o[(size_t)nseg * SV] = run;
+}
+
+// Suffix states of the reverse aggregates, in place: ragg[bh][s] <- sum over
+// p > s of ragg[bh][p], summed from the last segment down.
+template <int D, int M>
+__global__ __launch_bounds__(NT) void k_scan_rev(float* __restrict__ ragg, int nseg) {
+  constexpr int SV = D * M + D, BT = 16;
+  const int bh = blockIdx.x;
+  const int e = blockIdx.y * NT + threadIdx.x;
+  if (e >= SV) return;
+  float* a = ragg + (size_t)bh * nseg * SV + e;
+  float run = 0.f;
+  for (int s1 = nseg; s1 > 0; s1 -= BT) {
+    const int s0 = s1 - BT;
+    float v[BT];
+#pragma unroll
+    for (int j = 0; j < BT; ++j) v[j] = s0 + j >= 0 ? a[(size_t)(s0 + j) * SV] : 0.f;
+#pragma unroll
+    for (int j = BT - 1; j >= 0; --j) {
+      if (s0 + j >= 0) {
+        a[(size_t)(s0 + j) * SV] = run;
+        run += v[j];
+      }
+    }
+  }
 }
 
 // Final state for an empty sequence (N = 0): S_out = S0, checkpoint = [S0].
@@ -440,24 +539,28 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = zero4();
 
-  RowBuf<T, CH, D> bq;
-  RowBuf<T, CH, M> bo, bd;
-  bq.load(Qh + (size_t)t0 * D, min(CH, t1 - t0));
-  bo.load(Oh + (size_t)t0 * M, min(CH, t1 - t0));
-  bd.load(dOh + (size_t)t0 * M, min(CH, t1 - t0));
-  for (int c0 = t0; c0 < t1; c0 += CH) {
+  // two chunks of global reads in flight (see k_seg_state)
+  RowBuf<T, CH, D> bq[2];
+  RowBuf<T, CH, M> bo[2], bd[2];
+  auto fetch = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& o_, RowBuf<T, CH, M>& d_, int c0) {
     const int nv = min(CH, t1 - c0);
-    const int nn = min(CH, t1 - c0 - CH);
+    if (nv > 0) {
+      q_.load(Qh + (size_t)c0 * D, nv);
+      o_.load(Oh + (size_t)c0 * M, nv);
+      d_.load(dOh + (size_t)c0 * M, nv);
+    }
+  };
+  auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& o_, RowBuf<T, CH, M>& d_, int c0) {
+    const int nv = min(CH, t1 - c0);
     __syncthreads();
-    bq.stage_phi(qt, nv);
+    q_.stage_phi(qt, nv);
     // g and c need den (per row) and dO . O (a row reduction over PRM lanes)
 #pragma unroll
     for (int i = 0; i < RowBuf<T, CH, M>::CNT; ++i) {
-      const int v = tid + i * NT;
-      const int r = v / PRM, c = (v % PRM) * E;
+      const int r = RowBuf<T, CH, M>::row_of(i), c = RowBuf<T, CH, M>::col_of(i);
       float xo[E], xd[E];
-      IO<T>::unpack(bo.r[i], xo);
-      IO<T>::unpack(bd.r[i], xd);
+      IO<T>::unpack(o_.r[i], xo);
+      IO<T>::unpack(d_.r[i], xd);
       const float inv = r < nv ? 1.f / denh[c0 + r] : 0.f;
       float part = 0.f;
 #pragma unroll
@@ -470,11 +573,7 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
       gt.template put<E>(r, c, xd);
       if (c == 0) gt.put1(r, M, -part * inv);
     }
-    if (nn > 0) {
-      bq.load(Qh + (size_t)(c0 + CH) * D, nn);
-      bo.load(Oh + (size_t)(c0 + CH) * M, nn);
-      bd.load(dOh + (size_t)(c0 + CH) * M, nn);
-    }
+    fetch(q_, o_, d_, c0 + 2 * CH);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
@@ -486,6 +585,12 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
       }
       if (zw) mmaf<P::dR, P::dR>(accr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
     }
+  };
+  fetch(bq[0], bo[0], bd[0], t0);
+  fetch(bq[1], bo[1], bd[1], t0 + CH);
+  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
+    chunk(bq[0], bo[0], bd[0], c0);
+    if (c0 + CH < t1) chunk(bq[1], bo[1], bd[1], c0 + CH);
   }
   float* out = ragg + ((size_t)bh * nseg + seg) * SV;
   store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
@@ -493,12 +598,16 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 }
 
 // ===================================================================== B3
-// Backward over one segment, chunks in reverse order.  Registers carry
+// Backward over one segment, chunks in reverse order.  A backward segment is
+// kb consecutive segments of the checkpoint ([bh][nseg + 1] states), so its
+// start and end states are checkpoint entries sb kb and min((sb+1) kb, nseg).
+// Registers carry
 //   S (forward sum of phi(K) V^T, eq. 13), walked backwards from the
 //     segment's end state by removing each chunk's contribution (the first
 //     chunk restarts from the segment's start state), and
-//   R (backward sum of phi(Q) g^T, eq. 14-15) from the sum of the later
-//     segments' aggregates.
+//   R (backward sum of phi(Q) g^T, eq. 14-15) from the reverse aggregates
+//     of all later checkpoint segments: entry f1 - 1 of `ragg` when it holds
+//     suffix sums (k_scan_rev, scanned = 1), else their sum in segment order.
 // Per chunk, the waves produce
 //   dQ: with u_i = S_i dO_i, Z_i the inclusive normaliser, den_i =
 //     phi(Q_i).Z_i and O_i.dO_i = phi(Q_i).u_i / den_i (both recomputed
@@ -518,7 +627,7 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
                                              const T* __restrict__ V, const T* __restrict__ dO,
                                              const float* __restrict__ ckpt, const float* __restrict__ ragg,
                                              T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, int N, int L,
-                                             int nseg) {
+                                             int nsegb, int kb, int nseg, int scanned) {
   using P = Prec<T>;
   constexpr int CB = BwdChunk<T, D, M>::value;
   constexpr int RB = CB / 16, NPAIR = CB / 32;
@@ -530,13 +639,18 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
   __shared__ Planes<P::NG, CB, M + 16> gt;  // [g | c | 0], g = dO / den
   __shared__ Planes<P::NS, D, M> sp;        // S before this chunk, [d][m]
   __shared__ Planes<P::NR, D, M> rp;        // R after this chunk, [d][m]
+  // phi(Q), phi(K) as float32 for the elementwise terms; rows padded by 4 so
+  // the 16 rows a fragment reads start in different banks
+  __shared__ alignas(16) float q32[CB][D + 4];
+  __shared__ alignas(16) float k32[CB][D + 4];
   __shared__ alignas(16) float sZ[D];       // Z before this chunk
   __shared__ alignas(16) float sr[D];       // r after this chunk
   __shared__ alignas(16) float sInv[CB];    // 1 / den_i (0 past the end)
   __shared__ alignas(16) float sOdo[CB];    // O_i . dO_i (0 past the end)
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
-  const int t0 = seg * L, t1 = min(N, t0 + L);
+  const int sb = blockIdx.x % nsegb, bh = blockIdx.x / nsegb;
+  const int t0 = sb * L, t1 = min(N, t0 + L);
+  const int f0 = sb * kb, f1 = min(f0 + kb, nseg);  // checkpoint entries of the segment's ends
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
   const bool zw = w < DB;
@@ -560,8 +674,11 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     }
   }
 
-  const float* st_start = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
-  const float* st_end = st_start + SV;
+  const float* st_start = ckpt + ((size_t)bh * (nseg + 1) + f0) * SV;
+  const float* st_end = ckpt + ((size_t)bh * (nseg + 1) + f1) * SV;
+  // reverse aggregates to add: entries [r0, r1) of this head
+  const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
+  const int r0 = scanned ? f1 - 1 : f1, r1 = scanned ? f1 : nseg;
 
   const int nchunk = (t1 - t0 + CB - 1) / CB;
   RowBuf<T, CB, D> bq, bk;
@@ -581,8 +698,21 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     accR[k] = zero4();
   }
   add_ST_tiles<D, M, NTW>(accS, st_end, 0, 0, 1, w, r16, g);
-  const float* raggh = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
-  if (raggh) add_ST_tiles<D, M, NTW>(accR, raggh, SV, seg + 1, nseg, w, r16, g);
+  float rsum = 0.f;  // r of feature 16 db + r16
+  if (rg) {
+    static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
+    float* sb = reinterpret_cast<float*>(&rp.v[0][0][0]);
+    sum_states<D, M>(sb, nullptr, nullptr, rg, r0, r1);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+      const int mb = (w + 4 * k) / DB;
+      const float4 a = *reinterpret_cast<const float4*>(sb + (16 * db + r16) * M + 16 * mb + 4 * g);
+      accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
+    }
+    if (zw) rsum = sb[D * M + 16 * db + r16];
+    __syncthreads();
+  }
   auto stage_R = [&]() {
     float v4[4];
 #pragma unroll
@@ -597,8 +727,7 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
   if (zw) {
     const int d = 16 * db + r16;
     zcur = st_end[D * M + d];
-    if (raggh)
-      for (int p = seg + 1; p < nseg; ++p) rcur += raggh[(size_t)p * SV + D * M + d];
+    rcur = rsum;
     if (g == 0) sr[d] = rcur;
   }
 
@@ -607,8 +736,8 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     const int nv = min(CB, t1 - c0);
     // ---- stage this chunk from registers, then start reading the previous one
     __syncthreads();
-    bq.stage_phi(qt, nv);
-    bk.stage_phi(kt, nv);
+    bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0]);
+    bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0]);
     bv.stage_values(vt);
     bd.stage_values(ot);
     if (ci > 0) {
@@ -711,7 +840,8 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
       float qv[DB][4];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
+        qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pu += qv[d0][r] * U[d0][r];
@@ -818,8 +948,9 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
         for (int s = 0; s < M / 32; ++s)
           mmaf<P::KR_a, P::KR_b>(acc, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
         if (row_ok) {
-          float kv[4], o[4];
-          kt.get4(jl, 16 * d0 + 4 * g, kv);
+          float o[4];
+          const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
+          const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
           const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
           const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll

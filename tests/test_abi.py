@@ -123,10 +123,10 @@ def test_decode_validation(lib):
 
 
 def _plan(B, H, N):
-    """The segment plan, restated: about 256 workgroups, segments of whole 64-token chunks."""
+    """The segment plan, restated: about 1024 segments over all heads, each of whole 64-token chunks."""
     bh = B * H
     nch = -(-N // 64)
-    segs = max(1, min(nch, -(-256 // bh)))
+    segs = max(1, min(nch, -(-1024 // bh)))
     L = -(-nch // segs) * 64
     return L, -(-N // L)
 
@@ -141,9 +141,10 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     # linear-memory bound: the checkpoint never exceeds B*H*N*max(D,M) floats by more than one state per head
     assert lib.la_checkpoint_size(B, H, N, D, M) <= 4 * B * H * (N * max(D, M) + 2 * sv)
     assert lib.la_workspace_size(3, B, H, N, D, M, 1) == 0
-    # forward: segment aggregates when there is more than one segment
-    assert lib.la_workspace_size(0, B, H, N, D, M, 0) == (0 if nseg == 1 else _al(B * H * nseg * sv * 4))
-    assert lib.la_workspace_size(1, B, H, N, D, M, 0) == _al(B * H * nseg * sv * 4)
+    # forward: segment aggregates and their prefix scan when there is more than one segment
+    agg, pref = _al(B * H * nseg * sv * 4), _al(B * H * (nseg + 1) * sv * 4)
+    assert lib.la_workspace_size(0, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref)
+    assert lib.la_workspace_size(1, B, H, N, D, M, 0) == agg + pref
     # backward: room to recompute the checkpoint, plus reverse aggregates
     bwd = _al(B * H * nseg * sv * 4) + _al(B * H * (nseg + 1) * sv * 4) + (0 if nseg == 1 else _al(B * H * nseg * sv * 4))
     assert lib.la_workspace_size(2, B, H, N, D, M, 0) == bwd
