@@ -304,7 +304,10 @@ template <typename T, int D, int M>
 int backward_resident() {
   static const int n = [] {
     int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, la::k_bwd<T, D, M>, la::NT, 0) != hipSuccess || r < 1) r = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, la::k_bwd<T, D, M>, la::BwdShape<T, D, M>::NTH, 0) !=
+            hipSuccess ||
+        r < 1)
+      r = 1;
     return r;
   }();
   return n;
@@ -341,8 +344,8 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   }
   const int kb = backward_group(p, backward_resident<T, D, M>());
   const int nsegb = (p.nseg + kb - 1) / kb;
-  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::NT), s, (const T*)Q,
-                (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N,
+  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::BwdShape<T, D, M>::NTH), s,
+                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N,
                 p.L * kb, nsegb, kb, p.nseg, scanned);
 }
 

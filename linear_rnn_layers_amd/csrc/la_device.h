@@ -234,10 +234,10 @@ struct Planes {
     for (int p = 0; p < N; ++p) f.p[p] = cat44(lds_read_tr4(&v[p][r][c]), lds_read_tr4(&v[p][r + 16][c]));
     return f;
   }
-  // zero columns [c0, c1) of every row and plane (cooperative, whole workgroup)
-  __device__ __forceinline__ void zero_cols(int c0, int c1) {
+  // zero columns [c0, c1) of every row and plane (cooperative: nth threads)
+  __device__ __forceinline__ void zero_cols(int c0, int c1, int nth = NT) {
     const int w = c1 - c0;
-    for (int i = threadIdx.x; i < NP * ROWS * w; i += NT) {
+    for (int i = threadIdx.x; i < NP * ROWS * w; i += nth) {
       const int p = i / (ROWS * w), rem = i % (ROWS * w);
       v[p][rem / w][c0 + rem % w] = 0;
     }
@@ -293,21 +293,26 @@ struct IO<bf16_t> {
 // reductions over groups of COLS/E lanes are safe.  A full chunk is read
 // from a uniform base plus this thread's fixed 32-bit byte offsets, with no
 // per-row test; only a partial chunk takes the masked path.
-template <typename T, int CH, int COLS>
+template <typename T, int CH, int COLS, int NTH = NT>
 struct RowBuf {
   static constexpr int E = IO<T>::E;
-  static constexpr int PR = COLS / E;       // vectors per row
-  static constexpr int CNT = CH * PR / NT;  // vectors per thread
-  static_assert((CH * PR) % NT == 0, "row visit must be uniform over the workgroup");
+  static constexpr int PR = COLS / E;                  // vectors per row
+  static constexpr int VEC = CH * PR;                  // vectors per chunk
+  static constexpr int CNT = (VEC + NTH - 1) / NTH;    // vectors per thread
+  static_assert(VEC % NTH == 0 || (VEC < NTH && VEC % 64 == 0),
+                "row visit must be uniform over each wavefront");
   typename IO<T>::raw r[CNT];
 
-  __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x + i * NT) / PR; }
-  __device__ static __forceinline__ int col_of(int i) { return ((threadIdx.x + i * NT) % PR) * E; }
+  // threads past the chunk's vectors (only when VEC < NTH: whole wavefronts) hold nothing
+  __device__ static __forceinline__ bool owns() { return VEC >= NTH || (int)threadIdx.x < VEC; }
+  __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x + i * NTH) / PR; }
+  __device__ static __forceinline__ int col_of(int i) { return ((threadIdx.x + i * NTH) % PR) * E; }
   __device__ static __forceinline__ uint32_t byte_off(int i) {
     return (uint32_t)(row_of(i) * COLS + col_of(i)) * (uint32_t)sizeof(T);
   }
 
   __device__ __forceinline__ void load(const T* base, int nvalid) {
+    if (!owns()) return;
     const char* b = reinterpret_cast<const char*>(base);
     if (nvalid >= CH) {
 #pragma unroll
@@ -327,6 +332,7 @@ struct RowBuf {
   // the end were loaded as zeros.)
   template <int NP, int ROWS, int PC, int PAD>
   __device__ __forceinline__ void stage_values(Planes<NP, ROWS, PC, PAD>& dst) const {
+    if (!owns()) return;
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int row = row_of(i), c0 = col_of(i);
@@ -343,6 +349,7 @@ struct RowBuf {
   // as float32 into a [CH][F32C] array.
   template <int NP, int ROWS, int PC, int PAD, int F32C = 0>
   __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid, float* f32 = nullptr) const {
+    if (!owns()) return;
     const bool full = nvalid >= CH;
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {

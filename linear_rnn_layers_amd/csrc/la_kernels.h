@@ -126,11 +126,11 @@ __device__ __forceinline__ void store_ST_tiles(float* dst, const f32x4_t* acc, i
 // the D*M + D floats of a state (S then Z; init from S0/Z0 or zero).  The
 // whole workgroup sums: each thread owns float4 columns and keeps a batch of
 // independent loads in flight.  The caller synchronises before reading sb.
-template <int D, int M>
+template <int D, int M, int NTH = NT>
 __device__ __forceinline__ void sum_states(float* sb, const float* S0, const float* Z0, const float* base, int p0,
                                            int p1) {
   constexpr int SV = D * M + D, BT = 8;
-  for (int e = 4 * threadIdx.x; e < SV; e += 4 * NT) {
+  for (int e = 4 * threadIdx.x; e < SV; e += 4 * NTH) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const float* init = e < D * M ? (S0 ? S0 + e : nullptr) : (Z0 ? Z0 + (e - D * M) : nullptr);
     if (init) acc = *reinterpret_cast<const float4*>(init);
@@ -601,14 +601,8 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // Backward over one segment, chunks in reverse order.  A backward segment is
 // kb consecutive segments of the checkpoint ([bh][nseg + 1] states), so its
 // start and end states are checkpoint entries sb kb and min((sb+1) kb, nseg).
-// Registers carry
-//   S (forward sum of phi(K) V^T, eq. 13), walked backwards from the
-//     segment's end state by removing each chunk's contribution (the first
-//     chunk restarts from the segment's start state), and
-//   R (backward sum of phi(Q) g^T, eq. 14-15) from the reverse aggregates
-//     of all later checkpoint segments: entry f1 - 1 of `ragg` when it holds
-//     suffix sums (k_scan_rev, scanned = 1), else their sum in segment order.
-// Per chunk, the waves produce
+//
+// Per chunk the gradients are
 //   dQ: with u_i = S_i dO_i, Z_i the inclusive normaliser, den_i =
 //     phi(Q_i).Z_i and O_i.dO_i = phi(Q_i).u_i / den_i (both recomputed
 //     here), dphiQ_i = (u_i - Z_i (O_i.dO_i)) / den_i, which is eq. 13's
@@ -620,18 +614,44 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // and the chain rule through phi.  The stored O and den are not read: the
 // recomputed den_i and O_i.dO_i are exact to float32, so dO_i.V_j - O_i.dO_i
 // cancels exactly where V_j = O_i even for bf16 storage.
-// With 64-token chunks wave w handles both gradients of tokens 16w..; with
-// 32-token chunks waves 0-1 produce dQ and waves 2-3 dK, dV.
+//
+// Two roles of RB = CB / 16 wavefronts each, one wavefront of each role per
+// SIMD for 64-token chunks, so that each SIMD interleaves two instruction
+// streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
+// reverse state R (backward sum of phi(Q) g^T, eq. 14-15, started from the
+// reverse aggregates of all later checkpoint segments: entry f1 - 1 of `ragg`
+// when it holds suffix sums (scanned = 1), else their sum in segment order).
+// Key wavefront k owns key rows 16k.. and the tiles of S (forward sum of
+// phi(K) V^T, eq. 13), walked backwards from the segment's end state by
+// removing each chunk's contribution (the first chunk restarts from the start
+// state).  Phases of a chunk, separated by barriers:
+//   stage   all: phi(Q), phi(K), V, dO to LDS; next chunk's reads issued
+//   A  key: S, Z before the chunk           query: V_j.dO_i tiles
+//   B  key: A_ij, dO_i.V_j                  query: dQ, g, c, 1/den
+//   C  key: dK, dV (intra-chunk terms and the later chunks' R V_j, R^T phi(K_j))
+//      query: R, r += this chunk (staged for the next chunk after the key
+//      wavefronts' last read of them: R, r are read in phase C only, and
+//      written after the barrier that ends it -- see below)
 template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __restrict__ K,
-                                             const T* __restrict__ V, const T* __restrict__ dO,
-                                             const float* __restrict__ ckpt, const float* __restrict__ ragg,
-                                             T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV, int N, int L,
-                                             int nsegb, int kb, int nseg, int scanned) {
+struct BwdShape {
+  static constexpr int CB = BwdChunk<T, D, M>::value;
+  static constexpr int RB = CB / 16;  // row blocks per chunk
+  static constexpr int NW = 2 * RB;   // wavefronts: RB per role
+  static constexpr int NTH = 64 * NW;
+};
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ ckpt, const float* __restrict__ ragg, T* __restrict__ dQ, T* __restrict__ dK,
+    T* __restrict__ dV, int N, int L, int nsegb, int kb, int nseg, int scanned) {
   using P = Prec<T>;
-  constexpr int CB = BwdChunk<T, D, M>::value;
-  constexpr int RB = CB / 16, NPAIR = CB / 32;
-  constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
+  using BS = BwdShape<T, D, M>;
+  constexpr int CB = BS::CB, RB = BS::RB, NTH = BS::NTH, NPAIR = CB / 32;
+  constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
+  constexpr int NTT = DB * MB / RB;        // state tiles per wavefront
+  constexpr int NZW = (DB + RB - 1) / RB;  // normaliser feature blocks per wavefront
+  static_assert((DB * MB) % RB == 0, "state tiles must divide evenly over the wavefronts of a role");
   __shared__ Planes<P::NQ, CB, D> qt;       // phi(Q)
   __shared__ Planes<P::NK, CB, D> kt;       // phi(K)
   __shared__ Planes<P::NV, CB, M> vt;       // V
@@ -643,28 +663,29 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
   // the 16 rows a fragment reads start in different banks
   __shared__ alignas(16) float q32[CB][D + 4];
   __shared__ alignas(16) float k32[CB][D + 4];
-  __shared__ alignas(16) float sZ[D];       // Z before this chunk
-  __shared__ alignas(16) float sr[D];       // r after this chunk
-  __shared__ alignas(16) float sInv[CB];    // 1 / den_i (0 past the end)
-  __shared__ alignas(16) float sOdo[CB];    // O_i . dO_i (0 past the end)
+  __shared__ alignas(16) float sZ[D];     // Z before this chunk
+  __shared__ alignas(16) float sr[D];     // r after this chunk
+  __shared__ alignas(16) float sInv[CB];  // 1 / den_i (0 past the end)
+  __shared__ alignas(16) float sOdo[CB];  // O_i . dO_i (0 past the end)
 
   const int sb = blockIdx.x % nsegb, bh = blockIdx.x / nsegb;
   const int t0 = sb * L, t1 = min(N, t0 + L);
   const int f0 = sb * kb, f1 = min(f0 + kb, nseg);  // checkpoint entries of the segment's ends
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const int db = w % DB;
-  const bool zw = w < DB;
+  const bool qrole = w < RB;  // query wavefront, else key wavefront
+  const int rb = w % RB;      // row block of the wavefront
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
-  const bool has_q = RB == 4 || w < 2;
-  const bool has_kv = RB == 4 || w >= 2;
-  const int qrb = w, kvrb = RB == 4 ? w : w - 2;
   const Frag<1> ones = ones_frag();
-  gt.zero_cols(M + 1, M + 16);
+  gt.zero_cols(M + 1, M + 16, NTH);
+
+  // state tile k of this wavefront: t = rb + RB k, feature block t % DB, value block t / DB
+  auto tdb = [&](int k) { return (rb + RB * k) % DB; };
+  auto tmb = [&](int k) { return (rb + RB * k) / DB; };
 
   // 0/1 masks j <= i of the query rows, under the accumulator map
   Frag<1> onef[NPAIR];
   {
-    const int il = 16 * qrb + r16;
+    const int il = 16 * rb + r16;
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {
       bool on[8];
@@ -676,13 +697,10 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
 
   const float* st_start = ckpt + ((size_t)bh * (nseg + 1) + f0) * SV;
   const float* st_end = ckpt + ((size_t)bh * (nseg + 1) + f1) * SV;
-  // reverse aggregates to add: entries [r0, r1) of this head
-  const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
-  const int r0 = scanned ? f1 - 1 : f1, r1 = scanned ? f1 : nseg;
 
   const int nchunk = (t1 - t0 + CB - 1) / CB;
-  RowBuf<T, CB, D> bq, bk;
-  RowBuf<T, CB, M> bv, bd;
+  RowBuf<T, CB, D, NTH> bq, bk;
+  RowBuf<T, CB, M, NTH> bv, bd;
   {
     const int c0 = t0 + (nchunk - 1) * CB, nv = min(CB, t1 - c0);
     bq.load(Q + offD + (size_t)c0 * D, nv);
@@ -691,51 +709,62 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     bd.load(dO + offM + (size_t)c0 * M, nv);
   }
 
-  f32x4_t accS[NTW], accR[NTW];  // S^T layout
+  // key wavefronts: S^T tiles; query wavefronts: R^T tiles (layout of add_ST_tiles)
+  f32x4_t acc[NTT];
+  float zr[NZW];  // key: Z, query: r, of features 16 (rb + RB j) + r16
 #pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    accS[k] = zero4();
-    accR[k] = zero4();
-  }
-  add_ST_tiles<D, M, NTW>(accS, st_end, 0, 0, 1, w, r16, g);
-  float rsum = 0.f;  // r of feature 16 db + r16
-  if (rg) {
-    static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
-    float* sb = reinterpret_cast<float*>(&rp.v[0][0][0]);
-    sum_states<D, M>(sb, nullptr, nullptr, rg, r0, r1);
-    __syncthreads();
+  for (int k = 0; k < NTT; ++k) acc[k] = zero4();
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int mb = (w + 4 * k) / DB;
-      const float4 a = *reinterpret_cast<const float4*>(sb + (16 * db + r16) * M + 16 * mb + 4 * g);
-      accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
-    }
-    if (zw) rsum = sb[D * M + 16 * db + r16];
-    __syncthreads();
-  }
-  auto stage_R = [&]() {
-    float v4[4];
+  for (int j = 0; j < NZW; ++j) zr[j] = 0.f;
+  auto load_tiles = [&](const float* src) {
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      acc_to4(accR[k], v4);
-      rp.put4(16 * db + r16, 16 * ((w + 4 * k) / DB) + 4 * g, v4);
+    for (int k = 0; k < NTT; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(src + (16 * tdb(k) + r16) * M + 16 * tmb(k) + 4 * g);
+      acc[k] = f32x4_t{a.x, a.y, a.z, a.w};
     }
   };
-  stage_R();
-  // zcur, rcur: Z and r of feature 16 db + r16 (waves w < DB)
-  float zcur = 0.f, rcur = 0.f;
-  if (zw) {
-    const int d = 16 * db + r16;
-    zcur = st_end[D * M + d];
-    rcur = rsum;
-    if (g == 0) sr[d] = rcur;
+  if (!qrole) {
+    load_tiles(st_end);
+#pragma unroll
+    for (int j = 0; j < NZW; ++j)
+      if (rb + RB * j < DB) zr[j] = st_end[D * M + 16 * (rb + RB * j) + r16];
   }
+  const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
+  if (rg) {  // reverse aggregates of the later segments, summed through R's planes as scratch
+    const int r0 = scanned ? f1 - 1 : f1, r1 = scanned ? f1 : nseg;
+    static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
+    float* sbuf = reinterpret_cast<float*>(&rp.v[0][0][0]);
+    sum_states<D, M, NTH>(sbuf, nullptr, nullptr, rg, r0, r1);
+    __syncthreads();
+    if (qrole) {
+      load_tiles(sbuf);
+#pragma unroll
+      for (int j = 0; j < NZW; ++j)
+        if (rb + RB * j < DB) zr[j] = sbuf[D * M + 16 * (rb + RB * j) + r16];
+    }
+    __syncthreads();
+  }
+  // R and r after the last chunk
+  auto stage_R = [&](int) {
+    float v4[4];
+#pragma unroll
+    for (int k = 0; k < NTT; ++k) {
+      acc_to4(acc[k], v4);
+      rp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < NZW; ++j)
+        if (rb + RB * j < DB) sr[16 * (rb + RB * j) + r16] = zr[j];
+    }
+  };
+  if (qrole) stage_R(0);
 
   for (int ci = nchunk - 1; ci >= 0; --ci) {
     const int c0 = t0 + ci * CB;
     const int nv = min(CB, t1 - c0);
     // ---- stage this chunk from registers, then start reading the previous one
-    __syncthreads();
+    // (the barrier ending the previous chunk separates its reads from these writes)
     bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0]);
     bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0]);
     bv.stage_values(vt);
@@ -749,51 +778,14 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
     }
     __syncthreads();
 
-    // ---- S and Z before this chunk
-    if (ci == 0) {
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) accS[k] = zero4();
-      add_ST_tiles<D, M, NTW>(accS, st_start, 0, 0, 1, w, r16, g);
-      if (zw) zcur = st_start[D * M + 16 * db + r16];
-    } else {
-      f32x4_t ds[NTW], dz = zero4();
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) ds[k] = zero4();
-#pragma unroll
-      for (int s = 0; s < CB / 32; ++s) {
-        constexpr int NKB = cmax(P::dS_b, P::Zc);
-        const Frag<NKB> kb = kt.template tfrag<NKB>(32 * s, 16 * db, g, r16);
-#pragma unroll
-        for (int k = 0; k < NTW; ++k) {
-          const int mb = (w + 4 * k) / DB;
-          mmaf<P::dS_a, P::dS_b>(ds[k], vt.template tfrag<P::dS_a>(32 * s, 16 * mb, g, r16), kb);
-        }
-        if (zw) mmaf<1, P::Zc>(dz, ones, kb);
-      }
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) accS[k] -= ds[k];
-      zcur -= dz[0];
-    }
-    {
-      float v4[4];
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        acc_to4(accS[k], v4);
-        sp.put4(16 * db + r16, 16 * ((w + 4 * k) / DB) + 4 * g, v4);
-      }
-    }
-    if (zw && g == 0) sZ[16 * db + r16] = zcur;
-    __syncthreads();
-
-    // ---- dQ for query rows 16 qrb + r16
-    if (has_q) {
-      const int ib = qrb, il = 16 * ib + r16;
-      const bool row_ok = il < nv;
-      constexpr int NO = cmax(P::Bt, P::U1_b);
-      Frag<NO> dof[M / 32];
+    // ================= phase A
+    constexpr int NO = cmax(cmax(P::Bt, P::U1_b), P::Wt);
+    Frag<NO> dof[M / 32];  // query: dO rows of this wavefront
+    Frag<P::U2> btf[NPAIR];
+    if (qrole) {
+      const int ib = rb, il = 16 * ib + r16;
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
-      Frag<P::U2> btf[NPAIR];
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
         f32x4_t bt[2];
@@ -815,6 +807,56 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
         }
         btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
       }
+    } else {
+      // S and Z before this chunk
+      if (ci == 0) {
+        load_tiles(st_start);
+#pragma unroll
+        for (int j = 0; j < NZW; ++j)
+          if (rb + RB * j < DB) zr[j] = st_start[D * M + 16 * (rb + RB * j) + r16];
+      } else {
+        constexpr int NKB = cmax(P::dS_b, P::Zc);
+#pragma unroll
+        for (int k = 0; k < NTT; ++k) {
+          f32x4_t ds = zero4();
+#pragma unroll
+          for (int s = 0; s < CB / 32; ++s)
+            mmaf<P::dS_a, P::dS_b>(ds, vt.template tfrag<P::dS_a>(32 * s, 16 * tmb(k), g, r16),
+                                   kt.template tfrag<NKB>(32 * s, 16 * tdb(k), g, r16));
+          acc[k] -= ds;
+        }
+#pragma unroll
+        for (int j = 0; j < NZW; ++j) {
+          const int d0 = rb + RB * j;
+          if (d0 < DB) {
+            f32x4_t dz = zero4();
+#pragma unroll
+            for (int s = 0; s < CB / 32; ++s) mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * d0, g, r16));
+            zr[j] -= dz[0];
+          }
+        }
+      }
+      float v4[4];
+#pragma unroll
+      for (int k = 0; k < NTT; ++k) {
+        acc_to4(acc[k], v4);
+        sp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < NZW; ++j)
+          if (rb + RB * j < DB) sZ[16 * (rb + RB * j) + r16] = zr[j];
+      }
+    }
+    __syncthreads();
+
+    // ================= phase B
+    constexpr int NKT = cmax(P::At, P::VR);
+    constexpr int NVT = cmax(P::Wt, P::KR_b);
+    f32x4_t at[NPAIR][2], wt[NPAIR][2];  // key: raw A_ij, dO_i.V_j
+    if (qrole) {
+      const int ib = rb, il = 16 * ib + r16;
+      const bool row_ok = il < nv;
       f32x4_t U[DB], ZC[DB];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
@@ -875,39 +917,16 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
         gt.put4(il, g * (M / 4) + mm, dv);
       }
       if (g == 0) gt.put1(il, M, -odo * invz);
-    }
-    __syncthreads();
-
-    // ---- reverse-state increment of this chunk (applied after the chunk):
-    //      R^T += g^T phi(Q), and r += phi(Q)^T c as the extra tile
-    f32x4_t dr = zero4();
-#pragma unroll
-    for (int s = 0; s < CB / 32; ++s) {
-      const Frag<P::dR> qb = qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16);
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int mb = (w + 4 * k) / DB;
-        mmaf<P::dR, P::dR>(accR[k], gt.template tfrag<P::dR>(32 * s, 16 * mb, g, r16), qb);
-      }
-      if (zw) mmaf<P::dR, P::dR>(dr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
-    }
-
-    // ---- dK, dV for key rows 16 kvrb + r16
-    if (has_kv) {
-      const int jb = kvrb, jl = 16 * jb + r16;
-      constexpr int NKT = cmax(P::At, P::VR);
+    } else {
+      const int jb = rb, jl = 16 * jb + r16;
       Frag<NKT> kfr[D / 32];
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
-      constexpr int NVT = cmax(P::Wt, P::KR_b);
       Frag<NVT> vfr[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
-      Frag<P::dK> wfr[NPAIR];
-      Frag<P::dV> afr[NPAIR];
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
-        f32x4_t at[2], wt[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int ib = 2 * p + h;
@@ -919,66 +938,106 @@ __global__ __launch_bounds__(NT) void k_bwd(const T* __restrict__ Q, const T* __
 #pragma unroll
             for (int s = 0; s < M / 32; ++s)
               mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
+          }
+          at[p][h] = a;
+          wt[p][h] = b;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= phase C
+    if (qrole) {
+      // R^T += g^T phi(Q) and r += phi(Q)^T c (row M of [g | c]) for the next (earlier) chunk
+#pragma unroll
+      for (int s = 0; s < CB / 32; ++s) {
+#pragma unroll
+        for (int k = 0; k < NTT; ++k)
+          mmaf<P::dR, P::dR>(acc[k], gt.template tfrag<P::dR>(32 * s, 16 * tmb(k), g, r16),
+                             qt.template tfrag<P::dR>(32 * s, 16 * tdb(k), g, r16));
+      }
+#pragma unroll
+      for (int j = 0; j < NZW; ++j) {
+        const int d0 = rb + RB * j;
+        if (d0 < DB) {
+          f32x4_t dr = zero4();
+#pragma unroll
+          for (int s = 0; s < CB / 32; ++s)
+            mmaf<P::dR, P::dR>(dr, gt.template tfrag<P::dR>(32 * s, M, g, r16),
+                               qt.template tfrag<P::dR>(32 * s, 16 * d0, g, r16));
+          zr[j] += dr[0];  // row M of the tile, on lanes g = 0
+        }
+      }
+    } else {
+      const int jb = rb, jl = 16 * jb + r16;
+      Frag<P::dK> wfr[NPAIR];
+      Frag<P::dV> afr[NPAIR];
+#pragma unroll
+      for (int p = 0; p < NPAIR; ++p) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ib = 2 * p + h;
+          if (ib >= jb) {
             const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
             const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
             const float ivr[4] = {iv.x, iv.y, iv.z, iv.w}, odr[4] = {od.x, od.y, od.z, od.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              b[r] = (b[r] - odr[r]) * ivr[r];  // (dO_i . V_j - O_i . dO_i) / den_i
+              wt[p][h][r] = (wt[p][h][r] - odr[r]) * ivr[r];  // (dO_i . V_j - O_i . dO_i) / den_i
               if (ib == jb && 4 * g + r < r16) {
-                a[r] = 0.f;
-                b[r] = 0.f;
+                at[p][h][r] = 0.f;
+                wt[p][h][r] = 0.f;
               }
             }
           }
-          at[h] = a;
-          wt[h] = b;
         }
-        wfr[p] = acc2frag<P::dK>(wt[0], wt[1]);
-        afr[p] = acc2frag<P::dV>(at[0], at[1]);
+        wfr[p] = acc2frag<P::dK>(wt[p][0], wt[p][1]);
+        afr[p] = acc2frag<P::dV>(at[p][0], at[p][1]);
       }
       const bool row_ok = jl < nv;
+      Frag<NVT> vfr[M / 32];
+#pragma unroll
+      for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t acc = zero4();
+        f32x4_t a = zero4();
+#pragma unroll
+        for (int s = 0; s < M / 32; ++s)  // later chunks: R V_j
+          mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(acc, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
-#pragma unroll
-        for (int s = 0; s < M / 32; ++s)
-          mmaf<P::KR_a, P::KR_b>(acc, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
+          if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
         if (row_ok) {
           float o[4];
           const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
-          const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
           const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
-          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+          const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (acc[r] + rr[r]) * dphi_from_phi(kv[r]);
+          for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dphi_from_phi(kv[r]);
           IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
         }
       }
+      Frag<NKT> kfr[D / 32];
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        f32x4_t acc = zero4();
+        f32x4_t a = zero4();
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)  // later chunks: R^T phi(K_j)
+          mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dV, P::dV>(acc, gt.template tfrag_acc<P::dV>(32 * p, 16 * mb, g, r16), afr[p]);
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-          mmaf<P::VR, P::VR>(acc, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
+          if (2 * p + 1 >= jb) mmaf<P::dV, P::dV>(a, gt.template tfrag_acc<P::dV>(32 * p, 16 * mb, g, r16), afr[p]);
         if (row_ok) {
-          float o[4] = {acc[0], acc[1], acc[2], acc[3]};
+          float o[4] = {a[0], a[1], a[2], a[3]};
           IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
         }
       }
     }
-    __syncthreads();
-    // ---- R and r for the next (earlier) chunk
-    stage_R();
-    if (zw) {
-      rcur += dr[0];
-      if (g == 0) sr[16 * db + r16] = rcur;
+    if (ci > 0) {
+      __syncthreads();  // every wavefront is done with this chunk's LDS, and the key ones with R, r
+      if (qrole) stage_R(0);
     }
   }
 }
