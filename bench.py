@@ -29,6 +29,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MFMA_FLOPS_PER_INST = 2 * 16 * 16 * 32  # v_mfma_f32_16x16x32_bf16, per wavefront instruction
+CLOCK_GHZ = 2.4
+SIMDS = 256 * 4
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -46,6 +50,9 @@ def parse():
                     "rocprofv3 --kernel-trace --stats kernel_stats.csv")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<kernel>_<label>.json/.md from rocprofv3 --pmc counter CSVs")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "STATS_CSV"),
+                    help="write profiles/<label>_mfma.md from a --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES ... run "
+                         "and the kernel statistics of a --kernel-trace --stats run")
     ap.add_argument("--label", default="mnist")
     ap.add_argument("--command", default="", help="the command that produced the CSVs (recorded in the summary)")
     return ap.parse_args()
@@ -306,6 +313,71 @@ def summarize_traffic(args):
     print(md)
 
 
+def summarize_mfma(args):
+    """Executed MFMA work per kernel (counters) against its duration (kernel statistics)."""
+    import csv
+
+    pmc_csv, stats_csv = args.summarize_mfma
+    inst, n = _counter_means(pmc_csv, "SQ_INSTS_MFMA")
+    busy, _ = _counter_means(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
+    valu, _ = _counter_means(pmc_csv, "SQ_INSTS_VALU")
+    dur = {}
+    for r in csv.DictReader(open(stats_csv)):
+        dur[kernel_tag(r["Name"])] = float(r["AverageNs"]) * 1e-9
+    wl = {"mnist": "MNIST", "cifar": "CIFAR", "long": "LONG", "decode": "DECODE", "small": "SMALL"}[args.label]
+    from linear_rnn_layers_amd import inputs
+
+    w = getattr(inputs, wl)
+    md = os.path.join(PROFILES, f"{args.label}_mfma.md")
+    with open(md, "w") as f:
+        f.write(f"# MFMA utilisation from rocprofv3 counters: {args.label} workload\n\n")
+        f.write(f"Commands (run from the repository root on one MI355X):\n\n    {args.command}\n\n")
+        f.write(f"Kernel sources: sha256[:16] = {source_hash()}\n\n")
+        f.write("Executed MFMA flops = SQ_INSTS_MFMA x 16384 (every matrix instruction is v_mfma_f32_16x16x32_bf16, "
+                "split-precision products included) over the kernel's average duration from the kernel statistics; "
+                f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (duration x {CLOCK_GHZ} GHz x {SIMDS} SIMDs); useful "
+                "flops are the method's own per token-head counts (forward 4DM+5D+M, backward 10DM+9D+3M). "
+                f"Peak: {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s dense bf16.\n\n")
+        f.write("| kernel | dispatches | SQ_INSTS_MFMA | SQ_INSTS_VALU | avg us | executed MFMA TFLOP/s | of bf16 peak "
+                "| MFMA busy | useful TFLOP/s |\n|---|---|---|---|---|---|---|---|---|\n")
+        for k in sorted(inst, key=lambda x: -inst[x]):
+            tag = kernel_tag(k)
+            if "la::" not in k or tag not in dur:
+                continue
+            t = dur[tag]
+            ex = inst[k] * MFMA_FLOPS_PER_INST / t / 1e12
+            b = busy.get(k, 0.0) / (t * CLOCK_GHZ * 1e9 * SIMDS)
+            fl = kernel_flops(tag, w)
+            useful = f"{fl / t / 1e12:.1f}" if fl else "-"
+            f.write(f"| {tag} | {n[k]} | {inst[k]:.4g} | {valu.get(k, 0.0):.4g} | {t * 1e6:.1f} | {ex:.1f} | "
+                    f"{ex / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% | {b * 100:.1f}% | {useful} |\n")
+    print(md)
+
+
+def copy_bandwidth():
+    """Achievable streaming bandwidth on this GPU: a plain 512 MiB device-to-device copy, GB/s of bytes
+    read + written."""
+    import torch
+
+    n = (512 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del a, b
+    return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
 # ------------------------------------------------------------ cpu baseline
 def cpu_baseline(args, w):
     import numpy as np
@@ -365,6 +437,9 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; heads are independent, so more GPUs "
@@ -440,6 +515,9 @@ def main():
         fl = kernel_flops(dominant, w)
         if fl:
             roof["useful_tflops"] = fl / avg_s / 1e12
+        copy = copy_bandwidth()
+        roof["copy_gbs"] = copy
+        roof["frac_of_copy"] = achieved / copy if achieved else None
 
     breakdown = {k: {"us_per_step": round(v["ms_per_step"] * 1e3, 2),
                      "launches_per_step": v["launches_per_step"]} for k, v in probe.items()}
