@@ -5,7 +5,9 @@
 // la_prof_collect, which waits for its own events by design).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <functional>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -74,14 +76,37 @@ Plan make_plan(int B, int H, int N, int D, int M) {
 // scan kernel forms all prefix sums once.
 bool use_scan(const Plan& p) { return (size_t)p.nseg * p.SV * sizeof(float) / 2 > (64u << 10); }
 
-// Checkpoint segments per backward segment: about kCUs x (resident backward
-// workgroups per compute unit) backward workgroups in all.
-int backward_group(const Plan& p, int resident) {
-  const long target = kCUs * (resident > 0 ? resident : 1);
-  long kb = (p.BH * p.nseg + target / 2) / target;
-  if (kb < 1) kb = 1;
-  if (kb > p.nseg) kb = p.nseg;
-  return (int)kb;
+// Checkpoint segments per backward segment.  A backward workgroup costs
+// about one chunk of set-up plus one per chunk it walks; workgroups are
+// dispatched in order onto kCUs x resident slots, each starting when the
+// earliest slot frees.  kb minimises the finish time of that schedule
+// (ties: fewer, longer segments).
+int backward_group(const Plan& p, int N, int resident) {
+  const int slots = (int)(kCUs * (resident > 0 ? resident : 1));
+  int best = 1;
+  long best_t = -1;
+  std::vector<long> heap;
+  for (int kb = 1; kb <= p.nseg; ++kb) {
+    const long Lb = (long)kb * p.L;
+    const long nsegb = (N + Lb - 1) / Lb;
+    heap.assign((size_t)slots, 0);  // min-heap of slot finish times
+    long finish = 0;
+    for (long h = 0; h < p.BH; ++h) {
+      for (long sb = 0; sb < nsegb; ++sb) {
+        const long tok = std::min((long)N, (sb + 1) * Lb) - sb * Lb;
+        const long cost = (tok + la::CH - 1) / la::CH + 1;
+        std::pop_heap(heap.begin(), heap.end(), std::greater<long>());
+        heap.back() += cost;
+        finish = std::max(finish, heap.back());
+        std::push_heap(heap.begin(), heap.end(), std::greater<long>());
+      }
+    }
+    if (best_t < 0 || finish <= best_t) {
+      best_t = finish;
+      best = kb;
+    }
+  }
+  return best;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -342,7 +367,7 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
       if (st) return st;
     }
   }
-  const int kb = backward_group(p, backward_resident<T, D, M>());
+  const int kb = backward_group(p, N, backward_resident<T, D, M>());
   const int nsegb = (p.nseg + kb - 1) / kb;
   return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::BwdShape<T, D, M>::NTH), s,
                 (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N,

@@ -293,20 +293,24 @@ struct IO<bf16_t> {
 // reductions over groups of COLS/E lanes are safe.  A full chunk is read
 // from a uniform base plus this thread's fixed 32-bit byte offsets, with no
 // per-row test; only a partial chunk takes the masked path.
-template <typename T, int CH, int COLS, int NTH = NT>
+// When a chunk has fewer vectors than the workgroup has threads, the
+// threads [OFF, OFF + VEC) -- whole wavefronts -- hold them, so that several
+// tensors can be spread over different wavefronts.
+template <typename T, int CH, int COLS, int NTH = NT, int OFF = 0>
 struct RowBuf {
   static constexpr int E = IO<T>::E;
   static constexpr int PR = COLS / E;                  // vectors per row
   static constexpr int VEC = CH * PR;                  // vectors per chunk
-  static constexpr int CNT = (VEC + NTH - 1) / NTH;    // vectors per thread
-  static_assert(VEC % NTH == 0 || (VEC < NTH && VEC % 64 == 0),
+  static constexpr int VT = VEC < NTH ? VEC : NTH;     // threads holding vectors
+  static constexpr int CNT = VEC / VT;                 // vectors per thread
+  static_assert(VEC % VT == 0 && VT % 64 == 0 && OFF % 64 == 0 && OFF + VT <= NTH,
                 "row visit must be uniform over each wavefront");
   typename IO<T>::raw r[CNT];
 
-  // threads past the chunk's vectors (only when VEC < NTH: whole wavefronts) hold nothing
-  __device__ static __forceinline__ bool owns() { return VEC >= NTH || (int)threadIdx.x < VEC; }
-  __device__ static __forceinline__ int row_of(int i) { return (threadIdx.x + i * NTH) / PR; }
-  __device__ static __forceinline__ int col_of(int i) { return ((threadIdx.x + i * NTH) % PR) * E; }
+  __device__ static __forceinline__ int te() { return (int)threadIdx.x - OFF; }
+  __device__ static __forceinline__ bool owns() { return VEC >= NTH || (te() >= 0 && te() < VT); }
+  __device__ static __forceinline__ int row_of(int i) { return (te() + i * VT) / PR; }
+  __device__ static __forceinline__ int col_of(int i) { return ((te() + i * VT) % PR) * E; }
   __device__ static __forceinline__ uint32_t byte_off(int i) {
     return (uint32_t)(row_of(i) * COLS + col_of(i)) * (uint32_t)sizeof(T);
   }

@@ -22,6 +22,8 @@
 // the 16 tokens 16w..16w+15 of a 64-token chunk.  Sums over tokens of a single
 // vector (the normaliser Z, the reverse normaliser r) are MFMA products with
 // an all-ones operand, the form of eq. 14-15 on [V, 1].
+#include <type_traits>
+
 #include "la_device.h"
 
 namespace la {
@@ -125,11 +127,11 @@ __device__ __forceinline__ void store_ST_tiles(float* dst, const f32x4_t* acc, i
 // sb[e] = init[e] + sum over p in [p0, p1), in order, of base[p * SV + e] for
 // the D*M + D floats of a state (S then Z; init from S0/Z0 or zero).  The
 // whole workgroup sums: each thread owns float4 columns and keeps a batch of
-// independent loads in flight.  The caller synchronises before reading sb.
+// 16 independent loads in flight.  The caller synchronises before reading sb.
 template <int D, int M, int NTH = NT>
 __device__ __forceinline__ void sum_states(float* sb, const float* S0, const float* Z0, const float* base, int p0,
                                            int p1) {
-  constexpr int SV = D * M + D, BT = 8;
+  constexpr int SV = D * M + D, BT = 16;
   for (int e = 4 * threadIdx.x; e < SV; e += 4 * NTH) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const float* init = e < D * M ? (S0 ? S0 + e : nullptr) : (Z0 ? Z0 + (e - D * M) : nullptr);
@@ -599,8 +601,8 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 
 // ===================================================================== B3
 // Backward over one segment, chunks in reverse order.  A backward segment is
-// kb consecutive segments of the checkpoint ([bh][nseg + 1] states), so its
-// start and end states are checkpoint entries sb kb and min((sb+1) kb, nseg).
+// kb consecutive segments of the checkpoint ([bh][nseg + 1] states); its end
+// state is checkpoint entry min((sb+1) kb, nseg).
 //
 // Per chunk the gradients are
 //   dQ: with u_i = S_i dO_i, Z_i the inclusive normaliser, den_i =
@@ -615,23 +617,35 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // recomputed den_i and O_i.dO_i are exact to float32, so dO_i.V_j - O_i.dO_i
 // cancels exactly where V_j = O_i even for bf16 storage.
 //
+// Walking backwards, the state after a chunk is known before the chunk is
+// processed (it is the state before the later chunk), so the query side uses
+//   S_i = S_after - sum_{j>i in the chunk} phi(K_j) V_j^T,
+//   Z_i = Z_after - sum_{j>i in the chunk} phi(K_j),
+// the complement of the causal mask, and the state before the chunk
+// (S_after minus the chunk's whole contribution) is formed for the next
+// chunk while the gradients are finished.  The first chunk of the sequence
+// is the exception: its S_i may be far smaller than S_after (a few tokens of
+// history against a whole chunk), so the subtraction would cancel; there the
+// state before the chunk -- the initial state, checkpoint entry 0 -- is
+// staged instead and the causal sum over j <= i is added.
+//
 // Two roles of RB = CB / 16 wavefronts each, one wavefront of each role per
 // SIMD for 64-token chunks, so that each SIMD interleaves two instruction
 // streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
 // reverse state R (backward sum of phi(Q) g^T, eq. 14-15, started from the
 // reverse aggregates of all later checkpoint segments: entry f1 - 1 of `ragg`
 // when it holds suffix sums (scanned = 1), else their sum in segment order).
-// Key wavefront k owns key rows 16k.. and the tiles of S (forward sum of
-// phi(K) V^T, eq. 13), walked backwards from the segment's end state by
-// removing each chunk's contribution (the first chunk restarts from the start
-// state).  Phases of a chunk, separated by barriers:
+// Key wavefront k owns key rows 16 (RB-1-k)..; it shares a SIMD with query
+// wavefront k, whose work falls with k while the key rows' work (all later
+// rows of the chunk) rises with k.  The tiles of S (forward sum of
+// phi(K) V^T, eq. 13) and Z are held by the query wavefronts (the key
+// wavefronts carry the longest phase).  Phases
+// of a chunk, separated by barriers:
 //   stage   all: phi(Q), phi(K), V, dO to LDS; next chunk's reads issued
-//   A  key: S, Z before the chunk           query: V_j.dO_i tiles
-//   B  key: A_ij, dO_i.V_j                  query: dQ, g, c, 1/den
-//   C  key: dK, dV (intra-chunk terms and the later chunks' R V_j, R^T phi(K_j))
-//      query: R, r += this chunk (staged for the next chunk after the key
-//      wavefronts' last read of them: R, r are read in phase C only, and
-//      written after the barrier that ends it -- see below)
+//   B  query: dQ, g, c, 1/den          key: A_ij, dO_i.V_j, R V_j
+//   C  query: R, r += this chunk; S, Z before the chunk, staged as the next
+//      chunk's S_after                 key: R^T phi(K_j), intra-chunk dK, dV
+// (R, r are staged for the next chunk after the barrier that ends C).
 template <typename T, int D, int M>
 struct BwdShape {
   static constexpr int CB = BwdChunk<T, D, M>::value;
@@ -647,60 +661,61 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     T* __restrict__ dV, int N, int L, int nsegb, int kb, int nseg, int scanned) {
   using P = Prec<T>;
   using BS = BwdShape<T, D, M>;
-  constexpr int CB = BS::CB, RB = BS::RB, NTH = BS::NTH, NPAIR = CB / 32;
+  constexpr int CB = BS::CB, RB = BS::RB, NW = BS::NW, NTH = BS::NTH, NPAIR = CB / 32;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
-  constexpr int NTT = DB * MB / RB;        // state tiles per wavefront
-  constexpr int NZW = (DB + RB - 1) / RB;  // normaliser feature blocks per wavefront
-  static_assert((DB * MB) % RB == 0, "state tiles must divide evenly over the wavefronts of a role");
+  constexpr int NTR = DB * MB / RB;                 // R tiles per query wavefront
+  constexpr int NWS = RB < DB * MB ? RB : DB * MB;  // query wavefronts holding S tiles
+  constexpr int NTS = DB * MB / NWS;                // S tiles per holder
+  constexpr int NZS = (DB + NWS - 1) / NWS;         // Z blocks per holder: so + NWS j
+  constexpr int NZW = (DB + RB - 1) / RB;           // r blocks per query wavefront
+  static_assert((DB * MB) % RB == 0 && (DB * MB) % NWS == 0, "state tiles must divide evenly");
   __shared__ Planes<P::NQ, CB, D> qt;       // phi(Q)
   __shared__ Planes<P::NK, CB, D> kt;       // phi(K)
   __shared__ Planes<P::NV, CB, M> vt;       // V
   __shared__ Planes<P::NDO, CB, M> ot;      // dO
   __shared__ Planes<P::NG, CB, M + 16> gt;  // [g | c | 0], g = dO / den
-  __shared__ Planes<P::NS, D, M> sp;        // S before this chunk, [d][m]
+  __shared__ Planes<P::NS, D, M> sp;        // S after this chunk, [d][m]
   __shared__ Planes<P::NR, D, M> rp;        // R after this chunk, [d][m]
   // phi(Q), phi(K) as float32 for the elementwise terms; rows padded by 4 so
   // the 16 rows a fragment reads start in different banks
   __shared__ alignas(16) float q32[CB][D + 4];
   __shared__ alignas(16) float k32[CB][D + 4];
-  __shared__ alignas(16) float sZ[D];     // Z before this chunk
+  __shared__ alignas(16) float sZ[D];     // Z after this chunk
   __shared__ alignas(16) float sr[D];     // r after this chunk
   __shared__ alignas(16) float sInv[CB];  // 1 / den_i (0 past the end)
   __shared__ alignas(16) float sOdo[CB];  // O_i . dO_i (0 past the end)
 
   const int sb = blockIdx.x % nsegb, bh = blockIdx.x / nsegb;
   const int t0 = sb * L, t1 = min(N, t0 + L);
-  const int f0 = sb * kb, f1 = min(f0 + kb, nseg);  // checkpoint entries of the segment's ends
+  const int f1 = min(sb * kb + kb, nseg);  // checkpoint entry of the segment's end
+  const bool seqstart = t0 == 0;           // the segment holds the sequence's first chunk
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const bool qrole = w < RB;  // query wavefront, else key wavefront
-  const int rb = w % RB;      // row block of the wavefront
+  const bool qrole = w < RB;     // query wavefront, else key wavefront
+  const int rb = w % RB;         // row block of the wavefront
+  const int so = w;              // rank among the S holders (query wavefronts first)
+  const bool shold = so < NWS;   // holds S tiles
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
   const Frag<1> ones = ones_frag();
   gt.zero_cols(M + 1, M + 16, NTH);
 
-  // state tile k of this wavefront: t = rb + RB k, feature block t % DB, value block t / DB
-  auto tdb = [&](int k) { return (rb + RB * k) % DB; };
-  auto tmb = [&](int k) { return (rb + RB * k) / DB; };
+  // R tile k of a query wavefront: t = rb + RB k; S tile k of a holder: t = so + NWS k;
+  // feature block t % DB, value block t / DB
+  auto rdb = [&](int k) { return (rb + RB * k) % DB; };
+  auto rmb = [&](int k) { return (rb + RB * k) / DB; };
+  auto sdb = [&](int k) { return (so + NWS * k) % DB; };
+  auto smb = [&](int k) { return (so + NWS * k) / DB; };
 
-  // 0/1 masks j <= i of the query rows, under the accumulator map
-  Frag<1> onef[NPAIR];
-  {
-    const int il = 16 * rb + r16;
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p) {
-      bool on[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) on[e] = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) <= il;
-      onef[p] = mask_frag(on);
-    }
-  }
-
-  const float* st_start = ckpt + ((size_t)bh * (nseg + 1) + f0) * SV;
   const float* st_end = ckpt + ((size_t)bh * (nseg + 1) + f1) * SV;
+  const float* st_init = ckpt + (size_t)bh * (nseg + 1) * SV;  // the initial state
 
   const int nchunk = (t1 - t0 + CB - 1) / CB;
-  RowBuf<T, CB, D, NTH> bq, bk;
-  RowBuf<T, CB, M, NTH> bv, bd;
+  // a tensor with half as many vectors per chunk as threads goes to one half of the workgroup
+  constexpr int OK_ = RowBuf<T, CB, D, NTH>::VEC < NTH ? NTH / 2 : 0;
+  constexpr int OD_ = RowBuf<T, CB, M, NTH>::VEC < NTH ? NTH / 2 : 0;
+  RowBuf<T, CB, D, NTH> bq;
+  RowBuf<T, CB, D, NTH, OK_> bk;
+  RowBuf<T, CB, M, NTH> bv;
+  RowBuf<T, CB, M, NTH, OD_> bd;
   {
     const int c0 = t0 + (nchunk - 1) * CB, nv = min(CB, t1 - c0);
     bq.load(Q + offD + (size_t)c0 * D, nv);
@@ -709,25 +724,43 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     bd.load(dO + offM + (size_t)c0 * M, nv);
   }
 
-  // key wavefronts: S^T tiles; query wavefronts: R^T tiles (layout of add_ST_tiles)
-  f32x4_t acc[NTT];
-  float zr[NZW];  // key: Z, query: r, of features 16 (rb + RB j) + r16
+  // S^T and R^T tiles in the layout of add_ST_tiles
+  f32x4_t accS[NTS], accR[NTR];
+  float zr[NZW];   // query: r of features 16 (rb + RB j) + r16
+  float zz[NZS];   // Z of features 16 (so + NWS j) + r16
 #pragma unroll
-  for (int k = 0; k < NTT; ++k) acc[k] = zero4();
+  for (int j = 0; j < NZS; ++j) zz[j] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NTR; ++k) accR[k] = zero4();
 #pragma unroll
   for (int j = 0; j < NZW; ++j) zr[j] = 0.f;
-  auto load_tiles = [&](const float* src) {
+  // S, Z after the last chunk: the segment's end state
+  auto stage_S = [&]() {
+    float v4[4];
 #pragma unroll
-    for (int k = 0; k < NTT; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(src + (16 * tdb(k) + r16) * M + 16 * tmb(k) + 4 * g);
-      acc[k] = f32x4_t{a.x, a.y, a.z, a.w};
+    for (int k = 0; k < NTS; ++k) {
+      acc_to4(accS[k], v4);
+      sp.put4(16 * sdb(k) + r16, 16 * smb(k) + 4 * g, v4);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < NZS; ++j)
+        if (so + NWS * j < DB) sZ[16 * (so + NWS * j) + r16] = zz[j];
     }
   };
-  if (!qrole) {
-    load_tiles(st_end);
+  auto load_S = [&](const float* src) {
 #pragma unroll
-    for (int j = 0; j < NZW; ++j)
-      if (rb + RB * j < DB) zr[j] = st_end[D * M + 16 * (rb + RB * j) + r16];
+    for (int k = 0; k < NTS; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(src + (16 * sdb(k) + r16) * M + 16 * smb(k) + 4 * g);
+      accS[k] = f32x4_t{a.x, a.y, a.z, a.w};
+    }
+#pragma unroll
+    for (int j = 0; j < NZS; ++j)
+      if (so + NWS * j < DB) zz[j] = src[D * M + 16 * (so + NWS * j) + r16];
+  };
+  if (shold) {
+    load_S(seqstart && nchunk == 1 ? st_init : st_end);
+    stage_S();
   }
   const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
   if (rg) {  // reverse aggregates of the later segments, summed through R's planes as scratch
@@ -737,20 +770,24 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     sum_states<D, M, NTH>(sbuf, nullptr, nullptr, rg, r0, r1);
     __syncthreads();
     if (qrole) {
-      load_tiles(sbuf);
+#pragma unroll
+      for (int k = 0; k < NTR; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(sbuf + (16 * rdb(k) + r16) * M + 16 * rmb(k) + 4 * g);
+        accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
+      }
 #pragma unroll
       for (int j = 0; j < NZW; ++j)
         if (rb + RB * j < DB) zr[j] = sbuf[D * M + 16 * (rb + RB * j) + r16];
     }
     __syncthreads();
   }
-  // R and r after the last chunk
-  auto stage_R = [&](int) {
+  // R and r after the chunk about to be processed
+  auto stage_R = [&]() {
     float v4[4];
 #pragma unroll
-    for (int k = 0; k < NTT; ++k) {
-      acc_to4(acc[k], v4);
-      rp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
+    for (int k = 0; k < NTR; ++k) {
+      acc_to4(accR[k], v4);
+      rp.put4(16 * rdb(k) + r16, 16 * rmb(k) + 4 * g, v4);
     }
     if (g == 0) {
 #pragma unroll
@@ -758,7 +795,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         if (rb + RB * j < DB) sr[16 * (rb + RB * j) + r16] = zr[j];
     }
   };
-  if (qrole) stage_R(0);
+  if (qrole) stage_R();
 
   for (int ci = nchunk - 1; ci >= 0; --ci) {
     const int c0 = t0 + ci * CB;
@@ -778,14 +815,25 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     }
     __syncthreads();
 
-    // ================= phase A
-    constexpr int NO = cmax(cmax(P::Bt, P::U1_b), P::Wt);
-    Frag<NO> dof[M / 32];  // query: dO rows of this wavefront
-    Frag<P::U2> btf[NPAIR];
-    if (qrole) {
+    // ================= phase B
+    constexpr int NKT = cmax(P::At, P::VR);
+    constexpr int NVT = cmax(P::Wt, P::KR_b);
+    f32x4_t at[NPAIR][2], wt[NPAIR][2];  // key: raw A_ij, dO_i.V_j
+    f32x4_t gk[DB];                      // key: dK accumulators
+    // query side; the sequence's first chunk adds the causal part j <= i to the state
+    // before it, every other chunk removes the part j > i from the state after it
+    auto query_b = [&](auto causal_tag) {
+      constexpr bool causal = decltype(causal_tag)::value;
       const int ib = rb, il = 16 * ib + r16;
+      const bool row_ok = il < nv;
+      constexpr int NO = cmax(P::Bt, P::U1_b);
+      Frag<NO> dof[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
+      // +-(V_j . dO_i) over the tokens j of that part, and the mask +-[j in it], as B
+      // operands under the accumulator map
+      Frag<P::U2> btf[NPAIR];
+      Frag<1> onef[NPAIR];
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
         f32x4_t bt[2];
@@ -793,70 +841,25 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         for (int h = 0; h < 2; ++h) {
           const int jb = 2 * p + h;
           f32x4_t a = zero4();
-          if (jb <= ib) {
+          if (causal ? jb <= ib : jb >= ib) {
 #pragma unroll
             for (int s = 0; s < M / 32; ++s)
               mmaf<P::Bt, P::Bt>(a, vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
-            if (jb == ib) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (4 * g + r > r16) a[r] = 0.f;  // V_j . dO_i with j > i is masked
+            for (int r = 0; r < 4; ++r) {
+              const bool later = jb > ib || (jb == ib && 4 * g + r > r16);  // j > i
+              a[r] = causal ? (later ? 0.f : a[r]) : (later ? -a[r] : 0.f);
             }
           }
           bt[h] = a;
         }
         btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
-      }
-    } else {
-      // S and Z before this chunk
-      if (ci == 0) {
-        load_tiles(st_start);
 #pragma unroll
-        for (int j = 0; j < NZW; ++j)
-          if (rb + RB * j < DB) zr[j] = st_start[D * M + 16 * (rb + RB * j) + r16];
-      } else {
-        constexpr int NKB = cmax(P::dS_b, P::Zc);
-#pragma unroll
-        for (int k = 0; k < NTT; ++k) {
-          f32x4_t ds = zero4();
-#pragma unroll
-          for (int s = 0; s < CB / 32; ++s)
-            mmaf<P::dS_a, P::dS_b>(ds, vt.template tfrag<P::dS_a>(32 * s, 16 * tmb(k), g, r16),
-                                   kt.template tfrag<NKB>(32 * s, 16 * tdb(k), g, r16));
-          acc[k] -= ds;
-        }
-#pragma unroll
-        for (int j = 0; j < NZW; ++j) {
-          const int d0 = rb + RB * j;
-          if (d0 < DB) {
-            f32x4_t dz = zero4();
-#pragma unroll
-            for (int s = 0; s < CB / 32; ++s) mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * d0, g, r16));
-            zr[j] -= dz[0];
-          }
+        for (int e = 0; e < 8; ++e) {
+          const bool later = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) > il;
+          onef[p].p[0][e] = causal ? (later ? (__bf16)0.0f : (__bf16)1.0f) : (later ? (__bf16)-1.0f : (__bf16)0.0f);
         }
       }
-      float v4[4];
-#pragma unroll
-      for (int k = 0; k < NTT; ++k) {
-        acc_to4(acc[k], v4);
-        sp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
-      }
-      if (g == 0) {
-#pragma unroll
-        for (int j = 0; j < NZW; ++j)
-          if (rb + RB * j < DB) sZ[16 * (rb + RB * j) + r16] = zr[j];
-      }
-    }
-    __syncthreads();
-
-    // ================= phase B
-    constexpr int NKT = cmax(P::At, P::VR);
-    constexpr int NVT = cmax(P::Wt, P::KR_b);
-    f32x4_t at[NPAIR][2], wt[NPAIR][2];  // key: raw A_ij, dO_i.V_j
-    if (qrole) {
-      const int ib = rb, il = 16 * ib + r16;
-      const bool row_ok = il < nv;
       f32x4_t U[DB], ZC[DB];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
@@ -866,7 +869,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
           mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p) {
-          if (2 * p <= ib) {
+          if (causal ? 2 * p <= ib : 2 * p + 1 >= ib) {
             constexpr int NKA = cmax(P::U2, P::Zc);
             const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
             mmaf<P::U2, P::U2>(u, kfa, btf[p]);
@@ -917,8 +920,14 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         gt.put4(il, g * (M / 4) + mm, dv);
       }
       if (g == 0) gt.put1(il, M, -odo * invz);
+    };
+    if (qrole) {
+      if (seqstart && ci == 0)
+        query_b(std::true_type{});
+      else
+        query_b(std::false_type{});
     } else {
-      const int jb = rb, jl = 16 * jb + r16;
+      const int jb = RB - 1 - rb, jl = 16 * jb + r16;
       Frag<NKT> kfr[D / 32];
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
@@ -943,6 +952,15 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
           wt[p][h] = b;
         }
       }
+      // later chunks' share of dK: R V_j
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
+        f32x4_t a = zero4();
+#pragma unroll
+        for (int s = 0; s < M / 32; ++s)
+          mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
+        gk[d0] = a;
+      }
     }
     __syncthreads();
 
@@ -952,9 +970,9 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
 #pragma unroll
       for (int s = 0; s < CB / 32; ++s) {
 #pragma unroll
-        for (int k = 0; k < NTT; ++k)
-          mmaf<P::dR, P::dR>(acc[k], gt.template tfrag<P::dR>(32 * s, 16 * tmb(k), g, r16),
-                             qt.template tfrag<P::dR>(32 * s, 16 * tdb(k), g, r16));
+        for (int k = 0; k < NTR; ++k)
+          mmaf<P::dR, P::dR>(accR[k], gt.template tfrag<P::dR>(32 * s, 16 * rmb(k), g, r16),
+                             qt.template tfrag<P::dR>(32 * s, 16 * rdb(k), g, r16));
       }
 #pragma unroll
       for (int j = 0; j < NZW; ++j) {
@@ -969,7 +987,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         }
       }
     } else {
-      const int jb = rb, jl = 16 * jb + r16;
+      const int jb = RB - 1 - rb, jl = 16 * jb + r16;
       Frag<P::dK> wfr[NPAIR];
       Frag<P::dV> afr[NPAIR];
 #pragma unroll
@@ -995,15 +1013,9 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         afr[p] = acc2frag<P::dV>(at[p][0], at[p][1]);
       }
       const bool row_ok = jl < nv;
-      Frag<NVT> vfr[M / 32];
-#pragma unroll
-      for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t a = zero4();
-#pragma unroll
-        for (int s = 0; s < M / 32; ++s)  // later chunks: R V_j
-          mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
+        f32x4_t a = gk[d0];
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
           if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
@@ -1035,9 +1047,37 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         }
       }
     }
+    // S, Z before this chunk = S, Z after the next one to process (its reads of sp, sZ ended at the
+    // barrier); before the sequence's first chunk, the initial state itself
+    if (ci == 1 && seqstart && shold) {
+      load_S(st_init);
+      stage_S();
+    } else if (ci > 0 && shold) {
+      constexpr int NKB = cmax(P::dS_b, P::Zc);
+#pragma unroll
+      for (int k = 0; k < NTS; ++k) {
+        f32x4_t ds = zero4();
+#pragma unroll
+        for (int s = 0; s < CB / 32; ++s)
+          mmaf<P::dS_a, P::dS_b>(ds, vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16),
+                                 kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16));
+        accS[k] -= ds;
+      }
+#pragma unroll
+      for (int j = 0; j < NZS; ++j) {
+        const int d0 = so + NWS * j;
+        if (d0 < DB) {
+          f32x4_t dz = zero4();
+#pragma unroll
+          for (int s = 0; s < CB / 32; ++s) mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * d0, g, r16));
+          zz[j] -= dz[0];
+        }
+      }
+      stage_S();
+    }
     if (ci > 0) {
       __syncthreads();  // every wavefront is done with this chunk's LDS, and the key ones with R, r
-      if (qrole) stage_R(0);
+      if (qrole) stage_R();
     }
   }
 }
