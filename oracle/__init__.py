@@ -51,6 +51,7 @@ def _configure(lib):
     lib.orc_forward_noncausal.argtypes = [dp] * 4 + [L] * 5
     lib.orc_numerator_backward.argtypes = [dp] * 7 + [L] * 3
     lib.orc_backward_causal.argtypes = [dp] * 9 + [L] * 5
+    lib.orc_backward_noncausal.argtypes = [dp] * 7 + [L] * 5
     lib.orc_decode_step.argtypes = [dp] * 6 + [L] * 4
     lib.orc_num_threads.restype = ctypes.c_int
     return lib
@@ -151,6 +152,19 @@ def backward_causal(q, k, v, do, s0=None, z0=None):
     dv = np.empty((B, H, N, M))
     _load().orc_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dq), _ptr(dk),
                                 _ptr(dv), B, H, N, D, M)
+    return dq, dk, dv
+
+
+def backward_noncausal(q, k, v, do):
+    """Gradients of sum(dO * O) for the non-causal forward w.r.t. raw Q, K, V.  Returns (dQ, dK, dV)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    dq = np.empty((B, H, N, D))
+    dk = np.empty((B, H, N, D))
+    dv = np.empty((B, H, N, M))
+    _load().orc_backward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, H, N, D, M)
     return dq, dk, dv
 
 

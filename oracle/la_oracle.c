@@ -311,6 +311,85 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
 }
 
 /*
+ * Non-causal backward: gradients of L = sum(dO * O) with respect to the raw
+ * Q, K, V for the non-causal forward ([TaRn] section 3.2, eq. 5-6), where
+ * every query sees every key.  The same steps as the causal backward with
+ * the masks removed, so the cumulative sums of eq. 13-15 become totals:
+ *  1. S = sum_j phi(K_j) V_j^T, Z = sum_j phi(K_j); den_i = phi(Q_i) . Z,
+ *     O_i = phi(Q_i)^T S / den_i;
+ *  2. quotient rule: g_i = dO_i / den_i, c_i = -(dO_i . O_i) / den_i;
+ *  3. on [V, 1] with upstream [g, c]:
+ *       dphiQ_i = S g_i + c_i Z                    (eq. 13 with S_i = S),
+ *       R = sum_i phi(Q_i) g_i^T, r = sum_i c_i phi(Q_i)   (eq. 14's sum over all i),
+ *       dphiK_j = R V_j + r,  dV_j = R^T phi(K_j)  (eq. 14-15);
+ *  4. chain rule through phi.
+ */
+void orc_backward_noncausal(const double *Q, const double *K, const double *V,
+                            const double *dO, double *dQ, double *dK,
+                            double *dV, long B, long H, long N, long D,
+                            long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    const double *q = Q + bh * N * D, *k = K + bh * N * D, *v = V + bh * N * M;
+    const double *go = dO + bh * N * M;
+    double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+    double *Z = (double *)calloc((size_t)D, sizeof(double));
+    double *R = (double *)calloc((size_t)(D * M), sizeof(double));
+    double *r = (double *)calloc((size_t)D, sizeof(double));
+    double *pq = (double *)malloc((size_t)D * sizeof(double));
+    double *g = (double *)malloc((size_t)M * sizeof(double));
+    /* 1. totals of the keys */
+    for (long j = 0; j < N; ++j)
+      for (long d = 0; d < D; ++d) {
+        double pk = orc_phi(k[j * D + d]);
+        for (long m = 0; m < M; ++m) S[d * M + m] += pk * v[j * M + m];
+        Z[d] += pk;
+      }
+    /* 2-3. per query: den, O, g, c; dphiQ; accumulate R, r */
+    for (long i = 0; i < N; ++i) {
+      for (long d = 0; d < D; ++d) pq[d] = orc_phi(q[i * D + d]);
+      double den = 0.0;
+      for (long d = 0; d < D; ++d) den += pq[d] * Z[d];
+      double dot = 0.0;
+      for (long m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (long d = 0; d < D; ++d) num += pq[d] * S[d * M + m];
+        dot += go[i * M + m] * (num / den);
+        g[m] = go[i * M + m] / den;
+      }
+      double c = -dot / den;
+      for (long d = 0; d < D; ++d) {
+        double acc = c * Z[d];
+        for (long m = 0; m < M; ++m) acc += S[d * M + m] * g[m];
+        dQ[(bh * N + i) * D + d] = acc * orc_dphi(q[i * D + d]);
+        for (long m = 0; m < M; ++m) R[d * M + m] += pq[d] * g[m];
+        r[d] += c * pq[d];
+      }
+    }
+    /* 3-4. per key */
+    for (long j = 0; j < N; ++j) {
+      for (long d = 0; d < D; ++d) {
+        double acc = r[d];
+        for (long m = 0; m < M; ++m) acc += R[d * M + m] * v[j * M + m];
+        dK[(bh * N + j) * D + d] = acc * orc_dphi(k[j * D + d]);
+      }
+      for (long m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(k[j * D + d]);
+        dV[(bh * N + j) * M + m] = acc;
+      }
+    }
+    free(S);
+    free(Z);
+    free(R);
+    free(r);
+    free(pq);
+    free(g);
+  }
+}
+
+/*
  * One RNN decode step ([TaR] eq. 18-20, attention part; [LA] recurrent
  * form): S += phi(k) v^T, Z += phi(k), then y = phi(q)^T S / phi(q).Z.
  * S [B,H,D,M] and Z [B,H,D] are updated in place; y [B,H,M].

@@ -48,6 +48,18 @@ def brute_noncausal(q, k, v):
     return out
 
 
+def brute_noncausal_grad(q, k, v, do):
+    """Gradients of sum(dO * O) of the unmasked form, by PyTorch autograd in float64 (library elu)."""
+    ts = [torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True) for a in (q, k, v)]
+    tq, tk, tv = ts
+    pq = torch.nn.functional.elu(tq, alpha=1.0) + 1.0
+    pk = torch.nn.functional.elu(tk, alpha=1.0) + 1.0
+    sim = pq @ pk.transpose(-1, -2)
+    out = (sim @ tv) / sim.sum(dim=-1, keepdim=True)
+    (out * torch.from_numpy(np.asarray(do, dtype=np.float64))).sum().backward()
+    return tuple(t.grad.numpy() for t in ts)
+
+
 def brute_numerator(p, kf, vb):
     """Numerator of eq. 9 on feature-mapped inputs: Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j."""
     n = p.shape[0]

@@ -34,6 +34,11 @@ MUTATIONS = {
                                       "    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m] * (i > 0);\n      dP[i * C + c] = acc;\n    }\n  }"),
     "non-causal drops phi on keys": ("double pk = orc_phi(k[d]);\n        for", "double pk = k[d];\n        for"),
     "decode normaliser ignores keys": ("      z[d] += pk;", "      z[d] += 1.0;"),
+    "non-causal backward denominator sign": ("double c = -dot / den;", "double c = dot / den;"),
+    "non-causal reverse sum of phi(K)": ("for (long m = 0; m < M; ++m) R[d * M + m] += pq[d] * g[m];",
+                                         "for (long m = 0; m < M; ++m) R[d * M + m] += orc_phi(k[i * D + d]) * g[m];"),
+    "non-causal value gradient uses phi(Q)": ("for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(k[j * D + d]);",
+                                              "for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(q[j * D + d]);"),
     "initial state ignored in backward": ("acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];",
                                           "acc += 0.0 * G[i * Mb + M];"),
 }
@@ -55,6 +60,10 @@ PIN_CALLS = [
     lambda: P.test_backward_finite_differences(4, 8, True),
     P.test_numerator_gradient_finite_differences,
     P.test_euler_identities,
+    lambda: P.test_noncausal_backward_finite_differences(3, 3),
+    lambda: P.test_noncausal_backward_equals_autograd((2, 3, 17, 5, 3)),
+    P.test_noncausal_backward_last_row_is_causal,
+    P.test_noncausal_backward_constant_values,
 ]
 
 

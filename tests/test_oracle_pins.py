@@ -349,3 +349,65 @@ def test_euler_identities():
     o, _, _, _ = oracle.forward_causal(q, k, v)
     np.testing.assert_allclose(np.sum(dv * v, axis=(2, 3)), np.sum(do * o, axis=(2, 3)), rtol=1e-12,
                                atol=1e-12)
+
+
+# ------------------------------------ non-causal backward (reading notes eq. 5-6)
+def _loss_nc(q, k, v, do):
+    return float(np.sum(do * oracle.forward_noncausal(q, k, v)))
+
+
+@pytest.mark.parametrize("D,M", [(3, 3), (4, 8)])
+def test_noncausal_backward_finite_differences(D, M):
+    """Central differences of L = sum(dO * O) for the unmasked form agree with the oracle's gradients."""
+    N = 6
+    q, k, v = _qkv((1, 1, N, D, M), 171 + D + M)
+    q, k, v = _nudge(q), _nudge(k), np.asarray(v, np.float64)
+    do = inputs.gaussian((1, 1, N, M), 179).astype(np.float64)
+    dq, dk, dv = oracle.backward_noncausal(q, k, v, do)
+    h = 1e-6
+    for name, x, g in (("Q", q, dq), ("K", k, dk), ("V", v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"Q": (xp, k, v), "K": (q, xp, v), "V": (q, k, xp)}[name]
+            args_m = {"Q": (xm, k, v), "K": (q, xm, v), "V": (q, k, xm)}[name]
+            fd[idx] = (_loss_nc(*args_p, do) - _loss_nc(*args_m, do)) / (2 * h)
+        scale = max(np.max(np.abs(fd)), 1e-12)
+        assert np.max(np.abs(fd - g)) / scale < 1e-6, name
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 17, 5, 3), (1, 2, 40, 8, 6)])
+def test_noncausal_backward_equals_autograd(shape):
+    """The unmasked quadratic form differentiated by PyTorch autograd (float64, library elu)."""
+    q, k, v = _qkv(shape, 181)
+    do = inputs.gaussian(v.shape, 184).astype(np.float64)
+    got = oracle.backward_noncausal(q, k, v, do)
+    ref = pins.brute_noncausal_grad(q, k, v, do)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12 * np.max(np.abs(r)))
+
+
+def test_noncausal_backward_last_row_is_causal():
+    """The last causal row sees every key (eq. 8), so with the upstream gradient on the last row only the
+    causal and non-causal gradients coincide."""
+    q, k, v = _qkv((2, 2, 13, 4, 5), 191)
+    do = np.zeros(v.shape)
+    do[:, :, -1] = inputs.gaussian((2, 2, 5), 194)
+    nc = oracle.backward_noncausal(q, k, v, do)
+    ca = oracle.backward_causal(q, k, v, do)
+    for a, b in zip(nc, ca):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_noncausal_backward_constant_values():
+    """Rows of V all equal: O = V for any Q, K, so dQ = dK = 0 and dV_j = sum_i A_ij dO_i / den_i sums to dO."""
+    q, k, _ = _qkv((1, 2, 9, 4, 3), 197)
+    v = np.broadcast_to(np.array([0.5, -1.25, 2.0]), (1, 2, 9, 3)).copy()
+    do = inputs.gaussian(v.shape, 199).astype(np.float64)
+    dq, dk, dv = oracle.backward_noncausal(q, k, v, do)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+    # the attention weights of every row sum to one, so the value gradients sum to the upstream gradients
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=1e-12, atol=1e-12)
