@@ -65,7 +65,8 @@ typedef enum {
   LA_OP_FWD_CAUSAL = 0,
   LA_OP_FWD_NONCAUSAL = 1,
   LA_OP_BWD_CAUSAL = 2,
-  LA_OP_DECODE = 3
+  LA_OP_DECODE = 3,
+  LA_OP_BWD_NONCAUSAL = 4
 } la_op;
 
 /* Library version, as 10000*major + 100*minor + patch. */
@@ -148,6 +149,27 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
                        void *dQ, void *dK, void *dV, int B, int H, int N,
                        int D, int M, int dtype, void *ws, size_t ws_bytes,
                        void *stream);
+
+/*
+ * Non-causal backward: gradients of a scalar loss with respect to the raw Q,
+ * K, V of la_forward_noncausal given dO = dL/dO.  The causal backward's
+ * quotient rule with the masks removed (reading notes on "Transformers are
+ * RNNs", section 3.2, eq. 5-6): the running sums of eq. 13-15 become the
+ * totals S = sum_j phi(K_j) V_j^T, Z = sum_j phi(K_j) (query side) and
+ * R = sum_i phi(Q_i) g_i^T, r = sum_i c_i phi(Q_i) with g_i = dO_i / den_i,
+ * c_i = -(dO_i . O_i) / den_i (key side):
+ *   dphi(Q_i) = S g_i + c_i Z,  dphi(K_j) = R V_j + r,  dV_j = R^T phi(K_j).
+ * den_i and dO_i . O_i are recomputed from S, Z, so neither O nor den is an
+ * input.  Linear time, O(D M) state per head.
+ *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype`.
+ *   dQ, dK, dV  outputs in `dtype`.
+ *   ws          la_workspace_size(LA_OP_BWD_NONCAUSAL, ...) bytes (never 0
+ *               for N > 0).
+ */
+int la_backward_noncausal(const void *Q, const void *K, const void *V,
+                          const void *dO, void *dQ, void *dK, void *dV, int B,
+                          int H, int N, int D, int M, int dtype, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /*
  * One RNN step of the attention ("Transformers are RNNs -- part 2/3",

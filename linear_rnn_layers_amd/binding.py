@@ -18,10 +18,11 @@ import torch
 from . import build as _build
 
 LA_F32, LA_BF16 = 0, 1
-LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_DECODE = 0, 1, 2, 3
+LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_DECODE, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3, 4
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
-                "la_forward_noncausal", "la_backward_causal", "la_decode_step", "la_status_string", "la_last_error",
-                "la_prof_select", "la_prof_collect", "la_kernel_names", "la_set_segment_chunks")
+                "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
+                "la_status_string", "la_last_error", "la_prof_select", "la_prof_collect", "la_kernel_names",
+                "la_set_segment_chunks")
 
 _lib = None
 
@@ -58,6 +59,8 @@ def load(path: str | None = None):
     lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
     lib.la_backward_causal.restype = i
     lib.la_backward_causal.argtypes = [vp] * 12 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_noncausal.restype = i
+    lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [vp] * 6 + [i] * 5 + [vp]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -166,6 +169,14 @@ def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=N
     _check(st, "la_backward_causal")
 
 
+def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None):
+    B, H, N, D, M = _sizes(Q, V)
+    nb = ws.numel() if ws is not None else 0
+    st = load().la_backward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, D,
+                                      M, dtype_code(Q.dtype), _ptr(ws), nb, _stream(stream))
+    _check(st, "la_backward_noncausal")
+
+
 def la_decode_step(q, k, v, S, Z, y, stream=None):
     if q.dim() != 3:
         raise ValueError("decode expects q, k [B,H,D], v [B,H,M]")
@@ -214,6 +225,16 @@ def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None):
     return dq, dk, dv
 
 
+def backward_noncausal(q, k, v, do):
+    B, H, N, D, M = _sizes(q, v)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = alloc_workspace(LA_OP_BWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
+    la_backward_noncausal(q, k, v, do, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
 def decode_step(q, k, v, s, z, y=None):
     """One RNN step: updates s, z in place and returns y."""
     if y is None:
@@ -240,6 +261,25 @@ class CausalLinearAttention(torch.autograd.Function):
 
 def causal_linear_attention(q, k, v):
     return CausalLinearAttention.apply(q, k, v)
+
+
+class NonCausalLinearAttention(torch.autograd.Function):
+    """Autograd wrapper of the non-causal form: forward and backward both run in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        ctx.save_for_backward(q, k, v)
+        return forward_noncausal(q, k, v)
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v = ctx.saved_tensors
+        return backward_noncausal(q, k, v, do.contiguous())
+
+
+def noncausal_linear_attention(q, k, v):
+    return NonCausalLinearAttention.apply(q, k, v)
 
 
 # ------------------------------------------------------------- timing hooks

@@ -115,14 +115,15 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 
 // Workspace regions (bytes) per operation.
 struct WsLayout {
-  size_t agg = 0, ckpt = 0, ragg = 0;
-  size_t bytes() const { return agg + ckpt + ragg; }
+  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0;
+  size_t bytes() const { return agg + ckpt + ragg + rpref; }
 };
 
 // fwd causal: aggregates and prefix states when there is more than one
 //   segment (the prefix states go to the caller's checkpoint when given and
 //   are only formed by the scan kernel);
 // fwd non-causal: aggregates and their scan (its last entry is the total);
+// bwd non-causal: both for the key side and for the reverse side;
 // bwd: aggregates and prefix states to recompute a missing checkpoint, and
 //   the reverse aggregates (scanned in place) when there is more than one
 //   segment.
@@ -144,6 +145,12 @@ WsLayout ws_layout(int op, const Plan& p) {
       w.agg = state_bytes(p, p.nseg);       // checkpoint recomputation only
       w.ckpt = state_bytes(p, p.nseg + 1);  // checkpoint recomputation only
       if (p.nseg > 1) w.ragg = state_bytes(p, p.nseg);
+      break;
+    case LA_OP_BWD_NONCAUSAL:  // key aggregates and their scan; reverse aggregates and their scan
+      w.agg = state_bytes(p, p.nseg);
+      w.ckpt = state_bytes(p, p.nseg + 1);
+      w.ragg = state_bytes(p, p.nseg);
+      w.rpref = state_bytes(p, p.nseg + 1);
       break;
     default:
       break;
@@ -375,6 +382,34 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
 }
 
 template <typename T, int D, int M>
+int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO, void* dQ,
+                       void* dK, void* dV, int N, void* ws, hipStream_t s) {
+  if (p.nseg == 0) return LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_BWD_NONCAUSAL, p);
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  float* pref = reinterpret_cast<float*>(region(ws, wl.agg));
+  float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
+  float* rpref = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+  const bool scan = use_scan(p);
+  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
+  if (st) return st;
+  if (scan) {
+    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s);
+    if (st) return st;
+  }
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  st = launch("nc_qr", la::k_nc_qr<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, (const float*)agg,
+              (const float*)(scan ? pref : nullptr), (T*)dQ, ragg, N, p.L, p.nseg);
+  if (st) return st;
+  if (scan) {
+    st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s);
+    if (st) return st;
+  }
+  return launch("nc_kv", la::k_nc_kv<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, (const float*)ragg,
+                (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg);
+}
+
+template <typename T, int D, int M>
 int decode_impl(long BH, const void* q, const void* k, const void* v, float* S, float* Z, void* y, hipStream_t s) {
   return launch("decode", la::k_decode<T, D, M>, dim3((unsigned)((BH + 3) / 4)), dim3(la::NT), s, (const T*)q,
                 (const T*)k, (const T*)v, S, Z, (T*)y, (int)BH);
@@ -408,12 +443,13 @@ const char* la_status_string(int status) {
 const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
-  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,decode,scan_states,scan_rev,state_copy";
+  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
+         "state_copy";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
   if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
-  if (op < LA_OP_FWD_CAUSAL || op > LA_OP_DECODE) return 0;
+  if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_NONCAUSAL) return 0;
   return ws_layout(op, make_plan(B, H, N, D, M)).bytes();
 }
 
@@ -507,6 +543,27 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const void* 
   if (st) return st;
   LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dQ, dK, dV, N, ws,
               (hipStream_t)stream);
+}
+
+int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, void* dQ, void* dK,
+                          void* dV, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  if (N == 0) return LA_OK;
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(LA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
+  const Plan p = make_plan(B, H, N, D, M);
+  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const size_t need = ws_layout(LA_OP_BWD_NONCAUSAL, p).bytes();
+  if (ws == nullptr || ws_bytes < need)
+    return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
+                   rng("V", V, bh * N * M * es, false), rng("dO", dO, bh * N * M * es, false),
+                   rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
+                   rng("dV", dV, bh * N * M * es, true), rng("ws", ws, need, true)});
+  if (st) return st;
+  LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, dQ, dK, dV, N, ws, (hipStream_t)stream);
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, float* S, float* Z, void* y, int B, int H, int D,

@@ -1082,6 +1082,249 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
   }
 }
 
+// ============================================================ non-causal B
+// Non-causal backward (reading notes on "Transformers are RNNs", section 3.2,
+// eq. 5-6; the causal backward's quotient rule with the masks removed): with
+// the totals S = sum_j phi(K_j) V_j^T, Z = sum_j phi(K_j) and, per query,
+// u_i = S dO_i, den_i = phi(Q_i).Z, O_i.dO_i = phi(Q_i).u_i / den_i,
+//   dphiQ_i = (u_i - Z (O_i.dO_i)) / den_i,
+//   R = sum_i phi(Q_i) g_i^T, r = sum_i c_i phi(Q_i)  (g_i = dO_i / den_i,
+//     c_i = -(O_i.dO_i) / den_i),
+//   dphiK_j = R V_j + r,  dV_j = R^T phi(K_j).
+// Totals come from entry nseg of a scanned prefix array `pref` when given,
+// else from summing all segment aggregates `agg` here.
+
+// Stage a state total (S then Z, row-major [d][m]) into planes and a float32 vector.
+template <int D, int M, int NP, int NTH>
+__device__ __forceinline__ void stage_total(Planes<NP, D, M>& sp, float* sz, float* sbuf, const float* pref,
+                                            const float* agg, int nseg) {
+  constexpr int SV = D * M + D;
+  const float* src;
+  if (pref) {
+    src = pref + (size_t)nseg * SV;
+  } else {
+    sum_states<D, M, NTH>(sbuf, nullptr, nullptr, agg, 0, nseg);
+    __syncthreads();
+    src = sbuf;
+  }
+  for (int e = 4 * threadIdx.x; e < SV; e += 4 * NTH) {
+    const float4 a = *reinterpret_cast<const float4*>(src + e);
+    if (e < D * M) {
+      const float x[4] = {a.x, a.y, a.z, a.w};
+      sp.put4(e / M, e % M, x);
+    } else {
+      *reinterpret_cast<float4*>(sz + (e - D * M)) = a;
+    }
+  }
+}
+
+// Query pass: dQ, and the reverse aggregates (R^T, r) of each segment.
+template <typename T, int D, int M>
+__global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* __restrict__ dO,
+                                               const float* __restrict__ agg, const float* __restrict__ pref,
+                                               T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg) {
+  using P = Prec<T>;
+  constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
+  constexpr int E = IO<T>::E;
+  __shared__ Planes<cmax(P::NQ, P::dR), CH, D> qt;  // phi(Q)
+  __shared__ Planes<P::NDO, CH, M> ot;               // dO
+  __shared__ Planes<P::NG, CH, M + 16> gt;           // [g | c | 0]
+  __shared__ Planes<P::NS, D, M> sp;                 // S total, [d][m]
+  __shared__ alignas(16) float q32[CH][D + 4];       // phi(Q), float32
+  __shared__ alignas(16) float sZ[D];                // Z total
+
+  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int t0 = seg * L, t1 = min(N, t0 + L);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* dOh = dO + (size_t)bh * N * M;
+  static_assert(sizeof(gt.v) >= SV * sizeof(float), "g planes too small to hold a float32 state");
+  stage_total<D, M, P::NS, NT>(sp, sZ, reinterpret_cast<float*>(&gt.v[0][0][0]),
+                               pref ? pref + (size_t)bh * (nseg + 1) * SV : nullptr,
+                               agg + (size_t)bh * nseg * SV, nseg);
+  __syncthreads();
+  gt.zero_cols(M + 1, M + 16);
+
+  f32x4_t acc[NTW], accr = zero4();  // R^T layout; accr[0] on lanes g = 0 is r[16db + r16]
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) acc[k] = zero4();
+
+  RowBuf<T, CH, D> bq[2];
+  RowBuf<T, CH, M> bd[2];
+  auto fetch = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& d_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    if (nv > 0) {
+      q_.load(Qh + (size_t)c0 * D, nv);
+      d_.load(dOh + (size_t)c0 * M, nv);
+    }
+  };
+  auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& d_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    __syncthreads();
+    q_.template stage_phi<cmax(P::NQ, P::dR), CH, D, 8, D + 4>(qt, nv, &q32[0][0]);
+    d_.stage_values(ot);
+    fetch(q_, d_, c0 + 2 * CH);
+    __syncthreads();
+    {
+      const int il = 16 * w + r16;
+      const bool row_ok = il < nv;
+      Frag<P::U1_b> dof[M / 32];
+#pragma unroll
+      for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<P::U1_b>(il, 32 * s, g);
+      f32x4_t U[DB];
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
+        f32x4_t u = zero4();
+#pragma unroll
+        for (int s = 0; s < M / 32; ++s)
+          mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
+        U[d0] = u;  // S dO_i   [d][i]
+      }
+      float pu = 0.f, pz = 0.f, qv[DB][4], zv[DB][4];
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
+        const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
+        qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
+        zv[d0][0] = z4.x; zv[d0][1] = z4.y; zv[d0][2] = z4.z; zv[d0][3] = z4.w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pu += qv[d0][r] * U[d0][r];
+          pz += qv[d0][r] * zv[d0][r];
+        }
+      }
+      pu = sum_over_g(pu);
+      pz = sum_over_g(pz);
+      const float invz = row_ok ? 1.f / pz : 0.f;
+      const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
+      if (row_ok) {
+#pragma unroll
+        for (int d0 = 0; d0 < DB; ++d0) {
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - zv[d0][r] * odo) * invz * dphi_from_phi(qv[d0][r]);
+          IO<T>::store4(dQ + (size_t)bh * N * D + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < M / 4; mm += 4) {
+        float dv[4];
+        ot.get4(il, g * (M / 4) + mm, dv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dv[q] *= invz;
+        gt.put4(il, g * (M / 4) + mm, dv);
+      }
+      if (g == 0) gt.put1(il, M, -odo * invz);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < CH / 32; ++s) {
+      const Frag<P::dR> qb = qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16);
+#pragma unroll
+      for (int k = 0; k < NTW; ++k) {
+        const int mb = (w + 4 * k) / DB;
+        mmaf<P::dR, P::dR>(acc[k], gt.template tfrag<P::dR>(32 * s, 16 * mb, g, r16), qb);
+      }
+      if (zw) mmaf<P::dR, P::dR>(accr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
+    }
+  };
+  fetch(bq[0], bd[0], t0);
+  fetch(bq[1], bd[1], t0 + CH);
+  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
+    chunk(bq[0], bd[0], c0);
+    if (c0 + CH < t1) chunk(bq[1], bd[1], c0 + CH);
+  }
+  float* out = ragg + ((size_t)bh * nseg + seg) * SV;
+  store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
+  if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
+}
+
+// Key pass: dK = (R V_j + r) phi'(K_j), dV = R^T phi(K_j) with the totals R, r.
+template <typename T, int D, int M>
+__global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* __restrict__ V,
+                                               const float* __restrict__ ragg, const float* __restrict__ rpref,
+                                               T* __restrict__ dK, T* __restrict__ dV, int N, int L, int nseg) {
+  using P = Prec<T>;
+  constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
+  constexpr int NKT = P::VR, NVT = cmax(P::KR_b, 1);
+  __shared__ Planes<cmax(NKT, 1), CH, D> kt;  // phi(K)
+  __shared__ Planes<cmax(P::NV, NVT), CH, M> vt;
+  __shared__ Planes<P::NR, D, M> rp;          // R total, [d][m]
+  __shared__ alignas(16) float k32[CH][D + 4];
+  __shared__ alignas(16) float sr[D];         // r total
+
+  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int t0 = seg * L, t1 = min(N, t0 + L);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * M;
+  static_assert(sizeof(kt.v) >= SV * sizeof(float), "key planes too small to hold a float32 state");
+  stage_total<D, M, P::NR, NT>(rp, sr, reinterpret_cast<float*>(&kt.v[0][0][0]),
+                               rpref ? rpref + (size_t)bh * (nseg + 1) * SV : nullptr,
+                               ragg + (size_t)bh * nseg * SV, nseg);
+
+  RowBuf<T, CH, D> bk[2];
+  RowBuf<T, CH, M> bv[2];
+  auto fetch = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    if (nv > 0) {
+      k_.load(Kh + (size_t)c0 * D, nv);
+      v_.load(Vh + (size_t)c0 * M, nv);
+    }
+  };
+  auto chunk = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    __syncthreads();
+    k_.template stage_phi<cmax(NKT, 1), CH, D, 8, D + 4>(kt, nv, &k32[0][0]);
+    v_.stage_values(vt);
+    fetch(k_, v_, c0 + 2 * CH);
+    __syncthreads();
+    const int jl = 16 * w + r16;
+    const bool row_ok = jl < nv;
+    Frag<NVT> vfr[M / 32];
+#pragma unroll
+    for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
+#pragma unroll
+    for (int d0 = 0; d0 < DB; ++d0) {
+      f32x4_t a = zero4();
+#pragma unroll
+      for (int s = 0; s < M / 32; ++s)
+        mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
+      if (row_ok) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
+        const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dphi_from_phi(kv[r]);
+        IO<T>::store4(dK + (size_t)bh * N * D + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
+      }
+    }
+    Frag<NKT> kfr[D / 32];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      f32x4_t a = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
+      if (row_ok) {
+        float o[4] = {a[0], a[1], a[2], a[3]};
+        IO<T>::store4(dV + (size_t)bh * N * M + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+      }
+    }
+  };
+  fetch(bk[0], bv[0], t0);
+  fetch(bk[1], bv[1], t0 + CH);
+  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
+    chunk(bk[0], bv[0], c0);
+    if (c0 + CH < t1) chunk(bk[1], bv[1], c0 + CH);
+  }
+}
+
 // ================================================================= decode
 // One RNN step per head (eq. 18-20): S += phi(k) v^T, Z += phi(k),
 // y = phi(q)^T S / phi(q)^T Z.  One wavefront per head streams the head's

@@ -115,6 +115,21 @@ def test_noncausal_and_backward_validation(lib):
     assert lib.la_backward_causal(*args, 2, 2, 0, 32, 32, 0, None, 0, None) == OK
 
 
+def test_noncausal_backward_validation(lib):
+    ws = lib.la_workspace_size(4, 2, 2, 100, 32, 32, 0)
+    assert ws > 0
+    args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7)]
+    a = list(args)
+    a[4] = None
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, addr(20), ws, None) == NULL
+    a = list(args)
+    a[5] = addr(1)  # dK on top of Q
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, addr(20), ws, None) == ALIAS
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 32, 32, 0, addr(20), ws - 1, None) == WORKSPACE
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 48, 32, 0, addr(20), ws, None) == UNSUPPORTED
+    assert lib.la_backward_noncausal(*args, 2, 2, 0, 32, 32, 0, None, 0, None) == OK
+
+
 def test_decode_validation(lib):
     assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), None, 2, 2, 64, 64, 1, None) == NULL
     assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, None) == ALIAS
@@ -148,6 +163,8 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     # backward: room to recompute the checkpoint, plus reverse aggregates
     bwd = _al(B * H * nseg * sv * 4) + _al(B * H * (nseg + 1) * sv * 4) + (0 if nseg == 1 else _al(B * H * nseg * sv * 4))
     assert lib.la_workspace_size(2, B, H, N, D, M, 0) == bwd
+    # non-causal backward: key aggregates + scan, reverse aggregates + scan
+    assert lib.la_workspace_size(4, B, H, N, D, M, 0) == 2 * (agg + pref)
     assert lib.la_workspace_size(9, B, H, N, D, M, 0) == 0
 
 

@@ -311,3 +311,106 @@ def test_decode_workload_sampled():
     assert rowerr(host(ys).transpose(1, 0, 2)[None], yo) <= 2e-2
     assert rowerr(host(s)[bi, hi][None], sn) <= 1e-4
     assert rowerr(host(z)[bi, hi][None], zn, False) <= 1e-4
+
+
+# ------------------------------------------------ non-causal backward
+def nc_cancel_scales(q, k, v, do):
+    """Per-row sizes of the terms the non-causal gradients cancel: |S g_i * phi'(Q_i)|_inf for dQ and
+    |R V_j * phi'(K_j)|_inf for dK (S, R the totals of the reading notes' eq. 5-6 and its reverse sum)."""
+    pq, pk = pins.phi_lib(q), pins.phi_lib(k)
+    v64, do64 = v.astype(np.float64), do.astype(np.float64)
+    S = np.einsum("bhnd,bhnm->bhdm", pk, v64)
+    den = np.einsum("bhnd,bhd->bhn", pq, pk.sum(axis=2))
+    g = do64 / den[..., None]
+    R = np.einsum("bhnd,bhnm->bhdm", pq, g)
+    uq = np.einsum("bhdm,bhnm->bhnd", S, g) * np.minimum(pq, 1.0)
+    uk = np.einsum("bhdm,bhnm->bhnd", R, v64) * np.minimum(pk, 1.0)
+    return np.abs(uq).max(-1), np.abs(uk).max(-1)
+
+
+def check_backward_noncausal(q, k, v, do, dtype, tol=None):
+    tol = TOL[dtype] if tol is None else tol
+    dq, dk, dv = binding.backward_noncausal(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_noncausal(q, k, v, do)
+    dq, dk, dv = host(dq), host(dk), host(dv)
+    sq, sk = nc_cancel_scales(q, k, v, do)
+    if q.shape[2] == 1:
+        # N = 1: O_1 = V_1, so dQ_1 and dK_1 are exact zeros.  The library forms them through the totals
+        # S = phi(K) V^T and R = phi(Q) g^T, whose elements are rounded before the products with g and V,
+        # so the attainable error is the dot-product bound sum_m |S_dm| |g_m| (resp. |R_dm| |V_m|), not the
+        # size of the (possibly cancelling) dot product itself.  The bar is the one the causal first-token
+        # query gradient meets: a residual below kappa of that bound.
+        kappa = {F32: 1e-5, BF16: 1e-3}[dtype]
+        pq, pk = pins.phi_lib(q[:, :, 0]), pins.phi_lib(k[:, :, 0])
+        v1, do1 = v[:, :, 0].astype(np.float64), do[:, :, 0].astype(np.float64)
+        den = (pq * pk).sum(-1, keepdims=True)
+        bq = (pk * (np.abs(v1) * np.abs(do1)).sum(-1, keepdims=True) / den * np.minimum(pq, 1.0)).max(-1)
+        bk = (pq * (np.abs(do1) * np.abs(v1)).sum(-1, keepdims=True) / den * np.minimum(pk, 1.0)).max(-1)
+        errs = {"dQ": float((np.abs(dq[:, :, 0]).max(-1) / bq).max()) * tol / kappa,
+                "dK": float((np.abs(dk[:, :, 0]).max(-1) / bk).max()) * tol / kappa,
+                "dV": rowerr(dv, rv)}
+    else:
+        errs = {"dQ": rowerr(dq, rq, row_floor=CANCEL_FLOOR * sq), "dK": rowerr(dk, rk, row_floor=CANCEL_FLOOR * sk),
+                "dV": rowerr(dv, rv)}
+    assert max(errs.values()) <= tol, errs
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 65, 200, 784])
+def test_backward_noncausal_sweep(N, D, M, dtype):
+    q, k, v = _qkv(2, 3, N, D, M, dtype, 9000 + N)
+    do = inputs.gaussian((2, 3, N, M), 9999, 1.0, dtype)
+    check_backward_noncausal(q, k, v, do, dtype)
+
+
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_backward_noncausal_segment_invariance(chunks):
+    """Segment lengths change only the summation order of the totals."""
+    q, k, v = _qkv(2, 2, 700, 64, 32, F32, 9100)
+    do = inputs.gaussian((2, 2, 700, 32), 9104, 1.0, F32)
+    prev = binding.set_segment_chunks(chunks)
+    try:
+        check_backward_noncausal(q, k, v, do, F32)
+    finally:
+        binding.set_segment_chunks(prev)
+
+
+def test_backward_noncausal_mnist_shape():
+    """B=16 H=8 N=784 D=M=32 float32 (the MNIST-shaped layer, non-causal), every head."""
+    w = inputs.MNIST
+    q, k, v = w.qkv()
+    check_backward_noncausal(q, k, v, w.grad_out(), F32)
+
+
+def test_backward_noncausal_long_shape_sampled():
+    """B=1 H=16 N=65536 D=M=64 bf16: the whole problem on the GPU, the oracle on two heads."""
+    w = inputs.LONG
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    dq, dk, dv = binding.backward_noncausal(dev(q, BF16), dev(k, BF16), dev(v, BF16), dev(do, BF16))
+    torch.cuda.synchronize()
+    hs = [0, 11]
+    sub = lambda a: a[:, hs]  # noqa: E731
+    rq, rk, rv = oracle.backward_noncausal(sub(q), sub(k), sub(v), sub(do))
+    sq, sk = nc_cancel_scales(sub(q), sub(k), sub(v), sub(do))
+    errs = {"dQ": rowerr(sub(host(dq)), rq, row_floor=CANCEL_FLOOR * sq),
+            "dK": rowerr(sub(host(dk)), rk, row_floor=CANCEL_FLOOR * sk), "dV": rowerr(sub(host(dv)), rv)}
+    assert max(errs.values()) <= TOL[BF16], errs
+
+
+def test_noncausal_autograd_wrapper():
+    """torch.autograd through the library's non-causal forward and backward equals the oracle."""
+    q, k, v = _qkv(2, 2, 150, 32, 64, F32, 9200)
+    do = inputs.gaussian((2, 2, 150, 64), 9204, 1.0, F32)
+    Q, K, V = (dev(a).requires_grad_(True) for a in (q, k, v))
+    out = binding.noncausal_linear_attention(Q, K, V)
+    out.backward(dev(do))
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_noncausal(q, k, v, do)
+    sq, sk = nc_cancel_scales(q, k, v, do)
+    errs = [rowerr(host(Q.grad), rq, row_floor=CANCEL_FLOOR * sq), rowerr(host(K.grad), rk, row_floor=CANCEL_FLOOR * sk),
+            rowerr(host(V.grad), rv), rowerr(host(out), oracle.forward_noncausal(q, k, v))]
+    assert max(errs) <= 1e-4, errs
