@@ -6,7 +6,9 @@ whole hot path over one batch: causal forward (phi prologue, intra-chunk
 blocks, state carry, epilogue), causal backward, and the non-causal forward
 at the same shape.  Other workloads (--workload): cifar (16 independent layers
 of B=4 H=8 N=3072 D=M=32, bf16, sigma 0.5, forward + backward each), long
-(B=1 H=16 N=65536 D=M=64, bf16, sigma 1/8, forward + backward), decode (one
+(B=1 H=16 N=65536 D=M=64, bf16, sigma 1/8, forward + backward), speech (9
+independent non-causal layers of B=16 H=6 N=800 D=M=32, float32, non-causal
+forward + backward each), decode (one
 step = one la_decode_step on B=256 H=16 D=M=64 after a 512-token prefill),
 small (B=1 H=1 N=64 D=M=32 float32 causal forward).
 
@@ -41,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "decode", "small"])
+    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "speech", "decode", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
@@ -70,8 +72,7 @@ class Step:
         self.torch, self.b, self.inputs = torch, binding, inputs
         self.args = args
         wl = args.workload
-        self.w = {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "decode": inputs.DECODE,
-                  "small": inputs.SMALL}[wl]
+        self.w = WORKLOADS(inputs)[wl]
         w = self.w
         dt = torch.float32 if w.dtype == inputs.F32 else torch.bfloat16
         self.dt = dt
@@ -82,14 +83,14 @@ class Step:
         if wl == "decode":
             self._init_decode(dev)
             return
-        if wl == "cifar":
+        if wl in ("cifar", "speech"):
             nsets = w.layers  # one independent input set per layer
         elif wl == "mnist":
             nsets = 6  # rotate batches so successive steps do not hit the 256 MB last-level cache
         else:
             nsets = 1
         for i in range(nsets):
-            if wl == "cifar":
+            if wl in ("cifar", "speech"):
                 q, k, v = w.qkv(layer=i)
                 do = w.grad_out(layer=i)
             elif i == 0:
@@ -108,6 +109,8 @@ class Step:
         self.ws_f = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, code, "cuda")
         self.ws_b = binding.alloc_workspace(binding.LA_OP_BWD_CAUSAL, B, H, N, D, M, code, "cuda")
         self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+        if wl == "speech":
+            self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
         self.i = 0
 
     def _extra_set(self, i):
@@ -158,6 +161,11 @@ class Step:
             for (q, k, v, do) in self.sets:
                 self._fwd_bwd(q, k, v, do)
             return
+        if wl == "speech":
+            for (q, k, v, do) in self.sets:
+                b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n)
+                b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb)
+            return
         q, k, v, do = self.sets[self.i % len(self.sets)]
         self.i += 1
         if wl == "small":
@@ -173,6 +181,11 @@ class Step:
         b.la_backward_causal(q, k, v, self.o, self.den, do, self.dq, self.dk, self.dv, ckpt=self.ck, ws=self.ws_b)
 
 
+def WORKLOADS(inputs):
+    return {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "speech": inputs.SPEECH,
+            "decode": inputs.DECODE, "small": inputs.SMALL}
+
+
 # ---------------------------------------------------- algorithmic figures
 def kernel_bytes(name, w, s):
     """Algorithmic HBM bytes per launch: the tensors the kernel must read or write by its function
@@ -185,6 +198,8 @@ def kernel_bytes(name, w, s):
         "fwd_noncausal": (D + M) * s,            # read Q; write O
         "seg_rstate": (D + 2 * M) * s + 4,       # read Q, O, dO, den
         "bwd_causal": (4 * D + 3 * M) * s,       # read Q, K, V, dO; write dQ, dK, dV
+        "nc_qr": (2 * D + M) * s,                # read Q, dO; write dQ
+        "nc_kv": (2 * D + 2 * M) * s,            # read K, V; write dK, dV
     }
     if name == "decode":
         return w.B * w.H * (2 * D * M * 4 + 2 * D * 4 + (2 * D + 2 * M) * s)
@@ -228,7 +243,7 @@ def traffic_from_profiles(kernel, workload):
 # ------------------------------------------------------ profile summaries
 KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_seg_state<", "seg_state"),
                ("k_scan_states<", "scan_states"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
-               ("k_fwd_fused<", "fwd_causal"))
+               ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"))
 
 
 def kernel_tag(full_name):
@@ -280,10 +295,9 @@ def summarize_traffic(args):
     copy_bytes = 1024 * (1 << 20)  # bench.py --copy-only 1024: 1 GiB read and 1 GiB written per launch
     f_read = copy_bytes / (cf[copy_key] * 1024.0)
     f_write = copy_bytes / (cw[copy_key] * 1024.0)
-    wl = {"mnist": "MNIST", "cifar": "CIFAR", "long": "LONG", "decode": "DECODE", "small": "SMALL"}[args.label]
     from linear_rnn_layers_amd import inputs
 
-    w = getattr(inputs, wl)
+    w = WORKLOADS(inputs)[args.label]
     s = 4 if w.dtype == "f32" else 2
     os.makedirs(PROFILES, exist_ok=True)
     md = os.path.join(PROFILES, f"{args.label}_traffic.md")
@@ -324,10 +338,9 @@ def summarize_mfma(args):
     dur = {}
     for r in csv.DictReader(open(stats_csv)):
         dur[kernel_tag(r["Name"])] = float(r["AverageNs"]) * 1e-9
-    wl = {"mnist": "MNIST", "cifar": "CIFAR", "long": "LONG", "decode": "DECODE", "small": "SMALL"}[args.label]
     from linear_rnn_layers_amd import inputs
 
-    w = getattr(inputs, wl)
+    w = WORKLOADS(inputs)[args.label]
     md = os.path.join(PROFILES, f"{args.label}_mfma.md")
     with open(md, "w") as f:
         f.write(f"# MFMA utilisation from rocprofv3 counters: {args.label} workload\n\n")
@@ -404,14 +417,22 @@ def cpu_baseline(args, w):
                 "kind": "oracle", "sample": f"{steps} steps on {nheads} of {w.B * w.H} heads, scaled to all heads"}
     # token workloads: run the oracle's passes of one step on a subset of heads until >= 10 s
     B, H, N = w.B, w.H, w.N
-    nb = {"mnist": 4, "cifar": 1, "long": 1, "small": 1}[wl]
-    nh = {"mnist": H, "cifar": 8, "long": 2, "small": 1}[wl]
-    n = {"mnist": N, "cifar": N, "long": 16384, "small": N}[wl]
+    nb = {"mnist": 4, "cifar": 1, "long": 1, "speech": 4, "small": 1}[wl]
+    nh = {"mnist": H, "cifar": 8, "long": 2, "speech": H, "small": 1}[wl]
+    n = {"mnist": N, "cifar": N, "long": 16384, "speech": N, "small": N}[wl]
     q, k, v = (a[:nb, :nh, :n] for a in w.qkv(n=n))
     do = w.grad_out(n=n)[:nb, :nh, :n]
     reps = 0
     t = time.perf_counter()
     while True:
+        if wl == "speech":
+            oracle.forward_noncausal(q, k, v)
+            oracle.backward_noncausal(q, k, v, do)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= 10.0 or reps >= 1000:
+                break
+            continue
         oracle.forward_causal(q, k, v)
         if wl != "small":
             oracle.backward_causal(q, k, v, do)
@@ -422,11 +443,11 @@ def cpu_baseline(args, w):
         if el >= 10.0 or reps >= 1000:
             break
     head_tokens_per_s = reps * nb * nh * n / el
-    layers = w.layers if wl == "cifar" else 1
+    layers = w.layers if wl in ("cifar", "speech") else 1
     value = head_tokens_per_s / (H * layers)  # model tokens/s: every token goes through H heads (x layers)
     return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} x one step's passes on {nb}x{nh} of {B}x{H} sequences, {n} of {N} tokens"
-                      f"{', scaled to 16 layers' if wl == 'cifar' else ''}"}
+                      f"{f', scaled to {layers} layers' if layers > 1 else ''}"}
 
 
 # -------------------------------------------------------------------- main
@@ -499,6 +520,9 @@ def main():
     if args.workload == "decode":
         metric, unit = "decode steps/s", "steps/s"
         value = args.steps / el
+    elif args.workload == "speech":
+        metric, unit = "non-causal linear-attn fwd+bwd tokens/s", "tokens/s"
+        value = w.B * w.N * args.steps / el
     else:
         metric, unit = "causal linear-attn fwd+bwd tokens/s", "tokens/s"
         value = w.B * w.N * args.steps / el
@@ -533,6 +557,9 @@ def main():
         cfg["layers"] = 16
     elif args.workload == "long":
         cfg["step"] = "causal forward + backward"
+    elif args.workload == "speech":
+        cfg["step"] = "9 layers x (non-causal forward + backward)"
+        cfg["layers"] = 9
     elif args.workload == "decode":
         cfg["step"] = "one decode step of all B*H heads after a 512-token prefill"
     else:

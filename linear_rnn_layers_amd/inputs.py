@@ -14,8 +14,8 @@ Recipe (every array):
 
 The workloads mirror the shapes of the experiments on the pages (MNIST-sized
 sequences of 784 pixels with 8 heads of 32 dimensions, CIFAR-10-sized
-sequences of 3072 pixels, a 2**16-long synthetic sequence, batched RNN
-decoding); the datasets themselves are not used, Gaussian inputs stand in.
+sequences of 3072 pixels, a 2**16-long synthetic sequence, a bidirectional
+speech encoder over 800-frame utterances, batched RNN decoding); the datasets themselves are not used, Gaussian inputs stand in.
 """
 from __future__ import annotations
 
@@ -98,14 +98,18 @@ class Workload:
         return self.B * self.N
 
 
-# The five workloads.  Seeds follow one fixed scheme so every run of every
+# The workloads.  Seeds follow one fixed scheme so every run of every
 # test or benchmark sees the same numbers.
 SMALL = Workload("causal-fwd-b1h1n64d32-f32", 1, 1, 64, 32, 32, F32, 1.0, (101, 102, 103, 104))
 MNIST = Workload("mnist-layer-b16h8n784d32-f32", 16, 8, 784, 32, 32, F32, 1.0, (201, 202, 203, 204))
 CIFAR = Workload("cifar-16layers-b4h8n3072d32-bf16", 4, 8, 3072, 32, 32, BF16, 0.5, (3000, 3001, 3002, 3003),
                  layers=16)
 LONG = Workload("long-b1h16n65536d64-bf16", 1, 16, 65536, 64, 64, BF16, 1.0 / 8.0, (401, 402, 403, 404))
+# Bidirectional speech encoder: 9 layers of 6 heads x 32 over the average utterance length of 800 frames
+# (the pages give no batch size; 16 as in the MNIST workload).
+SPEECH = Workload("speech-encoder-9layers-b16h6n800d32-f32", 16, 6, 800, 32, 32, F32, 1.0, (6000, 6001, 6002, 6003),
+                  layers=9)
 DECODE = Workload("decode-b256h16d64-4096steps-bf16", 256, 16, 512, 64, 64, BF16, 1.0, (501, 502, 503, 504),
                   steps=4096)
 
-WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, DECODE)}
+WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, DECODE)}
