@@ -49,8 +49,8 @@ def _configure(lib):
     lib.orc_forward_causal.argtypes = [dp] * 9 + [L] * 5
     lib.orc_forward_causal_parallel.argtypes = [dp] * 5 + [L] * 5
     lib.orc_forward_noncausal.argtypes = [dp] * 4 + [L] * 5
-    lib.orc_numerator_backward.argtypes = [dp] * 7 + [L] * 3
-    lib.orc_backward_causal.argtypes = [dp] * 9 + [L] * 5
+    lib.orc_numerator_backward.argtypes = [dp] * 9 + [L] * 3
+    lib.orc_backward_causal.argtypes = [dp] * 13 + [L] * 5
     lib.orc_backward_noncausal.argtypes = [dp] * 7 + [L] * 5
     lib.orc_decode_step.argtypes = [dp] * 6 + [L] * 4
     lib.orc_num_threads.restype = ctypes.c_int
@@ -127,32 +127,42 @@ def forward_noncausal(q, k, v):
     return o
 
 
-def numerator_backward(p, kf, vb, g):
-    """eq. 13-15 for one head on feature-mapped inputs: returns (dP, dKf, dVb)."""
+def numerator_backward(p, kf, vb, g, rn=None, return_r0=False):
+    """eq. 13-15 for one head on feature-mapped inputs: returns (dP, dKf, dVb), and the gradient R0 of the
+    initial state when return_r0 (rn: the final state's upstream gradient [C, Mb], None for zero)."""
     p, kf, vb, g = _f64(p), _f64(kf), _f64(vb), _f64(g)
     N, C = p.shape
     Mb = vb.shape[1]
+    rn = None if rn is None else _f64(rn)
     dp_ = np.empty((N, C))
     dk = np.empty((N, C))
     dv = np.empty((N, Mb))
-    _load().orc_numerator_backward(_ptr(p), _ptr(kf), _ptr(vb), _ptr(g), _ptr(dp_), _ptr(dk), _ptr(dv),
-                                   N, C, Mb)
-    return dp_, dk, dv
+    r0 = np.empty((C, Mb))
+    _load().orc_numerator_backward(_ptr(p), _ptr(kf), _ptr(vb), _ptr(g), _ptr(rn), _ptr(dp_), _ptr(dk), _ptr(dv),
+                                   _ptr(r0), N, C, Mb)
+    return (dp_, dk, dv, r0) if return_r0 else (dp_, dk, dv)
 
 
-def backward_causal(q, k, v, do, s0=None, z0=None):
-    """Gradients of sum(dO * O) w.r.t. raw Q, K, V.  Returns (dQ, dK, dV)."""
+def backward_causal(q, k, v, do, s0=None, z0=None, dsn=None, dzn=None, state_grad=False):
+    """Gradients of sum(dO * O) + sum(dSN * S_N) + sum(dZN * Z_N) w.r.t. raw Q, K, V (and, with state_grad,
+    the initial state).  Returns (dQ, dK, dV) or (dQ, dK, dV, dS0, dZ0)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, D = q.shape
     M = v.shape[-1]
     s0 = None if s0 is None else _f64(s0)
     z0 = None if z0 is None else _f64(z0)
+    if (dsn is None) != (dzn is None):
+        raise ValueError("dsn and dzn go together")
+    dsn = None if dsn is None else _f64(dsn)
+    dzn = None if dzn is None else _f64(dzn)
     dq = np.empty((B, H, N, D))
     dk = np.empty((B, H, N, D))
     dv = np.empty((B, H, N, M))
-    _load().orc_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dq), _ptr(dk),
-                                _ptr(dv), B, H, N, D, M)
-    return dq, dk, dv
+    ds0 = np.empty((B, H, D, M)) if state_grad else None
+    dz0 = np.empty((B, H, D)) if state_grad else None
+    _load().orc_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dsn), _ptr(dzn),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds0), _ptr(dz0), B, H, N, D, M)
+    return (dq, dk, dv, ds0, dz0) if state_grad else (dq, dk, dv)
 
 
 def backward_noncausal(q, k, v, do):

@@ -197,12 +197,22 @@ void orc_forward_noncausal(const double *Q, const double *K, const double *V,
  *   eq. 14: dKf_i = R_i Vb_i,     R_i = sum_{j>=i} P_j G_j^T     (reverse sum)
  *   eq. 15: dVb_i = R_i^T Kf_i.
  * The two sums are accumulated token by token in opposite directions.
+ *
+ * State gradients.  The state after the last token, S_N = S_0 +
+ * sum_j Kf_j Vb_j^T, may itself feed the loss with upstream gradient RN
+ * [C,Mb] (NULL: zero).  Every term Kf_j Vb_j^T is part of S_N, so RN is the
+ * starting value of the reverse sum: R_i = RN + sum_{j>=i} P_j G_j^T.  The
+ * initial state S_0 is part of every S_i and of S_N, so its gradient is the
+ * reverse sum carried through token 1, R0 = RN + sum_j P_j G_j^T (output when
+ * R0 is not NULL; equal to RN for N = 0).
  */
 void orc_numerator_backward(const double *P, const double *Kf, const double *Vb,
-                            const double *G, double *dP, double *dKf,
-                            double *dVb, long N, long C, long Mb) {
+                            const double *G, const double *RN, double *dP,
+                            double *dKf, double *dVb, double *R0, long N,
+                            long C, long Mb) {
   double *S = (double *)calloc((size_t)(C * Mb), sizeof(double));
   double *R = (double *)calloc((size_t)(C * Mb), sizeof(double));
+  if (RN) memcpy(R, RN, (size_t)(C * Mb) * sizeof(double));
   for (long i = 0; i < N; ++i) { /* forward cumulative sum, eq. 13 */
     for (long c = 0; c < C; ++c)
       for (long m = 0; m < Mb; ++m) S[c * Mb + m] += Kf[i * C + c] * Vb[i * Mb + m];
@@ -226,6 +236,7 @@ void orc_numerator_backward(const double *P, const double *Kf, const double *Vb,
       dVb[i * Mb + m] = acc;
     }
   }
+  if (R0) memcpy(R0, R, (size_t)(C * Mb) * sizeof(double));
   free(S);
   free(R);
 }
@@ -233,19 +244,26 @@ void orc_numerator_backward(const double *P, const double *Kf, const double *Vb,
 /*
  * Full causal backward: gradients of L = sum(dO * O) with respect to the raw
  * Q, K, V, where O is the causal forward of eq. 12 started from (S0, Z0)
- * (both may be NULL: zero state).  Steps:
+ * (both may be NULL: zero state).  The loss may also depend on the final
+ * state (S_N, Z_N) of eq. 10-11 with upstream gradients dSN [B,H,D,M],
+ * dZN [B,H,D] (both or neither, NULL: zero); then dS0 [B,H,D,M] and
+ * dZ0 [B,H,D] (both or neither, may be NULL) receive the gradient with
+ * respect to the initial state.  Steps:
  *  1. forward recurrence (eq. 10-12) for den_i and O_i;
  *  2. quotient rule: d num_i = dO_i / den_i, d den_i = -(dO_i . O_i) / den_i;
  *  3. eq. 13-15 on the augmented values Vbar = [V, 1] with upstream
- *     [d num, d den] (the denominator is the numerator of a ones column);
- *     an initial state contributes S0 G_i to the phi(Q) gradient (it is the
- *     j = 0 term of the forward sum of eq. 13);
+ *     [d num, d den] (the denominator is the numerator of a ones column, and
+ *     Z is the state of that column, so [S | Z] is the augmented state and
+ *     [dSN | dZN] its final gradient); an initial state contributes S0 G_i to
+ *     the phi(Q) gradient (it is the j = 0 term of the forward sum of
+ *     eq. 13), and receives the reverse sum carried through token 1;
  *  4. chain rule through phi: dQ = dphiQ * phi'(Q), dK = dphiK * phi'(K).
  */
 void orc_backward_causal(const double *Q, const double *K, const double *V,
                          const double *dO, const double *S0, const double *Z0,
-                         double *dQ, double *dK, double *dV, long B, long H,
-                         long N, long D, long M) {
+                         const double *dSN, const double *dZN, double *dQ,
+                         double *dK, double *dV, double *dS0, double *dZ0,
+                         long B, long H, long N, long D, long M) {
   long BH = B * H;
   long Mb = M + 1;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -261,6 +279,13 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
     double *dP = (double *)malloc((size_t)(N * D) * sizeof(double));
     double *dKf = (double *)malloc((size_t)(N * D) * sizeof(double));
     double *dVb = (double *)malloc((size_t)(N * Mb) * sizeof(double));
+    double *RN = (double *)calloc((size_t)(D * Mb), sizeof(double));
+    double *R0 = (double *)malloc((size_t)(D * Mb) * sizeof(double));
+    if (dSN)
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) RN[d * Mb + m] = dSN[bh * D * M + d * M + m];
+        RN[d * Mb + M] = dZN[bh * D + d];
+      }
     /* 1. forward pass of this head */
     orc_forward_causal(q, k, v, S0 ? S0 + bh * D * M : NULL,
                        Z0 ? Z0 + bh * D : NULL, O, den, NULL, NULL, 1, 1, N, D, M);
@@ -279,7 +304,12 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
       Vb[i * Mb + M] = 1.0;
       G[i * Mb + M] = -dot / den[i];
     }
-    orc_numerator_backward(P, Kf, Vb, G, dP, dKf, dVb, N, D, Mb);
+    orc_numerator_backward(P, Kf, Vb, G, RN, dP, dKf, dVb, R0, N, D, Mb);
+    if (dS0)
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) dS0[bh * D * M + d * M + m] = R0[d * Mb + m];
+        dZ0[bh * D + d] = R0[d * Mb + M];
+      }
     if (S0 || Z0) { /* initial state: the j = 0 term of eq. 13's sum */
       for (long i = 0; i < N; ++i)
         for (long d = 0; d < D; ++d) {
@@ -307,6 +337,8 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
     free(dP);
     free(dKf);
     free(dVb);
+    free(RN);
+    free(R0);
   }
 }
 

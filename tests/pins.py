@@ -60,6 +60,26 @@ def brute_noncausal_grad(q, k, v, do):
     return tuple(t.grad.numpy() for t in ts)
 
 
+def brute_causal_state_grad(q, k, v, s0, z0, do, dsn, dzn):
+    """Gradients of sum(dO * O) + sum(dSN * S_N) + sum(dZN * Z_N) with respect to Q, K, V, S0, Z0, by
+    PyTorch autograd in float64 (library elu), where O is eq. 8's masked quotient with the initial state
+    added to both sums and S_N = S0 + sum_j phi(K_j) V_j^T, Z_N = Z0 + sum_j phi(K_j)."""
+    ts = [torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True) for a in (q, k, v, s0, z0)]
+    tq, tk, tv, ts0, tz0 = ts
+    pq = torch.nn.functional.elu(tq, alpha=1.0) + 1.0
+    pk = torch.nn.functional.elu(tk, alpha=1.0) + 1.0
+    n = tq.shape[-2]
+    sim = (pq @ pk.transpose(-1, -2)) * torch.tril(torch.ones((n, n), dtype=torch.float64))
+    num = sim @ tv + pq @ ts0
+    den = sim.sum(dim=-1) + (pq * tz0.unsqueeze(-2)).sum(dim=-1)
+    out = num / den.unsqueeze(-1)
+    s_n = ts0 + pk.transpose(-1, -2) @ tv
+    z_n = tz0 + pk.sum(dim=-2)
+    f = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    ((out * f(do)).sum() + (s_n * f(dsn)).sum() + (z_n * f(dzn)).sum()).backward()
+    return tuple(t.grad.numpy() for t in ts)
+
+
 def brute_numerator(p, kf, vb):
     """Numerator of eq. 9 on feature-mapped inputs: Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j."""
     n = p.shape[0]

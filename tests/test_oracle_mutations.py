@@ -39,6 +39,11 @@ MUTATIONS = {
                                          "for (long m = 0; m < M; ++m) R[d * M + m] += orc_phi(k[i * D + d]) * g[m];"),
     "non-causal value gradient uses phi(Q)": ("for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(k[j * D + d]);",
                                               "for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(q[j * D + d]);"),
+    "final-state gradient not carried": ("if (RN) memcpy(R, RN, (size_t)(C * Mb) * sizeof(double));",
+                                         "if (RN) memset(R, 0, (size_t)(C * Mb) * sizeof(double));"),
+    "initial-state gradient misses token 1": (
+        "if (R0) memcpy(R0, R, (size_t)(C * Mb) * sizeof(double));",
+        "if (R0) for (long e = 0; e < C * Mb; ++e) R0[e] = R[e] - (N > 0 ? P[e / Mb] * G[e % Mb] : 0.0);"),
     "initial state ignored in backward": ("acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];",
                                           "acc += 0.0 * G[i * Mb + M];"),
 }
@@ -64,6 +69,10 @@ PIN_CALLS = [
     lambda: P.test_noncausal_backward_equals_autograd((2, 3, 17, 5, 3)),
     P.test_noncausal_backward_last_row_is_causal,
     P.test_noncausal_backward_constant_values,
+    lambda: P.test_state_gradient_finite_differences(3, 3),
+    lambda: P.test_state_gradient_equals_autograd((2, 3, 17, 5, 3)),
+    P.test_state_gradient_chains_across_a_split,
+    P.test_state_gradient_without_output_gradient,
 ]
 
 

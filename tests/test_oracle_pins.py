@@ -411,3 +411,103 @@ def test_noncausal_backward_constant_values():
     assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
     # the attention weights of every row sum to one, so the value gradients sum to the upstream gradients
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------- state gradients (f2)
+def _state(B, H, D, M, seed):
+    s0 = np.abs(inputs.gaussian((B, H, D, M), seed)).astype(np.float64)
+    z0 = np.abs(inputs.gaussian((B, H, D), seed + 1)).astype(np.float64) + 0.5
+    dsn = inputs.gaussian((B, H, D, M), seed + 2).astype(np.float64)
+    dzn = inputs.gaussian((B, H, D), seed + 3).astype(np.float64)
+    return s0, z0, dsn, dzn
+
+
+def _loss_state(q, k, v, do, s0, z0, dsn, dzn):
+    o, _, sn, zn = oracle.forward_causal(q, k, v, s0, z0)
+    return float(np.sum(do * o) + np.sum(dsn * sn) + np.sum(dzn * zn))
+
+
+@pytest.mark.parametrize("D,M", [(3, 3), (4, 6)])
+def test_state_gradient_finite_differences(D, M):
+    """Central differences of sum(dO*O) + sum(dSN*S_N) + sum(dZN*Z_N) in Q, K, V, S0 and Z0."""
+    N = 6
+    q, k, v = _qkv((1, 1, N, D, M), 211 + D + M)
+    q, k, v = _nudge(q), _nudge(k), np.asarray(v, np.float64)
+    do = inputs.gaussian((1, 1, N, M), 217).astype(np.float64)
+    s0, z0, dsn, dzn = _state(1, 1, D, M, 220)
+    got = oracle.backward_causal(q, k, v, do, s0, z0, dsn, dzn, state_grad=True)
+    base = [q, k, v, s0, z0]
+    h = 1e-6
+    for which, g in enumerate(got):
+        x = base[which]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            ap, am = list(base), list(base)
+            ap[which] = x.copy()
+            am[which] = x.copy()
+            ap[which][idx] += h
+            am[which][idx] -= h
+            fd[idx] = (_loss_state(*ap[:3], do, *ap[3:], dsn, dzn) - _loss_state(*am[:3], do, *am[3:], dsn, dzn)) / (2 * h)
+        scale = max(np.max(np.abs(fd)), 1e-12)
+        assert np.max(np.abs(fd - g)) / scale < 1e-6, "QKVSZ"[which]
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 17, 5, 3), (1, 2, 40, 8, 6)])
+def test_state_gradient_equals_autograd(shape):
+    """eq. 8 with an initial state, and the final state, differentiated by PyTorch autograd (float64)."""
+    B, H, N, D, M = shape
+    q, k, v = _qkv(shape, 231)
+    do = inputs.gaussian(v.shape, 234).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 240)
+    got = oracle.backward_causal(q, k, v, do, s0, z0, dsn, dzn, state_grad=True)
+    ref = pins.brute_causal_state_grad(q, k, v, s0, z0, do, dsn, dzn)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12 * np.max(np.abs(r)))
+
+
+def test_state_gradient_chains_across_a_split():
+    """Chain rule across a cut of the sequence: the second part's initial-state gradient, used as the final-
+    state gradient of the first part, gives the whole sequence's gradients (what a sequence-sharded backward
+    relies on)."""
+    B, H, N, D, M, cut = 2, 2, 23, 4, 5, 9
+    q, k, v = _qkv((B, H, N, D, M), 251)
+    do = inputs.gaussian(v.shape, 254).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 260)
+    whole = oracle.backward_causal(q, k, v, do, s0, z0, dsn, dzn, state_grad=True)
+    _, _, s_mid, z_mid = oracle.forward_causal(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], s0, z0)
+    sl = slice(cut, None)
+    dq2, dk2, dv2, ds_mid, dz_mid = oracle.backward_causal(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl],
+                                                           s_mid, z_mid, dsn, dzn, state_grad=True)
+    sl = slice(None, cut)
+    dq1, dk1, dv1, ds0, dz0 = oracle.backward_causal(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl],
+                                                     s0, z0, ds_mid, dz_mid, state_grad=True)
+    for a, b in zip((np.concatenate((dq1, dq2), 2), np.concatenate((dk1, dk2), 2), np.concatenate((dv1, dv2), 2),
+                     ds0, dz0), whole):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13 * np.max(np.abs(b)))
+
+
+def test_state_gradient_without_output_gradient():
+    """dO = 0: the loss is linear in S_N = S0 + sum phi(K_j) V_j^T and Z_N = Z0 + sum phi(K_j), so
+    dQ = 0, dV_j = dSN^T phi(K_j), dK_j = (dSN V_j + dZN) * phi'(K_j), dS0 = dSN, dZ0 = dZN."""
+    B, H, N, D, M = 1, 2, 11, 4, 3
+    q, k, v = (np.asarray(a, np.float64) for a in _qkv((B, H, N, D, M), 271))
+    s0, z0, dsn, dzn = _state(B, H, D, M, 280)
+    dq, dk, dv, ds0, dz0 = oracle.backward_causal(q, k, v, np.zeros(v.shape), s0, z0, dsn, dzn, state_grad=True)
+    pk = pins.phi_lib(k)
+    dpk = np.where(k > 0, 1.0, np.exp(k))
+    assert np.max(np.abs(dq)) == 0.0
+    np.testing.assert_allclose(dv, np.einsum("bhdm,bhnd->bhnm", dsn, pk), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dk, (np.einsum("bhdm,bhnm->bhnd", dsn, v) + dzn[:, :, None, :]) * dpk,
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(ds0, dsn)
+    np.testing.assert_array_equal(dz0, dzn)
+
+
+def test_state_gradient_of_empty_sequence():
+    """N = 0: the final state is the initial state, so its gradient passes through unchanged."""
+    s0, z0, dsn, dzn = _state(1, 2, 4, 3, 290)
+    e = np.zeros((1, 2, 0, 4))
+    _, _, _, ds0, dz0 = oracle.backward_causal(e, e, np.zeros((1, 2, 0, 3)), np.zeros((1, 2, 0, 3)), s0, z0, dsn,
+                                               dzn, state_grad=True)
+    np.testing.assert_array_equal(ds0, dsn)
+    np.testing.assert_array_equal(dz0, dzn)
