@@ -136,19 +136,31 @@ int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
  * The denominator's share (left by the pages to automatic differentiation)
  * is the quotient rule: dL/dnum_i = dO_i / den_i, dL/dden_i =
  * -(dO_i . O_i) / den_i.
- *   O, den      the forward's O and den (required).
+ *   O, den      the forward's O and den (required when N > 0).
  *   S0, Z0      the initial state the forward started from (both or neither).
  *   ckpt        the forward's checkpoint (same sizes) or NULL: then the
  *               segment states are recomputed into `ws`.
+ *   dS_N, dZ_N  optional gradients [B,H,D,M], [B,H,D] float32 of the loss
+ *               with respect to the forward's final state S_out, Z_out (both
+ *               or neither; NULL: the final state does not reach the loss).
+ *               Every term phi(K_j) V_j^T is part of S_N, so they start the
+ *               backward-running sum of eq. 14-15.
  *   dQ, dK, dV  outputs in `dtype`.
- * The gradient with respect to S0/Z0 is not produced.
+ *   dS0, dZ0    optional outputs [B,H,D,M], [B,H,D] float32 (both or
+ *               neither): the gradient with respect to the initial state S0,
+ *               Z0 (zero state when those were NULL), i.e. the
+ *               backward-running sum carried through token 1.  With dS_N, dZ_N
+ *               this chains a backward over consecutive pieces of a sequence.
+ *               They must not overlap dS_N, dZ_N.  For N = 0 they receive
+ *               dS_N, dZ_N (zero when NULL) and nothing else is read.
  */
 int la_backward_causal(const void *Q, const void *K, const void *V,
                        const void *O, const float *den, const void *dO,
                        const float *S0, const float *Z0, const float *ckpt,
-                       void *dQ, void *dK, void *dV, int B, int H, int N,
-                       int D, int M, int dtype, void *ws, size_t ws_bytes,
-                       void *stream);
+                       const float *dS_N, const float *dZ_N, void *dQ,
+                       void *dK, void *dV, float *dS0, float *dZ0, int B, int H,
+                       int N, int D, int M, int dtype, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /*
  * Non-causal backward: gradients of a scalar loss with respect to the raw Q,

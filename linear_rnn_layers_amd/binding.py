@@ -58,7 +58,7 @@ def load(path: str | None = None):
     lib.la_forward_noncausal.restype = i
     lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
     lib.la_backward_causal.restype = i
-    lib.la_backward_causal.argtypes = [vp] * 12 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_causal.argtypes = [vp] * 16 + [i] * 6 + [vp, sz, vp]
     lib.la_backward_noncausal.restype = i
     lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
     lib.la_decode_step.restype = i
@@ -160,12 +160,13 @@ def la_forward_noncausal(Q, K, V, O, ws=None, stream=None):
     _check(st, "la_forward_noncausal")
 
 
-def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, ws=None, stream=None):
+def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, dS_N=None, dZ_N=None,
+                       dS0=None, dZ0=None, ws=None, stream=None):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
     st = load().la_backward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(den), _ptr(dO), _ptr(S0), _ptr(Z0),
-                                   _ptr(ckpt), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, D, M, dtype_code(Q.dtype),
-                                   _ptr(ws), nb, _stream(stream))
+                                   _ptr(ckpt), _ptr(dS_N), _ptr(dZ_N), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS0),
+                                   _ptr(dZ0), B, H, N, D, M, dtype_code(Q.dtype), _ptr(ws), nb, _stream(stream))
     _check(st, "la_backward_causal")
 
 
@@ -215,14 +216,20 @@ def forward_noncausal(q, k, v):
     return o
 
 
-def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None):
+def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=None, dz_n=None, state_grad=False):
+    """Causal backward.  Returns (dq, dk, dv), and with state_grad also (ds0, dz0), the gradient with respect to
+    the initial state; ds_n, dz_n are the upstream gradients of the final state (None: not in the loss)."""
     B, H, N, D, M = _sizes(q, v)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
+    ds0 = dz0 = None
+    if state_grad:
+        ds0 = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+        dz0 = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     ws = alloc_workspace(LA_OP_BWD_CAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ws)
-    return dq, dk, dv
+    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ds_n, dz_n, ds0, dz0, ws)
+    return (dq, dk, dv, ds0, dz0) if state_grad else (dq, dk, dv)
 
 
 def backward_noncausal(q, k, v, do):
@@ -244,23 +251,39 @@ def decode_step(q, k, v, s, z, y=None):
 
 
 class CausalLinearAttention(torch.autograd.Function):
-    """Autograd wrapper: forward and backward both run in the HIP library."""
+    """Autograd wrapper: forward and backward both run in the HIP library.  With an initial state (s0, z0,
+    float32) the gradient reaches it; with return_state the final state (s, z) is returned as well and its
+    gradient flows back through the same backward."""
 
     @staticmethod
-    def forward(ctx, q, k, v):
+    def forward(ctx, q, k, v, s0, z0, return_state):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        out = forward_causal(q, k, v)
-        ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"])
+        if (s0 is None) != (z0 is None):
+            raise ValueError("s0 and z0 go together")
+        if s0 is not None:
+            s0, z0 = s0.contiguous(), z0.contiguous()
+        out = forward_causal(q, k, v, s0=s0, z0=z0, return_state=return_state)
+        ctx.has_state = s0 is not None
+        ctx.return_state = return_state
+        ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"], s0, z0)
+        if return_state:
+            return out["o"], out["s"], out["z"]
         return out["o"]
 
     @staticmethod
-    def backward(ctx, do):
-        q, k, v, o, den, ck = ctx.saved_tensors
-        return backward_causal(q, k, v, o, den, do.contiguous(), ckpt=ck)
+    def backward(ctx, do, ds_n=None, dz_n=None):
+        q, k, v, o, den, ck, s0, z0 = ctx.saved_tensors
+        want_state = ctx.has_state and (ctx.needs_input_grad[3] or ctx.needs_input_grad[4])
+        if ds_n is not None:
+            ds_n, dz_n = ds_n.contiguous(), dz_n.contiguous()
+        g = backward_causal(q, k, v, o, den, do.contiguous(), s0=s0, z0=z0, ckpt=ck, ds_n=ds_n, dz_n=dz_n,
+                            state_grad=want_state)
+        ds0, dz0 = (g[3], g[4]) if want_state else (None, None)
+        return g[0], g[1], g[2], ds0, dz0, None
 
 
-def causal_linear_attention(q, k, v):
-    return CausalLinearAttention.apply(q, k, v)
+def causal_linear_attention(q, k, v, s0=None, z0=None, return_state=False):
+    return CausalLinearAttention.apply(q, k, v, s0, z0, return_state)
 
 
 class NonCausalLinearAttention(torch.autograd.Function):

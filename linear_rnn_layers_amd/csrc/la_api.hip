@@ -347,9 +347,13 @@ int backward_resident() {
 
 template <typename T, int D, int M>
 int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* O, const float* den,
-                    const void* dO, const float* S0, const float* Z0, const float* ckpt, void* dQ, void* dK,
-                    void* dV, int N, void* ws, hipStream_t s) {
-  if (p.nseg == 0) return LA_OK;
+                    const void* dO, const float* S0, const float* Z0, const float* ckpt, const float* dSN,
+                    const float* dZN, void* dQ, void* dK, void* dV, float* dS0, float* dZ0, int N, void* ws,
+                    hipStream_t s) {
+  if (p.nseg == 0)  // empty sequence: the initial state is the final state
+    return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
+                        (float*)nullptr, dS0, dZ0)
+               : LA_OK;
   const WsLayout wl = ws_layout(LA_OP_BWD_CAUSAL, p);
   int st = LA_OK;
   const float* ck = ckpt;
@@ -377,8 +381,8 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   const int kb = backward_group(p, N, backward_resident<T, D, M>());
   const int nsegb = (p.nseg + kb - 1) / kb;
   return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::BwdShape<T, D, M>::NTH), s,
-                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, (T*)dQ, (T*)dK, (T*)dV, N,
-                p.L * kb, nsegb, kb, p.nseg, scanned);
+                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, dSN, dZN, (T*)dQ, (T*)dK,
+                (T*)dV, dS0, dZ0, N, p.L * kb, nsegb, kb, p.nseg, scanned);
 }
 
 template <typename T, int D, int M>
@@ -517,18 +521,29 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, i
 }
 
 int la_backward_causal(const void* Q, const void* K, const void* V, const void* O, const float* den,
-                       const void* dO, const float* S0, const float* Z0, const float* ckpt, void* dQ, void* dK,
-                       void* dV, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       const void* dO, const float* S0, const float* Z0, const float* ckpt, const float* dS_N,
+                       const float* dZ_N, void* dQ, void* dK, void* dV, float* dS0, float* dZ0, int B, int H, int N,
+                       int D, int M, int dtype, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
-  if (N == 0) return LA_OK;
+  if ((dS_N == nullptr) != (dZ_N == nullptr)) return fail(LA_ERR_ARG, "dS_N and dZ_N must be given together");
+  if ((dS0 == nullptr) != (dZ0 == nullptr)) return fail(LA_ERR_ARG, "dS0 and dZ0 must be given together");
+  const size_t bh = (size_t)B * H;
+  if (N == 0) {
+    if (!dS0) return LA_OK;
+    st = check_ptrs({rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
+                     rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true)});
+    if (st) return st;
+    const Plan p = make_plan(B, H, N, D, M);
+    LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
+                dZ0, N, ws, (hipStream_t)stream);
+  }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
   const Plan p = make_plan(B, H, N, D, M);
-  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const size_t es = esize(dtype);
   const size_t need = ws_layout(LA_OP_BWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0 && (ckpt == nullptr || p.nseg > 1);
   if (uses_ws && (ws == nullptr || ws_bytes < need))
@@ -538,11 +553,13 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const void* 
                    rng("den", den, bh * N * 4, false), rng("dO", dO, bh * N * M * es, false),
                    rng("S0", S0, bh * D * M * 4, false), rng("Z0", Z0, bh * D * 4, false),
                    rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), false),
+                   rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
-                   rng("dV", dV, bh * N * M * es, true), rng("ws", uses_ws ? ws : nullptr, need, true)});
+                   rng("dV", dV, bh * N * M * es, true), rng("dS0", dS0, bh * D * M * 4, true),
+                   rng("dZ0", dZ0, bh * D * 4, true), rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dQ, dK, dV, N, ws,
-              (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0,
+              N, ws, (hipStream_t)stream);
 }
 
 int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, void* dQ, void* dK,

@@ -633,8 +633,12 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // SIMD for 64-token chunks, so that each SIMD interleaves two instruction
 // streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
 // reverse state R (backward sum of phi(Q) g^T, eq. 14-15, started from the
-// reverse aggregates of all later checkpoint segments: entry f1 - 1 of `ragg`
-// when it holds suffix sums (scanned = 1), else their sum in segment order).
+// gradient of the final state (dSN, dZN; zero when absent) plus the reverse
+// aggregates of all later checkpoint segments: entry f1 - 1 of `ragg` when it
+// holds suffix sums (scanned = 1), else their sum in segment order).  Every
+// term phi(K_j) V_j^T is part of the final state, hence the start value; the
+// initial state is part of every S_i, so its gradient (dS0, dZ0) is R, r
+// carried through the sequence's first token, written by that segment.
 // Key wavefront k owns key rows 16 (RB-1-k)..; it shares a SIMD with query
 // wavefront k, whose work falls with k while the key rows' work (all later
 // rows of the chunk) rises with k.  The tiles of S (forward sum of
@@ -657,8 +661,9 @@ struct BwdShape {
 template <typename T, int D, int M>
 __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ ckpt, const float* __restrict__ ragg, T* __restrict__ dQ, T* __restrict__ dK,
-    T* __restrict__ dV, int N, int L, int nsegb, int kb, int nseg, int scanned) {
+    const float* __restrict__ ckpt, const float* __restrict__ ragg, const float* __restrict__ dSN,
+    const float* __restrict__ dZN, T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV,
+    float* __restrict__ dS0, float* __restrict__ dZ0, int N, int L, int nsegb, int kb, int nseg, int scanned) {
   using P = Prec<T>;
   using BS = BwdShape<T, D, M>;
   constexpr int CB = BS::CB, RB = BS::RB, NW = BS::NW, NTH = BS::NTH, NPAIR = CB / 32;
@@ -763,11 +768,13 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     stage_S();
   }
   const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
-  if (rg) {  // reverse aggregates of the later segments, summed through R's planes as scratch
-    const int r0 = scanned ? f1 - 1 : f1, r1 = scanned ? f1 : nseg;
+  if (rg || dSN) {  // final-state gradient plus the reverse aggregates of the later segments, summed
+                    // through R's planes as scratch
+    const int r0 = !rg ? 0 : scanned ? f1 - 1 : f1, r1 = !rg ? 0 : scanned ? f1 : nseg;
     static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
     float* sbuf = reinterpret_cast<float*>(&rp.v[0][0][0]);
-    sum_states<D, M, NTH>(sbuf, nullptr, nullptr, rg, r0, r1);
+    sum_states<D, M, NTH>(sbuf, dSN ? dSN + (size_t)bh * D * M : nullptr, dZN ? dZN + (size_t)bh * D : nullptr, rg,
+                          r0, r1);
     __syncthreads();
     if (qrole) {
 #pragma unroll
@@ -1078,6 +1085,21 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     if (ci > 0) {
       __syncthreads();  // every wavefront is done with this chunk's LDS, and the key ones with R, r
       if (qrole) stage_R();
+    }
+  }
+  // The reverse state carried through the sequence's first token is the gradient of the initial state.
+  if (seqstart && dS0 && qrole) {
+    float v4[4];
+#pragma unroll
+    for (int k = 0; k < NTR; ++k) {
+      acc_to4(accR[k], v4);
+      *reinterpret_cast<float4*>(dS0 + (size_t)bh * D * M + (16 * rdb(k) + r16) * M + 16 * rmb(k) + 4 * g) =
+          make_float4(v4[0], v4[1], v4[2], v4[3]);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < NZW; ++j)
+        if (rb + RB * j < DB) dZ0[(size_t)bh * D + 16 * (rb + RB * j) + r16] = zr[j];
     }
   }
 }

@@ -101,18 +101,26 @@ def test_noncausal_and_backward_validation(lib):
     # N = 0 is a no-op
     assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, None, 0, None) == OK
     wsb = lib.la_workspace_size(2, 2, 2, 100, 32, 32, 0)
-    args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), None, None, None, addr(7), addr(8), addr(9)]
-    a = list(args)
-    a[4] = None  # den is required
-    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == NULL
-    a = list(args)
-    a[9] = addr(6)  # dQ on top of dO
-    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == ALIAS
-    a = list(args)
-    a[6] = addr(10)  # S0 without Z0
-    assert lib.la_backward_causal(*a, 2, 2, 100, 32, 32, 0, addr(20), wsb, None) == ARG
-    assert lib.la_backward_causal(*args, 2, 2, 100, 32, 32, 0, addr(20), wsb - 1, None) == WORKSPACE
-    assert lib.la_backward_causal(*args, 2, 2, 0, 32, 32, 0, None, 0, None) == OK
+    names = ["Q", "K", "V", "O", "den", "dO", "S0", "Z0", "ckpt", "dS_N", "dZ_N", "dQ", "dK", "dV", "dS0", "dZ0"]
+    base = dict(Q=addr(1), K=addr(2), V=addr(3), O=addr(4), den=addr(5), dO=addr(6), dQ=addr(7), dK=addr(8),
+                dV=addr(9))
+
+    def bwd(N=100, ws=addr(20), nb=wsb, **over):
+        a = dict(base)
+        a.update(over)
+        return lib.la_backward_causal(*[a.get(n) for n in names], 2, 2, N, 32, 32, 0, ws, nb, None)
+
+    assert bwd(den=None) == NULL  # den is required
+    assert bwd(dQ=addr(6)) == ALIAS  # dQ on top of dO
+    assert bwd(S0=addr(10)) == ARG  # S0 without Z0
+    assert bwd(dS_N=addr(10)) == ARG  # dS_N without dZ_N
+    assert bwd(dS0=addr(12)) == ARG  # dS0 without dZ0
+    assert bwd(dS_N=addr(10), dZ_N=addr(11), dS0=addr(10), dZ0=addr(13)) == ALIAS  # dS0 on top of dS_N
+    assert bwd(dS0=ctypes.c_void_p(BASE + 12 * (1 << 32) + 4), dZ0=addr(13)) == ALIGN
+    assert bwd(nb=wsb - 1) == WORKSPACE
+    assert bwd(N=0, ws=None, nb=0) == OK
+    # N = 0 with a state gradient requested still validates that request (no launch happens on failure)
+    assert bwd(N=0, ws=None, nb=0, dS0=addr(12), dZ0=addr(13), dS_N=addr(12), dZ_N=addr(11)) == ALIAS
 
 
 def test_noncausal_backward_validation(lib):

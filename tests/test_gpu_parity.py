@@ -414,3 +414,146 @@ def test_noncausal_autograd_wrapper():
     errs = [rowerr(host(Q.grad), rq, row_floor=CANCEL_FLOOR * sq), rowerr(host(K.grad), rk, row_floor=CANCEL_FLOOR * sk),
             rowerr(host(V.grad), rv), rowerr(host(out), oracle.forward_noncausal(q, k, v))]
     assert max(errs) <= 1e-4, errs
+
+
+# ------------------------------------------------------- state gradients
+def _state_inputs(B, H, D, M, dtype, seed, sigma=0.1):
+    """A realistic initial state (the final state of a 50-token prefix) and final-state gradients."""
+    _, _, s0, z0 = oracle.forward_causal(*_qkv(B, H, 50, D, M, dtype, seed))
+    s0, z0 = (a.astype(np.float32).astype(np.float64) for a in (s0, z0))  # what the library receives
+    dsn = inputs.gaussian((B, H, D, M), seed + 10, sigma)
+    dzn = inputs.gaussian((B, H, D), seed + 11, sigma)
+    return s0, z0, dsn, dzn
+
+
+def gpu_backward_state(q, k, v, do, dtype, s0, z0, dsn, dzn, use_ckpt=True):
+    out = gpu_forward(q, k, v, dtype, s0, z0)
+    Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    g = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, dtype),
+                                s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                ckpt=out["ckpt"] if use_ckpt else None,
+                                ds_n=None if dsn is None else dev32(dsn), dz_n=None if dzn is None else dev32(dzn),
+                                state_grad=True)
+    torch.cuda.synchronize()
+    return [host(t) for t in g]
+
+
+def state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn):
+    dq, dk, dv, ds0, dz0 = got
+    rq, rk, rv, rs, rz = oracle.backward_causal(q, k, v, do, s0, z0, dsn, dzn, state_grad=True)
+    return {"dQ": rowerr(dq, rq, row_floor=CANCEL_FLOOR * dq_cancel_scale(q, k, v, do, s0, z0)),
+            "dK": rowerr(dk, rk), "dV": rowerr(dv, rv), "dS0": rowerr(ds0, rs),
+            # dZ0 = dZ_N + sum_i c_i phi(Q_i) is a signed sum, one D-vector per head like a row of dK
+            "dZ0": rowerr(dz0[:, :, None, :], rz[:, :, None, :])}
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 64, 65, 200, 784])
+def test_state_gradient_sweep(N, D, M, dtype):
+    """Gradients with an initial state and a final-state gradient: dQ, dK, dV and dS0, dZ0."""
+    B, H = 2, 3
+    q, k, v = _qkv(B, H, N, D, M, dtype, 9300 + N)
+    do = inputs.gaussian((B, H, N, M), 9390, 1.0, dtype)
+    s0, z0, dsn, dzn = _state_inputs(B, H, D, M, dtype, 9400)
+    got = gpu_backward_state(q, k, v, do, dtype, s0, z0, dsn, dzn)
+    errs = state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn)
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("D,M", [(32, 32), (64, 64)])
+@pytest.mark.parametrize("chunks", [1, 3])
+@pytest.mark.parametrize("use_ckpt", [True, False])
+def test_state_gradient_segments(D, M, chunks, use_ckpt):
+    """Many segments (reverse aggregates summed in the workgroup for D=M=32, scanned for 64) with the
+    final-state gradient added to every segment's start; initial-state gradient from the first segment."""
+    B, H, N = 1, 2, 784
+    q, k, v = _qkv(B, H, N, D, M, F32, 9500 + chunks)
+    do = inputs.gaussian((B, H, N, M), 9590)
+    s0, z0, dsn, dzn = _state_inputs(B, H, D, M, F32, 9600)
+    binding.set_segment_chunks(chunks)
+    try:
+        got = gpu_backward_state(q, k, v, do, F32, s0, z0, dsn, dzn, use_ckpt)
+    finally:
+        binding.set_segment_chunks(0)
+    errs = state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn)
+    assert max(errs.values()) <= TOL[F32], errs
+
+
+def test_state_gradient_without_initial_state():
+    """No S0, Z0 (zero initial state): dS0, dZ0 are still the gradient with respect to it."""
+    B, H, N, D, M = 2, 2, 300, 64, 32
+    q, k, v = _qkv(B, H, N, D, M, BF16, 9700)
+    do = inputs.gaussian((B, H, N, M), 9703, 1.0, BF16)
+    _, _, dsn, dzn = _state_inputs(B, H, D, M, BF16, 9710)
+    got = gpu_backward_state(q, k, v, do, BF16, None, None, dsn, dzn)
+    errs = state_grad_errors(got, q, k, v, do, None, None, dsn, dzn)
+    assert max(errs.values()) <= TOL[BF16], errs
+    # and without a final-state gradient the initial-state gradient is the reverse sum alone
+    got = gpu_backward_state(q, k, v, do, BF16, None, None, None, None)
+    errs = state_grad_errors(got, q, k, v, do, None, None, None, None)
+    assert max(errs.values()) <= TOL[BF16], errs
+
+
+def test_state_gradient_empty_sequence():
+    """N = 0: dS0, dZ0 receive dS_N, dZ_N unchanged (zeros when absent)."""
+    B, H, D, M = 2, 3, 32, 64
+    e = torch.empty((B, H, 0, D), device="cuda")
+    ev = torch.empty((B, H, 0, M), device="cuda")
+    dsn = dev32(inputs.gaussian((B, H, D, M), 9800))
+    dzn = dev32(inputs.gaussian((B, H, D), 9801))
+    ds0 = torch.full((B, H, D, M), 7.0, device="cuda")
+    dz0 = torch.full((B, H, D), 7.0, device="cuda")
+    binding.la_backward_causal(e, e, ev, ev, None, ev, e, e, ev, dS_N=dsn, dZ_N=dzn, dS0=ds0, dZ0=dz0)
+    torch.cuda.synchronize()
+    assert torch.equal(ds0, dsn) and torch.equal(dz0, dzn)
+    binding.la_backward_causal(e, e, ev, ev, None, ev, e, e, ev, dS0=ds0, dZ0=dz0)
+    torch.cuda.synchronize()
+    assert not torch.any(ds0) and not torch.any(dz0)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_state_gradient_chains_across_a_split(dtype):
+    """A sequence cut in two: the second part's backward (with the final-state gradient) gives dS0, dZ0 that,
+    as the first part's final-state gradient, reproduce the whole sequence's gradients."""
+    B, H, N, D, M, cut = 2, 2, 700, 64, 64, 300
+    q, k, v = _qkv(B, H, N, D, M, dtype, 9900)
+    do = inputs.gaussian((B, H, N, M), 9903, 1.0, dtype)
+    s0, z0, dsn, dzn = _state_inputs(B, H, D, M, dtype, 9910)
+    _, _, s_mid, z_mid = oracle.forward_causal(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], s0, z0)
+    sl2, sl1 = slice(cut, None), slice(None, cut)
+    g2 = gpu_backward_state(q[:, :, sl2], k[:, :, sl2], v[:, :, sl2], do[:, :, sl2], dtype, s_mid, z_mid, dsn, dzn)
+    g1 = gpu_backward_state(q[:, :, sl1], k[:, :, sl1], v[:, :, sl1], do[:, :, sl1], dtype, s0, z0, g2[3], g2[4])
+    got = [np.concatenate((a, b), 2) for a, b in zip(g1[:3], g2[:3])] + g1[3:]
+    errs = state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn)
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+def test_state_gradient_autograd_wrapper():
+    """torch.autograd through the library with an initial state and the final state in the loss."""
+    B, H, N, D, M = 2, 2, 260, 32, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 9950)
+    do = inputs.gaussian((B, H, N, M), 9953)
+    s0, z0, dsn, dzn = _state_inputs(B, H, D, M, F32, 9960)
+    Q, K, V, S0, Z0 = (dev32(a).requires_grad_(True) for a in (q, k, v, s0, z0))
+    o, s, z = binding.causal_linear_attention(Q, K, V, S0, Z0, return_state=True)
+    ((o * dev32(do)).sum() + (s * dev32(dsn)).sum() + (z * dev32(dzn)).sum()).backward()
+    torch.cuda.synchronize()
+    got = [host(t.grad) for t in (Q, K, V, S0, Z0)]
+    errs = state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn)
+    assert max(errs.values()) <= TOL[F32], errs
+
+
+def test_state_gradient_long_shape_sampled():
+    """B=1 H=16 N=65536 D=M=64 bf16 with an initial state and a final-state gradient; the oracle follows
+    heads 0 and 11."""
+    w = inputs.LONG
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    s0, z0, dsn, dzn = _state_inputs(w.B, w.H, w.D, w.M, BF16, 9990)
+    got = gpu_backward_state(q, k, v, do, BF16, s0, z0, dsn, dzn)
+    hs = [0, 11]
+    sub = lambda a: a[:, hs]  # noqa: E731
+    errs = state_grad_errors([sub(a) for a in got], sub(q), sub(k), sub(v), sub(do), sub(s0), sub(z0), sub(dsn),
+                             sub(dzn))
+    assert max(errs.values()) <= TOL[BF16], errs
