@@ -52,7 +52,9 @@ def _configure(lib):
     lib.orc_numerator_backward.argtypes = [dp] * 9 + [L] * 3
     lib.orc_backward_causal.argtypes = [dp] * 13 + [L] * 5
     lib.orc_backward_noncausal.argtypes = [dp] * 7 + [L] * 5
-    lib.orc_decode_step.argtypes = [dp] * 6 + [L] * 4
+    lib.orc_decode_step.argtypes = [dp] * 7 + [L] * 4
+    lib.orc_forward_decay.argtypes = [dp] * 10 + [L] * 5
+    lib.orc_backward_decay.argtypes = [dp] * 15 + [L] * 5
     lib.orc_num_threads.restype = ctypes.c_int
     return lib
 
@@ -178,13 +180,55 @@ def backward_noncausal(q, k, v, do):
     return dq, dk, dv
 
 
-def decode_step(q, k, v, s, z):
-    """eq. 18-20 (attention part).  Returns (y, S_new, Z_new); inputs untouched."""
+def decode_step(q, k, v, s, z, log_a=None):
+    """eq. 18-20 (attention part), decayed by exp(log_a) [B,H] when given.  Returns (y, S_new, Z_new); inputs
+    untouched."""
     q, k, v = _f64(q), _f64(k), _f64(v)
+    log_a = None if log_a is None else _f64(log_a)
     s = np.array(s, dtype=np.float64, copy=True, order="C")
     z = np.array(z, dtype=np.float64, copy=True, order="C")
     B, H, D = q.shape
     M = v.shape[-1]
     y = np.empty((B, H, M))
-    _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(z), _ptr(y), B, H, D, M)
+    _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(s), _ptr(z), _ptr(y), B, H, D, M)
     return y, s, z
+
+
+def forward_decay(q, k, v, log_a, s0=None, z0=None):
+    """Decayed causal forward (per-token, per-head log-decay log_a [B,H,N]).  Returns (O, den, S_N, Z_N)."""
+    q, k, v, log_a = _f64(q), _f64(k), _f64(v), _f64(log_a)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    s0 = None if s0 is None else _f64(s0)
+    z0 = None if z0 is None else _f64(z0)
+    o = np.empty((B, H, N, M))
+    den = np.empty((B, H, N))
+    s = np.empty((B, H, D, M))
+    z = np.empty((B, H, D))
+    _load().orc_forward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(s0), _ptr(z0), _ptr(o), _ptr(den),
+                              _ptr(s), _ptr(z), B, H, N, D, M)
+    return o, den, s, z
+
+
+def backward_decay(q, k, v, log_a, do, s0=None, z0=None, dsn=None, dzn=None):
+    """Gradients of sum(dO*O) + sum(dSN*S_N) + sum(dZN*Z_N) for the decayed forward.  Returns
+    (dQ, dK, dV, dlogA, dS0, dZ0)."""
+    q, k, v, log_a, do = _f64(q), _f64(k), _f64(v), _f64(log_a), _f64(do)
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    s0 = None if s0 is None else _f64(s0)
+    z0 = None if z0 is None else _f64(z0)
+    if (dsn is None) != (dzn is None):
+        raise ValueError("dsn and dzn go together")
+    dsn = None if dsn is None else _f64(dsn)
+    dzn = None if dzn is None else _f64(dzn)
+    dq = np.empty((B, H, N, D))
+    dk = np.empty((B, H, N, D))
+    dv = np.empty((B, H, N, M))
+    dla = np.empty((B, H, N))
+    ds0 = np.empty((B, H, D, M))
+    dz0 = np.empty((B, H, D))
+    _load().orc_backward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dsn),
+                               _ptr(dzn), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(ds0), _ptr(dz0),
+                               B, H, N, D, M)
+    return dq, dk, dv, dla, ds0, dz0

@@ -422,21 +422,187 @@ void orc_backward_noncausal(const double *Q, const double *K, const double *V,
 }
 
 /*
+ * Decayed causal forward ([LA] "Variants and extensions": RetNet replaces
+ * the unbounded cumulative sum by S_t = gamma S_{t-1} + phi(k_t) v_t^T with
+ * gamma in (0, 1); gated linear attention makes the decay data-dependent).
+ * Here the decay is one scalar per token and head, given by its logarithm
+ * logA [B,H,N] (a_t = exp(logA_t) in (0, 1]; a constant per head is the
+ * RetNet case).  The pages give the update of S only; the normaliser Z takes
+ * the same decay, so that the output stays a weighted average of the values:
+ *   S_t = a_t S_{t-1} + phi(K_t) V_t^T,  Z_t = a_t Z_{t-1} + phi(K_t),
+ *   den_t = phi(Q_t) . Z_t,  O_t = phi(Q_t)^T S_t / den_t.
+ * With logA = 0 this is orc_forward_causal.  S0/Z0 (both or neither) are the
+ * state before token 1 (decayed by a_1 like any earlier state); den, S_out,
+ * Z_out may be NULL.
+ */
+void orc_forward_decay(const double *Q, const double *K, const double *V,
+                       const double *logA, const double *S0, const double *Z0,
+                       double *O, double *den, double *S_out, double *Z_out,
+                       long B, long H, long N, long D, long M) {
+  long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+    double *Z = (double *)calloc((size_t)D, sizeof(double));
+    double *pq = (double *)malloc((size_t)D * sizeof(double));
+    double *pk = (double *)malloc((size_t)D * sizeof(double));
+    if (S0) memcpy(S, S0 + bh * D * M, (size_t)(D * M) * sizeof(double));
+    if (Z0) memcpy(Z, Z0 + bh * D, (size_t)D * sizeof(double));
+    for (long i = 0; i < N; ++i) {
+      const double *q = Q + (bh * N + i) * D;
+      const double *k = K + (bh * N + i) * D;
+      const double *v = V + (bh * N + i) * M;
+      const double a = exp(logA[bh * N + i]);
+      for (long d = 0; d < D; ++d) {
+        pq[d] = orc_phi(q[d]);
+        pk[d] = orc_phi(k[d]);
+      }
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) S[d * M + m] = a * S[d * M + m] + pk[d] * v[m];
+        Z[d] = a * Z[d] + pk[d];
+      }
+      double dn = 0.0;
+      for (long d = 0; d < D; ++d) dn += pq[d] * Z[d];
+      double *o = O + (bh * N + i) * M;
+      for (long m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (long d = 0; d < D; ++d) num += pq[d] * S[d * M + m];
+        o[m] = num / dn;
+      }
+      if (den) den[bh * N + i] = dn;
+    }
+    if (S_out) memcpy(S_out + bh * D * M, S, (size_t)(D * M) * sizeof(double));
+    if (Z_out) memcpy(Z_out + bh * D, Z, (size_t)D * sizeof(double));
+    free(S);
+    free(Z);
+    free(pq);
+    free(pk);
+  }
+}
+
+/*
+ * Backward of orc_forward_decay: reverse-mode differentiation of its
+ * recurrence, token by token.  The loss is sum(dO * O) + sum(dSN * S_N) +
+ * sum(dZN * Z_N) (dSN/dZN both or neither, NULL: zero).  With the augmented
+ * state Sb_t = [S_t | Z_t] (D x (M+1)), the augmented value [V_t, 1] and the
+ * quotient rule's upstream Gb_t = [dO_t / den_t, -(dO_t . O_t) / den_t]:
+ *   R = [dSN | dZN];  for t = N .. 1:
+ *     R += phi(Q_t) Gb_t^T               (the gradient of Sb_t is complete)
+ *     dphiQ_t = Sb_t Gb_t,  dphiK_t = R [V_t, 1],  dV_t = (R^T phi(K_t))[:M]
+ *     dlogA_t = a_t <R, Sb_{t-1}>        (Sb_t depends on a_t through a_t Sb_{t-1})
+ *     R = a_t R                          (the gradient of Sb_{t-1})
+ *   [dS0 | dZ0] = R.
+ * then the chain rule through phi.  The forward states Sb_0 .. Sb_N are kept
+ * (O(N D M) memory per head: this is the oracle, not the product).
+ * dS0/dZ0 (both or neither) may be NULL.
+ */
+void orc_backward_decay(const double *Q, const double *K, const double *V,
+                        const double *logA, const double *dO,
+                        const double *S0, const double *Z0, const double *dSN,
+                        const double *dZN, double *dQ, double *dK, double *dV,
+                        double *dlogA, double *dS0, double *dZ0, long B, long H,
+                        long N, long D, long M) {
+  long BH = B * H;
+  long Mb = M + 1, SB = D * (M + 1);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bh = 0; bh < BH; ++bh) {
+    const double *q = Q + bh * N * D, *k = K + bh * N * D, *v = V + bh * N * M;
+    const double *go = dO + bh * N * M, *la = logA + bh * N;
+    double *Sb = (double *)calloc((size_t)((N + 1) * SB), sizeof(double));
+    double *R = (double *)calloc((size_t)SB, sizeof(double));
+    double *pq = (double *)malloc((size_t)D * sizeof(double));
+    double *pk = (double *)malloc((size_t)D * sizeof(double));
+    double *G = (double *)malloc((size_t)Mb * sizeof(double));
+    /* forward: Sb_0 = [S0 | Z0], Sb_t = a_t Sb_{t-1} + phi(K_t) [V_t, 1]^T */
+    for (long d = 0; d < D; ++d) {
+      for (long m = 0; m < M; ++m) Sb[d * Mb + m] = S0 ? S0[bh * D * M + d * M + m] : 0.0;
+      Sb[d * Mb + M] = Z0 ? Z0[bh * D + d] : 0.0;
+    }
+    for (long t = 1; t <= N; ++t) {
+      const double a = exp(la[t - 1]);
+      const double *prev = Sb + (t - 1) * SB;
+      double *cur = Sb + t * SB;
+      for (long d = 0; d < D; ++d) {
+        const double p = orc_phi(k[(t - 1) * D + d]);
+        for (long m = 0; m < M; ++m) cur[d * Mb + m] = a * prev[d * Mb + m] + p * v[(t - 1) * M + m];
+        cur[d * Mb + M] = a * prev[d * Mb + M] + p;
+      }
+    }
+    if (dSN)
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) R[d * Mb + m] = dSN[bh * D * M + d * M + m];
+        R[d * Mb + M] = dZN[bh * D + d];
+      }
+    for (long t = N; t >= 1; --t) {
+      const long i = t - 1;
+      const double a = exp(la[i]);
+      const double *cur = Sb + t * SB, *prev = Sb + (t - 1) * SB;
+      for (long d = 0; d < D; ++d) {
+        pq[d] = orc_phi(q[i * D + d]);
+        pk[d] = orc_phi(k[i * D + d]);
+      }
+      /* output of token t and the quotient rule */
+      double dn = 0.0;
+      for (long d = 0; d < D; ++d) dn += pq[d] * cur[d * Mb + M];
+      double dot = 0.0;
+      for (long m = 0; m < M; ++m) {
+        double num = 0.0;
+        for (long d = 0; d < D; ++d) num += pq[d] * cur[d * Mb + m];
+        dot += go[i * M + m] * (num / dn);
+        G[m] = go[i * M + m] / dn;
+      }
+      G[M] = -dot / dn;
+      for (long d = 0; d < D; ++d)
+        for (long m = 0; m < Mb; ++m) R[d * Mb + m] += pq[d] * G[m];
+      for (long d = 0; d < D; ++d) {
+        double aq = 0.0, ak = R[d * Mb + M];
+        for (long m = 0; m < Mb; ++m) aq += cur[d * Mb + m] * G[m];
+        for (long m = 0; m < M; ++m) ak += R[d * Mb + m] * v[i * M + m];
+        dQ[(bh * N + i) * D + d] = aq * orc_dphi(q[i * D + d]);
+        dK[(bh * N + i) * D + d] = ak * orc_dphi(k[i * D + d]);
+      }
+      for (long m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (long d = 0; d < D; ++d) acc += R[d * Mb + m] * pk[d];
+        dV[(bh * N + i) * M + m] = acc;
+      }
+      double ip = 0.0;
+      for (long e = 0; e < SB; ++e) ip += R[e] * prev[e];
+      dlogA[bh * N + i] = a * ip;
+      for (long e = 0; e < SB; ++e) R[e] *= a;
+    }
+    if (dS0)
+      for (long d = 0; d < D; ++d) {
+        for (long m = 0; m < M; ++m) dS0[bh * D * M + d * M + m] = R[d * Mb + m];
+        dZ0[bh * D + d] = R[d * Mb + M];
+      }
+    free(Sb);
+    free(R);
+    free(pq);
+    free(pk);
+    free(G);
+  }
+}
+
+/*
  * One RNN decode step ([TaR] eq. 18-20, attention part; [LA] recurrent
- * form): S += phi(k) v^T, Z += phi(k), then y = phi(q)^T S / phi(q).Z.
+ * form): S = a S + phi(k) v^T, Z = a Z + phi(k), then y = phi(q)^T S /
+ * phi(q).Z, with a = exp(logA) per (batch, head) for the decayed recurrence
+ * of orc_forward_decay, and a = 1 when logA is NULL.
  * S [B,H,D,M] and Z [B,H,D] are updated in place; y [B,H,M].
  */
 void orc_decode_step(const double *q, const double *k, const double *v,
-                     double *S, double *Z, double *y, long B, long H, long D,
-                     long M) {
+                     const double *logA, double *S, double *Z, double *y,
+                     long B, long H, long D, long M) {
   long BH = B * H;
 #pragma omp parallel for schedule(static)
   for (long bh = 0; bh < BH; ++bh) {
     double *s = S + bh * D * M, *z = Z + bh * D;
+    const double a = logA ? exp(logA[bh]) : 1.0;
     for (long d = 0; d < D; ++d) {
       double pk = orc_phi(k[bh * D + d]);
-      for (long m = 0; m < M; ++m) s[d * M + m] += pk * v[bh * M + m];
-      z[d] += pk;
+      for (long m = 0; m < M; ++m) s[d * M + m] = a * s[d * M + m] + pk * v[bh * M + m];
+      z[d] = a * z[d] + pk;
     }
     double dn = 0.0;
     for (long d = 0; d < D; ++d) dn += orc_phi(q[bh * D + d]) * z[d];

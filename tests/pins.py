@@ -80,6 +80,65 @@ def brute_causal_state_grad(q, k, v, s0, z0, do, dsn, dzn):
     return tuple(t.grad.numpy() for t in ts)
 
 
+def brute_decay(q, k, v, log_a, s0=None, z0=None):
+    """Decayed attention as an explicit weighted average: token j's weight at query i >= j is
+    (phi(q_i).phi(k_j)) times the product of the decays a_{j+1} .. a_i, the initial state's weight the
+    product a_1 .. a_i (products of the gates formed one by one).  Returns (O, den, S_N, Z_N)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    a = np.exp(np.asarray(log_a, dtype=np.float64))
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    out = np.empty((B, H, N, M))
+    den = np.empty((B, H, N))
+    sn = np.empty((B, H, D, M))
+    zn = np.empty((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            pq, pk = phi_lib(q[b, h]), phi_lib(k[b, h])
+            w = np.zeros((N, N + 1))  # column 0: the initial state, column j + 1: token j
+            for i in range(N):
+                prod = 1.0
+                for j in range(i, -1, -1):
+                    w[i, j + 1] = prod
+                    prod *= a[b, h, j]
+                w[i, 0] = prod
+            s_init = np.zeros((D, M)) if s0 is None else np.asarray(s0, np.float64)[b, h]
+            z_init = np.zeros(D) if z0 is None else np.asarray(z0, np.float64)[b, h]
+            sim = (pq @ pk.T) * w[:, 1:]
+            num = sim @ v[b, h] + w[:, :1] * (pq @ s_init)
+            den[b, h] = sim.sum(axis=1) + w[:, 0] * (pq @ z_init)
+            out[b, h] = num / den[b, h][:, None]
+            wl = w[N - 1] if N else np.array([1.0])
+            sn[b, h] = wl[0] * s_init + (pk * wl[1:, None]).T @ v[b, h]
+            zn[b, h] = wl[0] * z_init + (pk * wl[1:, None]).sum(axis=0)
+    return out, den, sn, zn
+
+
+def brute_decay_grad(q, k, v, log_a, s0, z0, do, dsn, dzn):
+    """Gradients of sum(dO*O) + sum(dSN*S_N) + sum(dZN*Z_N) of the decayed form with respect to Q, K, V,
+    logA, S0, Z0 by PyTorch autograd in float64: weights exp(L_i - L_j) with L the running sum of logA."""
+    ts = [torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True) for x in (q, k, v, log_a, s0, z0)]
+    tq, tk, tv, tla, ts0, tz0 = ts
+    pq = torch.nn.functional.elu(tq, alpha=1.0) + 1.0
+    pk = torch.nn.functional.elu(tk, alpha=1.0) + 1.0
+    n = tq.shape[-2]
+    lam = torch.cumsum(tla, dim=-1)
+    mask = torch.tril(torch.ones((n, n), dtype=torch.bool))
+    diff = lam.unsqueeze(-1) - lam.unsqueeze(-2)
+    w = torch.where(mask, torch.exp(torch.where(mask, diff, torch.zeros_like(diff))), torch.zeros_like(diff))
+    sim = (pq @ pk.transpose(-1, -2)) * w
+    w0 = torch.exp(lam)
+    num = sim @ tv + w0.unsqueeze(-1) * (pq @ ts0)
+    den = sim.sum(dim=-1) + w0 * (pq * tz0.unsqueeze(-2)).sum(dim=-1)
+    out = num / den.unsqueeze(-1)
+    wl = w[..., n - 1, :]
+    s_n = w0[..., n - 1, None, None] * ts0 + (pk * wl.unsqueeze(-1)).transpose(-1, -2) @ tv
+    z_n = w0[..., n - 1, None] * tz0 + (pk * wl.unsqueeze(-1)).sum(dim=-2)
+    f = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))  # noqa: E731
+    ((out * f(do)).sum() + (s_n * f(dsn)).sum() + (z_n * f(dzn)).sum()).backward()
+    return tuple(t.grad.numpy() for t in ts)
+
+
 def brute_numerator(p, kf, vb):
     """Numerator of eq. 9 on feature-mapped inputs: Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j."""
     n = p.shape[0]

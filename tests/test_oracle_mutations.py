@@ -33,7 +33,7 @@ MUTATIONS = {
     "eq. 13 forward sum off by one": ("    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m];\n      dP[i * C + c] = acc;\n    }\n  }",
                                       "    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m] * (i > 0);\n      dP[i * C + c] = acc;\n    }\n  }"),
     "non-causal drops phi on keys": ("double pk = orc_phi(k[d]);\n        for", "double pk = k[d];\n        for"),
-    "decode normaliser ignores keys": ("      z[d] += pk;", "      z[d] += 1.0;"),
+    "decode normaliser ignores keys": ("      z[d] = a * z[d] + pk;", "      z[d] = a * z[d] + 1.0;"),
     "non-causal backward denominator sign": ("double c = -dot / den;", "double c = dot / den;"),
     "non-causal reverse sum of phi(K)": ("for (long m = 0; m < M; ++m) R[d * M + m] += pq[d] * g[m];",
                                          "for (long m = 0; m < M; ++m) R[d * M + m] += orc_phi(k[i * D + d]) * g[m];"),
@@ -44,6 +44,12 @@ MUTATIONS = {
     "initial-state gradient misses token 1": (
         "if (R0) memcpy(R0, R, (size_t)(C * Mb) * sizeof(double));",
         "if (R0) for (long e = 0; e < C * Mb; ++e) R0[e] = R[e] - (N > 0 ? P[e / Mb] * G[e % Mb] : 0.0);"),
+    "decay applied after the update": ("S[d * M + m] = a * S[d * M + m] + pk[d] * v[m];",
+                                       "S[d * M + m] = a * (S[d * M + m] + pk[d] * v[m]);"),
+    "normaliser not decayed": ("Z[d] = a * Z[d] + pk[d];", "Z[d] = Z[d] + pk[d];"),
+    "decay gradient misses a_t": ("dlogA[bh * N + i] = a * ip;", "dlogA[bh * N + i] = ip;"),
+    "decay gradient uses the current state": ("ip += R[e] * prev[e];", "ip += R[e] * cur[e];"),
+    "reverse state not decayed": ("for (long e = 0; e < SB; ++e) R[e] *= a;", "(void)a;"),
     "initial state ignored in backward": ("acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];",
                                           "acc += 0.0 * G[i * Mb + M];"),
 }
@@ -73,6 +79,12 @@ PIN_CALLS = [
     lambda: P.test_state_gradient_equals_autograd((2, 3, 17, 5, 3)),
     P.test_state_gradient_chains_across_a_split,
     P.test_state_gradient_without_output_gradient,
+    lambda: P.test_decay_forward_equals_bruteforce((2, 3, 17, 5, 3), True),
+    P.test_decay_of_one_is_the_base_method,
+    lambda: P.test_decay_backward_equals_autograd((2, 3, 17, 5, 3)),
+    P.test_decay_backward_finite_differences,
+    P.test_decay_decode_equals_forward,
+    P.test_decay_log_gradient_identity,
 ]
 
 

@@ -511,3 +511,140 @@ def test_state_gradient_of_empty_sequence():
                                                dzn, state_grad=True)
     np.testing.assert_array_equal(ds0, dsn)
     np.testing.assert_array_equal(dz0, dzn)
+
+
+# ------------------------------------------------- decayed recurrence (f3)
+def _log_gates(shape, seed, bias=1.0):
+    """Per-token gates in (0, 1): log of a logistic of N(bias, 1)."""
+    x = inputs.gaussian(shape, seed).astype(np.float64) + bias
+    return -np.log1p(np.exp(-x))
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 17, 5, 3), (1, 2, 40, 8, 6)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_decay_forward_equals_bruteforce(shape, with_state):
+    """The decayed recurrence equals the explicit weighted average with products of the gates."""
+    B, H, N, D, M = shape
+    q, k, v = _qkv(shape, 301)
+    la = _log_gates((B, H, N), 305)
+    s0 = z0 = None
+    if with_state:
+        s0, z0, _, _ = _state(B, H, D, M, 306)
+    got = oracle.forward_decay(q, k, v, la, s0, z0)
+    ref = pins.brute_decay(q, k, v, la, s0, z0)
+    for g, r in zip(got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-12, atol=1e-14)
+
+
+def test_decay_of_one_is_the_base_method():
+    """logA = 0 (a = 1): the decayed forward and its gradients are those of the plain causal method."""
+    B, H, N, D, M = 2, 2, 19, 4, 5
+    q, k, v = _qkv((B, H, N, D, M), 311)
+    do = inputs.gaussian(v.shape, 314).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 315)
+    zero = np.zeros((B, H, N))
+    for g, r in zip(oracle.forward_decay(q, k, v, zero, s0, z0), oracle.forward_causal(q, k, v, s0, z0)):
+        np.testing.assert_allclose(g, r, rtol=1e-13, atol=1e-14)
+    got = oracle.backward_decay(q, k, v, zero, do, s0, z0, dsn, dzn)
+    ref = oracle.backward_causal(q, k, v, do, s0, z0, dsn, dzn, state_grad=True)
+    for g, r in zip(got[:3] + got[4:], ref):
+        np.testing.assert_allclose(g, r, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 17, 5, 3), (1, 2, 40, 8, 6)])
+def test_decay_backward_equals_autograd(shape):
+    """All six gradients (Q, K, V, logA, S0, Z0) against PyTorch autograd of the weighted-average form."""
+    B, H, N, D, M = shape
+    q, k, v = _qkv(shape, 321)
+    la = _log_gates((B, H, N), 325)
+    do = inputs.gaussian(v.shape, 326).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 327)
+    got = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
+    ref = pins.brute_decay_grad(q, k, v, la, s0, z0, do, dsn, dzn)
+    for name, g, r in zip(("dQ", "dK", "dV", "dlogA", "dS0", "dZ0"), got, ref):
+        np.testing.assert_allclose(g, r, rtol=1e-9, atol=1e-11 * np.max(np.abs(r)), err_msg=name)
+
+
+def test_decay_backward_finite_differences():
+    """Central differences of the loss in logA, Q and K through the decayed forward."""
+    B, H, N, D, M = 1, 1, 6, 3, 4
+    q, k, v = _qkv((B, H, N, D, M), 331)
+    q, k = _nudge(q), _nudge(k)
+    la = _log_gates((B, H, N), 335)
+    do = inputs.gaussian(v.shape, 336).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 337)
+
+    def loss(q_, k_, la_):
+        o, _, sn, zn = oracle.forward_decay(q_, k_, v, la_, s0, z0)
+        return float(np.sum(do * o) + np.sum(dsn * sn) + np.sum(dzn * zn))
+
+    dq, dk, _, dla, _, _ = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
+    h = 1e-6
+    for which, g in ((0, dq), (1, dk), (2, dla)):
+        base = [q, k, la]
+        x = base[which]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(base), list(base)
+            ap[which], am[which] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+        assert np.max(np.abs(fd - g)) / max(np.max(np.abs(fd)), 1e-12) < 1e-6, which
+
+
+def test_decay_strong_limit():
+    """a = exp(-200): every earlier token and the initial state vanish, so O_t = V_t."""
+    B, H, N, D, M = 1, 2, 12, 4, 3
+    q, k, v = _qkv((B, H, N, D, M), 341)
+    s0, z0, _, _ = _state(B, H, D, M, 345)
+    o, _, _, _ = oracle.forward_decay(q, k, v, np.full((B, H, N), -200.0), s0, z0)
+    np.testing.assert_allclose(o, v, rtol=1e-12, atol=1e-12)
+
+
+def test_decay_decode_equals_forward():
+    """Decayed decode steps (eq. 16-19 with the decay) reproduce the decayed forward and its final state."""
+    B, H, N, D, M = 2, 2, 15, 4, 5
+    q, k, v = _qkv((B, H, N, D, M), 351)
+    la = _log_gates((B, H, N), 355)
+    s0, z0, _, _ = _state(B, H, D, M, 356)
+    o, _, sn, zn = oracle.forward_decay(q, k, v, la, s0, z0)
+    s, z = s0, z0
+    for t in range(N):
+        y, s, z = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, z, la[:, :, t])
+        np.testing.assert_allclose(y, o[:, :, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s, sn, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(z, zn, rtol=1e-12, atol=1e-14)
+
+
+def test_decay_split_continuation():
+    """The final state of a prefix, as the initial state of the rest, continues the decayed forward."""
+    B, H, N, D, M, cut = 2, 2, 21, 4, 3, 8
+    q, k, v = _qkv((B, H, N, D, M), 361)
+    la = _log_gates((B, H, N), 365)
+    o, den, sn, zn = oracle.forward_decay(q, k, v, la)
+    o1, d1, s1, z1 = oracle.forward_decay(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], la[:, :, :cut])
+    o2, d2, s2, z2 = oracle.forward_decay(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], la[:, :, cut:], s1, z1)
+    np.testing.assert_allclose(np.concatenate((o1, o2), 2), o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate((d1, d2), 2), den, rtol=1e-12)
+    np.testing.assert_allclose(s2, sn, rtol=1e-12, atol=1e-14)
+
+
+def test_decay_log_gradient_identity():
+    """logA_l enters the weights of every pair (i, j) with j < l <= i and of the final state, so its gradient
+    is the reverse running sum of phi(Q_m).dphiQ_m - phi(K_m).dphiK_m plus <dSN, S_N> + <dZN, Z_N>."""
+    B, H, N, D, M = 2, 2, 23, 4, 5
+    q, k, v = _qkv((B, H, N, D, M), 371)
+    la = _log_gates((B, H, N), 375)
+    do = inputs.gaussian(v.shape, 376).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 377)
+    dq, dk, _, dla, _, _ = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
+    _, _, sn, zn = oracle.forward_decay(q, k, v, la, s0, z0)
+    qd, kd = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    dpq = dq / np.where(qd > 0, 1.0, np.exp(qd))
+    dpk = dk / np.where(kd > 0, 1.0, np.exp(kd))
+    x = (pins.phi_lib(q) * dpq).sum(-1) - (pins.phi_lib(k) * dpk).sum(-1)
+    tail = (dsn * sn).sum((-1, -2)) + (dzn * zn).sum(-1)
+    ref = np.flip(np.cumsum(np.flip(x, -1), -1), -1) + tail[..., None]
+    np.testing.assert_allclose(dla, ref, rtol=1e-10, atol=1e-12 * np.max(np.abs(ref)))
