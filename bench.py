@@ -8,7 +8,9 @@ at the same shape.  Other workloads (--workload): cifar (16 independent layers
 of B=4 H=8 N=3072 D=M=32, bf16, sigma 0.5, forward + backward each), long
 (B=1 H=16 N=65536 D=M=64, bf16, sigma 1/8, forward + backward), speech (9
 independent non-causal layers of B=16 H=6 N=800 D=M=32, float32, non-causal
-forward + backward each), decode (one
+forward + backward each), long-decay (the long shape with a per-token,
+per-head decay on the state: decayed forward + backward including the
+gradient of the log-decay), decode (one
 step = one la_decode_step on B=256 H=16 D=M=64 after a 512-token prefill),
 small (B=1 H=1 N=64 D=M=32 float32 causal forward).
 
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "speech", "decode", "small"])
+    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "long-decay", "speech", "decode", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
@@ -111,6 +113,11 @@ class Step:
         self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
         if wl == "speech":
             self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+        if wl == "long-decay":
+            self.log_a = torch.from_numpy(w.log_a()).to("cuda").contiguous()
+            self.dla = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+            self.ws_f = binding.alloc_workspace(binding.LA_OP_FWD_DECAY, B, H, N, D, M, code, "cuda")
+            self.ws_b = binding.alloc_workspace(binding.LA_OP_BWD_DECAY, B, H, N, D, M, code, "cuda")
         self.i = 0
 
     def _extra_set(self, i):
@@ -143,7 +150,7 @@ class Step:
         code = b.dtype_code(self.dt)
         qs, ks, vs = self.pool_q.stride(0) * 2, self.pool_k.stride(0) * 2, self.pool_v.stride(0) * 2
         self._args = [(ctypes.c_void_p(self.pool_q.data_ptr() + i * qs), ctypes.c_void_p(self.pool_k.data_ptr() + i * ks),
-                       ctypes.c_void_p(self.pool_v.data_ptr() + i * vs), ctypes.c_void_p(self.S.data_ptr()),
+                       ctypes.c_void_p(self.pool_v.data_ptr() + i * vs), None, ctypes.c_void_p(self.S.data_ptr()),
                        ctypes.c_void_p(self.Z.data_ptr()), ctypes.c_void_p(self.y.data_ptr()), B, H, D, M, code, stream)
                       for i in range(pool)]
         self.i = 0
@@ -166,6 +173,12 @@ class Step:
                 b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n)
                 b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb)
             return
+        if wl == "long-decay":
+            q, k, v, do = self.sets[0]
+            b.la_forward_causal(q, k, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f, logA=self.log_a)
+            b.la_backward_causal(q, k, v, self.o, self.den, do, self.dq, self.dk, self.dv, ckpt=self.ck,
+                                 ws=self.ws_b, logA=self.log_a, dlogA=self.dla)
+            return
         q, k, v, do = self.sets[self.i % len(self.sets)]
         self.i += 1
         if wl == "small":
@@ -183,7 +196,7 @@ class Step:
 
 def WORKLOADS(inputs):
     return {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "speech": inputs.SPEECH,
-            "decode": inputs.DECODE, "small": inputs.SMALL}
+            "long-decay": inputs.LONG_DECAY, "decode": inputs.DECODE, "small": inputs.SMALL}
 
 
 # ---------------------------------------------------- algorithmic figures
@@ -200,6 +213,11 @@ def kernel_bytes(name, w, s):
         "bwd_causal": (4 * D + 3 * M) * s,       # read Q, K, V, dO; write dQ, dK, dV
         "nc_qr": (2 * D + M) * s,                # read Q, dO; write dQ
         "nc_kv": (2 * D + 2 * M) * s,            # read K, V; write dK, dV
+        "dseg_state": (D + M) * s + 4,           # read K, V, logA
+        "dfwd": (2 * D + 2 * M) * s + 8,         # read Q, K, V, logA; write O, den
+        "dbq": (3 * D + 2 * M) * s + 12,         # read Q, K, V, dO, logA; write dQ, (1/den, c)
+        "dbkv": (3 * D + 3 * M) * s + 16,        # read Q, K, V, dO, logA, (1/den, c); write dK, dV, dlogA terms
+        "dla_scan": 8,                           # read and write dlogA
     }
     if name == "decode":
         return w.B * w.H * (2 * D * M * 4 + 2 * D * 4 + (2 * D + 2 * M) * s)
@@ -243,7 +261,9 @@ def traffic_from_profiles(kernel, workload):
 # ------------------------------------------------------ profile summaries
 KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_seg_state<", "seg_state"),
                ("k_scan_states<", "scan_states"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
-               ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"))
+               ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"), ("k_dseg_state<", "dseg_state"),
+               ("k_dscan_states<", "dscan_states"), ("k_dfwd<", "dfwd"), ("k_dbq<", "dbq"),
+               ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_scan<", "dla_scan"))
 
 
 def kernel_tag(full_name):
@@ -417,14 +437,23 @@ def cpu_baseline(args, w):
                 "kind": "oracle", "sample": f"{steps} steps on {nheads} of {w.B * w.H} heads, scaled to all heads"}
     # token workloads: run the oracle's passes of one step on a subset of heads until >= 10 s
     B, H, N = w.B, w.H, w.N
-    nb = {"mnist": 4, "cifar": 1, "long": 1, "speech": 4, "small": 1}[wl]
-    nh = {"mnist": H, "cifar": 8, "long": 2, "speech": H, "small": 1}[wl]
-    n = {"mnist": N, "cifar": N, "long": 16384, "speech": N, "small": N}[wl]
+    nb = {"mnist": 4, "cifar": 1, "long": 1, "long-decay": 1, "speech": 4, "small": 1}[wl]
+    nh = {"mnist": H, "cifar": 8, "long": 2, "long-decay": 2, "speech": H, "small": 1}[wl]
+    n = {"mnist": N, "cifar": N, "long": 16384, "long-decay": 8192, "speech": N, "small": N}[wl]
     q, k, v = (a[:nb, :nh, :n] for a in w.qkv(n=n))
     do = w.grad_out(n=n)[:nb, :nh, :n]
     reps = 0
     t = time.perf_counter()
+    la = w.log_a(n=n)[:nb, :nh, :n] if wl == "long-decay" else None
     while True:
+        if wl == "long-decay":
+            oracle.forward_decay(q, k, v, la)
+            oracle.backward_decay(q, k, v, la, do)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= 10.0 or reps >= 1000:
+                break
+            continue
         if wl == "speech":
             oracle.forward_noncausal(q, k, v)
             oracle.backward_noncausal(q, k, v, do)
@@ -523,6 +552,9 @@ def main():
     elif args.workload == "speech":
         metric, unit = "non-causal linear-attn fwd+bwd tokens/s", "tokens/s"
         value = w.B * w.N * args.steps / el
+    elif args.workload == "long-decay":
+        metric, unit = "decayed causal linear-attn fwd+bwd tokens/s", "tokens/s"
+        value = w.B * w.N * args.steps / el
     else:
         metric, unit = "causal linear-attn fwd+bwd tokens/s", "tokens/s"
         value = w.B * w.N * args.steps / el
@@ -557,6 +589,8 @@ def main():
         cfg["layers"] = 16
     elif args.workload == "long":
         cfg["step"] = "causal forward + backward"
+    elif args.workload == "long-decay":
+        cfg["step"] = "decayed causal forward + backward (dQ, dK, dV, dlogA)"
     elif args.workload == "speech":
         cfg["step"] = "9 layers x (non-causal forward + backward)"
         cfg["layers"] = 9

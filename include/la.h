@@ -66,7 +66,9 @@ typedef enum {
   LA_OP_FWD_NONCAUSAL = 1,
   LA_OP_BWD_CAUSAL = 2,
   LA_OP_DECODE = 3,
-  LA_OP_BWD_NONCAUSAL = 4
+  LA_OP_BWD_NONCAUSAL = 4,
+  LA_OP_FWD_DECAY = 5, /* la_forward_causal with logA */
+  LA_OP_BWD_DECAY = 6  /* la_backward_causal with logA */
 } la_op;
 
 /* Library version, as 10000*major + 100*minor + patch. */
@@ -101,6 +103,15 @@ int la_set_segment_chunks(int chunks);
 /*
  * Causal forward, eq. 9-12 ("Transformers are RNNs -- part 2/3", section 3.3).
  *   Q, K, V     inputs.
+ *   logA        optional [B,H,N] float32 log-decay per token and head
+ *               ("Linear Attention/zh", variants and extensions: RetNet's
+ *               decay, a constant per head, or a data-dependent gate):
+ *               S_t = a_t S_{t-1} + phi(K_t) V_t^T and Z_t = a_t Z_{t-1} +
+ *               phi(K_t) with a_t = exp(logA_t); values must be finite and
+ *               <= 0 (a_t in (0, 1]).  NULL: the plain running sums.  The
+ *               workspace is then la_workspace_size(LA_OP_FWD_DECAY, ...),
+ *               and the checkpoint holds the decayed states (valid only for
+ *               a backward with the same logA).
  *   O           output [B,H,N,M] in `dtype` (float32 values rounded to
  *               nearest even for bf16).
  *   den         optional output [B,H,N] float32: phi(Q_i)^T Z_i (needed by
@@ -112,11 +123,11 @@ int la_set_segment_chunks(int chunks);
  *   ckpt        optional output of la_checkpoint_size(...) bytes: segment
  *               boundary states for la_backward_causal.  NULL to skip.
  */
-int la_forward_causal(const void *Q, const void *K, const void *V, void *O,
-                      float *den, const float *S0, const float *Z0,
-                      float *S_out, float *Z_out, float *ckpt, int B, int H,
-                      int N, int D, int M, int dtype, void *ws,
-                      size_t ws_bytes, void *stream);
+int la_forward_causal(const void *Q, const void *K, const void *V,
+                      const float *logA, void *O, float *den, const float *S0,
+                      const float *Z0, float *S_out, float *Z_out,
+                      float *ckpt, int B, int H, int N, int D, int M,
+                      int dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
@@ -136,6 +147,11 @@ int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
  * The denominator's share (left by the pages to automatic differentiation)
  * is the quotient rule: dL/dnum_i = dO_i / den_i, dL/dden_i =
  * -(dO_i . O_i) / den_i.
+ *   logA        the forward's log-decay, or NULL (see la_forward_causal).
+ *               With logA the workspace is la_workspace_size(
+ *               LA_OP_BWD_DECAY, ...) and O, den are validated but not read
+ *               (den_i and O_i . dO_i are recomputed in the order that keeps
+ *               every decay factor <= 1).
  *   O, den      the forward's O and den (required when N > 0).
  *   S0, Z0      the initial state the forward started from (both or neither).
  *   ckpt        the forward's checkpoint (same sizes) or NULL: then the
@@ -146,6 +162,8 @@ int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
  *               Every term phi(K_j) V_j^T is part of S_N, so they start the
  *               backward-running sum of eq. 14-15.
  *   dQ, dK, dV  outputs in `dtype`.
+ *   dlogA       [B,H,N] float32 output, required with logA and NULL
+ *               without: the gradient with respect to logA.
  *   dS0, dZ0    optional outputs [B,H,D,M], [B,H,D] float32 (both or
  *               neither): the gradient with respect to the initial state S0,
  *               Z0 (zero state when those were NULL), i.e. the
@@ -155,10 +173,11 @@ int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
  *               dS_N, dZ_N (zero when NULL) and nothing else is read.
  */
 int la_backward_causal(const void *Q, const void *K, const void *V,
-                       const void *O, const float *den, const void *dO,
-                       const float *S0, const float *Z0, const float *ckpt,
-                       const float *dS_N, const float *dZ_N, void *dQ,
-                       void *dK, void *dV, float *dS0, float *dZ0, int B, int H,
+                       const float *logA, const void *O, const float *den,
+                       const void *dO, const float *S0, const float *Z0,
+                       const float *ckpt, const float *dS_N,
+                       const float *dZ_N, void *dQ, void *dK, void *dV,
+                       float *dlogA, float *dS0, float *dZ0, int B, int H,
                        int N, int D, int M, int dtype, void *ws,
                        size_t ws_bytes, void *stream);
 
@@ -187,14 +206,16 @@ int la_backward_noncausal(const void *Q, const void *K, const void *V,
  * One RNN step of the attention ("Transformers are RNNs -- part 2/3",
  * section 3.4, eq. 18-20 without the projections, f_l and residual):
  *   S += phi(k) v^T;  Z += phi(k);  y = phi(q)^T S / phi(q)^T Z.
+ *   logA        optional [B,H] float32 log-decay of this step (as in
+ *               la_forward_causal): S = a S + phi(k) v^T, Z = a Z + phi(k).
  *   q, k [B,H,D], v [B,H,M], y [B,H,M] in `dtype`; S [B,H,D,M] and Z [B,H,D]
  *   float32, updated in place (the update comes first: masking is
  *   inclusive).  Calls on one stream are ordered; overlapping calls on
  *   different streams that share S/Z race.
  */
-int la_decode_step(const void *q, const void *k, const void *v, float *S,
-                   float *Z, void *y, int B, int H, int D, int M, int dtype,
-                   void *stream);
+int la_decode_step(const void *q, const void *k, const void *v,
+                   const float *logA, float *S, float *Z, void *y, int B,
+                   int H, int D, int M, int dtype, void *stream);
 
 /* Name of a status code. */
 const char *la_status_string(int status);

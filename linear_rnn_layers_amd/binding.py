@@ -19,6 +19,7 @@ from . import build as _build
 
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_DECODE, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3, 4
+LA_OP_FWD_DECAY, LA_OP_BWD_DECAY = 5, 6
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
                 "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
                 "la_status_string", "la_last_error", "la_prof_select", "la_prof_collect", "la_kernel_names",
@@ -54,15 +55,15 @@ def load(path: str | None = None):
     lib.la_segment_length.restype = i
     lib.la_segment_length.argtypes = [i] * 5
     lib.la_forward_causal.restype = i
-    lib.la_forward_causal.argtypes = [vp] * 10 + [i] * 6 + [vp, sz, vp]
+    lib.la_forward_causal.argtypes = [vp] * 11 + [i] * 6 + [vp, sz, vp]
     lib.la_forward_noncausal.restype = i
     lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
     lib.la_backward_causal.restype = i
-    lib.la_backward_causal.argtypes = [vp] * 16 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_causal.argtypes = [vp] * 18 + [i] * 6 + [vp, sz, vp]
     lib.la_backward_noncausal.restype = i
     lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
     lib.la_decode_step.restype = i
-    lib.la_decode_step.argtypes = [vp] * 6 + [i] * 5 + [vp]
+    lib.la_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_last_error.restype = ctypes.c_char_p
@@ -143,12 +144,13 @@ def alloc_workspace(op: int, B, H, N, D, M, dtype: int, device) -> torch.Tensor:
 
 # --------------------------------------------------------- one-to-one calls
 def la_forward_causal(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=None, ckpt=None, ws=None,
-                      stream=None):
+                      stream=None, logA=None):
     B, H, N, D, M = _sizes(Q, V)
     dt = dtype_code(Q.dtype)
     nb = ws.numel() if ws is not None else 0
-    st = load().la_forward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(den), _ptr(S0), _ptr(Z0), _ptr(S_out),
-                                  _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, _ptr(ws), nb, _stream(stream))
+    st = load().la_forward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(logA), _ptr(O), _ptr(den), _ptr(S0), _ptr(Z0),
+                                  _ptr(S_out), _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, _ptr(ws), nb,
+                                  _stream(stream))
     _check(st, "la_forward_causal")
 
 
@@ -161,12 +163,13 @@ def la_forward_noncausal(Q, K, V, O, ws=None, stream=None):
 
 
 def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, dS_N=None, dZ_N=None,
-                       dS0=None, dZ0=None, ws=None, stream=None):
+                       dS0=None, dZ0=None, ws=None, stream=None, logA=None, dlogA=None):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
-    st = load().la_backward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(den), _ptr(dO), _ptr(S0), _ptr(Z0),
-                                   _ptr(ckpt), _ptr(dS_N), _ptr(dZ_N), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS0),
-                                   _ptr(dZ0), B, H, N, D, M, dtype_code(Q.dtype), _ptr(ws), nb, _stream(stream))
+    st = load().la_backward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(logA), _ptr(O), _ptr(den), _ptr(dO), _ptr(S0),
+                                   _ptr(Z0), _ptr(ckpt), _ptr(dS_N), _ptr(dZ_N), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                   _ptr(dlogA), _ptr(dS0), _ptr(dZ0), B, H, N, D, M, dtype_code(Q.dtype), _ptr(ws),
+                                   nb, _stream(stream))
     _check(st, "la_backward_causal")
 
 
@@ -178,19 +181,19 @@ def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None):
     _check(st, "la_backward_noncausal")
 
 
-def la_decode_step(q, k, v, S, Z, y, stream=None):
+def la_decode_step(q, k, v, S, Z, y, stream=None, logA=None):
     if q.dim() != 3:
         raise ValueError("decode expects q, k [B,H,D], v [B,H,M]")
     B, H, D = q.shape
     M = v.shape[-1]
-    st = load().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(Z), _ptr(y), B, H, D, M,
+    st = load().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(logA), _ptr(S), _ptr(Z), _ptr(y), B, H, D, M,
                                dtype_code(q.dtype), _stream(stream))
     _check(st, "la_decode_step")
 
 
 # ------------------------------------------------------ allocating helpers
-def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=True):
-    """Causal forward.  Returns dict(o, den, ckpt[, s, z])."""
+def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=True, log_a=None):
+    """Causal forward (decayed by exp(log_a) [B,H,N] float32 when given).  Returns dict(o, den, ckpt[, s, z])."""
     B, H, N, D, M = _sizes(q, v)
     dev = q.device
     o = torch.empty((B, H, N, M), dtype=q.dtype, device=dev)
@@ -200,8 +203,9 @@ def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=
     if return_state:
         s = torch.empty((B, H, D, M), dtype=torch.float32, device=dev)
         z = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    ws = alloc_workspace(LA_OP_FWD_CAUSAL, B, H, N, D, M, dtype_code(q.dtype), dev)
-    la_forward_causal(q, k, v, o, den, s0, z0, s, z, ck, ws)
+    ws = alloc_workspace(LA_OP_FWD_DECAY if log_a is not None else LA_OP_FWD_CAUSAL, B, H, N, D, M,
+                         dtype_code(q.dtype), dev)
+    la_forward_causal(q, k, v, o, den, s0, z0, s, z, ck, ws, logA=log_a)
     out = {"o": o, "den": den, "ckpt": ck}
     if return_state:
         out["s"], out["z"] = s, z
@@ -216,20 +220,26 @@ def forward_noncausal(q, k, v):
     return o
 
 
-def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=None, dz_n=None, state_grad=False):
-    """Causal backward.  Returns (dq, dk, dv), and with state_grad also (ds0, dz0), the gradient with respect to
-    the initial state; ds_n, dz_n are the upstream gradients of the final state (None: not in the loss)."""
+def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=None, dz_n=None, state_grad=False,
+                    log_a=None):
+    """Causal backward.  Returns (dq, dk, dv), then dlog_a when log_a is given, then (ds0, dz0) with
+    state_grad: the gradient with respect to the initial state; ds_n, dz_n are the upstream gradients of the
+    final state (None: not in the loss)."""
     B, H, N, D, M = _sizes(q, v)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ds0 = dz0 = None
+    ds0 = dz0 = dla = None
     if state_grad:
         ds0 = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
         dz0 = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
-    ws = alloc_workspace(LA_OP_BWD_CAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ds_n, dz_n, ds0, dz0, ws)
-    return (dq, dk, dv, ds0, dz0) if state_grad else (dq, dk, dv)
+    if log_a is not None:
+        dla = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = alloc_workspace(LA_OP_BWD_DECAY if log_a is not None else LA_OP_BWD_CAUSAL, B, H, N, D, M,
+                         dtype_code(q.dtype), q.device)
+    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ds_n, dz_n, ds0, dz0, ws, logA=log_a, dlogA=dla)
+    out = (dq, dk, dv) + ((dla,) if log_a is not None else ())
+    return out + ((ds0, dz0) if state_grad else ())
 
 
 def backward_noncausal(q, k, v, do):
@@ -242,11 +252,11 @@ def backward_noncausal(q, k, v, do):
     return dq, dk, dv
 
 
-def decode_step(q, k, v, s, z, y=None):
-    """One RNN step: updates s, z in place and returns y."""
+def decode_step(q, k, v, s, z, y=None, log_a=None):
+    """One RNN step (decayed by exp(log_a) [B,H] when given): updates s, z in place and returns y."""
     if y is None:
         y = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    la_decode_step(q, k, v, s, z, y)
+    la_decode_step(q, k, v, s, z, y, logA=log_a)
     return y
 
 
@@ -256,34 +266,39 @@ class CausalLinearAttention(torch.autograd.Function):
     gradient flows back through the same backward."""
 
     @staticmethod
-    def forward(ctx, q, k, v, s0, z0, return_state):
+    def forward(ctx, q, k, v, s0, z0, return_state, log_a):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         if (s0 is None) != (z0 is None):
             raise ValueError("s0 and z0 go together")
         if s0 is not None:
             s0, z0 = s0.contiguous(), z0.contiguous()
-        out = forward_causal(q, k, v, s0=s0, z0=z0, return_state=return_state)
+        if log_a is not None:
+            log_a = log_a.contiguous()
+        out = forward_causal(q, k, v, s0=s0, z0=z0, return_state=return_state, log_a=log_a)
         ctx.has_state = s0 is not None
-        ctx.return_state = return_state
-        ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"], s0, z0)
+        ctx.has_decay = log_a is not None
+        ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"], s0, z0, log_a)
         if return_state:
             return out["o"], out["s"], out["z"]
         return out["o"]
 
     @staticmethod
     def backward(ctx, do, ds_n=None, dz_n=None):
-        q, k, v, o, den, ck, s0, z0 = ctx.saved_tensors
+        q, k, v, o, den, ck, s0, z0, log_a = ctx.saved_tensors
         want_state = ctx.has_state and (ctx.needs_input_grad[3] or ctx.needs_input_grad[4])
         if ds_n is not None:
             ds_n, dz_n = ds_n.contiguous(), dz_n.contiguous()
-        g = backward_causal(q, k, v, o, den, do.contiguous(), s0=s0, z0=z0, ckpt=ck, ds_n=ds_n, dz_n=dz_n,
-                            state_grad=want_state)
+        g = list(backward_causal(q, k, v, o, den, do.contiguous(), s0=s0, z0=z0, ckpt=ck, ds_n=ds_n, dz_n=dz_n,
+                                 state_grad=want_state, log_a=log_a))
+        dla = g.pop(3) if ctx.has_decay else None
         ds0, dz0 = (g[3], g[4]) if want_state else (None, None)
-        return g[0], g[1], g[2], ds0, dz0, None
+        return g[0], g[1], g[2], ds0, dz0, None, dla
 
 
-def causal_linear_attention(q, k, v, s0=None, z0=None, return_state=False):
-    return CausalLinearAttention.apply(q, k, v, s0, z0, return_state)
+def causal_linear_attention(q, k, v, s0=None, z0=None, return_state=False, log_a=None):
+    """Causal linear attention through the HIP library, differentiable in q, k, v, the initial state (s0, z0)
+    and the log-decay log_a [B,H,N] (float32, <= 0) when given."""
+    return CausalLinearAttention.apply(q, k, v, s0, z0, return_state, log_a)
 
 
 class NonCausalLinearAttention(torch.autograd.Function):

@@ -16,7 +16,7 @@
 #include <vector>
 
 #include "../../include/la.h"
-#include "la_kernels.h"
+#include "la_decay.h"
 
 namespace {
 
@@ -38,6 +38,7 @@ int fail(int status, const std::string& msg) {
 // segment plan depends on the sizes only.
 struct Plan {
   long BH = 0;
+  long N = 0;
   int L = 0;
   int nseg = 0;
   int SV = 0;  // floats per state vector: D*M + D
@@ -51,6 +52,7 @@ std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
 Plan make_plan(int B, int H, int N, int D, int M) {
   Plan p;
   p.BH = (long)B * H;
+  p.N = N;
   p.SV = D * M + D;
   const long nchunks = ((long)N + la::CH - 1) / la::CH;
   if (N <= 0) {
@@ -115,8 +117,8 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 
 // Workspace regions (bytes) per operation.
 struct WsLayout {
-  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0;
-  size_t bytes() const { return agg + ckpt + ragg + rpref; }
+  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0;
+  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc; }
 };
 
 // fwd causal: aggregates and prefix states when there is more than one
@@ -151,6 +153,20 @@ WsLayout ws_layout(int op, const Plan& p) {
       w.ckpt = state_bytes(p, p.nseg + 1);
       w.ragg = state_bytes(p, p.nseg);
       w.rpref = state_bytes(p, p.nseg + 1);
+      break;
+    case LA_OP_FWD_DECAY:  // aggregates, per-segment log-decay sums and the prefix states
+      if (p.nseg > 1) {
+        w.agg = state_bytes(p, p.nseg);
+        w.ckpt = state_bytes(p, p.nseg + 1);
+        w.dlam = align256((size_t)p.BH * p.nseg * sizeof(float));
+      }
+      break;
+    case LA_OP_BWD_DECAY:  // checkpoint recomputation, log-decay sums, reverse aggregates, (1/den, c) per token
+      w.agg = state_bytes(p, p.nseg);
+      w.ckpt = state_bytes(p, p.nseg + 1);
+      w.dlam = align256((size_t)p.BH * p.nseg * sizeof(float));
+      w.ragg = state_bytes(p, p.nseg);
+      w.gc = align256((size_t)p.BH * p.N * 2 * sizeof(float));
       break;
     default:
       break;
@@ -413,10 +429,77 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
                 (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg);
 }
 
+// ----------------------------------------------------- decayed recurrence
 template <typename T, int D, int M>
-int decode_impl(long BH, const void* q, const void* k, const void* v, float* S, float* Z, void* y, hipStream_t s) {
+int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, void* O,
+                   float* den, const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int N,
+                   void* ws, hipStream_t s) {
+  if (p.nseg == 0)
+    return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
+                  Z_out);
+  const float* pref = nullptr;
+  if (p.nseg > 1) {  // segment aggregates and their decayed prefix states (into the checkpoint when given)
+    const WsLayout wl = ws_layout(LA_OP_FWD_DECAY, p);
+    float* agg = reinterpret_cast<float*>(region(ws, 0));
+    float* dlam = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
+    int st = launch("dseg_state", la::k_dseg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                    (const T*)K, (const T*)V, logA, agg, dlam, N, p.L, p.nseg);
+    if (st) return st;
+    float* pr = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
+    st = launch("dscan_states", la::k_dscan_states<D, M>, scan_grid(p), dim3(la::NT), s, (const float*)agg,
+                (const float*)dlam, S0, Z0, pr, p.nseg);
+    if (st) return st;
+    pref = pr;
+  }
+  return launch("dfwd", la::k_dfwd<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s, (const T*)Q,
+                (const T*)K, (const T*)V, logA, (T*)O, den, pref, S0, Z0, pref ? (float*)nullptr : ckpt, S_out, Z_out,
+                N, p.L, p.nseg);
+}
+
+template <typename T, int D, int M>
+int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, const void* dO,
+                   const float* S0, const float* Z0, const float* ckpt, const float* dSN, const float* dZN, void* dQ,
+                   void* dK, void* dV, float* dlogA, float* dS0, float* dZ0, int N, void* ws, hipStream_t s) {
+  if (p.nseg == 0)
+    return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
+                        (float*)nullptr, dS0, dZ0)
+               : LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_BWD_DECAY, p);
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
+  float* dlam = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
+  float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.dlam));
+  float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.dlam + wl.ragg));
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  int st = LA_OK;
+  const float* ck = ckpt;
+  if (!ck) {  // recompute the checkpoint
+    st = launch("dseg_state", la::k_dseg_state<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, logA, agg,
+                dlam, N, p.L, p.nseg);
+    if (st) return st;
+    st = launch("dscan_states", la::k_dscan_states<D, M>, scan_grid(p), dim3(la::NT), s, (const float*)agg,
+                (const float*)dlam, S0, Z0, ckw, p.nseg);
+    if (st) return st;
+    ck = ckw;
+  }
+  st = launch("dbq", la::k_dbq<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V, (const T*)dO,
+              logA, ck, (T*)dQ, gc, ragg, dlam, N, p.L, p.nseg);
+  if (st) return st;
+  st = launch("dscan_rev", la::k_dscan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, (const float*)dlam, dSN, dZN,
+              dS0, dZ0, p.nseg);
+  if (st) return st;
+  st = launch("dbkv", la::k_dbkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+              (const T*)dO, logA, (const float2*)gc, (const float*)ragg, (T*)dK, (T*)dV, dlogA, N, p.L, p.nseg);
+  if (st) return st;
+  return launch("dla_scan", la::k_dla_scan<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dlogA, ck, dSN, dZN, N,
+                p.nseg);
+}
+
+template <typename T, int D, int M>
+int decode_impl(long BH, const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
+                hipStream_t s) {
   return launch("decode", la::k_decode<T, D, M>, dim3((unsigned)((BH + 3) / 4)), dim3(la::NT), s, (const T*)q,
-                (const T*)k, (const T*)v, S, Z, (T*)y, (int)BH);
+                (const T*)k, (const T*)v, logA, S, Z, (T*)y, (int)BH);
 }
 
 size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
@@ -448,12 +531,12 @@ const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
-         "state_copy";
+         "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_scan";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
   if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
-  if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_NONCAUSAL) return 0;
+  if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
   return ws_layout(op, make_plan(B, H, N, D, M)).bytes();
 }
 
@@ -473,9 +556,9 @@ int la_set_segment_chunks(int chunks) {
   return g_seg_chunks.exchange(chunks);
 }
 
-int la_forward_causal(const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
-                      const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H, int N, int D, int M,
-                      int dtype, void* ws, size_t ws_bytes, void* stream) {
+int la_forward_causal(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
+                      const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H, int N,
+                      int D, int M, int dtype, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
@@ -484,12 +567,13 @@ int la_forward_causal(const void* Q, const void* K, const void* V, void* O, floa
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
-  const size_t need = ws_layout(LA_OP_FWD_CAUSAL, p).bytes();
+  const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
   if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
-                   rng("V", V, bh * N * M * es, false), rng("S0", S0, bh * D * M * 4, false),
+                   rng("V", V, bh * N * M * es, false), rng("logA", logA, bh * N * 4, false),
+                   rng("S0", S0, bh * D * M * 4, false),
                    rng("Z0", Z0, bh * D * 4, false), rng("O", O, bh * N * M * es, true),
                    rng("den", den, bh * N * 4, true), rng("S_out", S_out, bh * D * M * 4, true),
                    rng("Z_out", Z_out, bh * D * 4, true),
@@ -497,6 +581,9 @@ int la_forward_causal(const void* Q, const void* K, const void* V, void* O, floa
                    rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
   if (N == 0 && !S_out && !ckpt) return LA_OK;
+  if (logA)
+    LA_DISPATCH(dtype, D, M, fwd_decay_impl, p, Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
+                (hipStream_t)stream);
   LA_DISPATCH(dtype, D, M, fwd_causal_impl, p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
               (hipStream_t)stream);
 }
@@ -520,13 +607,15 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, i
   LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, N, ws, (hipStream_t)stream);
 }
 
-int la_backward_causal(const void* Q, const void* K, const void* V, const void* O, const float* den,
-                       const void* dO, const float* S0, const float* Z0, const float* ckpt, const float* dS_N,
-                       const float* dZ_N, void* dQ, void* dK, void* dV, float* dS0, float* dZ0, int B, int H, int N,
-                       int D, int M, int dtype, void* ws, size_t ws_bytes, void* stream) {
+int la_backward_causal(const void* Q, const void* K, const void* V, const float* logA, const void* O,
+                       const float* den, const void* dO, const float* S0, const float* Z0, const float* ckpt,
+                       const float* dS_N, const float* dZ_N, void* dQ, void* dK, void* dV, float* dlogA, float* dS0,
+                       float* dZ0, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
+                       void* stream) {
   g_err.clear();
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
+  if ((logA == nullptr) != (dlogA == nullptr)) return fail(LA_ERR_ARG, "logA and dlogA must be given together");
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((dS_N == nullptr) != (dZ_N == nullptr)) return fail(LA_ERR_ARG, "dS_N and dZ_N must be given together");
   if ((dS0 == nullptr) != (dZ0 == nullptr)) return fail(LA_ERR_ARG, "dS0 and dZ0 must be given together");
@@ -544,20 +633,24 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const void* 
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype);
-  const size_t need = ws_layout(LA_OP_BWD_CAUSAL, p).bytes();
-  const bool uses_ws = need > 0 && (ckpt == nullptr || p.nseg > 1);
+  const size_t need = ws_layout(logA ? LA_OP_BWD_DECAY : LA_OP_BWD_CAUSAL, p).bytes();
+  const bool uses_ws = need > 0 && (logA || ckpt == nullptr || p.nseg > 1);
   if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
-                   rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, false),
-                   rng("den", den, bh * N * 4, false), rng("dO", dO, bh * N * M * es, false),
-                   rng("S0", S0, bh * D * M * 4, false), rng("Z0", Z0, bh * D * 4, false),
-                   rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), false),
+                   rng("V", V, bh * N * M * es, false), rng("logA", logA, bh * N * 4, false),
+                   rng("O", O, bh * N * M * es, false), rng("den", den, bh * N * 4, false),
+                   rng("dO", dO, bh * N * M * es, false), rng("S0", S0, bh * D * M * 4, false),
+                   rng("Z0", Z0, bh * D * 4, false), rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), false),
                    rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
-                   rng("dV", dV, bh * N * M * es, true), rng("dS0", dS0, bh * D * M * 4, true),
-                   rng("dZ0", dZ0, bh * D * 4, true), rng("ws", uses_ws ? ws : nullptr, need, true)});
+                   rng("dV", dV, bh * N * M * es, true), rng("dlogA", dlogA, bh * N * 4, true),
+                   rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true),
+                   rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
+  if (logA)
+    LA_DISPATCH(dtype, D, M, bwd_decay_impl, p, Q, K, V, logA, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dlogA, dS0,
+                dZ0, N, ws, (hipStream_t)stream);
   LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0,
               N, ws, (hipStream_t)stream);
 }
@@ -583,17 +676,18 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
   LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, dQ, dK, dV, N, ws, (hipStream_t)stream);
 }
 
-int la_decode_step(const void* q, const void* k, const void* v, float* S, float* Z, void* y, int B, int H, int D,
-                   int M, int dtype, void* stream) {
+int la_decode_step(const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
+                   int B, int H, int D, int M, int dtype, void* stream) {
   g_err.clear();
   int st = check_sizes(B, H, 1, D, M, dtype);
   if (st) return st;
   if (!q || !k || !v || !S || !Z || !y) return fail(LA_ERR_NULL, "q, k, v, S, Z and y are required");
   const size_t es = esize(dtype), bh = (size_t)B * H;
   st = check_ptrs({rng("q", q, bh * D * es, false), rng("k", k, bh * D * es, false), rng("v", v, bh * M * es, false),
-                   rng("S", S, bh * D * M * 4, true), rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
+                   rng("logA", logA, bh * 4, false), rng("S", S, bh * D * M * 4, true),
+                   rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, S, Z, y, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, (hipStream_t)stream);
 }
 
 int la_prof_select(const char* kernel_name) {

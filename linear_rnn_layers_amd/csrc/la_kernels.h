@@ -1349,13 +1349,16 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
 
 // ================================================================= decode
 // One RNN step per head (eq. 18-20): S += phi(k) v^T, Z += phi(k),
-// y = phi(q)^T S / phi(q)^T Z.  One wavefront per head streams the head's
+// y = phi(q)^T S / phi(q)^T Z; with a log-decay per head ("Linear
+// Attention/zh", RetNet and gated variants) S = a S + phi(k) v^T and
+// Z = a Z + phi(k), a = exp(logA[head]).  One wavefront per head streams the head's
 // D x M float32 state through registers in 1 KiB coalesced rows per
 // instruction, updates it in place and reduces phi(q)^T S across lanes.
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
-                                                const T* __restrict__ v, float* __restrict__ S,
-                                                float* __restrict__ Z, T* __restrict__ y, int BH) {
+                                                const T* __restrict__ v, const float* __restrict__ logA,
+                                                float* __restrict__ S, float* __restrict__ Z, T* __restrict__ y,
+                                                int BH) {
   constexpr int NV = D * M / 4 / 64;  // float4 per lane
   constexpr int CPL = M / 4;          // lanes covering one state row
   constexpr int RPI = 64 / CPL;       // state rows per instruction
@@ -1370,12 +1373,13 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
       return bf2f(*reinterpret_cast<const bf16_t*>(p));
   };
   float zn = 0.f;
+  const float a = live && logA ? __builtin_amdgcn_exp2f(logA[head] * 1.4426950408889634f) : 1.f;
   if (live) {
     if (l < D) {
       sq[w][l] = phi(ld(q + (size_t)head * D + l));
       const float pk = phi(ld(k + (size_t)head * D + l));
       sk[w][l] = pk;
-      zn = Z[(size_t)head * D + l] + pk;
+      zn = a * Z[(size_t)head * D + l] + pk;
     }
     if (l < M) sv[w][l] = ld(v + (size_t)head * M + l);
   }
@@ -1394,10 +1398,10 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
     const int d = l / CPL + RPI * it;
     const float pk = sk[w][d], pq = sq[w][d];
     float4 s = st[it];
-    s.x += pk * v0;
-    s.y += pk * v1;
-    s.z += pk * v2;
-    s.w += pk * v3;
+    s.x = a * s.x + pk * v0;
+    s.y = a * s.y + pk * v1;
+    s.z = a * s.z + pk * v2;
+    s.w = a * s.w + pk * v3;
     S4[l + 64 * it] = s;
     y0 += pq * s.x;
     y1 += pq * s.y;

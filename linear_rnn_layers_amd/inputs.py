@@ -63,6 +63,8 @@ class Workload:
     seeds: tuple  # seeds for Q, K, V, dO (and extra as the workload needs)
     layers: int = 1
     steps: int = 0  # decode steps (decode workload only)
+    gate_seed: int = 0  # decayed workloads: seed of the per-token gates
+    gate_bias: float = 3.0
 
     def qkv(self, layer: int = 0, n: int | None = None):
         """Q [B,H,N,D], K [B,H,N,D], V [B,H,N,M] for one layer (float32 arrays)."""
@@ -93,6 +95,15 @@ class Workload:
         v = gaussian((self.B, self.H, self.M), base + 2, 1.0, self.dtype)
         return q, k, v
 
+    def log_a(self, n: int | None = None):
+        """Per-token, per-head log-decay [B,H,N] float32 for the decayed workloads: the log of a gate
+        a = 1 / (1 + exp(-x)), x ~ N(gate_bias, 1) (seed gate_seed); None for the others."""
+        if not self.gate_seed:
+            return None
+        n = self.N if n is None else n
+        x = gaussian((self.B, self.H, n), self.gate_seed).astype(np.float64) + self.gate_bias
+        return (-np.log1p(np.exp(-x))).astype(np.float32)
+
     @property
     def tokens(self) -> int:
         return self.B * self.N
@@ -109,7 +120,11 @@ LONG = Workload("long-b1h16n65536d64-bf16", 1, 16, 65536, 64, 64, BF16, 1.0 / 8.
 # (the pages give no batch size; 16 as in the MNIST workload).
 SPEECH = Workload("speech-encoder-9layers-b16h6n800d32-f32", 16, 6, 800, 32, 32, F32, 1.0, (6000, 6001, 6002, 6003),
                   layers=9)
+# The long sequence with a data-dependent decay on the state (gated variant of the recurrence): per-token gates
+# 1 / (1 + exp(-x)), x ~ N(3, 1), i.e. about 0.95 on average.
+LONG_DECAY = Workload("long-decay-b1h16n65536d64-bf16", 1, 16, 65536, 64, 64, BF16, 1.0 / 8.0, (421, 422, 423, 424),
+                      gate_seed=425)
 DECODE = Workload("decode-b256h16d64-4096steps-bf16", 256, 16, 512, 64, 64, BF16, 1.0, (501, 502, 503, 504),
                   steps=4096)
 
-WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, DECODE)}
+WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, LONG_DECAY, DECODE)}

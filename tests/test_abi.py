@@ -60,17 +60,18 @@ def addr(i):
 
 
 def fwd(lib, B=2, H=2, N=100, D=32, M=32, dtype=0, ws=True, **over):
-    args = dict(Q=addr(1), K=addr(2), V=addr(3), O=addr(4), den=addr(5), S0=None, Z0=None, S_out=None, Z_out=None,
-                ckpt=None)
+    args = dict(Q=addr(1), K=addr(2), V=addr(3), logA=None, O=addr(4), den=addr(5), S0=None, Z0=None, S_out=None,
+                Z_out=None, ckpt=None)
     args.update(over)
-    need = lib.la_workspace_size(0, B, H, N, D, M, dtype)
+    need = lib.la_workspace_size(5 if args["logA"] else 0, B, H, N, D, M, dtype)
     wsp = addr(20) if ws else None
     nb = need if ws else 0
     if "ws_bytes" in over:
         nb = over.pop("ws_bytes")
         args.pop("ws_bytes")
-    return lib.la_forward_causal(args["Q"], args["K"], args["V"], args["O"], args["den"], args["S0"], args["Z0"],
-                                 args["S_out"], args["Z_out"], args["ckpt"], B, H, N, D, M, dtype, wsp, nb, None)
+    return lib.la_forward_causal(args["Q"], args["K"], args["V"], args["logA"], args["O"], args["den"], args["S0"],
+                                 args["Z0"], args["S_out"], args["Z_out"], args["ckpt"], B, H, N, D, M, dtype, wsp, nb,
+                                 None)
 
 
 def test_forward_validation(lib):
@@ -101,7 +102,8 @@ def test_noncausal_and_backward_validation(lib):
     # N = 0 is a no-op
     assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, None, 0, None) == OK
     wsb = lib.la_workspace_size(2, 2, 2, 100, 32, 32, 0)
-    names = ["Q", "K", "V", "O", "den", "dO", "S0", "Z0", "ckpt", "dS_N", "dZ_N", "dQ", "dK", "dV", "dS0", "dZ0"]
+    names = ["Q", "K", "V", "logA", "O", "den", "dO", "S0", "Z0", "ckpt", "dS_N", "dZ_N", "dQ", "dK", "dV", "dlogA",
+             "dS0", "dZ0"]
     base = dict(Q=addr(1), K=addr(2), V=addr(3), O=addr(4), den=addr(5), dO=addr(6), dQ=addr(7), dK=addr(8),
                 dV=addr(9))
 
@@ -121,6 +123,20 @@ def test_noncausal_and_backward_validation(lib):
     assert bwd(N=0, ws=None, nb=0) == OK
     # N = 0 with a state gradient requested still validates that request (no launch happens on failure)
     assert bwd(N=0, ws=None, nb=0, dS0=addr(12), dZ0=addr(13), dS_N=addr(12), dZ_N=addr(11)) == ALIAS
+    # decayed recurrence: logA and dlogA go together, dlogA is an output, the workspace grows
+    assert bwd(logA=addr(14)) == ARG
+    assert bwd(dlogA=addr(15)) == ARG
+    wsd = lib.la_workspace_size(6, 2, 2, 100, 32, 32, 0)
+    assert wsd > wsb
+    assert bwd(logA=addr(14), dlogA=addr(15), nb=wsb) == WORKSPACE
+    assert bwd(logA=addr(14), dlogA=addr(14), nb=wsd) == ALIAS
+    assert bwd(logA=ctypes.c_void_p(BASE + 14 * (1 << 32) + 4), dlogA=addr(15), nb=wsd) == ALIGN
+
+
+def test_decay_forward_validation(lib):
+    assert fwd(lib, logA=addr(14), ws_bytes=lib.la_workspace_size(0, 2, 2, 100, 32, 32, 0)) == WORKSPACE
+    assert fwd(lib, logA=addr(4)) == ALIAS  # O on top of logA
+    assert fwd(lib, logA=ctypes.c_void_p(BASE + 14 * (1 << 32) + 8)) == ALIGN
 
 
 def test_noncausal_backward_validation(lib):
@@ -139,10 +155,13 @@ def test_noncausal_backward_validation(lib):
 
 
 def test_decode_validation(lib):
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), None, 2, 2, 64, 64, 1, None) == NULL
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, None) == ALIAS
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), 2, 2, 16, 64, 1, None) == UNSUPPORTED
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, None) == SHAPE
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), None, 2, 2, 64, 64, 1, None) == NULL
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, None) == ALIAS
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(5), addr(6), 2, 2, 64, 64, 1,
+                              None) == ALIAS  # S on top of logA
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 16, 64, 1,
+                              None) == UNSUPPORTED
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, None) == SHAPE
 
 
 def _plan(B, H, N):
@@ -173,6 +192,11 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     assert lib.la_workspace_size(2, B, H, N, D, M, 0) == bwd
     # non-causal backward: key aggregates + scan, reverse aggregates + scan
     assert lib.la_workspace_size(4, B, H, N, D, M, 0) == 2 * (agg + pref)
+    # decayed forward: aggregates, prefix states, per-segment log-decay sums (more than one segment);
+    # decayed backward: those, reverse aggregates and (1/den, c) per token
+    dl = _al(B * H * nseg * 4)
+    assert lib.la_workspace_size(5, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref + dl)
+    assert lib.la_workspace_size(6, B, H, N, D, M, 1) == agg + pref + dl + agg + _al(B * H * N * 8)
     assert lib.la_workspace_size(9, B, H, N, D, M, 0) == 0
 
 

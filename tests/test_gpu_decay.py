@@ -1,0 +1,292 @@
+"""GPU parity of the decayed recurrence (per-token, per-head log-decay on S and Z) against the float64 oracle.
+
+Gate as elsewhere: rowerr <= 1e-4 (float32 storage) / 2e-2 (bf16).  Rows whose value is a cancellation of
+larger terms (dQ always, dK where the decay makes O_i close to V_i) are floored at 1e-2 of the cancelled terms,
+computed here from the plain recurrences.  dlogA_t is the running sum over m >= t of -phi(K_m).dphiK_m (plus
+the final-state term), so each entry is floored at 1e-2 of the running sum of those terms' magnitudes; dZ0 is
+a signed sum, read as one vector per head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_rnn_layers_amd import binding, inputs
+from tests import pins
+from tests.gpu_util import TOL, dev, dev32, host, rowerr
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = inputs.F32, inputs.BF16
+DM = [(32, 32), (64, 64), (32, 64), (64, 32)]
+CANCEL_FLOOR = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    binding.load()
+    binding.set_segment_chunks(0)
+    yield
+    binding.set_segment_chunks(0)
+
+
+def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
+    q = inputs.gaussian((B, H, N, D), seed, sigma, dtype)
+    k = inputs.gaussian((B, H, N, D), seed + 1, sigma, dtype)
+    v = inputs.gaussian((B, H, N, M), seed + 2, sigma, dtype)
+    return q, k, v
+
+
+def _gates(B, H, N, seed, bias=2.0):
+    """log of 1 / (1 + exp(-x)), x ~ N(bias, 1), float32 (what the library receives)."""
+    x = inputs.gaussian((B, H, N), seed).astype(np.float64) + bias
+    return (-np.log1p(np.exp(-x))).astype(np.float32).astype(np.float64)
+
+
+def _state(B, H, D, M, dtype, seed, sigma=0.1):
+    _, _, s0, z0 = oracle.forward_causal(*_qkv(B, H, 50, D, M, dtype, seed))
+    s0, z0 = (a.astype(np.float32).astype(np.float64) for a in (s0, z0))
+    return s0, z0, inputs.gaussian((B, H, D, M), seed + 10, sigma), inputs.gaussian((B, H, D), seed + 11, sigma)
+
+
+def gpu_forward(q, k, v, la, dtype, s0=None, z0=None):
+    out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
+                                 s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                 return_state=True, checkpoint=True, log_a=dev32(la))
+    torch.cuda.synchronize()
+    return out
+
+
+def check_forward(q, k, v, la, dtype, s0=None, z0=None):
+    out = gpu_forward(q, k, v, la, dtype, s0, z0)
+    o, den, s, z = oracle.forward_decay(q, k, v, la, s0, z0)
+    errs = {"O": rowerr(host(out["o"]), o), "den": rowerr(host(out["den"]), den, False),
+            "S_N": rowerr(host(out["s"]), s), "Z_N": rowerr(host(out["z"]), z, False)}
+    assert max(errs.values()) <= TOL[dtype], errs
+    return out
+
+
+def cancel_scales(q, k, v, la, do, s0, z0, dsn, dzn):
+    """Per-row |S_i g_i * phi'(Q_i)| and |(R_j V_j) * phi'(K_j)| (numerator terms only, g = dO / den) from
+    the plain decayed recurrences, float64."""
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    B, H, N, D = q.shape
+    M = v.shape[-1]
+    pq, pk = pins.phi_lib(q), pins.phi_lib(k)
+    a = np.exp(la)
+    S = np.zeros((B, H, D, M)) if s0 is None else s0.copy()
+    Z = np.zeros((B, H, D)) if z0 is None else z0.copy()
+    g = np.empty((B, H, N, M))
+    sq = np.empty((B, H, N))
+    for t in range(N):
+        S = a[:, :, t, None, None] * S + pk[:, :, t, :, None] * v[:, :, t, None, :]
+        Z = a[:, :, t, None] * Z + pk[:, :, t]
+        den = (pq[:, :, t] * Z).sum(-1)
+        g[:, :, t] = do[:, :, t] / den[..., None]
+        sq[:, :, t] = np.abs(np.einsum("bhdm,bhm->bhd", S, g[:, :, t]) * np.minimum(pq[:, :, t], 1.0)).max(-1)
+    R = np.zeros((B, H, D, M)) if dsn is None else np.asarray(dsn, np.float64).copy()
+    sk = np.empty((B, H, N))
+    for t in range(N - 1, -1, -1):
+        R = R + pq[:, :, t, :, None] * g[:, :, t, None, :]
+        sk[:, :, t] = np.abs(np.einsum("bhdm,bhm->bhd", R, v[:, :, t]) * np.minimum(pk[:, :, t], 1.0)).max(-1)
+        R = a[:, :, t, None, None] * R
+    return sq, sk
+
+
+def dla_floor(k, rk, tail):
+    """Per token: CANCEL_FLOOR x (sum over m >= t of |phi(K_m).dphiK_m| + |tail|) from the oracle's dK."""
+    kd = np.asarray(k, np.float64)
+    x = np.abs((pins.phi_lib(kd) * rk / np.where(kd > 0, 1.0, np.exp(kd))).sum(-1))
+    run = np.flip(np.cumsum(np.flip(x, -1), -1), -1)
+    return CANCEL_FLOOR * (run + np.abs(tail)[..., None])
+
+
+def state_tail(q, k, v, la, s0, z0, dsn, dzn):
+    if dsn is None:
+        return np.zeros(np.asarray(q).shape[:2])
+    _, _, sn, zn = oracle.forward_decay(q, k, v, la, s0, z0)
+    return (dsn * sn).sum((-1, -2)) + (dzn * zn).sum(-1)
+
+
+def check_backward(q, k, v, la, do, dtype, s0=None, z0=None, dsn=None, dzn=None, use_ckpt=True):
+    out = gpu_forward(q, k, v, la, dtype, s0, z0)
+    Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    g = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, dtype),
+                                s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                ckpt=out["ckpt"] if use_ckpt else None,
+                                ds_n=None if dsn is None else dev32(dsn), dz_n=None if dzn is None else dev32(dzn),
+                                state_grad=True, log_a=dev32(la))
+    torch.cuda.synchronize()
+    dq, dk, dv, dla, ds0, dz0 = (host(t) for t in g)
+    rq, rk, rv, rla, rs, rz = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
+    sq, sk = cancel_scales(q, k, v, la, do, s0, z0, dsn, dzn)
+    errs = {"dQ": rowerr(dq, rq, row_floor=CANCEL_FLOOR * sq), "dK": rowerr(dk, rk, row_floor=CANCEL_FLOOR * sk),
+            "dV": rowerr(dv, rv),
+            "dlogA": rowerr(dla, rla, False, row_floor=dla_floor(k, rk, state_tail(q, k, v, la, s0, z0, dsn, dzn))),
+            "dS0": rowerr(ds0, rs), "dZ0": rowerr(dz0[:, :, None, :], rz[:, :, None, :])}
+    assert max(errs.values()) <= TOL[dtype], errs
+    return errs
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 784])
+def test_decay_forward_sweep(N, D, M, dtype):
+    B, H = 2, 3
+    q, k, v = _qkv(B, H, N, D, M, dtype, 12000 + N)
+    la = _gates(B, H, N, 12090)
+    s0, z0, _, _ = _state(B, H, D, M, dtype, 12100)
+    check_forward(q, k, v, la, dtype)
+    check_forward(q, k, v, la, dtype, s0, z0)
+
+
+@pytest.mark.parametrize("D,M", [(32, 32), (64, 64)])
+@pytest.mark.parametrize("chunks", [1, 3])
+def test_decay_forward_segments(D, M, chunks):
+    """Many segments: decayed aggregates and their prefix scan (the checkpoint)."""
+    B, H, N = 1, 2, 784
+    q, k, v = _qkv(B, H, N, D, M, F32, 12200 + chunks)
+    la = _gates(B, H, N, 12290)
+    s0, z0, _, _ = _state(B, H, D, M, F32, 12300)
+    binding.set_segment_chunks(chunks)
+    try:
+        check_forward(q, k, v, la, F32, s0, z0)
+    finally:
+        binding.set_segment_chunks(0)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 200, 784])
+def test_decay_backward_sweep(N, D, M, dtype):
+    B, H = 2, 3
+    q, k, v = _qkv(B, H, N, D, M, dtype, 13000 + N)
+    la = _gates(B, H, N, 13090)
+    do = inputs.gaussian((B, H, N, M), 13095, 1.0, dtype)
+    s0, z0, dsn, dzn = _state(B, H, D, M, dtype, 13100)
+    check_backward(q, k, v, la, do, dtype, s0, z0, dsn, dzn)
+
+
+@pytest.mark.parametrize("D,M", [(32, 32), (64, 64)])
+@pytest.mark.parametrize("chunks", [1, 3])
+@pytest.mark.parametrize("use_ckpt", [True, False])
+def test_decay_backward_segments(D, M, chunks, use_ckpt):
+    B, H, N = 1, 2, 784
+    q, k, v = _qkv(B, H, N, D, M, F32, 13200 + chunks)
+    la = _gates(B, H, N, 13290)
+    do = inputs.gaussian((B, H, N, M), 13295)
+    s0, z0, dsn, dzn = _state(B, H, D, M, F32, 13300)
+    binding.set_segment_chunks(chunks)
+    try:
+        check_backward(q, k, v, la, do, F32, s0, z0, dsn, dzn, use_ckpt)
+    finally:
+        binding.set_segment_chunks(0)
+
+
+def test_decay_without_states():
+    """No initial state and no final-state gradient."""
+    B, H, N, D, M = 2, 2, 300, 64, 32
+    q, k, v = _qkv(B, H, N, D, M, BF16, 13400)
+    la = _gates(B, H, N, 13490)
+    do = inputs.gaussian((B, H, N, M), 13495, 1.0, BF16)
+    check_backward(q, k, v, la, do, BF16)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_decay_limits(dtype):
+    """logA = 0 gives the plain method; logA = -30 leaves only the current token (O_t = V_t)."""
+    B, H, N, D, M = 2, 2, 200, 32, 64
+    q, k, v = _qkv(B, H, N, D, M, dtype, 13500)
+    zero = np.zeros((B, H, N))
+    out = gpu_forward(q, k, v, zero, dtype)
+    o, den, _, _ = oracle.forward_causal(q, k, v)
+    assert rowerr(host(out["o"]), o) <= TOL[dtype]
+    strong = np.full((B, H, N), -30.0)
+    out = gpu_forward(q, k, v, strong, dtype)
+    assert rowerr(host(out["o"]), v) <= TOL[dtype]
+    do = inputs.gaussian((B, H, N, M), 13505, 1.0, dtype)
+    check_backward(q, k, v, zero, do, dtype)
+    # a = exp(-30): O_t = V_t, so dQ, dK and dlogA are exact zeros up to exp(-30), formed as differences of
+    # dot products (dO_t.V_t - O_t.dO_t); each is judged against the dot-product bound sum_m |dO_tm| |V_tm|
+    # (per token, and its running sum for dlogA) with the bar of the plain method's exact-zero first-token
+    # query gradient: kappa = 1e-5 (float32) / 1e-3 (bf16).  dV and the state gradients keep the regular gate.
+    kappa = {F32: 1e-5, BF16: 1e-3}[dtype]
+    out = gpu_forward(q, k, v, strong, dtype)
+    g = binding.backward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype), out["o"], out["den"], dev(do, dtype),
+                                ckpt=out["ckpt"], state_grad=True, log_a=dev32(strong))
+    torch.cuda.synchronize()
+    dq, dk, dv, dla, ds0, dz0 = (host(t) for t in g)
+    rq, rk, rv, rla, rs, rz = oracle.backward_decay(q, k, v, strong, do)
+    pq, pk = pins.phi_lib(q), pins.phi_lib(k)
+    dot = (np.abs(do.astype(np.float64)) * np.abs(v)).sum(-1)  # sum_m |dO_tm| |V_tm|
+    den = (pq * pk).sum(-1)
+    bq = (pk * np.minimum(pq, 1.0)).max(-1) * dot / den
+    bk = (pq * np.minimum(pk, 1.0)).max(-1) * dot / den
+    bla = np.flip(np.cumsum(np.flip(dot, -1), -1), -1)
+    errs = {"dQ": float((np.abs(dq).max(-1) / bq).max()), "dK": float((np.abs(dk).max(-1) / bk).max()),
+            "dlogA": float((np.abs(dla) / bla).max())}
+    assert max(errs.values()) <= kappa, errs
+    assert max(rowerr(dv, rv), rowerr(ds0, rs), rowerr(dz0[:, :, None], rz[:, :, None])) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_decay_decode_steps(dtype):
+    """Decayed decode steps after a decayed prefill follow the decayed forward, step by step."""
+    B, H, N, D, M, pre = 2, 3, 40, 64, 64, 24
+    q, k, v = _qkv(B, H, N, D, M, dtype, 13600)
+    la = _gates(B, H, N, 13690)
+    o, _, s_ref, z_ref = oracle.forward_decay(q, k, v, la)
+    out = gpu_forward(q[:, :, :pre], k[:, :, :pre], v[:, :, :pre], la[:, :, :pre], dtype)
+    s, z = out["s"], out["z"]
+    for t in range(pre, N):
+        y = binding.decode_step(dev(q[:, :, t], dtype), dev(k[:, :, t], dtype), dev(v[:, :, t], dtype), s, z,
+                                log_a=dev32(la[:, :, t]))
+        torch.cuda.synchronize()
+        assert rowerr(host(y)[:, :, None], o[:, :, t:t + 1]) <= TOL[dtype], t
+    assert rowerr(host(s), s_ref) <= TOL[dtype]
+    assert rowerr(host(z), z_ref, False) <= TOL[dtype]
+
+
+def test_decay_autograd_wrapper():
+    """torch.autograd through the library: gradients in q, k, v, the initial state and logA."""
+    B, H, N, D, M = 2, 2, 260, 32, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 13700)
+    la = _gates(B, H, N, 13790)
+    do = inputs.gaussian((B, H, N, M), 13795)
+    s0, z0, dsn, dzn = _state(B, H, D, M, F32, 13800)
+    Q, K, V, S0, Z0, LA = (dev32(a).requires_grad_(True) for a in (q, k, v, s0, z0, la))
+    o, s, z = binding.causal_linear_attention(Q, K, V, S0, Z0, return_state=True, log_a=LA)
+    ((o * dev32(do)).sum() + (s * dev32(dsn)).sum() + (z * dev32(dzn)).sum()).backward()
+    torch.cuda.synchronize()
+    ref = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
+    sq, sk = cancel_scales(q, k, v, la, do, s0, z0, dsn, dzn)
+    got = [host(t.grad) for t in (Q, K, V, LA, S0, Z0)]
+    errs = [rowerr(got[0], ref[0], row_floor=CANCEL_FLOOR * sq), rowerr(got[1], ref[1], row_floor=CANCEL_FLOOR * sk),
+            rowerr(got[2], ref[2]),
+            rowerr(got[3], ref[3], False, row_floor=dla_floor(k, ref[1], state_tail(q, k, v, la, s0, z0, dsn, dzn))),
+            rowerr(got[4], ref[4]), rowerr(got[5][:, :, None], ref[5][:, :, None])]
+    assert max(errs) <= 1e-4, errs
+
+
+def test_decay_long_workload_sampled():
+    """B=1 H=16 N=65536 D=M=64 bf16 with per-token gates: forward and backward on all heads, the oracle on
+    heads 0 and 11 over the whole sequence."""
+    w = inputs.LONG_DECAY
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    la = w.log_a().astype(np.float64)
+    out = gpu_forward(q, k, v, la, BF16)
+    Q, K, V = dev(q, BF16), dev(k, BF16), dev(v, BF16)
+    g = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, BF16), ckpt=out["ckpt"], log_a=dev32(la))
+    torch.cuda.synchronize()
+    hs = [0, 11]
+    sub = lambda a: np.ascontiguousarray(a[:, hs])  # noqa: E731
+    o, _, _, _ = oracle.forward_decay(sub(q), sub(k), sub(v), sub(la))
+    assert rowerr(sub(host(out["o"])), o) <= TOL[BF16]
+    rq, rk, rv, rla, _, _ = oracle.backward_decay(sub(q), sub(k), sub(v), sub(la), sub(do))
+    sq, sk = cancel_scales(sub(q), sub(k), sub(v), sub(la), sub(do), None, None, None, None)
+    dq, dk, dv, dla = (sub(host(t)) for t in g)
+    errs = {"dQ": rowerr(dq, rq, row_floor=CANCEL_FLOOR * sq), "dK": rowerr(dk, rk, row_floor=CANCEL_FLOOR * sk),
+            "dV": rowerr(dv, rv), "dlogA": rowerr(dla, rla, False, row_floor=dla_floor(sub(k), rk, np.zeros((1, 2))))}
+    assert max(errs.values()) <= TOL[BF16], errs

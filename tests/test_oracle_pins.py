@@ -648,3 +648,18 @@ def test_decay_log_gradient_identity():
     tail = (dsn * sn).sum((-1, -2)) + (dzn * zn).sum(-1)
     ref = np.flip(np.cumsum(np.flip(x, -1), -1), -1) + tail[..., None]
     np.testing.assert_allclose(dla, ref, rtol=1e-10, atol=1e-12 * np.max(np.abs(ref)))
+
+
+def test_decay_query_gradient_is_orthogonal_to_phi_q():
+    """O_m is homogeneous of degree 0 in phi(Q_m), so phi(Q_m).dphiQ_m = 0 for the decayed form too (with
+    initial and final states); the dlogA running sum then needs only the key terms."""
+    B, H, N, D, M = 2, 2, 17, 5, 4
+    q, k, v = _qkv((B, H, N, D, M), 381)
+    la = _log_gates((B, H, N), 385)
+    do = inputs.gaussian(v.shape, 386).astype(np.float64)
+    s0, z0, dsn, dzn = _state(B, H, D, M, 387)
+    dq = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)[0]
+    qd = np.asarray(q, np.float64)
+    x = (pins.phi_lib(q) * dq / np.where(qd > 0, 1.0, np.exp(qd))).sum(-1)
+    scale = (np.abs(pins.phi_lib(q)) * np.abs(dq / np.where(qd > 0, 1.0, np.exp(qd)))).sum(-1)
+    assert np.max(np.abs(x) / scale) < 1e-12
