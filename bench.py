@@ -217,7 +217,7 @@ def kernel_bytes(name, w, s):
         "dfwd": (2 * D + 2 * M) * s + 8,         # read Q, K, V, logA; write O, den
         "dbq": (3 * D + 2 * M) * s + 12,         # read Q, K, V, dO, logA; write dQ, (1/den, c)
         "dbkv": (3 * D + 3 * M) * s + 16,        # read Q, K, V, dO, logA, (1/den, c); write dK, dV, dlogA terms
-        "dla_scan": 8,                           # read and write dlogA
+        "dla_fix": 8,                            # read and write dlogA
     }
     if name == "decode":
         return w.B * w.H * (2 * D * M * 4 + 2 * D * 4 + (2 * D + 2 * M) * s)
@@ -263,7 +263,7 @@ KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_se
                ("k_scan_states<", "scan_states"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
                ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"), ("k_dseg_state<", "dseg_state"),
                ("k_dscan_states<", "dscan_states"), ("k_dfwd<", "dfwd"), ("k_dbq<", "dbq"),
-               ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_scan<", "dla_scan"))
+               ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_fix", "dla_fix"))
 
 
 def kernel_tag(full_name):

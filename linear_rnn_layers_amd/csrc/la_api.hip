@@ -117,8 +117,8 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 
 // Workspace regions (bytes) per operation.
 struct WsLayout {
-  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0;
-  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc; }
+  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0, xseg = 0;
+  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg; }
 };
 
 // fwd causal: aggregates and prefix states when there is more than one
@@ -161,12 +161,14 @@ WsLayout ws_layout(int op, const Plan& p) {
         w.dlam = align256((size_t)p.BH * p.nseg * sizeof(float));
       }
       break;
-    case LA_OP_BWD_DECAY:  // checkpoint recomputation, log-decay sums, reverse aggregates, (1/den, c) per token
+    case LA_OP_BWD_DECAY:  // checkpoint recomputation, log-decay sums, reverse aggregates, (1/den, c) per
+                           // token, per-segment totals of the dlogA terms
       w.agg = state_bytes(p, p.nseg);
       w.ckpt = state_bytes(p, p.nseg + 1);
       w.dlam = align256((size_t)p.BH * p.nseg * sizeof(float));
       w.ragg = state_bytes(p, p.nseg);
       w.gc = align256((size_t)p.BH * p.N * 2 * sizeof(float));
+      w.xseg = align256((size_t)p.BH * p.nseg * sizeof(float));
       break;
     default:
       break;
@@ -470,6 +472,7 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
   float* dlam = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
   float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.dlam));
   float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.dlam + wl.ragg));
+  float* xseg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.dlam + wl.ragg + wl.gc));
   const dim3 grid((unsigned)(p.BH * p.nseg));
   int st = LA_OK;
   const float* ck = ckpt;
@@ -489,10 +492,11 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
               dS0, dZ0, p.nseg);
   if (st) return st;
   st = launch("dbkv", la::k_dbkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
-              (const T*)dO, logA, (const float2*)gc, (const float*)ragg, (T*)dK, (T*)dV, dlogA, N, p.L, p.nseg);
+              (const T*)dO, logA, (const float2*)gc, (const float*)ragg, ck, dSN, dZN, (T*)dK, (T*)dV, dlogA, xseg, N,
+              p.L, p.nseg);
   if (st) return st;
-  return launch("dla_scan", la::k_dla_scan<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dlogA, ck, dSN, dZN, N,
-                p.nseg);
+  if (p.nseg == 1) return LA_OK;
+  return launch("dla_fix", la::k_dla_fix, grid, dim3(la::NT), s, dlogA, (const float*)xseg, N, p.L, p.nseg);
 }
 
 template <typename T, int D, int M>
@@ -531,7 +535,7 @@ const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
-         "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_scan";
+         "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {

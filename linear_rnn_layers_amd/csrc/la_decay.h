@@ -26,7 +26,7 @@
 // (logA_l enters every weight exp(L_i - L_j) with j < l <= i and the final
 // state).  O_m is a ratio of two linear functions of phi(Q_m), homogeneous
 // of degree 0, so phi(Q_m).dphiQ_m = 0 exactly and only the key terms are
-// summed (k_dbkv writes them, k_dla_scan forms the running sum).  The query side needs S_i, which
+// summed (k_dbkv within each segment, k_dla_fix across segments).  The query side needs S_i, which
 // only the forward order reaches stably (subtracting later tokens from the
 // state after a chunk would multiply by exp(+lam)); the key side runs in
 // reverse, where the carried R only decays.
@@ -673,13 +673,18 @@ __global__ __launch_bounds__(NT) void k_dscan_rev(float* __restrict__ ragg, cons
 //   dphiK_j = sum_{i>=j} exp(lam_i - lam_j) (g_i.V_j + c_i) phi(Q_i) + f_j (R+ V_j + r+),
 // with g_i = dO_i / den_i and (1/den_i, c_i) from the query pass; then
 // R+ <- exp(lam_last) R+ + sum_i exp(lam_i) phi(Q_i) [g_i | c_i]^T for the
-// chunk before.  dla[j] = -phi(K_j).dphiK_j.
+// chunk before.  With x_j = -phi(K_j).dphiK_j, dla[j] gets the running sum
+// of x over the segment's tokens from j on (plus, in the last segment, the
+// final-state term <[dS_N|dZ_N], [S_N|Z_N]> with S_N checkpoint entry nseg),
+// and xseg[bh][seg] the segment's total; k_dla_fix adds the later segments'.
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* __restrict__ K,
                                               const T* __restrict__ V, const T* __restrict__ dO,
                                               const float* __restrict__ logA, const float2* __restrict__ gc,
-                                              const float* __restrict__ rin, T* __restrict__ dK,
-                                              T* __restrict__ dV, float* __restrict__ dla, int N, int L, int nseg) {
+                                              const float* __restrict__ rin, const float* __restrict__ ckpt,
+                                              const float* __restrict__ dSN, const float* __restrict__ dZN,
+                                              T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dla,
+                                              float* __restrict__ xseg, int N, int L, int nseg) {
   using P = DPrec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   __shared__ Planes<P::Q, CH, D> qt;
@@ -692,6 +697,7 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
   __shared__ alignas(16) float slam[CH];
   __shared__ alignas(16) float sInv[CH];
   __shared__ alignas(16) float sC[CH];
+  __shared__ alignas(16) float sX[CH];  // x_j of the chunk just processed
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
@@ -702,6 +708,29 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
   const float* la = logA + (size_t)bh * N;
   const float2* gch = gc + (size_t)bh * N;
   gt.zero_cols(M + 1, M + 16);
+
+  // running sum of x from the segment's end (wave 0); the last segment starts it at the final-state term
+  float carry = 0.f;
+  if (seg == nseg - 1 && dSN) {
+    const float* sn = ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV;
+    float acc = 0.f;
+    for (int e = tid; e < SV; e += NT)
+      acc += (e < D * M ? dSN[(size_t)bh * D * M + e] : dZN[(size_t)bh * D + e - D * M]) * sn[e];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (l == 0) sX[w] = acc;
+    __syncthreads();
+    carry = sX[0] + sX[1] + sX[2] + sX[3];
+    __syncthreads();
+  }
+  int pend_c0 = -1, pend_nv = 0;  // chunk whose x values wait in sX
+  auto flush_x = [&]() {          // wave 0: dla of the pending chunk = suffix sums of x + carry
+    if (w != 0 || pend_c0 < 0) return;
+    const float x = sX[l];
+    const float sfx = __shfl(wave_incl_sum(__shfl(x, 63 - l, 64)), 63 - l, 64);  // sum over lanes >= l
+    if (l < pend_nv) dla[(size_t)bh * N + pend_c0 + l] = sfx + carry;
+    carry += __shfl(sfx, 0, 64);
+  };
 
   const int nchunk = (t1 - t0 + CH - 1) / CH;
   RowBuf<T, CH, D> bq[2], bk[2];
@@ -745,6 +774,7 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
     const float last = __shfl(lam, 63, 64);
     const float2 gcv = gcl[b];
     __syncthreads();
+    flush_x();
     stage_R();
     bq[b].stage_phi(qt, nv);
     bk[b].stage_phi(kt, nv);
@@ -858,7 +888,9 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
       if (row_ok) IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
     }
     xk = sum_over_g(xk);
-    if (g == 0 && row_ok) dla[(size_t)bh * N + c0 + jl] = -xk;
+    if (g == 0) sX[jl] = row_ok ? -xk : 0.f;
+    pend_c0 = c0;
+    pend_nv = nv;
 
     // R+ for the chunk before
     const float dec = exp_nat(last);
@@ -880,58 +912,22 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
     chunk(0, ci);
     if (ci - 1 >= 0) chunk(1, ci - 1);
   }
+  __syncthreads();
+  flush_x();
+  if (tid == 0) xseg[(size_t)bh * nseg + seg] = carry;
 }
 
-// dlogA_t = sum_{m >= t} x_m + <[dS_N | dZ_N], [S_N | Z_N]>, in place over
-// x = dla; one workgroup per head, tiles of 4 NT tokens from the end.
-template <int D, int M>
-__global__ __launch_bounds__(NT) void k_dla_scan(float* __restrict__ dla, const float* __restrict__ ckpt,
-                                                  const float* __restrict__ dSN, const float* __restrict__ dZN, int N,
-                                                  int nseg) {
-  constexpr int SV = D * M + D, TILE = 4 * NT;
-  __shared__ float part[NT];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  float tail = 0.f;
-  if (dSN) {  // <dS_N, S_N> + <dZ_N, Z_N>, S_N = checkpoint entry nseg
-    const float* sn = ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV;
-    float acc = 0.f;
-    for (int e = tid; e < SV; e += NT)
-      acc += (e < D * M ? dSN[(size_t)bh * D * M + e] : dZN[(size_t)bh * D + e - D * M]) * sn[e];
-    part[tid] = acc;
-    __syncthreads();
-    for (int o = NT / 2; o > 0; o >>= 1) {
-      if (tid < o) part[tid] += part[tid + o];
-      __syncthreads();
-    }
-    tail = part[0];
-    __syncthreads();
-  }
+// dla over segment seg += the totals xseg of the later segments (summed in
+// segment order).
+__global__ __launch_bounds__(NT) void k_dla_fix(float* __restrict__ dla, const float* __restrict__ xseg, int N,
+                                                 int L, int nseg) {
+  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  if (seg == nseg - 1) return;
+  float off = 0.f;
+  for (int s = seg + 1; s < nseg; ++s) off += xseg[(size_t)bh * nseg + s];
+  const int t0 = seg * L, t1 = min(N, t0 + L);
   float* x = dla + (size_t)bh * N;
-  float carry = tail;  // sum of everything after the current tile
-  for (int base = ((N - 1) / TILE) * TILE; base >= 0; base -= TILE) {
-    float v[4];
-    const int i0 = base + 4 * tid;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = i0 + q < N ? x[i0 + q] : 0.f;
-    // suffix within the thread's four
-    v[2] += v[3];
-    v[1] += v[2];
-    v[0] += v[1];
-    part[tid] = v[0];
-    __syncthreads();
-    // suffix over threads (Hillis-Steele on the thread totals)
-    for (int o = 1; o < NT; o <<= 1) {
-      const float add = tid + o < NT ? part[tid + o] : 0.f;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
-    }
-    const float after = (tid + 1 < NT ? part[tid + 1] : 0.f) + carry;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (i0 + q < N) x[i0 + q] = v[q] + after;
-    carry += part[0];
-    __syncthreads();
-  }
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += NT) x[t] += off;
 }
+
 }  // namespace la

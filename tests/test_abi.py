@@ -196,7 +196,7 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     # decayed backward: those, reverse aggregates and (1/den, c) per token
     dl = _al(B * H * nseg * 4)
     assert lib.la_workspace_size(5, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref + dl)
-    assert lib.la_workspace_size(6, B, H, N, D, M, 1) == agg + pref + dl + agg + _al(B * H * N * 8)
+    assert lib.la_workspace_size(6, B, H, N, D, M, 1) == agg + pref + dl + agg + _al(B * H * N * 8) + dl
     assert lib.la_workspace_size(9, B, H, N, D, M, 0) == 0
 
 
