@@ -297,8 +297,10 @@ int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int 
 }
 
 template <int D, int M>
-int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z0, float* pref, hipStream_t s) {
-  return launch("scan_states", la::k_scan_states<D, M>, scan_grid(p), dim3(la::NT), s, agg, S0, Z0, pref, p.nseg);
+int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z0, float* pref, hipStream_t s,
+                int last_only = 0) {
+  return launch("scan_states", la::k_scan_states<D, M>, scan_grid(p), dim3(la::NT), s, agg, S0, Z0, pref, p.nseg,
+                last_only);
 }
 
 template <typename T, int D, int M>
@@ -337,9 +339,9 @@ int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
   if (st) return st;
   const float* pref = nullptr;
-  if (use_scan(p)) {
+  if (use_scan(p)) {  // the total once per head (else every workgroup sums the aggregates)
     float* pr = reinterpret_cast<float*>(region(ws, wl.agg));
-    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pr, s);
+    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pr, s, 1);
     if (st) return st;
     pref = pr;
   }
@@ -412,11 +414,11 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   float* pref = reinterpret_cast<float*>(region(ws, wl.agg));
   float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
   float* rpref = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
-  const bool scan = use_scan(p);
+  const bool scan = use_scan(p);  // the totals once per head (else every workgroup sums the aggregates)
   int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
   if (st) return st;
   if (scan) {
-    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s);
+    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s, 1);
     if (st) return st;
   }
   const dim3 grid((unsigned)(p.BH * p.nseg));
@@ -424,7 +426,7 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
               (const float*)(scan ? pref : nullptr), (T*)dQ, ragg, N, p.L, p.nseg);
   if (st) return st;
   if (scan) {
-    st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s);
+    st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s, 1);
     if (st) return st;
   }
   return launch("nc_kv", la::k_nc_kv<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, (const float*)ragg,

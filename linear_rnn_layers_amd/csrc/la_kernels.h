@@ -432,12 +432,13 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
 
 // Prefix states from segment aggregates: pref[bh][s] = init + sum_{t<s}
 // agg[bh][t], s = 0..nseg (init = (S0, Z0) or zero), summed in segment
-// order.  One thread per state element; the aggregates are read in batches
-// so that many loads are in flight.
+// order; with last_only, only the total (entry nseg) is written.  One thread
+// per state element; the aggregates are read in batches so that many loads
+// are in flight.
 template <int D, int M>
 __global__ __launch_bounds__(NT) void k_scan_states(const float* __restrict__ agg, const float* __restrict__ S0,
                                                      const float* __restrict__ Z0, float* __restrict__ pref,
-                                                     int nseg) {
+                                                     int nseg, int last_only) {
   constexpr int SV = D * M + D, BT = 16;
   const int bh = blockIdx.x;
   const int e = blockIdx.y * NT + threadIdx.x;
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(NT) void k_scan_states(const float* __restrict__ ag
 #pragma unroll
     for (int j = 0; j < BT; ++j) {
       if (s0 + j < nseg) {
-        o[(size_t)(s0 + j) * SV] = run;
+        if (!last_only) o[(size_t)(s0 + j) * SV] = run;
         run += v[j];
       }
     }
