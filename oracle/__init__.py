@@ -46,15 +46,19 @@ def _configure(lib):
     lib.orc_phi.argtypes = [ctypes.c_double]
     lib.orc_dphi.restype = ctypes.c_double
     lib.orc_dphi.argtypes = [ctypes.c_double]
-    lib.orc_forward_causal.argtypes = [dp] * 9 + [L] * 5
+    lib.orc_forward_causal.argtypes = [dp] * 9 + [L] * 6
     lib.orc_forward_causal_parallel.argtypes = [dp] * 5 + [L] * 5
-    lib.orc_forward_noncausal.argtypes = [dp] * 4 + [L] * 5
+    lib.orc_forward_noncausal.argtypes = [dp] * 4 + [L] * 6
     lib.orc_numerator_backward.argtypes = [dp] * 9 + [L] * 3
-    lib.orc_backward_causal.argtypes = [dp] * 13 + [L] * 5
-    lib.orc_backward_noncausal.argtypes = [dp] * 7 + [L] * 5
-    lib.orc_decode_step.argtypes = [dp] * 7 + [L] * 4
-    lib.orc_forward_decay.argtypes = [dp] * 10 + [L] * 5
-    lib.orc_backward_decay.argtypes = [dp] * 15 + [L] * 5
+    lib.orc_backward_causal.argtypes = [dp] * 13 + [L] * 6
+    lib.orc_backward_noncausal.argtypes = [dp] * 7 + [L] * 6
+    lib.orc_decode_step.argtypes = [dp] * 7 + [L] * 5
+    lib.orc_forward_decay.argtypes = [dp] * 10 + [L] * 6
+    lib.orc_backward_decay.argtypes = [dp] * 15 + [L] * 6
+    lib.orc_feature_performer.argtypes = [dp] * 3 + [L] * 5
+    lib.orc_feature_performer_vjp.argtypes = [dp] * 4 + [L] * 5
+    lib.orc_feature_poly2.argtypes = [dp] * 2 + [L] * 3
+    lib.orc_feature_poly2_vjp.argtypes = [dp] * 3 + [L] * 3
     lib.orc_num_threads.restype = ctypes.c_int
     return lib
 
@@ -90,7 +94,7 @@ def dphi(x: float) -> float:
     return float(_load().orc_dphi(float(x)))
 
 
-def forward_causal(q, k, v, s0=None, z0=None):
+def forward_causal(q, k, v, s0=None, z0=None, feature=0):
     """Recurrent form, eq. 10-12.  Returns (O, den, S_N, Z_N) in float64."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, D = q.shape
@@ -104,7 +108,7 @@ def forward_causal(q, k, v, s0=None, z0=None):
     s = np.empty((B, H, D, M))
     z = np.empty((B, H, D))
     _load().orc_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(s0), _ptr(z0), _ptr(o), _ptr(den),
-                               _ptr(s), _ptr(z), B, H, N, D, M)
+                               _ptr(s), _ptr(z), B, H, N, D, M, int(feature))
     return o, den, s, z
 
 
@@ -119,13 +123,13 @@ def forward_causal_parallel(q, k, v):
     return o, den
 
 
-def forward_noncausal(q, k, v):
+def forward_noncausal(q, k, v, feature=0):
     """eq. 5-6: S and Z summed over the whole sequence, reused by every query."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, D = q.shape
     M = v.shape[-1]
     o = np.empty((B, H, N, M))
-    _load().orc_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M)
+    _load().orc_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, D, M, int(feature))
     return o
 
 
@@ -145,7 +149,7 @@ def numerator_backward(p, kf, vb, g, rn=None, return_r0=False):
     return (dp_, dk, dv, r0) if return_r0 else (dp_, dk, dv)
 
 
-def backward_causal(q, k, v, do, s0=None, z0=None, dsn=None, dzn=None, state_grad=False):
+def backward_causal(q, k, v, do, s0=None, z0=None, dsn=None, dzn=None, state_grad=False, feature=0):
     """Gradients of sum(dO * O) + sum(dSN * S_N) + sum(dZN * Z_N) w.r.t. raw Q, K, V (and, with state_grad,
     the initial state).  Returns (dQ, dK, dV) or (dQ, dK, dV, dS0, dZ0)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -163,11 +167,11 @@ def backward_causal(q, k, v, do, s0=None, z0=None, dsn=None, dzn=None, state_gra
     ds0 = np.empty((B, H, D, M)) if state_grad else None
     dz0 = np.empty((B, H, D)) if state_grad else None
     _load().orc_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dsn), _ptr(dzn),
-                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds0), _ptr(dz0), B, H, N, D, M)
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds0), _ptr(dz0), B, H, N, D, M, int(feature))
     return (dq, dk, dv, ds0, dz0) if state_grad else (dq, dk, dv)
 
 
-def backward_noncausal(q, k, v, do):
+def backward_noncausal(q, k, v, do, feature=0):
     """Gradients of sum(dO * O) for the non-causal forward w.r.t. raw Q, K, V.  Returns (dQ, dK, dV)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, D = q.shape
@@ -176,11 +180,11 @@ def backward_noncausal(q, k, v, do):
     dk = np.empty((B, H, N, D))
     dv = np.empty((B, H, N, M))
     _load().orc_backward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                                   B, H, N, D, M)
+                                   B, H, N, D, M, int(feature))
     return dq, dk, dv
 
 
-def decode_step(q, k, v, s, z, log_a=None):
+def decode_step(q, k, v, s, z, log_a=None, feature=0):
     """eq. 18-20 (attention part), decayed by exp(log_a) [B,H] when given.  Returns (y, S_new, Z_new); inputs
     untouched."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -190,11 +194,11 @@ def decode_step(q, k, v, s, z, log_a=None):
     B, H, D = q.shape
     M = v.shape[-1]
     y = np.empty((B, H, M))
-    _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(s), _ptr(z), _ptr(y), B, H, D, M)
+    _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(s), _ptr(z), _ptr(y), B, H, D, M, int(feature))
     return y, s, z
 
 
-def forward_decay(q, k, v, log_a, s0=None, z0=None):
+def forward_decay(q, k, v, log_a, s0=None, z0=None, feature=0):
     """Decayed causal forward (per-token, per-head log-decay log_a [B,H,N]).  Returns (O, den, S_N, Z_N)."""
     q, k, v, log_a = _f64(q), _f64(k), _f64(v), _f64(log_a)
     B, H, N, D = q.shape
@@ -206,11 +210,11 @@ def forward_decay(q, k, v, log_a, s0=None, z0=None):
     s = np.empty((B, H, D, M))
     z = np.empty((B, H, D))
     _load().orc_forward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(s0), _ptr(z0), _ptr(o), _ptr(den),
-                              _ptr(s), _ptr(z), B, H, N, D, M)
+                              _ptr(s), _ptr(z), B, H, N, D, M, int(feature))
     return o, den, s, z
 
 
-def backward_decay(q, k, v, log_a, do, s0=None, z0=None, dsn=None, dzn=None):
+def backward_decay(q, k, v, log_a, do, s0=None, z0=None, dsn=None, dzn=None, feature=0):
     """Gradients of sum(dO*O) + sum(dSN*S_N) + sum(dZN*Z_N) for the decayed forward.  Returns
     (dQ, dK, dV, dlogA, dS0, dZ0)."""
     q, k, v, log_a, do = _f64(q), _f64(k), _f64(v), _f64(log_a), _f64(do)
@@ -230,5 +234,43 @@ def backward_decay(q, k, v, log_a, do, s0=None, z0=None, dsn=None, dzn=None):
     dz0 = np.empty((B, H, D))
     _load().orc_backward_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(do), _ptr(s0), _ptr(z0), _ptr(dsn),
                                _ptr(dzn), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dla), _ptr(ds0), _ptr(dz0),
-                               B, H, N, D, M)
+                               B, H, N, D, M, int(feature))
     return dq, dk, dv, dla, ds0, dz0
+
+
+def feature_performer(x, w):
+    """Positive random features phi(x)_c = exp(w_c . x - |x|^2 / 2) / sqrt(C); x [B,H,N,Din], w [H,C,Din]."""
+    x, w = _f64(x), _f64(w)
+    B, H, N, Din = x.shape
+    C = w.shape[1]
+    phi_ = np.empty((B, H, N, C))
+    _load().orc_feature_performer(_ptr(x), _ptr(w), _ptr(phi_), B, H, N, Din, C)
+    return phi_
+
+
+def feature_performer_vjp(x, w, dphi_):
+    x, w, dphi_ = _f64(x), _f64(w), _f64(dphi_)
+    B, H, N, Din = x.shape
+    C = w.shape[1]
+    dx = np.empty((B, H, N, Din))
+    _load().orc_feature_performer_vjp(_ptr(x), _ptr(w), _ptr(dphi_), _ptr(dx), B, H, N, Din, C)
+    return dx
+
+
+def feature_poly2(x, C):
+    """Degree-2 polynomial features (1, x, x_a x_b) zero-padded to C; x [..., Din]."""
+    x = _f64(x)
+    Din = x.shape[-1]
+    rows = x.size // Din
+    phi_ = np.empty(x.shape[:-1] + (C,))
+    _load().orc_feature_poly2(_ptr(x), _ptr(phi_), rows, Din, C)
+    return phi_
+
+
+def feature_poly2_vjp(x, dphi_):
+    x, dphi_ = _f64(x), _f64(dphi_)
+    Din = x.shape[-1]
+    rows = x.size // Din
+    dx = np.empty(x.shape)
+    _load().orc_feature_poly2_vjp(_ptr(x), _ptr(dphi_), _ptr(dx), rows, Din, dphi_.shape[-1])
+    return dx

@@ -8,7 +8,9 @@
  * library.
  *
  * Every routine is the plain definition written out, in float64, one token
- * at a time; there is no chunking, blocking or fusion.  Parallelism is only
+ * at a time; there is no chunking, blocking or fusion.  The attention
+ * routines take a last argument fm: 0 applies eq. 7 to Q and K, 1 takes them
+ * as feature vectors already (the feature maps at the end of this file).  Parallelism is only
  * across independent (batch, head) pairs (heads never interact: Transformer
  * Family v2, multi-head attention section).
  *
@@ -55,6 +57,13 @@ double orc_phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
 /* Derivative of eq. 7: 1 for x > 0, exp(x) otherwise (both sides give 1 at 0). */
 double orc_dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
 
+/* Feature-map selection of every attention routine: fm = 0 applies eq. 7 to
+ * Q and K; fm = 1 takes them as feature vectors already (another feature map
+ * applied beforehand, "Linear Attention/zh", feature maps), i.e. the identity
+ * with derivative 1, and the gradients are with respect to those features. */
+static double feat(double x, long fm) { return fm ? x : orc_phi(x); }
+static double dfeat(double x, long fm) { return fm ? 1.0 : orc_dphi(x); }
+
 /*
  * Causal forward, recurrent form ([TaR] eq. 10-12, eq. 16-19 without the
  * projections):  S_i = S_{i-1} + phi(K_i) V_i^T,  Z_i = Z_{i-1} + phi(K_i),
@@ -65,7 +74,7 @@ double orc_dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
 void orc_forward_causal(const double *Q, const double *K, const double *V,
                         const double *S0, const double *Z0, double *O,
                         double *den, double *S_out, double *Z_out, long B,
-                        long H, long N, long D, long M) {
+                        long H, long N, long D, long M, long fm) {
   long BH = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
@@ -80,8 +89,8 @@ void orc_forward_causal(const double *Q, const double *K, const double *V,
       const double *k = K + (bh * N + i) * D;
       const double *v = V + (bh * N + i) * M;
       for (long d = 0; d < D; ++d) {
-        pq[d] = orc_phi(q[d]);
-        pk[d] = orc_phi(k[d]);
+        pq[d] = feat(q[d], fm);
+        pk[d] = feat(k[d], fm);
       }
       /* state update first: the mask is inclusive (eq. 8, j <= i) */
       for (long d = 0; d < D; ++d) {
@@ -153,7 +162,7 @@ void orc_forward_causal_parallel(const double *Q, const double *K,
  * once per head and reused for every query: O_i = phi(Q_i)^T S / phi(Q_i).Z.
  */
 void orc_forward_noncausal(const double *Q, const double *K, const double *V,
-                           double *O, long B, long H, long N, long D, long M) {
+                           double *O, long B, long H, long N, long D, long M, long fm) {
   long BH = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
@@ -164,14 +173,14 @@ void orc_forward_noncausal(const double *Q, const double *K, const double *V,
       const double *k = K + (bh * N + j) * D;
       const double *v = V + (bh * N + j) * M;
       for (long d = 0; d < D; ++d) {
-        double pk = orc_phi(k[d]);
+        double pk = feat(k[d], fm);
         for (long m = 0; m < M; ++m) S[d * M + m] += pk * v[m];
         Z[d] += pk;
       }
     }
     for (long i = 0; i < N; ++i) {
       const double *q = Q + (bh * N + i) * D;
-      for (long d = 0; d < D; ++d) pq[d] = orc_phi(q[d]);
+      for (long d = 0; d < D; ++d) pq[d] = feat(q[d], fm);
       double dn = 0.0;
       for (long d = 0; d < D; ++d) dn += pq[d] * Z[d];
       double *o = O + (bh * N + i) * M;
@@ -263,7 +272,7 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
                          const double *dO, const double *S0, const double *Z0,
                          const double *dSN, const double *dZN, double *dQ,
                          double *dK, double *dV, double *dS0, double *dZ0,
-                         long B, long H, long N, long D, long M) {
+                         long B, long H, long N, long D, long M, long fm) {
   long BH = B * H;
   long Mb = M + 1;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -288,12 +297,12 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
       }
     /* 1. forward pass of this head */
     orc_forward_causal(q, k, v, S0 ? S0 + bh * D * M : NULL,
-                       Z0 ? Z0 + bh * D : NULL, O, den, NULL, NULL, 1, 1, N, D, M);
+                       Z0 ? Z0 + bh * D : NULL, O, den, NULL, NULL, 1, 1, N, D, M, fm);
     /* 2. quotient rule, 3. augmented numerator */
     for (long i = 0; i < N; ++i) {
       for (long d = 0; d < D; ++d) {
-        P[i * D + d] = orc_phi(q[i * D + d]);
-        Kf[i * D + d] = orc_phi(k[i * D + d]);
+        P[i * D + d] = feat(q[i * D + d], fm);
+        Kf[i * D + d] = feat(k[i * D + d], fm);
       }
       double dot = 0.0;
       for (long m = 0; m < M; ++m) {
@@ -323,8 +332,8 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
     /* 4. chain rule through phi */
     for (long i = 0; i < N; ++i) {
       for (long d = 0; d < D; ++d) {
-        dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_dphi(q[i * D + d]);
-        dK[(bh * N + i) * D + d] = dKf[i * D + d] * orc_dphi(k[i * D + d]);
+        dQ[(bh * N + i) * D + d] = dP[i * D + d] * dfeat(q[i * D + d], fm);
+        dK[(bh * N + i) * D + d] = dKf[i * D + d] * dfeat(k[i * D + d], fm);
       }
       for (long m = 0; m < M; ++m) dV[(bh * N + i) * M + m] = dVb[i * Mb + m];
     }
@@ -359,7 +368,7 @@ void orc_backward_causal(const double *Q, const double *K, const double *V,
 void orc_backward_noncausal(const double *Q, const double *K, const double *V,
                             const double *dO, double *dQ, double *dK,
                             double *dV, long B, long H, long N, long D,
-                            long M) {
+                            long M, long fm) {
   long BH = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
@@ -374,13 +383,13 @@ void orc_backward_noncausal(const double *Q, const double *K, const double *V,
     /* 1. totals of the keys */
     for (long j = 0; j < N; ++j)
       for (long d = 0; d < D; ++d) {
-        double pk = orc_phi(k[j * D + d]);
+        double pk = feat(k[j * D + d], fm);
         for (long m = 0; m < M; ++m) S[d * M + m] += pk * v[j * M + m];
         Z[d] += pk;
       }
     /* 2-3. per query: den, O, g, c; dphiQ; accumulate R, r */
     for (long i = 0; i < N; ++i) {
-      for (long d = 0; d < D; ++d) pq[d] = orc_phi(q[i * D + d]);
+      for (long d = 0; d < D; ++d) pq[d] = feat(q[i * D + d], fm);
       double den = 0.0;
       for (long d = 0; d < D; ++d) den += pq[d] * Z[d];
       double dot = 0.0;
@@ -394,7 +403,7 @@ void orc_backward_noncausal(const double *Q, const double *K, const double *V,
       for (long d = 0; d < D; ++d) {
         double acc = c * Z[d];
         for (long m = 0; m < M; ++m) acc += S[d * M + m] * g[m];
-        dQ[(bh * N + i) * D + d] = acc * orc_dphi(q[i * D + d]);
+        dQ[(bh * N + i) * D + d] = acc * dfeat(q[i * D + d], fm);
         for (long m = 0; m < M; ++m) R[d * M + m] += pq[d] * g[m];
         r[d] += c * pq[d];
       }
@@ -404,11 +413,11 @@ void orc_backward_noncausal(const double *Q, const double *K, const double *V,
       for (long d = 0; d < D; ++d) {
         double acc = r[d];
         for (long m = 0; m < M; ++m) acc += R[d * M + m] * v[j * M + m];
-        dK[(bh * N + j) * D + d] = acc * orc_dphi(k[j * D + d]);
+        dK[(bh * N + j) * D + d] = acc * dfeat(k[j * D + d], fm);
       }
       for (long m = 0; m < M; ++m) {
         double acc = 0.0;
-        for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(k[j * D + d]);
+        for (long d = 0; d < D; ++d) acc += R[d * M + m] * feat(k[j * D + d], fm);
         dV[(bh * N + j) * M + m] = acc;
       }
     }
@@ -438,7 +447,7 @@ void orc_backward_noncausal(const double *Q, const double *K, const double *V,
 void orc_forward_decay(const double *Q, const double *K, const double *V,
                        const double *logA, const double *S0, const double *Z0,
                        double *O, double *den, double *S_out, double *Z_out,
-                       long B, long H, long N, long D, long M) {
+                       long B, long H, long N, long D, long M, long fm) {
   long BH = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (long bh = 0; bh < BH; ++bh) {
@@ -454,8 +463,8 @@ void orc_forward_decay(const double *Q, const double *K, const double *V,
       const double *v = V + (bh * N + i) * M;
       const double a = exp(logA[bh * N + i]);
       for (long d = 0; d < D; ++d) {
-        pq[d] = orc_phi(q[d]);
-        pk[d] = orc_phi(k[d]);
+        pq[d] = feat(q[d], fm);
+        pk[d] = feat(k[d], fm);
       }
       for (long d = 0; d < D; ++d) {
         for (long m = 0; m < M; ++m) S[d * M + m] = a * S[d * M + m] + pk[d] * v[m];
@@ -501,7 +510,7 @@ void orc_backward_decay(const double *Q, const double *K, const double *V,
                         const double *S0, const double *Z0, const double *dSN,
                         const double *dZN, double *dQ, double *dK, double *dV,
                         double *dlogA, double *dS0, double *dZ0, long B, long H,
-                        long N, long D, long M) {
+                        long N, long D, long M, long fm) {
   long BH = B * H;
   long Mb = M + 1, SB = D * (M + 1);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -523,7 +532,7 @@ void orc_backward_decay(const double *Q, const double *K, const double *V,
       const double *prev = Sb + (t - 1) * SB;
       double *cur = Sb + t * SB;
       for (long d = 0; d < D; ++d) {
-        const double p = orc_phi(k[(t - 1) * D + d]);
+        const double p = feat(k[(t - 1) * D + d], fm);
         for (long m = 0; m < M; ++m) cur[d * Mb + m] = a * prev[d * Mb + m] + p * v[(t - 1) * M + m];
         cur[d * Mb + M] = a * prev[d * Mb + M] + p;
       }
@@ -538,8 +547,8 @@ void orc_backward_decay(const double *Q, const double *K, const double *V,
       const double a = exp(la[i]);
       const double *cur = Sb + t * SB, *prev = Sb + (t - 1) * SB;
       for (long d = 0; d < D; ++d) {
-        pq[d] = orc_phi(q[i * D + d]);
-        pk[d] = orc_phi(k[i * D + d]);
+        pq[d] = feat(q[i * D + d], fm);
+        pk[d] = feat(k[i * D + d], fm);
       }
       /* output of token t and the quotient rule */
       double dn = 0.0;
@@ -558,8 +567,8 @@ void orc_backward_decay(const double *Q, const double *K, const double *V,
         double aq = 0.0, ak = R[d * Mb + M];
         for (long m = 0; m < Mb; ++m) aq += cur[d * Mb + m] * G[m];
         for (long m = 0; m < M; ++m) ak += R[d * Mb + m] * v[i * M + m];
-        dQ[(bh * N + i) * D + d] = aq * orc_dphi(q[i * D + d]);
-        dK[(bh * N + i) * D + d] = ak * orc_dphi(k[i * D + d]);
+        dQ[(bh * N + i) * D + d] = aq * dfeat(q[i * D + d], fm);
+        dK[(bh * N + i) * D + d] = ak * dfeat(k[i * D + d], fm);
       }
       for (long m = 0; m < M; ++m) {
         double acc = 0.0;
@@ -593,23 +602,109 @@ void orc_backward_decay(const double *Q, const double *K, const double *V,
  */
 void orc_decode_step(const double *q, const double *k, const double *v,
                      const double *logA, double *S, double *Z, double *y,
-                     long B, long H, long D, long M) {
+                     long B, long H, long D, long M, long fm) {
   long BH = B * H;
 #pragma omp parallel for schedule(static)
   for (long bh = 0; bh < BH; ++bh) {
     double *s = S + bh * D * M, *z = Z + bh * D;
     const double a = logA ? exp(logA[bh]) : 1.0;
     for (long d = 0; d < D; ++d) {
-      double pk = orc_phi(k[bh * D + d]);
+      double pk = feat(k[bh * D + d], fm);
       for (long m = 0; m < M; ++m) s[d * M + m] = a * s[d * M + m] + pk * v[bh * M + m];
       z[d] = a * z[d] + pk;
     }
     double dn = 0.0;
-    for (long d = 0; d < D; ++d) dn += orc_phi(q[bh * D + d]) * z[d];
+    for (long d = 0; d < D; ++d) dn += feat(q[bh * D + d], fm) * z[d];
     for (long m = 0; m < M; ++m) {
       double num = 0.0;
-      for (long d = 0; d < D; ++d) num += orc_phi(q[bh * D + d]) * s[d * M + m];
+      for (long d = 0; d < D; ++d) num += feat(q[bh * D + d], fm) * s[d * M + m];
       y[bh * M + m] = num / dn;
+    }
+  }
+}
+
+/*
+ * Positive random features ("Linear Attention/zh", feature maps: Performer
+ * approximates the softmax kernel with phi(x) proportional to
+ * exp(W x - |x|^2 / 2); "The Transformer Family v2", random feature
+ * attention).  With a projection W [C, Din] per head (random, passed in):
+ *   phi(x)_c = exp(w_c . x - |x|^2 / 2) / sqrt(C),
+ * so phi(x) . phi(y) = mean_c exp(w_c . (x + y) - (|x|^2 + |y|^2) / 2),
+ * whose expectation over standard normal w_c is exp(x . y).
+ * X [B,H,N,Din], W [H,C,Din], Phi [B,H,N,C].
+ */
+void orc_feature_performer(const double *X, const double *W, double *Phi,
+                           long B, long H, long N, long Din, long C) {
+  const double sc = 1.0 / sqrt((double)C);
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < B * H * N; ++r) {
+    const double *x = X + r * Din, *w = W + ((r / N) % H) * C * Din;
+    double nx = 0.0;
+    for (long d = 0; d < Din; ++d) nx += x[d] * x[d];
+    for (long c = 0; c < C; ++c) {
+      double t = 0.0;
+      for (long d = 0; d < Din; ++d) t += w[c * Din + d] * x[d];
+      Phi[r * C + c] = exp(t - 0.5 * nx) * sc;
+    }
+  }
+}
+
+/* Vector-Jacobian product of orc_feature_performer: d phi_c / d x =
+ * phi_c (w_c - x), so dX = sum_c dPhi_c phi_c (w_c - x). */
+void orc_feature_performer_vjp(const double *X, const double *W,
+                               const double *dPhi, double *dX, long B, long H,
+                               long N, long Din, long C) {
+  const double sc = 1.0 / sqrt((double)C);
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < B * H * N; ++r) {
+    const double *x = X + r * Din, *w = W + ((r / N) % H) * C * Din;
+    double nx = 0.0;
+    for (long d = 0; d < Din; ++d) nx += x[d] * x[d];
+    for (long d = 0; d < Din; ++d) dX[r * Din + d] = 0.0;
+    for (long c = 0; c < C; ++c) {
+      double t = 0.0;
+      for (long d = 0; d < Din; ++d) t += w[c * Din + d] * x[d];
+      const double gphi = dPhi[r * C + c] * exp(t - 0.5 * nx) * sc;
+      for (long d = 0; d < Din; ++d) dX[r * Din + d] += gphi * (w[c * Din + d] - x[d]);
+    }
+  }
+}
+
+/*
+ * Degree-2 polynomial features ("Linear Attention/zh", feature maps:
+ * phi(x) = (1, x, x (x) x, ...) truncated; "Transformers are RNNs -- part
+ * 2/3", section 3.2.1: the polynomial kernel has an exact finite feature
+ * map, degree 2 costs O(N D^2 M)):
+ *   phi(x) = (1, x_1 .. x_Din, x_a x_b for a, b = 1..Din, a-major),
+ * followed by zeros up to C >= 1 + Din + Din^2, so that
+ * phi(x) . phi(y) = 1 + x . y + (x . y)^2.  X [rows, Din], Phi [rows, C].
+ */
+void orc_feature_poly2(const double *X, double *Phi, long rows, long Din,
+                       long C) {
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const double *x = X + r * Din;
+    double *f = Phi + r * C;
+    for (long c = 0; c < C; ++c) f[c] = 0.0;
+    f[0] = 1.0;
+    for (long a = 0; a < Din; ++a) f[1 + a] = x[a];
+    for (long a = 0; a < Din; ++a)
+      for (long b = 0; b < Din; ++b) f[1 + Din + a * Din + b] = x[a] * x[b];
+  }
+}
+
+/* Vector-Jacobian product of orc_feature_poly2: dX_a = dPhi[1 + a] +
+ * sum_b (dPhi[1 + Din + a Din + b] + dPhi[1 + Din + b Din + a]) x_b. */
+void orc_feature_poly2_vjp(const double *X, const double *dPhi, double *dX,
+                           long rows, long Din, long C) {
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    const double *x = X + r * Din, *g = dPhi + r * C;
+    for (long a = 0; a < Din; ++a) {
+      double acc = g[1 + a];
+      for (long b = 0; b < Din; ++b)
+        acc += (g[1 + Din + a * Din + b] + g[1 + Din + b * Din + a]) * x[b];
+      dX[r * Din + a] = acc;
     }
   }
 }

@@ -139,6 +139,21 @@ def brute_decay_grad(q, k, v, log_a, s0, z0, do, dsn, dzn):
     return tuple(t.grad.numpy() for t in ts)
 
 
+def brute_poly2_attention_grad(q, k, v, do, causal=True):
+    """Attention with the degree-2 polynomial kernel sim(q, k) = 1 + q.k + (q.k)^2 written directly (no feature
+    map), O and the gradients of sum(dO * O) with respect to q, k, v by PyTorch autograd in float64."""
+    ts = [torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True) for a in (q, k, v)]
+    tq, tk, tv = ts
+    dot = tq @ tk.transpose(-1, -2)
+    sim = 1.0 + dot + dot * dot
+    if causal:
+        n = tq.shape[-2]
+        sim = sim * torch.tril(torch.ones((n, n), dtype=torch.float64))
+    out = (sim @ tv) / sim.sum(dim=-1, keepdim=True)
+    (out * torch.from_numpy(np.asarray(do, dtype=np.float64))).sum().backward()
+    return (out.detach().numpy(),) + tuple(t.grad.numpy() for t in ts)
+
+
 def brute_numerator(p, kf, vb):
     """Numerator of eq. 9 on feature-mapped inputs: Vbar_i = sum_{j<=i} (P_i . Kf_j) Vb_j."""
     n = p.shape[0]

@@ -70,8 +70,8 @@ def fwd(lib, B=2, H=2, N=100, D=32, M=32, dtype=0, ws=True, **over):
         nb = over.pop("ws_bytes")
         args.pop("ws_bytes")
     return lib.la_forward_causal(args["Q"], args["K"], args["V"], args["logA"], args["O"], args["den"], args["S0"],
-                                 args["Z0"], args["S_out"], args["Z_out"], args["ckpt"], B, H, N, D, M, dtype, wsp, nb,
-                                 None)
+                                 args["Z0"], args["S_out"], args["Z_out"], args["ckpt"], B, H, N, D, M, dtype,
+                                 args.get("feature", 0), wsp, nb, None)
 
 
 def test_forward_validation(lib):
@@ -95,12 +95,12 @@ def test_forward_validation(lib):
 
 def test_noncausal_and_backward_validation(lib):
     ws = lib.la_workspace_size(1, 1, 1, 64, 64, 64, 1)
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), None, 1, 1, 64, 64, 64, 1, addr(20), ws, None) == NULL
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), 1, 1, 64, 64, 64, 1, None, 0, None) == WORKSPACE
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(3), 1, 1, 64, 64, 64, 1, addr(20), ws,
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), None, 1, 1, 64, 64, 64, 1, 0, addr(20), ws, None) == NULL
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), 1, 1, 64, 64, 64, 1, 0, None, 0, None) == WORKSPACE
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(3), 1, 1, 64, 64, 64, 1, 0, addr(20), ws,
                                     None) == ALIAS
     # N = 0 is a no-op
-    assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, None, 0, None) == OK
+    assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, 0, None, 0, None) == OK
     wsb = lib.la_workspace_size(2, 2, 2, 100, 32, 32, 0)
     names = ["Q", "K", "V", "logA", "O", "den", "dO", "S0", "Z0", "ckpt", "dS_N", "dZ_N", "dQ", "dK", "dV", "dlogA",
              "dS0", "dZ0"]
@@ -110,7 +110,7 @@ def test_noncausal_and_backward_validation(lib):
     def bwd(N=100, ws=addr(20), nb=wsb, **over):
         a = dict(base)
         a.update(over)
-        return lib.la_backward_causal(*[a.get(n) for n in names], 2, 2, N, 32, 32, 0, ws, nb, None)
+        return lib.la_backward_causal(*[a.get(n) for n in names], 2, 2, N, 32, 32, 0, a.get("feature", 0), ws, nb, None)
 
     assert bwd(den=None) == NULL  # den is required
     assert bwd(dQ=addr(6)) == ALIAS  # dQ on top of dO
@@ -133,6 +133,14 @@ def test_noncausal_and_backward_validation(lib):
     assert bwd(logA=ctypes.c_void_p(BASE + 14 * (1 << 32) + 4), dlogA=addr(15), nb=wsd) == ALIGN
 
 
+def test_feature_argument_validation(lib):
+    assert fwd(lib, feature=2) == ARG
+    assert fwd(lib, feature=-1) == ARG
+    assert b"feature" in lib.la_last_error()
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 64, 64, 1, 5,
+                              None) == ARG
+
+
 def test_decay_forward_validation(lib):
     assert fwd(lib, logA=addr(14), ws_bytes=lib.la_workspace_size(0, 2, 2, 100, 32, 32, 0)) == WORKSPACE
     assert fwd(lib, logA=addr(4)) == ALIAS  # O on top of logA
@@ -145,23 +153,23 @@ def test_noncausal_backward_validation(lib):
     args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7)]
     a = list(args)
     a[4] = None
-    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, addr(20), ws, None) == NULL
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == NULL
     a = list(args)
     a[5] = addr(1)  # dK on top of Q
-    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, addr(20), ws, None) == ALIAS
-    assert lib.la_backward_noncausal(*args, 2, 2, 100, 32, 32, 0, addr(20), ws - 1, None) == WORKSPACE
-    assert lib.la_backward_noncausal(*args, 2, 2, 100, 48, 32, 0, addr(20), ws, None) == UNSUPPORTED
-    assert lib.la_backward_noncausal(*args, 2, 2, 0, 32, 32, 0, None, 0, None) == OK
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == ALIAS
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 32, 32, 0, 0, addr(20), ws - 1, None) == WORKSPACE
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 48, 32, 0, 0, addr(20), ws, None) == UNSUPPORTED
+    assert lib.la_backward_noncausal(*args, 2, 2, 0, 32, 32, 0, 0, None, 0, None) == OK
 
 
 def test_decode_validation(lib):
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), None, 2, 2, 64, 64, 1, None) == NULL
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, None) == ALIAS
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(5), addr(6), 2, 2, 64, 64, 1,
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), None, 2, 2, 64, 64, 1, 0, None) == NULL
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(4), addr(6), 2, 2, 64, 64, 1, 0, None) == ALIAS
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(4), addr(4), addr(5), addr(6), 2, 2, 64, 64, 1, 0,
                               None) == ALIAS  # S on top of logA
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 16, 64, 1,
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 16, 64, 1, 0,
                               None) == UNSUPPORTED
-    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, None) == SHAPE
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, 0, None) == SHAPE
 
 
 def _plan(B, H, N):

@@ -25,20 +25,20 @@ MUTATIONS = {
     "parallel form sees one future token": ("for (long j = 0; j <= i; ++j) {\n        double a",
                                              "for (long j = 0; j <= i + (i + 1 < N); ++j) {\n        double a"),
     "denominator gradient sign": ("G[i * Mb + M] = -dot / den[i];", "G[i * Mb + M] = dot / den[i];"),
-    "chain rule uses phi not phi'": ("dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_dphi(q[i * D + d]);",
-                                     "dQ[(bh * N + i) * D + d] = dP[i * D + d] * orc_phi(q[i * D + d]);"),
+    "chain rule uses phi not phi'": ("dQ[(bh * N + i) * D + d] = dP[i * D + d] * dfeat(q[i * D + d], fm);",
+                                     "dQ[(bh * N + i) * D + d] = dP[i * D + d] * feat(q[i * D + d], fm);"),
     "eq. 15 transposed operand": ("acc += R[c * Mb + m] * Kf[i * C + c];", "acc += R[c * Mb + m] * P[i * C + c];"),
     "eq. 14 reverse sum of wrong factor": ("R[c * Mb + m] += P[i * C + c] * G[i * Mb + m];",
                                            "R[c * Mb + m] += Kf[i * C + c] * G[i * Mb + m];"),
     "eq. 13 forward sum off by one": ("    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m];\n      dP[i * C + c] = acc;\n    }\n  }",
                                       "    for (long c = 0; c < C; ++c) {\n      double acc = 0.0;\n      for (long m = 0; m < Mb; ++m) acc += S[c * Mb + m] * G[i * Mb + m] * (i > 0);\n      dP[i * C + c] = acc;\n    }\n  }"),
-    "non-causal drops phi on keys": ("double pk = orc_phi(k[d]);\n        for", "double pk = k[d];\n        for"),
+    "non-causal drops phi on keys": ("double pk = feat(k[d], fm);\n        for", "double pk = k[d];\n        for"),
     "decode normaliser ignores keys": ("      z[d] = a * z[d] + pk;", "      z[d] = a * z[d] + 1.0;"),
     "non-causal backward denominator sign": ("double c = -dot / den;", "double c = dot / den;"),
     "non-causal reverse sum of phi(K)": ("for (long m = 0; m < M; ++m) R[d * M + m] += pq[d] * g[m];",
-                                         "for (long m = 0; m < M; ++m) R[d * M + m] += orc_phi(k[i * D + d]) * g[m];"),
-    "non-causal value gradient uses phi(Q)": ("for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(k[j * D + d]);",
-                                              "for (long d = 0; d < D; ++d) acc += R[d * M + m] * orc_phi(q[j * D + d]);"),
+                                         "for (long m = 0; m < M; ++m) R[d * M + m] += feat(k[i * D + d], fm) * g[m];"),
+    "non-causal value gradient uses phi(Q)": ("for (long d = 0; d < D; ++d) acc += R[d * M + m] * feat(k[j * D + d], fm);",
+                                              "for (long d = 0; d < D; ++d) acc += R[d * M + m] * feat(q[j * D + d], fm);"),
     "final-state gradient not carried": ("if (RN) memcpy(R, RN, (size_t)(C * Mb) * sizeof(double));",
                                          "if (RN) memset(R, 0, (size_t)(C * Mb) * sizeof(double));"),
     "initial-state gradient misses token 1": (
@@ -50,6 +50,15 @@ MUTATIONS = {
     "decay gradient misses a_t": ("dlogA[bh * N + i] = a * ip;", "dlogA[bh * N + i] = ip;"),
     "decay gradient uses the current state": ("ip += R[e] * prev[e];", "ip += R[e] * cur[e];"),
     "reverse state not decayed": ("for (long e = 0; e < SB; ++e) R[e] *= a;", "(void)a;"),
+    "feature mode still applies elu + 1": ("static double feat(double x, long fm) { return fm ? x : orc_phi(x); }",
+                                          "static double feat(double x, long fm) { return orc_phi(x); }"),
+    "poly2 features drop the constant": ("    f[0] = 1.0;\n", "    f[0] = 0.0;\n"),
+    "poly2 gradient misses the transposed term": (
+        "acc += (g[1 + Din + a * Din + b] + g[1 + Din + b * Din + a]) * x[b];",
+        "acc += 2.0 * g[1 + Din + a * Din + b] * x[b];"),
+    "random features miss the norm term": ("Phi[r * C + c] = exp(t - 0.5 * nx) * sc;", "Phi[r * C + c] = exp(t) * sc;"),
+    "random-feature gradient misses -x": ("dX[r * Din + d] += gphi * (w[c * Din + d] - x[d]);",
+                                          "dX[r * Din + d] += gphi * w[c * Din + d];"),
     "initial state ignored in backward": ("acc += (Z0 ? Z0[bh * D + d] : 0.0) * G[i * Mb + M];",
                                           "acc += 0.0 * G[i * Mb + M];"),
 }
@@ -85,6 +94,12 @@ PIN_CALLS = [
     P.test_decay_backward_finite_differences,
     P.test_decay_decode_equals_forward,
     P.test_decay_log_gradient_identity,
+    P.test_poly2_features_give_the_polynomial_kernel,
+    P.test_performer_features_are_unbiased_for_exp,
+    lambda: P.test_feature_vjp_finite_differences("poly2"),
+    lambda: P.test_feature_vjp_finite_differences("performer"),
+    lambda: P.test_feature_mode_with_poly2_is_the_polynomial_attention(True),
+    P.test_feature_mode_with_elu_features_is_the_method,
 ]
 
 

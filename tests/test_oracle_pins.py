@@ -663,3 +663,86 @@ def test_decay_query_gradient_is_orthogonal_to_phi_q():
     x = (pins.phi_lib(q) * dq / np.where(qd > 0, 1.0, np.exp(qd))).sum(-1)
     scale = (np.abs(pins.phi_lib(q)) * np.abs(dq / np.where(qd > 0, 1.0, np.exp(qd)))).sum(-1)
     assert np.max(np.abs(x) / scale) < 1e-12
+
+
+# ----------------------------------------------------- other feature maps (f4)
+def test_poly2_features_give_the_polynomial_kernel():
+    """phi(x).phi(y) = 1 + x.y + (x.y)^2 for the degree-2 features, zero padding included."""
+    x = inputs.gaussian((7, 5), 401).astype(np.float64)
+    y = inputs.gaussian((9, 5), 402).astype(np.float64)
+    fx, fy = oracle.feature_poly2(x, 32), oracle.feature_poly2(y, 32)
+    dot = x @ y.T
+    np.testing.assert_allclose(fx @ fy.T, 1.0 + dot + dot ** 2, rtol=1e-13, atol=1e-13)
+
+
+def test_performer_features_are_unbiased_for_exp():
+    """E over standard normal projections of phi(x).phi(y) is exp(x.y) (Gaussian moment generating function);
+    checked with 400000 random features within five standard errors."""
+    rng = np.random.Generator(np.random.PCG64(403))
+    x = 0.4 * rng.standard_normal((1, 1, 3, 4))
+    y = 0.4 * rng.standard_normal((1, 1, 3, 4))
+    C = 400_000
+    w = rng.standard_normal((1, C, 4))
+    fx, fy = oracle.feature_performer(x, w), oracle.feature_performer(y, w)
+    est = np.einsum("bhnc,bhmc->nm", fx, fy)
+    terms = np.einsum("bhnc,bhmc->nmc", fx, fy) * C  # per-feature samples of the estimator
+    se = terms.std(axis=-1) / np.sqrt(C)
+    ref = np.exp(np.einsum("bhnd,bhmd->nm", x, y))
+    assert np.all(np.abs(est - ref) <= 5 * se + 1e-12)
+
+
+@pytest.mark.parametrize("which", ["poly2", "performer"])
+def test_feature_vjp_finite_differences(which):
+    rng = np.random.Generator(np.random.PCG64(404))
+    x = 0.7 * rng.standard_normal((1, 2, 3, 4))
+    dphi = rng.standard_normal((1, 2, 3, 32))
+    w = rng.standard_normal((2, 32, 4))
+    f = (lambda a: oracle.feature_poly2(a, 32)) if which == "poly2" else (lambda a: oracle.feature_performer(a, w))
+    g = oracle.feature_poly2_vjp(x, dphi) if which == "poly2" else oracle.feature_performer_vjp(x, w, dphi)
+    h = 1e-6
+    fd = np.empty_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = (np.sum(dphi * f(xp)) - np.sum(dphi * f(xm))) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-7, atol=1e-9)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_feature_mode_with_poly2_is_the_polynomial_attention(causal):
+    """Degree-2 features through the attention in feature mode, then the chain rule through the features,
+    equal the attention with the polynomial kernel written directly, and its autograd gradients."""
+    B, H, N, Din, M = 2, 2, 13, 5, 4
+    rng = np.random.Generator(np.random.PCG64(405))
+    q, k = 0.6 * rng.standard_normal((B, H, N, Din)), 0.6 * rng.standard_normal((B, H, N, Din))
+    v, do = rng.standard_normal((B, H, N, M)), rng.standard_normal((B, H, N, M))
+    fq, fk = oracle.feature_poly2(q, 32), oracle.feature_poly2(k, 32)
+    if causal:
+        o = oracle.forward_causal(fq, fk, v, feature=1)[0]
+        dfq, dfk, dv = oracle.backward_causal(fq, fk, v, do, feature=1)
+    else:
+        o = oracle.forward_noncausal(fq, fk, v, feature=1)
+        dfq, dfk, dv = oracle.backward_noncausal(fq, fk, v, do, feature=1)
+    ro, rq, rk, rv = pins.brute_poly2_attention_grad(q, k, v, do, causal)
+    np.testing.assert_allclose(o, ro, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(oracle.feature_poly2_vjp(q, dfq), rq, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(oracle.feature_poly2_vjp(k, dfk), rk, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, rv, rtol=1e-10, atol=1e-12)
+
+
+def test_feature_mode_with_elu_features_is_the_method():
+    """elu + 1 applied beforehand and the identity in the attention reproduce the plain method; the feature
+    gradients times phi' are its raw gradients."""
+    B, H, N, D, M = 1, 2, 11, 4, 3
+    q, k, v = _qkv((B, H, N, D, M), 406)
+    do = inputs.gaussian(v.shape, 407).astype(np.float64)
+    fq, fk = pins.phi_lib(q), pins.phi_lib(k)
+    for a, b in zip(oracle.forward_causal(fq, fk, v, feature=1), oracle.forward_causal(q, k, v)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    dfq, dfk, dv = oracle.backward_causal(fq, fk, v, do, feature=1)
+    dq, dk, dv0 = oracle.backward_causal(q, k, v, do)
+    qd, kd = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    np.testing.assert_allclose(dfq * np.where(qd > 0, 1.0, np.exp(qd)), dq, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dfk * np.where(kd > 0, 1.0, np.exp(kd)), dk, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dv, dv0, rtol=1e-12, atol=1e-14)
