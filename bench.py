@@ -10,7 +10,9 @@ of B=4 H=8 N=3072 D=M=32, bf16, sigma 0.5, forward + backward each), long
 independent non-causal layers of B=16 H=6 N=800 D=M=32, float32, non-causal
 forward + backward each), long-decay (the long shape with a per-token,
 per-head decay on the state: decayed forward + backward including the
-gradient of the log-decay), decode (one
+gradient of the log-decay), mnist-rf (the mnist shape with 64 positive random
+features in place of elu + 1: feature maps, causal forward and backward in
+feature mode, chain rule through the features), decode (one
 step = one la_decode_step on B=256 H=16 D=M=64 after a 512-token prefill),
 small (B=1 H=1 N=64 D=M=32 float32 causal forward).
 
@@ -45,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "long-decay", "speech", "decode", "small"])
+    ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "long-decay", "mnist-rf", "speech", "decode",
+                                                            "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
@@ -87,7 +90,7 @@ class Step:
             return
         if wl in ("cifar", "speech"):
             nsets = w.layers  # one independent input set per layer
-        elif wl == "mnist":
+        elif wl in ("mnist", "mnist-rf"):
             nsets = 6  # rotate batches so successive steps do not hit the 256 MB last-level cache
         else:
             nsets = 1
@@ -113,6 +116,16 @@ class Step:
         self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
         if wl == "speech":
             self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+        if wl == "mnist-rf":
+            C = w.features
+            self.W = torch.from_numpy(w.projection()).to("cuda").contiguous()
+            self.fq = torch.empty((B, H, N, C), dtype=dt, device="cuda")
+            self.fk = torch.empty((B, H, N, C), dtype=dt, device="cuda")
+            self.dfq = torch.empty((B, H, N, C), dtype=dt, device="cuda")
+            self.dfk = torch.empty((B, H, N, C), dtype=dt, device="cuda")
+            self.ck = torch.empty(binding.checkpoint_size(B, H, N, C, M) // 4, dtype=torch.float32, device="cuda")
+            self.ws_f = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, C, M, code, "cuda")
+            self.ws_b = binding.alloc_workspace(binding.LA_OP_BWD_CAUSAL, B, H, N, C, M, code, "cuda")
         if wl == "long-decay":
             self.log_a = torch.from_numpy(w.log_a()).to("cuda").contiguous()
             self.dla = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -151,7 +164,8 @@ class Step:
         qs, ks, vs = self.pool_q.stride(0) * 2, self.pool_k.stride(0) * 2, self.pool_v.stride(0) * 2
         self._args = [(ctypes.c_void_p(self.pool_q.data_ptr() + i * qs), ctypes.c_void_p(self.pool_k.data_ptr() + i * ks),
                        ctypes.c_void_p(self.pool_v.data_ptr() + i * vs), None, ctypes.c_void_p(self.S.data_ptr()),
-                       ctypes.c_void_p(self.Z.data_ptr()), ctypes.c_void_p(self.y.data_ptr()), B, H, D, M, code, stream)
+                       ctypes.c_void_p(self.Z.data_ptr()), ctypes.c_void_p(self.y.data_ptr()), B, H, D, M, code, 0,
+                       stream)
                       for i in range(pool)]
         self.i = 0
 
@@ -172,6 +186,21 @@ class Step:
             for (q, k, v, do) in self.sets:
                 b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n)
                 b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb)
+            return
+        if wl == "mnist-rf":
+            q, k, v, do = self.sets[self.i % len(self.sets)]
+            self.i += 1
+            lib, st = b.load(), b._stream(None)
+            B, H, N, D, M, C = self.w.B, self.w.H, self.w.N, self.w.D, self.w.M, self.w.features
+            IDENT = b.LA_FEATURE_IDENTITY
+            for x, f in ((q, self.fq), (k, self.fk)):
+                b._check(lib.la_feature_random(b._ptr(x), b._ptr(self.W), b._ptr(f), B, H, N, D, C, 0, st), "rf")
+            b.la_forward_causal(self.fq, self.fk, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f, feature=IDENT)
+            b.la_backward_causal(self.fq, self.fk, v, self.o, self.den, do, self.dfq, self.dfk, self.dv, ckpt=self.ck,
+                                 ws=self.ws_b, feature=IDENT)
+            for x, g, dx in ((q, self.dfq, self.dq), (k, self.dfk, self.dk)):
+                b._check(lib.la_feature_random_vjp(b._ptr(x), b._ptr(self.W), b._ptr(g), b._ptr(dx), B, H, N, D, C, 0,
+                                                   st), "rf_vjp")
             return
         if wl == "long-decay":
             q, k, v, do = self.sets[0]
@@ -196,14 +225,17 @@ class Step:
 
 def WORKLOADS(inputs):
     return {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "speech": inputs.SPEECH,
-            "long-decay": inputs.LONG_DECAY, "decode": inputs.DECODE, "small": inputs.SMALL}
+            "long-decay": inputs.LONG_DECAY, "mnist-rf": inputs.MNIST_RF, "decode": inputs.DECODE,
+            "small": inputs.SMALL}
 
 
 # ---------------------------------------------------- algorithmic figures
 def kernel_bytes(name, w, s):
     """Algorithmic HBM bytes per launch: the tensors the kernel must read or write by its function
-    (per token-head: the survey's forward (2D+2M)s+4 and backward figures split over the kernels)."""
-    D, M = w.D, w.M
+    (per token-head: the survey's forward (2D+2M)s+4 and backward figures split over the kernels).  With
+    random features the attention kernels see feature vectors of size C in place of D."""
+    Din, M = w.D, w.M
+    D = w.features or Din
     th = w.B * w.H * w.N
     per_th = {
         "fwd_causal": (2 * D + 2 * M) * s + 4,   # read Q, K, V; write O, den
@@ -218,6 +250,8 @@ def kernel_bytes(name, w, s):
         "dbq": (3 * D + 2 * M) * s + 12,         # read Q, K, V, dO, logA; write dQ, (1/den, c)
         "dbkv": (3 * D + 3 * M) * s + 16,        # read Q, K, V, dO, logA, (1/den, c); write dK, dV, dlogA terms
         "dla_fix": 8,                            # read and write dlogA
+        "feat_rf": (Din + D) * s,                # read X; write Phi
+        "feat_rf_vjp": (2 * Din + D) * s,        # read X, dPhi; write dX
     }
     if name == "decode":
         return w.B * w.H * (2 * D * M * 4 + 2 * D * 4 + (2 * D + 2 * M) * s)
@@ -227,7 +261,7 @@ def kernel_bytes(name, w, s):
 
 
 def kernel_flops(name, w):
-    D, M = w.D, w.M
+    D, M = w.features or w.D, w.M
     th = w.B * w.H * w.N
     if name == "fwd_causal":
         return th * (4 * D * M + 5 * D + M)
@@ -263,7 +297,8 @@ KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_se
                ("k_scan_states<", "scan_states"), ("k_scan_rev<", "scan_rev"), ("k_decode<", "decode"),
                ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"), ("k_dseg_state<", "dseg_state"),
                ("k_dscan_states<", "dscan_states"), ("k_dfwd<", "dfwd"), ("k_dbq<", "dbq"),
-               ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_fix", "dla_fix"))
+               ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_fix", "dla_fix"),
+               ("k_feat_rf_vjp<", "feat_rf_vjp"), ("k_feat_rf<", "feat_rf"))
 
 
 def kernel_tag(full_name):
@@ -437,15 +472,27 @@ def cpu_baseline(args, w):
                 "kind": "oracle", "sample": f"{steps} steps on {nheads} of {w.B * w.H} heads, scaled to all heads"}
     # token workloads: run the oracle's passes of one step on a subset of heads until >= 10 s
     B, H, N = w.B, w.H, w.N
-    nb = {"mnist": 4, "cifar": 1, "long": 1, "long-decay": 1, "speech": 4, "small": 1}[wl]
-    nh = {"mnist": H, "cifar": 8, "long": 2, "long-decay": 2, "speech": H, "small": 1}[wl]
-    n = {"mnist": N, "cifar": N, "long": 16384, "long-decay": 8192, "speech": N, "small": N}[wl]
+    nb = {"mnist": 4, "cifar": 1, "long": 1, "long-decay": 1, "mnist-rf": 4, "speech": 4, "small": 1}[wl]
+    nh = {"mnist": H, "cifar": 8, "long": 2, "long-decay": 2, "mnist-rf": H, "speech": H, "small": 1}[wl]
+    n = {"mnist": N, "cifar": N, "long": 16384, "long-decay": 8192, "mnist-rf": N, "speech": N, "small": N}[wl]
     q, k, v = (a[:nb, :nh, :n] for a in w.qkv(n=n))
     do = w.grad_out(n=n)[:nb, :nh, :n]
     reps = 0
     t = time.perf_counter()
     la = w.log_a(n=n)[:nb, :nh, :n] if wl == "long-decay" else None
+    wp = w.projection() if wl == "mnist-rf" else None
     while True:
+        if wl == "mnist-rf":
+            fq, fk = oracle.feature_performer(q, wp[:nh]), oracle.feature_performer(k, wp[:nh])
+            oracle.forward_causal(fq, fk, v, feature=1)
+            dfq, dfk, _ = oracle.backward_causal(fq, fk, v, do, feature=1)
+            oracle.feature_performer_vjp(q, wp[:nh], dfq)
+            oracle.feature_performer_vjp(k, wp[:nh], dfk)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= 10.0 or reps >= 1000:
+                break
+            continue
         if wl == "long-decay":
             oracle.forward_decay(q, k, v, la)
             oracle.backward_decay(q, k, v, la, do)
@@ -552,6 +599,9 @@ def main():
     elif args.workload == "speech":
         metric, unit = "non-causal linear-attn fwd+bwd tokens/s", "tokens/s"
         value = w.B * w.N * args.steps / el
+    elif args.workload == "mnist-rf":
+        metric, unit = "random-feature causal linear-attn fwd+bwd tokens/s", "tokens/s"
+        value = w.B * w.N * args.steps / el
     elif args.workload == "long-decay":
         metric, unit = "decayed causal linear-attn fwd+bwd tokens/s", "tokens/s"
         value = w.B * w.N * args.steps / el
@@ -591,6 +641,9 @@ def main():
         cfg["step"] = "causal forward + backward"
     elif args.workload == "long-decay":
         cfg["step"] = "decayed causal forward + backward (dQ, dK, dV, dlogA)"
+    elif args.workload == "mnist-rf":
+        cfg["step"] = "random features of Q, K (C = 64) + causal forward and backward on them + chain rule to Q, K"
+        cfg["features"] = w.features
     elif args.workload == "speech":
         cfg["step"] = "9 layers x (non-causal forward + backward)"
         cfg["layers"] = 9

@@ -71,6 +71,18 @@ typedef enum {
   LA_OP_BWD_DECAY = 6  /* la_backward_causal with logA */
 } la_op;
 
+/* Feature map applied to Q and K by the attention entry points.
+ *   LA_FEATURE_ELU1      phi(x) = elu(x) + 1 ("Transformers are RNNs -- part 2/3",
+ *                        eq. 7); gradients are with respect to the raw Q, K.
+ *   LA_FEATURE_IDENTITY  Q and K already hold feature vectors phi(q), phi(k)
+ *                        of dimension D (another feature map: "Linear
+ *                        Attention/zh", feature maps -- polynomial, positive
+ *                        random features; see la_feature_*); they are used as
+ *                        they are and the gradients are with respect to them.
+ *                        The similarities phi(q).phi(k) summed into each
+ *                        denominator must be positive. */
+typedef enum { LA_FEATURE_ELU1 = 0, LA_FEATURE_IDENTITY = 1 } la_feature;
+
 /* Library version, as 10000*major + 100*minor + patch. */
 int la_version(void);
 
@@ -127,7 +139,7 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
                       const float *logA, void *O, float *den, const float *S0,
                       const float *Z0, float *S_out, float *Z_out,
                       float *ckpt, int B, int H, int N, int D, int M,
-                      int dtype, void *ws, size_t ws_bytes, void *stream);
+                      int dtype, int feature, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
@@ -135,7 +147,7 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
  * per head and reused for every query, O_i = phi(Q_i)^T S / phi(Q_i)^T Z.
  */
 int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
-                         int B, int H, int N, int D, int M, int dtype,
+                         int B, int H, int N, int D, int M, int dtype, int feature,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -178,7 +190,7 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
                        const float *ckpt, const float *dS_N,
                        const float *dZ_N, void *dQ, void *dK, void *dV,
                        float *dlogA, float *dS0, float *dZ0, int B, int H,
-                       int N, int D, int M, int dtype, void *ws,
+                       int N, int D, int M, int dtype, int feature, void *ws,
                        size_t ws_bytes, void *stream);
 
 /*
@@ -199,7 +211,7 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
  */
 int la_backward_noncausal(const void *Q, const void *K, const void *V,
                           const void *dO, void *dQ, void *dK, void *dV, int B,
-                          int H, int N, int D, int M, int dtype, void *ws,
+                          int H, int N, int D, int M, int dtype, int feature, void *ws,
                           size_t ws_bytes, void *stream);
 
 /*
@@ -215,9 +227,48 @@ int la_backward_noncausal(const void *Q, const void *K, const void *V,
  */
 int la_decode_step(const void *q, const void *k, const void *v,
                    const float *logA, float *S, float *Z, void *y, int B,
-                   int H, int D, int M, int dtype, void *stream);
+                   int H, int D, int M, int dtype, int feature, void *stream);
 
 /* Name of a status code. */
+/*
+ * Positive random features ("Linear Attention/zh", feature maps: Performer's
+ * phi(x) proportional to exp(W x - |x|^2 / 2); "The Transformer Family v2",
+ * random feature attention): Phi[b,h,n,c] = exp(W[h,c,:] . X[b,h,n,:] -
+ * |X[b,h,n,:]|^2 / 2) / sqrt(C), so phi(x) . phi(y) estimates exp(x . y)
+ * without bias when the rows of W are standard normal.  Feed Phi of queries
+ * and keys to the attention entry points with LA_FEATURE_IDENTITY.
+ *   X    [B,H,N,Din] in `dtype`; W [H,C,Din] float32 (the random projection,
+ *        owned by the caller); Phi [B,H,N,C] output in `dtype`.
+ *   Din, C in {32, 64}.  Same validation and error behaviour as the
+ *   attention entry points; asynchronous on `stream`.
+ */
+int la_feature_random(const void *X, const float *W, void *Phi, int B, int H,
+                      int N, int Din, int C, int dtype, void *stream);
+
+/* Vector-Jacobian product of la_feature_random: dX = sum_c dPhi_c phi_c
+ * (W_c - x), with phi recomputed in float32.  dPhi [B,H,N,C], dX
+ * [B,H,N,Din] in `dtype`. */
+int la_feature_random_vjp(const void *X, const float *W, const void *dPhi,
+                          void *dX, int B, int H, int N, int Din, int C,
+                          int dtype, void *stream);
+
+/*
+ * Degree-2 polynomial features ("Linear Attention/zh", feature maps:
+ * phi(x) = (1, x, x (x) x) truncated; "Transformers are RNNs -- part 2/3",
+ * section 3.2.1): Phi = (1, x_1 .. x_Din, x_a x_b for a, b = 1..Din
+ * a-major, then zeros up to C), so phi(x) . phi(y) = 1 + x.y + (x.y)^2 > 0.
+ *   X [B,H,N,Din], Phi [B,H,N,C] in `dtype`; C in {32, 64} with
+ *   1 + Din + Din^2 <= C (Din <= 5 for C = 32, <= 7 for C = 64).
+ */
+int la_feature_poly2(const void *X, void *Phi, int B, int H, int N, int Din,
+                     int C, int dtype, void *stream);
+
+/* Vector-Jacobian product of la_feature_poly2: dX_a = dPhi[1 + a] +
+ * sum_b (dPhi[1 + Din + a Din + b] + dPhi[1 + Din + b Din + a]) x_b. */
+int la_feature_poly2_vjp(const void *X, const void *dPhi, void *dX, int B,
+                         int H, int N, int Din, int C, int dtype,
+                         void *stream);
+
 const char *la_status_string(int status);
 
 /* Detail of the last non-OK status returned on this thread ("" if none). */

@@ -20,10 +20,12 @@ from . import build as _build
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FWD_CAUSAL, LA_OP_FWD_NONCAUSAL, LA_OP_BWD_CAUSAL, LA_OP_DECODE, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3, 4
 LA_OP_FWD_DECAY, LA_OP_BWD_DECAY = 5, 6
+LA_FEATURE_ELU1, LA_FEATURE_IDENTITY = 0, 1
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
                 "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
                 "la_status_string", "la_last_error", "la_prof_select", "la_prof_collect", "la_kernel_names",
-                "la_set_segment_chunks")
+                "la_set_segment_chunks", "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
+                "la_feature_poly2_vjp")
 
 _lib = None
 
@@ -55,15 +57,19 @@ def load(path: str | None = None):
     lib.la_segment_length.restype = i
     lib.la_segment_length.argtypes = [i] * 5
     lib.la_forward_causal.restype = i
-    lib.la_forward_causal.argtypes = [vp] * 11 + [i] * 6 + [vp, sz, vp]
+    lib.la_forward_causal.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
     lib.la_forward_noncausal.restype = i
-    lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 6 + [vp, sz, vp]
+    lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 7 + [vp, sz, vp]
     lib.la_backward_causal.restype = i
-    lib.la_backward_causal.argtypes = [vp] * 18 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_causal.argtypes = [vp] * 18 + [i] * 7 + [vp, sz, vp]
     lib.la_backward_noncausal.restype = i
-    lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 6 + [vp, sz, vp]
+    lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 7 + [vp, sz, vp]
     lib.la_decode_step.restype = i
-    lib.la_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
+    lib.la_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    for name, nptr in (("la_feature_random", 3), ("la_feature_random_vjp", 4), ("la_feature_poly2", 2),
+                       ("la_feature_poly2_vjp", 3)):
+        getattr(lib, name).restype = i
+        getattr(lib, name).argtypes = [vp] * nptr + [i] * 6 + [vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_last_error.restype = ctypes.c_char_p
@@ -144,55 +150,55 @@ def alloc_workspace(op: int, B, H, N, D, M, dtype: int, device) -> torch.Tensor:
 
 # --------------------------------------------------------- one-to-one calls
 def la_forward_causal(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=None, ckpt=None, ws=None,
-                      stream=None, logA=None):
+                      stream=None, logA=None, feature=0):
     B, H, N, D, M = _sizes(Q, V)
     dt = dtype_code(Q.dtype)
     nb = ws.numel() if ws is not None else 0
     st = load().la_forward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(logA), _ptr(O), _ptr(den), _ptr(S0), _ptr(Z0),
-                                  _ptr(S_out), _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, _ptr(ws), nb,
+                                  _ptr(S_out), _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, feature, _ptr(ws), nb,
                                   _stream(stream))
     _check(st, "la_forward_causal")
 
 
-def la_forward_noncausal(Q, K, V, O, ws=None, stream=None):
+def la_forward_noncausal(Q, K, V, O, ws=None, stream=None, feature=0):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
-    st = load().la_forward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, N, D, M, dtype_code(Q.dtype),
+    st = load().la_forward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, N, D, M, dtype_code(Q.dtype), feature,
                                      _ptr(ws), nb, _stream(stream))
     _check(st, "la_forward_noncausal")
 
 
 def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, dS_N=None, dZ_N=None,
-                       dS0=None, dZ0=None, ws=None, stream=None, logA=None, dlogA=None):
+                       dS0=None, dZ0=None, ws=None, stream=None, logA=None, dlogA=None, feature=0):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
     st = load().la_backward_causal(_ptr(Q), _ptr(K), _ptr(V), _ptr(logA), _ptr(O), _ptr(den), _ptr(dO), _ptr(S0),
                                    _ptr(Z0), _ptr(ckpt), _ptr(dS_N), _ptr(dZ_N), _ptr(dQ), _ptr(dK), _ptr(dV),
-                                   _ptr(dlogA), _ptr(dS0), _ptr(dZ0), B, H, N, D, M, dtype_code(Q.dtype), _ptr(ws),
-                                   nb, _stream(stream))
+                                   _ptr(dlogA), _ptr(dS0), _ptr(dZ0), B, H, N, D, M, dtype_code(Q.dtype), feature,
+                                   _ptr(ws), nb, _stream(stream))
     _check(st, "la_backward_causal")
 
 
-def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None):
+def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None, feature=0):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
     st = load().la_backward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, D,
-                                      M, dtype_code(Q.dtype), _ptr(ws), nb, _stream(stream))
+                                      M, dtype_code(Q.dtype), feature, _ptr(ws), nb, _stream(stream))
     _check(st, "la_backward_noncausal")
 
 
-def la_decode_step(q, k, v, S, Z, y, stream=None, logA=None):
+def la_decode_step(q, k, v, S, Z, y, stream=None, logA=None, feature=0):
     if q.dim() != 3:
         raise ValueError("decode expects q, k [B,H,D], v [B,H,M]")
     B, H, D = q.shape
     M = v.shape[-1]
     st = load().la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(logA), _ptr(S), _ptr(Z), _ptr(y), B, H, D, M,
-                               dtype_code(q.dtype), _stream(stream))
+                               dtype_code(q.dtype), feature, _stream(stream))
     _check(st, "la_decode_step")
 
 
 # ------------------------------------------------------ allocating helpers
-def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=True, log_a=None):
+def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=True, log_a=None, feature=0):
     """Causal forward (decayed by exp(log_a) [B,H,N] float32 when given).  Returns dict(o, den, ckpt[, s, z])."""
     B, H, N, D, M = _sizes(q, v)
     dev = q.device
@@ -205,23 +211,23 @@ def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=
         z = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     ws = alloc_workspace(LA_OP_FWD_DECAY if log_a is not None else LA_OP_FWD_CAUSAL, B, H, N, D, M,
                          dtype_code(q.dtype), dev)
-    la_forward_causal(q, k, v, o, den, s0, z0, s, z, ck, ws, logA=log_a)
+    la_forward_causal(q, k, v, o, den, s0, z0, s, z, ck, ws, logA=log_a, feature=feature)
     out = {"o": o, "den": den, "ckpt": ck}
     if return_state:
         out["s"], out["z"] = s, z
     return out
 
 
-def forward_noncausal(q, k, v):
+def forward_noncausal(q, k, v, feature=0):
     B, H, N, D, M = _sizes(q, v)
     o = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
     ws = alloc_workspace(LA_OP_FWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_forward_noncausal(q, k, v, o, ws)
+    la_forward_noncausal(q, k, v, o, ws, feature=feature)
     return o
 
 
 def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=None, dz_n=None, state_grad=False,
-                    log_a=None):
+                    log_a=None, feature=0):
     """Causal backward.  Returns (dq, dk, dv), then dlog_a when log_a is given, then (ds0, dz0) with
     state_grad: the gradient with respect to the initial state; ds_n, dz_n are the upstream gradients of the
     final state (None: not in the loss)."""
@@ -237,26 +243,27 @@ def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=No
         dla = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     ws = alloc_workspace(LA_OP_BWD_DECAY if log_a is not None else LA_OP_BWD_CAUSAL, B, H, N, D, M,
                          dtype_code(q.dtype), q.device)
-    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ds_n, dz_n, ds0, dz0, ws, logA=log_a, dlogA=dla)
+    la_backward_causal(q, k, v, o, den, do, dq, dk, dv, s0, z0, ckpt, ds_n, dz_n, ds0, dz0, ws, logA=log_a, dlogA=dla,
+                       feature=feature)
     out = (dq, dk, dv) + ((dla,) if log_a is not None else ())
     return out + ((ds0, dz0) if state_grad else ())
 
 
-def backward_noncausal(q, k, v, do):
+def backward_noncausal(q, k, v, do, feature=0):
     B, H, N, D, M = _sizes(q, v)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     ws = alloc_workspace(LA_OP_BWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_backward_noncausal(q, k, v, do, dq, dk, dv, ws)
+    la_backward_noncausal(q, k, v, do, dq, dk, dv, ws, feature=feature)
     return dq, dk, dv
 
 
-def decode_step(q, k, v, s, z, y=None, log_a=None):
+def decode_step(q, k, v, s, z, y=None, log_a=None, feature=0):
     """One RNN step (decayed by exp(log_a) [B,H] when given): updates s, z in place and returns y."""
     if y is None:
         y = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    la_decode_step(q, k, v, s, z, y, logA=log_a)
+    la_decode_step(q, k, v, s, z, y, logA=log_a, feature=feature)
     return y
 
 
@@ -266,7 +273,7 @@ class CausalLinearAttention(torch.autograd.Function):
     gradient flows back through the same backward."""
 
     @staticmethod
-    def forward(ctx, q, k, v, s0, z0, return_state, log_a):
+    def forward(ctx, q, k, v, s0, z0, return_state, log_a, feature):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         if (s0 is None) != (z0 is None):
             raise ValueError("s0 and z0 go together")
@@ -274,7 +281,8 @@ class CausalLinearAttention(torch.autograd.Function):
             s0, z0 = s0.contiguous(), z0.contiguous()
         if log_a is not None:
             log_a = log_a.contiguous()
-        out = forward_causal(q, k, v, s0=s0, z0=z0, return_state=return_state, log_a=log_a)
+        out = forward_causal(q, k, v, s0=s0, z0=z0, return_state=return_state, log_a=log_a, feature=feature)
+        ctx.feature = feature
         ctx.has_state = s0 is not None
         ctx.has_decay = log_a is not None
         ctx.save_for_backward(q, k, v, out["o"], out["den"], out["ckpt"], s0, z0, log_a)
@@ -289,35 +297,118 @@ class CausalLinearAttention(torch.autograd.Function):
         if ds_n is not None:
             ds_n, dz_n = ds_n.contiguous(), dz_n.contiguous()
         g = list(backward_causal(q, k, v, o, den, do.contiguous(), s0=s0, z0=z0, ckpt=ck, ds_n=ds_n, dz_n=dz_n,
-                                 state_grad=want_state, log_a=log_a))
+                                 state_grad=want_state, log_a=log_a, feature=ctx.feature))
         dla = g.pop(3) if ctx.has_decay else None
         ds0, dz0 = (g[3], g[4]) if want_state else (None, None)
-        return g[0], g[1], g[2], ds0, dz0, None, dla
+        return g[0], g[1], g[2], ds0, dz0, None, dla, None
 
 
-def causal_linear_attention(q, k, v, s0=None, z0=None, return_state=False, log_a=None):
+def causal_linear_attention(q, k, v, s0=None, z0=None, return_state=False, log_a=None, feature=0):
     """Causal linear attention through the HIP library, differentiable in q, k, v, the initial state (s0, z0)
-    and the log-decay log_a [B,H,N] (float32, <= 0) when given."""
-    return CausalLinearAttention.apply(q, k, v, s0, z0, return_state, log_a)
+    and the log-decay log_a [B,H,N] (float32, <= 0) when given.  feature=LA_FEATURE_IDENTITY takes q, k as
+    feature vectors already (see feature_map)."""
+    return CausalLinearAttention.apply(q, k, v, s0, z0, return_state, log_a, feature)
 
 
 class NonCausalLinearAttention(torch.autograd.Function):
     """Autograd wrapper of the non-causal form: forward and backward both run in the HIP library."""
 
     @staticmethod
-    def forward(ctx, q, k, v):
+    def forward(ctx, q, k, v, feature):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         ctx.save_for_backward(q, k, v)
-        return forward_noncausal(q, k, v)
+        ctx.feature = feature
+        return forward_noncausal(q, k, v, feature=feature)
 
     @staticmethod
     def backward(ctx, do):
         q, k, v = ctx.saved_tensors
-        return backward_noncausal(q, k, v, do.contiguous())
+        return backward_noncausal(q, k, v, do.contiguous(), feature=ctx.feature) + (None,)
 
 
-def noncausal_linear_attention(q, k, v):
-    return NonCausalLinearAttention.apply(q, k, v)
+def noncausal_linear_attention(q, k, v, feature=0):
+    return NonCausalLinearAttention.apply(q, k, v, feature)
+
+
+# ------------------------------------------------------------ feature maps
+def _check_x(x):
+    if x.dim() != 4:
+        raise ValueError("expected X [B,H,N,Din]")
+    return x.shape
+
+
+def feature_random(x, w):
+    """Positive random features exp(W x - |x|^2 / 2) / sqrt(C) (w [H,C,Din] float32) in x's dtype."""
+    B, H, N, Din = _check_x(x)
+    C = w.shape[1]
+    phi = torch.empty((B, H, N, C), dtype=x.dtype, device=x.device)
+    _check(load().la_feature_random(_ptr(x), _ptr(w), _ptr(phi), B, H, N, Din, C, dtype_code(x.dtype),
+                                    _stream(None)), "la_feature_random")
+    return phi
+
+
+def feature_random_vjp(x, w, dphi):
+    B, H, N, Din = _check_x(x)
+    C = w.shape[1]
+    dx = torch.empty_like(x)
+    _check(load().la_feature_random_vjp(_ptr(x), _ptr(w), _ptr(dphi), _ptr(dx), B, H, N, Din, C,
+                                        dtype_code(x.dtype), _stream(None)), "la_feature_random_vjp")
+    return dx
+
+
+def feature_poly2(x, C):
+    """Degree-2 polynomial features (1, x, x_a x_b, zeros) of size C in x's dtype."""
+    B, H, N, Din = _check_x(x)
+    phi = torch.empty((B, H, N, C), dtype=x.dtype, device=x.device)
+    _check(load().la_feature_poly2(_ptr(x), _ptr(phi), B, H, N, Din, C, dtype_code(x.dtype), _stream(None)),
+           "la_feature_poly2")
+    return phi
+
+
+def feature_poly2_vjp(x, dphi):
+    B, H, N, Din = _check_x(x)
+    dx = torch.empty_like(x)
+    _check(load().la_feature_poly2_vjp(_ptr(x), _ptr(dphi), _ptr(dx), B, H, N, Din, dphi.shape[-1],
+                                       dtype_code(x.dtype), _stream(None)), "la_feature_poly2_vjp")
+    return dx
+
+
+class RandomFeatures(torch.autograd.Function):
+    """Positive random features through the HIP library (the projection w is not differentiated)."""
+
+    @staticmethod
+    def forward(ctx, x, w):
+        x, w = x.contiguous(), w.contiguous()
+        ctx.save_for_backward(x, w)
+        return feature_random(x, w)
+
+    @staticmethod
+    def backward(ctx, dphi):
+        x, w = ctx.saved_tensors
+        return feature_random_vjp(x, w, dphi.contiguous()), None
+
+
+class Poly2Features(torch.autograd.Function):
+    """Degree-2 polynomial features through the HIP library."""
+
+    @staticmethod
+    def forward(ctx, x, C):
+        x = x.contiguous()
+        ctx.save_for_backward(x)
+        return feature_poly2(x, C)
+
+    @staticmethod
+    def backward(ctx, dphi):
+        (x,) = ctx.saved_tensors
+        return feature_poly2_vjp(x, dphi.contiguous()), None
+
+
+def random_features(x, w):
+    return RandomFeatures.apply(x, w)
+
+
+def poly2_features(x, C):
+    return Poly2Features.apply(x, C)
 
 
 # ------------------------------------------------------------- timing hooks

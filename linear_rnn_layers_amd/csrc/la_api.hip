@@ -17,6 +17,7 @@
 
 #include "../../include/la.h"
 #include "la_decay.h"
+#include "la_feature.h"
 
 namespace {
 
@@ -291,9 +292,9 @@ char* region(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 dim3 scan_grid(const Plan& p) { return dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)); }
 
 template <typename T, int D, int M>
-int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, hipStream_t s) {
+int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, int fm, hipStream_t s) {
   return launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)K, (const T*)V, agg, N, p.L, p.nseg);
+                (const T*)K, (const T*)V, agg, N, p.L, p.nseg, fm);
 }
 
 template <int D, int M>
@@ -305,7 +306,7 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
 
 template <typename T, int D, int M>
 int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
-                    const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, hipStream_t s) {
+                    const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
@@ -315,7 +316,7 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   if (p.nseg > 1) {
     const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
     agg = reinterpret_cast<float*>(region(ws, 0));
-    int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
+    int st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
     if (st) return st;
     if (use_scan(p)) {
       float* pr = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
@@ -327,16 +328,16 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   }
   return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, pref, (const float*)agg, S0, Z0, ckw, S_out,
-                Z_out, N, p.L, p.nseg);
+                Z_out, N, p.L, p.nseg, fm);
 }
 
 template <typename T, int D, int M>
 int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, int N, void* ws,
-                       hipStream_t s) {
+                       int fm, hipStream_t s) {
   if (p.nseg == 0) return LA_OK;
   const WsLayout wl = ws_layout(LA_OP_FWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
-  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
+  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
   if (st) return st;
   const float* pref = nullptr;
   if (use_scan(p)) {  // the total once per head (else every workgroup sums the aggregates)
@@ -348,7 +349,7 @@ int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, pref, (const float*)agg,
                 (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, (float*)nullptr, N,
-                p.L, p.nseg);
+                p.L, p.nseg, fm);
 }
 
 // backward workgroups resident per compute unit (LDS and registers)
@@ -369,7 +370,7 @@ template <typename T, int D, int M>
 int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* O, const float* den,
                     const void* dO, const float* S0, const float* Z0, const float* ckpt, const float* dSN,
                     const float* dZN, void* dQ, void* dK, void* dV, float* dS0, float* dZ0, int N, void* ws,
-                    hipStream_t s) {
+                    int fm, hipStream_t s) {
   if (p.nseg == 0)  // empty sequence: the initial state is the final state
     return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
                         (float*)nullptr, dS0, dZ0)
@@ -380,7 +381,7 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   if (!ck) {  // recompute the checkpoint: aggregates, then their scan
     float* agg = reinterpret_cast<float*>(region(ws, 0));
     float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
-    st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
+    st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
     if (st) return st;
     st = scan_prefix<D, M>(p, agg, S0, Z0, ckw, s);
     if (st) return st;
@@ -391,7 +392,7 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   if (p.nseg > 1) {
     ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
     st = launch("seg_rstate", la::k_seg_rstate<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg);
+                (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg, fm);
     if (st) return st;
     if (scanned) {
       st = launch("scan_rev", la::k_scan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, p.nseg);
@@ -402,12 +403,12 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   const int nsegb = (p.nseg + kb - 1) / kb;
   return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::BwdShape<T, D, M>::NTH), s,
                 (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, dSN, dZN, (T*)dQ, (T*)dK,
-                (T*)dV, dS0, dZ0, N, p.L * kb, nsegb, kb, p.nseg, scanned);
+                (T*)dV, dS0, dZ0, N, p.L * kb, nsegb, kb, p.nseg, scanned, fm);
 }
 
 template <typename T, int D, int M>
 int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO, void* dQ,
-                       void* dK, void* dV, int N, void* ws, hipStream_t s) {
+                       void* dK, void* dV, int N, void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0) return LA_OK;
   const WsLayout wl = ws_layout(LA_OP_BWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
@@ -415,7 +416,7 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
   float* rpref = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
   const bool scan = use_scan(p);  // the totals once per head (else every workgroup sums the aggregates)
-  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, s);
+  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
   if (st) return st;
   if (scan) {
     st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s, 1);
@@ -423,21 +424,21 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   }
   const dim3 grid((unsigned)(p.BH * p.nseg));
   st = launch("nc_qr", la::k_nc_qr<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, (const float*)agg,
-              (const float*)(scan ? pref : nullptr), (T*)dQ, ragg, N, p.L, p.nseg);
+              (const float*)(scan ? pref : nullptr), (T*)dQ, ragg, N, p.L, p.nseg, fm);
   if (st) return st;
   if (scan) {
     st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s, 1);
     if (st) return st;
   }
   return launch("nc_kv", la::k_nc_kv<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, (const float*)ragg,
-                (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg);
+                (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg, fm);
 }
 
 // ----------------------------------------------------- decayed recurrence
 template <typename T, int D, int M>
 int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, void* O,
                    float* den, const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int N,
-                   void* ws, hipStream_t s) {
+                   void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
@@ -447,7 +448,7 @@ int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
     float* agg = reinterpret_cast<float*>(region(ws, 0));
     float* dlam = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
     int st = launch("dseg_state", la::k_dseg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                    (const T*)K, (const T*)V, logA, agg, dlam, N, p.L, p.nseg);
+                    (const T*)K, (const T*)V, logA, agg, dlam, N, p.L, p.nseg, fm);
     if (st) return st;
     float* pr = ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
     st = launch("dscan_states", la::k_dscan_states<D, M>, scan_grid(p), dim3(la::NT), s, (const float*)agg,
@@ -457,13 +458,13 @@ int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
   }
   return launch("dfwd", la::k_dfwd<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s, (const T*)Q,
                 (const T*)K, (const T*)V, logA, (T*)O, den, pref, S0, Z0, pref ? (float*)nullptr : ckpt, S_out, Z_out,
-                N, p.L, p.nseg);
+                N, p.L, p.nseg, fm);
 }
 
 template <typename T, int D, int M>
 int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, const void* dO,
                    const float* S0, const float* Z0, const float* ckpt, const float* dSN, const float* dZN, void* dQ,
-                   void* dK, void* dV, float* dlogA, float* dS0, float* dZ0, int N, void* ws, hipStream_t s) {
+                   void* dK, void* dV, float* dlogA, float* dS0, float* dZ0, int N, void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0)
     return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
                         (float*)nullptr, dS0, dZ0)
@@ -480,7 +481,7 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
   const float* ck = ckpt;
   if (!ck) {  // recompute the checkpoint
     st = launch("dseg_state", la::k_dseg_state<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, logA, agg,
-                dlam, N, p.L, p.nseg);
+                dlam, N, p.L, p.nseg, fm);
     if (st) return st;
     st = launch("dscan_states", la::k_dscan_states<D, M>, scan_grid(p), dim3(la::NT), s, (const float*)agg,
                 (const float*)dlam, S0, Z0, ckw, p.nseg);
@@ -488,14 +489,14 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
     ck = ckw;
   }
   st = launch("dbq", la::k_dbq<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V, (const T*)dO,
-              logA, ck, (T*)dQ, gc, ragg, dlam, N, p.L, p.nseg);
+              logA, ck, (T*)dQ, gc, ragg, dlam, N, p.L, p.nseg, fm);
   if (st) return st;
   st = launch("dscan_rev", la::k_dscan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, (const float*)dlam, dSN, dZN,
               dS0, dZ0, p.nseg);
   if (st) return st;
   st = launch("dbkv", la::k_dbkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
               (const T*)dO, logA, (const float2*)gc, (const float*)ragg, ck, dSN, dZN, (T*)dK, (T*)dV, dlogA, xseg, N,
-              p.L, p.nseg);
+              p.L, p.nseg, fm);
   if (st) return st;
   if (p.nseg == 1) return LA_OK;
   return launch("dla_fix", la::k_dla_fix, grid, dim3(la::NT), s, dlogA, (const float*)xseg, N, p.L, p.nseg);
@@ -503,12 +504,85 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
 
 template <typename T, int D, int M>
 int decode_impl(long BH, const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
-                hipStream_t s) {
+                int fm, hipStream_t s) {
   return launch("decode", la::k_decode<T, D, M>, dim3((unsigned)((BH + 3) / 4)), dim3(la::NT), s, (const T*)q,
-                (const T*)k, (const T*)v, logA, S, Z, (T*)y, (int)BH);
+                (const T*)k, (const T*)v, logA, S, Z, (T*)y, (int)BH, fm);
 }
 
 size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+// ----------------------------------------------------------- feature maps
+#define LA_FEAT_DISPATCH(dtype, DIN, C, FN, ...)                                                    \
+  do {                                                                                             \
+    if ((dtype) == LA_F32) {                                                                       \
+      if ((DIN) == 32 && (C) == 32) return FN<float, 32, 32>(__VA_ARGS__);                         \
+      if ((DIN) == 32 && (C) == 64) return FN<float, 32, 64>(__VA_ARGS__);                         \
+      if ((DIN) == 64 && (C) == 32) return FN<float, 64, 32>(__VA_ARGS__);                         \
+      return FN<float, 64, 64>(__VA_ARGS__);                                                       \
+    } else {                                                                                       \
+      if ((DIN) == 32 && (C) == 32) return FN<la::bf16_t, 32, 32>(__VA_ARGS__);                    \
+      if ((DIN) == 32 && (C) == 64) return FN<la::bf16_t, 32, 64>(__VA_ARGS__);                    \
+      if ((DIN) == 64 && (C) == 32) return FN<la::bf16_t, 64, 32>(__VA_ARGS__);                    \
+      return FN<la::bf16_t, 64, 64>(__VA_ARGS__);                                                  \
+    }                                                                                              \
+  } while (0)
+
+template <typename T, int DIN, int C>
+int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const void* dPhi, void* out, hipStream_t s) {
+  const dim3 grid((unsigned)(BH * ((N + la::CH - 1) / la::CH)));
+  if (dPhi)
+    return launch("feat_rf_vjp", la::k_feat_rf_vjp<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W,
+                  (const T*)dPhi, (T*)out, N, H);
+  return launch("feat_rf", la::k_feat_rf<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H);
+}
+
+template <typename T, int C>
+int feat_poly2_impl(long rows, int din, const void* X, const void* dPhi, void* out, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + la::NT - 1) / la::NT));
+  if (dPhi)
+    return launch("feat_poly2_vjp", la::k_feat_poly2_vjp<T, C>, grid, dim3(la::NT), s, (const T*)X,
+                  (const T*)dPhi, (T*)out, rows, din);
+  return launch("feat_poly2", la::k_feat_poly2<T, C>, grid, dim3(la::NT), s, (const T*)X, (T*)out, rows, din);
+}
+
+int feature_random(const void* X, const float* W, const void* dPhi, void* out, int B, int H, int N, int Din, int C,
+                   int dtype, void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, 32, 32, dtype);
+  if (st) return st;
+  if (!dims_ok(Din, C)) return fail(LA_ERR_UNSUPPORTED, "Din and C must each be 32 or 64");
+  if (N == 0) return LA_OK;
+  if (!X || !W || !out) return fail(LA_ERR_NULL, "X, W and the output are required");
+  const size_t es = esize(dtype), bh = (size_t)B * H;
+  st = check_ptrs({rng("X", X, bh * N * Din * es, false), rng("W", W, (size_t)H * C * Din * 4, false),
+                   rng("dPhi", dPhi, bh * N * C * es, false),
+                   rng(dPhi ? "dX" : "Phi", out, bh * N * (dPhi ? Din : C) * es, true)});
+  if (st) return st;
+  LA_FEAT_DISPATCH(dtype, Din, C, feat_rf_impl, (long)bh, H, N, X, W, dPhi, out, (hipStream_t)stream);
+}
+
+int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int N, int Din, int C, int dtype,
+                  void* stream) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, 32, 32, dtype);
+  if (st) return st;
+  if (C != 32 && C != 64) return fail(LA_ERR_UNSUPPORTED, "C must be 32 or 64");
+  if (Din < 1 || Din > 7 || 1 + Din + Din * Din > C)
+    return fail(LA_ERR_UNSUPPORTED, "degree-2 features need 1 + Din + Din^2 <= C (Din <= 5 for C = 32, 7 for 64)");
+  if (N == 0) return LA_OK;
+  if (!X || !out) return fail(LA_ERR_NULL, "X and the output are required");
+  const size_t es = esize(dtype), bh = (size_t)B * H;
+  st = check_ptrs({rng("X", X, bh * N * Din * es, false), rng("dPhi", dPhi, bh * N * C * es, false),
+                   rng(dPhi ? "dX" : "Phi", out, bh * N * (dPhi ? Din : C) * es, true)});
+  if (st) return st;
+  const long rows = (long)bh * N;
+  if (dtype == LA_F32) {
+    if (C == 32) return feat_poly2_impl<float, 32>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+    return feat_poly2_impl<float, 64>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+  }
+  if (C == 32) return feat_poly2_impl<la::bf16_t, 32>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+  return feat_poly2_impl<la::bf16_t, 64>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+}
 
 }  // namespace
 
@@ -537,7 +611,8 @@ const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
-         "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix";
+         "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
+         "feat_poly2_vjp";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
@@ -564,8 +639,11 @@ int la_set_segment_chunks(int chunks) {
 
 int la_forward_causal(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
                       const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H, int N,
-                      int D, int M, int dtype, void* ws, size_t ws_bytes, void* stream) {
+                      int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
+  const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
@@ -589,14 +667,17 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
   if (N == 0 && !S_out && !ckpt) return LA_OK;
   if (logA)
     LA_DISPATCH(dtype, D, M, fwd_decay_impl, p, Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
-                (hipStream_t)stream);
+                fm, (hipStream_t)stream);
   LA_DISPATCH(dtype, D, M, fwd_causal_impl, p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
-              (hipStream_t)stream);
+              fm, (hipStream_t)stream);
 }
 
 int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int D, int M,
-                         int dtype, void* ws, size_t ws_bytes, void* stream) {
+                         int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
+  if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
+  const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
   if (N == 0) return LA_OK;
@@ -610,15 +691,18 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, i
                    rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, true),
                    rng("ws", ws, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, N, ws, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, N, ws, fm, (hipStream_t)stream);
 }
 
 int la_backward_causal(const void* Q, const void* K, const void* V, const float* logA, const void* O,
                        const float* den, const void* dO, const float* S0, const float* Z0, const float* ckpt,
                        const float* dS_N, const float* dZ_N, void* dQ, void* dK, void* dV, float* dlogA, float* dS0,
-                       float* dZ0, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
+                       float* dZ0, int B, int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
                        void* stream) {
   g_err.clear();
+  if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
+  const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
   if ((logA == nullptr) != (dlogA == nullptr)) return fail(LA_ERR_ARG, "logA and dlogA must be given together");
@@ -633,7 +717,7 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
     if (st) return st;
     const Plan p = make_plan(B, H, N, D, M);
     LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
-                dZ0, N, ws, (hipStream_t)stream);
+                dZ0, N, ws, fm, (hipStream_t)stream);
   }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
@@ -656,15 +740,18 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
   if (st) return st;
   if (logA)
     LA_DISPATCH(dtype, D, M, bwd_decay_impl, p, Q, K, V, logA, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dlogA, dS0,
-                dZ0, N, ws, (hipStream_t)stream);
+                dZ0, N, ws, fm, (hipStream_t)stream);
   LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0,
-              N, ws, (hipStream_t)stream);
+              N, ws, fm, (hipStream_t)stream);
 }
 
 int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, void* dQ, void* dK,
-                          void* dV, int B, int H, int N, int D, int M, int dtype, void* ws, size_t ws_bytes,
+                          void* dV, int B, int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
                           void* stream) {
   g_err.clear();
+  if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
+  const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
   if (N == 0) return LA_OK;
@@ -679,12 +766,15 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
                    rng("dV", dV, bh * N * M * es, true), rng("ws", ws, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, dQ, dK, dV, N, ws, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, dQ, dK, dV, N, ws, fm, (hipStream_t)stream);
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
-                   int B, int H, int D, int M, int dtype, void* stream) {
+                   int B, int H, int D, int M, int dtype, int feature, void* stream) {
   g_err.clear();
+  if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
+  const int fm = feature;
   int st = check_sizes(B, H, 1, D, M, dtype);
   if (st) return st;
   if (!q || !k || !v || !S || !Z || !y) return fail(LA_ERR_NULL, "q, k, v, S, Z and y are required");
@@ -693,7 +783,34 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
                    rng("logA", logA, bh * 4, false), rng("S", S, bh * D * M * 4, true),
                    rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, fm, (hipStream_t)stream);
+}
+
+int la_feature_random(const void* X, const float* W, void* Phi, int B, int H, int N, int Din, int C, int dtype,
+                      void* stream) {
+  return feature_random(X, W, nullptr, Phi, B, H, N, Din, C, dtype, stream);
+}
+
+int la_feature_random_vjp(const void* X, const float* W, const void* dPhi, void* dX, int B, int H, int N, int Din,
+                          int C, int dtype, void* stream) {
+  if (!dPhi) {
+    g_err.clear();
+    return fail(LA_ERR_NULL, "dPhi is required");
+  }
+  return feature_random(X, W, dPhi, dX, B, H, N, Din, C, dtype, stream);
+}
+
+int la_feature_poly2(const void* X, void* Phi, int B, int H, int N, int Din, int C, int dtype, void* stream) {
+  return feature_poly2(X, nullptr, Phi, B, H, N, Din, C, dtype, stream);
+}
+
+int la_feature_poly2_vjp(const void* X, const void* dPhi, void* dX, int B, int H, int N, int Din, int C, int dtype,
+                         void* stream) {
+  if (!dPhi) {
+    g_err.clear();
+    return fail(LA_ERR_NULL, "dPhi is required");
+  }
+  return feature_poly2(X, dPhi, dX, B, H, N, Din, C, dtype, stream);
 }
 
 int la_prof_select(const char* kernel_name) {

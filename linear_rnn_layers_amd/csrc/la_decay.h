@@ -92,7 +92,7 @@ __device__ __forceinline__ float load_ell(const float* la, int c0, int nv) {
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_dseg_state(const T* __restrict__ K, const T* __restrict__ V,
                                                     const float* __restrict__ logA, float* __restrict__ agg,
-                                                    float* __restrict__ dlam, int N, int L, int nseg) {
+                                                    float* __restrict__ dlam, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   __shared__ Planes<P::FKF, CH, D> kt;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NT) void k_dseg_state(const T* __restrict__ K, cons
     const float lam = wave_incl_sum(ell[b]);
     const float last = __shfl(lam, 63, 64);
     __syncthreads();
-    bk[b].stage_phi(kt, nv);
+    bk[b].stage_phi(kt, nv, nullptr, fm);
     bv[b].stage_values(vt);
     if (w == 0) sF[l] = exp_nat(last - lam);
     fetch(b, c0 + 2 * CH);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
                                               const float* __restrict__ pref, const float* __restrict__ S0,
                                               const float* __restrict__ Z0, float* __restrict__ ckpt,
                                               float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
-                                              int nseg) {
+                                              int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   __shared__ Planes<P::FQ, CH, D> qt;
@@ -288,8 +288,8 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
     const float lam = wave_incl_sum(ell[b]);
     const float last = __shfl(lam, 63, 64);
     __syncthreads();
-    bq[b].stage_phi(qt, nv);
-    bk[b].stage_phi(kt, nv);
+    bq[b].stage_phi(qt, nv, nullptr, fm);
+    bk[b].stage_phi(kt, nv, nullptr, fm);
     bv[b].stage_values(vt);
     if (w == 0) {
       slam[l] = lam;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
                                              const float* __restrict__ logA, const float* __restrict__ ckpt,
                                              T* __restrict__ dQ, float2* __restrict__ gc, float* __restrict__ ragg,
                                              float* __restrict__ dlam, int N, int L,
-                                             int nseg) {
+                                             int nseg, int fm) {
   using P = DPrec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   __shared__ Planes<P::Q, CH, D> qt;
@@ -469,8 +469,8 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
     const float lam = wave_incl_sum(ell[b]);
     const float last = __shfl(lam, 63, 64);
     __syncthreads();
-    bq[b].stage_phi(qt, nv);
-    bk[b].stage_phi(kt, nv);
+    bq[b].stage_phi(qt, nv, nullptr, fm);
+    bk[b].stage_phi(kt, nv, nullptr, fm);
     bv[b].stage_values(vt);
     bd[b].stage_values(ot);
     if (w == 0) {
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float dpq = (acc[r] + e_i * (U[d0][r] - odo * zv[d0][r])) * inv;
-        o[r] = dpq * dphi_from_phi(qv[d0][r]);
+        o[r] = dpq * dfeat(qv[d0][r], fm);
       }
       if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
     }
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
                                               const float* __restrict__ rin, const float* __restrict__ ckpt,
                                               const float* __restrict__ dSN, const float* __restrict__ dZN,
                                               T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dla,
-                                              float* __restrict__ xseg, int N, int L, int nseg) {
+                                              float* __restrict__ xseg, int N, int L, int nseg, int fm) {
   using P = DPrec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   __shared__ Planes<P::Q, CH, D> qt;
@@ -776,8 +776,8 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
     __syncthreads();
     flush_x();
     stage_R();
-    bq[b].stage_phi(qt, nv);
-    bk[b].stage_phi(kt, nv);
+    bq[b].stage_phi(qt, nv, nullptr, fm);
+    bk[b].stage_phi(kt, nv, nullptr, fm);
     bv[b].stage_values(vt);
     // dO, and [g | c] weighted by exp(lam_i), from the same registers
     {
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
       for (int r = 0; r < 4; ++r) {
         const float dpk = acc[r] + f_j * (st[r] + rr[r]);
         xk += kv[r] * dpk;
-        o[r] = dpk * dphi_from_phi(kv[r]);
+        o[r] = dpk * dfeat(kv[r], fm);
       }
       if (row_ok) IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
     }

@@ -70,6 +70,13 @@ __device__ __forceinline__ float phi(float x) {
 // Its derivative is 1 for x > 0 and exp(x) otherwise, i.e. min(phi(x), 1).
 __device__ __forceinline__ float dphi_from_phi(float p) { return fminf(p, 1.f); }
 
+// Feature-map selection: every kernel takes a flag `fm`; fm = 0 applies eq. 7,
+// fm = 1 takes Q and K as feature vectors already (another feature map applied
+// by the caller, e.g. polynomial or positive random features): the identity,
+// with derivative 1.
+__device__ __forceinline__ float feat(float x, int fm) { return fm ? x : phi(x); }
+__device__ __forceinline__ float dfeat(float p, int fm) { return fm ? 1.f : dphi_from_phi(p); }
+
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, f32x4_t c) {
@@ -352,7 +359,8 @@ struct RowBuf {
   // Stage phi of the values (rows past `nvalid` are zero), optionally also
   // as float32 into a [CH][F32C] array.
   template <int NP, int ROWS, int PC, int PAD, int F32C = 0>
-  __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid, float* f32 = nullptr) const {
+  __device__ __forceinline__ void stage_phi(Planes<NP, ROWS, PC, PAD>& dst, int nvalid, float* f32 = nullptr,
+                                            int fm = 0) const {
     if (!owns()) return;
     const bool full = nvalid >= CH;
 #pragma unroll
@@ -362,11 +370,11 @@ struct RowBuf {
       IO<T>::unpack(r[i], x);
       if (full) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = phi(x[e]);
+        for (int e = 0; e < E; ++e) x[e] = feat(x[e], fm);
       } else {
         const bool ok = row < nvalid;
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = ok ? phi(x[e]) : 0.f;
+        for (int e = 0; e < E; ++e) x[e] = ok ? feat(x[e], fm) : 0.f;
       }
       dst.template put<E>(row, c0, x);
       if constexpr (F32C > 0) {

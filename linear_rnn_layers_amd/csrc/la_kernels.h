@@ -22,6 +22,8 @@
 // the 16 tokens 16w..16w+15 of a 64-token chunk.  Sums over tokens of a single
 // vector (the normaliser Z, the reverse normaliser r) are MFMA products with
 // an all-ones operand, the form of eq. 14-15 on [V, 1].
+#pragma once
+
 #include <type_traits>
 
 #include "la_device.h"
@@ -164,7 +166,7 @@ __device__ __forceinline__ void acc_to4(const f32x4_t& a, float* o) {
 // over the segment's tokens (eq. 10-11 restricted to one segment).
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const T* __restrict__ V,
-                                                   float* __restrict__ agg, int N, int L, int nseg) {
+                                                   float* __restrict__ agg, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   __shared__ Planes<P::FKF, CH, D> kt;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
   auto chunk = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    k_.stage_phi(kt, nv);
+    k_.stage_phi(kt, nv, nullptr, fm);
     v_.stage_values(vt);
     fetch(k_, v_, c0 + 2 * CH);
     __syncthreads();
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
                                              const float* __restrict__ S0, const float* __restrict__ Z0,
                                              float* __restrict__ ckpt,
                                              float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
-                                             int nseg) {
+                                             int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   constexpr int KR = CAUSAL ? CH : 1, KD = CAUSAL ? D : 8, KM = CAUSAL ? M : 8;
@@ -337,9 +339,9 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    q_.stage_phi(qt, nv);
+    q_.stage_phi(qt, nv, nullptr, fm);
     if constexpr (CAUSAL) {
-      k_.stage_phi(kt, nv);
+      k_.stage_phi(kt, nv, nullptr, fm);
       v_.stage_values(vt);
     }
     fetch(q_, k_, v_, c0 + 2 * CH);
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(NT) void k_state_copy(const float* __restrict__ S0,
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, const T* __restrict__ O,
                                                     const float* __restrict__ den, const T* __restrict__ dO,
-                                                    float* __restrict__ ragg, int N, int L, int nseg) {
+                                                    float* __restrict__ ragg, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   constexpr int E = IO<T>::E, PRM = M / E;
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
   auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& o_, RowBuf<T, CH, M>& d_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    q_.stage_phi(qt, nv);
+    q_.stage_phi(qt, nv, nullptr, fm);
     // g and c need den (per row) and dO . O (a row reduction over PRM lanes)
 #pragma unroll
     for (int i = 0; i < RowBuf<T, CH, M>::CNT; ++i) {
@@ -664,7 +666,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ ckpt, const float* __restrict__ ragg, const float* __restrict__ dSN,
     const float* __restrict__ dZN, T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV,
-    float* __restrict__ dS0, float* __restrict__ dZ0, int N, int L, int nsegb, int kb, int nseg, int scanned) {
+    float* __restrict__ dS0, float* __restrict__ dZ0, int N, int L, int nsegb, int kb, int nseg, int scanned, int fm) {
   using P = Prec<T>;
   using BS = BwdShape<T, D, M>;
   constexpr int CB = BS::CB, RB = BS::RB, NW = BS::NW, NTH = BS::NTH, NPAIR = CB / 32;
@@ -810,8 +812,8 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     const int nv = min(CB, t1 - c0);
     // ---- stage this chunk from registers, then start reading the previous one
     // (the barrier ending the previous chunk separates its reads from these writes)
-    bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0]);
-    bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0]);
+    bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
+    bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0], fm);
     bv.stage_values(vt);
     bd.stage_values(ot);
     if (ci > 0) {
@@ -914,7 +916,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
         for (int d0 = 0; d0 < DB; ++d0) {
           float o[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dphi_from_phi(qv[d0][r]);
+          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
           IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
         }
       }
@@ -1033,7 +1035,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
           const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
           const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dphi_from_phi(kv[r]);
+          for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dfeat(kv[r], fm);
           IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
         }
       }
@@ -1145,7 +1147,7 @@ __device__ __forceinline__ void stage_total(Planes<NP, D, M>& sp, float* sz, flo
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* __restrict__ dO,
                                                const float* __restrict__ agg, const float* __restrict__ pref,
-                                               T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg) {
+                                               T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   constexpr int E = IO<T>::E;
@@ -1186,7 +1188,7 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& d_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    q_.template stage_phi<cmax(P::NQ, P::dR), CH, D, 8, D + 4>(qt, nv, &q32[0][0]);
+    q_.template stage_phi<cmax(P::NQ, P::dR), CH, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
     d_.stage_values(ot);
     fetch(q_, d_, c0 + 2 * CH);
     __syncthreads();
@@ -1227,7 +1229,7 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
         for (int d0 = 0; d0 < DB; ++d0) {
           float o[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - zv[d0][r] * odo) * invz * dphi_from_phi(qv[d0][r]);
+          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - zv[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
           IO<T>::store4(dQ + (size_t)bh * N * D + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
         }
       }
@@ -1268,7 +1270,7 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* __restrict__ V,
                                                const float* __restrict__ ragg, const float* __restrict__ rpref,
-                                               T* __restrict__ dK, T* __restrict__ dV, int N, int L, int nseg) {
+                                               T* __restrict__ dK, T* __restrict__ dV, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NKT = P::VR, NVT = cmax(P::KR_b, 1);
@@ -1300,7 +1302,7 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
   auto chunk = [&](RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    k_.template stage_phi<cmax(NKT, 1), CH, D, 8, D + 4>(kt, nv, &k32[0][0]);
+    k_.template stage_phi<cmax(NKT, 1), CH, D, 8, D + 4>(kt, nv, &k32[0][0], fm);
     v_.stage_values(vt);
     fetch(k_, v_, c0 + 2 * CH);
     __syncthreads();
@@ -1321,7 +1323,7 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
         const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dphi_from_phi(kv[r]);
+        for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dfeat(kv[r], fm);
         IO<T>::store4(dK + (size_t)bh * N * D + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
       }
     }
@@ -1359,7 +1361,7 @@ template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
                                                 const T* __restrict__ v, const float* __restrict__ logA,
                                                 float* __restrict__ S, float* __restrict__ Z, T* __restrict__ y,
-                                                int BH) {
+                                                int BH, int fm) {
   constexpr int NV = D * M / 4 / 64;  // float4 per lane
   constexpr int CPL = M / 4;          // lanes covering one state row
   constexpr int RPI = 64 / CPL;       // state rows per instruction
@@ -1377,8 +1379,8 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
   const float a = live && logA ? __builtin_amdgcn_exp2f(logA[head] * 1.4426950408889634f) : 1.f;
   if (live) {
     if (l < D) {
-      sq[w][l] = phi(ld(q + (size_t)head * D + l));
-      const float pk = phi(ld(k + (size_t)head * D + l));
+      sq[w][l] = feat(ld(q + (size_t)head * D + l), fm);
+      const float pk = feat(ld(k + (size_t)head * D + l), fm);
       sk[w][l] = pk;
       zn = a * Z[(size_t)head * D + l] + pk;
     }

@@ -65,6 +65,11 @@ class Workload:
     steps: int = 0  # decode steps (decode workload only)
     gate_seed: int = 0  # decayed workloads: seed of the per-token gates
     gate_bias: float = 3.0
+    features: int = 0  # random-feature workloads: number of features C (projection seed seeds[0] + 50)
+
+    def projection(self):
+        """Random projection W [H, C, D] ~ N(0, 1) float32 for the random-feature workloads."""
+        return gaussian((self.H, self.features, self.D), self.seeds[0] + 50, 1.0, F32)
 
     def qkv(self, layer: int = 0, n: int | None = None):
         """Q [B,H,N,D], K [B,H,N,D], V [B,H,N,M] for one layer (float32 arrays)."""
@@ -124,7 +129,11 @@ SPEECH = Workload("speech-encoder-9layers-b16h6n800d32-f32", 16, 6, 800, 32, 32,
 # 1 / (1 + exp(-x)), x ~ N(3, 1), i.e. about 0.95 on average.
 LONG_DECAY = Workload("long-decay-b1h16n65536d64-bf16", 1, 16, 65536, 64, 64, BF16, 1.0 / 8.0, (421, 422, 423, 424),
                       gate_seed=425)
+# The MNIST-shaped layer with positive random features of size 64 in place of elu + 1; queries and keys scaled
+# by 32^(-1/4) (the temperature of the softmax kernel exp(q.k / sqrt(d)) that the features estimate).
+MNIST_RF = Workload("mnist-random-features-b16h8n784d32c64-f32", 16, 8, 784, 32, 32, F32, 32 ** -0.25,
+                    (241, 242, 243, 244), features=64)
 DECODE = Workload("decode-b256h16d64-4096steps-bf16", 256, 16, 512, 64, 64, BF16, 1.0, (501, 502, 503, 504),
                   steps=4096)
 
-WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, LONG_DECAY, DECODE)}
+WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, LONG_DECAY, MNIST_RF, DECODE)}

@@ -19,7 +19,7 @@ OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE, UNSUPPORTED, HIP, ARG = range(1
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -139,6 +139,22 @@ def test_feature_argument_validation(lib):
     assert b"feature" in lib.la_last_error()
     assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 64, 64, 1, 5,
                               None) == ARG
+
+
+def test_feature_map_validation(lib):
+    # random features: Din, C in {32, 64}; W [H,C,Din] float32; outputs must not overlap inputs
+    assert lib.la_feature_random(addr(1), addr(2), addr(3), 2, 2, 100, 48, 32, 0, None) == UNSUPPORTED
+    assert lib.la_feature_random(addr(1), None, addr(3), 2, 2, 100, 32, 32, 0, None) == NULL
+    assert lib.la_feature_random(addr(1), addr(2), addr(1), 2, 2, 100, 32, 32, 0, None) == ALIAS
+    assert lib.la_feature_random_vjp(addr(1), addr(2), None, addr(4), 2, 2, 100, 32, 32, 0, None) == NULL
+    assert lib.la_feature_random(None, None, None, 2, 2, 0, 32, 32, 0, None) == OK
+    # degree-2 polynomial: 1 + Din + Din^2 <= C
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 6, 32, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 8, 64, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 5, 48, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(1), 2, 2, 100, 5, 32, 0, None) == ALIAS
+    assert lib.la_feature_poly2_vjp(addr(1), None, addr(4), 2, 2, 100, 5, 32, 0, None) == NULL
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 5, 32, 3, None) == DTYPE
 
 
 def test_decay_forward_validation(lib):

@@ -1,0 +1,178 @@
+"""GPU parity of the other feature maps (degree-2 polynomial, positive random features) and of the attention in
+feature mode (Q, K taken as feature vectors) against the float64 oracle.
+
+Gate: rowerr <= 1e-4 (float32 storage) / 2e-2 (bf16), each step checked at its own inputs (the attention on
+the features the library produced, the chain rule through the map on the feature gradients it produced), and the
+float32 composition end to end through autograd.  The feature gradients dPhi_Q are floored at 1e-2 of the
+numerator term |S_i g_i| (the cancellation of the quotient rule, as for dQ of the plain method); the raw
+query gradient of the composition at 1e-2 of that term carried through the same map.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_rnn_layers_amd import binding, inputs
+from tests import pins
+from tests.gpu_util import TOL, dev, dev32, host, rowerr
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = inputs.F32, inputs.BF16
+IDENT = binding.LA_FEATURE_IDENTITY
+CANCEL_FLOOR = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    binding.load()
+    binding.set_segment_chunks(0)
+    yield
+
+
+def _x(shape, seed, sigma, dtype):
+    return inputs.gaussian(shape, seed, sigma, dtype)
+
+
+def _w(H, C, Din, seed):
+    return inputs.gaussian((H, C, Din), seed, 1.0, F32)
+
+
+def feat_cancel_scale(fq, fk, v, do, causal=True):
+    """Per-row |S_i g_i|, the numerator term of dPhi_Q (g = dO / den), from the oracle on the features."""
+    fq, fk, v, do = (np.asarray(a, np.float64) for a in (fq, fk, v, do))
+    if causal:
+        _, den, _, _ = oracle.forward_causal(fq, fk, v, feature=IDENT)
+    else:
+        den = np.einsum("bhnd,bhd->bhn", fq, fk.sum(2))
+    g = do / den[..., None]
+    u = np.empty(fq.shape)
+    for b in range(fq.shape[0]):
+        for h in range(fq.shape[1]):
+            if causal:
+                u[b, h] = oracle.numerator_backward(fq[b, h], fk[b, h], v[b, h], g[b, h])[0]
+            else:
+                u[b, h] = g[b, h] @ (fk[b, h].T @ v[b, h]).T
+    return u
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Din,C", [(32, 32), (32, 64), (64, 32), (64, 64)])
+def test_random_features(Din, C, dtype):
+    B, H, N = 2, 3, 150
+    x = _x((B, H, N, Din), 14000 + Din + C, 0.3, dtype)
+    w = _w(H, C, Din, 14010)
+    dphi = _x((B, H, N, C), 14020, 1.0, dtype)
+    phi = binding.feature_random(dev(x, dtype), dev32(w))
+    dx = binding.feature_random_vjp(dev(x, dtype), dev32(w), dev(dphi, dtype))
+    torch.cuda.synchronize()
+    assert rowerr(host(phi), oracle.feature_performer(x, w)) <= TOL[dtype]
+    assert rowerr(host(dx), oracle.feature_performer_vjp(x, w, dphi)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Din,C", [(3, 32), (5, 32), (7, 64), (4, 64)])
+def test_poly2_features(Din, C, dtype):
+    B, H, N = 2, 3, 150
+    x = _x((B, H, N, Din), 14100 + Din + C, 1.0, dtype)
+    dphi = _x((B, H, N, C), 14120, 1.0, dtype)
+    phi = binding.feature_poly2(dev(x, dtype), C)
+    dx = binding.feature_poly2_vjp(dev(x, dtype), dev(dphi, dtype))
+    torch.cuda.synchronize()
+    assert rowerr(host(phi), oracle.feature_poly2(x, C)) <= TOL[dtype]
+    assert rowerr(host(dx), oracle.feature_poly2_vjp(x, dphi)) <= TOL[dtype]
+
+
+def _attend(fq, fk, v, do, dtype, causal):
+    """GPU attention in feature mode on device features: (O, dPhiQ, dPhiK, dV) as device tensors."""
+    if causal:
+        out = binding.forward_causal(fq, fk, v, feature=IDENT)
+        g = binding.backward_causal(fq, fk, v, out["o"], out["den"], do, ckpt=out["ckpt"], feature=IDENT)
+        return (out["o"],) + tuple(g)
+    o = binding.forward_noncausal(fq, fk, v, feature=IDENT)
+    return (o,) + tuple(binding.backward_noncausal(fq, fk, v, do, feature=IDENT))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("which", ["random", "poly2"])
+def test_feature_mode_attention(which, causal, dtype):
+    """Features on the GPU, attention in feature mode, gradients through the features: against the oracle's
+    float64 composition of the same steps."""
+    B, H, N, M = 2, 2, 200, 32
+    if which == "random":
+        Din, C, sig = 32, 64, 0.3
+        w = _w(H, C, Din, 14210)
+        fmap = lambda a: oracle.feature_performer(a, w)  # noqa: E731
+        fvjp = lambda a, g: oracle.feature_performer_vjp(a, w, g)  # noqa: E731
+        gmap = lambda a: binding.feature_random(a, dev32(w))  # noqa: E731
+        gvjp = lambda a, g: binding.feature_random_vjp(a, dev32(w), g)  # noqa: E731
+    else:
+        Din, C, sig = 5, 32, 0.6
+        fmap = lambda a: oracle.feature_poly2(a, C)  # noqa: E731
+        fvjp = oracle.feature_poly2_vjp
+        gmap = lambda a: binding.feature_poly2(a, C)  # noqa: E731
+        gvjp = binding.feature_poly2_vjp
+    q, k = _x((B, H, N, Din), 14200, sig, dtype), _x((B, H, N, Din), 14201, sig, dtype)
+    v, do = _x((B, H, N, M), 14202, 1.0, dtype), _x((B, H, N, M), 14203, 1.0, dtype)
+    Q, K, V, dO = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype)
+    fQ, fK = gmap(Q), gmap(K)
+    o, dfq, dfk, dv = _attend(fQ, fK, V, dO, dtype, causal)
+    dq, dk = gvjp(Q, dfq), gvjp(K, dfk)
+    torch.cuda.synchronize()
+    # each step against the oracle at that step's own inputs: the features from the stored inputs, the attention
+    # on the features the library produced, the feature gradients' chain rule on the gradients it produced
+    fq, fk = host(fQ), host(fK)
+    assert max(rowerr(fq, fmap(q)), rowerr(fk, fmap(k))) <= TOL[dtype]
+    if causal:
+        ro = oracle.forward_causal(fq, fk, v, feature=IDENT)[0]
+        rfq, rfk, rv = oracle.backward_causal(fq, fk, v, do, feature=IDENT)
+    else:
+        ro = oracle.forward_noncausal(fq, fk, v, feature=IDENT)
+        rfq, rfk, rv = oracle.backward_noncausal(fq, fk, v, do, feature=IDENT)
+    u = feat_cancel_scale(fq, fk, v, do, causal)
+    errs = {"O": rowerr(host(o), ro), "dV": rowerr(host(dv), rv),
+            "dPhiQ": rowerr(host(dfq), rfq, row_floor=CANCEL_FLOOR * np.abs(u).max(-1)),
+            "dPhiK": rowerr(host(dfk), rfk),
+            "dQ": rowerr(host(dq), fvjp(q, host(dfq))), "dK": rowerr(host(dk), fvjp(k, host(dfk)))}
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+def test_feature_mode_with_elu_features_matches_the_method():
+    """elu + 1 applied by torch, then feature mode, equals the library's own elu + 1 path."""
+    B, H, N, D, M = 2, 2, 300, 64, 32
+    q, k, v = (inputs.gaussian((B, H, N, d), 14300 + i, 1.0, F32) for i, d in enumerate((D, D, M)))
+    do = inputs.gaussian((B, H, N, M), 14303)
+    Q, K, V, dO = dev(q), dev(k), dev(v), dev(do)
+    fQ, fK = torch.nn.functional.elu(Q) + 1.0, torch.nn.functional.elu(K) + 1.0
+    a = binding.forward_causal(Q, K, V)
+    b = binding.forward_causal(fQ, fK, V, feature=IDENT)
+    ga = binding.backward_causal(Q, K, V, a["o"], a["den"], dO, ckpt=a["ckpt"])
+    gb = binding.backward_causal(fQ, fK, V, b["o"], b["den"], dO, ckpt=b["ckpt"], feature=IDENT)
+    torch.cuda.synchronize()
+    dphi = lambda x: torch.where(x > 0, torch.ones_like(x), torch.exp(x))  # noqa: E731
+    assert rowerr(host(b["o"]), host(a["o"])) <= 1e-5
+    assert rowerr(host(gb[1] * dphi(K)), host(ga[1])) <= 1e-5
+    assert rowerr(host(gb[2]), host(ga[2])) <= 1e-5
+
+
+def test_feature_autograd_composition():
+    """torch.autograd through random features and the causal attention in feature mode."""
+    B, H, N, Din, C, M = 2, 2, 180, 32, 32, 64
+    q, k = _x((B, H, N, Din), 14400, 0.3, F32), _x((B, H, N, Din), 14401, 0.3, F32)
+    v, do = _x((B, H, N, M), 14402, 1.0, F32), _x((B, H, N, M), 14403, 1.0, F32)
+    w = _w(H, C, Din, 14410)
+    Q, K, V = (dev(a).requires_grad_(True) for a in (q, k, v))
+    W = dev32(w)
+    o = binding.causal_linear_attention(binding.random_features(Q, W), binding.random_features(K, W), V,
+                                        feature=IDENT)
+    (o * dev(do)).sum().backward()
+    torch.cuda.synchronize()
+    fq, fk = oracle.feature_performer(q, w), oracle.feature_performer(k, w)
+    rfq, rfk, rv = oracle.backward_causal(fq, fk, v, do, feature=IDENT)
+    u = feat_cancel_scale(fq, fk, v, do)
+    rq, rk = oracle.feature_performer_vjp(q, w, rfq), oracle.feature_performer_vjp(k, w, rfk)
+    errs = [rowerr(host(Q.grad), rq, row_floor=CANCEL_FLOOR * np.abs(oracle.feature_performer_vjp(q, w, u)).max(-1)),
+            rowerr(host(K.grad), rk), rowerr(host(V.grad), rv)]
+    assert max(errs) <= 1e-4, errs
