@@ -116,6 +116,8 @@ class Step:
         self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
         if wl == "speech":
             self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+            self.s_tot = torch.empty((B, H, D, M), dtype=torch.float32, device="cuda")
+            self.z_tot = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
         if wl == "mnist-rf":
             C = w.features
             self.W = torch.from_numpy(w.projection()).to("cuda").contiguous()
@@ -182,10 +184,11 @@ class Step:
             for (q, k, v, do) in self.sets:
                 self._fwd_bwd(q, k, v, do)
             return
-        if wl == "speech":
+        if wl == "speech":  # the forward's totals go to the backward, as a training step passes them
             for (q, k, v, do) in self.sets:
-                b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n)
-                b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb)
+                b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n, S_out=self.s_tot, Z_out=self.z_tot)
+                b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb, S_tot=self.s_tot,
+                                        Z_tot=self.z_tot)
             return
         if wl == "mnist-rf":
             q, k, v, do = self.sets[self.i % len(self.sets)]

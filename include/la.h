@@ -139,16 +139,21 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
                       const float *logA, void *O, float *den, const float *S0,
                       const float *Z0, float *S_out, float *Z_out,
                       float *ckpt, int B, int H, int N, int D, int M,
-                      int dtype, int feature, void *ws, size_t ws_bytes, void *stream);
+                      int dtype, int feature, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /*
  * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
  * eq. 5-6): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) are formed once
  * per head and reused for every query, O_i = phi(Q_i)^T S / phi(Q_i)^T Z.
+ *   S_out, Z_out optional outputs [B,H,D,M], [B,H,D] float32 (both or
+ *               neither): the totals S, Z, which la_backward_noncausal can
+ *               take instead of forming them again (zero for N = 0).
  */
 int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
-                         int B, int H, int N, int D, int M, int dtype, int feature,
-                         void *ws, size_t ws_bytes, void *stream);
+                         float *S_out, float *Z_out, int B, int H, int N,
+                         int D, int M, int dtype, int feature, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /*
  * Causal backward: gradients of a scalar loss with respect to the raw Q, K,
@@ -205,14 +210,18 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
  * den_i and dO_i . O_i are recomputed from S, Z, so neither O nor den is an
  * input.  Linear time, O(D M) state per head.
  *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype`.
+ *   S_tot, Z_tot optional: the totals written by la_forward_noncausal for the
+ *               same Q, K, V (both or neither); NULL: formed here again.
  *   dQ, dK, dV  outputs in `dtype`.
  *   ws          la_workspace_size(LA_OP_BWD_NONCAUSAL, ...) bytes (never 0
  *               for N > 0).
  */
 int la_backward_noncausal(const void *Q, const void *K, const void *V,
-                          const void *dO, void *dQ, void *dK, void *dV, int B,
-                          int H, int N, int D, int M, int dtype, int feature, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const void *dO, const float *S_tot,
+                          const float *Z_tot, void *dQ, void *dK, void *dV,
+                          int B, int H, int N, int D, int M, int dtype,
+                          int feature, void *ws, size_t ws_bytes,
+                          void *stream);
 
 /*
  * One RNN step of the attention ("Transformers are RNNs -- part 2/3",

@@ -59,11 +59,11 @@ def load(path: str | None = None):
     lib.la_forward_causal.restype = i
     lib.la_forward_causal.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp]
     lib.la_forward_noncausal.restype = i
-    lib.la_forward_noncausal.argtypes = [vp] * 4 + [i] * 7 + [vp, sz, vp]
+    lib.la_forward_noncausal.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp]
     lib.la_backward_causal.restype = i
     lib.la_backward_causal.argtypes = [vp] * 18 + [i] * 7 + [vp, sz, vp]
     lib.la_backward_noncausal.restype = i
-    lib.la_backward_noncausal.argtypes = [vp] * 7 + [i] * 7 + [vp, sz, vp]
+    lib.la_backward_noncausal.argtypes = [vp] * 9 + [i] * 7 + [vp, sz, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
     for name, nptr in (("la_feature_random", 3), ("la_feature_random_vjp", 4), ("la_feature_poly2", 2),
@@ -160,11 +160,11 @@ def la_forward_causal(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=
     _check(st, "la_forward_causal")
 
 
-def la_forward_noncausal(Q, K, V, O, ws=None, stream=None, feature=0):
+def la_forward_noncausal(Q, K, V, O, ws=None, stream=None, feature=0, S_out=None, Z_out=None):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
-    st = load().la_forward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, N, D, M, dtype_code(Q.dtype), feature,
-                                     _ptr(ws), nb, _stream(stream))
+    st = load().la_forward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(S_out), _ptr(Z_out), B, H, N, D, M,
+                                     dtype_code(Q.dtype), feature, _ptr(ws), nb, _stream(stream))
     _check(st, "la_forward_noncausal")
 
 
@@ -179,11 +179,12 @@ def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=N
     _check(st, "la_backward_causal")
 
 
-def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None, feature=0):
+def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None, feature=0, S_tot=None, Z_tot=None):
     B, H, N, D, M = _sizes(Q, V)
     nb = ws.numel() if ws is not None else 0
-    st = load().la_backward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, D,
-                                      M, dtype_code(Q.dtype), feature, _ptr(ws), nb, _stream(stream))
+    st = load().la_backward_noncausal(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(S_tot), _ptr(Z_tot), _ptr(dQ),
+                                      _ptr(dK), _ptr(dV), B, H, N, D, M, dtype_code(Q.dtype), feature, _ptr(ws), nb,
+                                      _stream(stream))
     _check(st, "la_backward_noncausal")
 
 
@@ -218,12 +219,17 @@ def forward_causal(q, k, v, *, s0=None, z0=None, return_state=False, checkpoint=
     return out
 
 
-def forward_noncausal(q, k, v, feature=0):
+def forward_noncausal(q, k, v, feature=0, return_state=False):
+    """Non-causal forward.  Returns O, or (O, S, Z) with the totals when return_state."""
     B, H, N, D, M = _sizes(q, v)
     o = torch.empty((B, H, N, M), dtype=q.dtype, device=q.device)
+    s = z = None
+    if return_state:
+        s = torch.empty((B, H, D, M), dtype=torch.float32, device=q.device)
+        z = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     ws = alloc_workspace(LA_OP_FWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_forward_noncausal(q, k, v, o, ws, feature=feature)
-    return o
+    la_forward_noncausal(q, k, v, o, ws, feature=feature, S_out=s, Z_out=z)
+    return (o, s, z) if return_state else o
 
 
 def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=None, dz_n=None, state_grad=False,
@@ -249,13 +255,14 @@ def backward_causal(q, k, v, o, den, do, *, s0=None, z0=None, ckpt=None, ds_n=No
     return out + ((ds0, dz0) if state_grad else ())
 
 
-def backward_noncausal(q, k, v, do, feature=0):
+def backward_noncausal(q, k, v, do, feature=0, s=None, z=None):
+    """Non-causal backward; s, z: the forward's totals (None: formed again)."""
     B, H, N, D, M = _sizes(q, v)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     ws = alloc_workspace(LA_OP_BWD_NONCAUSAL, B, H, N, D, M, dtype_code(q.dtype), q.device)
-    la_backward_noncausal(q, k, v, do, dq, dk, dv, ws, feature=feature)
+    la_backward_noncausal(q, k, v, do, dq, dk, dv, ws, feature=feature, S_tot=s, Z_tot=z)
     return dq, dk, dv
 
 
@@ -316,14 +323,15 @@ class NonCausalLinearAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, feature):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        ctx.save_for_backward(q, k, v)
+        o, s, z = forward_noncausal(q, k, v, feature=feature, return_state=True)
+        ctx.save_for_backward(q, k, v, s, z)
         ctx.feature = feature
-        return forward_noncausal(q, k, v, feature=feature)
+        return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v = ctx.saved_tensors
-        return backward_noncausal(q, k, v, do.contiguous(), feature=ctx.feature) + (None,)
+        q, k, v, s, z = ctx.saved_tensors
+        return backward_noncausal(q, k, v, do.contiguous(), feature=ctx.feature, s=s, z=z) + (None,)
 
 
 def noncausal_linear_attention(q, k, v, feature=0):

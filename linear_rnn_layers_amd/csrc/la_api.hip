@@ -332,9 +332,13 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
 }
 
 template <typename T, int D, int M>
-int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, int N, void* ws,
+int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* S_out,
+                       float* Z_out, int N, void* ws,
                        int fm, hipStream_t s) {
-  if (p.nseg == 0) return LA_OK;
+  if (p.nseg == 0)  // empty sequence: zero totals
+    return S_out ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s,
+                          (const float*)nullptr, (const float*)nullptr, (float*)nullptr, S_out, Z_out)
+                 : LA_OK;
   const WsLayout wl = ws_layout(LA_OP_FWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
   int st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
@@ -348,7 +352,7 @@ int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   }
   return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, pref, (const float*)agg,
-                (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, (float*)nullptr, N,
+                (const float*)nullptr, (const float*)nullptr, (float*)nullptr, S_out, Z_out, N,
                 p.L, p.nseg, fm);
 }
 
@@ -407,8 +411,8 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
 }
 
 template <typename T, int D, int M>
-int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO, void* dQ,
-                       void* dK, void* dV, int N, void* ws, int fm, hipStream_t s) {
+int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO,
+                       const float* St, const float* Zt, void* dQ, void* dK, void* dV, int N, void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0) return LA_OK;
   const WsLayout wl = ws_layout(LA_OP_BWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
@@ -416,15 +420,19 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
   float* rpref = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
   const bool scan = use_scan(p);  // the totals once per head (else every workgroup sums the aggregates)
-  int st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
-  if (st) return st;
-  if (scan) {
-    st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s, 1);
+  int st = LA_OK;
+  if (!St) {  // key totals: the forward's when given, else recomputed
+    st = seg_aggregates<T, D, M>(p, K, V, agg, N, fm, s);
     if (st) return st;
+    if (scan) {
+      st = scan_prefix<D, M>(p, agg, nullptr, nullptr, pref, s, 1);
+      if (st) return st;
+    }
   }
   const dim3 grid((unsigned)(p.BH * p.nseg));
-  st = launch("nc_qr", la::k_nc_qr<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, (const float*)agg,
-              (const float*)(scan ? pref : nullptr), (T*)dQ, ragg, N, p.L, p.nseg, fm);
+  st = launch("nc_qr", la::k_nc_qr<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, St, Zt,
+              (const float*)(St ? nullptr : agg), (const float*)(scan && !St ? pref : nullptr), (T*)dQ, ragg, N, p.L,
+              p.nseg, fm);
   if (st) return st;
   if (scan) {
     st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s, 1);
@@ -672,16 +680,18 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
               fm, (hipStream_t)stream);
 }
 
-int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int D, int M,
-                         int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
+int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, float* S_out, float* Z_out, int B,
+                         int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
+                         void* stream) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
-  if (N == 0) return LA_OK;
-  if (!Q || !K || !V || !O) return fail(LA_ERR_NULL, "Q, K, V and O are required");
+  if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
+  if (N == 0 && !S_out) return LA_OK;
+  if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_FWD_NONCAUSAL, p).bytes();
@@ -689,9 +699,10 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, i
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
                    rng("V", V, bh * N * M * es, false), rng("O", O, bh * N * M * es, true),
-                   rng("ws", ws, need, true)});
+                   rng("S_out", S_out, bh * D * M * 4, true), rng("Z_out", Z_out, bh * D * 4, true),
+                   rng("ws", need > 0 ? ws : nullptr, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, N, ws, fm, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, S_out, Z_out, N, ws, fm, (hipStream_t)stream);
 }
 
 int la_backward_causal(const void* Q, const void* K, const void* V, const float* logA, const void* O,
@@ -745,9 +756,9 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
               N, ws, fm, (hipStream_t)stream);
 }
 
-int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, void* dQ, void* dK,
-                          void* dV, int B, int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
-                          void* stream) {
+int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, const float* S_tot,
+                          const float* Z_tot, void* dQ, void* dK, void* dV, int B, int H, int N, int D, int M,
+                          int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
@@ -756,6 +767,7 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
   if (st) return st;
   if (N == 0) return LA_OK;
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(LA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
+  if ((S_tot == nullptr) != (Z_tot == nullptr)) return fail(LA_ERR_ARG, "S_tot and Z_tot must be given together");
   const Plan p = make_plan(B, H, N, D, M);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_BWD_NONCAUSAL, p).bytes();
@@ -763,10 +775,12 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
                    rng("V", V, bh * N * M * es, false), rng("dO", dO, bh * N * M * es, false),
+                   rng("S_tot", S_tot, bh * D * M * 4, false), rng("Z_tot", Z_tot, bh * D * 4, false),
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
                    rng("dV", dV, bh * N * M * es, true), rng("ws", ws, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, dQ, dK, dV, N, ws, fm, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, S_tot, Z_tot, dQ, dK, dV, N, ws, fm,
+              (hipStream_t)stream);
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,

@@ -241,7 +241,8 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
 //     entry seg and the last segment writes entry nseg.  The last segment
 //     writes the final state to S_out/Z_out.
 //   non-causal: num^T = S^T phi(Q)^T, den = Z^T phi(Q)^T with S, Z the total:
-//     entry nseg of `pref`, or the sum of all aggregates (eq. 5-6).
+//     entry nseg of `pref`, or the sum of all aggregates (eq. 5-6); segment 0
+//     writes the total to S_out/Z_out when given.
 // Z is staged as 16 identical rows, so phi(Q) Z is one more MFMA output tile
 // whose every row holds the denominators of the wave's tokens.
 template <typename T, int D, int M, bool CAUSAL>
@@ -337,6 +338,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
     float* ck = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
     write_state(ck, ck + D * M);
   }
+  if (!CAUSAL && S_out && seg == 0) write_state(S_out + (size_t)bh * D * M, Z_out + (size_t)bh * D);
   stage_state();
 
   auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
@@ -1119,15 +1121,29 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
 //   R = sum_i phi(Q_i) g_i^T, r = sum_i c_i phi(Q_i)  (g_i = dO_i / den_i,
 //     c_i = -(O_i.dO_i) / den_i),
 //   dphiK_j = R V_j + r,  dV_j = R^T phi(K_j).
-// Totals come from entry nseg of a scanned prefix array `pref` when given,
-// else from summing all segment aggregates `agg` here.
+// Totals come from S_t/Z_t when given (the forward's), else from entry nseg
+// of a scanned prefix array `pref`, else from summing all segment aggregates
+// `agg` here.
 
 // Stage a state total (S then Z, row-major [d][m]) into planes and a float32 vector.
 template <int D, int M, int NP, int NTH>
 __device__ __forceinline__ void stage_total(Planes<NP, D, M>& sp, float* sz, float* sbuf, const float* pref,
-                                            const float* agg, int nseg) {
+                                            const float* agg, int nseg, const float* St = nullptr,
+                                            const float* Zt = nullptr) {
   constexpr int SV = D * M + D;
   const float* src;
+  if (St) {  // the totals as given ([D][M] and [D])
+    for (int e = 4 * threadIdx.x; e < SV; e += 4 * NTH) {
+      if (e < D * M) {
+        const float4 a = *reinterpret_cast<const float4*>(St + e);
+        const float x[4] = {a.x, a.y, a.z, a.w};
+        sp.put4(e / M, e % M, x);
+      } else {
+        *reinterpret_cast<float4*>(sz + (e - D * M)) = *reinterpret_cast<const float4*>(Zt + (e - D * M));
+      }
+    }
+    return;
+  }
   if (pref) {
     src = pref + (size_t)nseg * SV;
   } else {
@@ -1149,6 +1165,7 @@ __device__ __forceinline__ void stage_total(Planes<NP, D, M>& sp, float* sz, flo
 // Query pass: dQ, and the reverse aggregates (R^T, r) of each segment.
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* __restrict__ dO,
+                                               const float* __restrict__ St, const float* __restrict__ Zt,
                                                const float* __restrict__ agg, const float* __restrict__ pref,
                                                T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg, int fm) {
   using P = Prec<T>;
@@ -1171,7 +1188,8 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   static_assert(sizeof(gt.v) >= SV * sizeof(float), "g planes too small to hold a float32 state");
   stage_total<D, M, P::NS, NT>(sp, sZ, reinterpret_cast<float*>(&gt.v[0][0][0]),
                                pref ? pref + (size_t)bh * (nseg + 1) * SV : nullptr,
-                               agg + (size_t)bh * nseg * SV, nseg);
+                               agg ? agg + (size_t)bh * nseg * SV : nullptr, nseg,
+                               St ? St + (size_t)bh * D * M : nullptr, Zt ? Zt + (size_t)bh * D : nullptr);
   __syncthreads();
   gt.zero_cols(M + 1, M + 16);
 

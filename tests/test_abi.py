@@ -95,12 +95,12 @@ def test_forward_validation(lib):
 
 def test_noncausal_and_backward_validation(lib):
     ws = lib.la_workspace_size(1, 1, 1, 64, 64, 64, 1)
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), None, 1, 1, 64, 64, 64, 1, 0, addr(20), ws, None) == NULL
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), 1, 1, 64, 64, 64, 1, 0, None, 0, None) == WORKSPACE
-    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(3), 1, 1, 64, 64, 64, 1, 0, addr(20), ws,
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), None, None, None, 1, 1, 64, 64, 64, 1, 0, addr(20), ws, None) == NULL
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), None, None, 1, 1, 64, 64, 64, 1, 0, None, 0, None) == WORKSPACE
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(3), None, None, 1, 1, 64, 64, 64, 1, 0, addr(20), ws,
                                     None) == ALIAS
     # N = 0 is a no-op
-    assert lib.la_forward_noncausal(None, None, None, None, 1, 1, 0, 64, 64, 1, 0, None, 0, None) == OK
+    assert lib.la_forward_noncausal(None, None, None, None, None, None, 1, 1, 0, 64, 64, 1, 0, None, 0, None) == OK
     wsb = lib.la_workspace_size(2, 2, 2, 100, 32, 32, 0)
     names = ["Q", "K", "V", "logA", "O", "den", "dO", "S0", "Z0", "ckpt", "dS_N", "dZ_N", "dQ", "dK", "dV", "dlogA",
              "dS0", "dZ0"]
@@ -166,16 +166,24 @@ def test_decay_forward_validation(lib):
 def test_noncausal_backward_validation(lib):
     ws = lib.la_workspace_size(4, 2, 2, 100, 32, 32, 0)
     assert ws > 0
-    args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7)]
+    args = [addr(1), addr(2), addr(3), addr(4), None, None, addr(5), addr(6), addr(7)]
     a = list(args)
-    a[4] = None
+    a[6] = None
     assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == NULL
     a = list(args)
-    a[5] = addr(1)  # dK on top of Q
+    a[7] = addr(1)  # dK on top of Q
     assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == ALIAS
     assert lib.la_backward_noncausal(*args, 2, 2, 100, 32, 32, 0, 0, addr(20), ws - 1, None) == WORKSPACE
     assert lib.la_backward_noncausal(*args, 2, 2, 100, 48, 32, 0, 0, addr(20), ws, None) == UNSUPPORTED
     assert lib.la_backward_noncausal(*args, 2, 2, 0, 32, 32, 0, 0, None, 0, None) == OK
+    a = list(args)
+    a[4] = addr(8)  # S_tot without Z_tot
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == ARG
+    a[5] = addr(9)
+    a[6] = addr(8)  # dQ on top of S_tot
+    assert lib.la_backward_noncausal(*a, 2, 2, 100, 32, 32, 0, 0, addr(20), ws, None) == ALIAS
+    assert lib.la_forward_noncausal(addr(1), addr(2), addr(3), addr(4), addr(5), None, 2, 2, 100, 32, 32, 0, 0,
+                                    addr(20), 1 << 30, None) == ARG
 
 
 def test_decode_validation(lib):

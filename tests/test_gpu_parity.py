@@ -328,9 +328,16 @@ def nc_cancel_scales(q, k, v, do):
     return np.abs(uq).max(-1), np.abs(uk).max(-1)
 
 
-def check_backward_noncausal(q, k, v, do, dtype, tol=None):
+def check_backward_noncausal(q, k, v, do, dtype, tol=None, totals=False):
     tol = TOL[dtype] if tol is None else tol
-    dq, dk, dv = binding.backward_noncausal(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype))
+    Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    s = z = None
+    if totals:  # the forward's totals, checked against the plain sums, passed on to the backward
+        _, s, z = binding.forward_noncausal(Q, K, V, return_state=True)
+        torch.cuda.synchronize()
+        _, _, rs, rz = oracle.forward_causal(q, k, v)
+        assert max(rowerr(host(s), rs), rowerr(host(z), rz, False)) <= tol
+    dq, dk, dv = binding.backward_noncausal(Q, K, V, dev(do, dtype), s=s, z=z)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.backward_noncausal(q, k, v, do)
     dq, dk, dv = host(dq), host(dk), host(dv)
@@ -557,3 +564,22 @@ def test_state_gradient_long_shape_sampled():
     errs = state_grad_errors([sub(a) for a in got], sub(q), sub(k), sub(v), sub(do), sub(s0), sub(z0), sub(dsn),
                              sub(dzn))
     assert max(errs.values()) <= TOL[BF16], errs
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("D,M", DM)
+@pytest.mark.parametrize("N", [1, 65, 784])
+def test_backward_noncausal_with_forward_totals(N, D, M, dtype):
+    """The non-causal forward's totals (S, Z) handed to the backward in place of forming them again."""
+    q, k, v = _qkv(2, 3, N, D, M, dtype, 15000 + N)
+    do = inputs.gaussian((2, 3, N, M), 15099, 1.0, dtype)
+    check_backward_noncausal(q, k, v, do, dtype, totals=True)
+
+
+def test_noncausal_totals_of_empty_sequence():
+    s = torch.full((2, 2, 32, 64), 3.0, device="cuda")
+    z = torch.full((2, 2, 32), 3.0, device="cuda")
+    e, ev = torch.empty((2, 2, 0, 32), device="cuda"), torch.empty((2, 2, 0, 64), device="cuda")
+    binding.la_forward_noncausal(e, e, ev, ev, S_out=s, Z_out=z)
+    torch.cuda.synchronize()
+    assert not torch.any(s) and not torch.any(z)
