@@ -496,13 +496,13 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
     if (st) return st;
     ck = ckw;
   }
-  st = launch("dbq", la::k_dbq<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V, (const T*)dO,
+  st = launch("dbq", la::k_dbq<T, D, M>, grid, dim3(2 * la::NT), s, (const T*)Q, (const T*)K, (const T*)V, (const T*)dO,
               logA, ck, (T*)dQ, gc, ragg, dlam, N, p.L, p.nseg, fm);
   if (st) return st;
   st = launch("dscan_rev", la::k_dscan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, (const float*)dlam, dSN, dZN,
               dS0, dZ0, p.nseg);
   if (st) return st;
-  st = launch("dbkv", la::k_dbkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+  st = launch("dbkv", la::k_dbkv<T, D, M>, grid, dim3(2 * la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
               (const T*)dO, logA, (const float2*)gc, (const float*)ragg, ck, dSN, dZN, (T*)dK, (T*)dV, dlogA, xseg, N,
               p.L, p.nseg, fm);
   if (st) return st;

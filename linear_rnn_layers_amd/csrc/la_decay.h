@@ -396,15 +396,21 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
 // aggregate ragg = sum_i exp(L_i - L_start) phi(Q_i) [g_i | c_i]^T (S^T
 // layout as the causal one; L_start the running sum before the segment) and
 // dlam[seg] = sum of logA over the segment.
+//
+// Eight wavefronts in two roles, one of each per SIMD: wavefronts 0-3 own the
+// query rows (dQ, 1/den, c and the weighted [g | c] rows), wavefronts 4-7
+// carry the state (its update for the next chunk runs while the query rows
+// are worked on) and, after the barrier that publishes [g | c], the reverse
+// aggregate.
 template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __restrict__ K,
-                                             const T* __restrict__ V, const T* __restrict__ dO,
-                                             const float* __restrict__ logA, const float* __restrict__ ckpt,
-                                             T* __restrict__ dQ, float2* __restrict__ gc, float* __restrict__ ragg,
-                                             float* __restrict__ dlam, int N, int L,
-                                             int nseg, int fm) {
+__global__ __launch_bounds__(2 * NT) void k_dbq(const T* __restrict__ Q, const T* __restrict__ K,
+                                                 const T* __restrict__ V, const T* __restrict__ dO,
+                                                 const float* __restrict__ logA, const float* __restrict__ ckpt,
+                                                 T* __restrict__ dQ, float2* __restrict__ gc,
+                                                 float* __restrict__ ragg, float* __restrict__ dlam, int N, int L,
+                                                 int nseg, int fm) {
   using P = DPrec<T>;
-  constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
+  constexpr int NTH = 2 * NT, DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   __shared__ Planes<P::Q, CH, D> qt;
   __shared__ Planes<P::K, CH, D> kt;
   __shared__ Planes<P::V, CH, M> vt;
@@ -418,15 +424,21 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const int db = w % DB;
-  const bool zw = w < DB;
+  const bool qrole = w < 4;
+  const int sw = w & 3;  // rank among the state wavefronts
+  const int db = sw % DB;
+  const bool zw = !qrole && sw < DB;
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
   const float* la = logA + (size_t)bh * N;
   const Frag<1> ones = ones_frag();
-  gt.zero_cols(M + 1, M + 16);
+  gt.zero_cols(M + 1, M + 16, NTH);
 
-  RowBuf<T, CH, D> bq[2], bk[2];
-  RowBuf<T, CH, M> bv[2], bd[2];
+  constexpr int OD_ = RowBuf<T, CH, D, NTH>::VEC < NTH ? NTH / 2 : 0;
+  constexpr int OM_ = RowBuf<T, CH, M, NTH>::VEC < NTH ? NTH / 2 : 0;
+  RowBuf<T, CH, D, NTH> bq[2];
+  RowBuf<T, CH, D, NTH, OD_> bk[2];
+  RowBuf<T, CH, M, NTH> bv[2];
+  RowBuf<T, CH, M, NTH, OM_> bd[2];
   float ell[2];
   auto fetch = [&](int b, int c0) {
     const int nv = min(CH, t1 - c0);
@@ -441,7 +453,8 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
   fetch(0, t0);
   fetch(1, t0 + CH);
 
-  // state S^T layout: accS[k][r] = S[16db + r16][16mb + 4g + r]; accZ[.] = Z[16db + r16]
+  // state wavefronts: S^T layout accS[k][r] = S[16db + r16][16mb + 4g + r] (tile sw + 4k),
+  // accZ[.] = Z[16db + r16]; the reverse aggregate in the same layout
   f32x4_t accS[NTW], accZ = zero4(), accR[NTW], accr = zero4();
 #pragma unroll
   for (int k = 0; k < NTW; ++k) {
@@ -449,13 +462,14 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
     accR[k] = zero4();
   }
   const float* st0 = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
-  add_ST_tiles<D, M, NTW>(accS, st0, 0, 0, 1, w, r16, g);
+  if (!qrole) add_ST_tiles<D, M, NTW>(accS, st0, 0, 0, 1, sw, r16, g);
   if (zw) accZ = f32x4_t{1.f, 1.f, 1.f, 1.f} * st0[D * M + 16 * db + r16];
   auto stage_state = [&]() {
+    if (qrole) return;
     float v4[4];
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
-      const int mb = (w + 4 * k) / DB;
+      const int mb = (sw + 4 * k) / DB;
       acc_to4(accS[k], v4);
       sp.put4(16 * db + r16, 16 * mb + 4 * g, v4);
     }
@@ -480,144 +494,153 @@ __global__ __launch_bounds__(NT) void k_dbq(const T* __restrict__ Q, const T* __
     fetch(b, c0 + 2 * CH);
     __syncthreads();
 
-    const int il = 16 * w + r16;
-    const bool row_ok = il < nv;
-    const float lam_i = slam[il], e_i = exp_nat(lam_i);
-    Frag<P::Q> qf[D / 32];
-    Frag<P::DO> dof[M / 32];
+    if (qrole) {
+      const int il = 16 * w + r16;
+      const bool row_ok = il < nv;
+      const float lam_i = slam[il], e_i = exp_nat(lam_i);
+      Frag<P::Q> qf[D / 32];
+      Frag<P::DO> dof[M / 32];
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = qt.template frag<P::Q>(il, 32 * s, g);
+      for (int s = 0; s < D / 32; ++s) qf[s] = qt.template frag<P::Q>(il, 32 * s, g);
 #pragma unroll
-    for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<P::DO>(il, 32 * s, g);
+      for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<P::DO>(il, 32 * s, g);
 
-    // intra-chunk tiles, [j][i] with j = 16jb + 4g + r
-    f32x4_t wt[4], pt[4];
-    float dpA = 0.f, dpP = 0.f;
+      // intra-chunk tiles, [j][i] with j = 16jb + 4g + r
+      f32x4_t wt[4], pt[4];
+      float dpA = 0.f, dpP = 0.f;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      f32x4_t a = zero4(), p = zero4(), e = zero4();
-      if (jb <= w) {
+      for (int jb = 0; jb < 4; ++jb) {
+        f32x4_t a = zero4(), p = zero4(), e = zero4();
+        if (jb <= w) {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) mmaf<P::K, P::Q>(a, kt.template frag<P::K>(16 * jb + r16, 32 * s, g), qf[s]);
+          for (int s = 0; s < D / 32; ++s) mmaf<P::K, P::Q>(a, kt.template frag<P::K>(16 * jb + r16, 32 * s, g), qf[s]);
 #pragma unroll
-        for (int s = 0; s < M / 32; ++s) mmaf<P::V, P::DO>(p, vt.template frag<P::V>(16 * jb + r16, 32 * s, g), dof[s]);
-        const float4 lj = *reinterpret_cast<const float4*>(&slam[16 * jb + 4 * g]);
-        const float ljv[4] = {lj.x, lj.y, lj.z, lj.w};
+          for (int s = 0; s < M / 32; ++s)
+            mmaf<P::V, P::DO>(p, vt.template frag<P::V>(16 * jb + r16, 32 * s, g), dof[s]);
+          const float4 lj = *reinterpret_cast<const float4*>(&slam[16 * jb + 4 * g]);
+          const float ljv[4] = {lj.x, lj.y, lj.z, lj.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool on = jb < w || 4 * g + r <= r16;
+            e[r] = on ? exp_nat(lam_i - ljv[r]) : 0.f;
+            dpA += a[r] * e[r];
+            dpP += a[r] * e[r] * p[r];
+          }
+        }
+        wt[jb] = e;
+        pt[jb] = p;
+      }
+      dpA = sum_over_g(dpA);
+      dpP = sum_over_g(dpP);
+
+      // state terms: U = S dO_i ([d][i]), phi(Q_i).Z and phi(Q_i).U
+      f32x4_t U[DB];
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
+        f32x4_t u = zero4();
+#pragma unroll
+        for (int s = 0; s < M / 32; ++s)
+          mmaf<P::S, P::DO>(u, sp.template frag<P::S>(16 * d0 + r16, 32 * s, g), dof[s]);
+        U[d0] = u;
+      }
+      float qv[DB][4], zv[DB][4], pu = 0.f, pz = 0.f;
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
+        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+        const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
+        zv[d0][0] = z4.x; zv[d0][1] = z4.y; zv[d0][2] = z4.z; zv[d0][3] = z4.w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool on = jb < w || 4 * g + r <= r16;
-          e[r] = on ? exp_nat(lam_i - ljv[r]) : 0.f;
-          dpA += a[r] * e[r];
-          dpP += a[r] * e[r] * p[r];
+          pu += qv[d0][r] * U[d0][r];
+          pz += qv[d0][r] * zv[d0][r];
         }
       }
-      wt[jb] = e;
-      pt[jb] = p;
-    }
-    dpA = sum_over_g(dpA);
-    dpP = sum_over_g(dpP);
+      pu = sum_over_g(pu);
+      pz = sum_over_g(pz);
+      const float den = dpA + e_i * pz;
+      const float inv = row_ok ? 1.f / den : 0.f;
+      const float odo = row_ok ? (dpP + e_i * pu) * inv : 0.f;  // O_i . dO_i
 
-    // state terms: U = S dO_i ([d][i]), phi(Q_i).Z and phi(Q_i).U
-    f32x4_t U[DB];
+      // W[j][i] = exp(lam_i - lam_j) (dO_i.V_j - O_i.dO_i), then sum_j W phi(K_j)
+      Frag<P::W> wf[2];
 #pragma unroll
-    for (int d0 = 0; d0 < DB; ++d0) {
-      f32x4_t u = zero4();
+      for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
-      for (int s = 0; s < M / 32; ++s) mmaf<P::S, P::DO>(u, sp.template frag<P::S>(16 * d0 + r16, 32 * s, g), dof[s]);
-      U[d0] = u;
-    }
-    float qv[DB][4], zv[DB][4], pu = 0.f, pz = 0.f;
+        for (int r = 0; r < 4; ++r) pt[jb][r] = wt[jb][r] * (pt[jb][r] - odo);
+      }
 #pragma unroll
-    for (int d0 = 0; d0 < DB; ++d0) {
-      qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
-      const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
-      zv[d0][0] = z4.x; zv[d0][1] = z4.y; zv[d0][2] = z4.z; zv[d0][3] = z4.w;
+      for (int p = 0; p < 2; ++p) wf[p] = acc2frag<P::W>(pt[2 * p], pt[2 * p + 1]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pu += qv[d0][r] * U[d0][r];
-        pz += qv[d0][r] * zv[d0][r];
+      for (int d0 = 0; d0 < DB; ++d0) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (2 * p <= w) mmaf<P::K, P::W>(acc, kt.template tfrag_acc<P::K>(32 * p, 16 * d0, g, r16), wf[p]);
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dpq = (acc[r] + e_i * (U[d0][r] - odo * zv[d0][r])) * inv;
+          o[r] = dpq * dfeat(qv[d0][r], fm);
+        }
+        if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
+      }
+      const float cc = -odo * inv;
+      if (g == 0 && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(inv, cc);
+      // [g_i | c_i] weighted to the segment start
+      const float sc = row_ok ? exp_nat(lstart + lam_i) : 0.f;
+#pragma unroll
+      for (int mm = 0; mm < M / 4; mm += 4) {
+        float dv[4];
+        ot.get4(il, g * (M / 4) + mm, dv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dv[q] *= inv * sc;
+        gt.put4(il, g * (M / 4) + mm, dv);
+      }
+      if (g == 0) gt.put1(il, M, cc * sc);
+    } else {
+      // state after the chunk: S^T = exp(lam_last) S^T + V^T diag(f) phi(K), in registers
+      const float dec = exp_nat(last);
+#pragma unroll
+      for (int k = 0; k < NTW; ++k) accS[k] *= dec;
+      accZ *= dec;
+#pragma unroll
+      for (int s = 0; s < CH / 32; ++s) {
+        const Frag<P::K> kb = scale_frag<P::K>(kt.template tfrag<P::K>(32 * s, 16 * db, g, r16), &sF[32 * s + 8 * g]);
+#pragma unroll
+        for (int k = 0; k < NTW; ++k) {
+          const int mb = (sw + 4 * k) / DB;
+          mmaf<P::V, P::K>(accS[k], vt.template tfrag<P::V>(32 * s, 16 * mb, g, r16), kb);
+        }
+        if (zw) mmaf<1, P::K>(accZ, ones, kb);
       }
     }
-    pu = sum_over_g(pu);
-    pz = sum_over_g(pz);
-    const float den = dpA + e_i * pz;
-    const float inv = row_ok ? 1.f / den : 0.f;
-    const float odo = row_ok ? (dpP + e_i * pu) * inv : 0.f;  // O_i . dO_i
+    __syncthreads();  // [g | c] complete; the query rows are done with S, Z of this chunk
 
-    // W[j][i] = exp(lam_i - lam_j) (dO_i.V_j - O_i.dO_i), then sum_j W phi(K_j)
-    Frag<P::W> wf[2];
+    if (!qrole) {
+      stage_state();  // read again only after the next chunk's first barrier
+      // reverse aggregate: R^T += [g|c]^T phi(Q) (weighted rows)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
+      for (int s = 0; s < CH / 32; ++s) {
+        const Frag<P::Q> qb = qt.template tfrag<P::Q>(32 * s, 16 * db, g, r16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pt[jb][r] = wt[jb][r] * (pt[jb][r] - odo);
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) wf[p] = acc2frag<P::W>(pt[2 * p], pt[2 * p + 1]);
-#pragma unroll
-    for (int d0 = 0; d0 < DB; ++d0) {
-      f32x4_t acc = zero4();
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p <= w) mmaf<P::K, P::W>(acc, kt.template tfrag_acc<P::K>(32 * p, 16 * d0, g, r16), wf[p]);
-      float o[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float dpq = (acc[r] + e_i * (U[d0][r] - odo * zv[d0][r])) * inv;
-        o[r] = dpq * dfeat(qv[d0][r], fm);
+        for (int k = 0; k < NTW; ++k) {
+          const int mb = (sw + 4 * k) / DB;
+          mmaf<P::G, P::Q>(accR[k], gt.template tfrag<P::G>(32 * s, 16 * mb, g, r16), qb);
+        }
+        if (zw) mmaf<P::G, P::Q>(accr, gt.template tfrag<P::G>(32 * s, M, g, r16), qb);
       }
-      if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
     }
-    const float cc = -odo * inv;
-    if (g == 0 && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(inv, cc);
-    // [g_i | c_i] weighted to the segment start
-    const float sc = row_ok ? exp_nat(lstart + lam_i) : 0.f;
-#pragma unroll
-    for (int mm = 0; mm < M / 4; mm += 4) {
-      float dv[4];
-      ot.get4(il, g * (M / 4) + mm, dv);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dv[q] *= inv * sc;
-      gt.put4(il, g * (M / 4) + mm, dv);
-    }
-    if (g == 0) gt.put1(il, M, cc * sc);
-    __syncthreads();
-
-    // reverse aggregate: R^T += [g|c]^T phi(Q) (weighted rows)
-#pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-      const Frag<P::Q> qb = qt.template tfrag<P::Q>(32 * s, 16 * db, g, r16);
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int mb = (w + 4 * k) / DB;
-        mmaf<P::G, P::Q>(accR[k], gt.template tfrag<P::G>(32 * s, 16 * mb, g, r16), qb);
-      }
-      if (zw) mmaf<P::G, P::Q>(accr, gt.template tfrag<P::G>(32 * s, M, g, r16), qb);
-    }
-    // state after the chunk: S^T = exp(lam_last) S^T + V^T diag(f) phi(K)
-    const float dec = exp_nat(last);
-#pragma unroll
-    for (int k = 0; k < NTW; ++k) accS[k] *= dec;
-    accZ *= dec;
-#pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-      const Frag<P::K> kb = scale_frag<P::K>(kt.template tfrag<P::K>(32 * s, 16 * db, g, r16), &sF[32 * s + 8 * g]);
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int mb = (w + 4 * k) / DB;
-        mmaf<P::V, P::K>(accS[k], vt.template tfrag<P::V>(32 * s, 16 * mb, g, r16), kb);
-      }
-      if (zw) mmaf<1, P::K>(accZ, ones, kb);
-    }
-    stage_state();  // read again only after the next chunk's first barrier
     lstart += last;
   };
   for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
     chunk(0, c0);
     if (c0 + CH < t1) chunk(1, c0 + CH);
   }
-  float* out = ragg + ((size_t)bh * nseg + seg) * SV;
-  store_ST_tiles<D, M, NTW>(out, accR, w, r16, g);
-  if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
+  if (!qrole) {
+    float* out = ragg + ((size_t)bh * nseg + seg) * SV;
+    store_ST_tiles<D, M, NTW>(out, accR, sw, r16, g);
+    if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
+  }
   if (tid == 0) dlam[(size_t)bh * nseg + seg] = lstart;
 }
 
@@ -677,16 +700,23 @@ __global__ __launch_bounds__(NT) void k_dscan_rev(float* __restrict__ ragg, cons
 // of x over the segment's tokens from j on (plus, in the last segment, the
 // final-state term <[dS_N|dZ_N], [S_N|Z_N]> with S_N checkpoint entry nseg),
 // and xseg[bh][seg] the segment's total; k_dla_fix adds the later segments'.
+// Eight wavefronts in two roles, one of each per SIMD: wavefront rb (0-3)
+// forms dV of key rows 16rb.., wavefront 4 + rb dphiK of the same rows (the
+// attention tiles for dV, the dO.V tiles for dK); the tiles of R+ are spread
+// over all eight.
 template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* __restrict__ K,
-                                              const T* __restrict__ V, const T* __restrict__ dO,
-                                              const float* __restrict__ logA, const float2* __restrict__ gc,
-                                              const float* __restrict__ rin, const float* __restrict__ ckpt,
-                                              const float* __restrict__ dSN, const float* __restrict__ dZN,
-                                              T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dla,
-                                              float* __restrict__ xseg, int N, int L, int nseg, int fm) {
+__global__ __launch_bounds__(2 * NT) void k_dbkv(const T* __restrict__ Q, const T* __restrict__ K,
+                                                  const T* __restrict__ V, const T* __restrict__ dO,
+                                                  const float* __restrict__ logA, const float2* __restrict__ gc,
+                                                  const float* __restrict__ rin, const float* __restrict__ ckpt,
+                                                  const float* __restrict__ dSN, const float* __restrict__ dZN,
+                                                  T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dla,
+                                                  float* __restrict__ xseg, int N, int L, int nseg, int fm) {
   using P = DPrec<T>;
-  constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
+  constexpr int NTH = 2 * NT, DB = D / 16, MB = M / 16, SV = D * M + D;
+  constexpr int NRW = DB * MB < 8 ? DB * MB : 8;  // wavefronts holding tiles of R+
+  constexpr int NTR = DB * MB / NRW;              // tiles per holder: t = w + NRW k
+  static_assert(NRW % DB == 0, "a holder's tiles share one feature block");
   __shared__ Planes<P::Q, CH, D> qt;
   __shared__ Planes<P::K, CH, D> kt;
   __shared__ Planes<P::V, CH, M> vt;
@@ -702,25 +732,27 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const int db = w % DB;
-  const bool zw = w < DB;
+  const bool vrole = w < 4;  // dV wavefront, else dK
+  const int rb = w & 3;      // key row block
+  const int db = w % DB;     // feature block of the wave's R+ tiles
+  const bool rhold = w < NRW, zw = w < DB;
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
   const float* la = logA + (size_t)bh * N;
   const float2* gch = gc + (size_t)bh * N;
-  gt.zero_cols(M + 1, M + 16);
+  gt.zero_cols(M + 1, M + 16, NTH);
 
   // running sum of x from the segment's end (wave 0); the last segment starts it at the final-state term
   float carry = 0.f;
   if (seg == nseg - 1 && dSN) {
     const float* sn = ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV;
     float acc = 0.f;
-    for (int e = tid; e < SV; e += NT)
+    for (int e = tid; e < SV; e += NTH)
       acc += (e < D * M ? dSN[(size_t)bh * D * M + e] : dZN[(size_t)bh * D + e - D * M]) * sn[e];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (l == 0) sX[w] = acc;
     __syncthreads();
-    carry = sX[0] + sX[1] + sX[2] + sX[3];
+    carry = ((sX[0] + sX[1]) + (sX[2] + sX[3])) + ((sX[4] + sX[5]) + (sX[6] + sX[7]));
     __syncthreads();
   }
   int pend_c0 = -1, pend_nv = 0;  // chunk whose x values wait in sX
@@ -733,8 +765,13 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
   };
 
   const int nchunk = (t1 - t0 + CH - 1) / CH;
-  RowBuf<T, CH, D> bq[2], bk[2];
-  RowBuf<T, CH, M> bv[2], bd[2];
+  // a tensor with fewer vectors per chunk than threads goes to one half of the workgroup
+  constexpr int OD_ = RowBuf<T, CH, D, NTH>::VEC < NTH ? NTH / 2 : 0;
+  constexpr int OM_ = RowBuf<T, CH, M, NTH>::VEC < NTH ? NTH / 2 : 0;
+  RowBuf<T, CH, D, NTH> bq[2];
+  RowBuf<T, CH, D, NTH, OD_> bk[2];
+  RowBuf<T, CH, M, NTH> bv[2];
+  RowBuf<T, CH, M, NTH, OM_> bd[2];
   float ell[2];
   float2 gcl[2];
   auto fetch = [&](int b, int ci) {
@@ -750,20 +787,29 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
   fetch(0, nchunk - 1);
   fetch(1, nchunk - 2);
 
-  // R+ in the S^T layout: accR[k][r] = R[16db + r16][16mb + 4g + r]; accr[.] = r[16db + r16]
-  f32x4_t accR[NTW], accr = zero4();
+  // R+ tiles of this wave in the S^T layout: accR[k][r] = R[16db + r16][16mb + 4g + r], t = w + NRW k
+  f32x4_t accR[NTR], accr = zero4();
+  auto rmb = [&](int k) { return (w + NRW * k) / DB; };
+  {
+    const float* r0 = rin + ((size_t)bh * nseg + seg) * SV;
 #pragma unroll
-  for (int k = 0; k < NTW; ++k) accR[k] = zero4();
-  const float* r0 = rin + ((size_t)bh * nseg + seg) * SV;
-  add_ST_tiles<D, M, NTW>(accR, r0, 0, 0, 1, w, r16, g);
-  if (zw) accr = f32x4_t{1.f, 1.f, 1.f, 1.f} * r0[D * M + 16 * db + r16];
+    for (int k = 0; k < NTR; ++k) {
+      accR[k] = zero4();
+      if (rhold) {
+        const float4 a = *reinterpret_cast<const float4*>(r0 + (16 * db + r16) * M + 16 * rmb(k) + 4 * g);
+        accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
+      }
+    }
+    if (zw) accr = f32x4_t{1.f, 1.f, 1.f, 1.f} * r0[D * M + 16 * db + r16];
+  }
   auto stage_R = [&]() {
-    float v4[4];
+    if (rhold) {
+      float v4[4];
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      const int mb = (w + 4 * k) / DB;
-      acc_to4(accR[k], v4);
-      rp.put4(16 * db + r16, 16 * mb + 4 * g, v4);
+      for (int k = 0; k < NTR; ++k) {
+        acc_to4(accR[k], v4);
+        rp.put4(16 * db + r16, 16 * rmb(k) + 4 * g, v4);
+      }
     }
     if (zw && g == 0) sr[16 * db + r16] = accr[0];
   };
@@ -806,106 +852,111 @@ __global__ __launch_bounds__(NT) void k_dbkv(const T* __restrict__ Q, const T* _
     fetch(b, ci - 2);
     __syncthreads();
 
-    const int jl = 16 * w + r16;
+    const int jl = 16 * rb + r16;
     const bool row_ok = jl < nv;
     const float lam_j = slam[jl], f_j = exp_nat(last - lam_j);
-    Frag<P::K> kf[D / 32];
-    Frag<P::V> vf[M / 32];
+    // tiles [i][j] with i = 16ib + 4g + r >= j: the attention A (dV role) or dO.V (dK role), weighted
+    f32x4_t tw[4];
+    {
+      Frag<P::K> kf[D / 32];
+      Frag<P::V> vf[M / 32];
+      if (vrole) {
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) kf[s] = kt.template frag<P::K>(jl, 32 * s, g);
+        for (int s = 0; s < D / 32; ++s) kf[s] = kt.template frag<P::K>(jl, 32 * s, g);
+      } else {
 #pragma unroll
-    for (int s = 0; s < M / 32; ++s) vf[s] = vt.template frag<P::V>(jl, 32 * s, g);
-
-    // tiles [i][j] with i = 16ib + 4g + r >= j
-    f32x4_t aw[4], ww[4];
+        for (int s = 0; s < M / 32; ++s) vf[s] = vt.template frag<P::V>(jl, 32 * s, g);
+      }
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-      f32x4_t a = zero4(), p = zero4();
-      if (ib >= w) {
+      for (int ib = 0; ib < 4; ++ib) {
+        f32x4_t a = zero4();
+        if (ib >= rb) {
+          if (vrole) {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) mmaf<P::Q, P::K>(a, qt.template frag<P::Q>(16 * ib + r16, 32 * s, g), kf[s]);
+            for (int s = 0; s < D / 32; ++s) mmaf<P::Q, P::K>(a, qt.template frag<P::Q>(16 * ib + r16, 32 * s, g), kf[s]);
+          } else {
 #pragma unroll
-        for (int s = 0; s < M / 32; ++s) mmaf<P::DO, P::V>(p, ot.template frag<P::DO>(16 * ib + r16, 32 * s, g), vf[s]);
-        const float4 li = *reinterpret_cast<const float4*>(&slam[16 * ib + 4 * g]);
-        const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
-        const float4 cv = *reinterpret_cast<const float4*>(&sC[16 * ib + 4 * g]);
-        const float liv[4] = {li.x, li.y, li.z, li.w}, ivv[4] = {iv.x, iv.y, iv.z, iv.w},
-                    cvv[4] = {cv.x, cv.y, cv.z, cv.w};
+            for (int s = 0; s < M / 32; ++s)
+              mmaf<P::DO, P::V>(a, ot.template frag<P::DO>(16 * ib + r16, 32 * s, g), vf[s]);
+          }
+          const float4 li = *reinterpret_cast<const float4*>(&slam[16 * ib + 4 * g]);
+          const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
+          const float4 cv = *reinterpret_cast<const float4*>(&sC[16 * ib + 4 * g]);
+          const float liv[4] = {li.x, li.y, li.z, li.w}, ivv[4] = {iv.x, iv.y, iv.z, iv.w},
+                      cvv[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool on = ib > w || 4 * g + r >= r16;
-          const float e = on ? exp_nat(liv[r] - lam_j) : 0.f;
-          a[r] = a[r] * e * ivv[r];
-          p[r] = e * (p[r] * ivv[r] + cvv[r]);
+          for (int r = 0; r < 4; ++r) {
+            const bool on = ib > rb || 4 * g + r >= r16;
+            const float e = on ? exp_nat(liv[r] - lam_j) : 0.f;
+            a[r] = vrole ? a[r] * e * ivv[r] : e * (a[r] * ivv[r] + cvv[r]);
+          }
         }
+        tw[ib] = a;
       }
-      aw[ib] = a;
-      ww[ib] = p;
-    }
-    Frag<P::W> awf[2], wwf[2];
+      Frag<P::W> wf[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      awf[p] = acc2frag<P::W>(aw[2 * p], aw[2 * p + 1]);
-      wwf[p] = acc2frag<P::W>(ww[2 * p], ww[2 * p + 1]);
-    }
-    // dV_j[m] = sum_i dO_i[m] aw[i][j] + f_j (R+^T phi(K_j))[m]
+      for (int p = 0; p < 2; ++p) wf[p] = acc2frag<P::W>(tw[2 * p], tw[2 * p + 1]);
+      if (vrole) {
+        // dV_j[m] = sum_i dO_i[m] aw[i][j] + f_j (R+^T phi(K_j))[m]
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      f32x4_t st = zero4(), acc = zero4();
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4_t st = zero4(), acc = zero4();
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) mmaf<P::R, P::K>(st, rp.template tfrag<P::R>(32 * s, 16 * mb, g, r16), kf[s]);
+          for (int s = 0; s < D / 32; ++s) mmaf<P::R, P::K>(st, rp.template tfrag<P::R>(32 * s, 16 * mb, g, r16), kf[s]);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p + 1 >= w) mmaf<P::DO, P::W>(acc, ot.template tfrag_acc<P::DO>(32 * p, 16 * mb, g, r16), awf[p]);
-      if (row_ok) {
-        float o[4];
+          for (int p = 0; p < 2; ++p)
+            if (2 * p + 1 >= rb) mmaf<P::DO, P::W>(acc, ot.template tfrag_acc<P::DO>(32 * p, 16 * mb, g, r16), wf[p]);
+          if (row_ok) {
+            float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[r] + f_j * st[r];
-        IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+            for (int r = 0; r < 4; ++r) o[r] = acc[r] + f_j * st[r];
+            IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+          }
+        }
+      } else {
+        // dphiK_j[d] = sum_i phi(Q_i)[d] ww[i][j] + f_j ((R+ V_j)[d] + r+[d])
+        float xk = 0.f;
+#pragma unroll
+        for (int d0 = 0; d0 < DB; ++d0) {
+          f32x4_t st = zero4(), acc = zero4();
+#pragma unroll
+          for (int s = 0; s < M / 32; ++s) mmaf<P::R, P::V>(st, rp.template frag<P::R>(16 * d0 + r16, 32 * s, g), vf[s]);
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            if (2 * p + 1 >= rb) mmaf<P::Q, P::W>(acc, qt.template tfrag_acc<P::Q>(32 * p, 16 * d0, g, r16), wf[p]);
+          float kv[4];
+          kt.get4(jl, 16 * d0 + 4 * g, kv);
+          const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
+          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float dpk = acc[r] + f_j * (st[r] + rr[r]);
+            xk += kv[r] * dpk;
+            o[r] = dpk * dfeat(kv[r], fm);
+          }
+          if (row_ok) IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
+        }
+        xk = sum_over_g(xk);
+        if (g == 0) sX[jl] = row_ok ? -xk : 0.f;
       }
     }
-    // dphiK_j[d] = sum_i phi(Q_i)[d] ww[i][j] + f_j ((R+ V_j)[d] + r+[d])
-    float xk = 0.f;
-#pragma unroll
-    for (int d0 = 0; d0 < DB; ++d0) {
-      f32x4_t st = zero4(), acc = zero4();
-#pragma unroll
-      for (int s = 0; s < M / 32; ++s) mmaf<P::R, P::V>(st, rp.template frag<P::R>(16 * d0 + r16, 32 * s, g), vf[s]);
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p + 1 >= w) mmaf<P::Q, P::W>(acc, qt.template tfrag_acc<P::Q>(32 * p, 16 * d0, g, r16), wwf[p]);
-      float kv[4];
-      kt.get4(jl, 16 * d0 + 4 * g, kv);
-      const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
-      const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-      float o[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float dpk = acc[r] + f_j * (st[r] + rr[r]);
-        xk += kv[r] * dpk;
-        o[r] = dpk * dfeat(kv[r], fm);
-      }
-      if (row_ok) IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
-    }
-    xk = sum_over_g(xk);
-    if (g == 0) sX[jl] = row_ok ? -xk : 0.f;
     pend_c0 = c0;
     pend_nv = nv;
 
     // R+ for the chunk before
     const float dec = exp_nat(last);
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) accR[k] *= dec;
+    for (int k = 0; k < NTR; ++k) accR[k] *= dec;
     accr *= dec;
+    if (rhold) {
 #pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-      const Frag<P::Q> qb = qt.template tfrag<P::Q>(32 * s, 16 * db, g, r16);
+      for (int s = 0; s < CH / 32; ++s) {
+        const Frag<P::Q> qb = qt.template tfrag<P::Q>(32 * s, 16 * db, g, r16);
 #pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int mb = (w + 4 * k) / DB;
-        mmaf<P::G, P::Q>(accR[k], gt.template tfrag<P::G>(32 * s, 16 * mb, g, r16), qb);
+        for (int k = 0; k < NTR; ++k) mmaf<P::G, P::Q>(accR[k], gt.template tfrag<P::G>(32 * s, 16 * rmb(k), g, r16), qb);
+        if (zw) mmaf<P::G, P::Q>(accr, gt.template tfrag<P::G>(32 * s, M, g, r16), qb);
       }
-      if (zw) mmaf<P::G, P::Q>(accr, gt.template tfrag<P::G>(32 * s, M, g, r16), qb);
     }
   };
   for (int ci = nchunk - 1; ci >= 0; ci -= 2) {
