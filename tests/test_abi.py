@@ -196,11 +196,12 @@ def test_decode_validation(lib):
     assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, 0, None) == SHAPE
 
 
-def _plan(B, H, N):
-    """The segment plan, restated: about 1024 segments over all heads, each of whole 64-token chunks."""
+def _plan(B, H, N, target=1024):
+    """The segment plan, restated: about `target` segments over all heads (1024 for the causal ops, 512 for
+    the non-causal ones), each of whole 64-token chunks."""
     bh = B * H
     nch = -(-N // 64)
-    segs = max(1, min(nch, -(-1024 // bh)))
+    segs = max(1, min(nch, -(-target // bh)))
     L = -(-nch // segs) * 64
     return L, -(-N // L)
 
@@ -218,12 +219,14 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     # forward: segment aggregates and their prefix scan when there is more than one segment
     agg, pref = _al(B * H * nseg * sv * 4), _al(B * H * (nseg + 1) * sv * 4)
     assert lib.la_workspace_size(0, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref)
-    assert lib.la_workspace_size(1, B, H, N, D, M, 0) == agg + pref
+    _, nseg_nc = _plan(B, H, N, 512)
+    agg_nc, pref_nc = _al(B * H * nseg_nc * sv * 4), _al(B * H * (nseg_nc + 1) * sv * 4)
+    assert lib.la_workspace_size(1, B, H, N, D, M, 0) == agg_nc + pref_nc
     # backward: room to recompute the checkpoint, plus reverse aggregates
     bwd = _al(B * H * nseg * sv * 4) + _al(B * H * (nseg + 1) * sv * 4) + (0 if nseg == 1 else _al(B * H * nseg * sv * 4))
     assert lib.la_workspace_size(2, B, H, N, D, M, 0) == bwd
     # non-causal backward: key aggregates + scan, reverse aggregates + scan
-    assert lib.la_workspace_size(4, B, H, N, D, M, 0) == 2 * (agg + pref)
+    assert lib.la_workspace_size(4, B, H, N, D, M, 0) == 2 * (agg_nc + pref_nc)
     # decayed forward: aggregates, prefix states, per-segment log-decay sums (more than one segment);
     # decayed backward: those, reverse aggregates and (1/den, c) per token
     dl = _al(B * H * nseg * 4)
