@@ -97,7 +97,8 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype);
  * checkpoint is valid for any call with the same sizes.  Its size is
  * O(N * D * M / segment) per head, well inside the pages' linear-memory
  * bound; no per-token state S_i is ever stored ("Transformers are RNNs --
- * part 2/3", section 3.3.1). */
+ * part 2/3", section 3.3.1).  The decayed recurrence (logA given) uses
+ * longer segments and at most this many bytes. */
 size_t la_checkpoint_size(int B, int H, int N, int D, int M);
 
 /* Sequence segment length (tokens) used for these sizes: the spacing of

@@ -47,10 +47,12 @@ struct Plan {
 
 constexpr long kCUs = 256;          // compute units of one MI355X
 constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels (causal ops)
-// The non-causal ops have no running state to carry between segments, only
-// totals that every workgroup needs; they do better with about half as many,
-// longer segments (measured on the 800-frame speech encoder: 26.7 -> 28.9 M
-// tokens/s).  Their segments are their own: no checkpoint is shared.
+// The non-causal ops (no running state between segments, only totals that
+// every workgroup needs) and the decayed recurrence (no grouping of segments
+// in its backward) do better with about half as many, longer segments
+// (measured: 800-frame speech encoder 26.7 -> 28.9 M tokens/s, gated 2^16
+// sequence 72.0 -> 75.9 M tokens/s).  Never more segments than the causal
+// plan, so la_checkpoint_size bounds the decayed checkpoint too.
 constexpr long kFineTargetNC = 512;
 
 std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
@@ -631,7 +633,8 @@ const char* la_kernel_names(void) {
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
   if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
   if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
-  const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL;
+  const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
+                  op == LA_OP_BWD_DECAY;
   return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : kFineTarget)).bytes();
 }
 
@@ -663,7 +666,7 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
@@ -732,13 +735,13 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
     st = check_ptrs({rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                      rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true)});
     if (st) return st;
-    const Plan p = make_plan(B, H, N, D, M);
+    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
     LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
                 dZ0, N, ws, fm, (hipStream_t)stream);
   }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
-  const Plan p = make_plan(B, H, N, D, M);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
   const size_t es = esize(dtype);
   const size_t need = ws_layout(logA ? LA_OP_BWD_DECAY : LA_OP_BWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0 && (logA || ckpt == nullptr || p.nseg > 1);

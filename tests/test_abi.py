@@ -229,9 +229,9 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     assert lib.la_workspace_size(4, B, H, N, D, M, 0) == 2 * (agg_nc + pref_nc)
     # decayed forward: aggregates, prefix states, per-segment log-decay sums (more than one segment);
     # decayed backward: those, reverse aggregates and (1/den, c) per token
-    dl = _al(B * H * nseg * 4)
-    assert lib.la_workspace_size(5, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref + dl)
-    assert lib.la_workspace_size(6, B, H, N, D, M, 1) == agg + pref + dl + agg + _al(B * H * N * 8) + dl
+    dl = _al(B * H * nseg_nc * 4)  # the decayed recurrence plans like the non-causal ops
+    assert lib.la_workspace_size(5, B, H, N, D, M, 0) == (0 if nseg_nc == 1 else agg_nc + pref_nc + dl)
+    assert lib.la_workspace_size(6, B, H, N, D, M, 1) == agg_nc + pref_nc + dl + agg_nc + _al(B * H * N * 8) + dl
     assert lib.la_workspace_size(9, B, H, N, D, M, 0) == 0
 
 
