@@ -176,3 +176,40 @@ def test_feature_autograd_composition():
     errs = [rowerr(host(Q.grad), rq, row_floor=CANCEL_FLOOR * np.abs(oracle.feature_performer_vjp(q, w, u)).max(-1)),
             rowerr(host(K.grad), rk), rowerr(host(V.grad), rv)]
     assert max(errs) <= 1e-4, errs
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_feature_mode_with_decay(dtype):
+    """Random features through the decayed recurrence (feature mode with logA): forward, the feature gradients
+    and dlogA against the oracle at the same features; dPhi_Q and dlogA floored as in the decay tests."""
+    B, H, N, Din, C, M = 2, 2, 300, 32, 32, 64
+    q, k = _x((B, H, N, Din), 14500, 0.3, dtype), _x((B, H, N, Din), 14501, 0.3, dtype)
+    v, do = _x((B, H, N, M), 14502, 1.0, dtype), _x((B, H, N, M), 14503, 1.0, dtype)
+    w = _w(H, C, Din, 14510)
+    la = (-np.log1p(np.exp(-(inputs.gaussian((B, H, N), 14511).astype(np.float64) + 2.0)))).astype(np.float32)
+    Q, K, V, dO, LA = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype), dev32(la)
+    fQ, fK = binding.feature_random(Q, dev32(w)), binding.feature_random(K, dev32(w))
+    out = binding.forward_causal(fQ, fK, V, feature=IDENT, log_a=LA)
+    dfq, dfk, dv, dla = binding.backward_causal(fQ, fK, V, out["o"], out["den"], dO, ckpt=out["ckpt"],
+                                                feature=IDENT, log_a=LA)
+    torch.cuda.synchronize()
+    fq, fk = host(fQ), host(fK)
+    la = la.astype(np.float64)
+    ro = oracle.forward_decay(fq, fk, v, la, feature=IDENT)[0]
+    rfq, rfk, rv, rla, _, _ = oracle.backward_decay(fq, fk, v, la, do, feature=IDENT)
+    # cancellation scales from the plain decayed recurrences on the features
+    a = np.exp(la)
+    S = np.zeros((B, H, C, M))
+    Z = np.zeros((B, H, C))
+    sq = np.empty((B, H, N))
+    for t in range(N):
+        S = a[:, :, t, None, None] * S + fk[:, :, t, :, None] * v[:, :, t, None, :]
+        Z = a[:, :, t, None] * Z + fk[:, :, t]
+        g = do[:, :, t] / (fq[:, :, t] * Z).sum(-1)[..., None]
+        sq[:, :, t] = np.abs(np.einsum("bhcm,bhm->bhc", S, g)).max(-1)
+    x = np.abs((fk * rfk).sum(-1))
+    dla_floor = CANCEL_FLOOR * np.flip(np.cumsum(np.flip(x, -1), -1), -1)
+    errs = {"O": rowerr(host(out["o"]), ro), "dV": rowerr(host(dv), rv), "dPhiK": rowerr(host(dfk), rfk),
+            "dPhiQ": rowerr(host(dfq), rfq, row_floor=CANCEL_FLOOR * sq),
+            "dlogA": rowerr(host(dla), rla, False, row_floor=dla_floor)}
+    assert max(errs.values()) <= TOL[dtype], errs
