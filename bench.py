@@ -277,7 +277,7 @@ def kernel_flops(name, w):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("la_device.h", "la_kernels.h", "la_api.hip"):
+    for f in ("la_device.h", "la_kernels.h", "la_decay.h", "la_feature.h", "la_api.hip"):
         with open(os.path.join(ROOT, "linear_rnn_layers_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
