@@ -256,12 +256,21 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   constexpr int KR = CAUSAL ? CH : 1, KD = CAUSAL ? D : 8, KM = CAUSAL ? M : 8;
+  using KPlanes = Planes<P::FKF, KR, KD>;
+  constexpr size_t KB_ = sizeof(KPlanes), SB_ = (size_t)SV * sizeof(float);
   __shared__ Planes<P::FQ, CH, D> qt;
-  __shared__ Planes<P::FKF, KR, KD> kt;
   __shared__ Planes<P::FV, KR, KM> vt;
   __shared__ Planes<P::FS, M, D> st;       // S^T
   __shared__ Planes<P::FZ, 16, D> zr;      // 16 copies of Z
-  __shared__ alignas(16) float sbuf[SV];   // start state summed from the aggregates
+  // The start state is summed in LDS and read into registers before the first
+  // chunk is staged (a barrier lies between), so in the causal kernel its
+  // buffer shares storage with the phi(K) planes: 8 KB less at D = 64, M = 32
+  // float32 (two workgroups per compute unit instead of one), 16 KB less at
+  // D = M = 64 bf16 (three instead of two).
+  __shared__ alignas(16) unsigned char kmem[CAUSAL && SB_ > KB_ ? SB_ : KB_];
+  __shared__ alignas(16) float sown[CAUSAL ? 4 : SV];
+  KPlanes& kt = *reinterpret_cast<KPlanes*>(kmem);
+  float* const sbuf = CAUSAL ? reinterpret_cast<float*>(kmem) : sown;  // start state summed from the aggregates
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);

@@ -139,6 +139,32 @@ def test_feature_mode_attention(which, causal, dtype):
     assert max(errs.values()) <= TOL[dtype], errs
 
 
+def test_mnist_random_features_workload():
+    """B=16 H=8 N=784 Din=32 float32 with 64 positive random features, every head, as the training step runs
+    it: the features of Q and K, the causal attention in feature mode (checkpointed forward, backward), the
+    chain rule back through the features; each step against the oracle at that step's own inputs."""
+    w = inputs.MNIST_RF
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    wp = w.projection()
+    Q, K, V, dO, W = dev(q), dev(k), dev(v), dev(do), dev32(wp)
+    fQ, fK = binding.feature_random(Q, W), binding.feature_random(K, W)
+    o, dfq, dfk, dv = _attend(fQ, fK, V, dO, F32, True)
+    dq, dk = binding.feature_random_vjp(Q, W, dfq), binding.feature_random_vjp(K, W, dfk)
+    torch.cuda.synchronize()
+    fq, fk = host(fQ), host(fK)
+    assert max(rowerr(fq, oracle.feature_performer(q, wp)), rowerr(fk, oracle.feature_performer(k, wp))) <= 1e-4
+    ro = oracle.forward_causal(fq, fk, v, feature=IDENT)[0]
+    rfq, rfk, rv = oracle.backward_causal(fq, fk, v, do, feature=IDENT)
+    u = feat_cancel_scale(fq, fk, v, do)
+    errs = {"O": rowerr(host(o), ro), "dV": rowerr(host(dv), rv),
+            "dPhiQ": rowerr(host(dfq), rfq, row_floor=CANCEL_FLOOR * np.abs(u).max(-1)),
+            "dPhiK": rowerr(host(dfk), rfk),
+            "dQ": rowerr(host(dq), oracle.feature_performer_vjp(q, wp, host(dfq))),
+            "dK": rowerr(host(dk), oracle.feature_performer_vjp(k, wp, host(dfk)))}
+    assert max(errs.values()) <= 1e-4, errs
+
+
 def test_feature_mode_with_elu_features_matches_the_method():
     """elu + 1 applied by torch, then feature mode, equals the library's own elu + 1 path."""
     B, H, N, D, M = 2, 2, 300, 64, 32

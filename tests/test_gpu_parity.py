@@ -280,6 +280,19 @@ def test_long_workload():
     check_backward(q, k, v, do, BF16)
 
 
+@pytest.mark.parametrize("layer", [0, 8])
+def test_speech_workload_layer(layer):
+    """B=16 H=6 N=800 D=M=32 float32: one layer of the 9-layer encoder as a training step runs it, the
+    non-causal forward returning its totals and the backward taking them, every head."""
+    w = inputs.SPEECH
+    q, k, v = w.qkv(layer)
+    do = w.grad_out(layer)
+    o = binding.forward_noncausal(dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert rowerr(host(o), oracle.forward_noncausal(q, k, v)) <= 1e-4
+    check_backward_noncausal(q, k, v, do, F32, totals=True)
+
+
 def test_decode_workload_sampled():
     """Batch 256, 16 heads, D=M=64, bf16 I/O: a 512-token prefill then 512 decode steps; every step's y and
     the final state are checked on 32 sampled heads (the oracle follows those heads only)."""
