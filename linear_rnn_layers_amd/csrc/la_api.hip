@@ -30,8 +30,8 @@ int fail(int status, const std::string& msg) {
 
 // ------------------------------------------------------------------ plan
 // The sequence of each head is cut into segments of L tokens, a multiple of
-// 64, so that about 1024 workgroups exist (four per compute unit) even when
-// B*H is small: the aggregate, forward and reverse-aggregate kernels keep
+// 64, so that about 512 or 1024 workgroups exist (two to four per compute
+// unit) even when B*H is small: the aggregate, forward and reverse-aggregate kernels keep
 // several workgroups resident per compute unit to hide their memory and LDS
 // latency.  Segment boundaries are the checkpoint entries.  The backward,
 // whose workgroup fills most of a compute unit's LDS, walks coarser segments
@@ -46,23 +46,36 @@ struct Plan {
 };
 
 constexpr long kCUs = 256;          // compute units of one MI355X
-constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels (causal ops)
-// The non-causal ops (no running state between segments, only totals that
-// every workgroup needs) and the decayed recurrence (no grouping of segments
-// in its backward) do better with about half as many, longer segments
+constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels: finer plan
+// About half as many, longer segments: fewer aggregates to sum or scan and
+// less set-up per token.  The non-causal ops (no running state between
+// segments, only totals that every workgroup needs) and the decayed
+// recurrence (no grouping of segments in its backward) always plan this way
 // (measured: 800-frame speech encoder 26.7 -> 28.9 M tokens/s, gated 2^16
-// sequence 72.0 -> 75.9 M tokens/s).  Never more segments than the causal
-// plan, so la_checkpoint_size bounds the decayed checkpoint too.
+// sequence 72.0 -> 75.9 M tokens/s), and so do the causal ops except on short
+// sequences of small states (measured per step: 16-layer 3072-token stack
+// 927 -> 889 us, 2^16-token sequence 709 -> 691 us, 784-token layer with 64
+// features 186 -> 180 us; the 784-token layer at D = M = 32 keeps the finer
+// plan, 96 against 101 us, its aggregate kernels running four to five
+// workgroups per compute unit over only a few segments per head).
 constexpr long kFineTargetNC = 512;
+
+// The causal ops' target; never below the other ops', so la_checkpoint_size
+// bounds the decayed recurrence's checkpoint too.
+long causal_target(long nchunks, int D, int M) {
+  return nchunks <= 16 && (long)D * M <= 1024 ? kFineTarget : kFineTargetNC;
+}
 
 std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
 
-Plan make_plan(int B, int H, int N, int D, int M, long target = kFineTarget) {
+// target 0: the causal ops' rule
+Plan make_plan(int B, int H, int N, int D, int M, long target = 0) {
   Plan p;
   p.BH = (long)B * H;
   p.N = N;
   p.SV = D * M + D;
   const long nchunks = ((long)N + la::CH - 1) / la::CH;
+  if (target <= 0) target = causal_target(nchunks, D, M);
   if (N <= 0) {
     p.L = la::CH;
     p.nseg = 0;
@@ -635,7 +648,7 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
   if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
   const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
                   op == LA_OP_BWD_DECAY;
-  return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : kFineTarget)).bytes();
+  return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : 0)).bytes();
 }
 
 size_t la_checkpoint_size(int B, int H, int N, int D, int M) {
@@ -666,7 +679,7 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
@@ -735,13 +748,13 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
     st = check_ptrs({rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                      rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true)});
     if (st) return st;
-    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
+    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
     LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
                 dZ0, N, ws, fm, (hipStream_t)stream);
   }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : kFineTarget);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
   const size_t es = esize(dtype);
   const size_t need = ws_layout(logA ? LA_OP_BWD_DECAY : LA_OP_BWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0 && (logA || ckpt == nullptr || p.nseg > 1);

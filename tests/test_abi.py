@@ -196,11 +196,14 @@ def test_decode_validation(lib):
     assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 0, 64, 64, 1, 0, None) == SHAPE
 
 
-def _plan(B, H, N, target=1024):
-    """The segment plan, restated: about `target` segments over all heads (1024 for the causal ops, 512 for
-    the non-causal ones), each of whole 64-token chunks."""
+def _plan(B, H, N, target=None, D=32, M=32):
+    """The segment plan, restated: about `target` segments over all heads, each of whole 64-token chunks
+    (512 for the non-causal ops and the decayed recurrence; for the causal ops 1024 when a head has at most
+    16 chunks and D*M <= 1024, else 512)."""
     bh = B * H
     nch = -(-N // 64)
+    if target is None:
+        target = 1024 if nch <= 16 and D * M <= 1024 else 512
     segs = max(1, min(nch, -(-target // bh)))
     L = -(-nch // segs) * 64
     return L, -(-N // L)
@@ -209,7 +212,7 @@ def _plan(B, H, N, target=1024):
 @pytest.mark.parametrize("B,H,N,D,M", [(1, 1, 64, 32, 32), (16, 8, 784, 32, 32), (4, 8, 3072, 32, 32),
                                         (1, 16, 65536, 64, 64), (3, 5, 1000, 64, 32), (1, 1, 1, 32, 64)])
 def test_plan_and_sizes(lib, B, H, N, D, M):
-    L, nseg = _plan(B, H, N)
+    L, nseg = _plan(B, H, N, D=D, M=M)
     assert lib.la_segment_length(B, H, N, D, M) == L
     sv = D * M + D
     assert lib.la_checkpoint_size(B, H, N, D, M) == B * H * (nseg + 1) * sv * 4
