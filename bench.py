@@ -575,6 +575,7 @@ def main():
         binding.prof_select(name)
         for _ in range(nprobe):
             step()
+        torch.cuda.synchronize()
         ms, n, _ = binding.prof_collect()
         if n:
             probe[name] = {"ms_per_step": ms / nprobe, "launches_per_step": n / nprobe}

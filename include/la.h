@@ -288,9 +288,10 @@ const char *la_last_error(void);
  * Kernel timing hooks for measurement.  la_prof_select(name) makes every
  * later launch of the kernel `name` (see la_kernel_names) be bracketed by a
  * pair of HIP events recorded on the launch stream; NULL or "" stops it.
- * la_prof_collect waits for the recorded events, returns the summed
- * duration in milliseconds and the number of launches, and clears the
- * record.  Up to 65536 launches are recorded; later ones are counted in
+ * The events are timing-only (no system-scope fence): synchronise the
+ * device (or the stream) before la_prof_collect, which then reads them and
+ * returns the summed duration in milliseconds and the number of launches,
+ * and clears the record.  Up to 65536 launches are recorded; later ones are counted in
  * `dropped`.  Not thread-safe with concurrent launches of the selected
  * kernel on several host threads.
  */

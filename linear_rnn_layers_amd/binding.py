@@ -425,6 +425,9 @@ def prof_select(name: str | None):
 
 
 def prof_collect():
+    """(summed ms, launches, dropped) of the selected kernel since the last collect; synchronises the device
+    first (the library's timing events carry no fence of their own)."""
+    torch.cuda.synchronize()
     ms = ctypes.c_double()
     n = ctypes.c_int()
     dropped = ctypes.c_int()
