@@ -45,12 +45,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; decode: 4096)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed warm-up steps (default 10; decode: 256)")
     ap.add_argument("--workload", default="mnist", choices=["mnist", "cifar", "long", "long-decay", "mnist-rf", "speech", "decode",
                                                             "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--eager-decode", action="store_true",
+                    help="decode: one host launch per step instead of replaying captured graphs of 64 steps")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (traffic-counter calibration)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="write profiles/<label>_kernels.md from a "
@@ -62,7 +64,12 @@ def parse():
                          "and the kernel statistics of a --kernel-trace --stats run")
     ap.add_argument("--label", default="mnist")
     ap.add_argument("--command", default="", help="the command that produced the CSVs (recorded in the summary)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.steps is None:
+        a.steps = 4096 if a.workload == "decode" else 50
+    if a.warmup is None:
+        a.warmup = 256 if a.workload == "decode" else 10
+    return a
 
 
 # ------------------------------------------------------------------ steps
@@ -170,6 +177,43 @@ class Step:
                        stream)
                       for i in range(pool)]
         self.i = 0
+        # A decode loop issues one small launch per step, so the host's launch cost shows between steps; a
+        # serving loop captures its steps in HIP graphs.  Graph g replays steps 64 g .. 64 g + 63 of the pool
+        # (64 launches back to back; the captured calls are the same C-ABI entry point on torch's capture
+        # stream).
+        self.graphs = []
+        if not getattr(self.args, "eager_decode", False):
+            for g0 in range(0, pool, DECODE_GRAPH):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                    for a in self._args[g0:g0 + DECODE_GRAPH]:
+                        st = self._call(*(a[:-1] + (cs,)))
+                        if st != 0:
+                            raise b.LAError(st, "la_decode_step")
+                self.graphs.append(g)
+            torch.cuda.synchronize()
+        self.gi = 0
+
+    def run(self, n, events=None):
+        """n steps: whole graphs of DECODE_GRAPH decode steps where captured (events: a list that receives a
+        (start, end) pair of timing events around every replay), the rest one launch at a time."""
+        if self.graphs:
+            torch = self.torch
+            for _ in range(n // DECODE_GRAPH):
+                g = self.graphs[self.gi % len(self.graphs)]
+                self.gi += 1
+                if events is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    events.append((e0, e1))
+                else:
+                    g.replay()
+            n %= DECODE_GRAPH
+        for _ in range(n):
+            self()
 
     def __call__(self):
         wl, b = self.args.workload, self.b
@@ -224,6 +268,9 @@ class Step:
         b = self.b
         b.la_forward_causal(q, k, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f)
         b.la_backward_causal(q, k, v, self.o, self.den, do, self.dq, self.dk, self.dv, ckpt=self.ck, ws=self.ws_b)
+
+
+DECODE_GRAPH = 64  # decode steps per captured graph
 
 
 def WORKLOADS(inputs):
@@ -564,8 +611,12 @@ def main():
     w = step.w
     s = 4 if w.dtype == "f32" else 2
     names = binding.kernel_names()
-    for _ in range(args.warmup):
-        step()
+    graphs = args.workload == "decode" and bool(step.graphs)
+    if graphs:
+        step.run(args.warmup)
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
 
     # per-kernel durations over a few untimed steps, to find the dominant kernel
@@ -584,16 +635,24 @@ def main():
 
     # timed region: exactly `steps` steps between synchronisations; the library records a pair of
     # HIP events on the launch stream around every launch of the dominant kernel
-    if not args.no_kernel_events:
+    # (decode with graphs: a pair of events around every graph replay instead; the per-launch duration is then
+    # the replay time over its 64 back-to-back launches, gaps included)
+    gev = [] if graphs and not args.no_kernel_events else None
+    if not args.no_kernel_events and not graphs:
         binding.prof_select(dominant)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    if graphs:
+        step.run(args.steps, gev)
+    else:
+        for _ in range(args.steps):
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kms, kn, dropped = binding.prof_collect()
     binding.prof_select(None)
+    if gev:
+        kms, kn = sum(e0.elapsed_time(e1) for e0, e1 in gev), len(gev) * DECODE_GRAPH
     el = t1 - t0
     ms_per_step = el * 1e3 / args.steps
 
@@ -622,6 +681,8 @@ def main():
         roof = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS if achieved else None, "traffic": traffic,
                 "algorithmic_bytes_per_launch": byts, "avg_launch_us": avg_s * 1e6, "launches": kn}
+        if gev:
+            roof["timing"] = f"events around each replay of a graph of {DECODE_GRAPH} launches, divided by {DECODE_GRAPH}"
         fl = kernel_flops(dominant, w)
         if fl:
             roof["useful_tflops"] = fl / avg_s / 1e12
@@ -653,6 +714,7 @@ def main():
         cfg["layers"] = 9
     elif args.workload == "decode":
         cfg["step"] = "one decode step of all B*H heads after a 512-token prefill"
+        cfg["launch"] = f"HIP graphs of {DECODE_GRAPH} steps" if graphs else "one host launch per step"
     else:
         cfg["step"] = "causal forward"
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,

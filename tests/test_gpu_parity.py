@@ -293,6 +293,40 @@ def test_speech_workload_layer(layer):
     check_backward_noncausal(q, k, v, do, F32, totals=True)
 
 
+def test_decode_graph_replay():
+    """Decode steps captured in a HIP graph, as a serving loop runs them, then replayed three times with eager
+    work and synchronisations between the replays: every replay equals the eager launches bit for bit (y of
+    every step, the final S and Z)."""
+    B, H, D, M, P, T = 4, 3, 64, 64, 100, 12
+    q, k, v = _qkv(B, H, P, D, M, BF16, 9600)
+    out = gpu_forward(q, k, v, BF16)
+    s0, z0 = out["s"].clone(), out["z"].clone()
+    steps = [tuple(dev(inputs.gaussian(shape, 9610 + 3 * t + i, 1.0, BF16), BF16)
+                   for i, shape in enumerate(((B, H, D), (B, H, D), (B, H, M)))) for t in range(T)]
+    se, ze = s0.clone(), z0.clone()
+    ye = torch.empty((T, B, H, M), dtype=torch.bfloat16, device="cuda")
+    for t, (qt, kt, vt) in enumerate(steps):
+        binding.la_decode_step(qt, kt, vt, se, ze, ye[t])
+    torch.cuda.synchronize()
+    sg, zg = s0.clone(), z0.clone()
+    yg = torch.empty_like(ye)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t, (qt, kt, vt) in enumerate(steps):
+            binding.la_decode_step(qt, kt, vt, sg, zg, yg[t])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        sg.copy_(s0)
+        zg.copy_(z0)
+        yg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye), f"replay {rep}: y differs"
+        assert torch.equal(sg, se) and torch.equal(zg, ze), f"replay {rep}: state differs"
+        (torch.randn(1000, device="cuda") * 2).sum().item()  # unrelated eager work between replays
+
+
 def test_decode_workload_sampled():
     """Batch 256, 16 heads, D=M=64, bf16 I/O: a 512-token prefill then 512 decode steps; every step's y and
     the final state are checked on 32 sampled heads (the oracle follows those heads only)."""
