@@ -558,13 +558,20 @@ size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
     }                                                                                              \
   } while (0)
 
+// A random-feature workgroup stages its head's projection once and walks cpw
+// consecutive chunks, cpw chosen so that about 1024 workgroups exist (the
+// projection is as large as a chunk of X, so one chunk per workgroup would
+// stage twice the data it maps).
 template <typename T, int DIN, int C>
 int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const void* dPhi, void* out, hipStream_t s) {
-  const dim3 grid((unsigned)(BH * ((N + la::CH - 1) / la::CH)));
+  const long nch = (N + la::CH - 1) / la::CH;
+  long cpw = (BH * nch + 1023) / 1024;
+  cpw = cpw < 1 ? 1 : cpw > nch ? nch : cpw;
+  const dim3 grid((unsigned)(BH * ((nch + cpw - 1) / cpw)));
   if (dPhi)
     return launch("feat_rf_vjp", la::k_feat_rf_vjp<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W,
-                  (const T*)dPhi, (T*)out, N, H);
-  return launch("feat_rf", la::k_feat_rf<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H);
+                  (const T*)dPhi, (T*)out, N, H, (int)cpw);
+  return launch("feat_rf", la::k_feat_rf<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H, (int)cpw);
 }
 
 template <typename T, int C>

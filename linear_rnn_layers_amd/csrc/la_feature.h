@@ -70,11 +70,10 @@ __device__ __forceinline__ void rf_tiles(const Planes<FPrec<T>::W, C, DIN>& wt, 
   }
 }
 
-// Stage the chunk's X rows and return |x_t|^2 for token t = 16w + r16.
+// Stage a chunk's X rows (already in registers) and return |x_t|^2 for
+// token t = 16w + r16.
 template <typename T, int DIN>
-__device__ __forceinline__ float stage_x(Planes<FPrec<T>::X, CH, DIN>& xt, float* snx, const T* X, int nv) {
-  RowBuf<T, CH, DIN> bx;
-  bx.load(X, nv);
+__device__ __forceinline__ float stage_x(Planes<FPrec<T>::X, CH, DIN>& xt, float* snx, const RowBuf<T, CH, DIN>& bx) {
   bx.stage_values(xt);
   __syncthreads();
   const int t = threadIdx.x >> 2, part = threadIdx.x & 3;  // four threads per token
@@ -94,86 +93,118 @@ __device__ __forceinline__ float stage_x(Planes<FPrec<T>::X, CH, DIN>& xt, float
   return snx[16 * (threadIdx.x >> 6) + (threadIdx.x & 15)];
 }
 
-// Random features of one 64-token chunk of one head per workgroup.
-template <typename T, int DIN, int C>
-__global__ __launch_bounds__(NT) void k_feat_rf(const T* __restrict__ X, const float* __restrict__ W,
-                                                 T* __restrict__ Phi, int N, int H) {
-  using P = FPrec<T>;
-  __shared__ Planes<P::W, C, DIN> wt;
-  __shared__ Planes<P::X, CH, DIN> xt;
-  __shared__ alignas(16) float snx[CH];
-  const int nch = (N + CH - 1) / CH;
-  const int bh = blockIdx.x / nch, c0 = (blockIdx.x % nch) * CH, nv = min(CH, N - c0);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  stage_w<P::W, C, DIN>(wt, W + (size_t)(bh % H) * C * DIN);
-  const float nx = stage_x<T, DIN>(xt, snx, X + ((size_t)bh * N + c0) * DIN, nv);
-  f32x4_t acc[C / 16];
-  rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
-  const int t = 16 * w + r16;
-  if (t < nv) {
-#pragma unroll
-    for (int cb = 0; cb < C / 16; ++cb) {
-      const float o[4] = {acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]};
-      IO<T>::store4(Phi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g, o);
-    }
+// Walk chunks ch0 .. ch1-1 of head bh: each chunk's X rows are read into
+// registers one chunk ahead (two buffers, alternating), then `body(ci, nx)`
+// runs with the chunk staged in xt.
+template <typename T, int DIN, typename Body>
+__device__ __forceinline__ void walk_chunks(Planes<FPrec<T>::X, CH, DIN>& xt, float* snx, const T* Xh, int N,
+                                            int ch0, int ch1, Body&& body) {
+  RowBuf<T, CH, DIN> b0, b1;
+  b0.load(Xh + (size_t)ch0 * CH * DIN, min(CH, N - ch0 * CH));
+  auto one = [&](RowBuf<T, CH, DIN>& cur, RowBuf<T, CH, DIN>& nxt, int ci) {
+    if (ci + 1 < ch1) nxt.load(Xh + (size_t)(ci + 1) * CH * DIN, min(CH, N - (ci + 1) * CH));
+    if (ci > ch0) __syncthreads();  // the previous chunk's reads of xt and snx are done
+    body(ci, stage_x<T, DIN>(xt, snx, cur));
+  };
+  for (int ci = ch0; ci < ch1; ci += 2) {
+    one(b0, b1, ci);
+    if (ci + 1 < ch1) one(b1, b0, ci + 1);
   }
 }
 
-// dX = W^T (dPhi * phi) - x (dPhi . phi) for one 64-token chunk of one head.
+// Random features of `cpw` consecutive 64-token chunks of one head per
+// workgroup (W staged once for all of them).
 template <typename T, int DIN, int C>
-__global__ __launch_bounds__(NT) void k_feat_rf_vjp(const T* __restrict__ X, const float* __restrict__ W,
-                                                     const T* __restrict__ dPhi, T* __restrict__ dX, int N, int H) {
+__global__ __launch_bounds__(NT) void k_feat_rf(const T* __restrict__ X, const float* __restrict__ W,
+                                                 T* __restrict__ Phi, int N, int H, int cpw) {
   using P = FPrec<T>;
   __shared__ Planes<P::W, C, DIN> wt;
   __shared__ Planes<P::X, CH, DIN> xt;
   __shared__ alignas(16) float snx[CH];
-  const int nch = (N + CH - 1) / CH;
-  const int bh = blockIdx.x / nch, c0 = (blockIdx.x % nch) * CH, nv = min(CH, N - c0);
+  const int nch = (N + CH - 1) / CH, ngr = (nch + cpw - 1) / cpw;
+  const int bh = blockIdx.x / ngr, ch0 = (blockIdx.x % ngr) * cpw, ch1 = min(nch, ch0 + cpw);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   stage_w<P::W, C, DIN>(wt, W + (size_t)(bh % H) * C * DIN);
-  const float nx = stage_x<T, DIN>(xt, snx, X + ((size_t)bh * N + c0) * DIN, nv);
-  f32x4_t acc[C / 16];
-  rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
   const int t = 16 * w + r16;
-  const bool ok = t < nv;
-  // G = dPhi * phi in the same layout, and its sum over the features
-  float sg = 0.f;
+  walk_chunks<T, DIN>(xt, snx, X + (size_t)bh * N * DIN, N, ch0, ch1, [&](int ci, float nx) {
+    const int c0 = ci * CH;
+    f32x4_t acc[C / 16];
+    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
+    if (t < N - c0) {
 #pragma unroll
-  for (int cb = 0; cb < C / 16; ++cb) {
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      if constexpr (sizeof(T) == 4) {
-        const float4 a = *reinterpret_cast<const float4*>(dPhi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g);
-        d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(dPhi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g);
-        d[0] = lo2f(u.x); d[1] = hi2f(u.x); d[2] = lo2f(u.y); d[3] = hi2f(u.y);
+      for (int cb = 0; cb < C / 16; ++cb) {
+        const float o[4] = {acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]};
+        IO<T>::store4(Phi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g, o);
       }
     }
+  });
+}
+
+// dX = W^T (dPhi * phi) - x (dPhi . phi) for `cpw` consecutive 64-token chunks
+// of one head per workgroup.
+template <typename T, int DIN, int C>
+__global__ __launch_bounds__(NT) void k_feat_rf_vjp(const T* __restrict__ X, const float* __restrict__ W,
+                                                     const T* __restrict__ dPhi, T* __restrict__ dX, int N, int H,
+                                                     int cpw) {
+  using P = FPrec<T>;
+  __shared__ Planes<P::W, C, DIN> wt;
+  __shared__ Planes<P::X, CH, DIN> xt;
+  __shared__ alignas(16) float snx[CH];
+  const int nch = (N + CH - 1) / CH, ngr = (nch + cpw - 1) / cpw;
+  const int bh = blockIdx.x / ngr, ch0 = (blockIdx.x % ngr) * cpw, ch1 = min(nch, ch0 + cpw);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  stage_w<P::W, C, DIN>(wt, W + (size_t)(bh % H) * C * DIN);
+  const int t = 16 * w + r16;
+  walk_chunks<T, DIN>(xt, snx, X + (size_t)bh * N * DIN, N, ch0, ch1, [&](int ci, float nx) {
+    const int c0 = ci * CH;
+    const bool ok = t < N - c0;
+    // dPhi of the wave's token, four consecutive features per lane, read
+    // before the projection so that the loads overlap it
+    float d[C / 16][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      acc[cb][r] *= d[r];
-      sg += acc[cb][r];
+    for (int cb = 0; cb < C / 16; ++cb) {
+      d[cb][0] = d[cb][1] = d[cb][2] = d[cb][3] = 0.f;
+      if (ok) {
+        if constexpr (sizeof(T) == 4) {
+          const float4 a = *reinterpret_cast<const float4*>(dPhi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g);
+          d[cb][0] = a.x; d[cb][1] = a.y; d[cb][2] = a.z; d[cb][3] = a.w;
+        } else {
+          const uint2 u = *reinterpret_cast<const uint2*>(dPhi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g);
+          d[cb][0] = lo2f(u.x); d[cb][1] = hi2f(u.x); d[cb][2] = lo2f(u.y); d[cb][3] = hi2f(u.y);
+        }
+      }
     }
-  }
-  sg = sum_over_g(sg);
-  Frag<P::G> gf[C / 32];
+    f32x4_t acc[C / 16];
+    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
+    // G = dPhi * phi in the same layout, and its sum over the features
+    float sg = 0.f;
 #pragma unroll
-  for (int p = 0; p < C / 32; ++p) gf[p] = acc2frag<P::G>(acc[2 * p], acc[2 * p + 1]);
+    for (int cb = 0; cb < C / 16; ++cb) {
 #pragma unroll
-  for (int d0 = 0; d0 < DIN / 16; ++d0) {
-    f32x4_t a = zero4();
-#pragma unroll
-    for (int p = 0; p < C / 32; ++p) mmaf<P::W, P::G>(a, wt.template tfrag_acc<P::W>(32 * p, 16 * d0, g, r16), gf[p]);
-    float xv[4];
-    xt.get4(t, 16 * d0 + 4 * g, xv);
-    if (ok) {
-      float o[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = a[r] - xv[r] * sg;
-      IO<T>::store4(dX + ((size_t)bh * N + c0 + t) * DIN + 16 * d0 + 4 * g, o);
+      for (int r = 0; r < 4; ++r) {
+        acc[cb][r] *= d[cb][r];
+        sg += acc[cb][r];
+      }
     }
-  }
+    sg = sum_over_g(sg);
+    Frag<P::G> gf[C / 32];
+#pragma unroll
+    for (int p = 0; p < C / 32; ++p) gf[p] = acc2frag<P::G>(acc[2 * p], acc[2 * p + 1]);
+#pragma unroll
+    for (int d0 = 0; d0 < DIN / 16; ++d0) {
+      f32x4_t a = zero4();
+#pragma unroll
+      for (int p = 0; p < C / 32; ++p) mmaf<P::W, P::G>(a, wt.template tfrag_acc<P::W>(32 * p, 16 * d0, g, r16), gf[p]);
+      float xv[4];
+      xt.get4(t, 16 * d0 + 4 * g, xv);
+      if (ok) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = a[r] - xv[r] * sg;
+        IO<T>::store4(dX + ((size_t)bh * N + c0 + t) * DIN + 16 * d0 + 4 * g, o);
+      }
+    }
+  });
 }
 
 // Degree-2 polynomial features, one thread per token (rows = B H N).

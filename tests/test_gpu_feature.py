@@ -72,6 +72,22 @@ def test_random_features(Din, C, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
+def test_random_features_several_chunks_per_workgroup(dtype):
+    """2 x 2 heads of 38417 tokens (601 chunks, the last of 17 tokens): about 2404 chunks over about 1024
+    workgroups, so each workgroup maps three chunks of one head with the projection staged once, and the
+    last workgroup of every head a single ragged chunk."""
+    B, H, N, Din, C = 2, 2, 38417, 32, 64
+    x = _x((B, H, N, Din), 14050, 0.3, dtype)
+    w = _w(H, C, Din, 14051)
+    dphi = _x((B, H, N, C), 14052, 1.0, dtype)
+    phi = binding.feature_random(dev(x, dtype), dev32(w))
+    dx = binding.feature_random_vjp(dev(x, dtype), dev32(w), dev(dphi, dtype))
+    torch.cuda.synchronize()
+    assert rowerr(host(phi), oracle.feature_performer(x, w)) <= TOL[dtype]
+    assert rowerr(host(dx), oracle.feature_performer_vjp(x, w, dphi)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
 @pytest.mark.parametrize("Din,C", [(3, 32), (5, 32), (7, 64), (4, 64)])
 def test_poly2_features(Din, C, dtype):
     B, H, N = 2, 3, 150
