@@ -1184,7 +1184,6 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   __shared__ Planes<P::NDO, CH, M> ot;               // dO
   __shared__ Planes<P::NG, CH, M + 16> gt;           // [g | c | 0]
   __shared__ Planes<P::NS, D, M> sp;                 // S total, [d][m]
-  __shared__ alignas(16) float q32[CH][D + 4];       // phi(Q), float32
   __shared__ alignas(16) float sZ[D];                // Z total
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
@@ -1218,7 +1217,7 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& d_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
-    q_.template stage_phi<cmax(P::NQ, P::dR), CH, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
+    q_.template stage_phi<cmax(P::NQ, P::dR), CH, D, 8>(qt, nv, nullptr, fm);
     d_.stage_values(ot);
     fetch(q_, d_, c0 + 2 * CH);
     __syncthreads();
@@ -1240,9 +1239,11 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
       float pu = 0.f, pz = 0.f, qv[DB][4], zv[DB][4];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
+        // phi(Q) as the sum of its planes (float32 level with three, 2^-16
+        // relative with two); den and O.dO below are formed from these same
+        // values, so the cancellation in dphiQ stays exact
+        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
         const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
-        qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
         zv[d0][0] = z4.x; zv[d0][1] = z4.y; zv[d0][2] = z4.z; zv[d0][3] = z4.w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
