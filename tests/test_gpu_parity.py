@@ -293,6 +293,69 @@ def test_speech_workload_layer(layer):
     check_backward_noncausal(q, k, v, do, F32, totals=True)
 
 
+def test_beyond_32bit_offsets_constant_values():
+    """One head of 2^25 + 17 tokens at D = M = 64 bf16 (2^31 elements per tensor, so element offsets pass
+    2^31) with every V row equal to one vector v: properties that hold at any size, since the attention
+    weights of a row are positive and sum to one.  Causal and non-causal O equal v; the final state is
+    S_N = Z_N v^T; dQ and dK vanish (O no longer depends on Q, K) up to rounding of the terms that cancel,
+    bounded per row from cumulative sums of scalars: |dphiQ_i| <= |v| |dO_i| / min_d phi(Q_i)_d and
+    |dphiK_j| <= sum_{i >= j} max_d phi(Q_i)_d |v| |dO_i| / den_i with den_i >= min_d phi(Q_i)_d sum_d Z_i,d;
+    column sums of dV equal those of dO.  Inputs drawn on the GPU (seeded Philox), Q and K ~ N(0, 1/64)."""
+    N, D, M = (1 << 25) + 17, 64, 64
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9700)
+    bf = torch.bfloat16
+    q = (torch.randn((1, 1, N, D), generator=gen, device="cuda") / 8).to(bf)
+    k = (torch.randn((1, 1, N, D), generator=gen, device="cuda") / 8).to(bf)
+    v0 = torch.randn((M,), generator=gen, device="cuda").to(bf)
+    v = v0.expand(1, 1, N, M).contiguous()
+    do = torch.randn((1, 1, N, M), generator=gen, device="cuda").to(bf)
+    out = binding.forward_causal(q, k, v, return_state=True)
+    o_nc = binding.forward_noncausal(q, k, v)
+    dq, dk, dv = binding.backward_causal(q, k, v, out["o"], out["den"], do, ckpt=out["ckpt"])
+    torch.cuda.synchronize()
+    vf = v0.double()
+    vn = vf.norm()
+
+    def chunks(n=1 << 22):
+        return [(a, min(N, a + n)) for a in range(0, N, n)]
+
+    err_o = err_nc = 0.0
+    for a, b in chunks():
+        err_o = max(err_o, float((out["o"][0, 0, a:b].double() - vf).abs().max()))
+        err_nc = max(err_nc, float((o_nc[0, 0, a:b].double() - vf).abs().max()))
+    assert max(err_o, err_nc) <= 2e-2 * float(vf.abs().max()), (err_o, err_nc)
+    s_n, z_n = out["s"][0, 0].double(), out["z"][0, 0].double()
+    assert float((s_n - torch.outer(z_n, vf)).abs().max()) <= 2e-2 * float(s_n.abs().max())
+    # per-token scalars for the bounds, float64
+    pq_min = torch.empty(N, dtype=torch.float64, device="cuda")
+    pq_max = torch.empty_like(pq_min)
+    pk_sum = torch.empty_like(pq_min)
+    don = torch.empty_like(pq_min)
+    phi = lambda x: torch.where(x > 0, x + 1, torch.exp(x))  # noqa: E731
+    for a, b in chunks():
+        pq = phi(q[0, 0, a:b].double())
+        pq_min[a:b], pq_max[a:b] = pq.min(-1).values, pq.max(-1).values
+        pk_sum[a:b] = phi(k[0, 0, a:b].double()).sum(-1)
+        don[a:b] = do[0, 0, a:b].double().norm(dim=-1)
+    tq = vn * don / pq_min
+    den_lb = pq_min * torch.cumsum(pk_sum, 0)
+    tk = torch.flip(torch.cumsum(torch.flip(pq_max * vn * don / den_lb, [0]), 0), [0])
+    rq = rk = 0.0
+    for a, b in chunks():
+        rq = max(rq, float((dq[0, 0, a:b].double().abs().max(-1).values / tq[a:b]).max()))
+        rk = max(rk, float((dk[0, 0, a:b].double().abs().max(-1).values / tk[a:b]).max()))
+    assert rq <= 1e-3 and rk <= 1e-3, (rq, rk)
+    sdv = torch.zeros(M, dtype=torch.float64, device="cuda")
+    sdo, sdo_abs = torch.zeros_like(sdv), torch.zeros_like(sdv)
+    for a, b in chunks():
+        sdv += dv[0, 0, a:b].double().sum(0)
+        x = do[0, 0, a:b].double()
+        sdo += x.sum(0)
+        sdo_abs += x.abs().sum(0)
+    assert float(((sdv - sdo).abs() / sdo_abs).max()) <= 2e-2
+
+
 def test_decode_graph_replay():
     """Decode steps captured in a HIP graph, as a serving loop runs them, then replayed three times with eager
     work and synchronisations between the replays: every replay equals the eager launches bit for bit (y of
