@@ -113,6 +113,19 @@ int la_segment_length(int B, int H, int N, int D, int M);
  * for a negative argument. */
 int la_set_segment_chunks(int chunks);
 
+/* Process-wide choice between the two forms of the causal forward without a
+ * decay.  The one-launch form serves segments of at most four chunks (when
+ * every workgroup sums the earlier aggregates itself): each workgroup walks
+ * its segment from a zero state, publishes the segment's aggregate, and adds
+ * the sum of the earlier segments' aggregates to its rows at the end.  The
+ * two-launch form runs a separate aggregate pass first.  Both compute eq.
+ * 9-12; results differ only in rounding.  mode 0: always two launches; 1 (the
+ * default): one launch where the segments allow it and D*M >= 2048 (where it
+ * measured faster); 2: one launch wherever the segments allow it.  It exists
+ * to test both forms and to measure them.  Returns the previous mode, or -1
+ * for a mode outside 0..2. */
+int la_set_forward_onepass(int mode);
+
 /*
  * Causal forward, eq. 9-12 ("Transformers are RNNs -- part 2/3", section 3.3).
  *   Q, K, V     inputs.

@@ -24,7 +24,7 @@ LA_FEATURE_ELU1, LA_FEATURE_IDENTITY = 0, 1
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
                 "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
                 "la_status_string", "la_last_error", "la_prof_select", "la_prof_collect", "la_kernel_names",
-                "la_set_segment_chunks", "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
+                "la_set_segment_chunks", "la_set_forward_onepass", "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
                 "la_feature_poly2_vjp")
 
 _lib = None
@@ -80,6 +80,8 @@ def load(path: str | None = None):
     lib.la_kernel_names.restype = ctypes.c_char_p
     lib.la_set_segment_chunks.restype = i
     lib.la_set_segment_chunks.argtypes = [i]
+    lib.la_set_forward_onepass.restype = i
+    lib.la_set_forward_onepass.argtypes = [i]
     if path is None or _lib is None:
         _lib = lib
     return lib
@@ -140,6 +142,15 @@ def set_segment_chunks(chunks: int) -> int:
     prev = int(load().la_set_segment_chunks(int(chunks)))
     if prev < 0:
         raise ValueError("chunks must be >= 0")
+    return prev
+
+
+def set_forward_onepass(mode: int) -> int:
+    """Form of the causal forward: 0 always with the separate aggregate pass, 1 in one launch by the library's
+    measured rule (the default), 2 in one launch wherever the segments allow; returns the previous mode."""
+    prev = int(load().la_set_forward_onepass(int(mode)))
+    if prev < 0:
+        raise ValueError("mode must be 0, 1 or 2")
     return prev
 
 

@@ -138,13 +138,14 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 
 // Workspace regions (bytes) per operation.
 struct WsLayout {
-  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0, xseg = 0;
-  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg; }
+  size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0, xseg = 0, sync = 0;
+  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg + sync; }
 };
 
 // fwd causal: aggregates and prefix states when there is more than one
 //   segment (the prefix states go to the caller's checkpoint when given and
-//   are only formed by the scan kernel);
+//   are only formed by the scan kernel), and the one-pass forward's error
+//   word and flags;
 // fwd non-causal: aggregates and their scan (its last entry is the total);
 // bwd non-causal: both for the key side and for the reverse side;
 // bwd: aggregates and prefix states to recompute a missing checkpoint, and
@@ -158,6 +159,7 @@ WsLayout ws_layout(int op, const Plan& p) {
       if (p.nseg > 1) {
         w.agg = state_bytes(p, p.nseg);
         w.ckpt = state_bytes(p, p.nseg + 1);
+        w.sync = align256((size_t)(1 + p.BH * p.nseg) * sizeof(unsigned));
       }
       break;
     case LA_OP_FWD_NONCAUSAL:
@@ -327,12 +329,50 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
                 last_only);
 }
 
+// The one-pass forward (k_fwd_lb) can serve segments of at most four chunks
+// whose aggregates every workgroup sums itself.  It saves the aggregate pass
+// but adds a launch that clears its flags and, at the end of every
+// workgroup, the round trips of publishing and reading aggregates between
+// XCDs; it is chosen for states of D*M >= 2048, where the aggregate pass
+// costs more than that (measured per 784-token layer of 16x8 heads, float32:
+// D = 64, M = 32: 48.0 -> 40.6 us; D = M = 32: 33.4 -> 37.4 us, and 21.2 ->
+// 25.6 us per 3072-token bf16 layer of 4x8 heads, so those keep two launches).
+// la_set_forward_onepass: 0 never, 1 by this rule (default), 2 wherever the
+// segments allow.
+std::atomic<int> g_fwd_onepass{1};
+
+bool use_onepass(const Plan& p, int D, int M) {
+  const int mode = g_fwd_onepass.load(std::memory_order_relaxed);
+  if (mode == 0 || p.nseg <= 1 || p.L > 4 * la::CH || use_scan(p)) return false;
+  return mode == 2 || D * M >= 2048;
+}
+
+template <typename T, int D, int M, int NC>
+int fwd_onepass(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
+                const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, hipStream_t s) {
+  const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  unsigned* sync = reinterpret_cast<unsigned*>(region(ws, wl.agg + wl.ckpt));
+  const int nsync = (int)(1 + p.BH * p.nseg);
+  int st = launch("sync_clear", la::k_sync_clear, dim3((unsigned)std::min(64, (nsync + la::NT - 1) / la::NT)),
+                  dim3(la::NT), s, sync, nsync);
+  if (st) return st;
+  return launch("fwd_causal", la::k_fwd_lb<T, D, M, NC>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
+                (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, S0, Z0, agg, sync, ckpt, S_out, Z_out, N, p.L,
+                p.nseg, fm);
+}
+
 template <typename T, int D, int M>
 int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
                     const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, hipStream_t s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
+  if (use_onepass(p, D, M)) {
+    if (p.L <= 2 * la::CH)
+      return fwd_onepass<T, D, M, 2>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
+    return fwd_onepass<T, D, M, 4>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
+  }
   const float* pref = nullptr;
   float* agg = nullptr;
   float* ckw = ckpt;  // checkpoint written by the forward itself unless the scan forms it
@@ -650,7 +690,7 @@ const char* la_last_error(void) { return g_err.c_str(); }
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
          "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
-         "feat_poly2_vjp";
+         "feat_poly2_vjp,sync_clear";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
@@ -675,6 +715,11 @@ int la_segment_length(int B, int H, int N, int D, int M) {
 int la_set_segment_chunks(int chunks) {
   if (chunks < 0) return -1;
   return g_seg_chunks.exchange(chunks);
+}
+
+int la_set_forward_onepass(int mode) {
+  if (mode < 0 || mode > 2) return -1;
+  return g_fwd_onepass.exchange(mode);
 }
 
 int la_forward_causal(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,

@@ -446,6 +446,315 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   }
 }
 
+// ===================================================================== F4
+// Causal forward in one launch, for segments of at most NC chunks: the
+// aggregate pass of F1 is folded in by deferring each segment's carry.
+//
+// Workgroup b owns segment b % nseg of head b / nseg and waits only for the
+// lower-numbered workgroups of its head.  Workgroups are dispatched in order
+// of their index on each XCD, so the lowest unfinished workgroup is always
+// resident and never waits: the waits end.  (A ticket taken from a counter at
+// workgroup start would not depend on that order, but same-address atomics
+// from every workgroup serialise: measured 0.11 us per workgroup.)  The
+// workgroup walks its segment from a zero state exactly as F3 does, but
+// keeps, per chunk, the unnormalised numerators V^T A^T + S_loc^T phi(Q)^T,
+// the denominators
+// rowsum(A) + phi(Q).Z_loc and the phi(Q) fragments in registers instead of
+// writing O.  At the end (S_loc, Z_loc) is the segment aggregate (eq. 10-11
+// over the segment): it is published with a flag, the aggregates of the
+// earlier segments of the head are summed in segment order onto (S0, Z0) into
+// the carry (S_c, Z_c), and O = (num + S_c^T phi(Q)) / (den + phi(Q).Z_c),
+// since by eq. 12 the state seen by token i is S_c plus the segment's tokens
+// up to i.  Checkpoint entries and the final state are written as by F3.
+//
+// sync: [0] error flag, [1 + bh * nseg + seg] published flag; all zero at
+// launch.  Each wait is bounded: a workgroup that polls too long sets
+// the error flag and goes on, so every wave reaches the end of the kernel.
+//
+// Coherence between XCDs.  Each XCD has its own L2, so data passed between
+// workgroups must not sit in (or be read from) one of them.  The aggregates
+// and flags are therefore written and read only with relaxed atomics of
+// device ("agent") scope, which write through and read past the L2; the
+// aggregate stores are complete (waited for) before the barrier that
+// precedes the flag store, and the aggregate loads are issued after the
+// barrier that follows the flag load.  Release and acquire fences of device
+// scope would instead write back and invalidate the whole L2 of the XCD for
+// every workgroup (measured: 24 -> 119 us on the MNIST-shaped layer).
+constexpr int kLbPolls = 1 << 22;
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ void lb_wait(const unsigned* f, unsigned* err) {
+  for (int it = 0; it < kLbPolls; ++it) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  atomicOr(err, 1u);
+}
+
+template <typename T, int D, int M, int NC>
+__global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T* __restrict__ K,
+                                                const T* __restrict__ V, T* __restrict__ O,
+                                                float* __restrict__ den_out, const float* __restrict__ S0,
+                                                const float* __restrict__ Z0, float* __restrict__ agg,
+                                                unsigned* __restrict__ sync, float* __restrict__ ckpt,
+                                                float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
+                                                int nseg, int fm) {
+  using P = Prec<T>;
+  constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D, DS = D / 32;
+  using KPlanes = Planes<P::FKF, CH, D>;
+  constexpr size_t KB_ = sizeof(KPlanes), SB_ = (size_t)SV * sizeof(float);
+  __shared__ Planes<P::FQ, CH, D> qt;
+  __shared__ Planes<P::FV, CH, M> vt;
+  __shared__ Planes<P::FS, M, D> st;   // S^T: the segment's running state, then the carry
+  __shared__ Planes<P::FZ, 16, D> zr;  // 16 copies of Z
+  // phi(K) planes during the walk; the carry summed from the aggregates after it
+  __shared__ alignas(16) unsigned char kmem[SB_ > KB_ ? SB_ : KB_];
+  KPlanes& kt = *reinterpret_cast<KPlanes*>(kmem);
+  float* const sbuf = reinterpret_cast<float*>(kmem);
+
+  const int item = blockIdx.x;
+  const int seg = item % nseg, bh = item / nseg;
+  const int t0 = seg * L, t1 = min(N, t0 + L);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
+  const int db = w % DB;
+  const bool zw = w < DB;
+  const T* Qh = Q + (size_t)bh * N * D;
+  const T* Kh = K + (size_t)bh * N * D;
+  const T* Vh = V + (size_t)bh * N * M;
+  T* Oh = O + (size_t)bh * N * M;
+  const Frag<1> ones = ones_frag();
+
+  RowBuf<T, CH, D> bq[2], bk[2];
+  RowBuf<T, CH, M> bv[2];
+  auto fetch = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, D>& k_, RowBuf<T, CH, M>& v_, int c0) {
+    const int nv = min(CH, t1 - c0);
+    if (nv > 0) {
+      q_.load(Qh + (size_t)c0 * D, nv);
+      k_.load(Kh + (size_t)c0 * D, nv);
+      v_.load(Vh + (size_t)c0 * M, nv);
+    }
+  };
+  fetch(bq[0], bk[0], bv[0], t0);
+  fetch(bq[1], bk[1], bv[1], t0 + CH);
+
+  // segment state from zero (S layout); staged as S^T planes and Z rows
+  f32x4_t accS[NTW], accZ = zero4();
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) accS[k] = zero4();
+  auto stage = [&](const f32x4_t* s_, const f32x4_t& z_) {
+    float v4[4];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+      acc_to4(s_[k], v4);
+      st.put4(16 * ((w + 4 * k) / DB) + r16, 16 * db + 4 * g, v4);
+    }
+    if (zw) {
+      acc_to4(z_, v4);
+      zr.put4(r16, 16 * db + 4 * g, v4);
+    }
+  };
+  stage(accS, accZ);
+
+  // per chunk: numerators (O^T tiles), denominators and phi(Q) fragments
+  f32x4_t num[NC][MB];
+  float dl[NC];
+  Frag<P::FQ> qk[NC][DS];
+
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int c0 = t0 + c * CH;
+    if (c0 < t1) {
+      RowBuf<T, CH, D>& q_ = bq[c & 1];
+      RowBuf<T, CH, D>& k_ = bk[c & 1];
+      RowBuf<T, CH, M>& v_ = bv[c & 1];
+      const int nv = min(CH, t1 - c0);
+      __syncthreads();
+      q_.stage_phi(qt, nv, nullptr, fm);
+      k_.stage_phi(kt, nv, nullptr, fm);
+      v_.stage_values(vt);
+      if (c + 2 < NC) fetch(q_, k_, v_, c0 + 2 * CH);
+      __syncthreads();
+
+      const int il = 16 * w + r16;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qk[c][s] = qt.template frag<P::FQ>(il, 32 * s, g);
+
+      f32x4_t accA[4];
+      float dp = 0.f;  // row sum of the masked A, float32
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        f32x4_t a = zero4();
+        if (jb <= w) {
+#pragma unroll
+          for (int s = 0; s < DS; ++s)
+            mmaf<P::FK, P::FQ>(a, kt.template frag<P::FK>(16 * jb + r16, 32 * s, g), qk[c][s]);
+          if (jb == w) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * g + r > r16) a[r] = 0.f;  // A^T[j][i] with j > i is masked (eq. 8)
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dp += a[r];
+        }
+        accA[jb] = a;
+      }
+      Frag<P::FA> af[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) af[p] = acc2frag<P::FA>(accA[2 * p], accA[2 * p + 1]);
+      dp = sum_over_g(dp);
+      f32x4_t dn = zero4();
+#pragma unroll
+      for (int s = 0; s < DS; ++s) mmaf<P::FZ, P::FQ>(dn, zr.template frag<P::FZ>(r16, 32 * s, g), qk[c][s]);
+      dl[c] = dp + dn[0];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (2 * p <= w) mmaf<P::FV, P::FA>(acc, vt.template tfrag_acc<P::FV>(32 * p, 16 * mb, g, r16), af[p]);
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+          mmaf<P::FS, P::FQ>(acc, st.template frag<P::FS>(16 * mb + r16, 32 * s, g), qk[c][s]);
+        num[c][mb] = acc;
+      }
+      // S += phi(K)^T V, Z += phi(K)^T 1 (eq. 10-11)
+#pragma unroll
+      for (int s = 0; s < CH / 32; ++s) {
+        const Frag<P::FKF> ka = kt.template tfrag<P::FKF>(32 * s, 16 * db, g, r16);
+#pragma unroll
+        for (int k = 0; k < NTW; ++k) {
+          const int mb = (w + 4 * k) / DB;
+          mmaf<P::FKF, P::FV>(accS[k], ka, vt.template tfrag<P::FV>(32 * s, 16 * mb, g, r16));
+        }
+        if (zw) mmaf<P::FKF, 1>(accZ, ka, ones);
+      }
+      if (c0 + CH < t1) {
+        __syncthreads();
+        stage(accS, accZ);
+      }
+    }
+  }
+
+  // publish the segment aggregate (the last segment has no successor)
+  if (seg + 1 < nseg) {
+    float* ag = agg + (size_t)item * SV;
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+      const int t = w + 4 * k, mb = t / DB;
+      float* e = ag + (16 * db + 4 * g) * M + 16 * mb + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_dev(e + r * M, accS[k][r]);
+    }
+    if (zw && r16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_dev(ag + D * M + 16 * db + 4 * g + r, accZ[r]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);  // every aggregate store acknowledged
+  }
+  __syncthreads();  // aggregate written; phi(K) planes, st and zr no longer read
+  if (seg + 1 < nseg && tid == 0) __hip_atomic_store(&sync[1 + item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // carry: (S0, Z0) plus the earlier segments' aggregates, in segment order
+  for (int p = tid; p < seg; p += NT) lb_wait(&sync[1 + (size_t)bh * nseg + p], &sync[0]);
+  __syncthreads();
+  {
+    const float* a0 = agg + (size_t)bh * nseg * SV;
+    const float* s0h = S0 ? S0 + (size_t)bh * D * M : nullptr;
+    const float* z0h = Z0 ? Z0 + (size_t)bh * D : nullptr;
+    constexpr int BT = 8;
+    for (int e = tid; e < SV; e += NT) {
+      float acc = 0.f;
+      if (e < D * M) {
+        if (s0h) acc = s0h[e];
+      } else if (z0h) {
+        acc = z0h[e - D * M];
+      }
+      for (int p = 0; p < seg; p += BT) {
+        float v[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) v[j] = p + j < seg ? ld_dev(a0 + (size_t)(p + j) * SV + e) : 0.f;
+#pragma unroll
+        for (int j = 0; j < BT; ++j) acc += v[j];
+      }
+      sbuf[e] = acc;
+    }
+  }
+  __syncthreads();
+  f32x4_t cS[NTW], cZ = zero4();
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) {
+    const int mb = (w + 4 * k) / DB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cS[k][r] = sbuf[(16 * db + 4 * g + r) * M + 16 * mb + r16];
+  }
+  if (zw) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cZ[r] = sbuf[D * M + 16 * db + 4 * g + r];
+  }
+  auto write_state = [&](const f32x4_t* s_, const f32x4_t& z_, float* dS, float* dZ) {
+    store_S_tiles<D, M, NTW>(dS, s_, w, r16, g);
+    if (zw && r16 == 0) *reinterpret_cast<float4*>(dZ + 16 * db + 4 * g) = make_float4(z_[0], z_[1], z_[2], z_[3]);
+  };
+  if (ckpt) {
+    float* ck = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
+    write_state(cS, cZ, ck, ck + D * M);
+  }
+  if (seg == nseg - 1 && (ckpt || S_out)) {
+    f32x4_t fS[NTW], fZ = cZ + accZ;
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) fS[k] = cS[k] + accS[k];
+    if (ckpt) {
+      float* ck = ckpt + ((size_t)bh * (nseg + 1) + nseg) * SV;
+      write_state(fS, fZ, ck, ck + D * M);
+    }
+    if (S_out) write_state(fS, fZ, S_out + (size_t)bh * D * M, Z_out + (size_t)bh * D);
+  }
+  stage(cS, cZ);
+  __syncthreads();
+
+  // O = (num + S_c^T phi(Q)) / (den + phi(Q).Z_c)
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int c0 = t0 + c * CH;
+    if (c0 < t1) {
+      const int il = 16 * w + r16;
+      const bool row_ok = il < t1 - c0;
+      f32x4_t dn = zero4();
+#pragma unroll
+      for (int s = 0; s < DS; ++s) mmaf<P::FZ, P::FQ>(dn, zr.template frag<P::FZ>(r16, 32 * s, g), qk[c][s]);
+      const float den = dl[c] + dn[0];
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x4_t acc = num[c][mb];
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+          mmaf<P::FS, P::FQ>(acc, st.template frag<P::FS>(16 * mb + r16, 32 * s, g), qk[c][s]);
+        if (row_ok) {
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = acc[r] * inv;
+          IO<T>::store4(Oh + (size_t)(c0 + il) * M + 16 * mb + 4 * g, o);
+        }
+      }
+      if (den_out && g == 0 && row_ok) den_out[(size_t)bh * N + c0 + il] = den;
+    }
+  }
+}
+
+// Clears the one-pass forward's `sync` words (n of them) before its launch.
+__global__ __launch_bounds__(NT) void k_sync_clear(unsigned* __restrict__ sync, int n) {
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) sync[i] = 0u;
+}
+
 // Prefix states from segment aggregates: pref[bh][s] = init + sum_{t<s}
 // agg[bh][t], s = 0..nseg (init = (S0, Z0) or zero), summed in segment
 // order; with last_only, only the total (entry nseg) is written.  One thread

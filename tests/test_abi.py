@@ -158,7 +158,9 @@ def test_feature_map_validation(lib):
 
 
 def test_decay_forward_validation(lib):
-    assert fwd(lib, logA=addr(14), ws_bytes=lib.la_workspace_size(0, 2, 2, 100, 32, 32, 0)) == WORKSPACE
+    need = lib.la_workspace_size(5, 2, 2, 100, 32, 32, 0)  # the decayed forward's workspace
+    assert need > 0
+    assert fwd(lib, logA=addr(14), ws_bytes=need - 1) == WORKSPACE
     assert fwd(lib, logA=addr(4)) == ALIAS  # O on top of logA
     assert fwd(lib, logA=ctypes.c_void_p(BASE + 14 * (1 << 32) + 8)) == ALIGN
 
@@ -219,9 +221,11 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
     # linear-memory bound: the checkpoint never exceeds B*H*N*max(D,M) floats by more than one state per head
     assert lib.la_checkpoint_size(B, H, N, D, M) <= 4 * B * H * (N * max(D, M) + 2 * sv)
     assert lib.la_workspace_size(3, B, H, N, D, M, 1) == 0
-    # forward: segment aggregates and their prefix scan when there is more than one segment
+    # forward: segment aggregates, their prefix scan and the one-pass form's error word and per-segment flags
+    # (32-bit words) when there is more than one segment
     agg, pref = _al(B * H * nseg * sv * 4), _al(B * H * (nseg + 1) * sv * 4)
-    assert lib.la_workspace_size(0, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref)
+    sync = _al((1 + B * H * nseg) * 4)
+    assert lib.la_workspace_size(0, B, H, N, D, M, 0) == (0 if nseg == 1 else agg + pref + sync)
     _, nseg_nc = _plan(B, H, N, 512)
     agg_nc, pref_nc = _al(B * H * nseg_nc * sv * 4), _al(B * H * (nseg_nc + 1) * sv * 4)
     assert lib.la_workspace_size(1, B, H, N, D, M, 0) == agg_nc + pref_nc
