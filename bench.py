@@ -352,6 +352,10 @@ KERNEL_TAGS = (("k_bwd<", "bwd_causal"), ("k_seg_rstate<", "seg_rstate"), ("k_se
 
 
 def kernel_tag(full_name):
+    if "k_fwd_lb<" in full_name:  # the one-launch causal forward
+        return "fwd_causal"
+    if "k_sync_clear" in full_name:
+        return "sync_clear"
     if "k_fwd<" in full_name:
         return "fwd_noncausal" if "false>" in full_name else "fwd_causal"
     for key, tag in KERNEL_TAGS:

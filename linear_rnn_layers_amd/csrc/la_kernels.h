@@ -867,29 +867,37 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = zero4();
 
-  // two chunks of global reads in flight (see k_seg_state)
+  // two chunks of global reads in flight (see k_seg_state), den of each
+  // row this thread stages included
+  using RB = RowBuf<T, CH, M>;
   RowBuf<T, CH, D> bq[2];
-  RowBuf<T, CH, M> bo[2], bd[2];
-  auto fetch = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& o_, RowBuf<T, CH, M>& d_, int c0) {
+  RB bo[2], bd[2];
+  float dn[2][RB::CNT];
+  auto fetch = [&](RowBuf<T, CH, D>& q_, RB& o_, RB& d_, float* dn_, int c0) {
     const int nv = min(CH, t1 - c0);
     if (nv > 0) {
       q_.load(Qh + (size_t)c0 * D, nv);
       o_.load(Oh + (size_t)c0 * M, nv);
       d_.load(dOh + (size_t)c0 * M, nv);
+#pragma unroll
+      for (int i = 0; i < RB::CNT; ++i) {
+        const int r = RB::row_of(i);
+        dn_[i] = r < nv ? denh[c0 + r] : 1.f;
+      }
     }
   };
-  auto chunk = [&](RowBuf<T, CH, D>& q_, RowBuf<T, CH, M>& o_, RowBuf<T, CH, M>& d_, int c0) {
+  auto chunk = [&](RowBuf<T, CH, D>& q_, RB& o_, RB& d_, float* dn_, int c0) {
     const int nv = min(CH, t1 - c0);
     __syncthreads();
     q_.stage_phi(qt, nv, nullptr, fm);
     // g and c need den (per row) and dO . O (a row reduction over PRM lanes)
 #pragma unroll
-    for (int i = 0; i < RowBuf<T, CH, M>::CNT; ++i) {
-      const int r = RowBuf<T, CH, M>::row_of(i), c = RowBuf<T, CH, M>::col_of(i);
+    for (int i = 0; i < RB::CNT; ++i) {
+      const int r = RB::row_of(i), c = RB::col_of(i);
       float xo[E], xd[E];
       IO<T>::unpack(o_.r[i], xo);
       IO<T>::unpack(d_.r[i], xd);
-      const float inv = r < nv ? 1.f / denh[c0 + r] : 0.f;
+      const float inv = r < nv ? 1.f / dn_[i] : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -901,7 +909,7 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
       gt.template put<E>(r, c, xd);
       if (c == 0) gt.put1(r, M, -part * inv);
     }
-    fetch(q_, o_, d_, c0 + 2 * CH);
+    fetch(q_, o_, d_, dn_, c0 + 2 * CH);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
@@ -914,11 +922,11 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
       if (zw) mmaf<P::dR, P::dR>(accr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
     }
   };
-  fetch(bq[0], bo[0], bd[0], t0);
-  fetch(bq[1], bo[1], bd[1], t0 + CH);
+  fetch(bq[0], bo[0], bd[0], dn[0], t0);
+  fetch(bq[1], bo[1], bd[1], dn[1], t0 + CH);
   for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
-    chunk(bq[0], bo[0], bd[0], c0);
-    if (c0 + CH < t1) chunk(bq[1], bo[1], bd[1], c0 + CH);
+    chunk(bq[0], bo[0], bd[0], dn[0], c0);
+    if (c0 + CH < t1) chunk(bq[1], bo[1], bd[1], dn[1], c0 + CH);
   }
   float* out = ragg + ((size_t)bh * nseg + seg) * SV;
   store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
