@@ -19,7 +19,9 @@ small (B=1 H=1 N=64 D=M=32 float32 causal forward).
 Prints one JSON line: throughput, the roofline of the dominant kernel (its
 duration measured with HIP events recorded by the library around every
 launch of that kernel inside the timed region), and the float64 oracle timed
-on the host cores on a bounded sample of the same workload.
+on the host cores on a bounded sample of the same workload.  After the timed
+region, untimed steps give the p10/p50/p90 of one step's duration with the
+caches as the timed loop leaves them and after a 512 MiB scrub ("step_us").
 """
 from __future__ import annotations
 
@@ -364,6 +366,36 @@ def kernel_tag(full_name):
     return full_name.split("(")[0][:60]
 
 
+def step_distribution(step, graphs, n=20):
+    """p10/p50/p90 of one step's duration (us), from HIP events on the launch stream around each step, over n
+    untimed steps: back to back as in the timed region ("warm": the step's data may still sit in the L2s and the
+    256 MB last-level cache), and with a 512 MiB buffer read and written before each step ("cold").  Decode with
+    graphs: one replay of DECODE_GRAPH steps per sample, divided by DECODE_GRAPH."""
+    import numpy as np
+    import torch
+
+    scrub = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    out = {"samples": n, "cold_scrub_bytes": scrub.numel() * 4}
+    for name, cold in (("warm", False), ("cold", True)):
+        ev = []
+        for _ in range(n):
+            if cold:
+                scrub.add_(1.0)
+            if graphs:
+                step.run(DECODE_GRAPH, ev)
+            else:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                step()
+                e1.record()
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) * 1e3 / (DECODE_GRAPH if graphs else 1) for a, b in ev])
+        out[name] = {f"p{q}": round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)}
+    del scrub
+    return out
+
+
 def summarize_stats(args):
     import csv
 
@@ -694,6 +726,7 @@ def main():
         roof["copy_gbs"] = copy
         roof["frac_of_copy"] = achieved / copy if achieved else None
 
+    dist = step_distribution(step, graphs)
     breakdown = {k: {"us_per_step": round(v["ms_per_step"] * 1e3, 2),
                      "launches_per_step": v["launches_per_step"]} for k, v in probe.items()}
     cpu = None
@@ -724,7 +757,7 @@ def main():
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if s == 4 else "bf16", "data": "synthetic", "config": cfg,
-           "roofline": roof, "cpu_baseline": cpu, "kernels_us_per_step": breakdown,
+           "roofline": roof, "cpu_baseline": cpu, "step_us": dist, "kernels_us_per_step": breakdown,
            "kernel_events_in_timed_region": not args.no_kernel_events, "events_dropped": dropped}
     print(json.dumps(out))
 
