@@ -126,6 +126,17 @@ int la_set_segment_chunks(int chunks);
  * for a mode outside 0..2. */
 int la_set_forward_onepass(int mode);
 
+/* Process-wide limit on the polls with which a workgroup of the one-launch
+ * forward waits for an earlier segment's aggregate (default 2^22, about
+ * 0.1 s).  The waits always end: workgroups are dispatched in index order and
+ * wait only for lower-numbered ones.  A workgroup that reaches the limit
+ * anyway gives up: its carry is NaN, so its rows of O and den, its checkpoint
+ * entries and (last segment) the final state are NaN rather than wrong
+ * values, and word 0 of the flag region of `ws` (after the aggregate and
+ * prefix-state regions) is set.  It exists to test that path.  Returns the
+ * previous limit, or -1 for a negative argument. */
+int la_set_wait_polls(int polls);
+
 /*
  * Causal forward, eq. 9-12 ("Transformers are RNNs -- part 2/3", section 3.3).
  *   Q, K, V     inputs.

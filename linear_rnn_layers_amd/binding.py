@@ -24,7 +24,8 @@ LA_FEATURE_ELU1, LA_FEATURE_IDENTITY = 0, 1
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
                 "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
                 "la_status_string", "la_last_error", "la_prof_select", "la_prof_collect", "la_kernel_names",
-                "la_set_segment_chunks", "la_set_forward_onepass", "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
+                "la_set_segment_chunks", "la_set_forward_onepass", "la_set_wait_polls",
+                "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
                 "la_feature_poly2_vjp")
 
 _lib = None
@@ -82,6 +83,8 @@ def load(path: str | None = None):
     lib.la_set_segment_chunks.argtypes = [i]
     lib.la_set_forward_onepass.restype = i
     lib.la_set_forward_onepass.argtypes = [i]
+    lib.la_set_wait_polls.restype = i
+    lib.la_set_wait_polls.argtypes = [i]
     if path is None or _lib is None:
         _lib = lib
     return lib
@@ -151,6 +154,14 @@ def set_forward_onepass(mode: int) -> int:
     prev = int(load().la_set_forward_onepass(int(mode)))
     if prev < 0:
         raise ValueError("mode must be 0, 1 or 2")
+    return prev
+
+
+def set_wait_polls(polls: int) -> int:
+    """Polls before a one-launch forward's wait gives up (its rows become NaN); returns the previous limit."""
+    prev = int(load().la_set_wait_polls(int(polls)))
+    if prev < 0:
+        raise ValueError("polls must be >= 0")
     return prev
 
 

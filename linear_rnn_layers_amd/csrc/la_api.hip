@@ -340,6 +340,9 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
 // la_set_forward_onepass: 0 never, 1 by this rule (default), 2 wherever the
 // segments allow.
 std::atomic<int> g_fwd_onepass{1};
+// Polls of a one-launch forward's wait for an earlier segment's flag before
+// it gives up (about 0.1 s of polling at 2^22).
+std::atomic<int> g_lb_polls{1 << 22};
 
 bool use_onepass(const Plan& p, int D, int M) {
   const int mode = g_fwd_onepass.load(std::memory_order_relaxed);
@@ -359,7 +362,7 @@ int fwd_onepass(const Plan& p, const void* Q, const void* K, const void* V, void
   if (st) return st;
   return launch("fwd_causal", la::k_fwd_lb<T, D, M, NC>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, S0, Z0, agg, sync, ckpt, S_out, Z_out, N, p.L,
-                p.nseg, fm);
+                p.nseg, fm, g_lb_polls.load(std::memory_order_relaxed));
 }
 
 template <typename T, int D, int M>
@@ -720,6 +723,11 @@ int la_set_segment_chunks(int chunks) {
 int la_set_forward_onepass(int mode) {
   if (mode < 0 || mode > 2) return -1;
   return g_fwd_onepass.exchange(mode);
+}
+
+int la_set_wait_polls(int polls) {
+  if (polls < 0) return -1;
+  return g_lb_polls.exchange(polls);
 }
 
 int la_forward_causal(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,

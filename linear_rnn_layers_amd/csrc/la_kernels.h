@@ -468,8 +468,10 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
 // up to i.  Checkpoint entries and the final state are written as by F3.
 //
 // sync: [0] error flag, [1 + bh * nseg + seg] published flag; all zero at
-// launch.  Each wait is bounded: a workgroup that polls too long sets
-// the error flag and goes on, so every wave reaches the end of the kernel.
+// launch.  Each wait is bounded: a workgroup that polls too long sets the
+// error flag, makes its carry NaN (so that its rows of O, den and the states
+// it writes show the failure instead of a wrong value) and goes on, so every
+// wave reaches the end of the kernel.
 //
 // Coherence between XCDs.  Each XCD has its own L2, so data passed between
 // workgroups must not sit in (or be read from) one of them.  The aggregates
@@ -480,7 +482,6 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
 // barrier that follows the flag load.  Release and acquire fences of device
 // scope would instead write back and invalidate the whole L2 of the XCD for
 // every workgroup (measured: 24 -> 119 us on the MNIST-shaped layer).
-constexpr int kLbPolls = 1 << 22;
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -490,12 +491,14 @@ __device__ __forceinline__ float ld_dev(const float* p) {
       __hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-__device__ __forceinline__ void lb_wait(const unsigned* f, unsigned* err) {
-  for (int it = 0; it < kLbPolls; ++it) {
-    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+// true when the flag was seen set within `polls` polls
+__device__ __forceinline__ bool lb_wait(const unsigned* f, unsigned* err, int polls) {
+  for (int it = 0; it < polls; ++it) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
     __builtin_amdgcn_s_sleep(2);
   }
   atomicOr(err, 1u);
+  return false;
 }
 
 template <typename T, int D, int M, int NC>
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
                                                 const float* __restrict__ Z0, float* __restrict__ agg,
                                                 unsigned* __restrict__ sync, float* __restrict__ ckpt,
                                                 float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
-                                                int nseg, int fm) {
+                                                int nseg, int fm, int polls) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D, DS = D / 32;
   using KPlanes = Planes<P::FKF, CH, D>;
@@ -663,8 +666,9 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
   if (seg + 1 < nseg && tid == 0) __hip_atomic_store(&sync[1 + item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // carry: (S0, Z0) plus the earlier segments' aggregates, in segment order
-  for (int p = tid; p < seg; p += NT) lb_wait(&sync[1 + (size_t)bh * nseg + p], &sync[0]);
-  __syncthreads();
+  bool late = false;
+  for (int p = tid; p < seg; p += NT) late |= !lb_wait(&sync[1 + (size_t)bh * nseg + p], &sync[0], polls);
+  const bool failed = __syncthreads_or(late);
   {
     const float* a0 = agg + (size_t)bh * nseg * SV;
     const float* s0h = S0 ? S0 + (size_t)bh * D * M : nullptr;
@@ -684,7 +688,7 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
 #pragma unroll
         for (int j = 0; j < BT; ++j) acc += v[j];
       }
-      sbuf[e] = acc;
+      sbuf[e] = failed ? __builtin_nanf("") : acc;
     }
   }
   __syncthreads();

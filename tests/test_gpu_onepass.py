@@ -76,6 +76,14 @@ def _ckpt_ref(q, k, v, L, s0=None, z0=None):
     return ref
 
 
+def _error_word(ws, B, H, N, D, M):
+    """Word 0 of the one-launch forward's flag region: after the aggregates and the prefix states of the workspace."""
+    L = binding.segment_length(B, H, N, D, M)
+    nseg, sv = -(-N // L), D * M + D
+    off = sum((x + 255) // 256 * 256 for x in (B * H * nseg * sv * 4, B * H * (nseg + 1) * sv * 4))
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
 def _check(out, q, k, v, dtype, s0=None, z0=None):
     o, den, s, z = oracle.forward_causal(q, k, v, s0, z0)
     errs = {"O": rowerr(host(out["o"]), o), "den": rowerr(host(out["den"]), den, False),
@@ -177,11 +185,51 @@ def test_onepass_reused_dirty_workspace():
         den = torch.empty((B, H, N), device="cuda")
         binding.la_forward_causal(Q, K, V, O, den, ws=ws)
         torch.cuda.synchronize()
+        assert _error_word(ws, B, H, N, D, M) == 0  # no wait gave up
         assert rowerr(host(O), ref[0]) <= 1e-4
         assert rowerr(host(den), ref[1], False) <= 1e-4
     _, launches, _ = binding.prof_collect()
     binding.prof_select(None)
     assert launches == 2
+
+
+def test_onepass_wait_limit():
+    """With the poll limit at 0 every wait gives up at once (forced from the host: no wave spins): the first segment
+    of each head needs no carry and stays exact, later segments' rows and the final state are NaN, the error word
+    is set; the next call at the normal limit is exact again."""
+    B, H, N, D, M = 2, 3, 5 * 64 + 11, 32, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 7950)
+    Q, K, V = dev(q), dev(k), dev(v)
+    o_ref, den_ref, _, _ = oracle.forward_causal(q, k, v)
+    prev_c = binding.set_segment_chunks(2)
+    try:
+        L = binding.segment_length(B, H, N, D, M)
+        ws = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, binding.dtype_code(torch.float32),
+                                     "cuda")
+        for polls in (0, 1 << 22):
+            prev_p = binding.set_wait_polls(polls)
+            try:
+                O = torch.empty((B, H, N, M), device="cuda")
+                den = torch.empty((B, H, N), device="cuda")
+                S = torch.empty((B, H, D, M), device="cuda")
+                Z = torch.empty((B, H, D), device="cuda")
+                binding.la_forward_causal(Q, K, V, O, den, S_out=S, Z_out=Z, ws=ws)
+                torch.cuda.synchronize()
+            finally:
+                binding.set_wait_polls(prev_p)
+            o, d = host(O), host(den)
+            if polls == 0:
+                assert _error_word(ws, B, H, N, D, M) == 1
+                assert rowerr(o[:, :, :L], o_ref[:, :, :L]) <= 1e-4
+                assert rowerr(d[:, :, :L], den_ref[:, :, :L], False) <= 1e-4
+                assert np.isnan(o[:, :, L:]).all() and np.isnan(d[:, :, L:]).all()
+                assert np.isnan(host(S)).all() and np.isnan(host(Z)).all()
+            else:
+                assert _error_word(ws, B, H, N, D, M) == 0
+                assert rowerr(o, o_ref) <= 1e-4
+                assert rowerr(d, den_ref, False) <= 1e-4
+    finally:
+        binding.set_segment_chunks(prev_c)
 
 
 def test_onepass_many_heads_full_shape():
