@@ -396,6 +396,25 @@ def step_distribution(step, graphs, n=20):
     return out
 
 
+def memory_report(step):
+    """Device memory the library needs beside the I/O tensors (checkpoint of segment states and workspaces), what
+    storing the state S_i of every token would take instead (B*H*N*D*M float32), and the run's peak allocation."""
+    import torch
+
+    w = step.w
+    out = {"peak_device_bytes": int(torch.cuda.max_memory_allocated())}
+    if step.args.workload == "decode":
+        return out
+    lib = 0
+    for name in ("ck", "ws_f", "ws_b", "ws_n", "ws_nb"):
+        t = getattr(step, name, None)
+        if t is not None:
+            lib += t.numel() * t.element_size()
+    d = getattr(w, "features", None) or w.D
+    out.update({"checkpoint_and_workspace_bytes": int(lib), "stored_states_bytes": w.B * w.H * w.N * d * w.M * 4})
+    return out
+
+
 def summarize_stats(args):
     import csv
 
@@ -727,6 +746,7 @@ def main():
         roof["frac_of_copy"] = achieved / copy if achieved else None
 
     dist = step_distribution(step, graphs)
+    mem = memory_report(step)
     breakdown = {k: {"us_per_step": round(v["ms_per_step"] * 1e3, 2),
                      "launches_per_step": v["launches_per_step"]} for k, v in probe.items()}
     cpu = None
@@ -757,7 +777,7 @@ def main():
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if s == 4 else "bf16", "data": "synthetic", "config": cfg,
-           "roofline": roof, "cpu_baseline": cpu, "step_us": dist, "kernels_us_per_step": breakdown,
+           "roofline": roof, "cpu_baseline": cpu, "step_us": dist, "memory": mem, "kernels_us_per_step": breakdown,
            "kernel_events_in_timed_region": not args.no_kernel_events, "events_dropped": dropped}
     print(json.dumps(out))
 
