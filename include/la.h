@@ -159,6 +159,13 @@ int la_set_wait_polls(int polls);
  *   S_out,Z_out optional final state S_N, Z_N (both or neither).
  *   ckpt        optional output of la_checkpoint_size(...) bytes: segment
  *               boundary states for la_backward_causal.  NULL to skip.
+ *   ws          la_workspace_size(LA_OP_FWD_CAUSAL, ...) bytes: segment
+ *               aggregates, their prefix states, and (one-launch form, see
+ *               la_set_forward_onepass) one 32-bit flag per segment plus an
+ *               error word, cleared by the call itself, so any contents are
+ *               accepted.  In the one-launch form the workgroups of a call
+ *               exchange segment aggregates through `ws`: calls that overlap
+ *               on one workspace race, as with any scratch buffer.
  */
 int la_forward_causal(const void *Q, const void *K, const void *V,
                       const float *logA, void *O, float *den, const float *S0,
