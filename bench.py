@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel events")
     ap.add_argument("--eager-decode", action="store_true",
                     help="decode: one host launch per step instead of replaying captured graphs of 64 steps")
+    ap.add_argument("--seq-sweep", action="store_true",
+                    help="causal forward + backward time and peak memory per sample for N = 2^9 .. 2^16 with the batch "
+                         "scaled inversely (B*N = 65536; H=16, D=M=64, bf16), one JSON line")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (traffic-counter calibration)")
     ap.add_argument("--summarize-stats", metavar="CSV", help="write profiles/<label>_kernels.md from a "
@@ -396,6 +399,66 @@ def step_distribution(step, graphs, n=20):
     return out
 
 
+def seq_sweep(args):
+    """The pages' sequence-length experiment ("Transformers are RNNs -- part 2/3", section 4.1.2, Figure 1): the
+    attention and its gradients on synthetic input for N = 2^9 .. 2^16, the batch scaled inversely with N, time and
+    peak allocated memory per sample.  Heads and widths follow the 2^16-token workload (H=16, D=M=64, bf16, inputs
+    N(0, 1/8^2)); B = 65536 / N.  The inputs of every N are the same 2^16 x 16 x 64 seeded draws (seeds 401-404)
+    cut into B sequences.  Per N: 3 warm-up steps, then `steps` (default 20) steps timed with events."""
+    import numpy as np
+    import torch
+
+    from linear_rnn_layers_amd import binding, inputs
+
+    w = inputs.LONG
+    H, D, M, total = w.H, w.D, w.M, w.N
+    full = [torch.from_numpy(a).to("cuda").to(torch.bfloat16) for a in (*w.qkv(), w.grad_out())]
+    code = binding.dtype_code(torch.bfloat16)
+    steps = args.steps if args.steps != 50 else 20
+    rows = []
+    for lg in range(9, 17):
+        N = 1 << lg
+        B = total // N
+        q, k, v, do = (x.reshape(H, B, N, x.shape[-1]).permute(1, 0, 2, 3).contiguous() for x in full)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o = torch.empty((B, H, N, M), dtype=torch.bfloat16, device="cuda")
+        den = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        ck = torch.empty(binding.checkpoint_size(B, H, N, D, M) // 4, dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_f = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, code, "cuda")
+        ws_b = binding.alloc_workspace(binding.LA_OP_BWD_CAUSAL, B, H, N, D, M, code, "cuda")
+
+        def step():
+            binding.la_forward_causal(q, k, v, o, den, ckpt=ck, ws=ws_f)
+            binding.la_backward_causal(q, k, v, o, den, do, dq, dk, dv, ckpt=ck, ws=ws_b)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        peak = torch.cuda.max_memory_allocated() - base  # outputs, checkpoint and workspaces of this N
+        lib = sum(t.numel() * t.element_size() for t in (ck, ws_f, ws_b))
+        io = sum(t.numel() * t.element_size() for t in (q, k, v, do))
+        rows.append({"N": N, "B": B, "us_per_step": round(us, 2), "us_per_sample": round(us / B, 3),
+                     "tokens_per_s": B * N / (us * 1e-6),
+                     "inputs_bytes_per_sample": io // B, "peak_bytes_per_sample": (io + peak) // B,
+                     "checkpoint_and_workspace_bytes_per_sample": lib // B,
+                     "stored_states_bytes_per_sample": H * N * D * M * 4})
+        del q, k, v, do, o, den, ck, dq, dk, dv, ws_f, ws_b
+    print(json.dumps({"metric": "causal linear-attn fwd+bwd time and peak memory per sample vs N (batch x N = 65536)",
+                      "unit": "us/sample", "n_gpus": 1, "steps": steps, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "sequence-length sweep", "H": H, "D": D, "M": M, "tokens": total},
+                      "rows": rows}))
+
+
 def memory_report(step):
     """Device memory the library needs beside the I/O tensors (checkpoint of segment states and workspaces), what
     storing the state S_i of every token would take instead (B*H*N*D*M float32), and the run's peak allocation."""
@@ -658,6 +721,10 @@ def main():
             bb.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": max(1, args.steps)}))
+        return
+
+    if args.seq_sweep:
+        seq_sweep(args)
         return
 
     from linear_rnn_layers_amd import binding
