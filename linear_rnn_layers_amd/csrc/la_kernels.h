@@ -64,14 +64,19 @@ struct Prec<float> {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Backward chunk: 64 tokens, or 32 for float32 I/O when D = M: at 64/64 the
-// float32 planes of a 64-token chunk would not fit in LDS, at 32/32 the
-// 32-token chunk halves the workgroup's LDS (60 KB) so that two workgroups
-// share a compute unit (measured: 46 -> 40 us on the MNIST-shaped layer; the
-// mixed shapes measured slower with the smaller chunk).
+// Backward chunk: 64 tokens, or 32 when D = M (float32 I/O, or bf16 at
+// D = M = 32).  The 32-token chunk takes four wavefronts instead of eight, so
+// two workgroups share a compute unit and each one's barriers overlap the
+// other's work: measured on the MNIST-shaped layer (float32, LDS 60 KB) 46 ->
+// 40 us, on the 3072-token bf16 stack 28.8 -> 24.7 us per layer (LDS 42 KB,
+// 180 VGPRs).  At D = M = 64 the float32 planes of a 64-token chunk would not
+// fit in LDS; bf16 at D = M = 64 keeps 64 tokens (with 32, 256 VGPRs and
+// spill AGPRs leave one wave per SIMD: 394 -> 552 us on the 2^16-token
+// sequence), and so do the mixed shapes (measured slower with the smaller
+// chunk).
 template <typename T, int D, int M>
 struct BwdChunk {
-  static constexpr int value = (sizeof(T) == 4 && D == M) ? 32 : 64;
+  static constexpr int value = D == M && (sizeof(T) == 4 || D == 32) ? 32 : 64;
 };
 
 // State tiles.  Tile t = w + 4k of wave w covers feature block db = t % DB
