@@ -127,8 +127,8 @@ int la_set_segment_chunks(int chunks);
 int la_set_forward_onepass(int mode);
 
 /* Process-wide limit on the polls with which a workgroup of the one-launch
- * forward waits for an earlier segment's aggregate (default 2^22, about
- * 0.1 s).  The waits always end: workgroups are dispatched in index order and
+ * forward waits for an earlier segment's aggregate (default 2^22: a few
+ * seconds, each poll waiting for a device-scope load).  The waits always end: workgroups are dispatched in index order and
  * wait only for lower-numbered ones.  A workgroup that reaches the limit
  * anyway gives up: its carry is NaN, so its rows of O and den, its checkpoint
  * entries and (last segment) the final state are NaN rather than wrong

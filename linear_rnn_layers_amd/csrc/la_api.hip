@@ -341,7 +341,8 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
 // segments allow.
 std::atomic<int> g_fwd_onepass{1};
 // Polls of a one-launch forward's wait for an earlier segment's flag before
-// it gives up (about 0.1 s of polling at 2^22).
+// it gives up (each poll waits for a device-scope load of about a
+// microsecond, so 2^22 polls are a few seconds).
 std::atomic<int> g_lb_polls{1 << 22};
 
 bool use_onepass(const Plan& p, int D, int M) {
