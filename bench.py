@@ -677,11 +677,12 @@ def cpu_baseline(args, w):
             if el >= 10.0 or reps >= 1000:
                 break
             continue
-        oracle.forward_causal(q, k, v)
+        o_ref, den_ref, _, _ = oracle.forward_causal(q, k, v)
+        ref = {"O": o_ref, "den": den_ref}
         if wl != "small":
-            oracle.backward_causal(q, k, v, do)
+            ref["dQ"], ref["dK"], ref["dV"] = oracle.backward_causal(q, k, v, do)
         if wl == "mnist":
-            oracle.forward_noncausal(q, k, v)
+            ref["O_noncausal"] = oracle.forward_noncausal(q, k, v)
         reps += 1
         el = time.perf_counter() - t
         if el >= 10.0 or reps >= 1000:
@@ -689,9 +690,39 @@ def cpu_baseline(args, w):
     head_tokens_per_s = reps * nb * nh * n / el
     layers = w.layers if wl in ("cifar", "speech") else 1
     value = head_tokens_per_s / (H * layers)  # model tokens/s: every token goes through H heads (x layers)
-    return {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} x one step's passes on {nb}x{nh} of {B}x{H} sequences, {n} of {N} tokens"
-                      f"{f', scaled to {layers} layers' if layers > 1 else ''}"}
+    out = {"value": value, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{reps} x one step's passes on {nb}x{nh} of {B}x{H} sequences, {n} of {N} tokens"
+                     f"{f', scaled to {layers} layers' if layers > 1 else ''}"}
+    if wl in ("mnist", "cifar", "small") and n == N:
+        out["_ref"] = (ref, nb, nh)  # whole sequences of the first input set: the GPU step can be compared
+    return out
+
+
+def sample_parity(step, ref, nb, nh):
+    """The GPU path on the first input set (one untimed step) against the oracle outputs of the CPU-baseline
+    sample: per tensor, the largest over the sampled heads of max|gpu - oracle| / max|oracle|."""
+    import numpy as np
+    import torch
+
+    b = step.b
+    q, k, v, do = step.sets[0]
+    b.la_forward_causal(q, k, v, step.o, step.den, ckpt=step.ck, ws=step.ws_f)
+    got = {}
+    if "dQ" in ref:
+        b.la_backward_causal(q, k, v, step.o, step.den, do, step.dq, step.dk, step.dv, ckpt=step.ck, ws=step.ws_b)
+        got.update(dQ=step.dq, dK=step.dk, dV=step.dv)
+    if "O_noncausal" in ref:
+        b.la_forward_noncausal(q, k, v, step.onc, ws=step.ws_n)
+        got["O_noncausal"] = step.onc
+    got.update(O=step.o, den=step.den)
+    torch.cuda.synchronize()
+    res = {}
+    for name, y in ref.items():
+        x = got[name][:nb, :nh].float().cpu().numpy().astype(np.float64)
+        y = np.asarray(y, dtype=np.float64)
+        ax = tuple(range(2, y.ndim))
+        res[name] = float((np.abs(x - y).max(axis=ax) / np.abs(y).max(axis=ax)).max())
+    return res
 
 
 # -------------------------------------------------------------------- main
@@ -817,8 +848,14 @@ def main():
     breakdown = {k: {"us_per_step": round(v["ms_per_step"] * 1e3, 2),
                      "launches_per_step": v["launches_per_step"]} for k, v in probe.items()}
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, w)
+        if "_ref" in cpu:
+            ref, nb, nh = cpu.pop("_ref")
+            parity = {"sample": f"first input set, {nb}x{nh} sequences of {w.B}x{w.H}, one untimed step",
+                      "measure": "max over sampled heads of max|gpu - oracle| / max|oracle| per tensor",
+                      "tolerance": 1e-4 if s == 4 else 2e-2, **sample_parity(step, ref, nb, nh)}
 
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M, "gpus": 1}
     if args.workload == "mnist":
@@ -844,7 +881,9 @@ def main():
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32" if s == 4 else "bf16", "data": "synthetic", "config": cfg,
-           "roofline": roof, "cpu_baseline": cpu, "step_us": dist, "memory": mem, "kernels_us_per_step": breakdown,
+           "roofline": roof, "cpu_baseline": cpu, "parity": parity, "step_us": dist, "memory": mem,
+           "gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip, "seeds": list(w.seeds),
+           "kernels_us_per_step": breakdown,
            "kernel_events_in_timed_region": not args.no_kernel_events, "events_dropped": dropped}
     print(json.dumps(out))
 
