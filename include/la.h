@@ -120,8 +120,9 @@ int la_set_segment_chunks(int chunks);
  * the sum of the earlier segments' aggregates to its rows at the end.  The
  * two-launch form runs a separate aggregate pass first.  Both compute eq.
  * 9-12; results differ only in rounding.  mode 0: always two launches; 1 (the
- * default): one launch where the segments allow it and D*M >= 2048 (where it
- * measured faster); 2: one launch wherever the segments allow it.  It exists
+ * default): one launch where the segments allow it, D*M >= 2048 (where it
+ * measured faster) and all its workgroups fit on the GPU at once; 2: one
+ * launch wherever the segments allow it.  It exists
  * to test both forms and to measure them.  Returns the previous mode, or -1
  * for a mode outside 0..2. */
 int la_set_forward_onepass(int mode);

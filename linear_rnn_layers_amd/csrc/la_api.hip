@@ -337,6 +337,8 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
 // costs more than that (measured per 784-token layer of 16x8 heads, float32:
 // D = 64, M = 32: 48.0 -> 40.6 us; D = M = 32: 33.4 -> 37.4 us, and 21.2 ->
 // 25.6 us per 3072-token bf16 layer of 4x8 heads, so those keep two launches).
+// The automatic rule also requires the whole grid to be resident at once, so
+// that no wait depends on the order in which workgroups are dispatched.
 // la_set_forward_onepass: 0 never, 1 by this rule (default), 2 wherever the
 // segments allow.
 std::atomic<int> g_fwd_onepass{1};
@@ -345,10 +347,25 @@ std::atomic<int> g_fwd_onepass{1};
 // microsecond, so 2^22 polls are a few seconds).
 std::atomic<int> g_lb_polls{1 << 22};
 
-bool use_onepass(const Plan& p, int D, int M) {
+// workgroups of the one-launch forward resident per compute unit
+template <typename T, int D, int M, int NC>
+int onepass_resident() {
+  static const int n = [] {
+    int r = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, la::k_fwd_lb<T, D, M, NC>, la::NT, 0) != hipSuccess)
+      r = 0;
+    return r;
+  }();
+  return n;
+}
+
+template <typename T, int D, int M>
+bool use_onepass(const Plan& p) {
   const int mode = g_fwd_onepass.load(std::memory_order_relaxed);
   if (mode == 0 || p.nseg <= 1 || p.L > 4 * la::CH || use_scan(p)) return false;
-  return mode == 2 || D * M >= 2048;
+  if (mode == 2) return true;
+  const int resident = p.L <= 2 * la::CH ? onepass_resident<T, D, M, 2>() : onepass_resident<T, D, M, 4>();
+  return D * M >= 2048 && p.BH * p.nseg <= (long)resident * kCUs;
 }
 
 template <typename T, int D, int M, int NC>
@@ -372,7 +389,7 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
-  if (use_onepass(p, D, M)) {
+  if (use_onepass<T, D, M>(p)) {
     if (p.L <= 2 * la::CH)
       return fwd_onepass<T, D, M, 2>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
     return fwd_onepass<T, D, M, 4>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
