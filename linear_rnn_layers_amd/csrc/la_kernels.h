@@ -64,19 +64,26 @@ struct Prec<float> {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Backward chunk: 64 tokens, or 32 when D = M (float32 I/O, or bf16 at
-// D = M = 32).  The 32-token chunk takes four wavefronts instead of eight, so
-// two workgroups share a compute unit and each one's barriers overlap the
-// other's work: measured on the MNIST-shaped layer (float32, LDS 60 KB) 46 ->
-// 40 us, on the 3072-token bf16 stack 28.8 -> 24.7 us per layer (LDS 42 KB,
-// 180 VGPRs).  At D = M = 64 the float32 planes of a 64-token chunk would not
-// fit in LDS; bf16 at D = M = 64 keeps 64 tokens (with 32, 256 VGPRs and
-// spill AGPRs leave one wave per SIMD: 394 -> 552 us on the 2^16-token
-// sequence), and so do the mixed shapes (measured slower with the smaller
-// chunk).
+// Backward chunk: 32 tokens when D = M, else 64.  The 32-token chunk takes
+// four wavefronts instead of eight, so two workgroups share a compute unit
+// and each one's barriers overlap the other's work: measured on the
+// MNIST-shaped layer (float32, LDS 60 KB) 46 -> 40 us, on the 3072-token bf16
+// stack 28.8 -> 24.7 us per layer, on the 2^16-token bf16 sequence 395 -> 381
+// us.  At D = M = 64 the float32 planes of a 64-token chunk would not fit in
+// LDS.  The mixed shapes keep 64 tokens (with 32 their state tiles take more
+// than 256 VGPRs per wavefront: one wave per SIMD).
 template <typename T, int D, int M>
 struct BwdChunk {
-  static constexpr int value = D == M && (sizeof(T) == 4 || D == 32) ? 32 : 64;
+  static constexpr int value = D == M ? 32 : 64;
+};
+// bf16 at D = M = 64 with 32-token chunks: the S tiles are spread over all
+// four wavefronts (not only the two query ones), which keeps a wavefront at
+// 238 VGPRs, and phi(Q), phi(K) are read as sums of their two bf16 planes
+// rather than from float32 copies, which keeps the workgroup at 76.5 KB of
+// LDS: two workgroups per compute unit.
+template <typename T, int D, int M>
+struct BwdWide {
+  static constexpr bool value = sizeof(T) == 2 && D == 64 && M == 64;
 };
 
 // State tiles.  Tile t = w + 4k of wave w covers feature block db = t % DB
@@ -986,7 +993,8 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // wavefront k, whose work falls with k while the key rows' work (all later
 // rows of the chunk) rises with k.  The tiles of S (forward sum of
 // phi(K) V^T, eq. 13) and Z are held by the query wavefronts (the key
-// wavefronts carry the longest phase).  Phases
+// wavefronts carry the longest phase), by all wavefronts for bf16 at
+// D = M = 64 (BwdWide: the registers a query wavefront would need).  Phases
 // of a chunk, separated by barriers:
 //   stage   all: phi(Q), phi(K), V, dO to LDS; next chunk's reads issued
 //   B  query: dQ, g, c, 1/den          key: A_ij, dO_i.V_j, R V_j
@@ -1012,7 +1020,7 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
   constexpr int CB = BS::CB, RB = BS::RB, NW = BS::NW, NTH = BS::NTH, NPAIR = CB / 32;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NTR = DB * MB / RB;                 // R tiles per query wavefront
-  constexpr int NWS = RB < DB * MB ? RB : DB * MB;  // query wavefronts holding S tiles
+  constexpr int NWS = BwdWide<T, D, M>::value ? NW : RB < DB * MB ? RB : DB * MB;  // wavefronts holding S tiles
   constexpr int NTS = DB * MB / NWS;                // S tiles per holder
   constexpr int NZS = (DB + NWS - 1) / NWS;         // Z blocks per holder: so + NWS j
   constexpr int NZW = (DB + RB - 1) / RB;           // r blocks per query wavefront
@@ -1026,8 +1034,9 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
   __shared__ Planes<P::NR, D, M> rp;        // R after this chunk, [d][m]
   // phi(Q), phi(K) as float32 for the elementwise terms; rows padded by 4 so
   // the 16 rows a fragment reads start in different banks
-  __shared__ alignas(16) float q32[CB][D + 4];
-  __shared__ alignas(16) float k32[CB][D + 4];
+  constexpr bool F32C = !BwdWide<T, D, M>::value;  // float32 copies of phi(Q), phi(K)
+  __shared__ alignas(16) float q32[F32C ? CB : 1][D + 4];
+  __shared__ alignas(16) float k32[F32C ? CB : 1][D + 4];
   __shared__ alignas(16) float sZ[D];     // Z after this chunk
   __shared__ alignas(16) float sr[D];     // r after this chunk
   __shared__ alignas(16) float sInv[CB];  // 1 / den_i (0 past the end)
@@ -1152,8 +1161,13 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
     const int nv = min(CB, t1 - c0);
     // ---- stage this chunk from registers, then start reading the previous one
     // (the barrier ending the previous chunk separates its reads from these writes)
-    bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
-    bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0], fm);
+    if constexpr (F32C) {
+      bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
+      bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0], fm);
+    } else {
+      bq.template stage_phi<P::NQ, CB, D, 8, 0>(qt, nv, nullptr, fm);
+      bk.template stage_phi<P::NK, CB, D, 8, 0>(kt, nv, nullptr, fm);
+    }
     bv.stage_values(vt);
     bd.stage_values(ot);
     if (ci > 0) {
@@ -1235,8 +1249,12 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
       float qv[DB][4];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
-        qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
+        if constexpr (F32C) {
+          const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
+          qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
+        } else {
+          qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pu += qv[d0][r] * U[d0][r];
@@ -1371,9 +1389,15 @@ __global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
           if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
         if (row_ok) {
           float o[4];
-          const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
+          float kv[4];
+          if constexpr (F32C) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
+            kv[0] = k4.x; kv[1] = k4.y; kv[2] = k4.z; kv[3] = k4.w;
+          } else {
+            kt.get4(jl, 16 * d0 + 4 * g, kv);
+          }
           const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
-          const float kv[4] = {k4.x, k4.y, k4.z, k4.w}, rr[4] = {r4.x, r4.y, r4.z, r4.w};
+          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dfeat(kv[r], fm);
           IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
