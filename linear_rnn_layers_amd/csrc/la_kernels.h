@@ -64,26 +64,28 @@ struct Prec<float> {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Backward chunk: 32 tokens when D = M, else 64.  The 32-token chunk takes
-// four wavefronts instead of eight, so two workgroups share a compute unit
-// and each one's barriers overlap the other's work: measured on the
-// MNIST-shaped layer (float32, LDS 60 KB) 46 -> 40 us, on the 3072-token bf16
-// stack 28.8 -> 24.7 us per layer, on the 2^16-token bf16 sequence 395 -> 381
-// us.  At D = M = 64 the float32 planes of a 64-token chunk would not fit in
-// LDS.  The mixed shapes keep 64 tokens (with 32 their state tiles take more
-// than 256 VGPRs per wavefront: one wave per SIMD).
+// Backward chunk: 32 tokens for every shape.  The 32-token chunk takes four
+// wavefronts instead of eight, so two workgroups share a compute unit and
+// each one's barriers overlap the other's work: measured on the
+// MNIST-shaped layer (float32, LDS 60 KB) 46 -> 40 us, on the 3072-token
+// bf16 stack 28.8 -> 24.7 us per layer, on the 2^16-token bf16 sequence
+// 395 -> 381 us, on the 64-feature layer (float32, D = 64, M = 32) 68.6 ->
+// 61.7 us, and 7-12 % on the other mixed shapes.  At float32 D = M = 64 the
+// planes of a 64-token chunk would not fit in LDS.
 template <typename T, int D, int M>
 struct BwdChunk {
-  static constexpr int value = D == M ? 32 : 64;
+  static constexpr int value = 32;
 };
-// bf16 at D = M = 64 with 32-token chunks: the S tiles are spread over all
-// four wavefronts (not only the two query ones), which keeps a wavefront at
-// 238 VGPRs, and phi(Q), phi(K) are read as sums of their two bf16 planes
-// rather than from float32 copies, which keeps the workgroup at 76.5 KB of
-// LDS: two workgroups per compute unit.
+// Where D or M is 64, two further changes keep a workgroup at four
+// wavefronts of at most 248 VGPRs and at most 78 KB of LDS (two per compute
+// unit): the S tiles are spread over all four wavefronts, not only the two
+// query ones, and phi(Q), phi(K) are read as sums of their bf16 planes rather
+// than from float32 copies.  float32 at D = M = 64 keeps the copies and the
+// query-held S (with the spread it still needs spill AGPRs, one wave per
+// SIMD either way, and measured 122.7 -> 132.6 us).
 template <typename T, int D, int M>
 struct BwdWide {
-  static constexpr bool value = sizeof(T) == 2 && D == 64 && M == 64;
+  static constexpr bool value = (D == 64 || M == 64) && !(sizeof(T) == 4 && D == 64 && M == 64);
 };
 
 // State tiles.  Tile t = w + 4k of wave w covers feature block db = t % DB
@@ -993,8 +995,8 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // wavefront k, whose work falls with k while the key rows' work (all later
 // rows of the chunk) rises with k.  The tiles of S (forward sum of
 // phi(K) V^T, eq. 13) and Z are held by the query wavefronts (the key
-// wavefronts carry the longest phase), by all wavefronts for bf16 at
-// D = M = 64 (BwdWide: the registers a query wavefront would need).  Phases
+// wavefronts carry the longest phase), by all wavefronts where D or M is 64
+// (BwdWide: the registers a query wavefront would need).  Phases
 // of a chunk, separated by barriers:
 //   stage   all: phi(Q), phi(K), V, dO to LDS; next chunk's reads issued
 //   B  query: dQ, g, c, 1/den          key: A_ij, dO_i.V_j, R V_j
