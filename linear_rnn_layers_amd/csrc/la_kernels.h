@@ -981,9 +981,9 @@ __global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, cons
 // state before the chunk -- the initial state, checkpoint entry 0 -- is
 // staged instead and the causal sum over j <= i is added.
 //
-// Two roles of RB = CB / 16 wavefronts each, one wavefront of each role per
-// SIMD for 64-token chunks, so that each SIMD interleaves two instruction
-// streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
+// Two roles of RB = CB / 16 wavefronts each: with the 32-token chunk
+// (BwdChunk) four wavefronts, and two workgroups per compute unit, so that
+// each SIMD interleaves two instruction streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
 // reverse state R (backward sum of phi(Q) g^T, eq. 14-15, started from the
 // gradient of the final state (dSN, dZN; zero when absent) plus the reverse
 // aggregates of all later checkpoint segments: entry f1 - 1 of `ragg` when it
