@@ -244,3 +244,32 @@ def test_plan_and_sizes(lib, B, H, N, D, M):
 
 def _al(x):
     return (x + 255) // 256 * 256
+
+
+def test_process_wide_switches(lib):
+    """The segment-length override, the forward's form and the one-launch wait limit: valid values are taken and
+    the previous one returned; invalid values are refused with -1 and change nothing."""
+    assert lib.la_set_segment_chunks(-1) == -1
+    prev = lib.la_set_segment_chunks(3)
+    try:
+        assert lib.la_set_segment_chunks(3) == 3
+        assert lib.la_segment_length(2, 2, 1000, 32, 32) == 3 * 64
+    finally:
+        lib.la_set_segment_chunks(prev)
+    for bad in (-1, 3):
+        assert lib.la_set_forward_onepass(bad) == -1
+    prev = lib.la_set_forward_onepass(2)
+    try:
+        assert lib.la_set_forward_onepass(0) == 2
+    finally:
+        lib.la_set_forward_onepass(prev)
+    assert lib.la_set_wait_polls(-5) == -1
+    prev = lib.la_set_wait_polls(7)
+    try:
+        assert lib.la_set_wait_polls(prev) == 7
+    finally:
+        lib.la_set_wait_polls(prev)
+    with pytest.raises(ValueError):
+        binding.set_forward_onepass(5)
+    with pytest.raises(ValueError):
+        binding.set_wait_polls(-1)
