@@ -286,9 +286,11 @@ def WORKLOADS(inputs):
 
 # ---------------------------------------------------- algorithmic figures
 def kernel_bytes(name, w, s):
-    """Algorithmic HBM bytes per launch: the tensors the kernel must read or write by its function
-    (per token-head: the survey's forward (2D+2M)s+4 and backward figures split over the kernels).  With
-    random features the attention kernels see feature vectors of size C in place of D."""
+    """Algorithmic HBM bytes per launch: the tensors the kernel must read or write by its function.  Per
+    token-head the method moves (2D+2M)s+4 bytes forward (read Q, K, V; write O, den) and (4D+4M)s+4 backward
+    (read Q, K, V, O, dO, den; write dQ, dK, dV), s the bytes per element; these totals are split over the
+    kernels that do the work.  With random features the attention kernels see feature vectors of size C in
+    place of D."""
     Din, M = w.D, w.M
     D = w.features or Din
     th = w.B * w.H * w.N
