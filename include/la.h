@@ -28,7 +28,8 @@
  *    la_workspace_size(...) (which may be 0; then ws may be NULL).  The
  *    library never allocates device memory.
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
- *    NULL = the default stream).  No host synchronisation, no other streams.
+ *    NULL = the default stream).  No host synchronisation (except the status
+ *    query la_forward_wait_status), no other streams.
  *  - All arguments are validated before any launch; on error nothing is
  *    launched and a status is returned (la_last_error() gives details).  A
  *    failed launch returns LA_ERR_HIP with the HIP message.  No C++
@@ -58,7 +59,9 @@ typedef enum {
   LA_ERR_WORKSPACE = 6,   /* ws_bytes < la_workspace_size(...) or ws NULL */
   LA_ERR_UNSUPPORTED = 7, /* D or M not in {32, 64} */
   LA_ERR_HIP = 8,         /* a HIP launch failed */
-  LA_ERR_ARG = 9          /* inconsistent optional arguments */
+  LA_ERR_ARG = 9,         /* inconsistent optional arguments */
+  LA_ERR_WAIT = 10        /* a one-launch forward gave up waiting (see
+                             la_forward_wait_status) */
 } la_status;
 
 typedef enum {
@@ -83,60 +86,112 @@ typedef enum {
  *                        denominator must be positive. */
 typedef enum { LA_FEATURE_ELU1 = 0, LA_FEATURE_IDENTITY = 1 } la_feature;
 
+/* Form of the causal forward without a decay (results differ only in
+ * rounding; both compute eq. 9-12 of "Transformers are RNNs -- part 2/3").
+ *   LA_FORM_AUTO        the library's measured rule: one launch where the
+ *                       segments allow it (at most four chunks, aggregates
+ *                       summed by every workgroup), the state has D*M >= 2048
+ *                       and every workgroup of the grid is resident at once;
+ *                       two launches otherwise.
+ *   LA_FORM_TWO_LAUNCH  a separate aggregate pass, then the forward.
+ *   LA_FORM_ONE_LAUNCH  one launch wherever the segments allow it: each
+ *                       workgroup walks its segment from a zero state,
+ *                       publishes the segment's aggregate behind a flag in
+ *                       `ws`, waits for the earlier segments' flags and adds
+ *                       their aggregates at the end.  Where the grid is not
+ *                       resident at once, progress relies on workgroups being
+ *                       dispatched in index order (the lowest unfinished one
+ *                       never waits); this order is not a documented
+ *                       guarantee, hence the bounded waits below. */
+typedef enum {
+  LA_FORM_AUTO = 0,
+  LA_FORM_TWO_LAUNCH = 1,
+  LA_FORM_ONE_LAUNCH = 2
+} la_form;
+
+/* Per-call options.  Every entry point that plans segments takes a
+ * `const la_options *opts`; NULL (or an all-zero struct) means the defaults.
+ * The library keeps no state between calls: whatever a call depends on is in
+ * its arguments, so concurrent calls from several host threads with
+ * different options are independent (calls that share an output, a
+ * workspace or a decode state still race, as with any buffer).
+ *   segment_chunks  0: automatic segment length; > 0: segments of that many
+ *                   64-token chunks (clamped to the sequence).  Results do
+ *                   not depend on it beyond rounding.  A checkpoint is laid
+ *                   out by it: la_checkpoint_size, la_forward_causal and the
+ *                   la_backward_causal that reads the checkpoint must be
+ *                   given the same value.
+ *   forward_form    la_form (above).
+ *   wait_polls      one-launch forward: polls (each waits for a device-scope
+ *                   load, about a microsecond) before a workgroup waiting for
+ *                   an earlier segment gives up; 0: the default 2^22 (a few
+ *                   seconds); < 0: none at all, every wait gives up at once
+ *                   (exercises the failure path: no wave spins).  A workgroup
+ *                   that gives up makes its carry NaN, so its rows of O and
+ *                   den, its checkpoint entries and the final state show the
+ *                   failure instead of a wrong value, and sets the status
+ *                   word of `ws` (la_forward_wait_status) and, when given,
+ *                   *status.
+ *   status          optional device pointer to one 32-bit word: the
+ *                   one-launch forward ORs 1 into it when a wait gave up.
+ *                   Never cleared by the library.
+ *   timed_kernel    optional kernel name (see la_kernel_names): every launch
+ *                   of that kernel in this call is bracketed by a pair of
+ *                   caller-created HIP events recorded on the launch stream,
+ *                   events[2 i] before and events[2 i + 1] after, for i =
+ *                   *events_used, *events_used + 1, ... while i <
+ *                   event_pairs; *events_used (host memory) is advanced by
+ *                   one per recorded pair.  Reading the times is the
+ *                   caller's (hipEventElapsedTime after a synchronisation). */
+typedef struct la_options {
+  int segment_chunks;
+  int forward_form;
+  int wait_polls;
+  int event_pairs;
+  unsigned *status;
+  const char *timed_kernel;
+  void **events;
+  int *events_used;
+} la_options;
+
 /* Library version, as 10000*major + 100*minor + patch. */
 int la_version(void);
 
 /* Bytes of scratch memory the operation `op` needs for these sizes
  * (0 when none).  Returns 0 for invalid arguments. */
-size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype);
+size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype,
+                         const la_options *opts);
 
 /* Bytes of the segment-state checkpoint written by la_forward_causal and
  * read by la_backward_causal: the float32 state (S, Z) before every segment
  * of the sequence and after the last one.  The sequence is cut into
- * segments of a fixed length chosen from (B, H, N, D, M) only, so a
- * checkpoint is valid for any call with the same sizes.  Its size is
+ * segments of a fixed length chosen from (B, H, N, D, M) and
+ * opts->segment_chunks only, so a checkpoint is valid for any call with the
+ * same sizes and segment option.  Its size is
  * O(N * D * M / segment) per head, well inside the pages' linear-memory
  * bound; no per-token state S_i is ever stored ("Transformers are RNNs --
  * part 2/3", section 3.3.1).  The decayed recurrence (logA given) uses
  * longer segments and at most this many bytes. */
-size_t la_checkpoint_size(int B, int H, int N, int D, int M);
+size_t la_checkpoint_size(int B, int H, int N, int D, int M,
+                          const la_options *opts);
 
-/* Sequence segment length (tokens) used for these sizes: the spacing of
- * the checkpoint entries.  About 1024 segments are planned over all heads,
- * each a whole number of 64-token chunks. */
-int la_segment_length(int B, int H, int N, int D, int M);
+/* Sequence segment length (tokens) used for these sizes and options: the
+ * spacing of the checkpoint entries.  By default about 1024 (short sequences
+ * of small states) or 512 segments are planned over all heads, each a whole
+ * number of 64-token chunks. */
+int la_segment_length(int B, int H, int N, int D, int M,
+                      const la_options *opts);
 
-/* Process-wide override of the segment length, in 64-token chunks (0 =
- * automatic, the default).  Results do not depend on it beyond rounding;
- * it exists to test that and to tune.  A checkpoint must be consumed under
- * the same setting it was written with.  Returns the previous value, or -1
- * for a negative argument. */
-int la_set_segment_chunks(int chunks);
-
-/* Process-wide choice between the two forms of the causal forward without a
- * decay.  The one-launch form serves segments of at most four chunks (when
- * every workgroup sums the earlier aggregates itself): each workgroup walks
- * its segment from a zero state, publishes the segment's aggregate, and adds
- * the sum of the earlier segments' aggregates to its rows at the end.  The
- * two-launch form runs a separate aggregate pass first.  Both compute eq.
- * 9-12; results differ only in rounding.  mode 0: always two launches; 1 (the
- * default): one launch where the segments allow it, D*M >= 2048 (where it
- * measured faster) and all its workgroups fit on the GPU at once; 2: one
- * launch wherever the segments allow it.  It exists
- * to test both forms and to measure them.  Returns the previous mode, or -1
- * for a mode outside 0..2. */
-int la_set_forward_onepass(int mode);
-
-/* Process-wide limit on the polls with which a workgroup of the one-launch
- * forward waits for an earlier segment's aggregate (default 2^22: a few
- * seconds, each poll waiting for a device-scope load).  The waits always end: workgroups are dispatched in index order and
- * wait only for lower-numbered ones.  A workgroup that reaches the limit
- * anyway gives up: its carry is NaN, so its rows of O and den, its checkpoint
- * entries and (last segment) the final state are NaN rather than wrong
- * values, and word 0 of the flag region of `ws` (after the aggregate and
- * prefix-state regions) is set.  It exists to test that path.  Returns the
- * previous limit, or -1 for a negative argument. */
-int la_set_wait_polls(int polls);
+/* Status of the last one-launch causal forward that used this workspace
+ * (same sizes and options): LA_ERR_WAIT when one of its workgroups gave up
+ * waiting for an earlier segment's aggregate (its rows of O and den, its
+ * checkpoint entries and the final state are then NaN), LA_OK otherwise
+ * (also when the call took the two-launch form or needed no workspace).
+ * Reads the status word of `ws` after synchronising `stream`: the only
+ * call of this library that blocks the host. */
+int la_forward_wait_status(const void *ws, size_t ws_bytes, int B, int H,
+                           int N, int D, int M, int dtype, void *stream,
+                           const la_options *opts);
 
 /*
  * Causal forward, eq. 9-12 ("Transformers are RNNs -- part 2/3", section 3.3).
@@ -162,8 +217,8 @@ int la_set_wait_polls(int polls);
  *               boundary states for la_backward_causal.  NULL to skip.
  *   ws          la_workspace_size(LA_OP_FWD_CAUSAL, ...) bytes: segment
  *               aggregates, their prefix states, and (one-launch form, see
- *               la_set_forward_onepass) one 32-bit flag per segment plus an
- *               error word, cleared by the call itself, so any contents are
+ *               la_form) one 32-bit flag per segment plus the status word,
+ *               cleared by the call itself, so any contents are
  *               accepted.  In the one-launch form the workgroups of a call
  *               exchange segment aggregates through `ws`: calls that overlap
  *               on one workspace race, as with any scratch buffer.
@@ -173,7 +228,7 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
                       const float *Z0, float *S_out, float *Z_out,
                       float *ckpt, int B, int H, int N, int D, int M,
                       int dtype, int feature, void *ws, size_t ws_bytes,
-                      void *stream);
+                      void *stream, const la_options *opts);
 
 /*
  * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
@@ -186,7 +241,8 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
 int la_forward_noncausal(const void *Q, const void *K, const void *V, void *O,
                          float *S_out, float *Z_out, int B, int H, int N,
                          int D, int M, int dtype, int feature, void *ws,
-                         size_t ws_bytes, void *stream);
+                         size_t ws_bytes, void *stream,
+                         const la_options *opts);
 
 /*
  * Causal backward: gradients of a scalar loss with respect to the raw Q, K,
@@ -229,7 +285,7 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
                        const float *dZ_N, void *dQ, void *dK, void *dV,
                        float *dlogA, float *dS0, float *dZ0, int B, int H,
                        int N, int D, int M, int dtype, int feature, void *ws,
-                       size_t ws_bytes, void *stream);
+                       size_t ws_bytes, void *stream, const la_options *opts);
 
 /*
  * Non-causal backward: gradients of a scalar loss with respect to the raw Q,
@@ -254,7 +310,7 @@ int la_backward_noncausal(const void *Q, const void *K, const void *V,
                           const float *Z_tot, void *dQ, void *dK, void *dV,
                           int B, int H, int N, int D, int M, int dtype,
                           int feature, void *ws, size_t ws_bytes,
-                          void *stream);
+                          void *stream, const la_options *opts);
 
 /*
  * One RNN step of the attention ("Transformers are RNNs -- part 2/3",
@@ -269,9 +325,9 @@ int la_backward_noncausal(const void *Q, const void *K, const void *V,
  */
 int la_decode_step(const void *q, const void *k, const void *v,
                    const float *logA, float *S, float *Z, void *y, int B,
-                   int H, int D, int M, int dtype, int feature, void *stream);
+                   int H, int D, int M, int dtype, int feature, void *stream,
+                   const la_options *opts);
 
-/* Name of a status code. */
 /*
  * Positive random features ("Linear Attention/zh", feature maps: Performer's
  * phi(x) proportional to exp(W x - |x|^2 / 2); "The Transformer Family v2",
@@ -311,24 +367,11 @@ int la_feature_poly2_vjp(const void *X, const void *dPhi, void *dX, int B,
                          int H, int N, int Din, int C, int dtype,
                          void *stream);
 
+/* Name of a status code. */
 const char *la_status_string(int status);
 
 /* Detail of the last non-OK status returned on this thread ("" if none). */
 const char *la_last_error(void);
-
-/*
- * Kernel timing hooks for measurement.  la_prof_select(name) makes every
- * later launch of the kernel `name` (see la_kernel_names) be bracketed by a
- * pair of HIP events recorded on the launch stream; NULL or "" stops it.
- * The events are timing-only (no system-scope fence): synchronise the
- * device (or the stream) before la_prof_collect, which then reads them and
- * returns the summed duration in milliseconds and the number of launches,
- * and clears the record.  Up to 65536 launches are recorded; later ones are counted in
- * `dropped`.  Not thread-safe with concurrent launches of the selected
- * kernel on several host threads.
- */
-int la_prof_select(const char *kernel_name);
-int la_prof_collect(double *total_ms, int *launches, int *dropped);
 
 /* Comma-separated names of the kernels the library launches. */
 const char *la_kernel_names(void);

@@ -2,7 +2,10 @@
 // planning, workspace layout, kernel dispatch and timing hooks.
 //
 // Nothing here allocates device memory or synchronises the stream (except
-// la_prof_collect, which waits for its own events by design).
+// la_forward_wait_status, a documented blocking query), and nothing keeps
+// mutable state between calls: every choice a call depends on comes from its
+// arguments (la_options).  The only process-wide data are immutable caches of
+// device properties (compute units, kernel occupancy), filled on first use.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -11,12 +14,12 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/la.h"
 #include "la_decay.h"
+#include "la_bwd2.h"
 #include "la_feature.h"
 
 namespace {
@@ -45,7 +48,6 @@ struct Plan {
   int SV = 0;  // floats per state vector: D*M + D
 };
 
-constexpr long kCUs = 256;          // compute units of one MI355X
 constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels: finer plan
 // About half as many, longer segments: fewer aggregates to sum or scan and
 // less set-up per token.  The non-causal ops (no running state between
@@ -66,10 +68,10 @@ long causal_target(long nchunks, int D, int M) {
   return nchunks <= 16 && (long)D * M <= 1024 ? kFineTarget : kFineTargetNC;
 }
 
-std::atomic<int> g_seg_chunks{0};  // 0: automatic segment length
+int opt_chunks(const la_options* o) { return o && o->segment_chunks > 0 ? o->segment_chunks : 0; }
 
-// target 0: the causal ops' rule
-Plan make_plan(int B, int H, int N, int D, int M, long target = 0) {
+// target 0: the causal ops' rule; forced > 0: segments of that many chunks
+Plan make_plan(int B, int H, int N, int D, int M, long target, int forced) {
   Plan p;
   p.BH = (long)B * H;
   p.N = N;
@@ -85,7 +87,6 @@ Plan make_plan(int B, int H, int N, int D, int M, long target = 0) {
   if (segs > nchunks) segs = nchunks;
   if (segs < 1) segs = 1;
   long cps = (nchunks + segs - 1) / segs;
-  const int forced = g_seg_chunks.load(std::memory_order_relaxed);
   if (forced > 0) cps = forced < nchunks ? forced : nchunks;
   p.L = (int)(cps * la::CH);
   p.nseg = (int)(((long)N + p.L - 1) / p.L);
@@ -99,37 +100,18 @@ Plan make_plan(int B, int H, int N, int D, int M, long target = 0) {
 // scan kernel forms all prefix sums once.
 bool use_scan(const Plan& p) { return (size_t)p.nseg * p.SV * sizeof(float) / 2 > (64u << 10); }
 
-// Checkpoint segments per backward segment.  A backward workgroup costs
-// about one chunk of set-up plus one per chunk it walks; workgroups are
-// dispatched in order onto kCUs x resident slots, each starting when the
-// earliest slot frees.  kb minimises the finish time of that schedule
-// (ties: fewer, longer segments).
-int backward_group(const Plan& p, int N, int resident) {
-  const int slots = (int)(kCUs * (resident > 0 ? resident : 1));
-  int best = 1;
-  long best_t = -1;
-  std::vector<long> heap;
-  for (int kb = 1; kb <= p.nseg; ++kb) {
-    const long Lb = (long)kb * p.L;
-    const long nsegb = (N + Lb - 1) / Lb;
-    heap.assign((size_t)slots, 0);  // min-heap of slot finish times
-    long finish = 0;
-    for (long h = 0; h < p.BH; ++h) {
-      for (long sb = 0; sb < nsegb; ++sb) {
-        const long tok = std::min((long)N, (sb + 1) * Lb) - sb * Lb;
-        const long cost = (tok + la::CH - 1) / la::CH + 1;
-        std::pop_heap(heap.begin(), heap.end(), std::greater<long>());
-        heap.back() += cost;
-        finish = std::max(finish, heap.back());
-        std::push_heap(heap.begin(), heap.end(), std::greater<long>());
-      }
-    }
-    if (best_t < 0 || finish <= best_t) {
-      best_t = finish;
-      best = kb;
-    }
+// Compute units of the current device (cached per device; 256 on MI355X).
+long device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>& c = cache[dev < 64 ? dev : 63];
+  int n = c.load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    c.store(n, std::memory_order_relaxed);
   }
-  return best;
+  return n;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -148,9 +130,10 @@ struct WsLayout {
 //   word and flags;
 // fwd non-causal: aggregates and their scan (its last entry is the total);
 // bwd non-causal: both for the key side and for the reverse side;
-// bwd: aggregates and prefix states to recompute a missing checkpoint, and
-//   the reverse aggregates (scanned in place) when there is more than one
-//   segment.
+// bwd: aggregates and prefix states to recompute a missing checkpoint, the
+//   reverse aggregates (scanned in place) when there is more than one
+//   segment, and the per-token pair (1/den, O.dO) passed from the query
+//   pass to the key pass.
 WsLayout ws_layout(int op, const Plan& p) {
   WsLayout w;
   if (p.nseg == 0) return w;
@@ -170,6 +153,7 @@ WsLayout ws_layout(int op, const Plan& p) {
       w.agg = state_bytes(p, p.nseg);       // checkpoint recomputation only
       w.ckpt = state_bytes(p, p.nseg + 1);  // checkpoint recomputation only
       if (p.nseg > 1) w.ragg = state_bytes(p, p.nseg);
+      w.gc = align256((size_t)p.BH * p.N * 2 * sizeof(float));  // (1/den, O.dO) per token
       break;
     case LA_OP_BWD_NONCAUSAL:  // key aggregates and their scan; reverse aggregates and their scan
       w.agg = state_bytes(p, p.nseg);
@@ -211,6 +195,18 @@ int check_sizes(int B, int H, int N, int D, int M, int dtype) {
   return LA_OK;
 }
 
+int check_opts(const la_options* o) {
+  if (!o) return LA_OK;
+  if (o->segment_chunks < 0) return fail(LA_ERR_ARG, "opts->segment_chunks must be >= 0");
+  if (o->forward_form < LA_FORM_AUTO || o->forward_form > LA_FORM_ONE_LAUNCH)
+    return fail(LA_ERR_ARG, "opts->forward_form must be LA_FORM_AUTO, LA_FORM_TWO_LAUNCH or LA_FORM_ONE_LAUNCH");
+  if (o->timed_kernel && (!o->events || !o->events_used || o->event_pairs < 0))
+    return fail(LA_ERR_ARG, "opts->timed_kernel needs events, event_pairs >= 0 and events_used");
+  if (o->status && reinterpret_cast<uintptr_t>(o->status) % 4)
+    return fail(LA_ERR_ALIGN, "opts->status is not 4-byte aligned");
+  return LA_OK;
+}
+
 struct Range {
   const char* name;
   uintptr_t lo, hi;  // [lo, hi)
@@ -238,61 +234,33 @@ Range rng(const char* name, const void* p, size_t bytes, bool out) {
   return Range{name, lo, lo ? lo + bytes : 0, out};
 }
 
-// ------------------------------------------------------------- profiling
-struct Prof {
-  std::mutex mu;
-  std::string sel;
-  std::vector<hipEvent_t> ev;  // pairs
-  size_t used = 0;             // pairs recorded
-  int dropped = 0;
-  static constexpr size_t kMax = 65536;
+// ------------------------------------------------------------ launching
+// What a launch needs besides its arguments: the stream and the caller's
+// options (timing events among them).
+struct Call {
+  hipStream_t s;
+  const la_options* o;
 };
-Prof& prof() {
-  static Prof* p = new Prof();  // never destroyed: events outlive static teardown order
-  return *p;
-}
 
-int prof_begin(const char* name, hipStream_t s) {
-  Prof& P = prof();
-  std::lock_guard<std::mutex> lk(P.mu);
-  if (P.sel.empty() || P.sel != name) return -1;
-  if (P.used >= Prof::kMax) {
-    ++P.dropped;
-    return -1;
-  }
-  if (P.ev.size() < 2 * (P.used + 1)) {
-    // timing-only events: without the system-scope fence (an L2 write-back
-    // and invalidate at each record, about 2.8 us per event between kernels);
-    // their times are read only after the caller has synchronised the device
-    hipEvent_t a, b;
-    if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return -1;
-    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
-      (void)hipEventDestroy(a);
-      return -1;
-    }
-    P.ev.push_back(a);
-    P.ev.push_back(b);
-  }
-  const int idx = (int)P.used++;
-  (void)hipEventRecord(P.ev[2 * idx], s);
-  return idx;
-}
-
-void prof_end(int idx, hipStream_t s) {
-  if (idx < 0) return;
-  Prof& P = prof();
-  std::lock_guard<std::mutex> lk(P.mu);
-  (void)hipEventRecord(P.ev[2 * idx + 1], s);
+bool timed(const Call& c, const char* name) {
+  const la_options* o = c.o;
+  return o && o->timed_kernel && o->events && o->events_used && *o->events_used >= 0 &&
+         *o->events_used < o->event_pairs && std::strcmp(o->timed_kernel, name) == 0;
 }
 
 template <typename Kern, typename... Args>
-int launch(const char* name, Kern kern, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+int launch(const char* name, Kern kern, dim3 grid, dim3 block, const Call& c, Args... args) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LA_OK;
-  const int idx = prof_begin(name, s);
-  hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
+  const bool ev = timed(c, name);
+  hipEvent_t* pair = ev ? reinterpret_cast<hipEvent_t*>(c.o->events) + 2 * (*c.o->events_used) : nullptr;
+  if (ev && hipEventRecord(pair[0], c.s) != hipSuccess) return fail(LA_ERR_HIP, std::string(name) + ": event record");
+  hipLaunchKernelGGL(kern, grid, block, 0, c.s, args...);
   const hipError_t e = hipGetLastError();
-  prof_end(idx, s);
   if (e != hipSuccess) return fail(LA_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e));
+  if (ev) {
+    if (hipEventRecord(pair[1], c.s) != hipSuccess) return fail(LA_ERR_HIP, std::string(name) + ": event record");
+    ++*c.o->events_used;
+  }
   return LA_OK;
 }
 
@@ -317,13 +285,13 @@ char* region(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 dim3 scan_grid(const Plan& p) { return dim3((unsigned)p.BH, (unsigned)((p.SV + la::NT - 1) / la::NT)); }
 
 template <typename T, int D, int M>
-int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, int fm, hipStream_t s) {
+int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, int fm, const Call& s) {
   return launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)K, (const T*)V, agg, N, p.L, p.nseg, fm);
 }
 
 template <int D, int M>
-int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z0, float* pref, hipStream_t s,
+int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z0, float* pref, const Call& s,
                 int last_only = 0) {
   return launch("scan_states", la::k_scan_states<D, M>, scan_grid(p), dim3(la::NT), s, agg, S0, Z0, pref, p.nseg,
                 last_only);
@@ -339,13 +307,13 @@ int scan_prefix(const Plan& p, const float* agg, const float* S0, const float* Z
 // 25.6 us per 3072-token bf16 layer of 4x8 heads, so those keep two launches).
 // The automatic rule also requires the whole grid to be resident at once, so
 // that no wait depends on the order in which workgroups are dispatched.
-// la_set_forward_onepass: 0 never, 1 by this rule (default), 2 wherever the
-// segments allow.
-std::atomic<int> g_fwd_onepass{1};
+// la_options::forward_form: LA_FORM_AUTO by this rule (the default),
+// LA_FORM_TWO_LAUNCH never, LA_FORM_ONE_LAUNCH wherever the segments allow.
 // Polls of a one-launch forward's wait for an earlier segment's flag before
 // it gives up (each poll waits for a device-scope load of about a
-// microsecond, so 2^22 polls are a few seconds).
-std::atomic<int> g_lb_polls{1 << 22};
+// microsecond, so 2^22 polls are a few seconds): la_options::wait_polls.
+constexpr int kDefaultPolls = 1 << 22;
+int opt_polls(const la_options* o) { return !o || o->wait_polls == 0 ? kDefaultPolls : o->wait_polls < 0 ? 0 : o->wait_polls; }
 
 // workgroups of the one-launch forward resident per compute unit
 template <typename T, int D, int M, int NC>
@@ -360,17 +328,17 @@ int onepass_resident() {
 }
 
 template <typename T, int D, int M>
-bool use_onepass(const Plan& p) {
-  const int mode = g_fwd_onepass.load(std::memory_order_relaxed);
-  if (mode == 0 || p.nseg <= 1 || p.L > 4 * la::CH || use_scan(p)) return false;
-  if (mode == 2) return true;
+bool use_onepass(const Plan& p, const la_options* o) {
+  const int mode = o ? o->forward_form : LA_FORM_AUTO;
+  if (mode == LA_FORM_TWO_LAUNCH || p.nseg <= 1 || p.L > 4 * la::CH || use_scan(p)) return false;
+  if (mode == LA_FORM_ONE_LAUNCH) return true;
   const int resident = p.L <= 2 * la::CH ? onepass_resident<T, D, M, 2>() : onepass_resident<T, D, M, 4>();
-  return D * M >= 2048 && p.BH * p.nseg <= (long)resident * kCUs;
+  return D * M >= 2048 && p.BH * p.nseg <= (long)resident * device_cus();
 }
 
 template <typename T, int D, int M, int NC>
 int fwd_onepass(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
-                const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, hipStream_t s) {
+                const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, const Call& s) {
   const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
   unsigned* sync = reinterpret_cast<unsigned*>(region(ws, wl.agg + wl.ckpt));
@@ -380,16 +348,16 @@ int fwd_onepass(const Plan& p, const void* Q, const void* K, const void* V, void
   if (st) return st;
   return launch("fwd_causal", la::k_fwd_lb<T, D, M, NC>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, S0, Z0, agg, sync, ckpt, S_out, Z_out, N, p.L,
-                p.nseg, fm, g_lb_polls.load(std::memory_order_relaxed));
+                p.nseg, fm, opt_polls(s.o), s.o ? s.o->status : (unsigned*)nullptr);
 }
 
 template <typename T, int D, int M>
 int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* den, const float* S0,
-                    const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, hipStream_t s) {
+                    const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm, const Call& s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
-  if (use_onepass<T, D, M>(p)) {
+  if (use_onepass<T, D, M>(p, s.o)) {
     if (p.L <= 2 * la::CH)
       return fwd_onepass<T, D, M, 2>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
     return fwd_onepass<T, D, M, 4>(p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm, s);
@@ -418,7 +386,7 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
 template <typename T, int D, int M>
 int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, void* O, float* S_out,
                        float* Z_out, int N, void* ws,
-                       int fm, hipStream_t s) {
+                       int fm, const Call& s) {
   if (p.nseg == 0)  // empty sequence: zero totals
     return S_out ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s,
                           (const float*)nullptr, (const float*)nullptr, (float*)nullptr, S_out, Z_out)
@@ -440,25 +408,13 @@ int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
                 p.L, p.nseg, fm);
 }
 
-// backward workgroups resident per compute unit (LDS and registers)
-template <typename T, int D, int M>
-int backward_resident() {
-  static const int n = [] {
-    int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, la::k_bwd<T, D, M>, la::BwdShape<T, D, M>::NTH, 0) !=
-            hipSuccess ||
-        r < 1)
-      r = 1;
-    return r;
-  }();
-  return n;
-}
-
 template <typename T, int D, int M>
 int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* O, const float* den,
                     const void* dO, const float* S0, const float* Z0, const float* ckpt, const float* dSN,
                     const float* dZN, void* dQ, void* dK, void* dV, float* dS0, float* dZ0, int N, void* ws,
-                    int fm, hipStream_t s) {
+                    int fm, const Call& s) {
+  (void)O;  // the query pass recomputes den and O.dO from the forward states (see la_bwd2.h)
+  (void)den;
   if (p.nseg == 0)  // empty sequence: the initial state is the final state
     return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
                         (float*)nullptr, dS0, dZ0)
@@ -475,28 +431,25 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
     if (st) return st;
     ck = ckw;
   }
-  float* ragg = nullptr;
+  float* ragg = p.nseg > 1 ? reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt)) : nullptr;
+  float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  st = launch("bwd_query", la::k_bq<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+              (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm);
+  if (st) return st;
   const int scanned = p.nseg > 1 && use_scan(p) ? 1 : 0;
-  if (p.nseg > 1) {
-    ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
-    st = launch("seg_rstate", la::k_seg_rstate<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)Q, (const T*)O, den, (const T*)dO, ragg, N, p.L, p.nseg, fm);
+  if (scanned) {
+    st = launch("scan_rev", la::k_scan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, p.nseg);
     if (st) return st;
-    if (scanned) {
-      st = launch("scan_rev", la::k_scan_rev<D, M>, scan_grid(p), dim3(la::NT), s, ragg, p.nseg);
-      if (st) return st;
-    }
   }
-  const int kb = backward_group(p, N, backward_resident<T, D, M>());
-  const int nsegb = (p.nseg + kb - 1) / kb;
-  return launch("bwd_causal", la::k_bwd<T, D, M>, dim3((unsigned)(p.BH * nsegb)), dim3(la::BwdShape<T, D, M>::NTH), s,
-                (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, ck, (const float*)ragg, dSN, dZN, (T*)dQ, (T*)dK,
-                (T*)dV, dS0, dZ0, N, p.L * kb, nsegb, kb, p.nseg, scanned, fm);
+  return launch("bwd_kv", la::k_bkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+                (const T*)dO, (const float2*)gc, (const float*)ragg, dSN, dZN, (T*)dK, (T*)dV, dS0, dZ0, N, p.L,
+                p.nseg, scanned, fm);
 }
 
 template <typename T, int D, int M>
 int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO,
-                       const float* St, const float* Zt, void* dQ, void* dK, void* dV, int N, void* ws, int fm, hipStream_t s) {
+                       const float* St, const float* Zt, void* dQ, void* dK, void* dV, int N, void* ws, int fm, const Call& s) {
   if (p.nseg == 0) return LA_OK;
   const WsLayout wl = ws_layout(LA_OP_BWD_NONCAUSAL, p);
   float* agg = reinterpret_cast<float*>(region(ws, 0));
@@ -530,7 +483,7 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
 template <typename T, int D, int M>
 int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, void* O,
                    float* den, const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int N,
-                   void* ws, int fm, hipStream_t s) {
+                   void* ws, int fm, const Call& s) {
   if (p.nseg == 0)
     return launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
                   Z_out);
@@ -556,7 +509,7 @@ int fwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
 template <typename T, int D, int M>
 int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, const float* logA, const void* dO,
                    const float* S0, const float* Z0, const float* ckpt, const float* dSN, const float* dZN, void* dQ,
-                   void* dK, void* dV, float* dlogA, float* dS0, float* dZ0, int N, void* ws, int fm, hipStream_t s) {
+                   void* dK, void* dV, float* dlogA, float* dS0, float* dZ0, int N, void* ws, int fm, const Call& s) {
   if (p.nseg == 0)
     return dS0 ? launch("state_copy", la::k_state_copy<D, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
                         (float*)nullptr, dS0, dZ0)
@@ -596,7 +549,7 @@ int bwd_decay_impl(const Plan& p, const void* Q, const void* K, const void* V, c
 
 template <typename T, int D, int M>
 int decode_impl(long BH, const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
-                int fm, hipStream_t s) {
+                int fm, const Call& s) {
   return launch("decode", la::k_decode<T, D, M>, dim3((unsigned)((BH + 3) / 4)), dim3(la::NT), s, (const T*)q,
                 (const T*)k, (const T*)v, logA, S, Z, (T*)y, (int)BH, fm);
 }
@@ -624,7 +577,7 @@ size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 // projection is as large as a chunk of X, so one chunk per workgroup would
 // stage twice the data it maps).
 template <typename T, int DIN, int C>
-int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const void* dPhi, void* out, hipStream_t s) {
+int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const void* dPhi, void* out, const Call& s) {
   const long nch = (N + la::CH - 1) / la::CH;
   long cpw = (BH * nch + 1023) / 1024;
   cpw = cpw < 1 ? 1 : cpw > nch ? nch : cpw;
@@ -636,7 +589,7 @@ int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const voi
 }
 
 template <typename T, int C>
-int feat_poly2_impl(long rows, int din, const void* X, const void* dPhi, void* out, hipStream_t s) {
+int feat_poly2_impl(long rows, int din, const void* X, const void* dPhi, void* out, const Call& s) {
   const dim3 grid((unsigned)((rows + la::NT - 1) / la::NT));
   if (dPhi)
     return launch("feat_poly2_vjp", la::k_feat_poly2_vjp<T, C>, grid, dim3(la::NT), s, (const T*)X,
@@ -657,7 +610,7 @@ int feature_random(const void* X, const float* W, const void* dPhi, void* out, i
                    rng("dPhi", dPhi, bh * N * C * es, false),
                    rng(dPhi ? "dX" : "Phi", out, bh * N * (dPhi ? Din : C) * es, true)});
   if (st) return st;
-  LA_FEAT_DISPATCH(dtype, Din, C, feat_rf_impl, (long)bh, H, N, X, W, dPhi, out, (hipStream_t)stream);
+  LA_FEAT_DISPATCH(dtype, Din, C, feat_rf_impl, (long)bh, H, N, X, W, dPhi, out, Call{(hipStream_t)stream, nullptr});
 }
 
 int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int N, int Din, int C, int dtype,
@@ -676,19 +629,24 @@ int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int 
   if (st) return st;
   const long rows = (long)bh * N;
   if (dtype == LA_F32) {
-    if (C == 32) return feat_poly2_impl<float, 32>(rows, Din, X, dPhi, out, (hipStream_t)stream);
-    return feat_poly2_impl<float, 64>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+    if (C == 32) return feat_poly2_impl<float, 32>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
+    return feat_poly2_impl<float, 64>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
   }
-  if (C == 32) return feat_poly2_impl<la::bf16_t, 32>(rows, Din, X, dPhi, out, (hipStream_t)stream);
-  return feat_poly2_impl<la::bf16_t, 64>(rows, Din, X, dPhi, out, (hipStream_t)stream);
+  if (C == 32) return feat_poly2_impl<la::bf16_t, 32>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
+  return feat_poly2_impl<la::bf16_t, 64>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
 }
+
+int forward_causal_entry(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
+                         const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H,
+                         int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
+                         const la_options* opts);
 
 }  // namespace
 
 #pragma GCC visibility push(default)
 extern "C" {
 
-int la_version(void) { return 100; }
+int la_version(void) { return 200; }
 
 const char* la_status_string(int status) {
   switch (status) {
@@ -702,6 +660,7 @@ const char* la_status_string(int status) {
     case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
     case LA_ERR_HIP: return "LA_ERR_HIP";
     case LA_ERR_ARG: return "LA_ERR_ARG";
+    case LA_ERR_WAIT: return "LA_ERR_WAIT";
     default: return "LA_ERR_UNKNOWN";
   }
 }
@@ -709,58 +668,80 @@ const char* la_status_string(int status) {
 const char* la_last_error(void) { return g_err.c_str(); }
 
 const char* la_kernel_names(void) {
-  return "seg_state,fwd_causal,fwd_noncausal,seg_rstate,bwd_causal,nc_qr,nc_kv,decode,scan_states,scan_rev,"
+  return "seg_state,fwd_causal,fwd_noncausal,bwd_query,bwd_kv,nc_qr,nc_kv,decode,scan_states,scan_rev,"
          "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
          "feat_poly2_vjp,sync_clear";
 }
 
-size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype) {
+size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype, const la_options* opts) {
   if (check_sizes(B, H, N, D, M, dtype) != LA_OK) return 0;
   if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
   const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
                   op == LA_OP_BWD_DECAY;
-  return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : 0)).bytes();
+  return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : 0, opt_chunks(opts))).bytes();
 }
 
-size_t la_checkpoint_size(int B, int H, int N, int D, int M) {
+size_t la_checkpoint_size(int B, int H, int N, int D, int M, const la_options* opts) {
   if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
-  const Plan p = make_plan(B, H, N, D, M);
+  const Plan p = make_plan(B, H, N, D, M, 0, opt_chunks(opts));
   return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float);
 }
 
-int la_segment_length(int B, int H, int N, int D, int M) {
+int la_segment_length(int B, int H, int N, int D, int M, const la_options* opts) {
   if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
-  return make_plan(B, H, N, D, M).L;
+  return make_plan(B, H, N, D, M, 0, opt_chunks(opts)).L;
 }
 
-int la_set_segment_chunks(int chunks) {
-  if (chunks < 0) return -1;
-  return g_seg_chunks.exchange(chunks);
-}
-
-int la_set_forward_onepass(int mode) {
-  if (mode < 0 || mode > 2) return -1;
-  return g_fwd_onepass.exchange(mode);
-}
-
-int la_set_wait_polls(int polls) {
-  if (polls < 0) return -1;
-  return g_lb_polls.exchange(polls);
+int la_forward_wait_status(const void* ws, size_t ws_bytes, int B, int H, int N, int D, int M, int dtype,
+                           void* stream, const la_options* opts) {
+  g_err.clear();
+  int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  st = check_opts(opts);
+  if (st) return st;
+  const Plan p = make_plan(B, H, N, D, M, 0, opt_chunks(opts));
+  const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
+  if (wl.sync == 0) return LA_OK;  // no flags: never the one-launch form
+  if (!ws || ws_bytes < wl.bytes())
+    return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(wl.bytes()) + " bytes required");
+  unsigned word = 0;
+  const hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&word, region(const_cast<void*>(ws), wl.agg + wl.ckpt), sizeof(word), hipMemcpyDeviceToHost,
+                     s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(LA_ERR_HIP, std::string("reading the status word: ") + hipGetErrorString(hipGetLastError()));
+  return word ? fail(LA_ERR_WAIT, "a one-launch forward workgroup gave up waiting for an earlier segment") : LA_OK;
 }
 
 int la_forward_causal(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
                       const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H, int N,
-                      int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
+                      int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
+                      const la_options* opts) {
+  return forward_causal_entry(Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, B, H, N, D, M, dtype, feature, ws,
+                              ws_bytes, stream, opts);
+}
+
+}  // extern "C"
+#pragma GCC visibility pop
+
+namespace {
+
+int forward_causal_entry(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
+                         const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H,
+                         int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
+                         const la_options* opts) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
+  st = check_opts(opts);
+  if (st) return st;
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
@@ -772,30 +753,37 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
                    rng("Z0", Z0, bh * D * 4, false), rng("O", O, bh * N * M * es, true),
                    rng("den", den, bh * N * 4, true), rng("S_out", S_out, bh * D * M * 4, true),
                    rng("Z_out", Z_out, bh * D * 4, true),
-                   rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), true),
+                   rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M, opts), true),
                    rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
   if (N == 0 && !S_out && !ckpt) return LA_OK;
   if (logA)
     LA_DISPATCH(dtype, D, M, fwd_decay_impl, p, Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
-                fm, (hipStream_t)stream);
+                fm, Call{(hipStream_t)stream, opts});
   LA_DISPATCH(dtype, D, M, fwd_causal_impl, p, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
-              fm, (hipStream_t)stream);
+              fm, Call{(hipStream_t)stream, opts});
 }
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
 
 int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, float* S_out, float* Z_out, int B,
                          int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         void* stream, const la_options* opts) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
+  st = check_opts(opts);
+  if (st) return st;
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N == 0 && !S_out) return LA_OK;
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC);
+  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_FWD_NONCAUSAL, p).bytes();
   if (need > 0 && (ws == nullptr || ws_bytes < need))
@@ -805,19 +793,21 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, f
                    rng("S_out", S_out, bh * D * M * 4, true), rng("Z_out", Z_out, bh * D * 4, true),
                    rng("ws", need > 0 ? ws : nullptr, need, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, S_out, Z_out, N, ws, fm, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, S_out, Z_out, N, ws, fm, Call{(hipStream_t)stream, opts});
 }
 
 int la_backward_causal(const void* Q, const void* K, const void* V, const float* logA, const void* O,
                        const float* den, const void* dO, const float* S0, const float* Z0, const float* ckpt,
                        const float* dS_N, const float* dZ_N, void* dQ, void* dK, void* dV, float* dlogA, float* dS0,
                        float* dZ0, int B, int H, int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, const la_options* opts) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
+  if (st) return st;
+  st = check_opts(opts);
   if (st) return st;
   if ((logA == nullptr) != (dlogA == nullptr)) return fail(LA_ERR_ARG, "logA and dlogA must be given together");
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
@@ -829,23 +819,23 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
     st = check_ptrs({rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                      rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true)});
     if (st) return st;
-    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
+    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
     LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
-                dZ0, N, ws, fm, (hipStream_t)stream);
+                dZ0, N, ws, fm, Call{(hipStream_t)stream, opts});
   }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0);
+  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
   const size_t es = esize(dtype);
   const size_t need = ws_layout(logA ? LA_OP_BWD_DECAY : LA_OP_BWD_CAUSAL, p).bytes();
-  const bool uses_ws = need > 0 && (logA || ckpt == nullptr || p.nseg > 1);
+  const bool uses_ws = need > 0;
   if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
                    rng("V", V, bh * N * M * es, false), rng("logA", logA, bh * N * 4, false),
                    rng("O", O, bh * N * M * es, false), rng("den", den, bh * N * 4, false),
                    rng("dO", dO, bh * N * M * es, false), rng("S0", S0, bh * D * M * 4, false),
-                   rng("Z0", Z0, bh * D * 4, false), rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M), false),
+                   rng("Z0", Z0, bh * D * 4, false), rng("ckpt", ckpt, la_checkpoint_size(B, H, N, D, M, opts), false),
                    rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
                    rng("dV", dV, bh * N * M * es, true), rng("dlogA", dlogA, bh * N * 4, true),
@@ -854,24 +844,27 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
   if (st) return st;
   if (logA)
     LA_DISPATCH(dtype, D, M, bwd_decay_impl, p, Q, K, V, logA, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dlogA, dS0,
-                dZ0, N, ws, fm, (hipStream_t)stream);
+                dZ0, N, ws, fm, Call{(hipStream_t)stream, opts});
   LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0,
-              N, ws, fm, (hipStream_t)stream);
+              N, ws, fm, Call{(hipStream_t)stream, opts});
 }
 
 int la_backward_noncausal(const void* Q, const void* K, const void* V, const void* dO, const float* S_tot,
                           const float* Z_tot, void* dQ, void* dK, void* dV, int B, int H, int N, int D, int M,
-                          int dtype, int feature, void* ws, size_t ws_bytes, void* stream) {
+                          int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
+                          const la_options* opts) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, N, D, M, dtype);
   if (st) return st;
+  st = check_opts(opts);
+  if (st) return st;
   if (N == 0) return LA_OK;
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(LA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
   if ((S_tot == nullptr) != (Z_tot == nullptr)) return fail(LA_ERR_ARG, "S_tot and Z_tot must be given together");
-  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC);
+  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(LA_OP_BWD_NONCAUSAL, p).bytes();
   if (ws == nullptr || ws_bytes < need)
@@ -883,16 +876,18 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
                    rng("dV", dV, bh * N * M * es, true), rng("ws", ws, need, true)});
   if (st) return st;
   LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, S_tot, Z_tot, dQ, dK, dV, N, ws, fm,
-              (hipStream_t)stream);
+              Call{(hipStream_t)stream, opts});
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, const float* logA, float* S, float* Z, void* y,
-                   int B, int H, int D, int M, int dtype, int feature, void* stream) {
+                   int B, int H, int D, int M, int dtype, int feature, void* stream, const la_options* opts) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
   const int fm = feature;
   int st = check_sizes(B, H, 1, D, M, dtype);
+  if (st) return st;
+  st = check_opts(opts);
   if (st) return st;
   if (!q || !k || !v || !S || !Z || !y) return fail(LA_ERR_NULL, "q, k, v, S, Z and y are required");
   const size_t es = esize(dtype), bh = (size_t)B * H;
@@ -900,7 +895,7 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
                    rng("logA", logA, bh * 4, false), rng("S", S, bh * D * M * 4, true),
                    rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
   if (st) return st;
-  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, fm, (hipStream_t)stream);
+  LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, fm, Call{(hipStream_t)stream, opts});
 }
 
 int la_feature_random(const void* X, const float* W, void* Phi, int B, int H, int N, int Din, int C, int dtype,
@@ -928,35 +923,6 @@ int la_feature_poly2_vjp(const void* X, const void* dPhi, void* dX, int B, int H
     return fail(LA_ERR_NULL, "dPhi is required");
   }
   return feature_poly2(X, dPhi, dX, B, H, N, Din, C, dtype, stream);
-}
-
-int la_prof_select(const char* kernel_name) {
-  Prof& P = prof();
-  std::lock_guard<std::mutex> lk(P.mu);
-  P.sel = kernel_name ? kernel_name : "";
-  P.used = 0;
-  P.dropped = 0;
-  return LA_OK;
-}
-
-int la_prof_collect(double* total_ms, int* launches, int* dropped) {
-  Prof& P = prof();
-  std::lock_guard<std::mutex> lk(P.mu);
-  double sum = 0.0;
-  for (size_t i = 0; i < P.used; ++i) {
-    if (hipEventSynchronize(P.ev[2 * i + 1]) != hipSuccess)
-      return fail(LA_ERR_HIP, "hipEventSynchronize failed in la_prof_collect");
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]) != hipSuccess)
-      return fail(LA_ERR_HIP, "hipEventElapsedTime failed in la_prof_collect");
-    sum += ms;
-  }
-  if (total_ms) *total_ms = sum;
-  if (launches) *launches = (int)P.used;
-  if (dropped) *dropped = P.dropped;
-  P.used = 0;
-  P.dropped = 0;
-  return LA_OK;
 }
 
 }  // extern "C"

@@ -10,7 +10,7 @@
 // Work decomposition.  Each (batch*head) sequence is cut into segments of L
 // tokens (a multiple of 64); one workgroup of four wavefronts owns one (head,
 // segment) and walks its chunks in order, carrying the state (S, Z) -- in the
-// backward also the reverse state (R, r) -- in registers, with the chunk's
+// non-causal backward also the reverse totals (R, r) -- in registers, with the chunk's
 // operands staged once per chunk in LDS, token-major, as bf16 planes
 // (la_device.h) while the next chunk's global reads are in flight.  A
 // segment's start state is the sum, in a fixed order, of the aggregates of
@@ -43,10 +43,11 @@ struct Prec;
 template <>
 struct Prec<bf16_t> {
   // forward: phi(Q), phi(K) in A^T, phi(K) in the state update, V, S^T, A,
-  // Z (the denominator feeds the reverse-state aggregates, where errors of
-  // many tokens add up, so Z keeps two planes)
+  // Z (the denominator is an output, and a 1-plane Z would leave it at bf16
+  // accuracy; two planes keep it near float32)
   static constexpr int FQ = 1, FK = 1, FKF = 2, FV = 1, FS = 1, FA = 1, FZ = 2;
-  // backward staging: phi(Q), phi(K), V, dO, g, S, R
+  // backward staging (la_bwd2.h and the non-causal backward): phi(Q), phi(K),
+  // V, dO, [g | c], S, R
   static constexpr int NQ = 2, NK = 2, NV = 1, NDO = 1, NG = 2, NS = 2, NR = 2;
   // backward products
   static constexpr int dS_a = 1, dS_b = 2, Bt = 1, U1_a = 2, U1_b = 1, U2 = 2, Zc = 2, dR = 2, At = 2, Wt = 1,
@@ -63,30 +64,6 @@ struct Prec<float> {
 };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
-// Backward chunk: 32 tokens for every shape.  The 32-token chunk takes four
-// wavefronts instead of eight, so two workgroups share a compute unit and
-// each one's barriers overlap the other's work: measured on the
-// MNIST-shaped layer (float32, LDS 60 KB) 46 -> 40 us, on the 3072-token
-// bf16 stack 28.8 -> 24.7 us per layer, on the 2^16-token bf16 sequence
-// 395 -> 381 us, on the 64-feature layer (float32, D = 64, M = 32) 68.6 ->
-// 61.7 us, and 7-12 % on the other mixed shapes.  At float32 D = M = 64 the
-// planes of a 64-token chunk would not fit in LDS.
-template <typename T, int D, int M>
-struct BwdChunk {
-  static constexpr int value = 32;
-};
-// Where D or M is 64, two further changes keep a workgroup at four
-// wavefronts of at most 248 VGPRs and at most 78 KB of LDS (two per compute
-// unit): the S tiles are spread over all four wavefronts, not only the two
-// query ones, and phi(Q), phi(K) are read as sums of their bf16 planes rather
-// than from float32 copies.  float32 at D = M = 64 keeps the copies and the
-// query-held S (with the spread it still needs spill AGPRs, one wave per
-// SIMD either way, and measured 122.7 -> 132.6 us).
-template <typename T, int D, int M>
-struct BwdWide {
-  static constexpr bool value = (D == 64 || M == 64) && !(sizeof(T) == 4 && D == 64 && M == 64);
-};
 
 // State tiles.  Tile t = w + 4k of wave w covers feature block db = t % DB
 // (the same for all of the wave's tiles, since DB divides 4) and value block
@@ -505,13 +482,17 @@ __device__ __forceinline__ float ld_dev(const float* p) {
       __hip_atomic_load(reinterpret_cast<unsigned*>(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// true when the flag was seen set within `polls` polls
-__device__ __forceinline__ bool lb_wait(const unsigned* f, unsigned* err, int polls) {
+// true when the flag was seen set within `polls` polls (polls = 0: gives up
+// at once without looking).  A wait that gives up sets the status word err
+// and, when given, the caller's status word xerr.
+__device__ __forceinline__ bool lb_wait(const unsigned* f, unsigned* err, unsigned* xerr, int polls) {
   for (int it = 0; it < polls; ++it) {
     if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
     __builtin_amdgcn_s_sleep(2);
   }
+  if (polls > 0 && __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
   atomicOr(err, 1u);
+  if (xerr) atomicOr(xerr, 1u);
   return false;
 }
 
@@ -522,7 +503,7 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
                                                 const float* __restrict__ Z0, float* __restrict__ agg,
                                                 unsigned* __restrict__ sync, float* __restrict__ ckpt,
                                                 float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
-                                                int nseg, int fm, int polls) {
+                                                int nseg, int fm, int polls, unsigned* __restrict__ xstatus) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D, DS = D / 32;
   using KPlanes = Planes<P::FKF, CH, D>;
@@ -681,7 +662,7 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
 
   // carry: (S0, Z0) plus the earlier segments' aggregates, in segment order
   bool late = false;
-  for (int p = tid; p < seg; p += NT) late |= !lb_wait(&sync[1 + (size_t)bh * nseg + p], &sync[0], polls);
+  for (int p = tid; p < seg; p += NT) late |= !lb_wait(&sync[1 + (size_t)bh * nseg + p], &sync[0], xstatus, polls);
   const bool failed = __syncthreads_or(late);
   {
     const float* a0 = agg + (size_t)bh * nseg * SV;
@@ -849,626 +830,6 @@ __global__ __launch_bounds__(NT) void k_state_copy(const float* __restrict__ S0,
         S_out[(size_t)bh * D * M + e] = v;
       else
         Z_out[(size_t)bh * D + e - D * M] = v;
-    }
-  }
-}
-
-// ===================================================================== B1
-// Segment aggregates of the reverse state: ragg[bh][seg] =
-//   ( R = sum_i phi(Q_i) g_i^T [D][M],  r = sum_i c_i phi(Q_i) [D] )
-// i.e. the backward-running sums of eq. 14-15 over one segment, with the
-// upstream [g, c] of the numerator and the denominator (g_i = dO_i / den_i,
-// c_i = -(dO_i . O_i) / den_i), taken from the forward's O and den.  g is
-// staged with c as an extra column, so r is one more tile of R^T.
-template <typename T, int D, int M>
-__global__ __launch_bounds__(NT) void k_seg_rstate(const T* __restrict__ Q, const T* __restrict__ O,
-                                                    const float* __restrict__ den, const T* __restrict__ dO,
-                                                    float* __restrict__ ragg, int N, int L, int nseg, int fm) {
-  using P = Prec<T>;
-  constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
-  constexpr int E = IO<T>::E, PRM = M / E;
-  __shared__ Planes<P::dR, CH, D> qt;       // phi(Q)
-  __shared__ Planes<P::dR, CH, M + 16> gt;  // [g | c | 0]
-
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
-  const int t0 = seg * L, t1 = min(N, t0 + L);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const int db = w % DB;
-  const bool zw = w < DB;
-  const T* Qh = Q + (size_t)bh * N * D;
-  const T* Oh = O + (size_t)bh * N * M;
-  const T* dOh = dO + (size_t)bh * N * M;
-  const float* denh = den + (size_t)bh * N;
-  gt.zero_cols(M + 1, M + 16);
-
-  f32x4_t acc[NTW], accr = zero4();  // R^T layout; accr[0] on lanes g = 0 is r[16db + r16]
-#pragma unroll
-  for (int k = 0; k < NTW; ++k) acc[k] = zero4();
-
-  // two chunks of global reads in flight (see k_seg_state), den of each
-  // row this thread stages included
-  using RB = RowBuf<T, CH, M>;
-  RowBuf<T, CH, D> bq[2];
-  RB bo[2], bd[2];
-  float dn[2][RB::CNT];
-  auto fetch = [&](RowBuf<T, CH, D>& q_, RB& o_, RB& d_, float* dn_, int c0) {
-    const int nv = min(CH, t1 - c0);
-    if (nv > 0) {
-      q_.load(Qh + (size_t)c0 * D, nv);
-      o_.load(Oh + (size_t)c0 * M, nv);
-      d_.load(dOh + (size_t)c0 * M, nv);
-#pragma unroll
-      for (int i = 0; i < RB::CNT; ++i) {
-        const int r = RB::row_of(i);
-        dn_[i] = r < nv ? denh[c0 + r] : 1.f;
-      }
-    }
-  };
-  auto chunk = [&](RowBuf<T, CH, D>& q_, RB& o_, RB& d_, float* dn_, int c0) {
-    const int nv = min(CH, t1 - c0);
-    __syncthreads();
-    q_.stage_phi(qt, nv, nullptr, fm);
-    // g and c need den (per row) and dO . O (a row reduction over PRM lanes)
-#pragma unroll
-    for (int i = 0; i < RB::CNT; ++i) {
-      const int r = RB::row_of(i), c = RB::col_of(i);
-      float xo[E], xd[E];
-      IO<T>::unpack(o_.r[i], xo);
-      IO<T>::unpack(d_.r[i], xd);
-      const float inv = r < nv ? 1.f / dn_[i] : 0.f;
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        part += xd[e] * xo[e];
-        xd[e] *= inv;
-      }
-#pragma unroll
-      for (int off = PRM / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-      gt.template put<E>(r, c, xd);
-      if (c == 0) gt.put1(r, M, -part * inv);
-    }
-    fetch(q_, o_, d_, dn_, c0 + 2 * CH);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-      const Frag<P::dR> qb = qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16);
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) {
-        const int mb = (w + 4 * k) / DB;
-        mmaf<P::dR, P::dR>(acc[k], gt.template tfrag<P::dR>(32 * s, 16 * mb, g, r16), qb);
-      }
-      if (zw) mmaf<P::dR, P::dR>(accr, gt.template tfrag<P::dR>(32 * s, M, g, r16), qb);
-    }
-  };
-  fetch(bq[0], bo[0], bd[0], dn[0], t0);
-  fetch(bq[1], bo[1], bd[1], dn[1], t0 + CH);
-  for (int c0 = t0; c0 < t1; c0 += 2 * CH) {
-    chunk(bq[0], bo[0], bd[0], dn[0], c0);
-    if (c0 + CH < t1) chunk(bq[1], bo[1], bd[1], dn[1], c0 + CH);
-  }
-  float* out = ragg + ((size_t)bh * nseg + seg) * SV;
-  store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
-  if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
-}
-
-// ===================================================================== B3
-// Backward over one segment, chunks in reverse order.  A backward segment is
-// kb consecutive segments of the checkpoint ([bh][nseg + 1] states); its end
-// state is checkpoint entry min((sb+1) kb, nseg).
-//
-// Per chunk the gradients are
-//   dQ: with u_i = S_i dO_i, Z_i the inclusive normaliser, den_i =
-//     phi(Q_i).Z_i and O_i.dO_i = phi(Q_i).u_i / den_i (both recomputed
-//     here), dphiQ_i = (u_i - Z_i (O_i.dO_i)) / den_i, which is eq. 13's
-//     S_i g_i plus the denominator's share c_i Z_i (g_i = dO_i / den_i,
-//     c_i = -(O_i.dO_i) / den_i);
-//   dK, dV: dphiK_j = sum_{i>=j} phi(Q_i)(dO_i.V_j - O_i.dO_i) / den_i
-//     + R V_j + r, dV_j = sum_{i>=j} g_i (phi(Q_i).phi(K_j)) + R^T phi(K_j)
-//     (eq. 14-15 on [V, 1] with upstream [g, c]);
-// and the chain rule through phi.  The stored O and den are not read: the
-// recomputed den_i and O_i.dO_i are exact to float32, so dO_i.V_j - O_i.dO_i
-// cancels exactly where V_j = O_i even for bf16 storage.
-//
-// Walking backwards, the state after a chunk is known before the chunk is
-// processed (it is the state before the later chunk), so the query side uses
-//   S_i = S_after - sum_{j>i in the chunk} phi(K_j) V_j^T,
-//   Z_i = Z_after - sum_{j>i in the chunk} phi(K_j),
-// the complement of the causal mask, and the state before the chunk
-// (S_after minus the chunk's whole contribution) is formed for the next
-// chunk while the gradients are finished.  The first chunk of the sequence
-// is the exception: its S_i may be far smaller than S_after (a few tokens of
-// history against a whole chunk), so the subtraction would cancel; there the
-// state before the chunk -- the initial state, checkpoint entry 0 -- is
-// staged instead and the causal sum over j <= i is added.
-//
-// Two roles of RB = CB / 16 wavefronts each: with the 32-token chunk
-// (BwdChunk) four wavefronts, and two workgroups per compute unit, so that
-// each SIMD interleaves two instruction streams.  Query wavefront q owns query rows 16q..16q+15 and the tiles of the
-// reverse state R (backward sum of phi(Q) g^T, eq. 14-15, started from the
-// gradient of the final state (dSN, dZN; zero when absent) plus the reverse
-// aggregates of all later checkpoint segments: entry f1 - 1 of `ragg` when it
-// holds suffix sums (scanned = 1), else their sum in segment order).  Every
-// term phi(K_j) V_j^T is part of the final state, hence the start value; the
-// initial state is part of every S_i, so its gradient (dS0, dZ0) is R, r
-// carried through the sequence's first token, written by that segment.
-// Key wavefront k owns key rows 16 (RB-1-k)..; it shares a SIMD with query
-// wavefront k, whose work falls with k while the key rows' work (all later
-// rows of the chunk) rises with k.  The tiles of S (forward sum of
-// phi(K) V^T, eq. 13) and Z are held by the query wavefronts (the key
-// wavefronts carry the longest phase), by all wavefronts where D or M is 64
-// (BwdWide: the registers a query wavefront would need).  Phases
-// of a chunk, separated by barriers:
-//   stage   all: phi(Q), phi(K), V, dO to LDS; next chunk's reads issued
-//   B  query: dQ, g, c, 1/den          key: A_ij, dO_i.V_j, R V_j
-//   C  query: R, r += this chunk; S, Z before the chunk, staged as the next
-//      chunk's S_after                 key: R^T phi(K_j), intra-chunk dK, dV
-// (R, r are staged for the next chunk after the barrier that ends C).
-template <typename T, int D, int M>
-struct BwdShape {
-  static constexpr int CB = BwdChunk<T, D, M>::value;
-  static constexpr int RB = CB / 16;  // row blocks per chunk
-  static constexpr int NW = 2 * RB;   // wavefronts: RB per role
-  static constexpr int NTH = 64 * NW;
-};
-
-template <typename T, int D, int M>
-__global__ __launch_bounds__((BwdShape<T, D, M>::NTH)) void k_bwd(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ ckpt, const float* __restrict__ ragg, const float* __restrict__ dSN,
-    const float* __restrict__ dZN, T* __restrict__ dQ, T* __restrict__ dK, T* __restrict__ dV,
-    float* __restrict__ dS0, float* __restrict__ dZ0, int N, int L, int nsegb, int kb, int nseg, int scanned, int fm) {
-  using P = Prec<T>;
-  using BS = BwdShape<T, D, M>;
-  constexpr int CB = BS::CB, RB = BS::RB, NW = BS::NW, NTH = BS::NTH, NPAIR = CB / 32;
-  constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
-  constexpr int NTR = DB * MB / RB;                 // R tiles per query wavefront
-  constexpr int NWS = BwdWide<T, D, M>::value ? NW : RB < DB * MB ? RB : DB * MB;  // wavefronts holding S tiles
-  constexpr int NTS = DB * MB / NWS;                // S tiles per holder
-  constexpr int NZS = (DB + NWS - 1) / NWS;         // Z blocks per holder: so + NWS j
-  constexpr int NZW = (DB + RB - 1) / RB;           // r blocks per query wavefront
-  static_assert((DB * MB) % RB == 0 && (DB * MB) % NWS == 0, "state tiles must divide evenly");
-  __shared__ Planes<P::NQ, CB, D> qt;       // phi(Q)
-  __shared__ Planes<P::NK, CB, D> kt;       // phi(K)
-  __shared__ Planes<P::NV, CB, M> vt;       // V
-  __shared__ Planes<P::NDO, CB, M> ot;      // dO
-  __shared__ Planes<P::NG, CB, M + 16> gt;  // [g | c | 0], g = dO / den
-  __shared__ Planes<P::NS, D, M> sp;        // S after this chunk, [d][m]
-  __shared__ Planes<P::NR, D, M> rp;        // R after this chunk, [d][m]
-  // phi(Q), phi(K) as float32 for the elementwise terms; rows padded by 4 so
-  // the 16 rows a fragment reads start in different banks
-  constexpr bool F32C = !BwdWide<T, D, M>::value;  // float32 copies of phi(Q), phi(K)
-  __shared__ alignas(16) float q32[F32C ? CB : 1][D + 4];
-  __shared__ alignas(16) float k32[F32C ? CB : 1][D + 4];
-  __shared__ alignas(16) float sZ[D];     // Z after this chunk
-  __shared__ alignas(16) float sr[D];     // r after this chunk
-  __shared__ alignas(16) float sInv[CB];  // 1 / den_i (0 past the end)
-  __shared__ alignas(16) float sOdo[CB];  // O_i . dO_i (0 past the end)
-
-  const int sb = blockIdx.x % nsegb, bh = blockIdx.x / nsegb;
-  const int t0 = sb * L, t1 = min(N, t0 + L);
-  const int f1 = min(sb * kb + kb, nseg);  // checkpoint entry of the segment's end
-  const bool seqstart = t0 == 0;           // the segment holds the sequence's first chunk
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const bool qrole = w < RB;     // query wavefront, else key wavefront
-  const int rb = w % RB;         // row block of the wavefront
-  const int so = w;              // rank among the S holders (query wavefronts first)
-  const bool shold = so < NWS;   // holds S tiles
-  const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
-  const Frag<1> ones = ones_frag();
-  gt.zero_cols(M + 1, M + 16, NTH);
-
-  // R tile k of a query wavefront: t = rb + RB k; S tile k of a holder: t = so + NWS k;
-  // feature block t % DB, value block t / DB
-  auto rdb = [&](int k) { return (rb + RB * k) % DB; };
-  auto rmb = [&](int k) { return (rb + RB * k) / DB; };
-  auto sdb = [&](int k) { return (so + NWS * k) % DB; };
-  auto smb = [&](int k) { return (so + NWS * k) / DB; };
-
-  const float* st_end = ckpt + ((size_t)bh * (nseg + 1) + f1) * SV;
-  const float* st_init = ckpt + (size_t)bh * (nseg + 1) * SV;  // the initial state
-
-  const int nchunk = (t1 - t0 + CB - 1) / CB;
-  // a tensor with half as many vectors per chunk as threads goes to one half of the workgroup
-  constexpr int OK_ = RowBuf<T, CB, D, NTH>::VEC < NTH ? NTH / 2 : 0;
-  constexpr int OD_ = RowBuf<T, CB, M, NTH>::VEC < NTH ? NTH / 2 : 0;
-  RowBuf<T, CB, D, NTH> bq;
-  RowBuf<T, CB, D, NTH, OK_> bk;
-  RowBuf<T, CB, M, NTH> bv;
-  RowBuf<T, CB, M, NTH, OD_> bd;
-  {
-    const int c0 = t0 + (nchunk - 1) * CB, nv = min(CB, t1 - c0);
-    bq.load(Q + offD + (size_t)c0 * D, nv);
-    bk.load(K + offD + (size_t)c0 * D, nv);
-    bv.load(V + offM + (size_t)c0 * M, nv);
-    bd.load(dO + offM + (size_t)c0 * M, nv);
-  }
-
-  // S^T and R^T tiles in the layout of add_ST_tiles
-  f32x4_t accS[NTS], accR[NTR];
-  float zr[NZW];   // query: r of features 16 (rb + RB j) + r16
-  float zz[NZS];   // Z of features 16 (so + NWS j) + r16
-#pragma unroll
-  for (int j = 0; j < NZS; ++j) zz[j] = 0.f;
-#pragma unroll
-  for (int k = 0; k < NTR; ++k) accR[k] = zero4();
-#pragma unroll
-  for (int j = 0; j < NZW; ++j) zr[j] = 0.f;
-  // S, Z after the last chunk: the segment's end state
-  auto stage_S = [&]() {
-    float v4[4];
-#pragma unroll
-    for (int k = 0; k < NTS; ++k) {
-      acc_to4(accS[k], v4);
-      sp.put4(16 * sdb(k) + r16, 16 * smb(k) + 4 * g, v4);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZS; ++j)
-        if (so + NWS * j < DB) sZ[16 * (so + NWS * j) + r16] = zz[j];
-    }
-  };
-  auto load_S = [&](const float* src) {
-#pragma unroll
-    for (int k = 0; k < NTS; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(src + (16 * sdb(k) + r16) * M + 16 * smb(k) + 4 * g);
-      accS[k] = f32x4_t{a.x, a.y, a.z, a.w};
-    }
-#pragma unroll
-    for (int j = 0; j < NZS; ++j)
-      if (so + NWS * j < DB) zz[j] = src[D * M + 16 * (so + NWS * j) + r16];
-  };
-  if (shold) {
-    load_S(seqstart && nchunk == 1 ? st_init : st_end);
-    stage_S();
-  }
-  const float* rg = ragg ? ragg + (size_t)bh * nseg * SV : nullptr;
-  if (rg || dSN) {  // final-state gradient plus the reverse aggregates of the later segments, summed
-                    // through R's planes as scratch
-    const int r0 = !rg ? 0 : scanned ? f1 - 1 : f1, r1 = !rg ? 0 : scanned ? f1 : nseg;
-    static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
-    float* sbuf = reinterpret_cast<float*>(&rp.v[0][0][0]);
-    sum_states<D, M, NTH>(sbuf, dSN ? dSN + (size_t)bh * D * M : nullptr, dZN ? dZN + (size_t)bh * D : nullptr, rg,
-                          r0, r1);
-    __syncthreads();
-    if (qrole) {
-#pragma unroll
-      for (int k = 0; k < NTR; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(sbuf + (16 * rdb(k) + r16) * M + 16 * rmb(k) + 4 * g);
-        accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
-      }
-#pragma unroll
-      for (int j = 0; j < NZW; ++j)
-        if (rb + RB * j < DB) zr[j] = sbuf[D * M + 16 * (rb + RB * j) + r16];
-    }
-    __syncthreads();
-  }
-  // R and r after the chunk about to be processed
-  auto stage_R = [&]() {
-    float v4[4];
-#pragma unroll
-    for (int k = 0; k < NTR; ++k) {
-      acc_to4(accR[k], v4);
-      rp.put4(16 * rdb(k) + r16, 16 * rmb(k) + 4 * g, v4);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZW; ++j)
-        if (rb + RB * j < DB) sr[16 * (rb + RB * j) + r16] = zr[j];
-    }
-  };
-  if (qrole) stage_R();
-
-  for (int ci = nchunk - 1; ci >= 0; --ci) {
-    const int c0 = t0 + ci * CB;
-    const int nv = min(CB, t1 - c0);
-    // ---- stage this chunk from registers, then start reading the previous one
-    // (the barrier ending the previous chunk separates its reads from these writes)
-    if constexpr (F32C) {
-      bq.template stage_phi<P::NQ, CB, D, 8, D + 4>(qt, nv, &q32[0][0], fm);
-      bk.template stage_phi<P::NK, CB, D, 8, D + 4>(kt, nv, &k32[0][0], fm);
-    } else {
-      bq.template stage_phi<P::NQ, CB, D, 8, 0>(qt, nv, nullptr, fm);
-      bk.template stage_phi<P::NK, CB, D, 8, 0>(kt, nv, nullptr, fm);
-    }
-    bv.stage_values(vt);
-    bd.stage_values(ot);
-    if (ci > 0) {
-      const int p0 = c0 - CB;
-      bq.load(Q + offD + (size_t)p0 * D, CB);
-      bk.load(K + offD + (size_t)p0 * D, CB);
-      bv.load(V + offM + (size_t)p0 * M, CB);
-      bd.load(dO + offM + (size_t)p0 * M, CB);
-    }
-    __syncthreads();
-
-    // ================= phase B
-    constexpr int NKT = cmax(P::At, P::VR);
-    constexpr int NVT = cmax(P::Wt, P::KR_b);
-    f32x4_t at[NPAIR][2], wt[NPAIR][2];  // key: raw A_ij, dO_i.V_j
-    f32x4_t gk[DB];                      // key: dK accumulators
-    // query side; the sequence's first chunk adds the causal part j <= i to the state
-    // before it, every other chunk removes the part j > i from the state after it
-    auto query_b = [&](auto causal_tag) {
-      constexpr bool causal = decltype(causal_tag)::value;
-      const int ib = rb, il = 16 * ib + r16;
-      const bool row_ok = il < nv;
-      constexpr int NO = cmax(P::Bt, P::U1_b);
-      Frag<NO> dof[M / 32];
-#pragma unroll
-      for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
-      // +-(V_j . dO_i) over the tokens j of that part, and the mask +-[j in it], as B
-      // operands under the accumulator map
-      Frag<P::U2> btf[NPAIR];
-      Frag<1> onef[NPAIR];
-#pragma unroll
-      for (int p = 0; p < NPAIR; ++p) {
-        f32x4_t bt[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int jb = 2 * p + h;
-          f32x4_t a = zero4();
-          if (causal ? jb <= ib : jb >= ib) {
-#pragma unroll
-            for (int s = 0; s < M / 32; ++s)
-              mmaf<P::Bt, P::Bt>(a, vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool later = jb > ib || (jb == ib && 4 * g + r > r16);  // j > i
-              a[r] = causal ? (later ? 0.f : a[r]) : (later ? -a[r] : 0.f);
-            }
-          }
-          bt[h] = a;
-        }
-        btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool later = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)) > il;
-          onef[p].p[0][e] = causal ? (later ? (__bf16)0.0f : (__bf16)1.0f) : (later ? (__bf16)-1.0f : (__bf16)0.0f);
-        }
-      }
-      f32x4_t U[DB], ZC[DB];
-#pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t u = zero4(), zc = zero4();
-#pragma unroll
-        for (int s = 0; s < M / 32; ++s)
-          mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
-#pragma unroll
-        for (int p = 0; p < NPAIR; ++p) {
-          if (causal ? 2 * p <= ib : 2 * p + 1 >= ib) {
-            constexpr int NKA = cmax(P::U2, P::Zc);
-            const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
-            mmaf<P::U2, P::U2>(u, kfa, btf[p]);
-            mmaf<P::Zc, 1>(zc, kfa, onef[p]);
-          }
-        }
-        const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
-        zc += f32x4_t{z4.x, z4.y, z4.z, z4.w};
-        U[d0] = u;    // S_i dO_i   [d][i]
-        ZC[d0] = zc;  // Z_i        [d][i]
-      }
-      float pu = 0.f, pz = 0.f;
-      float qv[DB][4];
-#pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        if constexpr (F32C) {
-          const float4 q4 = *reinterpret_cast<const float4*>(&q32[il][16 * d0 + 4 * g]);
-          qv[d0][0] = q4.x; qv[d0][1] = q4.y; qv[d0][2] = q4.z; qv[d0][3] = q4.w;
-        } else {
-          qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pu += qv[d0][r] * U[d0][r];
-          pz += qv[d0][r] * ZC[d0][r];
-        }
-      }
-      pu = sum_over_g(pu);  // phi(Q_i)^T S_i dO_i = num_i . dO_i
-      pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
-      const float invz = row_ok ? 1.f / pz : 0.f;
-      const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
-      if (g == 0) {
-        sInv[il] = invz;
-        sOdo[il] = odo;
-      }
-      if (row_ok) {
-#pragma unroll
-        for (int d0 = 0; d0 < DB; ++d0) {
-          float o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
-          IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
-        }
-      }
-      // row i of [g | c]: g_i = dO_i / den_i over this lane's quarter of the features
-#pragma unroll
-      for (int mm = 0; mm < M / 4; mm += 4) {
-        float dv[4];
-        ot.get4(il, g * (M / 4) + mm, dv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dv[q] *= invz;
-        gt.put4(il, g * (M / 4) + mm, dv);
-      }
-      if (g == 0) gt.put1(il, M, -odo * invz);
-    };
-    if (qrole) {
-      if (seqstart && ci == 0)
-        query_b(std::true_type{});
-      else
-        query_b(std::false_type{});
-    } else {
-      const int jb = RB - 1 - rb, jl = 16 * jb + r16;
-      Frag<NKT> kfr[D / 32];
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
-      Frag<NVT> vfr[M / 32];
-#pragma unroll
-      for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
-#pragma unroll
-      for (int p = 0; p < NPAIR; ++p) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ib = 2 * p + h;
-          f32x4_t a = zero4(), b = zero4();
-          if (ib >= jb) {
-#pragma unroll
-            for (int s = 0; s < D / 32; ++s)
-              mmaf<P::At, P::At>(a, qt.template frag<P::At>(16 * ib + r16, 32 * s, g), kfr[s]);
-#pragma unroll
-            for (int s = 0; s < M / 32; ++s)
-              mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
-          }
-          at[p][h] = a;
-          wt[p][h] = b;
-        }
-      }
-      // later chunks' share of dK: R V_j
-#pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t a = zero4();
-#pragma unroll
-        for (int s = 0; s < M / 32; ++s)
-          mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
-        gk[d0] = a;
-      }
-    }
-    __syncthreads();
-
-    // ================= phase C
-    if (qrole) {
-      // R^T += g^T phi(Q) and r += phi(Q)^T c (row M of [g | c]) for the next (earlier) chunk
-#pragma unroll
-      for (int s = 0; s < CB / 32; ++s) {
-#pragma unroll
-        for (int k = 0; k < NTR; ++k)
-          mmaf<P::dR, P::dR>(accR[k], gt.template tfrag<P::dR>(32 * s, 16 * rmb(k), g, r16),
-                             qt.template tfrag<P::dR>(32 * s, 16 * rdb(k), g, r16));
-      }
-#pragma unroll
-      for (int j = 0; j < NZW; ++j) {
-        const int d0 = rb + RB * j;
-        if (d0 < DB) {
-          f32x4_t dr = zero4();
-#pragma unroll
-          for (int s = 0; s < CB / 32; ++s)
-            mmaf<P::dR, P::dR>(dr, gt.template tfrag<P::dR>(32 * s, M, g, r16),
-                               qt.template tfrag<P::dR>(32 * s, 16 * d0, g, r16));
-          zr[j] += dr[0];  // row M of the tile, on lanes g = 0
-        }
-      }
-    } else {
-      const int jb = RB - 1 - rb, jl = 16 * jb + r16;
-      Frag<P::dK> wfr[NPAIR];
-      Frag<P::dV> afr[NPAIR];
-#pragma unroll
-      for (int p = 0; p < NPAIR; ++p) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ib = 2 * p + h;
-          if (ib >= jb) {
-            const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
-            const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
-            const float ivr[4] = {iv.x, iv.y, iv.z, iv.w}, odr[4] = {od.x, od.y, od.z, od.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              wt[p][h][r] = (wt[p][h][r] - odr[r]) * ivr[r];  // (dO_i . V_j - O_i . dO_i) / den_i
-              if (ib == jb && 4 * g + r < r16) {
-                at[p][h][r] = 0.f;
-                wt[p][h][r] = 0.f;
-              }
-            }
-          }
-        }
-        wfr[p] = acc2frag<P::dK>(wt[p][0], wt[p][1]);
-        afr[p] = acc2frag<P::dV>(at[p][0], at[p][1]);
-      }
-      const bool row_ok = jl < nv;
-#pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t a = gk[d0];
-#pragma unroll
-        for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
-        if (row_ok) {
-          float o[4];
-          float kv[4];
-          if constexpr (F32C) {
-            const float4 k4 = *reinterpret_cast<const float4*>(&k32[jl][16 * d0 + 4 * g]);
-            kv[0] = k4.x; kv[1] = k4.y; kv[2] = k4.z; kv[3] = k4.w;
-          } else {
-            kt.get4(jl, 16 * d0 + 4 * g, kv);
-          }
-          const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
-          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dfeat(kv[r], fm);
-          IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
-        }
-      }
-      Frag<NKT> kfr[D / 32];
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) kfr[s] = kt.template frag<NKT>(jl, 32 * s, g);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        f32x4_t a = zero4();
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s)  // later chunks: R^T phi(K_j)
-          mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
-#pragma unroll
-        for (int p = 0; p < NPAIR; ++p)
-          if (2 * p + 1 >= jb) mmaf<P::dV, P::dV>(a, gt.template tfrag_acc<P::dV>(32 * p, 16 * mb, g, r16), afr[p]);
-        if (row_ok) {
-          float o[4] = {a[0], a[1], a[2], a[3]};
-          IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
-        }
-      }
-    }
-    // S, Z before this chunk = S, Z after the next one to process (its reads of sp, sZ ended at the
-    // barrier); before the sequence's first chunk, the initial state itself
-    if (ci == 1 && seqstart && shold) {
-      load_S(st_init);
-      stage_S();
-    } else if (ci > 0 && shold) {
-      constexpr int NKB = cmax(P::dS_b, P::Zc);
-#pragma unroll
-      for (int k = 0; k < NTS; ++k) {
-        f32x4_t ds = zero4();
-#pragma unroll
-        for (int s = 0; s < CB / 32; ++s)
-          mmaf<P::dS_a, P::dS_b>(ds, vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16),
-                                 kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16));
-        accS[k] -= ds;
-      }
-#pragma unroll
-      for (int j = 0; j < NZS; ++j) {
-        const int d0 = so + NWS * j;
-        if (d0 < DB) {
-          f32x4_t dz = zero4();
-#pragma unroll
-          for (int s = 0; s < CB / 32; ++s) mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * d0, g, r16));
-          zz[j] -= dz[0];
-        }
-      }
-      stage_S();
-    }
-    if (ci > 0) {
-      __syncthreads();  // every wavefront is done with this chunk's LDS, and the key ones with R, r
-      if (qrole) stage_R();
-    }
-  }
-  // The reverse state carried through the sequence's first token is the gradient of the initial state.
-  if (seqstart && dS0 && qrole) {
-    float v4[4];
-#pragma unroll
-    for (int k = 0; k < NTR; ++k) {
-      acc_to4(accR[k], v4);
-      *reinterpret_cast<float4*>(dS0 + (size_t)bh * D * M + (16 * rdb(k) + r16) * M + 16 * rmb(k) + 4 * g) =
-          make_float4(v4[0], v4[1], v4[2], v4[3]);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZW; ++j)
-        if (rb + RB * j < DB) dZ0[(size_t)bh * D + 16 * (rb + RB * j) + r16] = zr[j];
     }
   }
 }

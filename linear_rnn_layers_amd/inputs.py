@@ -37,6 +37,19 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out.astype(np.uint32).view(np.float32).reshape(x.shape)
 
 
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to the nearest bfloat16 (ties to even); returns the uint16 bit patterns (the
+    same values as round_to_bf16, without the widening back to float32)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def gaussian_bf16_bits(shape, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """gaussian(shape, seed, sigma, BF16) as uint16 bfloat16 bit patterns (for uploading large pools)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    return bf16_bits((g.standard_normal(size=tuple(int(s) for s in shape)) * sigma).astype(np.float32))
+
+
 def gaussian(shape, seed: int, sigma: float = 1.0, dtype: str = F32) -> np.ndarray:
     """N(0, sigma^2) samples from PCG64(seed), rounded to ``dtype`` storage."""
     if dtype not in DTYPES:
@@ -99,6 +112,12 @@ class Workload:
         k = gaussian((self.B, self.H, self.D), base + 1, 1.0, self.dtype)
         v = gaussian((self.B, self.H, self.M), base + 2, 1.0, self.dtype)
         return q, k, v
+
+    def decode_step_bits(self, step: int, base: int = 5_000_000):
+        """decode_step_inputs(step) as uint16 bfloat16 bit patterns (bf16 workloads; seeds base + 3 step + i)."""
+        b = base + 3 * step
+        return (gaussian_bf16_bits((self.B, self.H, self.D), b + 0), gaussian_bf16_bits((self.B, self.H, self.D), b + 1),
+                gaussian_bf16_bits((self.B, self.H, self.M), b + 2))
 
     def log_a(self, n: int | None = None):
         """Per-token, per-head log-decay [B,H,N] float32 for the decayed workloads: the log of a gate

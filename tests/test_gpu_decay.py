@@ -26,9 +26,7 @@ CANCEL_FLOOR = 1e-2
 def _gpu():
     assert torch.cuda.is_available(), "the GPU tests need a GPU"
     binding.load()
-    binding.set_segment_chunks(0)
     yield
-    binding.set_segment_chunks(0)
 
 
 def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
@@ -50,16 +48,16 @@ def _state(B, H, D, M, dtype, seed, sigma=0.1):
     return s0, z0, inputs.gaussian((B, H, D, M), seed + 10, sigma), inputs.gaussian((B, H, D), seed + 11, sigma)
 
 
-def gpu_forward(q, k, v, la, dtype, s0=None, z0=None):
+def gpu_forward(q, k, v, la, dtype, s0=None, z0=None, opts=None):
     out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
                                  s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
-                                 return_state=True, checkpoint=True, log_a=dev32(la))
+                                 return_state=True, checkpoint=True, log_a=dev32(la), opts=opts)
     torch.cuda.synchronize()
     return out
 
 
-def check_forward(q, k, v, la, dtype, s0=None, z0=None):
-    out = gpu_forward(q, k, v, la, dtype, s0, z0)
+def check_forward(q, k, v, la, dtype, s0=None, z0=None, opts=None):
+    out = gpu_forward(q, k, v, la, dtype, s0, z0, opts)
     o, den, s, z = oracle.forward_decay(q, k, v, la, s0, z0)
     errs = {"O": rowerr(host(out["o"]), o), "den": rowerr(host(out["den"]), den, False),
             "S_N": rowerr(host(out["s"]), s), "Z_N": rowerr(host(out["z"]), z, False)}
@@ -109,14 +107,14 @@ def state_tail(q, k, v, la, s0, z0, dsn, dzn):
     return (dsn * sn).sum((-1, -2)) + (dzn * zn).sum(-1)
 
 
-def check_backward(q, k, v, la, do, dtype, s0=None, z0=None, dsn=None, dzn=None, use_ckpt=True):
-    out = gpu_forward(q, k, v, la, dtype, s0, z0)
+def check_backward(q, k, v, la, do, dtype, s0=None, z0=None, dsn=None, dzn=None, use_ckpt=True, opts=None):
+    out = gpu_forward(q, k, v, la, dtype, s0, z0, opts)
     Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     g = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, dtype),
                                 s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
                                 ckpt=out["ckpt"] if use_ckpt else None,
                                 ds_n=None if dsn is None else dev32(dsn), dz_n=None if dzn is None else dev32(dzn),
-                                state_grad=True, log_a=dev32(la))
+                                state_grad=True, log_a=dev32(la), opts=opts)
     torch.cuda.synchronize()
     dq, dk, dv, dla, ds0, dz0 = (host(t) for t in g)
     rq, rk, rv, rla, rs, rz = oracle.backward_decay(q, k, v, la, do, s0, z0, dsn, dzn)
@@ -149,11 +147,7 @@ def test_decay_forward_segments(D, M, chunks):
     q, k, v = _qkv(B, H, N, D, M, F32, 12200 + chunks)
     la = _gates(B, H, N, 12290)
     s0, z0, _, _ = _state(B, H, D, M, F32, 12300)
-    binding.set_segment_chunks(chunks)
-    try:
-        check_forward(q, k, v, la, F32, s0, z0)
-    finally:
-        binding.set_segment_chunks(0)
+    check_forward(q, k, v, la, F32, s0, z0, binding.options(segment_chunks=chunks))
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
@@ -177,11 +171,7 @@ def test_decay_backward_segments(D, M, chunks, use_ckpt):
     la = _gates(B, H, N, 13290)
     do = inputs.gaussian((B, H, N, M), 13295)
     s0, z0, dsn, dzn = _state(B, H, D, M, F32, 13300)
-    binding.set_segment_chunks(chunks)
-    try:
-        check_backward(q, k, v, la, do, F32, s0, z0, dsn, dzn, use_ckpt)
-    finally:
-        binding.set_segment_chunks(0)
+    check_backward(q, k, v, la, do, F32, s0, z0, dsn, dzn, use_ckpt, binding.options(segment_chunks=chunks))
 
 
 def test_decay_without_states():

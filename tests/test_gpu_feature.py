@@ -2,8 +2,12 @@
 feature mode (Q, K taken as feature vectors) against the float64 oracle.
 
 Gate: rowerr <= 1e-4 (float32 storage) / 2e-2 (bf16), each step checked at its own inputs (the attention on
-the features the library produced, the chain rule through the map on the feature gradients it produced), and the
-float32 composition end to end through autograd.  The feature gradients dPhi_Q are floored at 1e-2 of the
+the features the library produced, the chain rule through the map on the feature gradients it produced), and
+end to end against a chain of oracle steps only (the oracle's features, rounded to the storage type as the
+library stores them, its attention and its chain rule), also through autograd.  The chain rule of a feature map
+is a signed sum over the features, so an error within the gate in each feature gradient reaches dX as at most the
+gate times the size of the summed terms, sum_c |d phi_c / dx| |dPhi_c|: the end-to-end rows are judged against
+that size (the propagated per-step gate).  The feature gradients dPhi_Q are floored at 1e-2 of the
 numerator term |S_i g_i| (the cancellation of the quotient rule, as for dQ of the plain method); the raw
 query gradient of the composition at 1e-2 of that term carried through the same map.
 """
@@ -27,7 +31,6 @@ CANCEL_FLOOR = 1e-2
 def _gpu():
     assert torch.cuda.is_available(), "the GPU tests need a GPU"
     binding.load()
-    binding.set_segment_chunks(0)
     yield
 
 
@@ -37,6 +40,42 @@ def _x(shape, seed, sigma, dtype):
 
 def _w(H, C, Din, seed):
     return inputs.gaussian((H, C, Din), seed, 1.0, F32)
+
+
+def store(x, dtype):
+    """Round oracle values to the storage type, as the library stores a feature tensor between the map and the
+    attention (the oracle-only chain keeps this rounding: it is part of the computation the dtype defines)."""
+    x = np.asarray(x, np.float64).astype(np.float32)
+    return inputs.round_to_bf16(x).astype(np.float64) if dtype == BF16 else x.astype(np.float64)
+
+
+def rf_vjp_terms(x, w, dphi):
+    """Per-row size of the terms the random-feature chain rule dX = sum_c dPhi_c phi_c (W_c - x) sums (a signed
+    sum over the features), bounded by sum_c |dPhi_c| phi_c (|W_c| + |x|), float64: an error of e |dPhi_c| in
+    each feature gradient reaches dX as at most e times this size."""
+    x, dphi = np.asarray(x, np.float64), np.asarray(dphi, np.float64)
+    a = np.abs(dphi) * oracle.feature_performer(x, w)
+    t = np.einsum("bhnc,hcd->bhnd", a, np.abs(np.asarray(w, np.float64))) + np.abs(x) * a.sum(-1, keepdims=True)
+    return t.max(-1)
+
+
+def poly2_vjp_terms(x, dphi):
+    """Per-row size of the terms of the polynomial chain rule: the same sums with every term taken by magnitude."""
+    return np.abs(oracle.feature_poly2_vjp(np.abs(np.asarray(x, np.float64)), np.abs(np.asarray(dphi, np.float64))))\
+        .max(-1)
+
+
+def feat_key_cancel_terms(fq, fk, v, do):
+    """|sum_{i>=j} phi(Q_i) (g_i . V_j)|, the numerator term of dPhi_K that the denominator's share r cancels
+    (causal, g = dO / den), elementwise, from the oracle on the features."""
+    fq, fk, v, do = (np.asarray(a, np.float64) for a in (fq, fk, v, do))
+    _, den, _, _ = oracle.forward_causal(fq, fk, v, feature=IDENT)
+    g = do / den[..., None]
+    out = np.empty(fk.shape)
+    for b in range(fq.shape[0]):
+        for h in range(fq.shape[1]):
+            out[b, h] = oracle.numerator_backward(fq[b, h], fk[b, h], v[b, h], g[b, h])[1]
+    return np.abs(out)
 
 
 def feat_cancel_scale(fq, fk, v, do, causal=True):
@@ -153,6 +192,28 @@ def test_feature_mode_attention(which, causal, dtype):
             "dPhiK": rowerr(host(dfk), rfk),
             "dQ": rowerr(host(dq), fvjp(q, host(dfq))), "dK": rowerr(host(dk), fvjp(k, host(dfk)))}
     assert max(errs.values()) <= TOL[dtype], errs
+    # end to end, from the oracle alone: its features of the stored inputs (rounded to the storage type, as the
+    # library stores them), its attention gradients on them, its chain rule -- nothing the library produced
+    # enters the reference.  The chain rule is a signed sum over the features: its rows are judged against the
+    # size of the summed terms at 1e-2, as the quotient rule's cancellation in dQ is.
+    ofq, ofk = store(fmap(q), dtype), store(fmap(k), dtype)
+    terms = (lambda a, g: rf_vjp_terms(a, w, g)) if which == "random" else poly2_vjp_terms
+    if causal:
+        oo = oracle.forward_causal(ofq, ofk, v, feature=IDENT)[0]
+        ofq_g, ofk_g, ov = oracle.backward_causal(ofq, ofk, v, do, feature=IDENT)
+    else:
+        oo = oracle.forward_noncausal(ofq, ofk, v, feature=IDENT)
+        ofq_g, ofk_g, ov = oracle.backward_noncausal(ofq, ofk, v, do, feature=IDENT)
+    ou = feat_cancel_scale(ofq, ofk, v, do, causal)
+    # each feature gradient's own floor (1e-2 of the numerator term its denominator share cancels) carried along
+    fq_abs = np.abs(ofq_g) + CANCEL_FLOOR * np.abs(ou).max(-1, keepdims=True)
+    fk_abs = np.abs(ofk_g)
+    if causal:
+        fk_abs = fk_abs + CANCEL_FLOOR * feat_key_cancel_terms(ofq, ofk, v, do).max(-1, keepdims=True)
+    chain = {"O": rowerr(host(o), oo), "dV": rowerr(host(dv), ov),
+             "dQ": rowerr(host(dq), fvjp(q, ofq_g), row_floor=terms(q, fq_abs)),
+             "dK": rowerr(host(dk), fvjp(k, ofk_g), row_floor=terms(k, fk_abs))}
+    assert max(chain.values()) <= TOL[dtype], chain
 
 
 def test_mnist_random_features_workload():
@@ -179,6 +240,19 @@ def test_mnist_random_features_workload():
             "dQ": rowerr(host(dq), oracle.feature_performer_vjp(q, wp, host(dfq))),
             "dK": rowerr(host(dk), oracle.feature_performer_vjp(k, wp, host(dfk)))}
     assert max(errs.values()) <= 1e-4, errs
+    # end to end from the oracle alone (its features, attention gradients and chain rule; the chain rule's rows
+    # judged against the size of the terms it sums, as above)
+    ofq, ofk = store(oracle.feature_performer(q, wp), F32), store(oracle.feature_performer(k, wp), F32)
+    oo = oracle.forward_causal(ofq, ofk, v, feature=IDENT)[0]
+    gq, gk, gv = oracle.backward_causal(ofq, ofk, v, do, feature=IDENT)
+    ou = feat_cancel_scale(ofq, ofk, v, do)
+    # each feature gradient's own floor (1e-2 of the numerator term its denominator share cancels) carried along
+    gq_abs = np.abs(gq) + CANCEL_FLOOR * np.abs(ou).max(-1, keepdims=True)
+    gk_abs = np.abs(gk) + CANCEL_FLOOR * feat_key_cancel_terms(ofq, ofk, v, do).max(-1, keepdims=True)
+    chain = {"O": rowerr(host(o), oo), "dV": rowerr(host(dv), gv),
+             "dQ": rowerr(host(dq), oracle.feature_performer_vjp(q, wp, gq), row_floor=rf_vjp_terms(q, wp, gq_abs)),
+             "dK": rowerr(host(dk), oracle.feature_performer_vjp(k, wp, gk), row_floor=rf_vjp_terms(k, wp, gk_abs))}
+    assert max(chain.values()) <= 1e-4, chain
 
 
 def test_feature_mode_with_elu_features_matches_the_method():

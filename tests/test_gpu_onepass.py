@@ -30,11 +30,7 @@ DM = [(32, 32), (64, 64), (32, 64), (64, 32)]
 def _gpu():
     assert torch.cuda.is_available(), "the GPU tests need a GPU"
     binding.load()
-    binding.set_segment_chunks(0)
-    binding.set_forward_onepass(2)
     yield
-    binding.set_segment_chunks(0)
-    binding.set_forward_onepass(1)
 
 
 def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
@@ -44,18 +40,35 @@ def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
     return q, k, v
 
 
-def _run(q, k, v, dtype, s0=None, z0=None, onepass=True):
-    """Forward with checkpoint and final state; returns the outputs and whether the one-pass form ran."""
-    prev = binding.set_forward_onepass(2 if onepass else 0)
-    binding.prof_select("sync_clear")
-    try:
-        out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
-                                     s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
-                                     return_state=True, checkpoint=True)
-        _, launches, _ = binding.prof_collect()
-    finally:
-        binding.prof_select(None)
-        binding.set_forward_onepass(prev)
+def _opts(onepass=True, chunks=0, timer=None, **kw):
+    form = binding.LA_FORM_ONE_LAUNCH if onepass else binding.LA_FORM_TWO_LAUNCH
+    return binding.options(segment_chunks=chunks, forward_form=form, timer=timer, **kw)
+
+
+def _resident(B, H, N, D, M, opts):
+    """Forced one-launch tests keep the whole grid resident at once (at most one workgroup per compute unit), so
+    no wait depends on the order in which workgroups are dispatched."""
+    nseg = -(-N // binding.segment_length(B, H, N, D, M, opts))
+    assert B * H * nseg <= 256, (B, H, N, nseg)
+
+
+def _run(q, k, v, dtype, s0=None, z0=None, onepass=True, chunks=0):
+    """Forward with checkpoint and final state; returns the outputs and whether the one-pass form ran (it is the
+    form that launches the flag-clearing kernel)."""
+    timer = binding.KernelTimer("sync_clear", 4)
+    opts = _opts(onepass, chunks, timer)
+    B, H, N, D = q.shape
+    if onepass:
+        _resident(B, H, N, D, v.shape[-1], opts)
+    out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
+                                 s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
+                                 return_state=True, checkpoint=True, opts=opts)
+    torch.cuda.synchronize()
+    launches = timer.launches
+    if launches:
+        assert binding.forward_wait_status(out["ws"], B, H, N, D, v.shape[-1], binding.dtype_code(out["o"].dtype),
+                                           opts) == 0
+    out["opts"] = opts
     return out, launches > 0
 
 
@@ -76,9 +89,9 @@ def _ckpt_ref(q, k, v, L, s0=None, z0=None):
     return ref
 
 
-def _error_word(ws, B, H, N, D, M):
+def _error_word(ws, B, H, N, D, M, opts):
     """Word 0 of the one-launch forward's flag region: after the aggregates and the prefix states of the workspace."""
-    L = binding.segment_length(B, H, N, D, M)
+    L = binding.segment_length(B, H, N, D, M, opts)
     nseg, sv = -(-N // L), D * M + D
     off = sum((x + 255) // 256 * 256 for x in (B * H * nseg * sv * 4, B * H * (nseg + 1) * sv * 4))
     return int(ws[off:off + 4].view(torch.int32).item())
@@ -99,12 +112,8 @@ def test_onepass_segments(chunks, D, M, dtype):
     B, H = 2, 2
     N = 3 * 64 * chunks + 37 if D * M <= 1024 else 64 * chunks + 29  # few enough aggregates to sum per workgroup
     q, k, v = _qkv(B, H, N, D, M, dtype, 7000 + 10 * chunks + D + M)
-    prev = binding.set_segment_chunks(chunks)
-    try:
-        out, onepass = _run(q, k, v, dtype)
-        L = binding.segment_length(B, H, N, D, M)
-    finally:
-        binding.set_segment_chunks(prev)
+    out, onepass = _run(q, k, v, dtype, chunks=chunks)
+    L = binding.segment_length(B, H, N, D, M, out["opts"])
     assert onepass, "the one-pass forward did not run"
     assert L == 64 * chunks
     _check(out, q, k, v, dtype)
@@ -123,11 +132,7 @@ def test_onepass_initial_state(dtype):
     q, k, v = _qkv(B, H, N + 90, D, M, dtype, 7500)
     _, _, s0, z0 = oracle.forward_causal(q[:, :, :90], k[:, :, :90], v[:, :, :90])
     q, k, v = q[:, :, 90:], k[:, :, 90:], v[:, :, 90:]
-    prev = binding.set_segment_chunks(2)
-    try:
-        out, onepass = _run(q, k, v, dtype, s0, z0)
-    finally:
-        binding.set_segment_chunks(prev)
+    out, onepass = _run(q, k, v, dtype, s0, z0, chunks=2)
     assert onepass
     _check(out, q, k, v, dtype, s0, z0)
 
@@ -135,7 +140,7 @@ def test_onepass_initial_state(dtype):
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_onepass_matches_two_launch_form(dtype):
     """Both forms of the forward agree within the tolerance, and the backward from either checkpoint matches."""
-    B, H, N, D, M = 4, 4, 784, 32, 32
+    B, H, N, D, M = 2, 8, 784, 32, 32
     q, k, v = _qkv(B, H, N, D, M, dtype, 7600)
     do = inputs.gaussian((B, H, N, M), 7604, 1.0, dtype)
     a, ra = _run(q, k, v, dtype, onepass=True)
@@ -146,8 +151,8 @@ def test_onepass_matches_two_launch_form(dtype):
     for key in ("den", "z"):
         assert rowerr(host(a[key]), host(b[key]), False) <= TOL[dtype], key
     Q, K, V, dO = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype)
-    ga = binding.backward_causal(Q, K, V, a["o"], a["den"], dO, ckpt=a["ckpt"])
-    gb = binding.backward_causal(Q, K, V, b["o"], b["den"], dO, ckpt=b["ckpt"])
+    ga = binding.backward_causal(Q, K, V, a["o"], a["den"], dO, ckpt=a["ckpt"], opts=a["opts"])
+    gb = binding.backward_causal(Q, K, V, b["o"], b["den"], dO, ckpt=b["ckpt"], opts=b["opts"])
     torch.cuda.synchronize()
     rq, rk, rv = oracle.backward_causal(q, k, v, do)
     for x, y, r in zip(ga, gb, (rq, rk, rv)):
@@ -157,40 +162,37 @@ def test_onepass_matches_two_launch_form(dtype):
 
 def test_onepass_rule():
     """By default the one-launch form runs for states of D*M >= 2048 and the two-launch form below that."""
-    prev = binding.set_forward_onepass(1)
-    try:
-        for (D, M), want in (((32, 32), False), ((64, 32), True), ((64, 64), True)):
-            q, k, v = _qkv(2, 2, 300, D, M, F32, 7900)
-            binding.prof_select("sync_clear")
-            binding.forward_causal(dev(q), dev(k), dev(v))
-            _, launches, _ = binding.prof_collect()
-            binding.prof_select(None)
-            assert (launches > 0) == want, (D, M)
-    finally:
-        binding.set_forward_onepass(prev)
+    for (D, M), want in (((32, 32), False), ((64, 32), True), ((64, 64), True)):
+        q, k, v = _qkv(2, 2, 300, D, M, F32, 7900)
+        timer = binding.KernelTimer("sync_clear", 4)
+        binding.forward_causal(dev(q), dev(k), dev(v), opts=binding.options(timer=timer))
+        torch.cuda.synchronize()
+        assert (timer.launches > 0) == want, (D, M)
 
 
 def test_onepass_reused_dirty_workspace():
     """Two calls on one workspace that starts filled with 0xff bytes: the call clears its own flags."""
-    B, H, N, D, M = 8, 8, 784, 32, 32
+    B, H, N, D, M = 2, 8, 784, 32, 32
     q, k, v = _qkv(B, H, N, D, M, F32, 7700)
     Q, K, V = dev(q), dev(k), dev(v)
-    ws = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, binding.dtype_code(torch.float32), "cuda")
+    timer = binding.KernelTimer("sync_clear", 4)
+    opts = _opts(True, 0, timer)
+    _resident(B, H, N, D, M, opts)
+    ws = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, binding.dtype_code(torch.float32), "cuda",
+                                 opts)
     ws.fill_(255)
     ref = oracle.forward_causal(q, k, v)
-    binding.prof_select("sync_clear")
-    assert binding.segment_length(B, H, N, D, M) <= 4 * 64
+    assert binding.segment_length(B, H, N, D, M, opts) <= 4 * 64
     for _ in range(2):
         O = torch.empty((B, H, N, M), device="cuda")
         den = torch.empty((B, H, N), device="cuda")
-        binding.la_forward_causal(Q, K, V, O, den, ws=ws)
+        binding.la_forward_causal(Q, K, V, O, den, ws=ws, opts=opts)
         torch.cuda.synchronize()
-        assert _error_word(ws, B, H, N, D, M) == 0  # no wait gave up
+        assert _error_word(ws, B, H, N, D, M, opts) == 0  # no wait gave up
+        assert binding.forward_wait_status(ws, B, H, N, D, M, binding.LA_F32, opts) == 0
         assert rowerr(host(O), ref[0]) <= 1e-4
         assert rowerr(host(den), ref[1], False) <= 1e-4
-    _, launches, _ = binding.prof_collect()
-    binding.prof_select(None)
-    assert launches == 2
+    assert timer.launches == 2
 
 
 def test_onepass_wait_limit():
@@ -201,40 +203,42 @@ def test_onepass_wait_limit():
     q, k, v = _qkv(B, H, N, D, M, F32, 7950)
     Q, K, V = dev(q), dev(k), dev(v)
     o_ref, den_ref, _, _ = oracle.forward_causal(q, k, v)
-    prev_c = binding.set_segment_chunks(2)
-    try:
-        L = binding.segment_length(B, H, N, D, M)
-        ws = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, binding.dtype_code(torch.float32),
-                                     "cuda")
-        for polls in (0, 1 << 22):
-            prev_p = binding.set_wait_polls(polls)
-            try:
-                O = torch.empty((B, H, N, M), device="cuda")
-                den = torch.empty((B, H, N), device="cuda")
-                S = torch.empty((B, H, D, M), device="cuda")
-                Z = torch.empty((B, H, D), device="cuda")
-                binding.la_forward_causal(Q, K, V, O, den, S_out=S, Z_out=Z, ws=ws)
-                torch.cuda.synchronize()
-            finally:
-                binding.set_wait_polls(prev_p)
-            o, d = host(O), host(den)
-            if polls == 0:
-                assert _error_word(ws, B, H, N, D, M) == 1
-                assert rowerr(o[:, :, :L], o_ref[:, :, :L]) <= 1e-4
-                assert rowerr(d[:, :, :L], den_ref[:, :, :L], False) <= 1e-4
-                assert np.isnan(o[:, :, L:]).all() and np.isnan(d[:, :, L:]).all()
-                assert np.isnan(host(S)).all() and np.isnan(host(Z)).all()
-            else:
-                assert _error_word(ws, B, H, N, D, M) == 0
-                assert rowerr(o, o_ref) <= 1e-4
-                assert rowerr(d, den_ref, False) <= 1e-4
-    finally:
-        binding.set_segment_chunks(prev_c)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    base = _opts(True, 2)
+    L = binding.segment_length(B, H, N, D, M, base)
+    _resident(B, H, N, D, M, base)
+    ws = binding.alloc_workspace(binding.LA_OP_FWD_CAUSAL, B, H, N, D, M, binding.dtype_code(torch.float32), "cuda",
+                                 base)
+    for polls in (-1, 0):  # none at all (the failure path), then the default limit
+        opts = _opts(True, 2, wait_polls=polls, status=status)
+        O = torch.empty((B, H, N, M), device="cuda")
+        den = torch.empty((B, H, N), device="cuda")
+        S = torch.empty((B, H, D, M), device="cuda")
+        Z = torch.empty((B, H, D), device="cuda")
+        binding.la_forward_causal(Q, K, V, O, den, S_out=S, Z_out=Z, ws=ws, opts=opts)
+        torch.cuda.synchronize()
+        o, d = host(O), host(den)
+        if polls < 0:
+            assert _error_word(ws, B, H, N, D, M, opts) == 1
+            assert binding.forward_wait_status(ws, B, H, N, D, M, binding.LA_F32, opts) == binding.LA_ERR_WAIT
+            assert int(status.item()) == 1  # the caller's status word is set too
+            status.zero_()
+            assert rowerr(o[:, :, :L], o_ref[:, :, :L]) <= 1e-4
+            assert rowerr(d[:, :, :L], den_ref[:, :, :L], False) <= 1e-4
+            assert np.isnan(o[:, :, L:]).all() and np.isnan(d[:, :, L:]).all()
+            assert np.isnan(host(S)).all() and np.isnan(host(Z)).all()
+        else:
+            assert _error_word(ws, B, H, N, D, M, opts) == 0
+            assert binding.forward_wait_status(ws, B, H, N, D, M, binding.LA_F32, opts) == 0
+            assert int(status.item()) == 0
+            assert rowerr(o, o_ref) <= 1e-4
+            assert rowerr(d, den_ref, False) <= 1e-4
 
 
-def test_onepass_many_heads_full_shape():
-    """The MNIST-shaped layer (B=16 H=8 N=784 D=M=32 float32): rows sampled from every head."""
-    B, H, N, D, M = 16, 8, 784, 32, 32
+def test_onepass_many_heads():
+    """Sixteen heads of the MNIST-shaped layer (B=2 H=8 N=784 D=M=32 float32; the grid of 208 workgroups is
+    resident at once): rows sampled from every head."""
+    B, H, N, D, M = 2, 8, 784, 32, 32
     q, k, v = _qkv(B, H, N, D, M, F32, 7800)
     out, onepass = _run(q, k, v, F32)
     assert onepass
@@ -247,3 +251,55 @@ def test_onepass_many_heads_full_shape():
             ro, rd, _, _ = oracle.forward_causal(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1])
             assert rowerr(o[b:b + 1, h:h + 1, rows], ro[:, :, rows]) <= 1e-4
             assert rowerr(den[b:b + 1, h:h + 1, rows], rd[:, :, rows], False) <= 1e-4
+
+
+def test_threads_with_different_options():
+    """Two host threads run the causal forward and backward at the same time with different segment options and
+    forms, each on its own stream: each gets exactly (bitwise) what the same call gives alone, and the oracle's
+    outputs (the library keeps no state between calls)."""
+    import threading
+
+    B, H, N, D, M = 2, 4, 700, 64, 32
+    q, k, v = _qkv(B, H, N, D, M, F32, 7990)
+    do = inputs.gaussian((B, H, N, M), 7994)
+    o_ref, den_ref, _, _ = oracle.forward_causal(q, k, v)
+    cases = ((1, True), (3, False))
+
+    def run(chunks, onepass):
+        opts = _opts(onepass, chunks)
+        Q, K, V, dO = dev(q), dev(k), dev(v), dev(do)
+        out = binding.forward_causal(Q, K, V, opts=opts)
+        g = binding.backward_causal(Q, K, V, out["o"], out["den"], dO, ckpt=out["ckpt"], opts=opts)
+        return binding.segment_length(B, H, N, D, M, opts), [out["o"], out["den"]] + list(g)
+
+    alone = {}
+    for c in cases:
+        L, ts = run(*c)
+        torch.cuda.synchronize()
+        alone[c] = (L, [host(t) for t in ts])
+    results, errors = {}, []
+
+    def worker(chunks, onepass):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for _ in range(5):
+                    L, ts = run(chunks, onepass)
+                stream.synchronize()
+                results[(chunks, onepass)] = (L, [host(t) for t in ts])
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for c in cases:
+        L, got = results[c]
+        assert L == 64 * c[0] == alone[c][0]
+        for x, y in zip(got, alone[c][1]):
+            assert np.array_equal(x, y)
+        assert rowerr(got[0], o_ref) <= 1e-4
+        assert rowerr(got[1], den_ref, False) <= 1e-4

@@ -22,9 +22,7 @@ F32, BF16 = inputs.F32, inputs.BF16
 def _gpu():
     assert torch.cuda.is_available(), "the GPU tests need a GPU"
     binding.load()
-    binding.set_segment_chunks(0)
     yield
-    binding.set_segment_chunks(0)
 
 
 def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
@@ -34,17 +32,17 @@ def _qkv(B, H, N, D, M, dtype, seed, sigma=1.0):
     return q, k, v
 
 
-def gpu_forward(q, k, v, dtype, s0=None, z0=None):
+def gpu_forward(q, k, v, dtype, s0=None, z0=None, opts=None):
     out = binding.forward_causal(dev(q, dtype), dev(k, dtype), dev(v, dtype),
                                  s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
-                                 return_state=True, checkpoint=True)
+                                 return_state=True, checkpoint=True, opts=opts)
     torch.cuda.synchronize()
     return out
 
 
-def check_forward(q, k, v, dtype, s0=None, z0=None, tol=None):
+def check_forward(q, k, v, dtype, s0=None, z0=None, tol=None, opts=None):
     tol = TOL[dtype] if tol is None else tol
-    out = gpu_forward(q, k, v, dtype, s0, z0)
+    out = gpu_forward(q, k, v, dtype, s0, z0, opts)
     o, den, s, z = oracle.forward_causal(q, k, v, s0, z0)
     errs = {"O": rowerr(host(out["o"]), o), "den": rowerr(host(out["den"]), den, False),
             "S_N": rowerr(host(out["s"]), s), "Z_N": rowerr(host(out["z"]), z, False)}
@@ -89,14 +87,12 @@ def test_segment_length_invariance(chunks):
     B, H, N, D, M = 2, 2, 784, 32, 32
     q, k, v = _qkv(B, H, N, D, M, F32, 3000)
     do = inputs.gaussian((B, H, N, M), 3004)
-    prev = binding.set_segment_chunks(chunks)
-    try:
-        assert binding.segment_length(B, H, N, D, M) == 64 * chunks
-        out = check_forward(q, k, v, F32)
-        dq, dk, dv = binding.backward_causal(dev(q), dev(k), dev(v), out["o"], out["den"], dev(do), ckpt=out["ckpt"])
-        torch.cuda.synchronize()
-    finally:
-        binding.set_segment_chunks(prev)
+    opts = binding.options(segment_chunks=chunks)
+    assert binding.segment_length(B, H, N, D, M, opts) == 64 * chunks
+    out = check_forward(q, k, v, F32, opts=opts)
+    dq, dk, dv = binding.backward_causal(dev(q), dev(k), dev(v), out["o"], out["den"], dev(do), ckpt=out["ckpt"],
+                                         opts=opts)
+    torch.cuda.synchronize()
     rq, rk, rv = oracle.backward_causal(q, k, v, do)
     errs = [rowerr(host(dq), rq, row_floor=CANCEL_FLOOR * dq_cancel_scale(q, k, v, do)), rowerr(host(dk), rk),
             rowerr(host(dv), rv)]
@@ -252,10 +248,12 @@ def test_prefill_then_decode_equals_forward():
 
 # --------------------------------------------------------- full workloads
 def test_mnist_workload():
-    """B=16 H=8 N=784 D=M=32 float32: causal forward + backward and non-causal forward."""
+    """B=16 H=8 N=784 D=M=32 float32, every head element by element: causal forward (O, den, S_N, Z_N), causal
+    backward and non-causal forward."""
     w = inputs.MNIST
     q, k, v = w.qkv()
     do = w.grad_out()
+    check_forward(q, k, v, F32)
     check_backward(q, k, v, do, F32)
     o = binding.forward_noncausal(dev(q), dev(k), dev(v))
     torch.cuda.synchronize()
@@ -273,10 +271,26 @@ def test_cifar_workload_layer(layer):
 
 
 def test_long_workload():
-    """B=1 H=16 N=65536 D=M=64 bf16, inputs scaled by 1/sqrt(D): forward + backward, all heads."""
+    """B=1 H=16 N=65536 D=M=64 bf16, inputs scaled by 1/sqrt(D), all heads element by element: forward (O, den,
+    S_N, Z_N) and backward (dQ, dK, dV), in the segment plan and launch configuration the benchmark times."""
     w = inputs.LONG
     q, k, v = w.qkv()
     do = w.grad_out()
+    check_forward(q, k, v, BF16)
+    check_backward(q, k, v, do, BF16)
+
+
+@pytest.mark.parametrize("mean", [4.0, -3.0])
+def test_backward_values_around_a_nonzero_mean(mean):
+    """bf16, many segments (64 chunks per head, reverse aggregates scanned), V ~ N(mean, 1): every output row
+    O_i is then close to every V_j, so the key-gradient weights (dO_i.V_j - O_i.dO_i)/den_i cancel strongly --
+    in the chunk that holds both tokens and, through the reverse aggregates, across segments."""
+    B, H, N, D, M = 1, 2, 64 * 64, 64, 64
+    q, k, _ = _qkv(B, H, N, D, M, BF16, 9900, sigma=1.0 / 8.0)
+    v = inputs.round_to_bf16(inputs.gaussian((B, H, N, M), 9902) + np.float32(mean))
+    do = inputs.gaussian((B, H, N, M), 9903, 1.0, BF16)
+    assert -(-N // binding.segment_length(B, H, N, D, M)) > 1
+    check_forward(q, k, v, BF16)
     check_backward(q, k, v, do, BF16)
 
 
@@ -415,11 +429,41 @@ def test_decode_graph_replay():
         (torch.randn(1000, device="cuda") * 2).sum().item()  # unrelated eager work between replays
 
 
+def test_decode_state_saved_to_host_and_restored():
+    """Checkpoint and resume of a decode loop: after a prefill and 40 steps the state (S, Z) is copied to host
+    memory and back into fresh device buffers; the next 40 steps from the restored state equal, bit for bit,
+    those of the loop that kept its state on the device (the state is the whole carried context, eq. 16-19)."""
+    B, H, D, M, P, T = 8, 4, 64, 32, 300, 80
+    q, k, v = _qkv(B, H, P, D, M, BF16, 9700)
+    out = gpu_forward(q, k, v, BF16)
+    steps = [tuple(dev(inputs.gaussian(shape, 9710 + 3 * t + i, 1.0, BF16), BF16)
+                   for i, shape in enumerate(((B, H, D), (B, H, D), (B, H, M)))) for t in range(T)]
+    s, z = out["s"].clone(), out["z"].clone()
+    ys = [binding.decode_step(*steps[t], s, z) for t in range(T)]
+    torch.cuda.synchronize()
+    s2, z2 = out["s"].clone(), out["z"].clone()
+    for t in range(T // 2):
+        binding.decode_step(*steps[t], s2, z2)
+    torch.cuda.synchronize()
+    saved = (s2.cpu().numpy().copy(), z2.cpu().numpy().copy())  # host copy, device buffers dropped
+    del s2, z2
+    s3, z3 = torch.from_numpy(saved[0]).to("cuda"), torch.from_numpy(saved[1]).to("cuda")
+    for t in range(T // 2, T):
+        y = binding.decode_step(*steps[t], s3, z3)
+        assert torch.equal(y, ys[t]), t
+    torch.cuda.synchronize()
+    assert torch.equal(s3, s) and torch.equal(z3, z)
+
+
 def test_decode_workload_sampled():
-    """Batch 256, 16 heads, D=M=64, bf16 I/O: a 512-token prefill then 512 decode steps; every step's y and
-    the final state are checked on 32 sampled heads (the oracle follows those heads only)."""
+    """Batch 256, 16 heads, D=M=64, bf16 I/O: the 512-token prefill then all 4096 decode steps of the workload,
+    on the per-step inputs the benchmark times (seeds 5,000,000 + 3 step + {0, 1, 2}); every step's y and the
+    final state are checked on 32 sampled heads (the oracle follows those heads only: eq. 16-19 continued from
+    the prefill's state, which equals decode steps from it)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     w = inputs.DECODE
-    steps = 512
+    steps = w.steps
     B, H, D, M = w.B, w.H, w.D, w.M
     q, k, v = w.qkv()
     out = gpu_forward(q, k, v, BF16)
@@ -433,14 +477,19 @@ def test_decode_workload_sampled():
     idx_b = torch.from_numpy(bi).cuda()
     idx_h = torch.from_numpy(hi).cuda()
     qs, ks, vs = [], [], []
-    for t in range(steps):
-        qt, kt, vt = w.decode_step_inputs(t)
-        y = binding.decode_step(dev(qt, BF16), dev(kt, BF16), dev(vt, BF16), s, z)
-        ys[t] = y[idx_b, idx_h]
-        qs.append(qt[bi, hi])
-        ks.append(kt[bi, hi])
-        vs.append(vt[bi, hi])
-    torch.cuda.synchronize()
+    widen = lambda a: (a.astype(np.uint32) << np.uint32(16)).view(np.float32)  # noqa: E731
+    chunk = 256
+    with ThreadPoolExecutor(16) as ex:
+        for t0 in range(0, steps, chunk):
+            trip = list(ex.map(w.decode_step_bits, range(t0, min(steps, t0 + chunk))))
+            for j, (qt, kt, vt) in enumerate(trip):
+                qd, kd, vd = (torch.from_numpy(a).view(torch.bfloat16).to("cuda") for a in (qt, kt, vt))
+                y = binding.decode_step(qd, kd, vd, s, z)
+                ys[t0 + j] = y[idx_b, idx_h]
+                qs.append(widen(qt[bi, hi]))
+                ks.append(widen(kt[bi, hi]))
+                vs.append(widen(vt[bi, hi]))
+            torch.cuda.synchronize()
     qn, kn, vn = (np.stack(a, axis=1)[None] for a in (qs, ks, vs))  # [1, 32, steps, D]
     yo, _, sn, zn = oracle.forward_causal(qn, kn, vn, so, zo)
     assert rowerr(host(ys).transpose(1, 0, 2)[None], yo) <= 2e-2
@@ -463,16 +512,16 @@ def nc_cancel_scales(q, k, v, do):
     return np.abs(uq).max(-1), np.abs(uk).max(-1)
 
 
-def check_backward_noncausal(q, k, v, do, dtype, tol=None, totals=False):
+def check_backward_noncausal(q, k, v, do, dtype, tol=None, totals=False, opts=None):
     tol = TOL[dtype] if tol is None else tol
     Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     s = z = None
     if totals:  # the forward's totals, checked against the plain sums, passed on to the backward
-        _, s, z = binding.forward_noncausal(Q, K, V, return_state=True)
+        _, s, z = binding.forward_noncausal(Q, K, V, return_state=True, opts=opts)
         torch.cuda.synchronize()
         _, _, rs, rz = oracle.forward_causal(q, k, v)
         assert max(rowerr(host(s), rs), rowerr(host(z), rz, False)) <= tol
-    dq, dk, dv = binding.backward_noncausal(Q, K, V, dev(do, dtype), s=s, z=z)
+    dq, dk, dv = binding.backward_noncausal(Q, K, V, dev(do, dtype), s=s, z=z, opts=opts)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.backward_noncausal(q, k, v, do)
     dq, dk, dv = host(dq), host(dk), host(dv)
@@ -513,11 +562,7 @@ def test_backward_noncausal_segment_invariance(chunks):
     """Segment lengths change only the summation order of the totals."""
     q, k, v = _qkv(2, 2, 700, 64, 32, F32, 9100)
     do = inputs.gaussian((2, 2, 700, 32), 9104, 1.0, F32)
-    prev = binding.set_segment_chunks(chunks)
-    try:
-        check_backward_noncausal(q, k, v, do, F32)
-    finally:
-        binding.set_segment_chunks(prev)
+    check_backward_noncausal(q, k, v, do, F32, opts=binding.options(segment_chunks=chunks))
 
 
 def test_backward_noncausal_mnist_shape():
@@ -568,14 +613,14 @@ def _state_inputs(B, H, D, M, dtype, seed, sigma=0.1):
     return s0, z0, dsn, dzn
 
 
-def gpu_backward_state(q, k, v, do, dtype, s0, z0, dsn, dzn, use_ckpt=True):
-    out = gpu_forward(q, k, v, dtype, s0, z0)
+def gpu_backward_state(q, k, v, do, dtype, s0, z0, dsn, dzn, use_ckpt=True, opts=None):
+    out = gpu_forward(q, k, v, dtype, s0, z0, opts)
     Q, K, V = dev(q, dtype), dev(k, dtype), dev(v, dtype)
     g = binding.backward_causal(Q, K, V, out["o"], out["den"], dev(do, dtype),
                                 s0=None if s0 is None else dev32(s0), z0=None if z0 is None else dev32(z0),
                                 ckpt=out["ckpt"] if use_ckpt else None,
                                 ds_n=None if dsn is None else dev32(dsn), dz_n=None if dzn is None else dev32(dzn),
-                                state_grad=True)
+                                state_grad=True, opts=opts)
     torch.cuda.synchronize()
     return [host(t) for t in g]
 
@@ -613,11 +658,7 @@ def test_state_gradient_segments(D, M, chunks, use_ckpt):
     q, k, v = _qkv(B, H, N, D, M, F32, 9500 + chunks)
     do = inputs.gaussian((B, H, N, M), 9590)
     s0, z0, dsn, dzn = _state_inputs(B, H, D, M, F32, 9600)
-    binding.set_segment_chunks(chunks)
-    try:
-        got = gpu_backward_state(q, k, v, do, F32, s0, z0, dsn, dzn, use_ckpt)
-    finally:
-        binding.set_segment_chunks(0)
+    got = gpu_backward_state(q, k, v, do, F32, s0, z0, dsn, dzn, use_ckpt, binding.options(segment_chunks=chunks))
     errs = state_grad_errors(got, q, k, v, do, s0, z0, dsn, dzn)
     assert max(errs.values()) <= TOL[F32], errs
 
