@@ -231,6 +231,31 @@ int la_forward_causal(const void *Q, const void *K, const void *V,
                       void *stream, const la_options *opts);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the causal
+ * forward of la_forward_causal with the same arguments and results, minus
+ * `ws` and `ws_bytes`.  Its scratch (segment aggregates, prefix states, the
+ * one-launch form's flags and status word) is a static array of
+ * LA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the library's first use on that GPU until the process ends; the call
+ * allocates nothing.  Sizes whose la_workspace_size(LA_OP_FWD_CAUSAL, ...)
+ * (LA_OP_FWD_DECAY with logA) exceeds it are rejected with
+ * LA_ERR_WORKSPACE before any launch.  Every call on one GPU shares that
+ * GPU's array and leaves its contents behind (each call clears what must
+ * start at zero itself): calls that overlap on one GPU -- on different
+ * streams or host threads -- race; order them on one stream.
+ * la_forward_wait_status does not apply (its status word lives in the
+ * static array; pass opts->status to learn of a wait that gave up).
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+int la_forward_causal_noalloc(const void *Q, const void *K, const void *V,
+                              const float *logA, void *O, float *den,
+                              const float *S0, const float *Z0, float *S_out,
+                              float *Z_out, float *ckpt, int B, int H, int N,
+                              int D, int M, int dtype, int feature,
+                              void *stream, const la_options *opts);
+
+/*
  * Non-causal forward (reading notes on "Transformers are RNNs", section 3.2,
  * eq. 5-6): S = sum_j phi(K_j) V_j^T and Z = sum_j phi(K_j) are formed once
  * per head and reused for every query, O_i = phi(Q_i)^T S / phi(Q_i)^T Z.

@@ -26,6 +26,7 @@ LA_ERR_WAIT = 10
 ENTRY_POINTS = ("la_version", "la_workspace_size", "la_checkpoint_size", "la_segment_length", "la_forward_causal",
                 "la_forward_noncausal", "la_backward_causal", "la_backward_noncausal", "la_decode_step",
                 "la_status_string", "la_last_error", "la_kernel_names", "la_forward_wait_status",
+                "la_forward_causal_noalloc",
                 "la_feature_random", "la_feature_random_vjp", "la_feature_poly2",
                 "la_feature_poly2_vjp")
 
@@ -95,6 +96,8 @@ def load(path: str | None = None):
     lib.la_forward_wait_status.argtypes = [vp, sz] + [i] * 6 + [vp, op]
     lib.la_forward_causal.restype = i
     lib.la_forward_causal.argtypes = [vp] * 11 + [i] * 7 + [vp, sz, vp, op]
+    lib.la_forward_causal_noalloc.restype = i
+    lib.la_forward_causal_noalloc.argtypes = [vp] * 11 + [i] * 7 + [vp, op]
     lib.la_forward_noncausal.restype = i
     lib.la_forward_noncausal.argtypes = [vp] * 6 + [i] * 7 + [vp, sz, vp, op]
     lib.la_backward_causal.restype = i
@@ -298,6 +301,23 @@ def la_forward_causal(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=
                                   _ptr(S_out), _ptr(Z_out), _ptr(ckpt), B, H, N, D, M, dt, feature, _ptr(ws), nb,
                                   _stream(stream), _opt(opts))
     _check(st, "la_forward_causal")
+
+
+def la_forward_causal_noalloc(Q, K, V, O, den=None, S0=None, Z0=None, S_out=None, Z_out=None, ckpt=None,
+                              stream=None, logA=None, feature=0, opts=None):
+    """la_forward_causal with the library's static per-GPU scratch in place of a workspace (allocates nothing;
+    calls that overlap on one GPU race)."""
+    B, H, N, D, M = _sizes(Q, K, V)
+    _expect("O", O, (B, H, N, M), Q.dtype)
+    _expect("den", den, (B, H, N), torch.float32)
+    _expect("logA", logA, (B, H, N), torch.float32)
+    _expect_state(("S0", "Z0"), S0, Z0, B, H, D, M)
+    _expect_state(("S_out", "Z_out"), S_out, Z_out, B, H, D, M)
+    _expect_ckpt(ckpt, B, H, N, D, M, opts)
+    st = load().la_forward_causal_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(logA), _ptr(O), _ptr(den), _ptr(S0),
+                                          _ptr(Z0), _ptr(S_out), _ptr(Z_out), _ptr(ckpt), B, H, N, D, M,
+                                          dtype_code(Q.dtype), feature, _stream(stream), _opt(opts))
+    _check(st, "la_forward_causal_noalloc")
 
 
 def la_forward_noncausal(Q, K, V, O, ws=None, stream=None, feature=0, S_out=None, Z_out=None, opts=None):

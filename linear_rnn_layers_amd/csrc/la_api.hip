@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -21,6 +22,18 @@
 #include "la_decay.h"
 #include "la_bwd2.h"
 #include "la_feature.h"
+
+// la_forward_causal_noalloc takes the workspace of the causal forward from
+// this file-scope array instead of from the caller: for callers that cannot
+// allocate.  Each GPU holds its own copy (allocated when the code object is
+// loaded on it, kept until the process ends); host code reaches it only
+// through the device address that hipGetSymbolAddress returns with that
+// device current (scratch_ptr), never through the array's name.  Every call
+// on one GPU shares it: calls that overlap on one GPU race.  The forward
+// clears what must start at zero (the one-launch form's flags and status
+// word) itself, with a kernel.
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -636,10 +649,29 @@ int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int 
   return feat_poly2_impl<la::bf16_t, 64>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
 }
 
+// ------------------------------------------------------- static scratch
+// Device address of `scratch` (top of this file) on the current device,
+// looked up once per device with that device current.
+int scratch_ptr(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static void* ptrs[kMaxDev];
+  static hipError_t errs[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+    return fail(LA_ERR_HIP, "la_forward_causal_noalloc: no current device");
+  std::call_once(once[dev], [dev] { errs[dev] = hipGetSymbolAddress(&ptrs[dev], HIP_SYMBOL(scratch)); });
+  if (errs[dev] != hipSuccess || !ptrs[dev])
+    return fail(LA_ERR_HIP, std::string("la_forward_causal_noalloc: hipGetSymbolAddress(scratch): ") +
+                                hipGetErrorString(errs[dev]));
+  *out = ptrs[dev];
+  return LA_OK;
+}
+
 int forward_causal_entry(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
                          const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H,
                          int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
-                         const la_options* opts);
+                         const la_options* opts, bool use_scratch);
 
 }  // namespace
 
@@ -718,7 +750,14 @@ int la_forward_causal(const void* Q, const void* K, const void* V, const float* 
                       int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
                       const la_options* opts) {
   return forward_causal_entry(Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, B, H, N, D, M, dtype, feature, ws,
-                              ws_bytes, stream, opts);
+                              ws_bytes, stream, opts, false);
+}
+
+int la_forward_causal_noalloc(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
+                              const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H,
+                              int N, int D, int M, int dtype, int feature, void* stream, const la_options* opts) {
+  return forward_causal_entry(Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, B, H, N, D, M, dtype, feature,
+                              nullptr, 0, stream, opts, true);
 }
 
 }  // extern "C"
@@ -729,7 +768,7 @@ namespace {
 int forward_causal_entry(const void* Q, const void* K, const void* V, const float* logA, void* O, float* den,
                          const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int B, int H,
                          int N, int D, int M, int dtype, int feature, void* ws, size_t ws_bytes, void* stream,
-                         const la_options* opts) {
+                         const la_options* opts, bool use_scratch) {
   g_err.clear();
   if (feature != LA_FEATURE_ELU1 && feature != LA_FEATURE_IDENTITY)
     return fail(LA_ERR_ARG, "feature must be LA_FEATURE_ELU1 (0) or LA_FEATURE_IDENTITY (1)");
@@ -745,6 +784,15 @@ int forward_causal_entry(const void* Q, const void* K, const void* V, const floa
   const size_t es = esize(dtype), bh = (size_t)p.BH;
   const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
+  if (use_scratch && uses_ws) {  // the library's static scratch of this device in place of a workspace
+    if (need > kScratchBytes)
+      return fail(LA_ERR_WORKSPACE, "these sizes need " + std::to_string(need) + " bytes of scratch; the static "
+                  "scratch of la_forward_causal_noalloc holds " + std::to_string(kScratchBytes) +
+                  " (use la_forward_causal with a workspace)");
+    st = scratch_ptr(&ws);
+    if (st) return st;
+    ws_bytes = kScratchBytes;
+  }
   if (uses_ws && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
   st = check_ptrs({rng("Q", Q, bh * N * D * es, false), rng("K", K, bh * N * D * es, false),
