@@ -8,38 +8,76 @@
 //   dV_j      = sum_{i>=j} g_i (phi(Q_i) . phi(K_j))     (eq. 15, backward sum)
 // i.e. eq. 13-15 on [V, 1] with upstream [g, c].  The backward sums run over
 // the reverse state R = sum_{i>=j} phi(Q_i) g_i^T, r = sum_{i>=j} c_i phi(Q_i).
+// Writing q'_i = phi(Q_i) / den_i, every term that carries 1/den_i takes it
+// from q': R = sum_i q'_i dO_i^T, r = -sum_i (O_i . dO_i) q'_i,
+// phi(Q_i) (g_i . V_j + c_i) = q'_i (dO_i . V_j - O_i . dO_i) and
+// g_i (phi(Q_i) . phi(K_j)) = dO_i (q'_i . phi(K_j)), so dO (exact in one bf16
+// plane for bf16 storage) is the other operand and no g is staged.
 //
 // Pass A (k_bq) walks each segment forward from its checkpoint state, as
 // the forward did: it forms S_i, Z_i exactly (the state before the chunk plus
 // the causal part of the chunk), recomputes den_i = phi(Q_i) . Z_i and
 // O_i . dO_i = phi(Q_i)^T S_i dO_i / den_i in float32 -- so neither the stored
-// O nor den is read, and g_i . V_j + c_i = (dO_i . V_j - O_i . dO_i) / den_i
-// cancels exactly where V_j = O_i even for bf16 storage -- writes dQ and the
-// per-token pair (1/den_i, O_i . dO_i), and sums the segment's exact reverse
-// aggregate (R, r over its tokens).  The suffix sums of those aggregates
-// (the final-state gradient dS_N, dZ_N added) give every segment the
-// reverse state after its last token.  Pass B (k_bkv) walks each segment
-// backwards from that state and forms dK, dV from the stored pairs.
+// O nor den is read, and dO_i . V_j - O_i . dO_i cancels exactly where V_j = O_i
+// even for bf16 storage -- writes dQ and the per-token pair (1/den_i,
+// O_i . dO_i), and sums the segment's exact reverse aggregate (R, r over its
+// tokens).  The suffix sums of those aggregates (the final-state gradient
+// dS_N, dZ_N added) give every segment the reverse state after its last
+// token.  Pass B (k_bkv) walks each segment backwards from that state and
+// forms dK, dV from the stored pairs.
 //
-// Each pass carries one state, so a workgroup needs one state in registers
-// and LDS.  Chunks of 32 tokens, four wavefronts in two roles:
-//   pass A  waves 0, 1: query rows 16w..16w+15 (S_i dO_i, Z_i, den_i,
-//                       O_i . dO_i, dQ, the row [g_i | c_i]);
-//           waves 2, 3: the chunk's state update S += phi(K)^T V, Z +=
-//                       phi(K)^T 1 in registers, and the previous chunk's
-//                       share of the reverse aggregate [g | c]^T phi(Q).
-//   pass B  waves 0, 1: key rows 16w..16w+15 (dK, dV);
-//           waves 2, 3: the chunk's share of the reverse state, R^T +=
-//                       [g | c]^T phi(Q), in registers.
-// Two barriers per chunk: after staging, and after phase 1; the state the
-// next chunk reads is staged, and the next chunk's operands, after it.
+// Chunks of 64 tokens, four wavefronts in one role: wave w owns rows
+// 16w..16w+15 of the chunk (query rows in pass A, key rows in pass B) and a
+// quarter of the state's tiles (S^T and [R | r]^T in pass A, [R | r]^T in
+// pass B).  Each pass carries one state in registers and stages it in LDS
+// once per chunk.  Barriers per chunk: pass A three (after staging; after the
+// query rows, whose q' and O.dO the aggregate product reads; after that
+// product and the state update), pass B two (after staging; after the key
+// rows and the reverse-state update, which read only this chunk's operands).
 #pragma once
 
 #include "la_kernels.h"
 
 namespace la {
 
-constexpr int CB2 = 32;  // chunk of the two-pass backward
+// -O.dO of row i as the extra columns M (and M + 1) of the dO planes, so that
+// r is one more row block of [R | r]^T: for a one-plane dO (bf16 storage) the
+// value is written as a rounded part in column M and its rounded residual in
+// column M + 1 (their sum is float32-accurate), otherwise split into the
+// planes of column M.
+template <int NP, int ROWS, int COLS, int PAD>
+__device__ __forceinline__ void put_neg_odo(Planes<NP, ROWS, COLS, PAD>& p, int row, int M, float odo) {
+  const float x = -odo;
+  if constexpr (NP == 1) {
+    const __bf16 h = (__bf16)x;
+    const __bf16 l = (__bf16)(x - (float)h);
+    p.v[0][row][M] = __builtin_bit_cast(bf16_t, h);
+    p.v[0][row][M + 1] = __builtin_bit_cast(bf16_t, l);
+  } else {
+    p.put1(row, M, x);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) p.v[q][row][M + 1] = 0;
+  }
+}
+
+// [R | r]^T += [dO | -O.dO]^T q' over one 64-token chunk: tiles t = w + 4k
+// (t < the tile count) of the (M/16 + 1) x (D/16) tile grid, value block
+// t / DB (block M/16 holds the r rows M, M + 1), feature block t % DB.
+template <typename T, int D, int M, int NTR, int NPO, int NPQ>
+__device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, M + 16>& ot,
+                                           const Planes<NPQ, CH, D>& qt, int w, int g, int r16) {
+  using P = Prec<T>;
+  constexpr int DB = D / 16, NRT = (M / 16 + 1) * DB, NA = P::NDO < P::dR ? P::NDO : P::dR;
+#pragma unroll
+  for (int k = 0; k < NTR; ++k) {
+    const int t = w + 4 * k, mb = t / DB, db = t % DB;
+    if (t >= NRT) break;
+#pragma unroll
+    for (int s = 0; s < CH / 32; ++s)
+      mmaf<NA, P::dR>(accR[k], ot.template tfrag<NA>(32 * s, 16 * mb, g, r16),
+                      qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16));
+  }
+}
 
 // ===================================================================== B-A
 template <typename T, int D, int M>
@@ -49,43 +87,32 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
                                             float2* __restrict__ gc, float* __restrict__ ragg, int N, int L, int nseg,
                                             int fm) {
   using P = Prec<T>;
-  constexpr int CB = CB2;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
-  constexpr int NTS = DB * MB / 2;        // S^T tiles per update wave
-  constexpr int NZS = DB / 2;             // Z blocks per update wave
-  constexpr int NTR = (MB + 1) * DB / 2;  // [R | r]^T tiles per update wave
-  __shared__ Planes<P::NK, CB, D> kt;           // phi(K)
-  __shared__ Planes<P::NV, CB, M> vt;           // V
-  __shared__ Planes<P::NDO, CB, M> ot;          // dO
-  __shared__ Planes<P::NQ, CB, D> qt[2];        // phi(Q) of this chunk and the previous one
-  __shared__ Planes<P::NG, CB, M + 16> gt[2];   // [g | c | 0] of this chunk and the previous one
-  __shared__ Planes<P::NS, D, M> sp;            // S before this chunk, [d][m]
-  __shared__ alignas(16) float sZ[D];           // Z before this chunk
+  constexpr int NTS = DB * MB / 4;        // S^T tiles per wave
+  constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
+  static_assert((DB * MB) % 4 == 0, "S tiles must divide over four waves");
+  __shared__ Planes<P::NQ, CH, D> qt;          // phi(Q), then q' = phi(Q) / den row by row
+  __shared__ Planes<P::NK, CH, D> kt;          // phi(K)
+  __shared__ Planes<P::NV, CH, M> vt;          // V
+  __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]
+  __shared__ Planes<P::NS, D, M> sp;           // S before this chunk, [d][m]
+  __shared__ alignas(16) float sZ[D];          // Z before this chunk
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const bool qrole = w < 2;
-  const int so = w - 2;  // rank among the update waves
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
   const Frag<1> ones = ones_frag();
-  gt[0].zero_cols(M + 1, M + 16);
-  gt[1].zero_cols(M + 1, M + 16);
+  ot.zero_cols(M + 2, M + 16);
+  auto sdb = [&](int k) { return (w + 4 * k) % DB; };
+  auto smb = [&](int k) { return (w + 4 * k) / DB; };
+  const bool zw = w < DB;  // holds Z of feature block w
 
-  // update-wave tiles: S^T tile k: t = so + 2k, feature block t % DB, value block t / DB;
-  // [R | r]^T tile k: t = so + 2k, feature block t % DB, value block t / DB (block MB holds r)
-  auto tdb = [&](int k) { return (so + 2 * k) % DB; };
-  auto tmb = [&](int k) { return (so + 2 * k) / DB; };
-
-  const int nchunk = (t1 - t0 + CB - 1) / CB;
-  constexpr int OQ_ = RowBuf<T, CB, D>::VEC < NT ? NT / 2 : 0;
-  constexpr int OM_ = RowBuf<T, CB, M>::VEC < NT ? NT / 2 : 0;
-  RowBuf<T, CB, D> bq;
-  RowBuf<T, CB, D, NT, OQ_> bk;
-  RowBuf<T, CB, M> bv;
-  RowBuf<T, CB, M, NT, OM_> bd;
+  const int nchunk = (t1 - t0 + CH - 1) / CH;
+  RowBuf<T, CH, D> bq, bk;
+  RowBuf<T, CH, M> bv, bd;
   auto fetch = [&](int c0) {
-    const int nv = min(CB, t1 - c0);
+    const int nv = min(CH, t1 - c0);
     bq.load(Q + offD + (size_t)c0 * D, nv);
     bk.load(K + offD + (size_t)c0 * D, nv);
     bv.load(V + offM + (size_t)c0 * M, nv);
@@ -93,99 +120,98 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   };
   fetch(t0);
 
+  // S^T tiles (acc[r] = S[16 db + r16][16 mb + 4 g + r]) and Z of block w, from the forward's checkpoint entry
   f32x4_t accS[NTS], accR[NTR];
-  float zz[NZS];
-#pragma unroll
-  for (int k = 0; k < NTR; ++k) accR[k] = zero4();
-  auto stage_S = [&]() {
-    float v4[4];
-#pragma unroll
-    for (int k = 0; k < NTS; ++k) {
-      acc_to4(accS[k], v4);
-      sp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZS; ++j) sZ[16 * (so + 2 * j) + r16] = zz[j];
-    }
-  };
-  if (!qrole) {  // the state before the segment: the forward's checkpoint entry
+  float zz = 0.f;
+  {
     const float* st = ckpt + ((size_t)bh * (nseg + 1) + seg) * SV;
 #pragma unroll
     for (int k = 0; k < NTS; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(st + (16 * tdb(k) + r16) * M + 16 * tmb(k) + 4 * g);
+      const float4 a = *reinterpret_cast<const float4*>(st + (16 * sdb(k) + r16) * M + 16 * smb(k) + 4 * g);
       accS[k] = f32x4_t{a.x, a.y, a.z, a.w};
     }
-#pragma unroll
-    for (int j = 0; j < NZS; ++j) zz[j] = st[D * M + 16 * (so + 2 * j) + r16];
-    stage_S();
+    if (zw) zz = st[D * M + 16 * w + r16];
   }
-
-  // [R | r]^T += [g | c]^T phi(Q) over the chunk staged in buffer b
-  auto rproduct = [&](int b) {
 #pragma unroll
-    for (int k = 0; k < NTR; ++k)
-      mmaf<P::dR, P::dR>(accR[k], gt[b].template tfrag<P::dR>(0, 16 * tmb(k), g, r16),
-                         qt[b].template tfrag<P::dR>(0, 16 * tdb(k), g, r16));
-  };
+  for (int k = 0; k < NTR; ++k) accR[k] = zero4();
 
   for (int ci = 0; ci < nchunk; ++ci) {
-    const int c0 = t0 + ci * CB, cur = ci & 1;
-    const int nv = min(CB, t1 - c0);
-    // ---- stage this chunk (the barrier ending the previous phase 1 separates the previous reads)
-    bq.template stage_phi<P::NQ, CB, D, 8, 0>(qt[cur], nv, nullptr, fm);
-    bk.template stage_phi<P::NK, CB, D, 8, 0>(kt, nv, nullptr, fm);
+    const int c0 = t0 + ci * CH;
+    const int nv = min(CH, t1 - c0);
+    // ---- stage the state before this chunk and the chunk's operands (the barrier ending the previous
+    // chunk separates them from every read of the previous ones)
+    {
+      float v4[4];
+#pragma unroll
+      for (int k = 0; k < NTS; ++k) {
+        acc_to4(accS[k], v4);
+        sp.put4(16 * sdb(k) + r16, 16 * smb(k) + 4 * g, v4);
+      }
+      if (zw && g == 0) sZ[16 * w + r16] = zz;
+    }
+    bq.template stage_phi<P::NQ, CH, D, 8, 0>(qt, nv, nullptr, fm);
+    bk.template stage_phi<P::NK, CH, D, 8, 0>(kt, nv, nullptr, fm);
     bv.stage_values(vt);
     bd.stage_values(ot);
-    if (ci + 1 < nchunk) fetch(c0 + CB);
+    if (ci + 1 < nchunk) fetch(c0 + CH);
     __syncthreads();
 
-    if (qrole) {
-      // ================ query rows il: S_i = S + sum_{j<=i} phi(K_j) V_j^T, Z_i likewise
-      const int ib = w, il = 16 * ib + r16;
+    // ================ query rows il: S_i = S + sum_{j<=i} phi(K_j) V_j^T, Z_i likewise
+    {
+      const int il = 16 * w + r16;
       const bool row_ok = il < nv;
       constexpr int NO = cmax(P::Bt, P::U1_b);
       Frag<NO> dof[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
-      // (V_j . dO_i) for j <= i as a B operand under the accumulator map, and the mask [j <= i]
-      Frag<P::U2> btf;
-      Frag<1> onef;
-      {
-        f32x4_t bt[2];
+      // (V_j . dO_i) for j <= i as B operands under the accumulator map (pairs of 16-row blocks), and the
+      // mask [j <= i]
+      Frag<P::U2> btf[2];
+      Frag<1> onef[2];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          f32x4_t a = zero4();
-          if (jb <= ib) {
+      for (int p = 0; p < 2; ++p) {
+        if (2 * p <= w) {
+          f32x4_t bt[2];
 #pragma unroll
-            for (int s = 0; s < M / 32; ++s)
-              mmaf<P::Bt, P::Bt>(a, vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
-            if (jb == ib) {
+          for (int h = 0; h < 2; ++h) {
+            const int jb = 2 * p + h;
+            f32x4_t a = zero4();
+            if (jb <= w) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (4 * g + r > r16) a[r] = 0.f;  // j > i
+              for (int s = 0; s < M / 32; ++s)
+                mmaf<P::Bt, P::Bt>(a, vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
+              if (jb == w) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (4 * g + r > r16) a[r] = 0.f;  // j > i
+              }
             }
+            bt[h] = a;
           }
-          bt[jb] = a;
-        }
-        btf = acc2frag<P::U2>(bt[0], bt[1]);
+          btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-          onef.p[0][e] = j <= il ? (__bf16)1.0f : (__bf16)0.0f;
+          for (int e = 0; e < 8; ++e) {
+            const int j = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+            onef[p].p[0][e] = j <= il ? (__bf16)1.0f : (__bf16)0.0f;
+          }
         }
       }
       f32x4_t U[DB], ZC[DB];
+      constexpr int NKA = cmax(P::U2, P::Zc);
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
         f32x4_t u = zero4(), zc = zero4();
 #pragma unroll
         for (int s = 0; s < M / 32; ++s)
           mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
-        constexpr int NKA = cmax(P::U2, P::Zc);
-        const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(0, 16 * d0, g, r16);
-        mmaf<P::U2, P::U2>(u, kfa, btf);
-        mmaf<P::Zc, 1>(zc, kfa, onef);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if (2 * p <= w) {
+            const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
+            mmaf<P::U2, P::U2>(u, kfa, btf[p]);
+            mmaf<P::Zc, 1>(zc, kfa, onef[p]);
+          }
+        }
         const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
         zc += f32x4_t{z4.x, z4.y, z4.z, z4.w};
         U[d0] = u;    // S_i dO_i   [d][i]
@@ -195,7 +221,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
       float qv[DB][4];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
-        qt[cur].get4(il, 16 * d0 + 4 * g, qv[d0]);
+        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pu += qv[d0][r] * U[d0][r];
@@ -206,57 +232,54 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
       pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
       const float invz = row_ok ? 1.f / pz : 0.f;
       const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
-      if (row_ok) {
 #pragma unroll
-        for (int d0 = 0; d0 < DB; ++d0) {
-          float o[4];
+      for (int d0 = 0; d0 < DB; ++d0) {
+        float o[4], qs[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
-          IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
+        for (int r = 0; r < 4; ++r) {
+          o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
+          qs[r] = qv[d0][r] * invz;
         }
-        if (g == 0) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
+        if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
+        qt.put4(il, 16 * d0 + 4 * g, qs);  // this lane's own elements of its own row: q'_i
       }
-      // row i of [g | c]: g_i = dO_i / den_i over this lane's quarter of the features, c_i = -(O_i . dO_i) / den_i
-#pragma unroll
-      for (int mm = 0; mm < M / 4; mm += 4) {
-        float dv[4];
-        ot.get4(il, g * (M / 4) + mm, dv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dv[q] *= invz;
-        gt[cur].put4(il, g * (M / 4) + mm, dv);
-      }
-      if (g == 0) gt[cur].put1(il, M, -odo * invz);
-    } else {
-      // ================ the previous chunk's reverse aggregate, then the state update
-      if (ci > 0) rproduct(cur ^ 1);
-      constexpr int NKB = cmax(P::dS_b, P::Zc);
-#pragma unroll
-      for (int k = 0; k < NTS; ++k)
-        mmaf<P::dS_a, P::dS_b>(accS[k], vt.template tfrag<P::dS_a>(0, 16 * tmb(k), g, r16),
-                               kt.template tfrag<NKB>(0, 16 * tdb(k), g, r16));
-#pragma unroll
-      for (int j = 0; j < NZS; ++j) {
-        f32x4_t dz = zero4();
-        mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(0, 16 * (so + 2 * j), g, r16));
-        zz[j] += dz[0];
+      if (g == 0) {
+        if (row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
+        put_neg_odo(ot, il, M, odo);
       }
     }
     __syncthreads();
-    if (!qrole) stage_S();  // S, Z before the next chunk
+
+    // ================ the chunk's share of the reverse aggregate, then the state update
+    rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
+    constexpr int NKB = cmax(P::dS_b, P::Zc);
+#pragma unroll
+    for (int s = 0; s < CH / 32; ++s) {
+#pragma unroll
+      for (int k = 0; k < NTS; ++k)
+        mmaf<P::dS_a, P::dS_b>(accS[k], vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16),
+                               kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16));
+      if (zw) {
+        f32x4_t dz = zero4();
+        mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * w, g, r16));
+        zz += dz[0];
+      }
+    }
+    __syncthreads();
   }
-  if (!qrole && nchunk > 0) rproduct((nchunk - 1) & 1);
-  // the segment's reverse aggregate (sum over its tokens of phi(Q_i) g_i^T, c_i phi(Q_i)), [d][m] then r,
-  // for the segments before it; segment 0's is not needed
-  if (!qrole && seg > 0) {
+  // the segment's reverse aggregate (sum over its tokens of phi(Q_i) g_i^T, c_i phi(Q_i)), [d][m] then r, for the
+  // segments before it; segment 0's is not needed
+  if (seg > 0) {
     float* out = ragg + ((size_t)bh * nseg + seg) * SV;
 #pragma unroll
     for (int k = 0; k < NTR; ++k) {
-      const int db = tdb(k), mb = tmb(k);
+      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+      if (t >= NRT) break;
       if (mb < MB) {
         *reinterpret_cast<float4*>(out + (16 * db + r16) * M + 16 * mb + 4 * g) =
             make_float4(accR[k][0], accR[k][1], accR[k][2], accR[k][3]);
       } else if (g == 0) {
-        out[D * M + 16 * db + r16] = accR[k][0];  // row M of the tile: r
+        out[D * M + 16 * db + r16] = accR[k][0] + accR[k][1];  // rows M and M + 1 of the tile: r
       }
     }
   }
@@ -266,9 +289,9 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
 // Reverse walk of a segment: key rows form dK, dV from the reverse state
 // after the chunk (R, r: the final-state gradient plus the later segments'
 // aggregates plus the later chunks of this segment) and the chunk's own
-// causal part; the update waves carry R, r to before the chunk.  The
-// sequence's first segment writes the reverse state carried through token 1:
-// the gradient of the initial state (dS0, dZ0).
+// causal part; the same waves add the chunk's share to the reverse state in
+// registers.  The sequence's first segment writes the reverse state carried
+// through token 1: the gradient of the initial state (dS0, dZ0).
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __restrict__ K,
                                              const T* __restrict__ V, const T* __restrict__ dO,
@@ -277,131 +300,115 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
                                              T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dS0,
                                              float* __restrict__ dZ0, int N, int L, int nseg, int scanned, int fm) {
   using P = Prec<T>;
-  constexpr int CB = CB2;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
-  constexpr int NTR = DB * MB / 2;  // R^T tiles per update wave
-  constexpr int NZR = DB / 2;       // r blocks per update wave
-  __shared__ Planes<P::NQ, CB, D> qt;          // phi(Q)
-  __shared__ Planes<P::NK, CB, D> kt;          // phi(K)
-  __shared__ Planes<P::NV, CB, M> vt;          // V
-  __shared__ Planes<P::NDO, CB, M> ot;         // dO
-  __shared__ Planes<P::NG, CB, M + 16> gt;     // [g | c | 0]
+  constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
+  __shared__ Planes<P::NQ, CH, D> qt;          // q' = phi(Q) / den
+  __shared__ Planes<P::NK, CH, D> kt;          // phi(K)
+  __shared__ Planes<P::NV, CH, M> vt;          // V
+  __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]
   __shared__ Planes<P::NR, D, M> rp;           // R after this chunk, [d][m]
   __shared__ alignas(16) float sr[D];          // r after this chunk
-  __shared__ alignas(16) float sInv[CB];       // 1 / den_i (0 past the end)
-  __shared__ alignas(16) float sOdo[CB];       // O_i . dO_i (0 past the end)
+  __shared__ alignas(16) float sOdo[CH];       // O_i . dO_i (0 past the end)
 
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const bool krole = w < 2;
-  const int so = w - 2;
   const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
-  gt.zero_cols(M + 1, M + 16);
-  auto tdb = [&](int k) { return (so + 2 * k) % DB; };
-  auto tmb = [&](int k) { return (so + 2 * k) / DB; };
+  ot.zero_cols(M + 2, M + 16);
 
-  const int nchunk = (t1 - t0 + CB - 1) / CB;
-  constexpr int OQ_ = RowBuf<T, CB, D>::VEC < NT ? NT / 2 : 0;
-  constexpr int OM_ = RowBuf<T, CB, M>::VEC < NT ? NT / 2 : 0;
-  RowBuf<T, CB, D> bq;
-  RowBuf<T, CB, D, NT, OQ_> bk;
-  RowBuf<T, CB, M> bv;
-  RowBuf<T, CB, M, NT, OM_> bd;
-  using BD = RowBuf<T, CB, M, NT, OM_>;
-  float2 pgc = make_float2(0.f, 0.f);  // (1/den, O.dO) of token tid of the chunk (threads < CB)
-  float pinv[BD::CNT];                  // 1/den of the rows of this thread's dO vectors
+  const int nchunk = (t1 - t0 + CH - 1) / CH;
+  using BQ = RowBuf<T, CH, D>;
+  BQ bq;
+  RowBuf<T, CH, D> bk;
+  RowBuf<T, CH, M> bv, bd;
+  float2 pgc = make_float2(0.f, 0.f);  // (1/den, O.dO) of token tid of the chunk (threads < CH)
+  float pinv[BQ::CNT];                  // 1/den of the rows of this thread's Q vectors
   auto fetch = [&](int c0) {
-    const int nv = min(CB, t1 - c0);
+    const int nv = min(CH, t1 - c0);
     bq.load(Q + offD + (size_t)c0 * D, nv);
     bk.load(K + offD + (size_t)c0 * D, nv);
     bv.load(V + offM + (size_t)c0 * M, nv);
     bd.load(dO + offM + (size_t)c0 * M, nv);
-    if (tid < CB) pgc = tid < nv ? gc[(size_t)bh * N + c0 + tid] : make_float2(0.f, 0.f);
-    if (BD::owns()) {
+    if (tid < CH) pgc = tid < nv ? gc[(size_t)bh * N + c0 + tid] : make_float2(0.f, 0.f);
 #pragma unroll
-      for (int i = 0; i < BD::CNT; ++i) {
-        const int row = BD::row_of(i);
-        pinv[i] = row < nv ? gc[(size_t)bh * N + c0 + row].x : 0.f;
-      }
+    for (int i = 0; i < BQ::CNT; ++i) {
+      const int row = BQ::row_of(i);
+      pinv[i] = row < nv ? gc[(size_t)bh * N + c0 + row].x : 0.f;
     }
   };
-  fetch(t0 + (nchunk - 1) * CB);
+  fetch(t0 + (nchunk - 1) * CH);
 
   // reverse state after the segment: the final-state gradient plus the later segments' aggregates (entry seg
-  // of the suffix sums when scanned, else their sum in segment order), summed through R's planes as scratch
+  // of the suffix sums when scanned, which holds the sum over p > seg, else their sum in segment order),
+  // summed through R's planes as scratch.  Tile k of wave w: t = w + 4k, value block t / DB (block MB: r),
+  // feature block t % DB; acc[r] = R[16 db + r16][16 mb + 4 g + r].
   f32x4_t accR[NTR];
-  float zr[NZR];
 #pragma unroll
   for (int k = 0; k < NTR; ++k) accR[k] = zero4();
-#pragma unroll
-  for (int j = 0; j < NZR; ++j) zr[j] = 0.f;
   const float* rg = nseg > 1 ? ragg + (size_t)bh * nseg * SV : nullptr;
   const bool later = rg && seg + 1 < nseg;
   if (later || dSN) {
-    // (scanned: entry s holds the sum over p > s)
     const int r0 = !later ? 0 : scanned ? seg : seg + 1, r1 = !later ? 0 : scanned ? seg + 1 : nseg;
     static_assert(sizeof(rp.v) >= SV * sizeof(float), "R planes too small to hold a float32 state");
     float* sbuf = reinterpret_cast<float*>(&rp.v[0][0][0]);
     sum_states<D, M, NT>(sbuf, dSN ? dSN + (size_t)bh * D * M : nullptr, dZN ? dZN + (size_t)bh * D : nullptr,
                          later ? rg : nullptr, r0, r1);
     __syncthreads();
-    if (!krole) {
 #pragma unroll
-      for (int k = 0; k < NTR; ++k) {
-        const float4 a = *reinterpret_cast<const float4*>(sbuf + (16 * tdb(k) + r16) * M + 16 * tmb(k) + 4 * g);
+    for (int k = 0; k < NTR; ++k) {
+      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+      if (t >= NRT) break;
+      if (mb < MB) {
+        const float4 a = *reinterpret_cast<const float4*>(sbuf + (16 * db + r16) * M + 16 * mb + 4 * g);
         accR[k] = f32x4_t{a.x, a.y, a.z, a.w};
+      } else if (g == 0) {
+        accR[k][0] = sbuf[D * M + 16 * db + r16];  // r in row M of the tile
       }
-#pragma unroll
-      for (int j = 0; j < NZR; ++j) zr[j] = sbuf[D * M + 16 * (so + 2 * j) + r16];
     }
     __syncthreads();
   }
-  auto stage_R = [&]() {
-    float v4[4];
-#pragma unroll
-    for (int k = 0; k < NTR; ++k) {
-      acc_to4(accR[k], v4);
-      rp.put4(16 * tdb(k) + r16, 16 * tmb(k) + 4 * g, v4);
-    }
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZR; ++j) sr[16 * (so + 2 * j) + r16] = zr[j];
-    }
-  };
-  if (!krole) stage_R();
 
   for (int ci = nchunk - 1; ci >= 0; --ci) {
-    const int c0 = t0 + ci * CB;
-    const int nv = min(CB, t1 - c0);
-    // ---- stage this chunk
-    bq.template stage_phi<P::NQ, CB, D, 8, 0>(qt, nv, nullptr, fm);
-    bk.template stage_phi<P::NK, CB, D, 8, 0>(kt, nv, nullptr, fm);
-    bv.stage_values(vt);
-    bd.stage_values(ot);
-    // rows of [g | c]: g_i = dO_i / den_i from this thread's dO vectors, c_i = -(O_i . dO_i) / den_i
-    if (BD::owns()) {
+    const int c0 = t0 + ci * CH;
+    const int nv = min(CH, t1 - c0);
+    // ---- stage R, r after this chunk and the chunk's operands
+    {
+      float v4[4];
 #pragma unroll
-      for (int i = 0; i < BD::CNT; ++i) {
-        float x[BD::E];
-        IO<T>::unpack(bd.r[i], x);
-#pragma unroll
-        for (int e = 0; e < BD::E; ++e) x[e] *= pinv[i];
-        gt.template put<BD::E>(BD::row_of(i), BD::col_of(i), x);
+      for (int k = 0; k < NTR; ++k) {
+        const int t = w + 4 * k, mb = t / DB, db = t % DB;
+        if (t >= NRT) break;
+        if (mb < MB) {
+          acc_to4(accR[k], v4);
+          rp.put4(16 * db + r16, 16 * mb + 4 * g, v4);
+        } else if (g == 0) {
+          sr[16 * db + r16] = accR[k][0] + accR[k][1];
+        }
       }
     }
-    if (tid < CB) {
-      sInv[tid] = pgc.x;
-      sOdo[tid] = pgc.y;
-      gt.put1(tid, M, -pgc.y * pgc.x);
+#pragma unroll
+    for (int i = 0; i < BQ::CNT; ++i) {  // q' = phi(Q) / den from this thread's Q vectors
+      float x[BQ::E];
+      IO<T>::unpack(bq.r[i], x);
+#pragma unroll
+      for (int e = 0; e < BQ::E; ++e) x[e] = feat(x[e], fm) * pinv[i];
+      qt.template put<BQ::E>(BQ::row_of(i), BQ::col_of(i), x);
     }
-    if (ci > 0) fetch(c0 - CB);
+    bk.template stage_phi<P::NK, CH, D, 8, 0>(kt, nv, nullptr, fm);
+    bv.stage_values(vt);
+    bd.stage_values(ot);
+    if (tid < CH) {
+      sOdo[tid] = pgc.y;
+      put_neg_odo(ot, tid, M, pgc.y);
+    }
+    if (ci > 0) fetch(c0 - CH);
     __syncthreads();
 
-    if (krole) {
+    // ================ key rows jl
+    {
       constexpr int NKT = cmax(P::At, P::VR);
       constexpr int NVT = cmax(P::Wt, P::KR_b);
-      const int jb = w, jl = 16 * jb + r16;
+      const int jl = 16 * w + r16;
       const bool row_ok = jl < nv;
       Frag<NKT> kfr[D / 32];
 #pragma unroll
@@ -409,43 +416,53 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
       Frag<NVT> vfr[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
-      // A_ij = phi(Q_i) . phi(K_j) and W_ij = (dO_i . V_j - O_i . dO_i) / den_i for i >= j (rows i, columns j)
-      f32x4_t at[2], wt[2];
+      // A'_ij = q'_i . phi(K_j) and W'_ij = dO_i . V_j - O_i . dO_i for i >= j (rows i, columns j), in pairs of
+      // 16-row blocks as B operands under the accumulator map
+      Frag<P::dK> wfr[2];
+      Frag<P::dV> afr[2];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        f32x4_t a = zero4(), b = zero4();
-        if (ib >= jb) {
+      for (int p = 0; p < 2; ++p) {
+        if (2 * p + 1 >= w) {
+          f32x4_t at[2], wt[2];
 #pragma unroll
-          for (int s = 0; s < D / 32; ++s)
-            mmaf<P::At, P::At>(a, qt.template frag<P::At>(16 * ib + r16, 32 * s, g), kfr[s]);
+          for (int h = 0; h < 2; ++h) {
+            const int ib = 2 * p + h;
+            f32x4_t a = zero4(), b = zero4();
+            if (ib >= w) {
 #pragma unroll
-          for (int s = 0; s < M / 32; ++s)
-            mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
-          const float4 iv = *reinterpret_cast<const float4*>(&sInv[16 * ib + 4 * g]);
-          const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
-          const float ivr[4] = {iv.x, iv.y, iv.z, iv.w}, odr[4] = {od.x, od.y, od.z, od.w};
+              for (int s = 0; s < D / 32; ++s)
+                mmaf<P::At, P::At>(a, qt.template frag<P::At>(16 * ib + r16, 32 * s, g), kfr[s]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            b[r] = (b[r] - odr[r]) * ivr[r];
-            if (ib == jb && 4 * g + r < r16) {  // i < j
-              a[r] = 0.f;
-              b[r] = 0.f;
+              for (int s = 0; s < M / 32; ++s)
+                mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
+              const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
+              const float odr[4] = {od.x, od.y, od.z, od.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                b[r] -= odr[r];
+                if (ib == w && 4 * g + r < r16) {  // i < j
+                  a[r] = 0.f;
+                  b[r] = 0.f;
+                }
+              }
             }
+            at[h] = a;
+            wt[h] = b;
           }
+          wfr[p] = acc2frag<P::dK>(wt[0], wt[1]);
+          afr[p] = acc2frag<P::dV>(at[0], at[1]);
         }
-        at[ib] = a;
-        wt[ib] = b;
       }
-      const Frag<P::dK> wfr = acc2frag<P::dK>(wt[0], wt[1]);
-      const Frag<P::dV> afr = acc2frag<P::dV>(at[0], at[1]);
-      // dK_j = (R V_j + r + sum_{i>=j} phi(Q_i) W_ij) phi'(K_j)
+      // dK_j = (R V_j + r + sum_{i>=j} q'_i W'_ij) phi'(K_j)
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
         f32x4_t a = zero4();
 #pragma unroll
         for (int s = 0; s < M / 32; ++s)
           mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
-        mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(0, 16 * d0, g, r16), wfr);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (2 * p + 1 >= w) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
         if (row_ok) {
           float o[4], kv[4];
           kt.get4(jl, 16 * d0 + 4 * g, kv);
@@ -456,45 +473,39 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
           IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
         }
       }
-      // dV_j = R^T phi(K_j) + sum_{i>=j} g_i A_ij
+      // dV_j = R^T phi(K_j) + sum_{i>=j} dO_i A'_ij
+      constexpr int NA = P::NDO < P::dV ? P::NDO : P::dV;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         f32x4_t a = zero4();
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
           mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
-        mmaf<P::dV, P::dV>(a, gt.template tfrag_acc<P::dV>(0, 16 * mb, g, r16), afr);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (2 * p + 1 >= w) mmaf<NA, P::dV>(a, ot.template tfrag_acc<NA>(32 * p, 16 * mb, g, r16), afr[p]);
         if (row_ok) {
           float o[4] = {a[0], a[1], a[2], a[3]};
           IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
         }
       }
-    } else {
-      // R^T += g^T phi(Q), r += phi(Q)^T c (row M of [g | c]) for the earlier chunks
-#pragma unroll
-      for (int k = 0; k < NTR; ++k)
-        mmaf<P::dR, P::dR>(accR[k], gt.template tfrag<P::dR>(0, 16 * tmb(k), g, r16),
-                           qt.template tfrag<P::dR>(0, 16 * tdb(k), g, r16));
-#pragma unroll
-      for (int j = 0; j < NZR; ++j) {
-        f32x4_t dr = zero4();
-        mmaf<P::dR, P::dR>(dr, gt.template tfrag<P::dR>(0, M, g, r16),
-                           qt.template tfrag<P::dR>(0, 16 * (so + 2 * j), g, r16));
-        zr[j] += dr[0];  // row M of the tile, on lanes g = 0
-      }
     }
-    __syncthreads();  // every wavefront is done with this chunk's LDS, and the key rows with R, r
-    if (!krole) stage_R();
+    // ================ the chunk's share of the reverse state (for the earlier chunks)
+    rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
+    __syncthreads();
   }
   // the reverse state carried through the sequence's first token is the gradient of the initial state
-  if (t0 == 0 && dS0 && !krole) {
+  if (t0 == 0 && dS0) {
 #pragma unroll
-    for (int k = 0; k < NTR; ++k)
-      *reinterpret_cast<float4*>(dS0 + (size_t)bh * D * M + (16 * tdb(k) + r16) * M + 16 * tmb(k) + 4 * g) =
-          make_float4(accR[k][0], accR[k][1], accR[k][2], accR[k][3]);
-    if (g == 0) {
-#pragma unroll
-      for (int j = 0; j < NZR; ++j) dZ0[(size_t)bh * D + 16 * (so + 2 * j) + r16] = zr[j];
+    for (int k = 0; k < NTR; ++k) {
+      const int t = w + 4 * k, mb = t / DB, db = t % DB;
+      if (t >= NRT) break;
+      if (mb < MB) {
+        *reinterpret_cast<float4*>(dS0 + (size_t)bh * D * M + (16 * db + r16) * M + 16 * mb + 4 * g) =
+            make_float4(accR[k][0], accR[k][1], accR[k][2], accR[k][3]);
+      } else if (g == 0) {
+        dZ0[(size_t)bh * D + 16 * db + r16] = accR[k][0] + accR[k][1];
+      }
     }
   }
 }
