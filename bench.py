@@ -67,6 +67,8 @@ def parse():
                              "small"],
                     help="measure this workload alone (default: the headline plus the nested records)")
     ap.add_argument("--no-nested", action="store_true", help="headline only")
+    ap.add_argument("--segment-chunks", type=int, default=0,
+                    help="force the segment length of every call (64-token chunks; 0 = the library's plan)")
     ap.add_argument("--profile-run", action="store_true",
                     help="run exactly warm-up + timed steps of one workload and nothing else (for rocprofv3: "
                          "launches per step = calls / (warm-up + steps))")
@@ -119,7 +121,7 @@ class Step:
     """One workload: inputs resident in HBM, outputs and workspaces preallocated, one callable per step.  The
     options of every call carry a KernelTimer when the dominant kernel is being timed."""
 
-    def __init__(self, wl, timed_kernel=None, pairs=8192, eager_decode=False):
+    def __init__(self, wl, timed_kernel=None, pairs=8192, eager_decode=False, segment_chunks=0):
         import torch
 
         from linear_rnn_layers_amd import binding, inputs
@@ -129,7 +131,9 @@ class Step:
         self.w = w = WORKLOADS(inputs)[wl]
         self.dt = dt = torch.float32 if w.dtype == inputs.F32 else torch.bfloat16
         self.timer = binding.KernelTimer(timed_kernel, pairs) if timed_kernel else None
-        self.opts = binding.options(timer=self.timer) if self.timer else None
+        self.opts = (binding.options(timer=self.timer, segment_chunks=segment_chunks)
+                     if self.timer or segment_chunks else None)
+        so = self.opts
         self.graphs = []
         if wl.startswith("decode"):
             self._init_decode(eager_decode)
@@ -154,14 +158,14 @@ class Step:
         self.dk = torch.empty((B, H, N, D), dtype=dt, device="cuda")
         self.dv = torch.empty((B, H, N, M), dtype=dt, device="cuda")
         Dk = w.features or D  # the attention's feature size
-        self.ck = torch.empty(binding.checkpoint_size(B, H, N, Dk, M) // 4, dtype=torch.float32, device="cuda")
+        self.ck = torch.empty(binding.checkpoint_size(B, H, N, Dk, M, so) // 4, dtype=torch.float32, device="cuda")
         fwd_op = binding.LA_OP_FWD_DECAY if wl == "long-decay" else binding.LA_OP_FWD_CAUSAL
         bwd_op = binding.LA_OP_BWD_DECAY if wl == "long-decay" else binding.LA_OP_BWD_CAUSAL
-        self.ws_f = binding.alloc_workspace(fwd_op, B, H, N, Dk, M, code, "cuda")
-        self.ws_b = binding.alloc_workspace(bwd_op, B, H, N, Dk, M, code, "cuda")
-        self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+        self.ws_f = binding.alloc_workspace(fwd_op, B, H, N, Dk, M, code, "cuda", so)
+        self.ws_b = binding.alloc_workspace(bwd_op, B, H, N, Dk, M, code, "cuda", so)
+        self.ws_n = binding.alloc_workspace(binding.LA_OP_FWD_NONCAUSAL, B, H, N, D, M, code, "cuda", so)
         if wl == "speech":
-            self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda")
+            self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda", so)
             self.s_tot = torch.empty((B, H, D, M), dtype=torch.float32, device="cuda")
             self.z_tot = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
         if wl == "mnist-rf":
@@ -842,7 +846,8 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     per_step = {"cifar": 16, "speech": 9}.get(wl, 1)  # launches of the dominant kernel per step
     graphs_planned = wl.startswith("decode") and not eager  # replays are timed with events around each graph
     timed = None if args.no_kernel_events or graphs_planned else dominant
-    step = Step(wl, timed, pairs=per_step * (steps + warmup) + 8, eager_decode=eager)
+    step = Step(wl, timed, pairs=per_step * (steps + warmup) + 8, eager_decode=eager,
+                segment_chunks=args.segment_chunks)
     w = step.w
     s = 4 if w.dtype == "f32" else 2
     graphs = bool(step.graphs)
@@ -925,6 +930,8 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
                    "mnist-rf": "random features of Q, K (C = 64) + causal forward and backward on them + chain rule",
                    "speech": "9 layers x (non-causal forward + backward)",
                    "small": "causal forward"}.get(wl, "one decode step of all B*H heads after the prefill")
+    if args.segment_chunks:
+        cfg["segment_tokens"] = 64 * args.segment_chunks  # forced, not the library's plan
     if wl.startswith("decode"):
         cfg["prefill_tokens"] = w.N
         cfg["launch"] = f"HIP graphs of {DECODE_GRAPH} steps" if graphs else "one host launch per step"
@@ -1002,7 +1009,7 @@ def main():
     steps = args.steps if args.steps is not None else ds
     warmup = args.warmup if args.warmup is not None else dw
     if args.profile_run:
-        step = Step(wl, None, eager_decode=args.eager_decode)
+        step = Step(wl, None, eager_decode=args.eager_decode, segment_chunks=args.segment_chunks)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if step.graphs:

@@ -234,6 +234,7 @@ class KernelTimer:
         if KernelTimer._hip is None:
             KernelTimer._hip = ctypes.CDLL("libamdhip64.so")
         hip = KernelTimer._hip
+        self._lib = hip  # kept on the instance: module globals may be gone when it is collected at exit
         self.kernel = kernel.encode()
         self.pairs = int(pairs)
         self.events = (ctypes.c_void_p * (2 * self.pairs))()
@@ -276,7 +277,7 @@ class KernelTimer:
         return total, n
 
     def __del__(self):
-        hip = KernelTimer._hip
+        hip = getattr(self, "_lib", None)
         if hip is None:
             return
         for e in range(2 * self.pairs):

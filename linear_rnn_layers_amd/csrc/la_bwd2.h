@@ -68,15 +68,24 @@ __device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, 
                                            const Planes<NPQ, CH, D>& qt, int w, int g, int r16) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NRT = (M / 16 + 1) * DB, NA = P::NDO < P::dR ? P::NDO : P::dR;
+  f32x4_t acc[NTR];
 #pragma unroll
-  for (int k = 0; k < NTR; ++k) {
-    const int t = w + 4 * k, mb = t / DB, db = t % DB;
-    if (t >= NRT) break;
+  for (int k = 0; k < NTR; ++k) acc[k] = accR[k];
 #pragma unroll
-    for (int s = 0; s < CH / 32; ++s)
-      mmaf<NA, P::dR>(accR[k], ot.template tfrag<NA>(32 * s, 16 * mb, g, r16),
-                      qt.template tfrag<P::dR>(32 * s, 16 * db, g, r16));
+  for (int s = 0; s < CH / 32; ++s) {
+    Frag<NA> oa[NTR];
+    Frag<P::dR> qb[NTR];
+#pragma unroll
+    for (int k = 0; k < NTR; ++k) {
+      const int t = w + 4 * k < NRT ? w + 4 * k : w;  // past the grid (uneven split): a harmless repeat
+      oa[k] = ot.template tfrag<NA>(32 * s, 16 * (t / DB), g, r16);
+      qb[k] = qt.template tfrag<P::dR>(32 * s, 16 * (t % DB), g, r16);
+    }
+    mmaf_tiles<NA, P::dR>(acc, oa, qb);
   }
+#pragma unroll
+  for (int k = 0; k < NTR; ++k)
+    if (w + 4 * k < NRT) accR[k] = acc[k];
 }
 
 // ===================================================================== B-A
@@ -165,57 +174,61 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
       // (V_j . dO_i) for j <= i as B operands under the accumulator map (pairs of 16-row blocks), and the
-      // mask [j <= i]
+      // mask [j <= i]; blocks after the wave's own stay zero.
+      f32x4_t bt[4];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        bt[jb] = zero4();
+        if (jb <= w) {
+#pragma unroll
+          for (int s = 0; s < M / 32; ++s)
+            mmaf<P::Bt, P::Bt>(bt[jb], vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
+        }
+      }
       Frag<P::U2> btf[2];
       Frag<1> onef[2];
 #pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = jb < w || (jb == w && 4 * g + r <= r16);  // j <= i
+          bt[jb][r] = keep ? bt[jb][r] : 0.f;
+        }
+      }
+#pragma unroll
       for (int p = 0; p < 2; ++p) {
-        if (2 * p <= w) {
-          f32x4_t bt[2];
+        btf[p] = acc2frag<P::U2>(bt[2 * p], bt[2 * p + 1]);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int jb = 2 * p + h;
-            f32x4_t a = zero4();
-            if (jb <= w) {
-#pragma unroll
-              for (int s = 0; s < M / 32; ++s)
-                mmaf<P::Bt, P::Bt>(a, vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
-              if (jb == w) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (4 * g + r > r16) a[r] = 0.f;  // j > i
-              }
-            }
-            bt[h] = a;
-          }
-          btf[p] = acc2frag<P::U2>(bt[0], bt[1]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-            onef[p].p[0][e] = j <= il ? (__bf16)1.0f : (__bf16)0.0f;
-          }
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+          onef[p].p[0][e] = j <= il ? (__bf16)1.0f : (__bf16)0.0f;
         }
       }
       f32x4_t U[DB], ZC[DB];
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) U[d0] = ZC[d0] = zero4();
       constexpr int NKA = cmax(P::U2, P::Zc);
 #pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t u = zero4(), zc = zero4();
+      for (int s = 0; s < M / 32; ++s) {
+        Frag<P::U1_a> sa[DB];
 #pragma unroll
-        for (int s = 0; s < M / 32; ++s)
-          mmaf<P::U1_a, P::U1_b>(u, sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g), dof[s]);
+        for (int d0 = 0; d0 < DB; ++d0) sa[d0] = sp.template frag<P::U1_a>(16 * d0 + r16, 32 * s, g);
+        mmaf_tiles<P::U1_a, P::U1_b>(U, sa, dof[s]);
+      }
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          if (2 * p <= w) {
-            const Frag<NKA> kfa = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
-            mmaf<P::U2, P::U2>(u, kfa, btf[p]);
-            mmaf<P::Zc, 1>(zc, kfa, onef[p]);
-          }
+      for (int p = 0; p < 2; ++p) {
+        if (2 * p <= w) {
+          Frag<NKA> kfa[DB];
+#pragma unroll
+          for (int d0 = 0; d0 < DB; ++d0) kfa[d0] = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
+          mmaf_tiles<P::U2, P::U2>(U, kfa, btf[p]);
+          mmaf_tiles<P::Zc, 1>(ZC, kfa, onef[p]);
         }
+      }
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) {
         const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
-        zc += f32x4_t{z4.x, z4.y, z4.z, z4.w};
-        U[d0] = u;    // S_i dO_i   [d][i]
-        ZC[d0] = zc;  // Z_i        [d][i]
+        ZC[d0] += f32x4_t{z4.x, z4.y, z4.z, z4.w};  // U: S_i dO_i [d][i], ZC: Z_i [d][i]
       }
       float pu = 0.f, pz = 0.f;
       float qv[DB][4];
@@ -255,10 +268,14 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
     constexpr int NKB = cmax(P::dS_b, P::Zc);
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
+      Frag<P::dS_a> va[NTS];
+      Frag<NKB> kb[NTS];
 #pragma unroll
-      for (int k = 0; k < NTS; ++k)
-        mmaf<P::dS_a, P::dS_b>(accS[k], vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16),
-                               kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16));
+      for (int k = 0; k < NTS; ++k) {
+        va[k] = vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16);
+        kb[k] = kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16);
+      }
+      mmaf_tiles<P::dS_a, P::dS_b>(accS, va, kb);
       if (zw) {
         f32x4_t dz = zero4();
         mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * w, g, r16));
@@ -416,76 +433,97 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
       Frag<NVT> vfr[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) vfr[s] = vt.template frag<NVT>(jl, 32 * s, g);
-      // A'_ij = q'_i . phi(K_j) and W'_ij = dO_i . V_j - O_i . dO_i for i >= j (rows i, columns j), in pairs of
-      // 16-row blocks as B operands under the accumulator map
+      // A'_ij = q'_i . phi(K_j) and W'_ij = dO_i . V_j - O_i . dO_i (rows i, columns j), zero where i < j (whole
+      // blocks before this wave's, and the upper triangle of its own), in pairs of 16-row blocks as B operands
+      // under the accumulator map.
+      f32x4_t at[4], wt[4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        at[ib] = wt[ib] = zero4();
+        if (ib >= w) {
+#pragma unroll
+          for (int s = 0; s < D / 32; ++s)
+            mmaf<P::At, P::At>(at[ib], qt.template frag<P::At>(16 * ib + r16, 32 * s, g), kfr[s]);
+#pragma unroll
+          for (int s = 0; s < M / 32; ++s)
+            mmaf<P::Wt, P::Wt>(wt[ib], ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
+        const float odr[4] = {od.x, od.y, od.z, od.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = ib > w || (ib == w && 4 * g + r >= r16);  // i >= j
+          at[ib][r] = keep ? at[ib][r] : 0.f;
+          wt[ib][r] = keep ? wt[ib][r] - odr[r] : 0.f;
+        }
+      }
       Frag<P::dK> wfr[2];
       Frag<P::dV> afr[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
+        wfr[p] = acc2frag<P::dK>(wt[2 * p], wt[2 * p + 1]);
+        afr[p] = acc2frag<P::dV>(at[2 * p], at[2 * p + 1]);
+      }
+      // dK_j = (R V_j + r + sum_{i>=j} q'_i W'_ij) phi'(K_j), the feature blocks' tiles together
+      f32x4_t aK[DB];
+#pragma unroll
+      for (int d0 = 0; d0 < DB; ++d0) aK[d0] = zero4();
+#pragma unroll
+      for (int s = 0; s < M / 32; ++s) {
+        Frag<P::KR_a> ra[DB];
+#pragma unroll
+        for (int d0 = 0; d0 < DB; ++d0) ra[d0] = rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g);
+        mmaf_tiles<P::KR_a, P::KR_b>(aK, ra, vfr[s]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
         if (2 * p + 1 >= w) {
-          f32x4_t at[2], wt[2];
+          Frag<P::dK> qa[DB];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int ib = 2 * p + h;
-            f32x4_t a = zero4(), b = zero4();
-            if (ib >= w) {
-#pragma unroll
-              for (int s = 0; s < D / 32; ++s)
-                mmaf<P::At, P::At>(a, qt.template frag<P::At>(16 * ib + r16, 32 * s, g), kfr[s]);
-#pragma unroll
-              for (int s = 0; s < M / 32; ++s)
-                mmaf<P::Wt, P::Wt>(b, ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
-              const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
-              const float odr[4] = {od.x, od.y, od.z, od.w};
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                b[r] -= odr[r];
-                if (ib == w && 4 * g + r < r16) {  // i < j
-                  a[r] = 0.f;
-                  b[r] = 0.f;
-                }
-              }
-            }
-            at[h] = a;
-            wt[h] = b;
-          }
-          wfr[p] = acc2frag<P::dK>(wt[0], wt[1]);
-          afr[p] = acc2frag<P::dV>(at[0], at[1]);
+          for (int d0 = 0; d0 < DB; ++d0) qa[d0] = qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16);
+          mmaf_tiles<P::dK, P::dK>(aK, qa, wfr[p]);
         }
       }
-      // dK_j = (R V_j + r + sum_{i>=j} q'_i W'_ij) phi'(K_j)
+      if (row_ok) {
 #pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        f32x4_t a = zero4();
-#pragma unroll
-        for (int s = 0; s < M / 32; ++s)
-          mmaf<P::KR_a, P::KR_b>(a, rp.template frag<P::KR_a>(16 * d0 + r16, 32 * s, g), vfr[s]);
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          if (2 * p + 1 >= w) mmaf<P::dK, P::dK>(a, qt.template tfrag_acc<P::dK>(32 * p, 16 * d0, g, r16), wfr[p]);
-        if (row_ok) {
+        for (int d0 = 0; d0 < DB; ++d0) {
           float o[4], kv[4];
           kt.get4(jl, 16 * d0 + 4 * g, kv);
           const float4 r4 = *reinterpret_cast<const float4*>(&sr[16 * d0 + 4 * g]);
           const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (a[r] + rr[r]) * dfeat(kv[r], fm);
+          for (int r = 0; r < 4; ++r) o[r] = (aK[d0][r] + rr[r]) * dfeat(kv[r], fm);
           IO<T>::store4(dK + offD + (size_t)(c0 + jl) * D + 16 * d0 + 4 * g, o);
         }
       }
-      // dV_j = R^T phi(K_j) + sum_{i>=j} dO_i A'_ij
+      // dV_j = R^T phi(K_j) + sum_{i>=j} dO_i A'_ij, the value blocks' tiles together
       constexpr int NA = P::NDO < P::dV ? P::NDO : P::dV;
+      f32x4_t aV[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        f32x4_t a = zero4();
+      for (int mb = 0; mb < MB; ++mb) aV[mb] = zero4();
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-          mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
+      for (int s = 0; s < D / 32; ++s) {
+        Frag<P::VR> ra[MB];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-          if (2 * p + 1 >= w) mmaf<NA, P::dV>(a, ot.template tfrag_acc<NA>(32 * p, 16 * mb, g, r16), afr[p]);
-        if (row_ok) {
-          float o[4] = {a[0], a[1], a[2], a[3]};
+        for (int mb = 0; mb < MB; ++mb) ra[mb] = rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16);
+        mmaf_tiles<P::VR, P::VR>(aV, ra, kfr[s]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (2 * p + 1 >= w) {
+          Frag<NA> oa[MB];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) oa[mb] = ot.template tfrag_acc<NA>(32 * p, 16 * mb, g, r16);
+          mmaf_tiles<NA, P::dV>(aV, oa, afr[p]);
+        }
+      }
+      if (row_ok) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          float o[4] = {aV[mb][0], aV[mb][1], aV[mb][2], aV[mb][3]};
           IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
         }
       }

@@ -151,6 +151,61 @@ __device__ __forceinline__ void mmaf(f32x4_t& acc, const Frag<FA>& a, const Frag
   }
 }
 
+// The same product for NTL tiles at once, acc[t] += A[t] B (one B) or
+// acc[t] += A B[t] (one A), issued term by term across the tiles: consecutive
+// MFMAs then write different accumulators, so the matrix core does not wait
+// for one tile's result before the next instruction (a product of one tile
+// alone is a chain of dependent accumulations).
+template <int NA, int NB, int NTL, int FA, int FB>
+__device__ __forceinline__ void mmaf_tiles(f32x4_t (&acc)[NTL], const Frag<FA> (&a)[NTL], const Frag<FB>& b) {
+  static_assert(NA <= FA && NB <= FB, "operand has fewer planes than the product uses");
+  constexpr int ORD = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = ORD - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i <= s; ++i) {
+      const int j = s - i;
+      if (i < NA && j < NB) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) acc[t] = mfma_bf16(a[t].p[i], b.p[j], acc[t]);
+      }
+    }
+  }
+}
+template <int NA, int NB, int NTL, int FA, int FB>
+__device__ __forceinline__ void mmaf_tiles(f32x4_t (&acc)[NTL], const Frag<FA>& a, const Frag<FB> (&b)[NTL]) {
+  static_assert(NA <= FA && NB <= FB, "operand has fewer planes than the product uses");
+  constexpr int ORD = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = ORD - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i <= s; ++i) {
+      const int j = s - i;
+      if (i < NA && j < NB) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) acc[t] = mfma_bf16(a.p[i], b[t].p[j], acc[t]);
+      }
+    }
+  }
+}
+
+template <int NA, int NB, int NTL, int FA, int FB>
+__device__ __forceinline__ void mmaf_tiles(f32x4_t (&acc)[NTL], const Frag<FA> (&a)[NTL], const Frag<FB> (&b)[NTL]) {
+  static_assert(NA <= FA && NB <= FB, "operand has fewer planes than the product uses");
+  constexpr int ORD = NA > NB ? NA : NB;
+#pragma unroll
+  for (int s = ORD - 1; s >= 0; --s) {
+#pragma unroll
+    for (int i = 0; i <= s; ++i) {
+      const int j = s - i;
+      if (i < NA && j < NB) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) acc[t] = mfma_bf16(a[t].p[i], b[t].p[j], acc[t]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ transposed read
 __device__ __forceinline__ bf16x4_t lds_read_tr4(const bf16_t* p) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;

@@ -5,9 +5,9 @@ Gate: rowerr <= 1e-4 (float32 storage) / 2e-2 (bf16), each step checked at its o
 the features the library produced, the chain rule through the map on the feature gradients it produced), and
 end to end against a chain of oracle steps only (the oracle's features, rounded to the storage type as the
 library stores them, its attention and its chain rule), also through autograd.  The chain rule of a feature map
-is a signed sum over the features, so an error within the gate in each feature gradient reaches dX as at most the
-gate times the size of the summed terms, sum_c |d phi_c / dx| |dPhi_c|: the end-to-end rows are judged against
-that size (the propagated per-step gate).  The feature gradients dPhi_Q are floored at 1e-2 of the
+is a signed sum over the features, so an error within the gate in each feature gradient (at most the gate times
+the row's largest |dPhi_c|) reaches dX as at most the gate times sum_c |d phi_c / dx| max_c' |dPhi_c'|: the
+end-to-end rows are judged against that size (the propagated per-step gate).  The feature gradients dPhi_Q are floored at 1e-2 of the
 numerator term |S_i g_i| (the cancellation of the quotient rule, as for dQ of the plain method); the raw
 query gradient of the composition at 1e-2 of that term carried through the same map.
 """
@@ -206,8 +206,11 @@ def test_feature_mode_attention(which, causal, dtype):
         ofq_g, ofk_g, ov = oracle.backward_noncausal(ofq, ofk, v, do, feature=IDENT)
     ou = feat_cancel_scale(ofq, ofk, v, do, causal)
     # each feature gradient's own floor (1e-2 of the numerator term its denominator share cancels) carried along
-    fq_abs = np.abs(ofq_g) + CANCEL_FLOOR * np.abs(ou).max(-1, keepdims=True)
-    fk_abs = np.abs(ofk_g)
+    # (the per-step gate bounds each element's error by the row's largest magnitude, so that is what every
+    # feature's term carries)
+    fq_abs = np.abs(ofq_g).max(-1, keepdims=True) + CANCEL_FLOOR * np.abs(ou).max(-1, keepdims=True)
+    fq_abs = np.broadcast_to(fq_abs, ofq_g.shape)
+    fk_abs = np.broadcast_to(np.abs(ofk_g).max(-1, keepdims=True), ofk_g.shape)
     if causal:
         fk_abs = fk_abs + CANCEL_FLOOR * feat_key_cancel_terms(ofq, ofk, v, do).max(-1, keepdims=True)
     chain = {"O": rowerr(host(o), oo), "dV": rowerr(host(dv), ov),
@@ -252,8 +255,11 @@ def test_mnist_random_features_workload():
     # and the cancellation passes the difference on at the scale of the cancelled term
     eps = max(rowerr(fq, ofq), rowerr(fk, ofk)) / 1e-4
     fac = max(CANCEL_FLOOR, eps)
-    gq_abs = np.abs(gq) + fac * np.abs(ou).max(-1, keepdims=True)
-    gk_abs = np.abs(gk) + fac * feat_key_cancel_terms(ofq, ofk, v, do).max(-1, keepdims=True)
+    # (the per-step gate bounds each element's error by the row's largest magnitude, so that is what every
+    # feature's term carries)
+    rowmax = lambda a: np.broadcast_to(np.abs(a).max(-1, keepdims=True), a.shape)  # noqa: E731
+    gq_abs = rowmax(gq) + fac * np.abs(ou).max(-1, keepdims=True)
+    gk_abs = rowmax(gk) + fac * feat_key_cancel_terms(ofq, ofk, v, do).max(-1, keepdims=True)
     chain = {"O": rowerr(host(o), oo), "dV": rowerr(host(dv), gv),
              "dQ": rowerr(host(dq), oracle.feature_performer_vjp(q, wp, gq), row_floor=rf_vjp_terms(q, wp, gq_abs)),
              "dK": rowerr(host(dk), oracle.feature_performer_vjp(k, wp, gk), row_floor=rf_vjp_terms(k, wp, gk_abs))}
