@@ -21,7 +21,20 @@
  *  - Heads are independent; B*H is a batch axis (Transformer Family v2,
  *    multi-head attention).
  *  - Supported sizes: B, H >= 1; N >= 0 (N = 0 is a no-op returning LA_OK);
- *    D, M in {32, 64}.  Every pointer must be 16-byte aligned.
+ *    D, M in {32, 64}, or wide feature vectors (below) of D = 64 ns features
+ *    up to 4096.  Every pointer must be 16-byte aligned.
+ *  - Wide feature vectors ("Linear Attention/zh", feature maps: the degree-2
+ *    polynomial map, whose feature count is about the square of the head
+ *    size, or a few hundred positive random features; "Transformers are RNNs
+ *    -- part 2/3", section 3.2.1): D > 64, a multiple of 64, with feature =
+ *    LA_FEATURE_IDENTITY and no decay, in la_forward_causal,
+ *    la_backward_causal, la_forward_noncausal and la_decode_step (not
+ *    la_backward_noncausal).  Q, K, dQ, dK are then stored feature-sliced:
+ *    [B, H, D/64, N, 64], slice s holding features 64 s .. 64 s + 63 of every
+ *    token (the layout la_feature_random and la_feature_poly2 write for C >
+ *    64).  S [B, H, D, M], Z [B, H, D] and decode's q, k [B, H, D] keep their
+ *    layouts.  Sums over all D features (O's numerator and denominator, dV)
+ *    are formed per slice and added in a fixed order.
  *  - Outputs must not overlap inputs (decode's S and Z are updated in place
  *    by design).  Overlaps are rejected with LA_ERR_ALIAS.
  *  - Scratch memory is the caller's `ws` of `ws_bytes` bytes, at least
@@ -171,7 +184,10 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype,
  * O(N * D * M / segment) per head, well inside the pages' linear-memory
  * bound; no per-token state S_i is ever stored ("Transformers are RNNs --
  * part 2/3", section 3.3.1).  The decayed recurrence (logA given) uses
- * longer segments and at most this many bytes. */
+ * longer segments and at most this many bytes.  For wide feature vectors
+ * (D > 64) the states are those of the D/64 feature slices of every head,
+ * followed by float32 O and den of every token (what the backward needs of
+ * the whole head: each slice sees only its share of the denominator). */
 size_t la_checkpoint_size(int B, int H, int N, int D, int M,
                           const la_options *opts);
 
@@ -219,7 +235,8 @@ int la_forward_wait_status(const void *ws, size_t ws_bytes, int B, int H,
  *               aggregates, their prefix states, and (one-launch form, see
  *               la_form) one 32-bit flag per segment plus the status word,
  *               cleared by the call itself, so any contents are
- *               accepted.  In the one-launch form the workgroups of a call
+ *               accepted.  Wide feature vectors always take two launches
+ *               (and a third that sums the slices' shares, kept in `ws`).  In the one-launch form the workgroups of a call
  *               exchange segment aggregates through `ws`: calls that overlap
  *               on one workspace race, as with any scratch buffer.
  */
@@ -323,7 +340,7 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
  *   dphi(Q_i) = S g_i + c_i Z,  dphi(K_j) = R V_j + r,  dV_j = R^T phi(K_j).
  * den_i and dO_i . O_i are recomputed from S, Z, so neither O nor den is an
  * input.  Linear time, O(D M) state per head.
- *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype`.
+ *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype`; D in {32, 64}.
  *   S_tot, Z_tot optional: the totals written by la_forward_noncausal for the
  *               same Q, K, V (both or neither); NULL: formed here again.
  *   dQ, dK, dV  outputs in `dtype`.
@@ -345,7 +362,8 @@ int la_backward_noncausal(const void *Q, const void *K, const void *V,
  *               la_forward_causal): S = a S + phi(k) v^T, Z = a Z + phi(k).
  *   q, k [B,H,D], v [B,H,M], y [B,H,M] in `dtype`; S [B,H,D,M] and Z [B,H,D]
  *   float32, updated in place (the update comes first: masking is
- *   inclusive).  Calls on one stream are ordered; overlapping calls on
+ *   inclusive).  Wide feature vectors (D > 64): one workgroup per head
+ *   streams its state; no logA.  Calls on one stream are ordered; overlapping calls on
  *   different streams that share S/Z race.
  */
 int la_decode_step(const void *q, const void *k, const void *v,
@@ -361,15 +379,17 @@ int la_decode_step(const void *q, const void *k, const void *v,
  * without bias when the rows of W are standard normal.  Feed Phi of queries
  * and keys to the attention entry points with LA_FEATURE_IDENTITY.
  *   X    [B,H,N,Din] in `dtype`; W [H,C,Din] float32 (the random projection,
- *        owned by the caller); Phi [B,H,N,C] output in `dtype`.
- *   Din, C in {32, 64}.  Same validation and error behaviour as the
- *   attention entry points; asynchronous on `stream`.
+ *        owned by the caller); Phi output in `dtype`: [B,H,N,C] for C <= 64,
+ *        feature-sliced [B,H,C/64,N,64] for wider maps.
+ *   Din in {32, 64}; C in {32, 64} or a multiple of 64 up to 4096.  Same
+ *   validation and error behaviour as the attention entry points;
+ *   asynchronous on `stream`.
  */
 int la_feature_random(const void *X, const float *W, void *Phi, int B, int H,
                       int N, int Din, int C, int dtype, void *stream);
 
 /* Vector-Jacobian product of la_feature_random: dX = sum_c dPhi_c phi_c
- * (W_c - x), with phi recomputed in float32.  dPhi [B,H,N,C], dX
+ * (W_c - x), with phi recomputed in float32.  dPhi in the layout of Phi, dX
  * [B,H,N,Din] in `dtype`. */
 int la_feature_random_vjp(const void *X, const float *W, const void *dPhi,
                           void *dX, int B, int H, int N, int Din, int C,
@@ -380,8 +400,10 @@ int la_feature_random_vjp(const void *X, const float *W, const void *dPhi,
  * phi(x) = (1, x, x (x) x) truncated; "Transformers are RNNs -- part 2/3",
  * section 3.2.1): Phi = (1, x_1 .. x_Din, x_a x_b for a, b = 1..Din
  * a-major, then zeros up to C), so phi(x) . phi(y) = 1 + x.y + (x.y)^2 > 0.
- *   X [B,H,N,Din], Phi [B,H,N,C] in `dtype`; C in {32, 64} with
- *   1 + Din + Din^2 <= C (Din <= 5 for C = 32, <= 7 for C = 64).
+ *   X [B,H,N,Din], Phi in `dtype` ([B,H,N,C] for C <= 64, feature-sliced
+ *   [B,H,C/64,N,64] for wider maps); C in {32, 64} or a multiple of 64 up
+ *   to 4096, with 1 <= Din <= 64 and 1 + Din + Din^2 <= C (Din <= 5 for C =
+ *   32, <= 7 for C = 64, C = 1088 for Din = 32).
  */
 int la_feature_poly2(const void *X, void *Phi, int B, int H, int N, int Din,
                      int C, int dtype, void *stream);

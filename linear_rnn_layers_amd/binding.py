@@ -164,13 +164,42 @@ def _expect(name, t, shape, dtype):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def feature_shape(B, H, N, C):
+    """Shape of C-wide feature vectors: [B,H,N,C] up to 64 features, else feature-sliced [B,H,C/64,N,64] (slice s
+    holds features 64s..64s+63 of every token), the layout the library's wide kernels read and write."""
+    return (B, H, N, C) if C <= 64 else (B, H, C // 64, N, 64)
+
+
+def to_sliced(x):
+    """[B,H,N,C] -> feature-sliced [B,H,C/64,N,64] (a copy; C a multiple of 64)."""
+    B, H, N, C = x.shape
+    if C % 64:
+        raise ValueError("the feature-sliced layout needs C to be a multiple of 64")
+    return x.reshape(B, H, N, C // 64, 64).permute(0, 1, 3, 2, 4).contiguous()
+
+
+def from_sliced(x):
+    """Feature-sliced [B,H,ns,N,64] -> [B,H,N,ns*64] (a copy)."""
+    B, H, ns, N, c = x.shape
+    return x.permute(0, 1, 3, 2, 4).reshape(B, H, N, ns * c).contiguous()
+
+
 def _sizes(q, k, v):
-    """(B, H, N, D, M) from Q [B,H,N,D], K like Q, V [B,H,N,M] of Q's dtype."""
+    """(B, H, N, D, M) from Q [B,H,N,D] (or feature-sliced [B,H,D/64,N,64] for D > 64), K like Q, V [B,H,N,M] of
+    Q's dtype."""
     if not all(isinstance(t, torch.Tensor) for t in (q, k, v)):
         raise TypeError("Q, K and V must be torch tensors")
-    if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("expected Q/K [B,H,N,D] and V [B,H,N,M]")
-    B, H, N, D = q.shape
+    if q.dim() == 5 and v.dim() == 4:
+        B, H, ns, N, c = q.shape
+        if c != 64 or ns < 2:
+            raise ValueError("feature-sliced Q/K must be [B,H,D/64,N,64] with D/64 >= 2")
+        D = ns * 64
+    elif q.dim() == 4 and v.dim() == 4:
+        B, H, N, D = q.shape
+        if D > 64:
+            raise ValueError("Q/K wider than 64 features must be feature-sliced: [B,H,D/64,N,64] (see to_sliced)")
+    else:
+        raise ValueError("expected Q/K [B,H,N,D] (or [B,H,D/64,N,64]) and V [B,H,N,M]")
     M = v.shape[-1]
     dtype_code(q.dtype)
     _expect("K", k, q.shape, q.dtype)
@@ -335,8 +364,9 @@ def la_forward_noncausal(Q, K, V, O, ws=None, stream=None, feature=0, S_out=None
 def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=None, dS_N=None, dZ_N=None,
                        dS0=None, dZ0=None, ws=None, stream=None, logA=None, dlogA=None, feature=0, opts=None):
     B, H, N, D, M = _sizes(Q, K, V)
-    for name, t, last in (("O", O, M), ("dO", dO, M), ("dQ", dQ, D), ("dK", dK, D), ("dV", dV, M)):
-        _expect(name, t, (B, H, N, last), Q.dtype)
+    for name, t, shape in (("O", O, (B, H, N, M)), ("dO", dO, (B, H, N, M)), ("dQ", dQ, feature_shape(B, H, N, D)),
+                           ("dK", dK, feature_shape(B, H, N, D)), ("dV", dV, (B, H, N, M))):
+        _expect(name, t, shape, Q.dtype)
     _expect("den", den, (B, H, N), torch.float32)
     _expect("logA", logA, (B, H, N), torch.float32)
     _expect("dlogA", dlogA, (B, H, N), torch.float32)
@@ -356,8 +386,9 @@ def la_backward_causal(Q, K, V, O, den, dO, dQ, dK, dV, S0=None, Z0=None, ckpt=N
 def la_backward_noncausal(Q, K, V, dO, dQ, dK, dV, ws=None, stream=None, feature=0, S_tot=None, Z_tot=None,
                           opts=None):
     B, H, N, D, M = _sizes(Q, K, V)
-    for name, t, last in (("dO", dO, M), ("dQ", dQ, D), ("dK", dK, D), ("dV", dV, M)):
-        _expect(name, t, (B, H, N, last), Q.dtype)
+    for name, t, shape in (("dO", dO, (B, H, N, M)), ("dQ", dQ, feature_shape(B, H, N, D)),
+                           ("dK", dK, feature_shape(B, H, N, D)), ("dV", dV, (B, H, N, M))):
+        _expect(name, t, shape, Q.dtype)
     _expect_state(("S_tot", "Z_tot"), S_tot, Z_tot, B, H, D, M)
     _expect_ws(ws)
     nb = ws.numel() if ws is not None else 0
@@ -542,7 +573,7 @@ def feature_random(x, w):
     B, H, N, Din = _check_x(x)
     C = w.shape[1] if w.dim() == 3 else -1
     _expect("W", w, (H, C, Din), torch.float32)
-    phi = torch.empty((B, H, N, C), dtype=x.dtype, device=x.device)
+    phi = torch.empty(feature_shape(B, H, N, C), dtype=x.dtype, device=x.device)
     _check(load().la_feature_random(_ptr(x), _ptr(w), _ptr(phi), B, H, N, Din, C, dtype_code(x.dtype),
                                     _stream(None)), "la_feature_random")
     return phi
@@ -552,7 +583,7 @@ def feature_random_vjp(x, w, dphi):
     B, H, N, Din = _check_x(x)
     C = w.shape[1] if w.dim() == 3 else -1
     _expect("W", w, (H, C, Din), torch.float32)
-    _expect("dPhi", dphi, (B, H, N, C), x.dtype)
+    _expect("dPhi", dphi, feature_shape(B, H, N, C), x.dtype)
     dx = torch.empty_like(x)
     _check(load().la_feature_random_vjp(_ptr(x), _ptr(w), _ptr(dphi), _ptr(dx), B, H, N, Din, C,
                                         dtype_code(x.dtype), _stream(None)), "la_feature_random_vjp")
@@ -562,7 +593,7 @@ def feature_random_vjp(x, w, dphi):
 def feature_poly2(x, C):
     """Degree-2 polynomial features (1, x, x_a x_b, zeros) of size C in x's dtype."""
     B, H, N, Din = _check_x(x)
-    phi = torch.empty((B, H, N, C), dtype=x.dtype, device=x.device)
+    phi = torch.empty(feature_shape(B, H, N, C), dtype=x.dtype, device=x.device)
     _check(load().la_feature_poly2(_ptr(x), _ptr(phi), B, H, N, Din, C, dtype_code(x.dtype), _stream(None)),
            "la_feature_poly2")
     return phi
@@ -570,11 +601,15 @@ def feature_poly2(x, C):
 
 def feature_poly2_vjp(x, dphi):
     B, H, N, Din = _check_x(x)
-    if dphi.dim() != 4:
-        raise ValueError("expected dPhi [B,H,N,C]")
-    _expect("dPhi", dphi, (B, H, N, dphi.shape[-1]), x.dtype)
+    if dphi.dim() == 5:
+        C = dphi.shape[2] * dphi.shape[4]
+    elif dphi.dim() == 4:
+        C = dphi.shape[-1]
+    else:
+        raise ValueError("expected dPhi [B,H,N,C] (or [B,H,C/64,N,64])")
+    _expect("dPhi", dphi, feature_shape(B, H, N, C), x.dtype)
     dx = torch.empty_like(x)
-    _check(load().la_feature_poly2_vjp(_ptr(x), _ptr(dphi), _ptr(dx), B, H, N, Din, dphi.shape[-1],
+    _check(load().la_feature_poly2_vjp(_ptr(x), _ptr(dphi), _ptr(dx), B, H, N, Din, C,
                                        dtype_code(x.dtype), _stream(None)), "la_feature_poly2_vjp")
     return dx
 

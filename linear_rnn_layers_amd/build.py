@@ -15,7 +15,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "la_api.hip")
-HEADERS = [os.path.join(PKG, "csrc", h) for h in ("la_device.h", "la_kernels.h", "la_decay.h", "la_feature.h")] + [
+HEADERS = [os.path.join(PKG, "csrc", h) for h in ("la_device.h", "la_kernels.h", "la_decay.h", "la_feature.h", "la_bwd2.h", "la_wide.h")] + [
     os.path.join(ROOT, "include", "la.h")]
 LIB = os.path.join(PKG, "liblinattn.so")
 ARCH = "gfx950"

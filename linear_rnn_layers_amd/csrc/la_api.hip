@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <functional>
 #include <cstdint>
@@ -21,7 +22,7 @@
 #include "../../include/la.h"
 #include "la_decay.h"
 #include "la_bwd2.h"
-#include "la_feature.h"
+#include "la_wide.h"
 
 // la_forward_causal_noalloc takes the workspace of the causal forward from
 // this file-scope array instead of from the caller: for callers that cannot
@@ -54,11 +55,14 @@ int fail(int status, const std::string& msg) {
 // of kb consecutive segments (chosen at launch from its occupancy).  The
 // segment plan depends on the sizes only.
 struct Plan {
-  long BH = 0;
+  long BH = 0;  // heads the segment kernels see: B*H, or B*H*ns feature slices of a wide head
   long N = 0;
   int L = 0;
   int nseg = 0;
-  int SV = 0;  // floats per state vector: D*M + D
+  int SV = 0;  // floats per state vector: D*M + D (D = 64 for a slice)
+  int M = 0;
+  int ns = 1;  // feature slices per value head (wide feature vectors), else 1
+  long BHv() const { return BH / ns; }
 };
 
 constexpr long kFineTarget = 1024;  // workgroups of the segment-parallel kernels: finer plan
@@ -89,6 +93,7 @@ Plan make_plan(int B, int H, int N, int D, int M, long target, int forced) {
   p.BH = (long)B * H;
   p.N = N;
   p.SV = D * M + D;
+  p.M = M;
   const long nchunks = ((long)N + la::CH - 1) / la::CH;
   if (target <= 0) target = causal_target(nchunks, D, M);
   if (N <= 0) {
@@ -103,6 +108,17 @@ Plan make_plan(int B, int H, int N, int D, int M, long target, int forced) {
   if (forced > 0) cps = forced < nchunks ? forced : nchunks;
   p.L = (int)(cps * la::CH);
   p.nseg = (int)(((long)N + p.L - 1) / p.L);
+  return p;
+}
+
+// Wide feature vectors (D > 64, a multiple of 64): the plan of the D / 64
+// feature slices of every head, each a 64-feature head of its own.
+bool is_wide(int D) { return D > 64; }
+
+Plan plan_for(int B, int H, int N, int D, int M, long target, int forced) {
+  if (!is_wide(D)) return make_plan(B, H, N, D, M, target, forced);
+  Plan p = make_plan(B, H * (D / 64), N, 64, M, target, forced);
+  p.ns = D / 64;
   return p;
 }
 
@@ -134,8 +150,15 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 // Workspace regions (bytes) per operation.
 struct WsLayout {
   size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0, xseg = 0, sync = 0;
-  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg + sync; }
+  size_t pn = 0, pd = 0, o32 = 0;  // wide feature vectors: the slices' shares, float32 O and den
+  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg + sync + pn + pd + o32; }
 };
+
+// Wide feature vectors: per slice head, the share of the numerators
+// ([N][M]) and of the denominators ([N]); per value head, float32 O and den.
+size_t wide_pn(const Plan& p) { return align256((size_t)p.BH * p.N * p.M * sizeof(float)); }
+size_t wide_pd(const Plan& p) { return align256((size_t)p.BH * p.N * sizeof(float)); }
+size_t wide_o32(const Plan& p) { return align256((size_t)p.BHv() * p.N * (p.M + 1) * sizeof(float)); }
 
 // fwd causal: aggregates and prefix states when there is more than one
 //   segment (the prefix states go to the caller's checkpoint when given and
@@ -147,26 +170,43 @@ struct WsLayout {
 //   reverse aggregates (scanned in place) when there is more than one
 //   segment, and the per-token pair (1/den, O.dO) passed from the query
 //   pass to the key pass.
+// Wide feature vectors add the slices' shares of the forward's numerators and
+// denominators (and, in the backward, of dV, in the same space), and in the
+// backward float32 O and den when the checkpoint has to be recomputed.
 WsLayout ws_layout(int op, const Plan& p) {
   WsLayout w;
   if (p.nseg == 0) return w;
+  const bool wide = p.ns > 1;
   switch (op) {
     case LA_OP_FWD_CAUSAL:
       if (p.nseg > 1) {
         w.agg = state_bytes(p, p.nseg);
         w.ckpt = state_bytes(p, p.nseg + 1);
-        w.sync = align256((size_t)(1 + p.BH * p.nseg) * sizeof(unsigned));
+        if (!wide) w.sync = align256((size_t)(1 + p.BH * p.nseg) * sizeof(unsigned));
+      }
+      if (wide) {
+        w.pn = wide_pn(p);
+        w.pd = wide_pd(p);
       }
       break;
     case LA_OP_FWD_NONCAUSAL:
       w.agg = state_bytes(p, p.nseg);
       w.ckpt = state_bytes(p, p.nseg + 1);
+      if (wide) {
+        w.pn = wide_pn(p);
+        w.pd = wide_pd(p);
+      }
       break;
     case LA_OP_BWD_CAUSAL:
       w.agg = state_bytes(p, p.nseg);       // checkpoint recomputation only
       w.ckpt = state_bytes(p, p.nseg + 1);  // checkpoint recomputation only
       if (p.nseg > 1) w.ragg = state_bytes(p, p.nseg);
-      w.gc = align256((size_t)p.BH * p.N * 2 * sizeof(float));  // (1/den, O.dO) per token
+      w.gc = align256((size_t)p.BHv() * p.N * 2 * sizeof(float));  // (1/den, O.dO) per token
+      if (wide) {
+        w.pn = wide_pn(p);    // dV shares (and the numerators' when recomputing)
+        w.pd = wide_pd(p);    // checkpoint recomputation only
+        w.o32 = wide_o32(p);  // checkpoint recomputation only
+      }
       break;
     case LA_OP_BWD_NONCAUSAL:  // key aggregates and their scan; reverse aggregates and their scan
       w.agg = state_bytes(p, p.nseg);
@@ -198,13 +238,26 @@ WsLayout ws_layout(int op, const Plan& p) {
 
 // -------------------------------------------------------------- validation
 bool dims_ok(int D, int M) { return (D == 32 || D == 64) && (M == 32 || M == 64); }
+bool wide_ok(int C) { return C > 64 && C <= la::kWideMax && C % 64 == 0; }
 
 int check_sizes(int B, int H, int N, int D, int M, int dtype) {
   if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_DTYPE, "dtype must be LA_F32 (0) or LA_BF16 (1)");
   if (B < 1 || H < 1 || N < 0) return fail(LA_ERR_SHAPE, "need B >= 1, H >= 1, N >= 0");
-  if (!dims_ok(D, M)) return fail(LA_ERR_UNSUPPORTED, "D and M must each be 32 or 64");
+  if (!dims_ok(D, M) && !(wide_ok(D) && (M == 32 || M == 64)))
+    return fail(LA_ERR_UNSUPPORTED, "D must be 32, 64 or a multiple of 64 up to 4096 (wide feature vectors) and M "
+                                    "32 or 64");
   const double elems = (double)B * H * (double)N * (D > M ? D : M);
   if (elems > 4.0e18 || (double)B * H * (N > 0 ? N : 1) > 2.0e9) return fail(LA_ERR_SHAPE, "sizes overflow");
+  return LA_OK;
+}
+
+// Wide feature vectors come from a feature map: they are used as they are
+// (LA_FEATURE_IDENTITY), without a decay.
+int check_wide(int D, int feature, const float* logA) {
+  if (!is_wide(D)) return LA_OK;
+  if (feature != LA_FEATURE_IDENTITY)
+    return fail(LA_ERR_UNSUPPORTED, "D > 64 (wide feature vectors) needs feature = LA_FEATURE_IDENTITY");
+  if (logA) return fail(LA_ERR_UNSUPPORTED, "D > 64 (wide feature vectors) has no decayed form");
   return LA_OK;
 }
 
@@ -300,7 +353,7 @@ dim3 scan_grid(const Plan& p) { return dim3((unsigned)p.BH, (unsigned)((p.SV + l
 template <typename T, int D, int M>
 int seg_aggregates(const Plan& p, const void* K, const void* V, float* agg, int N, int fm, const Call& s) {
   return launch("seg_state", la::k_seg_state<T, D, M>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
-                (const T*)K, (const T*)V, agg, N, p.L, p.nseg, fm);
+                (const T*)K, (const T*)V, agg, N, p.L, p.nseg, fm, p.ns);
 }
 
 template <int D, int M>
@@ -393,7 +446,7 @@ int fwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   }
   return launch("fwd_causal", la::k_fwd<T, D, M, true>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, den, pref, (const float*)agg, S0, Z0, ckw, S_out,
-                Z_out, N, p.L, p.nseg, fm);
+                Z_out, N, p.L, p.nseg, fm, 1, (float*)nullptr);
 }
 
 template <typename T, int D, int M>
@@ -418,7 +471,7 @@ int fwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   return launch("fwd_noncausal", la::k_fwd<T, D, M, false>, dim3((unsigned)(p.BH * p.nseg)), dim3(la::NT), s,
                 (const T*)Q, (const T*)K, (const T*)V, (T*)O, (float*)nullptr, pref, (const float*)agg,
                 (const float*)nullptr, (const float*)nullptr, (float*)nullptr, S_out, Z_out, N,
-                p.L, p.nseg, fm);
+                p.L, p.nseg, fm, 1, (float*)nullptr);
 }
 
 template <typename T, int D, int M>
@@ -448,7 +501,7 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
   const dim3 grid((unsigned)(p.BH * p.nseg));
   st = launch("bwd_query", la::k_bq<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
-              (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm);
+              (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm, 1);
   if (st) return st;
   const int scanned = p.nseg > 1 && use_scan(p) ? 1 : 0;
   if (scanned) {
@@ -457,7 +510,7 @@ int bwd_causal_impl(const Plan& p, const void* Q, const void* K, const void* V, 
   }
   return launch("bwd_kv", la::k_bkv<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
                 (const T*)dO, (const float2*)gc, (const float*)ragg, dSN, dZN, (T*)dK, (T*)dV, dS0, dZ0, N, p.L,
-                p.nseg, scanned, fm);
+                p.nseg, scanned, fm, 1, (float*)nullptr);
 }
 
 template <typename T, int D, int M>
@@ -567,6 +620,143 @@ int decode_impl(long BH, const void* q, const void* k, const void* v, const floa
                 (const T*)k, (const T*)v, logA, S, Z, (T*)y, (int)BH, fm);
 }
 
+// ------------------------------------------------- wide feature vectors
+// Feature slices run as 64-feature heads of the chunked kernels (la_wide.h);
+// the sums over slices follow.  The checkpoint of a wide forward is the
+// slices' states followed by float32 O and den of every value head (what the
+// backward needs of the whole head).
+size_t ckpt_states_bytes(const Plan& p) { return state_bytes(p, p.nseg + 1); }
+size_t ckpt_bytes(const Plan& p) {
+  if (p.ns == 1) return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float);
+  return ckpt_states_bytes(p) + wide_o32(p);
+}
+
+template <int M>
+dim3 token_grid(long rows) { return dim3((unsigned)((rows * (M / 4) + la::NT - 1) / la::NT)); }
+
+template <typename T, int M>
+int fwd_wide_impl(const Plan& p, bool causal, const void* Q, const void* K, const void* V, void* O, float* den,
+                  const float* S0, const float* Z0, float* S_out, float* Z_out, float* ckpt, int N, void* ws, int fm,
+                  const Call& s) {
+  if (p.nseg == 0) {
+    if (!causal)
+      return S_out ? launch("state_copy", la::k_state_copy<64, M>, dim3((unsigned)p.BH), dim3(la::NT), s,
+                            (const float*)nullptr, (const float*)nullptr, (float*)nullptr, S_out, Z_out)
+                   : LA_OK;
+    return launch("state_copy", la::k_state_copy<64, M>, dim3((unsigned)p.BH), dim3(la::NT), s, S0, Z0, ckpt, S_out,
+                  Z_out);
+  }
+  const WsLayout wl = ws_layout(causal ? LA_OP_FWD_CAUSAL : LA_OP_FWD_NONCAUSAL, p);
+  float* agg = nullptr;
+  const float* pref = nullptr;
+  float* ckw = causal ? ckpt : nullptr;
+  int st = LA_OK;
+  if (p.nseg > 1 || !causal) {
+    agg = reinterpret_cast<float*>(region(ws, 0));
+    st = seg_aggregates<T, 64, M>(p, K, V, agg, N, fm, s);
+    if (st) return st;
+    if (use_scan(p)) {
+      float* pr = causal && ckpt ? ckpt : reinterpret_cast<float*>(region(ws, wl.agg));
+      st = scan_prefix<64, M>(p, agg, causal ? S0 : nullptr, causal ? Z0 : nullptr, pr, s, causal ? 0 : 1);
+      if (st) return st;
+      pref = pr;
+      ckw = nullptr;
+    }
+  }
+  float* pnum = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.sync));
+  float* pden = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.sync + wl.pn));
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  if (causal)
+    st = launch("fwd_causal", la::k_fwd<T, 64, M, true, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K,
+                (const T*)V, (T*)nullptr, pden, pref, (const float*)agg, S0, Z0, ckw, S_out, Z_out, N, p.L, p.nseg, fm,
+                p.ns, pnum);
+  else
+    st = launch("fwd_noncausal", la::k_fwd<T, 64, M, false, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K,
+                (const T*)V, (T*)nullptr, pden, pref, (const float*)agg, (const float*)nullptr,
+                (const float*)nullptr, (float*)nullptr, S_out, Z_out, N, p.L, p.nseg, fm, p.ns, pnum);
+  if (st) return st;
+  float* o32 = causal && ckpt ? reinterpret_cast<float*>(reinterpret_cast<char*>(ckpt) + ckpt_states_bytes(p))
+                              : nullptr;
+  float* d32 = o32 ? o32 + (size_t)p.BHv() * N * M : nullptr;
+  const long rows = p.BHv() * N;
+  return launch("wide_combine", la::k_wide_combine<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pnum,
+                (const float*)pden, (T*)O, den, o32, d32, rows, N, p.ns);
+}
+
+template <typename T, int M>
+int bwd_wide_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO, const float* S0,
+                  const float* Z0, const float* ckpt, const float* dSN, const float* dZN, void* dQ, void* dK, void* dV,
+                  float* dS0, float* dZ0, int N, void* ws, int fm, const Call& s) {
+  if (p.nseg == 0)
+    return dS0 ? launch("state_copy", la::k_state_copy<64, M>, dim3((unsigned)p.BH), dim3(la::NT), s, dSN, dZN,
+                        (float*)nullptr, dS0, dZ0)
+               : LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_BWD_CAUSAL, p);
+  float* ragg = p.nseg > 1 ? reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt)) : nullptr;
+  float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+  float* pn = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc));
+  float* pd = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc + wl.pn));
+  const long rows = p.BHv() * N;
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  int st = LA_OK;
+  const float* ck = ckpt;
+  const float* o32 = nullptr;
+  if (ck) {
+    o32 = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ck) + ckpt_states_bytes(p));
+  } else {  // recompute the checkpoint: the slices' states, then float32 O and den of the forward
+    float* agg = reinterpret_cast<float*>(region(ws, 0));
+    float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
+    float* o32w = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc + wl.pn + wl.pd));
+    st = seg_aggregates<T, 64, M>(p, K, V, agg, N, fm, s);
+    if (st) return st;
+    st = scan_prefix<64, M>(p, agg, S0, Z0, ckw, s);
+    if (st) return st;
+    st = launch("fwd_causal", la::k_fwd<T, 64, M, true, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K,
+                (const T*)V, (T*)nullptr, pd, (const float*)ckw, (const float*)nullptr, S0, Z0, (float*)nullptr,
+                (float*)nullptr, (float*)nullptr, N, p.L, p.nseg, fm, p.ns, pn);
+    if (st) return st;
+    st = launch("wide_combine", la::k_wide_combine<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pn,
+                (const float*)pd, (T*)nullptr, (float*)nullptr, o32w, o32w + (size_t)rows * M, rows, N, p.ns);
+    if (st) return st;
+    ck = ckw;
+    o32 = o32w;
+  }
+  st = launch("wide_pairs", la::k_wide_pairs<T, M>, token_grid<M>(rows), dim3(la::NT), s, o32,
+              o32 + (size_t)rows * M, (const T*)dO, gc, rows);
+  if (st) return st;
+  st = launch("bwd_query", la::k_bq<T, 64, M, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+              (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm, p.ns);
+  if (st) return st;
+  const int scanned = p.nseg > 1 && use_scan(p) ? 1 : 0;
+  if (scanned) {
+    st = launch("scan_rev", la::k_scan_rev<64, M>, scan_grid(p), dim3(la::NT), s, ragg, p.nseg);
+    if (st) return st;
+  }
+  st = launch("bwd_kv", la::k_bkv<T, 64, M, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
+              (const T*)dO, (const float2*)gc, (const float*)ragg, dSN, dZN, (T*)dK, (T*)nullptr, dS0, dZ0, N, p.L,
+              p.nseg, scanned, fm, p.ns, pn);
+  if (st) return st;
+  return launch("wide_sum", la::k_wide_sum<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pn, (T*)dV,
+                rows, N, p.ns);
+}
+
+template <typename T, int M>
+int decode_wide_impl(long BH, int C, const void* q, const void* k, const void* v, float* S, float* Z, void* y, int fm,
+                     const Call& s) {
+  return launch("decode_wide", la::k_decode_wide<T, M>, dim3((unsigned)BH), dim3(la::NT), s, (const T*)q,
+                (const T*)k, (const T*)v, S, Z, (T*)y, C, fm);
+}
+
+#define LA_WIDE_DISPATCH(dtype, M, FN, ...)                                  \
+  do {                                                                       \
+    if ((dtype) == LA_F32) {                                                 \
+      if ((M) == 32) return FN<float, 32>(__VA_ARGS__);                      \
+      return FN<float, 64>(__VA_ARGS__);                                     \
+    }                                                                        \
+    if ((M) == 32) return FN<la::bf16_t, 32>(__VA_ARGS__);                   \
+    return FN<la::bf16_t, 64>(__VA_ARGS__);                                  \
+  } while (0)
+
 size_t esize(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
 // ----------------------------------------------------------- feature maps
@@ -598,7 +788,49 @@ int feat_rf_impl(long BH, int H, int N, const void* X, const float* W, const voi
   if (dPhi)
     return launch("feat_rf_vjp", la::k_feat_rf_vjp<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W,
                   (const T*)dPhi, (T*)out, N, H, (int)cpw);
-  return launch("feat_rf", la::k_feat_rf<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H, (int)cpw);
+  return launch("feat_rf", la::k_feat_rf<T, DIN, C>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H, (int)cpw,
+                1, (float)(1.0 / std::sqrt((double)C)));
+}
+
+// Wide random features (C = 64 ns, feature-sliced output): the forward runs
+// one workgroup per slice and group of chunks; the vector-Jacobian product,
+// which sums over every feature, walks the slices inside each workgroup.
+template <typename T, int DIN>
+int feat_rf_wide_impl(long BH, int H, int N, int C, const void* X, const float* W, const void* dPhi, void* out,
+                      const Call& s) {
+  const int ns = C / 64;
+  const float sc = (float)(1.0 / std::sqrt((double)C));
+  const long nch = (N + la::CH - 1) / la::CH;
+  if (dPhi) {
+    constexpr int CPW = sizeof(T) == 2 ? 4 : 2;  // chunks of X resident per workgroup (LDS)
+    const dim3 grid((unsigned)(BH * ((nch + CPW - 1) / CPW)));
+    return launch("feat_rf_vjp_wide", la::k_feat_rf_vjp_wide<T, DIN, CPW>, grid, dim3(la::NT), s, (const T*)X, W,
+                  (const T*)dPhi, (T*)out, N, H, ns, sc);
+  }
+  long cpw = (BH * ns * nch + 1023) / 1024;
+  cpw = cpw < 1 ? 1 : cpw > nch ? nch : cpw;
+  const dim3 grid((unsigned)(BH * ns * ((nch + cpw - 1) / cpw)));
+  return launch("feat_rf", la::k_feat_rf<T, DIN, 64>, grid, dim3(la::NT), s, (const T*)X, W, (T*)out, N, H, (int)cpw,
+                ns, sc);
+}
+
+// Wide polynomial features (C = 64 ns, feature-sliced): a workgroup per
+// slice and 64 tokens forward; the vector-Jacobian product stages each
+// token's quadratic block in LDS.
+template <typename T>
+int feat_poly2_wide_impl(long BH, int N, int din, int C, const void* X, const void* dPhi, void* out, const Call& s) {
+  const int ns = C / 64;
+  if (dPhi) {
+    const long rows = BH * N;
+    if (din <= 32)
+      return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 32>, dim3((unsigned)((rows + 7) / 8)),
+                    dim3(la::NT), s, (const T*)X, (const T*)dPhi, (T*)out, rows, N, din, ns);
+    return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 64>, dim3((unsigned)((rows + 3) / 4)),
+                  dim3(la::NT), s, (const T*)X, (const T*)dPhi, (T*)out, rows, N, din, ns);
+  }
+  const long ntb = (N + la::CH - 1) / la::CH;
+  return launch("feat_poly2_wide", la::k_feat_poly2_wide<T>, dim3((unsigned)(BH * ns * ntb)), dim3(la::NT), s,
+                (const T*)X, (T*)out, N, din, ns);
 }
 
 template <typename T, int C>
@@ -615,7 +847,8 @@ int feature_random(const void* X, const float* W, const void* dPhi, void* out, i
   g_err.clear();
   int st = check_sizes(B, H, N, 32, 32, dtype);
   if (st) return st;
-  if (!dims_ok(Din, C)) return fail(LA_ERR_UNSUPPORTED, "Din and C must each be 32 or 64");
+  if ((Din != 32 && Din != 64) || (C != 32 && C != 64 && !wide_ok(C)))
+    return fail(LA_ERR_UNSUPPORTED, "Din must be 32 or 64 and C 32, 64 or a multiple of 64 up to 4096");
   if (N == 0) return LA_OK;
   if (!X || !W || !out) return fail(LA_ERR_NULL, "X, W and the output are required");
   const size_t es = esize(dtype), bh = (size_t)B * H;
@@ -623,7 +856,15 @@ int feature_random(const void* X, const float* W, const void* dPhi, void* out, i
                    rng("dPhi", dPhi, bh * N * C * es, false),
                    rng(dPhi ? "dX" : "Phi", out, bh * N * (dPhi ? Din : C) * es, true)});
   if (st) return st;
-  LA_FEAT_DISPATCH(dtype, Din, C, feat_rf_impl, (long)bh, H, N, X, W, dPhi, out, Call{(hipStream_t)stream, nullptr});
+  const Call call{(hipStream_t)stream, nullptr};
+  if (wide_ok(C)) {
+    if (dtype == LA_F32)
+      return Din == 32 ? feat_rf_wide_impl<float, 32>((long)bh, H, N, C, X, W, dPhi, out, call)
+                       : feat_rf_wide_impl<float, 64>((long)bh, H, N, C, X, W, dPhi, out, call);
+    return Din == 32 ? feat_rf_wide_impl<la::bf16_t, 32>((long)bh, H, N, C, X, W, dPhi, out, call)
+                     : feat_rf_wide_impl<la::bf16_t, 64>((long)bh, H, N, C, X, W, dPhi, out, call);
+  }
+  LA_FEAT_DISPATCH(dtype, Din, C, feat_rf_impl, (long)bh, H, N, X, W, dPhi, out, call);
 }
 
 int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int N, int Din, int C, int dtype,
@@ -631,9 +872,10 @@ int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int 
   g_err.clear();
   int st = check_sizes(B, H, N, 32, 32, dtype);
   if (st) return st;
-  if (C != 32 && C != 64) return fail(LA_ERR_UNSUPPORTED, "C must be 32 or 64");
-  if (Din < 1 || Din > 7 || 1 + Din + Din * Din > C)
-    return fail(LA_ERR_UNSUPPORTED, "degree-2 features need 1 + Din + Din^2 <= C (Din <= 5 for C = 32, 7 for 64)");
+  if (C != 32 && C != 64 && !wide_ok(C))
+    return fail(LA_ERR_UNSUPPORTED, "C must be 32, 64 or a multiple of 64 up to 4096");
+  if (Din < 1 || Din > 64 || 1 + Din + Din * Din > C)
+    return fail(LA_ERR_UNSUPPORTED, "degree-2 features need 1 <= Din <= 64 and 1 + Din + Din^2 <= C");
   if (N == 0) return LA_OK;
   if (!X || !out) return fail(LA_ERR_NULL, "X and the output are required");
   const size_t es = esize(dtype), bh = (size_t)B * H;
@@ -641,6 +883,11 @@ int feature_poly2(const void* X, const void* dPhi, void* out, int B, int H, int 
                    rng(dPhi ? "dX" : "Phi", out, bh * N * (dPhi ? Din : C) * es, true)});
   if (st) return st;
   const long rows = (long)bh * N;
+  if (wide_ok(C)) {
+    if (dtype == LA_F32)
+      return feat_poly2_wide_impl<float>((long)bh, N, Din, C, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
+    return feat_poly2_wide_impl<la::bf16_t>((long)bh, N, Din, C, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
+  }
   if (dtype == LA_F32) {
     if (C == 32) return feat_poly2_impl<float, 32>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
     return feat_poly2_impl<float, 64>(rows, Din, X, dPhi, out, Call{(hipStream_t)stream, nullptr});
@@ -702,7 +949,8 @@ const char* la_last_error(void) { return g_err.c_str(); }
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,bwd_query,bwd_kv,nc_qr,nc_kv,decode,scan_states,scan_rev,"
          "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
-         "feat_poly2_vjp,sync_clear";
+         "feat_poly2_vjp,sync_clear,wide_combine,wide_pairs,wide_sum,decode_wide,feat_rf_vjp_wide,feat_poly2_wide,"
+         "feat_poly2_vjp_wide";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype, const la_options* opts) {
@@ -710,18 +958,20 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype, c
   if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
   const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
                   op == LA_OP_BWD_DECAY;
-  return ws_layout(op, make_plan(B, H, N, D, M, nc ? kFineTargetNC : 0, opt_chunks(opts))).bytes();
+  if (is_wide(D) && (op == LA_OP_DECODE || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
+                     op == LA_OP_BWD_DECAY))
+    return 0;
+  return ws_layout(op, plan_for(B, H, N, D, M, nc ? kFineTargetNC : 0, opt_chunks(opts))).bytes();
 }
 
 size_t la_checkpoint_size(int B, int H, int N, int D, int M, const la_options* opts) {
   if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
-  const Plan p = make_plan(B, H, N, D, M, 0, opt_chunks(opts));
-  return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float);
+  return ckpt_bytes(plan_for(B, H, N, D, M, 0, opt_chunks(opts)));
 }
 
 int la_segment_length(int B, int H, int N, int D, int M, const la_options* opts) {
   if (check_sizes(B, H, N, D, M, LA_F32) != LA_OK) return 0;
-  return make_plan(B, H, N, D, M, 0, opt_chunks(opts)).L;
+  return plan_for(B, H, N, D, M, 0, opt_chunks(opts)).L;
 }
 
 int la_forward_wait_status(const void* ws, size_t ws_bytes, int B, int H, int N, int D, int M, int dtype,
@@ -731,7 +981,7 @@ int la_forward_wait_status(const void* ws, size_t ws_bytes, int B, int H, int N,
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
-  const Plan p = make_plan(B, H, N, D, M, 0, opt_chunks(opts));
+  const Plan p = plan_for(B, H, N, D, M, 0, opt_chunks(opts));
   const WsLayout wl = ws_layout(LA_OP_FWD_CAUSAL, p);
   if (wl.sync == 0) return LA_OK;  // no flags: never the one-launch form
   if (!ws || ws_bytes < wl.bytes())
@@ -777,11 +1027,13 @@ int forward_causal_entry(const void* Q, const void* K, const void* V, const floa
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
+  st = check_wide(D, feature, logA);
+  if (st) return st;
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
-  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const Plan p = plan_for(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
+  const size_t es = esize(dtype), bh = (size_t)p.BHv();
   const size_t need = ws_layout(logA ? LA_OP_FWD_DECAY : LA_OP_FWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
   if (use_scratch && uses_ws) {  // the library's static scratch of this device in place of a workspace
@@ -805,6 +1057,9 @@ int forward_causal_entry(const void* Q, const void* K, const void* V, const floa
                    rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
   if (N == 0 && !S_out && !ckpt) return LA_OK;
+  if (p.ns > 1)
+    LA_WIDE_DISPATCH(dtype, M, fwd_wide_impl, p, true, Q, K, V, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws, fm,
+                     Call{(hipStream_t)stream, opts});
   if (logA)
     LA_DISPATCH(dtype, D, M, fwd_decay_impl, p, Q, K, V, logA, O, den, S0, Z0, S_out, Z_out, ckpt, N, ws,
                 fm, Call{(hipStream_t)stream, opts});
@@ -828,11 +1083,13 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, f
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
+  st = check_wide(D, feature, nullptr);
+  if (st) return st;
   if ((S_out == nullptr) != (Z_out == nullptr)) return fail(LA_ERR_ARG, "S_out and Z_out must be given together");
   if (N == 0 && !S_out) return LA_OK;
   if (N > 0 && (!Q || !K || !V || !O)) return fail(LA_ERR_NULL, "Q, K, V and O are required");
-  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
-  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const Plan p = plan_for(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
+  const size_t es = esize(dtype), bh = (size_t)p.BHv();
   const size_t need = ws_layout(LA_OP_FWD_NONCAUSAL, p).bytes();
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
@@ -841,6 +1098,9 @@ int la_forward_noncausal(const void* Q, const void* K, const void* V, void* O, f
                    rng("S_out", S_out, bh * D * M * 4, true), rng("Z_out", Z_out, bh * D * 4, true),
                    rng("ws", need > 0 ? ws : nullptr, need, true)});
   if (st) return st;
+  if (p.ns > 1)
+    LA_WIDE_DISPATCH(dtype, M, fwd_wide_impl, p, false, Q, K, V, O, (float*)nullptr, (const float*)nullptr,
+                     (const float*)nullptr, S_out, Z_out, (float*)nullptr, N, ws, fm, Call{(hipStream_t)stream, opts});
   LA_DISPATCH(dtype, D, M, fwd_noncausal_impl, p, Q, K, V, O, S_out, Z_out, N, ws, fm, Call{(hipStream_t)stream, opts});
 }
 
@@ -857,6 +1117,8 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
+  st = check_wide(D, feature, logA);
+  if (st) return st;
   if ((logA == nullptr) != (dlogA == nullptr)) return fail(LA_ERR_ARG, "logA and dlogA must be given together");
   if ((S0 == nullptr) != (Z0 == nullptr)) return fail(LA_ERR_ARG, "S0 and Z0 must be given together");
   if ((dS_N == nullptr) != (dZ_N == nullptr)) return fail(LA_ERR_ARG, "dS_N and dZ_N must be given together");
@@ -867,13 +1129,16 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
     st = check_ptrs({rng("dS_N", dS_N, bh * D * M * 4, false), rng("dZ_N", dZ_N, bh * D * 4, false),
                      rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true)});
     if (st) return st;
-    const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
+    const Plan p = plan_for(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
+    if (p.ns > 1)
+      LA_WIDE_DISPATCH(dtype, M, bwd_wide_impl, p, Q, K, V, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0, N,
+                       ws, fm, Call{(hipStream_t)stream, opts});
     LA_DISPATCH(dtype, D, M, bwd_causal_impl, p, Q, K, V, O, den, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0,
                 dZ0, N, ws, fm, Call{(hipStream_t)stream, opts});
   }
   if (!Q || !K || !V || !O || !den || !dO || !dQ || !dK || !dV)
     return fail(LA_ERR_NULL, "Q, K, V, O, den, dO, dQ, dK and dV are required");
-  const Plan p = make_plan(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
+  const Plan p = plan_for(B, H, N, D, M, logA ? kFineTargetNC : 0, opt_chunks(opts));
   const size_t es = esize(dtype);
   const size_t need = ws_layout(logA ? LA_OP_BWD_DECAY : LA_OP_BWD_CAUSAL, p).bytes();
   const bool uses_ws = need > 0;
@@ -890,6 +1155,9 @@ int la_backward_causal(const void* Q, const void* K, const void* V, const float*
                    rng("dS0", dS0, bh * D * M * 4, true), rng("dZ0", dZ0, bh * D * 4, true),
                    rng("ws", uses_ws ? ws : nullptr, need, true)});
   if (st) return st;
+  if (p.ns > 1)
+    LA_WIDE_DISPATCH(dtype, M, bwd_wide_impl, p, Q, K, V, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dS0, dZ0, N, ws,
+                     fm, Call{(hipStream_t)stream, opts});
   if (logA)
     LA_DISPATCH(dtype, D, M, bwd_decay_impl, p, Q, K, V, logA, dO, S0, Z0, ckpt, dS_N, dZ_N, dQ, dK, dV, dlogA, dS0,
                 dZ0, N, ws, fm, Call{(hipStream_t)stream, opts});
@@ -909,6 +1177,7 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
+  if (is_wide(D)) return fail(LA_ERR_UNSUPPORTED, "the non-causal backward takes D of 32 or 64");
   if (N == 0) return LA_OK;
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(LA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
   if ((S_tot == nullptr) != (Z_tot == nullptr)) return fail(LA_ERR_ARG, "S_tot and Z_tot must be given together");
@@ -937,12 +1206,16 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
+  st = check_wide(D, feature, logA);
+  if (st) return st;
   if (!q || !k || !v || !S || !Z || !y) return fail(LA_ERR_NULL, "q, k, v, S, Z and y are required");
   const size_t es = esize(dtype), bh = (size_t)B * H;
   st = check_ptrs({rng("q", q, bh * D * es, false), rng("k", k, bh * D * es, false), rng("v", v, bh * M * es, false),
                    rng("logA", logA, bh * 4, false), rng("S", S, bh * D * M * 4, true),
                    rng("Z", Z, bh * D * 4, true), rng("y", y, bh * M * es, true)});
   if (st) return st;
+  if (is_wide(D))
+    LA_WIDE_DISPATCH(dtype, M, decode_wide_impl, (long)bh, D, q, k, v, S, Z, y, fm, Call{(hipStream_t)stream, opts});
   LA_DISPATCH(dtype, D, M, decode_impl, (long)bh, q, k, v, logA, S, Z, y, fm, Call{(hipStream_t)stream, opts});
 }
 

@@ -89,12 +89,16 @@ __device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, 
 }
 
 // ===================================================================== B-A
-template <typename T, int D, int M>
+// GIVEN (feature slices, ns per value head, la_wide.h): a slice sees only its
+// share of den_i and of num_i . dO_i, so the pair (1/den_i, O_i . dO_i) of
+// value head bh / ns is read from gc (formed from the whole head's float32
+// outputs) instead of recomputed and written.
+template <typename T, int D, int M, bool GIVEN = false>
 __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __restrict__ K,
                                             const T* __restrict__ V, const T* __restrict__ dO,
                                             const float* __restrict__ ckpt, T* __restrict__ dQ,
                                             float2* __restrict__ gc, float* __restrict__ ragg, int N, int L, int nseg,
-                                            int fm) {
+                                            int fm, int ns) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NTS = DB * MB / 4;        // S^T tiles per wave
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
+  const int vh = GIVEN ? bh / ns : bh;  // value head
+  const size_t offD = (size_t)bh * N * D, offM = (size_t)vh * N * M;
   const Frag<1> ones = ones_frag();
   ot.zero_cols(M + 2, M + 16);
   auto sdb = [&](int k) { return (w + 4 * k) % DB; };
@@ -230,21 +235,30 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
         ZC[d0] += f32x4_t{z4.x, z4.y, z4.z, z4.w};  // U: S_i dO_i [d][i], ZC: Z_i [d][i]
       }
-      float pu = 0.f, pz = 0.f;
       float qv[DB][4];
+      float invz, odo;
+      if constexpr (GIVEN) {
 #pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+        for (int d0 = 0; d0 < DB; ++d0) qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+        const float2 pr = row_ok ? gc[(size_t)vh * N + c0 + il] : make_float2(0.f, 0.f);
+        invz = pr.x;
+        odo = pr.y;
+      } else {
+        float pu = 0.f, pz = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pu += qv[d0][r] * U[d0][r];
-          pz += qv[d0][r] * ZC[d0][r];
+        for (int d0 = 0; d0 < DB; ++d0) {
+          qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pu += qv[d0][r] * U[d0][r];
+            pz += qv[d0][r] * ZC[d0][r];
+          }
         }
+        pu = sum_over_g(pu);  // phi(Q_i)^T S_i dO_i = num_i . dO_i
+        pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
+        invz = row_ok ? 1.f / pz : 0.f;
+        odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
       }
-      pu = sum_over_g(pu);  // phi(Q_i)^T S_i dO_i = num_i . dO_i
-      pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
-      const float invz = row_ok ? 1.f / pz : 0.f;
-      const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) {
         float o[4], qs[4];
@@ -257,7 +271,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         qt.put4(il, 16 * d0 + 4 * g, qs);  // this lane's own elements of its own row: q'_i
       }
       if (g == 0) {
-        if (row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
+        if (!GIVEN && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
         put_neg_odo(ot, il, M, odo);
       }
     }
@@ -309,13 +323,17 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
 // causal part; the same waves add the chunk's share to the reverse state in
 // registers.  The sequence's first segment writes the reverse state carried
 // through token 1: the gradient of the initial state (dS0, dZ0).
-template <typename T, int D, int M>
+// PART (feature slices, ns per value head, la_wide.h): dV_j sums over all of
+// a head's features, so each slice writes its share (float32, [bh][n][M] in
+// pdv), summed over the slices afterwards.
+template <typename T, int D, int M, bool PART = false>
 __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __restrict__ K,
                                              const T* __restrict__ V, const T* __restrict__ dO,
                                              const float2* __restrict__ gc, const float* __restrict__ ragg,
                                              const float* __restrict__ dSN, const float* __restrict__ dZN,
                                              T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ dS0,
-                                             float* __restrict__ dZ0, int N, int L, int nseg, int scanned, int fm) {
+                                             float* __restrict__ dZ0, int N, int L, int nseg, int scanned, int fm,
+                                             int ns, float* __restrict__ pdv) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
@@ -330,7 +348,8 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const size_t offD = (size_t)bh * N * D, offM = (size_t)bh * N * M;
+  const int vh = PART ? bh / ns : bh;  // value head
+  const size_t offD = (size_t)bh * N * D, offM = (size_t)vh * N * M;
   ot.zero_cols(M + 2, M + 16);
 
   const int nchunk = (t1 - t0 + CH - 1) / CH;
@@ -346,11 +365,11 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
     bk.load(K + offD + (size_t)c0 * D, nv);
     bv.load(V + offM + (size_t)c0 * M, nv);
     bd.load(dO + offM + (size_t)c0 * M, nv);
-    if (tid < CH) pgc = tid < nv ? gc[(size_t)bh * N + c0 + tid] : make_float2(0.f, 0.f);
+    if (tid < CH) pgc = tid < nv ? gc[(size_t)vh * N + c0 + tid] : make_float2(0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < BQ::CNT; ++i) {
       const int row = BQ::row_of(i);
-      pinv[i] = row < nv ? gc[(size_t)bh * N + c0 + row].x : 0.f;
+      pinv[i] = row < nv ? gc[(size_t)vh * N + c0 + row].x : 0.f;
     }
   };
   fetch(t0 + (nchunk - 1) * CH);
@@ -523,8 +542,13 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
       if (row_ok) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          float o[4] = {aV[mb][0], aV[mb][1], aV[mb][2], aV[mb][3]};
-          IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+          if constexpr (PART) {
+            *reinterpret_cast<float4*>(pdv + ((size_t)bh * N + c0 + jl) * M + 16 * mb + 4 * g) =
+                make_float4(aV[mb][0], aV[mb][1], aV[mb][2], aV[mb][3]);
+          } else {
+            float o[4] = {aV[mb][0], aV[mb][1], aV[mb][2], aV[mb][3]};
+            IO<T>::store4(dV + offM + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+          }
         }
       }
     }

@@ -329,6 +329,10 @@ struct IO<float> {
   __device__ static __forceinline__ void store4(float* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   }
+  __device__ static __forceinline__ void load4(const float* p, float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
 };
 template <>
 struct IO<bf16_t> {
@@ -345,6 +349,10 @@ struct IO<bf16_t> {
   }
   __device__ static __forceinline__ void store4(bf16_t* p, const float* x) {
     *reinterpret_cast<uint2*>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
+  }
+  __device__ static __forceinline__ void load4(const bf16_t* p, float* x) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    x[0] = lo2f(u.x); x[1] = hi2f(u.x); x[2] = lo2f(u.y); x[3] = hi2f(u.y);
   }
 };
 

@@ -50,11 +50,11 @@ __device__ __forceinline__ void stage_w(Planes<NP, C, DIN>& wt, const float* w) 
 
 // phi of the chunk's 16 tokens of this wave: acc[cb][r] = phi(x_t)_c with
 // c = 16cb + 4g + r, t = 16w + r16.  nx = |x_t|^2 of that token.
+// sc = 1 / sqrt(number of features of the whole map).
 template <typename T, int DIN, int C>
 __device__ __forceinline__ void rf_tiles(const Planes<FPrec<T>::W, C, DIN>& wt, const Planes<FPrec<T>::X, CH, DIN>& xt,
-                                         float nx, int w, int r16, int g, f32x4_t* acc) {
+                                         float nx, int w, int r16, int g, f32x4_t* acc, float sc) {
   using P = FPrec<T>;
-  const float sc = 1.f / sqrtf((float)C);
   Frag<P::X> xf[DIN / 32];
 #pragma unroll
   for (int s = 0; s < DIN / 32; ++s) xf[s] = xt.template frag<P::X>(16 * w + r16, 32 * s, g);
@@ -113,28 +113,33 @@ __device__ __forceinline__ void walk_chunks(Planes<FPrec<T>::X, CH, DIN>& xt, fl
 }
 
 // Random features of `cpw` consecutive 64-token chunks of one head per
-// workgroup (W staged once for all of them).
+// workgroup (W staged once for all of them).  A map of ns > 1 slices of C =
+// 64 features (la_wide.h) runs one workgroup per slice: slice s of head bh
+// takes rows 64 s .. 64 s + 63 of the head's projection and writes the
+// feature-sliced output [bh][s][n][64]; with ns = 1 that is the plain
+// [bh][n][C].
 template <typename T, int DIN, int C>
 __global__ __launch_bounds__(NT) void k_feat_rf(const T* __restrict__ X, const float* __restrict__ W,
-                                                 T* __restrict__ Phi, int N, int H, int cpw) {
+                                                 T* __restrict__ Phi, int N, int H, int cpw, int ns, float sc) {
   using P = FPrec<T>;
   __shared__ Planes<P::W, C, DIN> wt;
   __shared__ Planes<P::X, CH, DIN> xt;
   __shared__ alignas(16) float snx[CH];
   const int nch = (N + CH - 1) / CH, ngr = (nch + cpw - 1) / cpw;
-  const int bh = blockIdx.x / ngr, ch0 = (blockIdx.x % ngr) * cpw, ch1 = min(nch, ch0 + cpw);
+  const int bhs = blockIdx.x / ngr, ch0 = (blockIdx.x % ngr) * cpw, ch1 = min(nch, ch0 + cpw);
+  const int bh = bhs / ns, sl = bhs % ns;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  stage_w<P::W, C, DIN>(wt, W + (size_t)(bh % H) * C * DIN);
+  stage_w<P::W, C, DIN>(wt, W + ((size_t)(bh % H) * ns + sl) * C * DIN);
   const int t = 16 * w + r16;
   walk_chunks<T, DIN>(xt, snx, X + (size_t)bh * N * DIN, N, ch0, ch1, [&](int ci, float nx) {
     const int c0 = ci * CH;
     f32x4_t acc[C / 16];
-    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
+    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc, sc);
     if (t < N - c0) {
 #pragma unroll
       for (int cb = 0; cb < C / 16; ++cb) {
         const float o[4] = {acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]};
-        IO<T>::store4(Phi + ((size_t)bh * N + c0 + t) * C + 16 * cb + 4 * g, o);
+        IO<T>::store4(Phi + ((size_t)bhs * N + c0 + t) * C + 16 * cb + 4 * g, o);
       }
     }
   });
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(NT) void k_feat_rf_vjp(const T* __restrict__ X, con
       }
     }
     f32x4_t acc[C / 16];
-    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc);
+    rf_tiles<T, DIN, C>(wt, xt, nx, w, r16, g, acc, 1.f / sqrtf((float)C));
     // G = dPhi * phi in the same layout, and its sum over the features
     float sg = 0.f;
 #pragma unroll

@@ -157,10 +157,12 @@ __device__ __forceinline__ void acc_to4(const f32x4_t& a, float* o) {
 // ===================================================================== F1
 // Segment aggregates: agg[bh][seg] = ( sum_j phi(K_j) V_j^T  [D][M],
 //                                      sum_j phi(K_j)        [D] )
-// over the segment's tokens (eq. 10-11 restricted to one segment).
+// over the segment's tokens (eq. 10-11 restricted to one segment).  With ns
+// > 1 the heads are feature slices: head bh holds features of value head
+// bh / ns (wide feature maps, la_wide.h).
 template <typename T, int D, int M>
 __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const T* __restrict__ V,
-                                                   float* __restrict__ agg, int N, int L, int nseg, int fm) {
+                                                   float* __restrict__ agg, int N, int L, int nseg, int fm, int ns) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   __shared__ Planes<P::FKF, CH, D> kt;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
   const int db = w % DB;
   const bool zw = w < DB;
   const T* Kh = K + (size_t)bh * N * D;
-  const T* Vh = V + (size_t)bh * N * M;
+  const T* Vh = V + (size_t)(bh / ns) * N * M;
   const Frag<1> ones = ones_frag();
 
   f32x4_t acc[NTW], accZ = zero4();  // S layout; accZ[r] = Z[16db + 4g + r]
@@ -236,14 +238,17 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
 //     writes the total to S_out/Z_out when given.
 // Z is staged as 16 identical rows, so phi(Q) Z is one more MFMA output tile
 // whose every row holds the denominators of the wave's tokens.
-template <typename T, int D, int M, bool CAUSAL>
+// PART (feature slices, ns per value head, la_wide.h): the slice's share of
+// the numerator (float32, [bh][n][M] in pnum) and of the denominator (den_out)
+// instead of O; they are summed over the slices afterwards.
+template <typename T, int D, int M, bool CAUSAL, bool PART = false>
 __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __restrict__ K,
                                              const T* __restrict__ V, T* __restrict__ O, float* __restrict__ den_out,
                                              const float* __restrict__ pref, const float* __restrict__ agg,
                                              const float* __restrict__ S0, const float* __restrict__ Z0,
                                              float* __restrict__ ckpt,
                                              float* __restrict__ S_out, float* __restrict__ Z_out, int N, int L,
-                                             int nseg, int fm) {
+                                             int nseg, int fm, int ns, float* __restrict__ pnum) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, NTW = DB * MB / 4, SV = D * M + D;
   constexpr int KR = CAUSAL ? CH : 1, KD = CAUSAL ? D : 8, KM = CAUSAL ? M : 8;
@@ -270,8 +275,9 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   const bool zw = w < DB;
   const T* Qh = Q + (size_t)bh * N * D;
   const T* Kh = K + (size_t)bh * N * D;
-  const T* Vh = V + (size_t)bh * N * M;
-  T* Oh = O + (size_t)bh * N * M;
+  const T* Vh = V + (size_t)(PART ? bh / ns : bh) * N * M;
+  T* Oh = PART ? nullptr : O + (size_t)bh * N * M;
+  float* Ph = PART ? pnum + (size_t)bh * N * M : nullptr;
   const Frag<1> ones = ones_frag();
 
   // two chunks of global reads in flight (see k_seg_state)
@@ -399,10 +405,15 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) mmaf<P::FS, P::FQ>(acc, st.template frag<P::FS>(16 * mb + r16, 32 * s, g), qf[s]);
       if (row_ok) {
-        float o[4];
+        if constexpr (PART) {
+          *reinterpret_cast<float4*>(Ph + (size_t)(c0 + il) * M + 16 * mb + 4 * g) =
+              make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+          float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[r] * inv;
-        IO<T>::store4(Oh + (size_t)(c0 + il) * M + 16 * mb + 4 * g, o);
+          for (int r = 0; r < 4; ++r) o[r] = acc[r] * inv;
+          IO<T>::store4(Oh + (size_t)(c0 + il) * M + 16 * mb + 4 * g, o);
+        }
       }
     }
     if (den_out && g == 0 && row_ok) den_out[(size_t)bh * N + c0 + il] = den;

@@ -361,3 +361,73 @@ def test_binding_checks_tensor_agreement():
         # and the well-formed call only fails at the device check (no GPU here)
     with pytest.raises(ValueError, match="GPU"):
         binding.la_forward_causal(q, k, v, o, den=f(B, H, N))
+
+
+@pytest.mark.parametrize("B,H,N,C,M", [(2, 2, 300, 128, 32), (4, 8, 3072, 1088, 32), (16, 8, 784, 256, 32),
+                                        (1, 1, 1, 4096, 64), (1, 2, 5000, 192, 64)])
+def test_wide_plan_and_sizes(lib, B, H, N, C, M):
+    """Wide feature vectors (C = 64 ns): the plan of the B*H*ns feature slices as 64-feature heads; the
+    checkpoint holds the slices' states and then float32 O and den of every head; the workspaces add the
+    slices' shares of the numerators and denominators (the forward) and of dV (the backward, which also keeps
+    room for float32 O and den when it recomputes the checkpoint)."""
+    ns = C // 64
+    L, nseg = _plan(B, H * ns, N, D=64, M=M)
+    assert lib.la_segment_length(B, H, N, C, M, None) == L
+    sv = 64 * M + 64
+    bhs = B * H * ns
+    o32 = _al(B * H * N * (M + 1) * 4)
+    assert lib.la_checkpoint_size(B, H, N, C, M, None) == _al(bhs * (nseg + 1) * sv * 4) + o32
+    pn, pd = _al(bhs * N * M * 4), _al(bhs * N * 4)
+    agg, pref = _al(bhs * nseg * sv * 4), _al(bhs * (nseg + 1) * sv * 4)
+    assert lib.la_workspace_size(0, B, H, N, C, M, 0, None) == (0 if nseg == 1 else agg + pref) + pn + pd
+    _, nseg_nc = _plan(B, H * ns, N, 512)
+    assert lib.la_workspace_size(1, B, H, N, C, M, 1, None) == (_al(bhs * nseg_nc * sv * 4) +
+                                                                _al(bhs * (nseg_nc + 1) * sv * 4) + pn + pd)
+    bwd = agg + pref + (0 if nseg == 1 else agg) + _al(B * H * N * 8) + pn + pd + o32
+    assert lib.la_workspace_size(2, B, H, N, C, M, 0, None) == bwd
+    for op in (3, 4, 5, 6):  # decode needs none; no non-causal backward or decayed form for wide features
+        assert lib.la_workspace_size(op, B, H, N, C, M, 0, None) == 0
+
+
+def test_wide_validation(lib):
+    assert fwd(lib, D=96) == UNSUPPORTED
+    assert fwd(lib, D=4160) == UNSUPPORTED
+    assert fwd(lib, D=128) == UNSUPPORTED  # elu + 1 is applied to 32- or 64-wide heads only
+    assert b"LA_FEATURE_IDENTITY" in lib.la_last_error()
+    assert fwd(lib, D=128, feature=1, logA=addr(14)) == UNSUPPORTED
+    assert b"decay" in lib.la_last_error()
+    args = [addr(1), addr(2), addr(3), addr(4), None, None, addr(5), addr(6), addr(7)]
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 128, 32, 0, 1, addr(20), 1 << 30, None, None) == UNSUPPORTED
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 128, 64, 1, 0,
+                              None, None) == UNSUPPORTED
+    assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(8), addr(4), addr(5), addr(6), 2, 2, 128, 64, 1, 1,
+                              None, None) == UNSUPPORTED
+    # wide feature maps: C a multiple of 64 up to 4096; degree 2 needs 1 + Din + Din^2 <= C and Din <= 64
+    assert lib.la_feature_random(addr(1), addr(2), addr(3), 2, 2, 100, 32, 96, 0, None) == UNSUPPORTED
+    assert lib.la_feature_random(addr(1), addr(2), addr(3), 2, 2, 100, 32, 4160, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 32, 1024, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 65, 4096, 0, None) == UNSUPPORTED
+    assert lib.la_feature_poly2(addr(1), addr(1), 2, 2, 100, 32, 1088, 0, None) == ALIAS
+    names = binding.kernel_names()
+    assert all(n in names for n in ("wide_combine", "wide_pairs", "wide_sum", "decode_wide", "feat_rf_vjp_wide",
+                                    "feat_poly2_wide", "feat_poly2_vjp_wide"))
+
+
+def test_binding_feature_sliced_layout():
+    """Q, K wider than 64 features go in feature-sliced [B,H,D/64,N,64]; the plain layout is refused."""
+    import torch
+
+    q = torch.zeros((2, 3, 4, 10, 64))
+    v = torch.zeros((2, 3, 10, 32))
+    assert binding._sizes(q, q, v) == (2, 3, 10, 256, 32)
+    with pytest.raises(ValueError, match="feature-sliced"):
+        binding._sizes(torch.zeros((2, 3, 10, 256)), torch.zeros((2, 3, 10, 256)), v)
+    with pytest.raises(ValueError):
+        binding._sizes(torch.zeros((2, 3, 4, 10, 32)), torch.zeros((2, 3, 4, 10, 32)), v)
+    x = torch.arange(2 * 3 * 10 * 256, dtype=torch.float32).reshape(2, 3, 10, 256)
+    s = binding.to_sliced(x)
+    assert tuple(s.shape) == (2, 3, 4, 10, 64)
+    assert torch.equal(s[1, 2, 3, 7], x[1, 2, 7, 192:256])
+    assert torch.equal(binding.from_sliced(s), x)
+    assert binding.feature_shape(2, 3, 10, 64) == (2, 3, 10, 64)
+    assert binding.feature_shape(2, 3, 10, 1088) == (2, 3, 17, 10, 64)
