@@ -47,12 +47,13 @@ CLOCK_GHZ = 2.4
 SIMDS = 256 * 4
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE = "long"
-NESTED = ("mnist", "cifar", "decode", "decode-dram")
+NESTED = ("mnist", "cifar", "decode", "decode-dram", "mnist-rf256", "cifar-poly2")
 DECODE_GRAPH = 64  # decode steps per captured graph
 THREADS = 16  # host threads for input generation (the GPU host's share of cores)
 
 # The kernel with the largest share of a step's GPU time (rocprofv3 kernel statistics in profiles/).
-DOMINANT = {"long": "bwd_kv", "mnist": "bwd_kv", "cifar": "bwd_kv", "mnist-rf": "bwd_kv",
+DOMINANT = {"long": "bwd_kv", "mnist": "bwd_kv", "cifar": "bwd_kv", "mnist-rf": "bwd_kv", "mnist-rf256": "bwd_kv",
+            "cifar-poly2": "bwd_kv",
             "long-decay": "dbkv", "speech": "nc_qr", "decode": "decode", "decode-dram": "decode",
             "small": "fwd_causal"}
 
@@ -63,8 +64,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; decode: 4096)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed warm-up steps (default 10; decode: 256)")
     ap.add_argument("--workload", default=None,
-                    choices=["mnist", "cifar", "long", "long-decay", "mnist-rf", "speech", "decode", "decode-dram",
-                             "small"],
+                    choices=["mnist", "cifar", "long", "long-decay", "mnist-rf", "mnist-rf256", "cifar-poly2",
+                             "speech", "decode", "decode-dram", "small"],
                     help="measure this workload alone (default: the headline plus the nested records)")
     ap.add_argument("--no-nested", action="store_true", help="headline only")
     ap.add_argument("--segment-chunks", type=int, default=0,
@@ -113,7 +114,8 @@ def WORKLOADS(inputs):
     dram = inputs.Workload("decode-dram-b2048h16d64-256steps-bf16", 2048, 16, 64, 64, 64, inputs.BF16, 1.0,
                            (511, 512, 513, 514), steps=256)
     return {"mnist": inputs.MNIST, "cifar": inputs.CIFAR, "long": inputs.LONG, "speech": inputs.SPEECH,
-            "long-decay": inputs.LONG_DECAY, "mnist-rf": inputs.MNIST_RF, "decode": inputs.DECODE,
+            "long-decay": inputs.LONG_DECAY, "mnist-rf": inputs.MNIST_RF, "mnist-rf256": inputs.MNIST_RF256,
+            "cifar-poly2": inputs.CIFAR_POLY2, "decode": inputs.DECODE,
             "decode-dram": dram, "small": inputs.SMALL}
 
 
@@ -142,7 +144,7 @@ class Step:
         code = binding.dtype_code(dt)
         if wl in ("cifar", "speech"):
             specs = [("layer", i) for i in range(w.layers)]  # one independent input set per layer
-        elif wl in ("mnist", "mnist-rf"):
+        elif wl in ("mnist", "mnist-rf", "mnist-rf256"):
             specs = [("set", i) for i in range(6)]  # rotate batches so successive steps miss the 256 MB cache
         else:
             specs = [("set", 0)]
@@ -168,13 +170,14 @@ class Step:
             self.ws_nb = binding.alloc_workspace(binding.LA_OP_BWD_NONCAUSAL, B, H, N, D, M, code, "cuda", so)
             self.s_tot = torch.empty((B, H, D, M), dtype=torch.float32, device="cuda")
             self.z_tot = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-        if wl == "mnist-rf":
-            C = w.features
-            self.W = torch.from_numpy(w.projection()).to("cuda").contiguous()
-            self.fq = torch.empty((B, H, N, C), dtype=dt, device="cuda")
-            self.fk = torch.empty((B, H, N, C), dtype=dt, device="cuda")
-            self.dfq = torch.empty((B, H, N, C), dtype=dt, device="cuda")
-            self.dfk = torch.empty((B, H, N, C), dtype=dt, device="cuda")
+        if w.features:  # the feature vectors of Q, K and their gradients (feature-sliced when C > 64)
+            fs = binding.feature_shape(B, H, N, w.features)
+            if w.fmap == "random":
+                self.W = torch.from_numpy(w.projection()).to("cuda").contiguous()
+            self.fq = torch.empty(fs, dtype=dt, device="cuda")
+            self.fk = torch.empty(fs, dtype=dt, device="cuda")
+            self.dfq = torch.empty(fs, dtype=dt, device="cuda")
+            self.dfk = torch.empty(fs, dtype=dt, device="cuda")
         if wl == "long-decay":
             self.log_a = torch.from_numpy(w.log_a()).to("cuda").contiguous()
             self.dla = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
@@ -300,22 +303,10 @@ class Step:
                 b.la_backward_noncausal(q, k, v, do, self.dq, self.dk, self.dv, ws=self.ws_nb, S_tot=self.s_tot,
                                         Z_tot=self.z_tot, opts=o)
             return
-        if wl == "mnist-rf":
+        if self.w.features:
             q, k, v, do = self.sets[self.i % len(self.sets)]
             self.i += 1
-            IDENT = b.LA_FEATURE_IDENTITY
-            lib, st = b.load(), b._stream(None)
-            B, H, N, D, C = self.w.B, self.w.H, self.w.N, self.w.D, self.w.features
-            for x, f in ((q, self.fq), (k, self.fk)):
-                b._check(lib.la_feature_random(b._ptr(x), b._ptr(self.W), b._ptr(f), B, H, N, D, C, 0, st),
-                         "la_feature_random")
-            b.la_forward_causal(self.fq, self.fk, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f, feature=IDENT,
-                                opts=o)
-            b.la_backward_causal(self.fq, self.fk, v, self.o, self.den, do, self.dfq, self.dfk, self.dv, ckpt=self.ck,
-                                 ws=self.ws_b, feature=IDENT, opts=o)
-            for x, g, dx in ((q, self.dfq, self.dq), (k, self.dfk, self.dk)):
-                b._check(lib.la_feature_random_vjp(b._ptr(x), b._ptr(self.W), b._ptr(g), b._ptr(dx), B, H, N, D, C,
-                                                   0, st), "la_feature_random_vjp")
+            self._features_step(q, k, v, do)
             return
         if wl == "long-decay":
             q, k, v, do = self.sets[0]
@@ -331,6 +322,31 @@ class Step:
         self._fwd_bwd(q, k, v, do)
         if wl == "mnist":
             b.la_forward_noncausal(q, k, v, self.onc, ws=self.ws_n, opts=o)
+
+    def _features_step(self, q, k, v, do):
+        """The feature map of Q and K, the causal attention on the features (checkpointed forward, backward), the
+        chain rule back through the map."""
+        b, o, w = self.b, self.opts, self.w
+        IDENT = b.LA_FEATURE_IDENTITY
+        lib, st = b.load(), b._stream(None)
+        B, H, N, D, C = w.B, w.H, w.N, w.D, w.features
+        code = b.dtype_code(self.dt)
+        for x, f in ((q, self.fq), (k, self.fk)):
+            if w.fmap == "random":
+                b._check(lib.la_feature_random(b._ptr(x), b._ptr(self.W), b._ptr(f), B, H, N, D, C, code, st),
+                         "la_feature_random")
+            else:
+                b._check(lib.la_feature_poly2(b._ptr(x), b._ptr(f), B, H, N, D, C, code, st), "la_feature_poly2")
+        b.la_forward_causal(self.fq, self.fk, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f, feature=IDENT, opts=o)
+        b.la_backward_causal(self.fq, self.fk, v, self.o, self.den, do, self.dfq, self.dfk, self.dv, ckpt=self.ck,
+                             ws=self.ws_b, feature=IDENT, opts=o)
+        for x, g, dx in ((q, self.dfq, self.dq), (k, self.dfk, self.dk)):
+            if w.fmap == "random":
+                b._check(lib.la_feature_random_vjp(b._ptr(x), b._ptr(self.W), b._ptr(g), b._ptr(dx), B, H, N, D, C,
+                                                   code, st), "la_feature_random_vjp")
+            else:
+                b._check(lib.la_feature_poly2_vjp(b._ptr(x), b._ptr(g), b._ptr(dx), B, H, N, D, C, code, st),
+                         "la_feature_poly2_vjp")
 
     def _fwd_bwd(self, q, k, v, do):
         b, o = self.b, self.opts
@@ -370,6 +386,8 @@ def step_work(wl, w, s):
     passes = {"mnist": ("fwd", "bwd", "fwd_nc"), "small": ("fwd",), "speech": ("fwd_nc", "bwd")}.get(
         wl, ("fwd", "bwd"))
     byts = th * sum(pb[p] for p in passes)
+    if w.features:  # the map of Q and K (read X, write Phi) and its chain rule (read X and dPhi, write dX)
+        byts += th * 2 * ((w.D + w.features) + (2 * w.D + w.features)) * s
     if wl == "speech":  # non-causal backward reads Q, K, V, dO and writes dQ, dK, dV
         D, M = w.D, w.M
         byts = th * (pb["fwd_nc"] + (4 * D + 3 * M) * s)
@@ -398,7 +416,19 @@ def kernel_bytes(name, w, s):
         "dla_fix": 8,                            # read and write dlogA
         "feat_rf": (Din + D) * s,                # read X; write Phi
         "feat_rf_vjp": (2 * Din + D) * s,        # read X, dPhi; write dX
+        "feat_rf_vjp_wide": (2 * Din + D) * s,   # read X, dPhi; write dX
+        "feat_poly2": (Din + D) * s,             # read X; write Phi
+        "feat_poly2_wide": (Din + D) * s,        # read X; write Phi
+        "feat_poly2_vjp": (2 * Din + D) * s,     # read X, dPhi; write dX
+        "feat_poly2_vjp_wide": (2 * Din + D) * s,  # read X, dPhi; write dX
     }
+    ns = D // 64 if D > 64 else 1
+    per_th.update({  # wide feature vectors: the sums over the ns slices (shares written by the slice kernels)
+        "wide_combine": ns * (M + 1) * 4 + M * s + 4,  # read the shares; write O, den
+        "bwd_query_shares": (2 * D + 2 * M) * s,  # read Q, K, V, dO (shares of num.dO, den: ns * 8 written)
+        "wide_pairs": ns * 8 + 8,                # read the shares; write (1/den, O.dO)
+        "wide_sum": ns * M * 4 + M * s,          # read dV shares; write dV
+    })
     if name == "decode":
         return decode_step_bytes(w, s)
     if name in per_th:
@@ -415,7 +445,7 @@ def dominant_bytes(wl, name, w, s):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("la_device.h", "la_kernels.h", "la_decay.h", "la_feature.h", "la_api.hip"):
+    for f in ("la_device.h", "la_kernels.h", "la_decay.h", "la_feature.h", "la_bwd2.h", "la_wide.h", "la_api.hip"):
         with open(os.path.join(ROOT, "linear_rnn_layers_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -744,22 +774,30 @@ def cpu_baseline(wl, w):
                 "cores": oracle.num_threads(), "kind": "oracle",
                 "sample": f"{steps} steps on {nheads} of {w.B * w.H} heads, scaled to all heads"}
     B, H, N = w.B, w.H, w.N
-    nb = {"mnist": 4, "cifar": 1, "long": 1, "long-decay": 1, "mnist-rf": 4, "speech": 4, "small": 1}[wl]
-    nh = {"mnist": H, "cifar": 8, "long": 2, "long-decay": 2, "mnist-rf": H, "speech": H, "small": 1}[wl]
+    nb = {"mnist": 4, "cifar": 1, "long": 1, "long-decay": 1, "mnist-rf": 4, "mnist-rf256": 2, "cifar-poly2": 1,
+          "speech": 4, "small": 1}[wl]
+    nh = {"mnist": H, "cifar": 8, "long": 2, "long-decay": 2, "mnist-rf": H, "mnist-rf256": H, "cifar-poly2": 2,
+          "speech": H, "small": 1}[wl]
     n = {"long": 16384, "long-decay": 8192}.get(wl, N)
     q, k, v = (a[:nb, :nh, :n] for a in w.qkv(n=n))
     do = w.grad_out(n=n)[:nb, :nh, :n]
     la = w.log_a(n=n)[:nb, :nh, :n] if wl == "long-decay" else None
-    wp = w.projection() if wl == "mnist-rf" else None
+    wp = w.projection() if w.features and w.fmap == "random" else None
     reps = 0
     t = time.perf_counter()
     while True:
-        if wl == "mnist-rf":
+        if w.features and w.fmap == "random":
             fq, fk = oracle.feature_performer(q, wp[:nh]), oracle.feature_performer(k, wp[:nh])
             oracle.forward_causal(fq, fk, v, feature=1)
             dfq, dfk, _ = oracle.backward_causal(fq, fk, v, do, feature=1)
             oracle.feature_performer_vjp(q, wp[:nh], dfq)
             oracle.feature_performer_vjp(k, wp[:nh], dfk)
+        elif w.features:
+            fq, fk = oracle.feature_poly2(q, w.features), oracle.feature_poly2(k, w.features)
+            oracle.forward_causal(fq, fk, v, feature=1)
+            dfq, dfk, _ = oracle.backward_causal(fq, fk, v, do, feature=1)
+            oracle.feature_poly2_vjp(q, dfq)
+            oracle.feature_poly2_vjp(k, dfk)
         elif wl == "long-decay":
             oracle.forward_decay(q, k, v, la)
             oracle.backward_decay(q, k, v, la, do)
@@ -835,6 +873,58 @@ def headline_parity(step, heads=(0, 15)):
             **{k: round(v, 6) for k, v in out.items()}}
 
 
+def feature_parity(step, heads=(0,)):
+    """A feature-map step against the oracle on sampled heads of the first batch entry, each stage at its own
+    inputs: the map of the stored inputs, the attention (O, the feature gradients, dV) on the features the library
+    produced, the chain rule on the feature gradients it produced.  The query-side feature gradient is floored at
+    1e-2 of its numerator term |S_i g_i|, as in the parity tests."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    w, b = step.w, step.b
+    q, k, v, do = step.sets[0]
+    step._features_step(q, k, v, do)
+    torch.cuda.synchronize()
+    C = w.features
+
+    def host(t, h):
+        x = t[:1, h:h + 1].float().cpu().numpy().astype(np.float64)
+        if x.ndim == 5:  # feature-sliced [1, 1, ns, N, 64] -> [1, 1, N, C]
+            x = x.transpose(0, 1, 3, 2, 4).reshape(1, 1, x.shape[3], -1)
+        return x
+
+    out = {}
+    for h in heads:
+        qh, kh, vh, dh = (host(t, h) for t in (q, k, v, do))
+        if w.fmap == "random":
+            wp = step.W[h:h + 1].cpu().numpy().astype(np.float64)
+            fmap = lambda x: oracle.feature_performer(x, wp)  # noqa: E731
+            fvjp = lambda x, g: oracle.feature_performer_vjp(x, wp, g)  # noqa: E731
+        else:
+            fmap = lambda x: oracle.feature_poly2(x, C)  # noqa: E731
+            fvjp = oracle.feature_poly2_vjp
+        fq, fk, dfq, dfk = (host(t, h) for t in (step.fq, step.fk, step.dfq, step.dfk))
+        o, den, _, _ = oracle.forward_causal(fq, fk, vh, feature=1)
+        rq, rk, rv = oracle.backward_causal(fq, fk, vh, dh, feature=1)
+        sq = oracle.numerator_backward(fq[0, 0], fk[0, 0], vh[0, 0], dh[0, 0] / den[0, 0][:, None])[0][None, None]
+        floor = 1e-2 * np.abs(sq).max(-1)
+        errs = {"Phi": max(_rowerr(fq, fmap(qh)), _rowerr(fk, fmap(kh))), "O": _rowerr(host(step.o, h), o),
+                "den": _rowerr(host(step.den, h), den, True), "dPhiK": _rowerr(dfk, rk),
+                "dV": _rowerr(host(step.dv, h), rv),
+                "dQ": _rowerr(host(step.dq, h), fvjp(qh, dfq)), "dK": _rowerr(host(step.dk, h), fvjp(kh, dfk))}
+        d = np.abs(dfq - rq).max(-1)
+        yn = np.maximum(np.abs(rq).max(-1), 1e-3 * np.abs(rq).max())
+        errs["dPhiQ"] = float((d / np.maximum(yn, floor)).max())
+        for key, val in errs.items():
+            out[key] = max(out.get(key, 0.0), val)
+    return {"heads": list(heads), "batch_entries": [0], "tokens": w.N, "features": C,
+            "measure": "rowerr, each stage at its own inputs (the library's features into the attention, its "
+                       "feature gradients into the chain rule)", "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4,
+            **{k: round(v, 6) for k, v in out.items()}}
+
+
 # -------------------------------------------------------------- measuring
 def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     """One record: exactly `steps` timed steps after `warmup` untimed ones, the dominant kernel's launches
@@ -878,6 +968,8 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     else:
         metric = {"speech": "non-causal linear-attn fwd+bwd tokens/s",
                   "mnist-rf": "random-feature causal linear-attn fwd+bwd tokens/s",
+                  "mnist-rf256": "random-feature causal linear-attn fwd+bwd tokens/s",
+                  "cifar-poly2": "degree-2 polynomial-feature causal linear-attn fwd+bwd tokens/s",
                   "long-decay": "decayed causal linear-attn fwd+bwd tokens/s",
                   "small": "causal linear-attn fwd tokens/s"}.get(wl, "causal linear-attn fwd+bwd tokens/s")
         unit, value = "tokens/s", w.B * w.N * steps / el
@@ -924,10 +1016,16 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
                          "launches_per_step": (v["calls"] / tot) if tot else None}
                      for k, v in ks["kernels"].items()}
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "M": w.M}
+    if w.features:
+        cfg["C"] = w.features
     cfg["step"] = {"mnist": "causal forward + causal backward + non-causal forward",
                    "cifar": "16 layers x (causal forward + backward)", "long": "causal forward + backward",
                    "long-decay": "decayed causal forward + backward (dQ, dK, dV, dlogA)",
                    "mnist-rf": "random features of Q, K (C = 64) + causal forward and backward on them + chain rule",
+                   "mnist-rf256": "random features of Q, K (C = 256, feature-sliced) + causal forward and backward on "
+                                  "them + chain rule",
+                   "cifar-poly2": "degree-2 polynomial features of Q, K (Din = 32, C = 1088, feature-sliced) + causal "
+                                  "forward and backward on them + chain rule",
                    "speech": "9 layers x (non-causal forward + backward)",
                    "small": "causal forward"}.get(wl, "one decode step of all B*H heads after the prefill")
     if args.segment_chunks:
@@ -945,6 +1043,8 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
         rec["memory"] = memory_report(step)
         if not args.no_parity and wl in ("long", "mnist", "cifar"):
             rec["parity"] = headline_parity(step, (0, w.H - 1) if wl == "long" else (0,))
+    if not args.no_parity and w.features:
+        rec["parity"] = feature_parity(step)
     if wl == "decode" and not eager and not args.no_kernel_events:
         # the same steps launched one at a time from the host (the decode kernel timed per launch)
         del step

@@ -185,9 +185,8 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype,
  * bound; no per-token state S_i is ever stored ("Transformers are RNNs --
  * part 2/3", section 3.3.1).  The decayed recurrence (logA given) uses
  * longer segments and at most this many bytes.  For wide feature vectors
- * (D > 64) the states are those of the D/64 feature slices of every head,
- * followed by float32 O and den of every token (what the backward needs of
- * the whole head: each slice sees only its share of the denominator). */
+ * (D > 64) the states are those of the D/64 feature slices of every head
+ * (the same memory as the heads' states). */
 size_t la_checkpoint_size(int B, int H, int N, int D, int M,
                           const la_options *opts);
 

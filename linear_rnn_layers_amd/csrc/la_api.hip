@@ -150,15 +150,15 @@ size_t state_bytes(const Plan& p, long entries) { return align256((size_t)p.BH *
 // Workspace regions (bytes) per operation.
 struct WsLayout {
   size_t agg = 0, ckpt = 0, ragg = 0, rpref = 0, dlam = 0, gc = 0, xseg = 0, sync = 0;
-  size_t pn = 0, pd = 0, o32 = 0;  // wide feature vectors: the slices' shares, float32 O and den
-  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg + sync + pn + pd + o32; }
+  size_t pn = 0, pd = 0;  // wide feature vectors: the slices' shares
+  size_t bytes() const { return agg + ckpt + ragg + rpref + dlam + gc + xseg + sync + pn + pd; }
 };
 
-// Wide feature vectors: per slice head, the share of the numerators
-// ([N][M]) and of the denominators ([N]); per value head, float32 O and den.
+// Wide feature vectors, per slice head: the share of the numerators ([N][M];
+// in the backward, of dV), and of the denominators ([N]; in the backward, the
+// pair of shares that forms (1/den, O.dO), [N] float2).
 size_t wide_pn(const Plan& p) { return align256((size_t)p.BH * p.N * p.M * sizeof(float)); }
-size_t wide_pd(const Plan& p) { return align256((size_t)p.BH * p.N * sizeof(float)); }
-size_t wide_o32(const Plan& p) { return align256((size_t)p.BHv() * p.N * (p.M + 1) * sizeof(float)); }
+size_t wide_pd(const Plan& p, size_t per) { return align256((size_t)p.BH * p.N * per); }
 
 // fwd causal: aggregates and prefix states when there is more than one
 //   segment (the prefix states go to the caller's checkpoint when given and
@@ -171,8 +171,8 @@ size_t wide_o32(const Plan& p) { return align256((size_t)p.BHv() * p.N * (p.M + 
 //   segment, and the per-token pair (1/den, O.dO) passed from the query
 //   pass to the key pass.
 // Wide feature vectors add the slices' shares of the forward's numerators and
-// denominators (and, in the backward, of dV, in the same space), and in the
-// backward float32 O and den when the checkpoint has to be recomputed.
+// denominators, and in the backward those of dV and of the pair (1/den,
+// O.dO).
 WsLayout ws_layout(int op, const Plan& p) {
   WsLayout w;
   if (p.nseg == 0) return w;
@@ -186,7 +186,7 @@ WsLayout ws_layout(int op, const Plan& p) {
       }
       if (wide) {
         w.pn = wide_pn(p);
-        w.pd = wide_pd(p);
+        w.pd = wide_pd(p, sizeof(float));
       }
       break;
     case LA_OP_FWD_NONCAUSAL:
@@ -194,7 +194,7 @@ WsLayout ws_layout(int op, const Plan& p) {
       w.ckpt = state_bytes(p, p.nseg + 1);
       if (wide) {
         w.pn = wide_pn(p);
-        w.pd = wide_pd(p);
+        w.pd = wide_pd(p, sizeof(float));
       }
       break;
     case LA_OP_BWD_CAUSAL:
@@ -203,9 +203,8 @@ WsLayout ws_layout(int op, const Plan& p) {
       if (p.nseg > 1) w.ragg = state_bytes(p, p.nseg);
       w.gc = align256((size_t)p.BHv() * p.N * 2 * sizeof(float));  // (1/den, O.dO) per token
       if (wide) {
-        w.pn = wide_pn(p);    // dV shares (and the numerators' when recomputing)
-        w.pd = wide_pd(p);    // checkpoint recomputation only
-        w.o32 = wide_o32(p);  // checkpoint recomputation only
+        w.pn = wide_pn(p);                     // dV shares
+        w.pd = wide_pd(p, 2 * sizeof(float));  // shares of (num . dO, den)
       }
       break;
     case LA_OP_BWD_NONCAUSAL:  // key aggregates and their scan; reverse aggregates and their scan
@@ -623,13 +622,8 @@ int decode_impl(long BH, const void* q, const void* k, const void* v, const floa
 // ------------------------------------------------- wide feature vectors
 // Feature slices run as 64-feature heads of the chunked kernels (la_wide.h);
 // the sums over slices follow.  The checkpoint of a wide forward is the
-// slices' states followed by float32 O and den of every value head (what the
-// backward needs of the whole head).
-size_t ckpt_states_bytes(const Plan& p) { return state_bytes(p, p.nseg + 1); }
-size_t ckpt_bytes(const Plan& p) {
-  if (p.ns == 1) return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float);
-  return ckpt_states_bytes(p) + wide_o32(p);
-}
+// slices' states (S [B,H,D,M] is the same memory as [B H ns, 64, M]).
+size_t ckpt_bytes(const Plan& p) { return (size_t)p.BH * (p.nseg + 1) * p.SV * sizeof(float); }
 
 template <int M>
 dim3 token_grid(long rows) { return dim3((unsigned)((rows * (M / 4) + la::NT - 1) / la::NT)); }
@@ -675,12 +669,9 @@ int fwd_wide_impl(const Plan& p, bool causal, const void* Q, const void* K, cons
                 (const T*)V, (T*)nullptr, pden, pref, (const float*)agg, (const float*)nullptr,
                 (const float*)nullptr, (float*)nullptr, S_out, Z_out, N, p.L, p.nseg, fm, p.ns, pnum);
   if (st) return st;
-  float* o32 = causal && ckpt ? reinterpret_cast<float*>(reinterpret_cast<char*>(ckpt) + ckpt_states_bytes(p))
-                              : nullptr;
-  float* d32 = o32 ? o32 + (size_t)p.BHv() * N * M : nullptr;
   const long rows = p.BHv() * N;
   return launch("wide_combine", la::k_wide_combine<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pnum,
-                (const float*)pden, (T*)O, den, o32, d32, rows, N, p.ns);
+                (const float*)pden, (T*)O, den, rows, N, p.ns);
 }
 
 template <typename T, int M>
@@ -695,37 +686,29 @@ int bwd_wide_impl(const Plan& p, const void* Q, const void* K, const void* V, co
   float* ragg = p.nseg > 1 ? reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt)) : nullptr;
   float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
   float* pn = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc));
-  float* pd = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc + wl.pn));
+  float2* sh = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc + wl.pn));
   const long rows = p.BHv() * N;
   const dim3 grid((unsigned)(p.BH * p.nseg));
   int st = LA_OK;
   const float* ck = ckpt;
-  const float* o32 = nullptr;
-  if (ck) {
-    o32 = reinterpret_cast<const float*>(reinterpret_cast<const char*>(ck) + ckpt_states_bytes(p));
-  } else {  // recompute the checkpoint: the slices' states, then float32 O and den of the forward
+  if (!ck) {  // recompute the checkpoint: the slices' aggregates, then their scan
     float* agg = reinterpret_cast<float*>(region(ws, 0));
     float* ckw = reinterpret_cast<float*>(region(ws, wl.agg));
-    float* o32w = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.gc + wl.pn + wl.pd));
     st = seg_aggregates<T, 64, M>(p, K, V, agg, N, fm, s);
     if (st) return st;
     st = scan_prefix<64, M>(p, agg, S0, Z0, ckw, s);
     if (st) return st;
-    st = launch("fwd_causal", la::k_fwd<T, 64, M, true, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K,
-                (const T*)V, (T*)nullptr, pd, (const float*)ckw, (const float*)nullptr, S0, Z0, (float*)nullptr,
-                (float*)nullptr, (float*)nullptr, N, p.L, p.nseg, fm, p.ns, pn);
-    if (st) return st;
-    st = launch("wide_combine", la::k_wide_combine<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pn,
-                (const float*)pd, (T*)nullptr, (float*)nullptr, o32w, o32w + (size_t)rows * M, rows, N, p.ns);
-    if (st) return st;
     ck = ckw;
-    o32 = o32w;
   }
-  st = launch("wide_pairs", la::k_wide_pairs<T, M>, token_grid<M>(rows), dim3(la::NT), s, o32,
-              o32 + (size_t)rows * M, (const T*)dO, gc, rows);
+  // every slice's shares of (num . dO, den), their sums per token, then the query pass proper
+  st = launch("bwd_query_shares", la::k_bq<T, 64, M, la::kBqShares>, grid, dim3(la::NT), s, (const T*)Q,
+              (const T*)K, (const T*)V, (const T*)dO, ck, (T*)nullptr, sh, (float*)nullptr, N, p.L, p.nseg, fm, p.ns);
   if (st) return st;
-  st = launch("bwd_query", la::k_bq<T, 64, M, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
-              (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm, p.ns);
+  st = launch("wide_pairs", la::k_wide_pairs, dim3((unsigned)((rows + la::NT - 1) / la::NT)), dim3(la::NT), s,
+              (const float2*)sh, gc, rows, N, p.ns);
+  if (st) return st;
+  st = launch("bwd_query", la::k_bq<T, 64, M, la::kBqGiven>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K,
+              (const T*)V, (const T*)dO, ck, (T*)dQ, gc, ragg, N, p.L, p.nseg, fm, p.ns);
   if (st) return st;
   const int scanned = p.nseg > 1 && use_scan(p) ? 1 : 0;
   if (scanned) {
@@ -949,8 +932,8 @@ const char* la_last_error(void) { return g_err.c_str(); }
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,bwd_query,bwd_kv,nc_qr,nc_kv,decode,scan_states,scan_rev,"
          "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
-         "feat_poly2_vjp,sync_clear,wide_combine,wide_pairs,wide_sum,decode_wide,feat_rf_vjp_wide,feat_poly2_wide,"
-         "feat_poly2_vjp_wide";
+         "feat_poly2_vjp,sync_clear,wide_combine,bwd_query_shares,wide_pairs,wide_sum,decode_wide,feat_rf_vjp_wide,"
+         "feat_poly2_wide,feat_poly2_vjp_wide";
 }
 
 size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype, const la_options* opts) {

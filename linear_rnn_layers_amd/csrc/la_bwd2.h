@@ -89,11 +89,18 @@ __device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, 
 }
 
 // ===================================================================== B-A
-// GIVEN (feature slices, ns per value head, la_wide.h): a slice sees only its
-// share of den_i and of num_i . dO_i, so the pair (1/den_i, O_i . dO_i) of
-// value head bh / ns is read from gc (formed from the whole head's float32
-// outputs) instead of recomputed and written.
-template <typename T, int D, int M, bool GIVEN = false>
+// Feature slices (ns per value head, la_wide.h) see only their shares of
+// den_i = phi(Q_i) . Z_i and of num_i . dO_i = phi(Q_i)^T S_i dO_i, so a wide
+// head runs this pass twice:
+//   kBqShares  the slice's two shares of token i go to gc[bh][i] (as a float2)
+//              and nothing else is written;
+//   kBqGiven   the pair (1/den_i, O_i . dO_i) of value head bh / ns, formed
+//              from the sums of those shares, is read from gc instead of
+//              recomputed and written.
+// The pair is then exactly what a single head of all the features computes:
+// the same states and products, summed over the slices.
+constexpr int kBqFull = 0, kBqGiven = 1, kBqShares = 2;
+template <typename T, int D, int M, int MODE = kBqFull>
 __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __restrict__ K,
                                             const T* __restrict__ V, const T* __restrict__ dO,
                                             const float* __restrict__ ckpt, T* __restrict__ dQ,
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
-  const int vh = GIVEN ? bh / ns : bh;  // value head
+  const int vh = MODE != kBqFull ? bh / ns : bh;  // value head
   const size_t offD = (size_t)bh * N * D, offM = (size_t)vh * N * M;
   const Frag<1> ones = ones_frag();
   ot.zero_cols(M + 2, M + 16);
@@ -236,8 +243,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         ZC[d0] += f32x4_t{z4.x, z4.y, z4.z, z4.w};  // U: S_i dO_i [d][i], ZC: Z_i [d][i]
       }
       float qv[DB][4];
-      float invz, odo;
-      if constexpr (GIVEN) {
+      float invz = 0.f, odo = 0.f;
+      if constexpr (MODE == kBqGiven) {
 #pragma unroll
         for (int d0 = 0; d0 < DB; ++d0) qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
         const float2 pr = row_ok ? gc[(size_t)vh * N + c0 + il] : make_float2(0.f, 0.f);
@@ -256,29 +263,36 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         }
         pu = sum_over_g(pu);  // phi(Q_i)^T S_i dO_i = num_i . dO_i
         pz = sum_over_g(pz);  // phi(Q_i) . Z_i = den_i
-        invz = row_ok ? 1.f / pz : 0.f;
-        odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
-      }
-#pragma unroll
-      for (int d0 = 0; d0 < DB; ++d0) {
-        float o[4], qs[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
-          qs[r] = qv[d0][r] * invz;
+        if constexpr (MODE == kBqShares) {
+          if (g == 0 && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(pu, pz);
+        } else {
+          invz = row_ok ? 1.f / pz : 0.f;
+          odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
         }
-        if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
-        qt.put4(il, 16 * d0 + 4 * g, qs);  // this lane's own elements of its own row: q'_i
       }
-      if (g == 0) {
-        if (!GIVEN && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
-        put_neg_odo(ot, il, M, odo);
+      if constexpr (MODE != kBqShares) {
+#pragma unroll
+        for (int d0 = 0; d0 < DB; ++d0) {
+          float o[4], qs[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            o[r] = (U[d0][r] - ZC[d0][r] * odo) * invz * dfeat(qv[d0][r], fm);
+            qs[r] = qv[d0][r] * invz;
+          }
+          if (row_ok) IO<T>::store4(dQ + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g, o);
+          qt.put4(il, 16 * d0 + 4 * g, qs);  // this lane's own elements of its own row: q'_i
+        }
+        if (g == 0) {
+          if (MODE == kBqFull && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(invz, odo);
+          put_neg_odo(ot, il, M, odo);
+        }
       }
     }
-    __syncthreads();
+    // (the shares pass writes nothing that the state update reads: no barrier)
+    if constexpr (MODE != kBqShares) __syncthreads();
 
     // ================ the chunk's share of the reverse aggregate, then the state update
-    rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
+    if constexpr (MODE != kBqShares) rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
     constexpr int NKB = cmax(P::dS_b, P::Zc);
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   }
   // the segment's reverse aggregate (sum over its tokens of phi(Q_i) g_i^T, c_i phi(Q_i)), [d][m] then r, for the
   // segments before it; segment 0's is not needed
-  if (seg > 0) {
+  if (MODE != kBqShares && seg > 0) {
     float* out = ragg + ((size_t)bh * nseg + seg) * SV;
 #pragma unroll
     for (int k = 0; k < NTR; ++k) {

@@ -24,8 +24,6 @@
 // an all-ones operand, the form of eq. 14-15 on [V, 1].
 #pragma once
 
-#include <type_traits>
-
 #include "la_device.h"
 
 namespace la {

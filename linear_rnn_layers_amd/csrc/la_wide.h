@@ -20,8 +20,14 @@
 //             den_i (eq. 9-12 with phi(q_i) . S_i split over the features);
 //   backward: dV_j = sum_s (R^(s)_j)^T phi^(s)(K_j) + ... (eq. 15);
 // while dphi(Q) and dphi(K) (eq. 13-14) are slice-local once the pair
-// (1/den_i, O_i . dO_i) of the whole head is known: it is formed here from
-// the forward's float32 O and den, which the forward keeps in the checkpoint.
+// (1/den_i, O_i . dO_i) of the whole head is known.  That pair is formed as
+// the 64-feature heads form it, from the backward's own states: a first query
+// pass writes every slice's shares phi(Q_i)^T S_i dO_i and phi(Q_i) . Z_i
+// (la_bwd2.h, kBqShares), and their sums give den_i and O_i . dO_i = (sum of
+// the first) / den_i, consistent with the S_i dO_i and Z_i that the
+// quotient rule then cancels against each other (taking O_i . dO_i from the
+// forward's O instead would leave the two sides of that cancellation with
+// independent rounding).
 #pragma once
 
 #include "la_feature.h"
@@ -30,13 +36,11 @@ namespace la {
 
 // --------------------------------------------------------------- combine
 // O_i = sum_s pnum[bh ns + s][i] / sum_s pden[bh ns + s][i] for the B H N
-// tokens; M / 4 threads per token, four values each.  O (storage type), den
-// (float32), o32 / d32 (float32 copies for the backward) are each optional.
+// tokens; M / 4 threads per token, four values each.  den is optional.
 template <typename T, int M>
 __global__ __launch_bounds__(NT) void k_wide_combine(const float* __restrict__ pnum, const float* __restrict__ pden,
-                                                      T* __restrict__ O, float* __restrict__ den,
-                                                      float* __restrict__ o32, float* __restrict__ d32, long rows,
-                                                      int N, int ns) {
+                                                      T* __restrict__ O, float* __restrict__ den, long rows, int N,
+                                                      int ns) {
   constexpr int QPT = M / 4;
   const long id = (long)blockIdx.x * NT + threadIdx.x;
   const long tok = id / QPT;
@@ -58,34 +62,27 @@ __global__ __launch_bounds__(NT) void k_wide_combine(const float* __restrict__ p
   }
   const float inv = 1.f / d;
   float o[4] = {a.x * inv, a.y * inv, a.z * inv, a.w * inv};
-  if (O) IO<T>::store4(O + (size_t)tok * M + m0, o);
-  if (o32) *reinterpret_cast<float4*>(o32 + (size_t)tok * M + m0) = make_float4(o[0], o[1], o[2], o[3]);
-  if (m0 == 0) {
-    if (den) den[tok] = d;
-    if (d32) d32[tok] = d;
-  }
+  IO<T>::store4(O + (size_t)tok * M + m0, o);
+  if (den && m0 == 0) den[tok] = d;
 }
 
-// gc[i] = (1 / den_i, O_i . dO_i) from the float32 O and den; M / 4 threads
-// per token (aligned groups of a wavefront) reduce the dot product.
-template <typename T, int M>
-__global__ __launch_bounds__(NT) void k_wide_pairs(const float* __restrict__ o32, const float* __restrict__ d32,
-                                                    const T* __restrict__ dO, float2* __restrict__ gc, long rows) {
-  constexpr int QPT = M / 4;
-  const long id = (long)blockIdx.x * NT + threadIdx.x;
-  const long tok = id / QPT;
-  const bool ok = tok < rows;
-  const int m0 = 4 * (int)(id % QPT);
-  float dot = 0.f;
-  if (ok) {
-    const float4 o = *reinterpret_cast<const float4*>(o32 + (size_t)tok * M + m0);
-    float g[4];
-    IO<T>::load4(dO + (size_t)tok * M + m0, g);
-    dot = o.x * g[0] + o.y * g[1] + o.z * g[2] + o.w * g[3];
+// gc[i] = (1 / den_i, O_i . dO_i) from the slices' shares sh[bh ns + s][i] =
+// (phi^(s)(Q_i)^T S_i^(s) dO_i, phi^(s)(Q_i) . Z_i^(s)), summed in slice order;
+// one thread per token.
+__global__ __launch_bounds__(NT) void k_wide_pairs(const float2* __restrict__ sh, float2* __restrict__ gc, long rows,
+                                                    int N, int ns) {
+  const long tok = (long)blockIdx.x * NT + threadIdx.x;
+  if (tok >= rows) return;
+  const long bh = tok / N, n = tok % N;
+  const float2* p = sh + (size_t)bh * ns * N + n;
+  float u = 0.f, z = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float2 x = p[(size_t)s * N];
+    u += x.x;
+    z += x.y;
   }
-#pragma unroll
-  for (int off = 1; off < QPT; off <<= 1) dot += __shfl_xor(dot, off, 64);
-  if (ok && m0 == 0) gc[tok] = make_float2(1.f / d32[tok], dot);
+  const float inv = 1.f / z;
+  gc[tok] = make_float2(inv, u * inv);
 }
 
 // dV_j = sum_s pdv[bh ns + s][j] into the storage type.

@@ -78,7 +78,8 @@ class Workload:
     steps: int = 0  # decode steps (decode workload only)
     gate_seed: int = 0  # decayed workloads: seed of the per-token gates
     gate_bias: float = 3.0
-    features: int = 0  # random-feature workloads: number of features C (projection seed seeds[0] + 50)
+    features: int = 0  # feature-map workloads: number of features C (random: projection seed seeds[0] + 50)
+    fmap: str = "random"  # feature map of the feature-map workloads: "random" or "poly2" (degree 2)
 
     def projection(self):
         """Random projection W [H, C, D] ~ N(0, 1) float32 for the random-feature workloads."""
@@ -152,7 +153,17 @@ LONG_DECAY = Workload("long-decay-b1h16n65536d64-bf16", 1, 16, 65536, 64, 64, BF
 # by 32^(-1/4) (the temperature of the softmax kernel exp(q.k / sqrt(d)) that the features estimate).
 MNIST_RF = Workload("mnist-random-features-b16h8n784d32c64-f32", 16, 8, 784, 32, 32, F32, 32 ** -0.25,
                     (241, 242, 243, 244), features=64)
+# The same layer with 256 positive random features: four 64-feature slices per head.
+MNIST_RF256 = Workload("mnist-random-features-b16h8n784d32c256-f32", 16, 8, 784, 32, 32, F32, 32 ** -0.25,
+                       (251, 252, 253, 254), features=256)
+# One layer of the CIFAR-shaped stack with the degree-2 polynomial map of its 32-wide heads in place of elu + 1:
+# C = 1 + 32 + 32^2 = 1057 features, zero-padded to 1088 (17 slices of 64); the quadratic cost in D pays off once
+# N exceeds D^2 = 1024 ("Transformers are RNNs -- part 2/3", section 3.2.1).  Queries and keys scaled by
+# 32^(-1/4), as for the random features.
+CIFAR_POLY2 = Workload("cifar-poly2-b4h8n3072d32c1088-bf16", 4, 8, 3072, 32, 32, BF16, 32 ** -0.25,
+                       (3100, 3101, 3102, 3103), features=1088, fmap="poly2")
 DECODE = Workload("decode-b256h16d64-4096steps-bf16", 256, 16, 512, 64, 64, BF16, 1.0, (501, 502, 503, 504),
                   steps=4096)
 
-WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, LONG_DECAY, MNIST_RF, DECODE)}
+WORKLOADS = {w.name: w for w in (SMALL, MNIST, CIFAR, LONG, SPEECH, LONG_DECAY, MNIST_RF, MNIST_RF256, CIFAR_POLY2,
+                                  DECODE)}

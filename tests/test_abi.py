@@ -367,23 +367,21 @@ def test_binding_checks_tensor_agreement():
                                         (1, 1, 1, 4096, 64), (1, 2, 5000, 192, 64)])
 def test_wide_plan_and_sizes(lib, B, H, N, C, M):
     """Wide feature vectors (C = 64 ns): the plan of the B*H*ns feature slices as 64-feature heads; the
-    checkpoint holds the slices' states and then float32 O and den of every head; the workspaces add the
-    slices' shares of the numerators and denominators (the forward) and of dV (the backward, which also keeps
-    room for float32 O and den when it recomputes the checkpoint)."""
+    checkpoint holds the slices' states; the workspaces add the slices' shares of the numerators and
+    denominators (the forward), and of dV and of the pair (num . dO, den) per token (the backward)."""
     ns = C // 64
     L, nseg = _plan(B, H * ns, N, D=64, M=M)
     assert lib.la_segment_length(B, H, N, C, M, None) == L
     sv = 64 * M + 64
     bhs = B * H * ns
-    o32 = _al(B * H * N * (M + 1) * 4)
-    assert lib.la_checkpoint_size(B, H, N, C, M, None) == _al(bhs * (nseg + 1) * sv * 4) + o32
+    assert lib.la_checkpoint_size(B, H, N, C, M, None) == bhs * (nseg + 1) * sv * 4
     pn, pd = _al(bhs * N * M * 4), _al(bhs * N * 4)
     agg, pref = _al(bhs * nseg * sv * 4), _al(bhs * (nseg + 1) * sv * 4)
     assert lib.la_workspace_size(0, B, H, N, C, M, 0, None) == (0 if nseg == 1 else agg + pref) + pn + pd
     _, nseg_nc = _plan(B, H * ns, N, 512)
     assert lib.la_workspace_size(1, B, H, N, C, M, 1, None) == (_al(bhs * nseg_nc * sv * 4) +
                                                                 _al(bhs * (nseg_nc + 1) * sv * 4) + pn + pd)
-    bwd = agg + pref + (0 if nseg == 1 else agg) + _al(B * H * N * 8) + pn + pd + o32
+    bwd = agg + pref + (0 if nseg == 1 else agg) + _al(B * H * N * 8) + pn + _al(bhs * N * 8)
     assert lib.la_workspace_size(2, B, H, N, C, M, 0, None) == bwd
     for op in (3, 4, 5, 6):  # decode needs none; no non-causal backward or decayed form for wide features
         assert lib.la_workspace_size(op, B, H, N, C, M, 0, None) == 0
@@ -409,8 +407,8 @@ def test_wide_validation(lib):
     assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 65, 4096, 0, None) == UNSUPPORTED
     assert lib.la_feature_poly2(addr(1), addr(1), 2, 2, 100, 32, 1088, 0, None) == ALIAS
     names = binding.kernel_names()
-    assert all(n in names for n in ("wide_combine", "wide_pairs", "wide_sum", "decode_wide", "feat_rf_vjp_wide",
-                                    "feat_poly2_wide", "feat_poly2_vjp_wide"))
+    assert all(n in names for n in ("wide_combine", "bwd_query_shares", "wide_pairs", "wide_sum", "decode_wide",
+                                    "feat_rf_vjp_wide", "feat_poly2_wide", "feat_poly2_vjp_wide"))
 
 
 def test_binding_feature_sliced_layout():

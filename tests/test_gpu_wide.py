@@ -189,3 +189,48 @@ def test_wide_poly2_features(Din, C, dtype):
     torch.cuda.synchronize()
     assert rowerr(unsl(host(phi)), oracle.feature_poly2(x, C)) <= TOL[dtype]
     assert rowerr(host(dx), oracle.feature_poly2_vjp(x, dphi)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("name", ["mnist-rf256", "cifar-poly2"])
+def test_wide_feature_workloads(name):
+    """The two wide feature-map workloads at full size as the training step runs them: the map of Q and K, the
+    causal attention on the features (checkpointed forward, backward), the chain rule back through the map; each
+    stage against the oracle at its own inputs (random features C = 256: all 16 x 8 heads of 784 tokens; degree-2
+    polynomial Din = 32, C = 1088: the 8 heads of batch entry 0 of 3072 tokens)."""
+    w = inputs.MNIST_RF256 if name == "mnist-rf256" else inputs.CIFAR_POLY2
+    q, k, v = w.qkv()
+    do = w.grad_out()
+    dt = w.dtype
+    Q, K, V, dO = dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt)
+    C = w.features
+    if w.fmap == "random":
+        wp = w.projection()
+        W = dev32(wp)
+        fmap, fvjp = (lambda a: oracle.feature_performer(a, wp)), (lambda a, g: oracle.feature_performer_vjp(a, wp, g))
+        gmap, gvjp = (lambda a: binding.feature_random(a, W)), (lambda a, g: binding.feature_random_vjp(a, W, g))
+    else:
+        fmap, fvjp = (lambda a: oracle.feature_poly2(a, C)), oracle.feature_poly2_vjp
+        gmap, gvjp = (lambda a: binding.feature_poly2(a, C)), binding.feature_poly2_vjp
+    fQ, fK = gmap(Q), gmap(K)
+    out = binding.forward_causal(fQ, fK, V, feature=IDENT)
+    dfq, dfk, dv = binding.backward_causal(fQ, fK, V, out["o"], out["den"], dO, ckpt=out["ckpt"], feature=IDENT)
+    dq, dk = gvjp(Q, dfq), gvjp(K, dfk)
+    torch.cuda.synchronize()
+    nb = w.B if w.fmap == "random" else 1
+    cut = lambda a: np.asarray(a)[:nb]  # noqa: E731
+    hs = lambda t: cut(unsl(host(t))) if t.dim() == 5 else cut(host(t))  # noqa: E731
+    q, k, v, do = cut(q), cut(k), cut(v), cut(do)
+    fq, fk, gq, gk = hs(fQ), hs(fK), hs(dfq), hs(dfk)
+    tol = TOL[dt]
+    assert max(rowerr(fq, fmap(q)), rowerr(fk, fmap(k))) <= tol
+    ro, rden, _, _ = oracle.forward_causal(fq, fk, v, feature=IDENT)
+    rq, rk, rv = oracle.backward_causal(fq, fk, v, do, feature=IDENT)
+    g = np.asarray(do, np.float64) / rden[..., None]
+    u = np.empty(fq.shape)
+    for b in range(fq.shape[0]):
+        for h in range(fq.shape[1]):
+            u[b, h] = oracle.numerator_backward(fq[b, h], fk[b, h], v[b, h], g[b, h])[0]
+    errs = {"O": rowerr(hs(out["o"]), ro), "den": rowerr(hs(out["den"]), rden, False), "dV": rowerr(hs(dv), rv),
+            "dPhiQ": rowerr(gq, rq, row_floor=CANCEL_FLOOR * np.abs(u).max(-1)), "dPhiK": rowerr(gk, rk),
+            "dQ": rowerr(hs(dq), fvjp(q, gq)), "dK": rowerr(hs(dk), fvjp(k, gk))}
+    assert max(errs.values()) <= tol, errs
