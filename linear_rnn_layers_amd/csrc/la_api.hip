@@ -797,22 +797,25 @@ int feat_rf_wide_impl(long BH, int H, int N, int C, const void* X, const float* 
                 ns, sc);
 }
 
-// Wide polynomial features (C = 64 ns, feature-sliced): a workgroup per
-// slice and 64 tokens forward; the vector-Jacobian product stages each
-// token's quadratic block in LDS.
+// Wide polynomial features (C = 64 ns, feature-sliced): a workgroup per 64
+// tokens of a head writes every slice; the vector-Jacobian product stages
+// each token's feature gradient in LDS (as many tokens per workgroup as fit
+// 64 KiB, at most 32).
 template <typename T>
 int feat_poly2_wide_impl(long BH, int N, int din, int C, const void* X, const void* dPhi, void* out, const Call& s) {
   const int ns = C / 64;
   if (dPhi) {
     const long rows = BH * N;
+    const int tpw = std::min(32, (int)(la::kPolyVjpLds / ((size_t)C * sizeof(T))));  // tokens per workgroup
+    const dim3 grid((unsigned)((rows + tpw - 1) / tpw));
     if (din <= 32)
-      return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 32>, dim3((unsigned)((rows + 7) / 8)),
-                    dim3(la::NT), s, (const T*)X, (const T*)dPhi, (T*)out, rows, N, din, ns);
-    return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 64>, dim3((unsigned)((rows + 3) / 4)),
-                  dim3(la::NT), s, (const T*)X, (const T*)dPhi, (T*)out, rows, N, din, ns);
+      return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 32>, grid, dim3(la::NT), s, (const T*)X,
+                    (const T*)dPhi, (T*)out, rows, N, din, ns, tpw);
+    return launch("feat_poly2_vjp_wide", la::k_feat_poly2_vjp_wide<T, 64>, grid, dim3(la::NT), s, (const T*)X,
+                  (const T*)dPhi, (T*)out, rows, N, din, ns, tpw);
   }
   const long ntb = (N + la::CH - 1) / la::CH;
-  return launch("feat_poly2_wide", la::k_feat_poly2_wide<T>, dim3((unsigned)(BH * ns * ntb)), dim3(la::NT), s,
+  return launch("feat_poly2_wide", la::k_feat_poly2_wide<T>, dim3((unsigned)(BH * ntb)), dim3(la::NT), s,
                 (const T*)X, (T*)out, N, din, ns);
 }
 

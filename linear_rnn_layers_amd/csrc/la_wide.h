@@ -306,79 +306,138 @@ __global__ __launch_bounds__(NT) void k_feat_rf_vjp_wide(const T* __restrict__ X
 
 // ------------------------------------------------- polynomial features
 // Feature c of the degree-2 map of x (Din values): 1, then x_1 .. x_Din, then
-// x_a x_b (a-major), then zeros.
-__device__ __forceinline__ float poly2_at(const float* x, int din, int c) {
-  if (c == 0) return 1.f;
-  if (c <= din) return x[c - 1];
-  const int i = c - 1 - din;
-  if (i >= din * din) return 0.f;
-  return x[i / din] * x[i % din];
-}
+// x_a x_b (a-major), then zeros.  (a, b) of a quadratic feature i = c - 1 -
+// Din comes from a float reciprocal: (i + 1/2) / Din lies at least 1 / (2 Din)
+// from an integer, far beyond the rounding of (i + 1/2) * (1/Din) for i <
+// 4096, so the truncation is the exact quotient.
+struct Poly2Index {
+  int din;
+  float rdin;
+  __device__ explicit Poly2Index(int d) : din(d), rdin(1.f / (float)d) {}
+  // kind: 0 the constant, 1 linear (a), 2 quadratic (a, b), 3 padding
+  __device__ __forceinline__ int at(int c, int& a, int& b) const {
+    if (c == 0) return 0;
+    if (c <= din) {
+      a = c - 1;
+      return 1;
+    }
+    const int i = c - 1 - din;
+    if (i >= din * din) return 3;
+    a = (int)(((float)i + 0.5f) * rdin);
+    b = i - a * din;
+    return 2;
+  }
+};
 
-// Slice s of 64 tokens per workgroup: 4 threads per token, 16 features each.
+// 64 tokens of one head per workgroup, every slice: X staged once, each
+// 16-byte vector of the feature-sliced output (8 bf16 or 4 float32 features
+// of one token) formed in registers and written whole.
 template <typename T>
 __global__ __launch_bounds__(NT) void k_feat_poly2_wide(const T* __restrict__ X, T* __restrict__ Phi, int N, int din,
                                                          int ns) {
+  constexpr int E = IO<T>::E;  // features per 16-byte vector
+  constexpr int PR = 64 / E;   // vectors per token row of a slice
   __shared__ float xs[CH][64 + 1];
   const int ntb = (N + CH - 1) / CH;
-  const int bhs = blockIdx.x / ntb, n0 = (blockIdx.x % ntb) * CH;
-  const int bh = bhs / ns, s = bhs % ns;
-  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / ntb, n0 = (blockIdx.x % ntb) * CH;
+  const int tid = threadIdx.x, nrows = min(CH, N - n0);
+  const Poly2Index ix(din);
   for (int e = tid; e < CH * din; e += NT) {
     const int row = e / din, a = e % din;
-    xs[row][a] = n0 + row < N ? ld1(X + ((size_t)bh * N + n0 + row) * din + a) : 0.f;
+    xs[row][a] = row < nrows ? ld1(X + ((size_t)bh * N + n0 + row) * din + a) : 0.f;
   }
   __syncthreads();
-  const int tt = tid >> 2, part = tid & 3;
-  if (n0 + tt >= N) return;
-  T* out = Phi + ((size_t)bhs * N + n0 + tt) * 64 + 16 * part;
+  for (int p = tid; p < ns * CH * PR; p += NT) {
+    const int s = p / (CH * PR), r = p % (CH * PR), tt = r / PR, c0 = 64 * s + (r % PR) * E;
+    if (tt >= nrows) continue;
+    float f[E];
+    // (a, b) of the vector's first quadratic feature from the reciprocal, then stepped along the row
+    const int q0 = c0 - 1 - din;  // index among the quadratic features (negative: the head of the map)
+    int a = 0, b = 0;
+    if (q0 > 0) ix.at(c0, a, b);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float f[4];
+    for (int e = 0; e < E; ++e) {
+      const int c = c0 + e, q = q0 + e;
+      if (q < 0) {
+        f[e] = c == 0 ? 1.f : xs[tt][c - 1];
+      } else {
+        if (q == 0) a = b = 0;
+        f[e] = q < din * din ? xs[tt][a] * xs[tt][b] : 0.f;
+        if (++b == din) {
+          b = 0;
+          ++a;
+        }
+      }
+    }
+    T* out = Phi + (((size_t)bh * ns + s) * N + n0 + tt) * 64 + (r % PR) * E;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = poly2_at(xs[tt], din, 64 * s + 16 * part + 4 * q + e);
-    IO<T>::store4(out + 4 * q, f);
+    for (int q = 0; q < E; q += 4) IO<T>::store4(out + q, f + q);
   }
 }
 
 // dX_a = dPhi_(1 + a) + sum_b (G_ab + G_ba) x_b with G_ab = dPhi_(1 + din + a
-// din + b): 256 / DMAX tokens per workgroup, DMAX threads per token (one per
-// a), each token's G staged in LDS with rows padded to din + 1.
+// din + b): tpw tokens per workgroup (as many as fit a 64 KiB LDS buffer, at
+// most 32).  Each token's feature gradient is copied into LDS as one flat row
+// of C values in 16-byte vectors (slice by slice; each slice's rows of
+// consecutive tokens are contiguous in memory); then DMAX threads per token,
+// one per a, read G's row a (rotated by a, so that the lanes of a wavefront
+// fall in different banks) and column a.
+constexpr int kPolyVjpLds = 64 << 10;
+
 template <typename T, int DMAX>
 __global__ __launch_bounds__(NT) void k_feat_poly2_vjp_wide(const T* __restrict__ X, const T* __restrict__ dPhi,
-                                                             T* __restrict__ dX, long rows, int N, int din, int ns) {
-  constexpr int TPW = NT / DMAX;
-  __shared__ float gs[TPW][DMAX * (DMAX + 1)];
-  __shared__ float ls[TPW][DMAX], xs[TPW][DMAX];
-  const int tid = threadIdx.x;
-  const long tok0 = (long)blockIdx.x * TPW;
-  const int used = 1 + din + din * din;
-  for (int e = tid; e < TPW * used; e += NT) {
-    const int tt = e / used, c = e % used;
-    const long tok = tok0 + tt;
-    if (tok >= rows) continue;
-    const long bh = tok / N, n = tok % N;
-    const float v = ld1(dPhi + (((size_t)bh * ns + c / 64) * N + n) * 64 + c % 64);
-    if (c == 0) continue;
-    if (c <= din) {
-      ls[tt][c - 1] = v;
-    } else {
-      const int i = c - 1 - din;
-      gs[tt][(i / din) * (din + 1) + i % din] = v;
-    }
+                                                             T* __restrict__ dX, long rows, int N, int din, int ns,
+                                                             int tpw) {
+  constexpr int E = IO<T>::E, PR = 64 / E, BATCH = 8, TMAX = 32;
+  __shared__ alignas(16) T flat[kPolyVjpLds / sizeof(T)];
+  __shared__ float xs[TMAX][DMAX];
+  __shared__ long tbase[TMAX];  // element offset of the token's row in slice 0
+  const int tid = threadIdx.x, C = 64 * ns;
+  const long tok0 = (long)blockIdx.x * tpw;
+  const int ntok = (int)min((long)tpw, rows - tok0);
+  if (tid < ntok) {
+    const long tok = tok0 + tid, bh = tok / N, n = tok % N;
+    tbase[tid] = ((long)bh * ns * N + n) * 64;
   }
-  for (int e = tid; e < TPW * din; e += NT) {
+  for (int e = tid; e < ntok * din; e += NT) {
     const int tt = e / din, a = e % din;
-    const long tok = tok0 + tt;
-    xs[tt][a] = tok < rows ? ld1(X + (size_t)tok * din + a) : 0.f;
+    xs[tt][a] = ld1(X + (size_t)(tok0 + tt) * din + a);
   }
   __syncthreads();
-  const int tt = tid / DMAX, a = tid % DMAX;
-  const long tok = tok0 + tt;
-  if (a >= din || tok >= rows) return;
-  float acc = ls[tt][a];
-  for (int b = 0; b < din; ++b) acc += (gs[tt][a * (din + 1) + b] + gs[tt][b * (din + 1) + a]) * xs[tt][b];
-  st1(dX + (size_t)tok * din + a, acc);
+  const int total = ns * ntok * PR;  // 16-byte vectors: (slice, token, vector of the slice row)
+  for (int p0 = tid; p0 < total; p0 += NT * BATCH) {
+    typename IO<T>::raw v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int p = p0 + u * NT;
+      if (p < total) {
+        const int s = p / (ntok * PR), r = p % (ntok * PR), tt = r / PR;
+        v[u] = IO<T>::load_raw(dPhi + tbase[tt] + (size_t)s * N * 64 + (r % PR) * E);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int p = p0 + u * NT;
+      if (p < total) {
+        const int s = p / (ntok * PR), r = p % (ntok * PR), tt = r / PR;
+        *reinterpret_cast<typename IO<T>::raw*>(&flat[tt * C + 64 * s + (r % PR) * E]) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < ntok * DMAX; q += NT) {
+    const int tt = q / DMAX, a = q % DMAX;
+    if (a >= din) continue;
+    const T* f = flat + tt * C;
+    const T* g = f + 1 + din;  // G, row-major din x din
+    float acc = ld1(f + 1 + a);
+    int b = a;  // row a visited from b = a on
+    for (int k = 0; k < din; ++k) {
+      acc += ld1(g + a * din + b) * xs[tt][b] + ld1(g + k * din + a) * xs[tt][k];
+      b = b + 1 == din ? 0 : b + 1;
+    }
+    st1(dX + (size_t)(tok0 + tt) * din + a, acc);
+  }
 }
 
 }  // namespace la
