@@ -472,16 +472,29 @@ KERNEL_TAGS = (("k_bkv<", "bwd_kv"), ("k_bq<", "bwd_query"), ("k_seg_state<", "s
                ("k_nc_qr<", "nc_qr"), ("k_nc_kv<", "nc_kv"), ("k_dseg_state<", "dseg_state"),
                ("k_dscan_states<", "dscan_states"), ("k_dfwd<", "dfwd"), ("k_dbq<", "dbq"),
                ("k_dscan_rev<", "dscan_rev"), ("k_dbkv<", "dbkv"), ("k_dla_fix", "dla_fix"),
-               ("k_feat_rf_vjp<", "feat_rf_vjp"), ("k_feat_rf<", "feat_rf"), ("k_state_copy<", "state_copy"))
+               ("k_feat_rf_vjp<", "feat_rf_vjp"), ("k_feat_rf<", "feat_rf"), ("k_state_copy<", "state_copy"),
+               ("k_wide_combine<", "wide_combine"), ("k_wide_pairs", "wide_pairs"), ("k_wide_sum<", "wide_sum"),
+               ("k_decode_wide<", "decode_wide"), ("k_feat_rf_vjp_wide<", "feat_rf_vjp_wide"),
+               ("k_feat_poly2_vjp_wide<", "feat_poly2_vjp_wide"), ("k_feat_poly2_wide<", "feat_poly2_wide"),
+               ("k_feat_poly2_vjp<", "feat_poly2_vjp"), ("k_feat_poly2<", "feat_poly2"))
+
+
+def _template_args(full_name, kernel):
+    """Template arguments of `kernel<...>` in a demangled name, as strings."""
+    inner = full_name.split(kernel + "<", 1)[1].split(">", 1)[0]
+    return [a.strip() for a in inner.split(",")]
 
 
 def kernel_tag(full_name):
+    """The library's launch name (la_kernel_names) of a demangled kernel name."""
     if "k_fwd_lb<" in full_name:  # the one-launch causal forward
         return "fwd_causal"
     if "k_sync_clear" in full_name:
         return "sync_clear"
-    if "k_fwd<" in full_name:
-        return "fwd_noncausal" if "false>" in full_name else "fwd_causal"
+    if "k_fwd<" in full_name:  # k_fwd<T, D, M, CAUSAL, PART>
+        return "fwd_causal" if _template_args(full_name, "k_fwd")[3] == "true" else "fwd_noncausal"
+    if "k_bq<" in full_name and _template_args(full_name, "k_bq")[3] == "2":  # kBqShares
+        return "bwd_query_shares"
     for key, tag in KERNEL_TAGS:
         if key in full_name:
             return tag
@@ -1041,8 +1054,8 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     if headline:
         rec["step_us"] = step_distribution(step)
         rec["memory"] = memory_report(step)
-        if not args.no_parity and wl in ("long", "mnist", "cifar"):
-            rec["parity"] = headline_parity(step, (0, w.H - 1) if wl == "long" else (0,))
+    if not args.no_parity and wl in ("long", "mnist", "cifar"):
+        rec["parity"] = headline_parity(step, (0, w.H - 1) if wl == "long" else (0,))
     if not args.no_parity and w.features:
         rec["parity"] = feature_parity(step)
     if wl == "decode" and not eager and not args.no_kernel_events:
