@@ -495,6 +495,8 @@ def kernel_tag(full_name):
         return "fwd_causal" if _template_args(full_name, "k_fwd")[3] == "true" else "fwd_noncausal"
     if "k_bq<" in full_name and _template_args(full_name, "k_bq")[3] == "2":  # kBqShares
         return "bwd_query_shares"
+    if "k_nc_qr<" in full_name and _template_args(full_name, "k_nc_qr")[3] == "2":  # kNcShares
+        return "nc_qr_shares"
     for key, tag in KERNEL_TAGS:
         if key in full_name:
             return tag

@@ -28,8 +28,8 @@
  *    size, or a few hundred positive random features; "Transformers are RNNs
  *    -- part 2/3", section 3.2.1): D > 64, a multiple of 64, with feature =
  *    LA_FEATURE_IDENTITY and no decay, in la_forward_causal,
- *    la_backward_causal, la_forward_noncausal and la_decode_step (not
- *    la_backward_noncausal).  Q, K, dQ, dK are then stored feature-sliced:
+ *    la_backward_causal, la_forward_noncausal, la_backward_noncausal and
+ *    la_decode_step.  Q, K, dQ, dK are then stored feature-sliced:
  *    [B, H, D/64, N, 64], slice s holding features 64 s .. 64 s + 63 of every
  *    token (the layout la_feature_random and la_feature_poly2 write for C >
  *    64).  S [B, H, D, M], Z [B, H, D] and decode's q, k [B, H, D] keep their
@@ -339,7 +339,8 @@ int la_backward_causal(const void *Q, const void *K, const void *V,
  *   dphi(Q_i) = S g_i + c_i Z,  dphi(K_j) = R V_j + r,  dV_j = R^T phi(K_j).
  * den_i and dO_i . O_i are recomputed from S, Z, so neither O nor den is an
  * input.  Linear time, O(D M) state per head.
- *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype`; D in {32, 64}.
+ *   Q, K, V, dO inputs [B,H,N,D] / [B,H,N,M] in `dtype` (Q, K feature-sliced
+ *               for wide feature vectors).
  *   S_tot, Z_tot optional: the totals written by la_forward_noncausal for the
  *               same Q, K, V (both or neither); NULL: formed here again.
  *   dQ, dK, dV  outputs in `dtype`.

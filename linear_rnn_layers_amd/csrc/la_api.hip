@@ -212,6 +212,11 @@ WsLayout ws_layout(int op, const Plan& p) {
       w.ckpt = state_bytes(p, p.nseg + 1);
       w.ragg = state_bytes(p, p.nseg);
       w.rpref = state_bytes(p, p.nseg + 1);
+      if (wide) {
+        w.gc = align256((size_t)p.BHv() * p.N * 2 * sizeof(float));  // (1/den, O.dO) per token
+        w.pn = wide_pn(p);                                            // dV shares
+        w.pd = wide_pd(p, 2 * sizeof(float));                         // shares of (num . dO, den)
+      }
       break;
     case LA_OP_FWD_DECAY:  // aggregates, per-segment log-decay sums and the prefix states
       if (p.nseg > 1) {
@@ -534,14 +539,14 @@ int bwd_noncausal_impl(const Plan& p, const void* Q, const void* K, const void* 
   const dim3 grid((unsigned)(p.BH * p.nseg));
   st = launch("nc_qr", la::k_nc_qr<T, D, M>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, St, Zt,
               (const float*)(St ? nullptr : agg), (const float*)(scan && !St ? pref : nullptr), (T*)dQ, ragg, N, p.L,
-              p.nseg, fm);
+              p.nseg, fm, 1, (float2*)nullptr);
   if (st) return st;
   if (scan) {
     st = scan_prefix<D, M>(p, ragg, nullptr, nullptr, rpref, s, 1);
     if (st) return st;
   }
   return launch("nc_kv", la::k_nc_kv<T, D, M>, grid, dim3(la::NT), s, (const T*)K, (const T*)V, (const float*)ragg,
-                (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg, fm);
+                (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)dV, N, p.L, p.nseg, fm, 1, (float*)nullptr);
 }
 
 // ----------------------------------------------------- decayed recurrence
@@ -718,6 +723,55 @@ int bwd_wide_impl(const Plan& p, const void* Q, const void* K, const void* V, co
   st = launch("bwd_kv", la::k_bkv<T, 64, M, true>, grid, dim3(la::NT), s, (const T*)Q, (const T*)K, (const T*)V,
               (const T*)dO, (const float2*)gc, (const float*)ragg, dSN, dZN, (T*)dK, (T*)nullptr, dS0, dZ0, N, p.L,
               p.nseg, scanned, fm, p.ns, pn);
+  if (st) return st;
+  return launch("wide_sum", la::k_wide_sum<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pn, (T*)dV,
+                rows, N, p.ns);
+}
+
+template <typename T, int M>
+int bwd_noncausal_wide_impl(const Plan& p, const void* Q, const void* K, const void* V, const void* dO,
+                            const float* St, const float* Zt, void* dQ, void* dK, void* dV, int N, void* ws, int fm,
+                            const Call& s) {
+  if (p.nseg == 0) return LA_OK;
+  const WsLayout wl = ws_layout(LA_OP_BWD_NONCAUSAL, p);
+  float* agg = reinterpret_cast<float*>(region(ws, 0));
+  float* pref = reinterpret_cast<float*>(region(ws, wl.agg));
+  float* ragg = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt));
+  float* rpref = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg));
+  float2* gc = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.rpref));
+  float* pn = reinterpret_cast<float*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.rpref + wl.gc));
+  float2* sh = reinterpret_cast<float2*>(region(ws, wl.agg + wl.ckpt + wl.ragg + wl.rpref + wl.gc + wl.pn));
+  const bool scan = use_scan(p);
+  const long rows = p.BHv() * N;
+  int st = LA_OK;
+  if (!St) {  // key totals of every slice: the forward's when given, else formed here
+    st = seg_aggregates<T, 64, M>(p, K, V, agg, N, fm, s);
+    if (st) return st;
+    if (scan) {
+      st = scan_prefix<64, M>(p, agg, nullptr, nullptr, pref, s, 1);
+      if (st) return st;
+    }
+  }
+  const dim3 grid((unsigned)(p.BH * p.nseg));
+  const float* ag = St ? nullptr : agg;
+  const float* pr = scan && !St ? pref : nullptr;
+  // every slice's shares of (num . dO, den), their sums per token, then the query pass proper
+  st = launch("nc_qr_shares", la::k_nc_qr<T, 64, M, la::kNcShares>, grid, dim3(la::NT), s, (const T*)Q,
+              (const T*)dO, St, Zt, ag, pr, (T*)nullptr, (float*)nullptr, N, p.L, p.nseg, fm, p.ns, sh);
+  if (st) return st;
+  st = launch("wide_pairs", la::k_wide_pairs, dim3((unsigned)((rows + la::NT - 1) / la::NT)), dim3(la::NT), s,
+              (const float2*)sh, gc, rows, N, p.ns);
+  if (st) return st;
+  st = launch("nc_qr", la::k_nc_qr<T, 64, M, la::kNcGiven>, grid, dim3(la::NT), s, (const T*)Q, (const T*)dO, St, Zt,
+              ag, pr, (T*)dQ, ragg, N, p.L, p.nseg, fm, p.ns, gc);
+  if (st) return st;
+  if (scan) {
+    st = scan_prefix<64, M>(p, ragg, nullptr, nullptr, rpref, s, 1);
+    if (st) return st;
+  }
+  st = launch("nc_kv", la::k_nc_kv<T, 64, M, true>, grid, dim3(la::NT), s, (const T*)K, (const T*)V,
+              (const float*)ragg, (const float*)(scan ? rpref : nullptr), (T*)dK, (T*)nullptr, N, p.L, p.nseg, fm,
+              p.ns, pn);
   if (st) return st;
   return launch("wide_sum", la::k_wide_sum<T, M>, token_grid<M>(rows), dim3(la::NT), s, (const float*)pn, (T*)dV,
                 rows, N, p.ns);
@@ -935,7 +989,7 @@ const char* la_last_error(void) { return g_err.c_str(); }
 const char* la_kernel_names(void) {
   return "seg_state,fwd_causal,fwd_noncausal,bwd_query,bwd_kv,nc_qr,nc_kv,decode,scan_states,scan_rev,"
          "state_copy,dseg_state,dscan_states,dfwd,dbq,dscan_rev,dbkv,dla_fix,feat_rf,feat_rf_vjp,feat_poly2,"
-         "feat_poly2_vjp,sync_clear,wide_combine,bwd_query_shares,wide_pairs,wide_sum,decode_wide,feat_rf_vjp_wide,"
+         "feat_poly2_vjp,sync_clear,wide_combine,bwd_query_shares,nc_qr_shares,wide_pairs,wide_sum,decode_wide,feat_rf_vjp_wide,"
          "feat_poly2_wide,feat_poly2_vjp_wide";
 }
 
@@ -944,9 +998,7 @@ size_t la_workspace_size(int op, int B, int H, int N, int D, int M, int dtype, c
   if (op < LA_OP_FWD_CAUSAL || op > LA_OP_BWD_DECAY) return 0;
   const bool nc = op == LA_OP_FWD_NONCAUSAL || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
                   op == LA_OP_BWD_DECAY;
-  if (is_wide(D) && (op == LA_OP_DECODE || op == LA_OP_BWD_NONCAUSAL || op == LA_OP_FWD_DECAY ||
-                     op == LA_OP_BWD_DECAY))
-    return 0;
+  if (is_wide(D) && (op == LA_OP_DECODE || op == LA_OP_FWD_DECAY || op == LA_OP_BWD_DECAY)) return 0;
   return ws_layout(op, plan_for(B, H, N, D, M, nc ? kFineTargetNC : 0, opt_chunks(opts))).bytes();
 }
 
@@ -1163,12 +1215,13 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
   if (st) return st;
   st = check_opts(opts);
   if (st) return st;
-  if (is_wide(D)) return fail(LA_ERR_UNSUPPORTED, "the non-causal backward takes D of 32 or 64");
+  st = check_wide(D, feature, nullptr);
+  if (st) return st;
   if (N == 0) return LA_OK;
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return fail(LA_ERR_NULL, "Q, K, V, dO, dQ, dK and dV are required");
   if ((S_tot == nullptr) != (Z_tot == nullptr)) return fail(LA_ERR_ARG, "S_tot and Z_tot must be given together");
-  const Plan p = make_plan(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
-  const size_t es = esize(dtype), bh = (size_t)p.BH;
+  const Plan p = plan_for(B, H, N, D, M, kFineTargetNC, opt_chunks(opts));
+  const size_t es = esize(dtype), bh = (size_t)p.BHv();
   const size_t need = ws_layout(LA_OP_BWD_NONCAUSAL, p).bytes();
   if (ws == nullptr || ws_bytes < need)
     return fail(LA_ERR_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
@@ -1178,6 +1231,9 @@ int la_backward_noncausal(const void* Q, const void* K, const void* V, const voi
                    rng("dQ", dQ, bh * N * D * es, true), rng("dK", dK, bh * N * D * es, true),
                    rng("dV", dV, bh * N * M * es, true), rng("ws", ws, need, true)});
   if (st) return st;
+  if (p.ns > 1)
+    LA_WIDE_DISPATCH(dtype, M, bwd_noncausal_wide_impl, p, Q, K, V, dO, S_tot, Z_tot, dQ, dK, dV, N, ws, fm,
+                     Call{(hipStream_t)stream, opts});
   LA_DISPATCH(dtype, D, M, bwd_noncausal_impl, p, Q, K, V, dO, S_tot, Z_tot, dQ, dK, dV, N, ws, fm,
               Call{(hipStream_t)stream, opts});
 }

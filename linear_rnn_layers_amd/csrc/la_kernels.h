@@ -894,11 +894,18 @@ __device__ __forceinline__ void stage_total(Planes<NP, D, M>& sp, float* sz, flo
 }
 
 // Query pass: dQ, and the reverse aggregates (R^T, r) of each segment.
-template <typename T, int D, int M>
+// Feature slices (ns per value head, la_wide.h) see only their shares of den_i
+// = phi(Q_i) . Z and of num_i . dO_i = phi(Q_i)^T S dO_i: as in the causal
+// query pass (la_bwd2.h), MODE kNcShares writes the slice's two shares of
+// token i to gc[bh][i] and nothing else, and kNcGiven reads the pair (1/den_i,
+// O_i . dO_i) of value head bh / ns, formed from their sums, from gc.
+constexpr int kNcFull = 0, kNcGiven = 1, kNcShares = 2;
+template <typename T, int D, int M, int MODE = kNcFull>
 __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* __restrict__ dO,
                                                const float* __restrict__ St, const float* __restrict__ Zt,
                                                const float* __restrict__ agg, const float* __restrict__ pref,
-                                               T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg, int fm) {
+                                               T* __restrict__ dQ, float* __restrict__ ragg, int N, int L, int nseg, int fm,
+                                               int ns, float2* __restrict__ gc) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NTW = DB * (M / 16) / 4, SV = D * M + D;
   constexpr int E = IO<T>::E;
@@ -913,8 +920,9 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
   const bool zw = w < DB;
+  const int vh = MODE != kNcFull ? bh / ns : bh;  // value head
   const T* Qh = Q + (size_t)bh * N * D;
-  const T* dOh = dO + (size_t)bh * N * M;
+  const T* dOh = dO + (size_t)vh * N * M;
   static_assert(sizeof(gt.v) >= SV * sizeof(float), "g planes too small to hold a float32 state");
   stage_total<D, M, P::NS, NT>(sp, sZ, reinterpret_cast<float*>(&gt.v[0][0][0]),
                                pref ? pref + (size_t)bh * (nseg + 1) * SV : nullptr,
@@ -975,8 +983,17 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
       }
       pu = sum_over_g(pu);
       pz = sum_over_g(pz);
-      const float invz = row_ok ? 1.f / pz : 0.f;
-      const float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
+      if constexpr (MODE == kNcShares) {
+        if (g == 0 && row_ok) gc[(size_t)bh * N + c0 + il] = make_float2(pu, pz);
+        return;  // the shares are all this mode writes
+      }
+      float invz = row_ok ? 1.f / pz : 0.f;
+      float odo = row_ok ? pu * invz : 0.f;  // O_i . dO_i
+      if constexpr (MODE == kNcGiven) {
+        const float2 pr = row_ok ? gc[(size_t)vh * N + c0 + il] : make_float2(0.f, 0.f);
+        invz = pr.x;
+        odo = pr.y;
+      }
       if (row_ok) {
 #pragma unroll
         for (int d0 = 0; d0 < DB; ++d0) {
@@ -1014,16 +1031,22 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
     chunk(bq[0], bd[0], c0);
     if (c0 + CH < t1) chunk(bq[1], bd[1], c0 + CH);
   }
-  float* out = ragg + ((size_t)bh * nseg + seg) * SV;
-  store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
-  if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
+  if constexpr (MODE != kNcShares) {
+    float* out = ragg + ((size_t)bh * nseg + seg) * SV;
+    store_ST_tiles<D, M, NTW>(out, acc, w, r16, g);
+    if (zw && g == 0) out[D * M + 16 * db + r16] = accr[0];
+  }
 }
 
 // Key pass: dK = (R V_j + r) phi'(K_j), dV = R^T phi(K_j) with the totals R, r.
-template <typename T, int D, int M>
+// PART (feature slices, ns per value head, la_wide.h): dV sums over all of a
+// head's features, so each slice writes its share (float32, [bh][n][M] in
+// pdv), summed over the slices afterwards.
+template <typename T, int D, int M, bool PART = false>
 __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* __restrict__ V,
                                                const float* __restrict__ ragg, const float* __restrict__ rpref,
-                                               T* __restrict__ dK, T* __restrict__ dV, int N, int L, int nseg, int fm) {
+                                               T* __restrict__ dK, T* __restrict__ dV, int N, int L, int nseg, int fm,
+                                               int ns, float* __restrict__ pdv) {
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NKT = P::VR, NVT = cmax(P::KR_b, 1);
@@ -1037,7 +1060,7 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const T* Kh = K + (size_t)bh * N * D;
-  const T* Vh = V + (size_t)bh * N * M;
+  const T* Vh = V + (size_t)(PART ? bh / ns : bh) * N * M;
   static_assert(sizeof(kt.v) >= SV * sizeof(float), "key planes too small to hold a float32 state");
   stage_total<D, M, P::NR, NT>(rp, sr, reinterpret_cast<float*>(&kt.v[0][0][0]),
                                rpref ? rpref + (size_t)bh * (nseg + 1) * SV : nullptr,
@@ -1090,8 +1113,13 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
       for (int s = 0; s < D / 32; ++s)
         mmaf<P::VR, P::VR>(a, rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16), kfr[s]);
       if (row_ok) {
-        float o[4] = {a[0], a[1], a[2], a[3]};
-        IO<T>::store4(dV + (size_t)bh * N * M + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+        if constexpr (PART) {
+          *reinterpret_cast<float4*>(pdv + ((size_t)bh * N + c0 + jl) * M + 16 * mb + 4 * g) =
+              make_float4(a[0], a[1], a[2], a[3]);
+        } else {
+          float o[4] = {a[0], a[1], a[2], a[3]};
+          IO<T>::store4(dV + (size_t)bh * N * M + (size_t)(c0 + jl) * M + 16 * mb + 4 * g, o);
+        }
       }
     }
   };

@@ -383,7 +383,10 @@ def test_wide_plan_and_sizes(lib, B, H, N, C, M):
                                                                 _al(bhs * (nseg_nc + 1) * sv * 4) + pn + pd)
     bwd = agg + pref + (0 if nseg == 1 else agg) + _al(B * H * N * 8) + pn + _al(bhs * N * 8)
     assert lib.la_workspace_size(2, B, H, N, C, M, 0, None) == bwd
-    for op in (3, 4, 5, 6):  # decode needs none; no non-causal backward or decayed form for wide features
+    # non-causal backward: key and reverse aggregates with their scans, then the pair per token and the shares
+    nc_st = _al(bhs * nseg_nc * sv * 4) + _al(bhs * (nseg_nc + 1) * sv * 4)
+    assert lib.la_workspace_size(4, B, H, N, C, M, 0, None) == 2 * nc_st + _al(B * H * N * 8) + pn + _al(bhs * N * 8)
+    for op in (3, 5, 6):  # decode needs none; no decayed form for wide features
         assert lib.la_workspace_size(op, B, H, N, C, M, 0, None) == 0
 
 
@@ -395,7 +398,7 @@ def test_wide_validation(lib):
     assert fwd(lib, D=128, feature=1, logA=addr(14)) == UNSUPPORTED
     assert b"decay" in lib.la_last_error()
     args = [addr(1), addr(2), addr(3), addr(4), None, None, addr(5), addr(6), addr(7)]
-    assert lib.la_backward_noncausal(*args, 2, 2, 100, 128, 32, 0, 1, addr(20), 1 << 30, None, None) == UNSUPPORTED
+    assert lib.la_backward_noncausal(*args, 2, 2, 100, 128, 32, 0, 0, addr(20), 1 << 30, None, None) == UNSUPPORTED
     assert lib.la_decode_step(addr(1), addr(2), addr(3), None, addr(4), addr(5), addr(6), 2, 2, 128, 64, 1, 0,
                               None, None) == UNSUPPORTED
     assert lib.la_decode_step(addr(1), addr(2), addr(3), addr(8), addr(4), addr(5), addr(6), 2, 2, 128, 64, 1, 1,
@@ -407,7 +410,8 @@ def test_wide_validation(lib):
     assert lib.la_feature_poly2(addr(1), addr(3), 2, 2, 100, 65, 4096, 0, None) == UNSUPPORTED
     assert lib.la_feature_poly2(addr(1), addr(1), 2, 2, 100, 32, 1088, 0, None) == ALIAS
     names = binding.kernel_names()
-    assert all(n in names for n in ("wide_combine", "bwd_query_shares", "wide_pairs", "wide_sum", "decode_wide",
+    assert all(n in names for n in ("wide_combine", "bwd_query_shares", "nc_qr_shares", "wide_pairs", "wide_sum",
+                                    "decode_wide",
                                     "feat_rf_vjp_wide", "feat_poly2_wide", "feat_poly2_vjp_wide"))
 
 

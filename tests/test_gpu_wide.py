@@ -140,6 +140,32 @@ def test_wide_noncausal_forward(kind, C, M, N, dtype):
     assert max(errs.values()) <= TOL[dtype], errs
 
 
+@pytest.mark.parametrize("totals", [False, True])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("kind,C,M,N", CASES)
+def test_wide_noncausal_backward(kind, C, M, N, dtype, totals):
+    """dPhi_Q, dPhi_K, dV of the non-causal form on wide feature vectors, with the forward's totals S, Z or
+    forming them again; dPhi_Q floored at 1e-2 of |S g_i| and dPhi_K at 1e-2 of |R V_j| (the terms the
+    quotient rule's share cancels, as for the 64-feature heads)."""
+    fq, fk, v, do, _, _ = _inputs(kind, C, M, N, dtype, 20700 + C)
+    Q, K, V, dO = dev(sl(fq), dtype), dev(sl(fk), dtype), dev(v, dtype), dev(do, dtype)
+    s = z = None
+    if totals:
+        _, s, z = binding.forward_noncausal(Q, K, V, feature=IDENT, return_state=True)
+    dq, dk, dv = binding.backward_noncausal(Q, K, V, dO, feature=IDENT, s=s, z=z)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward_noncausal(fq, fk, v, do, feature=IDENT)
+    fq64, fk64, v64, do64 = (np.asarray(a, np.float64) for a in (fq, fk, v, do))
+    S = np.einsum("bhnc,bhnm->bhcm", fk64, v64)
+    g = do64 / np.einsum("bhnc,bhc->bhn", fq64, fk64.sum(2))[..., None]
+    R = np.einsum("bhnc,bhnm->bhcm", fq64, g)
+    fl_q = CANCEL_FLOOR * np.abs(np.einsum("bhcm,bhnm->bhnc", S, g)).max(-1)
+    fl_k = CANCEL_FLOOR * np.abs(np.einsum("bhcm,bhnm->bhnc", R, v64)).max(-1)
+    errs = {"dPhiQ": rowerr(unsl(host(dq)), rq, row_floor=fl_q), "dPhiK": rowerr(unsl(host(dk)), rk, row_floor=fl_k),
+            "dV": rowerr(host(dv), rv)}
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
 @pytest.mark.parametrize("dtype", [F32, BF16])
 @pytest.mark.parametrize("kind,C,M", [("random", 256, 64), ("poly2", 1088, 32), ("random", 4096, 32)])
 def test_wide_decode(kind, C, M, dtype):
