@@ -176,6 +176,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
     bd.stage_values(ot);
     if (ci + 1 < nchunk) fetch(c0 + CH);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
 
     // ================ query rows il: S_i = S + sum_{j<=i} phi(K_j) V_j^T, Z_i likewise
     {
@@ -310,6 +311,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         zz += dz[0];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
   // the segment's reverse aggregate (sum over its tokens of phi(Q_i) g_i^T, c_i phi(Q_i)), [d][m] then r, for the
@@ -453,6 +455,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
     }
     if (ci > 0) fetch(c0 - CH);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
 
     // ================ key rows jl
     {
@@ -568,6 +571,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
     }
     // ================ the chunk's share of the reverse state (for the earlier chunks)
     rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
   // the reverse state carried through the sequence's first token is the gradient of the initial state
