@@ -129,12 +129,14 @@ __global__ __launch_bounds__(NT) void k_dseg_state(const T* __restrict__ K, cons
     const int nv = min(CH, t1 - c0);
     const float lam = wave_incl_sum(ell[b]);
     const float last = __shfl(lam, 63, 64);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     bk[b].stage_phi(kt, nv, nullptr, fm);
     bv[b].stage_values(vt);
     if (w == 0) sF[l] = exp_nat(last - lam);
     fetch(b, c0 + 2 * CH);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
     const float dec = exp_nat(last);
 #pragma unroll
     for (int k = 0; k < NTW; ++k) acc[k] *= dec;
@@ -287,6 +289,7 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
     const int nv = min(CH, t1 - c0);
     const float lam = wave_incl_sum(ell[b]);
     const float last = __shfl(lam, 63, 64);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     bq[b].stage_phi(qt, nv, nullptr, fm);
     bk[b].stage_phi(kt, nv, nullptr, fm);
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
     }
     fetch(b, c0 + 2 * CH);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
 
     const int il = 16 * w + r16;
     const float lam_i = slam[il], e_i = exp_nat(lam_i);
