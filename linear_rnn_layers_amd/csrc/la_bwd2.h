@@ -67,21 +67,21 @@ template <typename T, int D, int M, int NTR, int NPO, int NPQ>
 __device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, M + 16>& ot,
                                            const Planes<NPQ, CH, D>& qt, int w, int g, int r16) {
   using P = Prec<T>;
-  constexpr int DB = D / 16, NRT = (M / 16 + 1) * DB, NA = P::NDO < P::dR ? P::NDO : P::dR;
+  constexpr int DB = D / 16, NRT = (M / 16 + 1) * DB, NA = P::NDO < P::Rq ? P::NDO : P::Rq;
   f32x4_t acc[NTR];
 #pragma unroll
   for (int k = 0; k < NTR; ++k) acc[k] = accR[k];
 #pragma unroll
   for (int s = 0; s < CH / 32; ++s) {
     Frag<NA> oa[NTR];
-    Frag<P::dR> qb[NTR];
+    Frag<P::Rq> qb[NTR];
 #pragma unroll
     for (int k = 0; k < NTR; ++k) {
       const int t = w + 4 * k < NRT ? w + 4 * k : w;  // past the grid (uneven split): a harmless repeat
       oa[k] = ot.template tfrag<NA>(32 * s, 16 * (t / DB), g, r16);
-      qb[k] = qt.template tfrag<P::dR>(32 * s, 16 * (t % DB), g, r16);
+      qb[k] = qt.template tfrag<P::Rq>(32 * s, 16 * (t % DB), g, r16);
     }
-    mmaf_tiles<NA, P::dR>(acc, oa, qb);
+    mmaf_tiles<NA, P::Rq>(acc, oa, qb);
   }
 #pragma unroll
   for (int k = 0; k < NTR; ++k)
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
   static_assert((DB * MB) % 4 == 0, "S tiles must divide over four waves");
   __shared__ Planes<P::NQ, CH, D> qt;          // phi(Q), then q' = phi(Q) / den row by row
-  __shared__ Planes<P::NK, CH, D> kt;          // phi(K)
+  __shared__ Planes<P::Ka, CH, D> kt;          // phi(K)
   __shared__ Planes<P::NV, CH, M> vt;          // V
   __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]
   __shared__ Planes<P::NS, D, M> sp;           // S before this chunk, [d][m]
@@ -128,6 +128,17 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   auto sdb = [&](int k) { return (w + 4 * k) % DB; };
   auto smb = [&](int k) { return (w + 4 * k) / DB; };
   const bool zw = w < DB;  // holds Z of feature block w
+
+  // the mask [j <= i] of the wave's query rows as B operands under the accumulator map (pairs of 16-row blocks)
+  Frag<1> onef[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+      onef[p].p[0][e] = j <= 16 * w + r16 ? (__bf16)1.0f : (__bf16)0.0f;
+    }
+  }
 
   const int nchunk = (t1 - t0 + CH - 1) / CH;
   RowBuf<T, CH, D> bq, bk;
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
       if (zw && g == 0) sZ[16 * w + r16] = zz;
     }
     bq.template stage_phi<P::NQ, CH, D, 8, 0>(qt, nv, nullptr, fm);
-    bk.template stage_phi<P::NK, CH, D, 8, 0>(kt, nv, nullptr, fm);
+    bk.template stage_phi<P::Ka, CH, D, 8, 0>(kt, nv, nullptr, fm);
     bv.stage_values(vt);
     bd.stage_values(ot);
     if (ci + 1 < nchunk) fetch(c0 + CH);
@@ -186,8 +197,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
       Frag<NO> dof[M / 32];
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) dof[s] = ot.template frag<NO>(il, 32 * s, g);
-      // (V_j . dO_i) for j <= i as B operands under the accumulator map (pairs of 16-row blocks), and the
-      // mask [j <= i]; blocks after the wave's own stay zero.
+      // (V_j . dO_i) for j <= i as B operands under the accumulator map (pairs of 16-row blocks); blocks after
+      // the wave's own stay zero.
       f32x4_t bt[4];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
@@ -198,29 +209,20 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
             mmaf<P::Bt, P::Bt>(bt[jb], vt.template frag<P::Bt>(16 * jb + r16, 32 * s, g), dof[s]);
         }
       }
-      Frag<P::U2> btf[2];
-      Frag<1> onef[2];
+      Frag<P::Ut> btf[2];
+      // the wave's own block keeps j <= i (earlier blocks every pair, later ones are zero)
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
+        if (jb != w) continue;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = jb < w || (jb == w && 4 * g + r <= r16);  // j <= i
-          bt[jb][r] = keep ? bt[jb][r] : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) bt[jb][r] = 4 * g + r <= r16 ? bt[jb][r] : 0.f;
       }
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        btf[p] = acc2frag<P::U2>(bt[2 * p], bt[2 * p + 1]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 32 * p + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-          onef[p].p[0][e] = j <= il ? (__bf16)1.0f : (__bf16)0.0f;
-        }
-      }
+      for (int p = 0; p < 2; ++p) btf[p] = acc2frag<P::Ut>(bt[2 * p], bt[2 * p + 1]);
       f32x4_t U[DB], ZC[DB];
 #pragma unroll
       for (int d0 = 0; d0 < DB; ++d0) U[d0] = ZC[d0] = zero4();
-      constexpr int NKA = cmax(P::U2, P::Zc);
+      constexpr int NKA = P::Ka;
 #pragma unroll
       for (int s = 0; s < M / 32; ++s) {
         Frag<P::U1_a> sa[DB];
@@ -234,8 +236,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
           Frag<NKA> kfa[DB];
 #pragma unroll
           for (int d0 = 0; d0 < DB; ++d0) kfa[d0] = kt.template tfrag_acc<NKA>(32 * p, 16 * d0, g, r16);
-          mmaf_tiles<P::U2, P::U2>(U, kfa, btf[p]);
-          mmaf_tiles<P::Zc, 1>(ZC, kfa, onef[p]);
+          mmaf_tiles<P::Ka, P::Ut>(U, kfa, btf[p]);
+          mmaf_tiles<P::Ka, 1>(ZC, kfa, onef[p]);
         }
       }
 #pragma unroll
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
 
     // ================ the chunk's share of the reverse aggregate, then the state update
     if constexpr (MODE != kBqShares) rproduct64<T, D, M, NTR>(accR, ot, qt, w, g, r16);
-    constexpr int NKB = cmax(P::dS_b, P::Zc);
+    constexpr int NKB = P::Ka;
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
       Frag<P::dS_a> va[NTS];
@@ -304,10 +306,10 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         va[k] = vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16);
         kb[k] = kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16);
       }
-      mmaf_tiles<P::dS_a, P::dS_b>(accS, va, kb);
+      mmaf_tiles<P::dS_a, P::Ka>(accS, va, kb);
       if (zw) {
         f32x4_t dz = zero4();
-        mmaf<1, P::Zc>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * w, g, r16));
+        mmaf<1, P::Ka>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * w, g, r16));
         zz += dz[0];
       }
     }
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
   using P = Prec<T>;
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
-  __shared__ Planes<P::NQ, CH, D> qt;          // q' = phi(Q) / den
+  __shared__ Planes<cmax(cmax(P::At, P::dK), P::Rq), CH, D> qt;  // q' = phi(Q) / den
   __shared__ Planes<P::NK, CH, D> kt;          // phi(K)
   __shared__ Planes<P::NV, CH, M> vt;          // V
   __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
 
     // ================ key rows jl
     {
-      constexpr int NKT = cmax(P::At, P::VR);
+      constexpr int NKT = cmax(P::At, P::Vk);
       constexpr int NVT = cmax(P::Wt, P::KR_b);
       const int jl = 16 * w + r16;
       const bool row_ok = jl < nv;
@@ -485,15 +487,22 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
             mmaf<P::Wt, P::Wt>(wt[ib], ot.template frag<P::Wt>(16 * ib + r16, 32 * s, g), vfr[s]);
         }
       }
+      // blocks before the wave's own stay zero; later blocks keep every pair; the wave's own keeps i >= j
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
+        if (ib < w) continue;
         const float4 od = *reinterpret_cast<const float4*>(&sOdo[16 * ib + 4 * g]);
         const float odr[4] = {od.x, od.y, od.z, od.w};
+        if (ib > w) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = ib > w || (ib == w && 4 * g + r >= r16);  // i >= j
-          at[ib][r] = keep ? at[ib][r] : 0.f;
-          wt[ib][r] = keep ? wt[ib][r] - odr[r] : 0.f;
+          for (int r = 0; r < 4; ++r) wt[ib][r] -= odr[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool keep = 4 * g + r >= r16;
+            at[ib][r] = keep ? at[ib][r] : 0.f;
+            wt[ib][r] = keep ? wt[ib][r] - odr[r] : 0.f;
+          }
         }
       }
       Frag<P::dK> wfr[2];
@@ -545,7 +554,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
         Frag<P::VR> ra[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) ra[mb] = rp.template tfrag<P::VR>(32 * s, 16 * mb, g, r16);
-        mmaf_tiles<P::VR, P::VR>(aV, ra, kfr[s]);
+        mmaf_tiles<P::VR, P::Vk>(aV, ra, kfr[s]);
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p) {

@@ -35,6 +35,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace la {
 
@@ -75,7 +76,11 @@ __device__ __forceinline__ float dphi_from_phi(float p) { return fminf(p, 1.f); 
 // by the caller, e.g. polynomial or positive random features): the identity,
 // with derivative 1.
 __device__ __forceinline__ float feat(float x, int fm) { return fm ? x : phi(x); }
-__device__ __forceinline__ float dfeat(float p, int fm) { return fm ? 1.f : dphi_from_phi(p); }
+// As one median of three per value (the bound is uniform): the median of
+// (p, -inf, 1) is min(p, 1), that of (p, 1, 1) is 1.
+__device__ __forceinline__ float dfeat(float p, int fm) {
+  return __builtin_amdgcn_fmed3f(p, fm ? 1.f : -__builtin_inff(), 1.f);
+}
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 

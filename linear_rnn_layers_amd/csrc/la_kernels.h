@@ -55,9 +55,18 @@ struct Prec<bf16_t> {
   // backward staging (la_bwd2.h and the non-causal backward): phi(Q), phi(K),
   // V, dO, [g | c], S, R
   static constexpr int NQ = 2, NK = 2, NV = 1, NDO = 1, NG = 2, NS = 2, NR = 2;
-  // backward products
-  static constexpr int dS_a = 1, dS_b = 2, Bt = 1, U1_a = 2, U1_b = 1, U2 = 2, Zc = 2, dR = 2, At = 2, Wt = 1,
-                       dK = 2, KR_a = 2, KR_b = 1, dV = 2, VR = 2;
+  // backward products: the non-causal backward's, and in the two-pass causal
+  // backward V^T phi(K) (dS_a), dO.V (Bt, Wt), S dO (U1) and R V (KR)
+  static constexpr int dS_a = 1, Bt = 1, U1_a = 2, U1_b = 1, dR = 2, Wt = 1, KR_a = 2, KR_b = 1, VR = 2;
+  // the two-pass causal backward's other products: phi(K) in pass A's chunk
+  // products and S, Z update (Ka), the masked V.dO there (Ut), q' in the
+  // reverse aggregates of both passes (Rq) -- all three feed running sums or
+  // the cancellations of eq. 13-14, where phi(x) ~ 1 + x leaves the rounding
+  // of a one-plane phi near 2^-9 against deviations of size x, so they keep
+  // two planes -- and pass B's q'.phi(K) (At), q'^T W' (dK), dO A' (dV) and
+  // the phi(K) of R^T phi(K) (Vk; R keeps VR planes): per-term products
+  // within a chunk or against a two-plane state, one plane.
+  static constexpr int Ka = 2, Ut = 2, Rq = 2, At = 1, dK = 2, dV = 1, Vk = 1;
 };
 template <>
 struct Prec<float> {
@@ -65,8 +74,8 @@ struct Prec<float> {
   static constexpr int NQ = 3, NK = 3, NV = 3, NDO = 3, NG = 2, NS = 3, NR = 2;
   // g_i.V_j - O_i.dO_i cancels where V_j = O_i, so dO.V and its product with
   // phi(Q) are taken at float32 level too (bf16 inputs make dO.V exact).
-  static constexpr int dS_a = 3, dS_b = 3, Bt = 3, U1_a = 3, U1_b = 3, U2 = 3, Zc = 3, dR = 2, At = 2, Wt = 3,
-                       dK = 3, KR_a = 2, KR_b = 2, dV = 2, VR = 2;
+  static constexpr int dS_a = 3, Bt = 3, U1_a = 3, U1_b = 3, dR = 2, Wt = 3, KR_a = 2, KR_b = 2, VR = 2;
+  static constexpr int Ka = 3, Ut = 3, Rq = 2, At = 2, dK = 3, dV = 2, Vk = 2;
 };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
