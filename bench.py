@@ -758,7 +758,7 @@ def seq_sweep(args):
                      "stored_states_bytes_per_sample": H * N * D * M * 4})
         del q, k, v, do, o, den, ck, dq, dk, dv, ws_f, ws_b
     print(json.dumps({"metric": "causal linear-attn fwd+bwd time and peak memory per sample vs N (batch x N = 65536)",
-                      "unit": "us/sample", "n_gpus": 1, "steps": steps, "dtype": "bf16 storage, f32 arithmetic",
+                      "unit": "us/sample", "n_gpus": 1, "steps": steps, "dtype": "bf16 storage, split-bf16 MFMA with f32 accumulate",
                       "data": "synthetic",
                       "config": {"workload": "sequence-length sweep", "H": H, "D": D, "M": M, "tokens": total},
                       "rows": rows}))
@@ -941,6 +941,16 @@ def feature_parity(step, heads=(0,)):
 
 
 # -------------------------------------------------------------- measuring
+def dtype_label(wl, s):
+    """Storage type and arithmetic: the attention passes multiply bf16 planes of their operands on MFMA with
+    float32 accumulation (one plane for bf16 inputs, split planes for computed and float32 operands); the decode
+    step is float32 vector arithmetic on a float32 state."""
+    store = "f32" if s == 4 else "bf16"
+    if wl.startswith("decode"):
+        return f"{store} storage, f32 state and arithmetic"
+    return f"{store} storage, split-bf16 MFMA with f32 accumulate"
+
+
 def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     """One record: exactly `steps` timed steps after `warmup` untimed ones, the dominant kernel's launches
     bracketed by HIP events inside the timed region."""
@@ -1050,7 +1060,7 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
         cfg["launch"] = f"HIP graphs of {DECODE_GRAPH} steps" if graphs else "one host launch per step"
         cfg["state_bytes"] = w.B * w.H * (w.D * w.M + w.D) * 4
     rec = {"metric": metric, "value": value, "unit": unit, "steps": steps, "warmup": warmup,
-           "ms_per_step": ms_per_step, "dtype": "f32" if s == 4 else "bf16 storage, f32 arithmetic",
+           "ms_per_step": ms_per_step, "dtype": dtype_label(wl, s),
            "config": cfg, "roofline": roof, "step_roofline": step_roof, "side_by_side": side,
            "kernels_from_rocprof": breakdown}
     if headline:

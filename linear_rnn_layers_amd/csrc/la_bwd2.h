@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   __shared__ Planes<P::NS, D, M> sp;           // S before this chunk, [d][m]
   __shared__ alignas(16) float sZ[D];          // Z before this chunk
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int vh = MODE != kBqFull ? bh / ns : bh;  // value head
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
   __shared__ alignas(16) float sr[D];          // r after this chunk
   __shared__ alignas(16) float sOdo[CH];       // O_i . dO_i (0 past the end)
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int vh = PART ? bh / ns : bh;  // value head

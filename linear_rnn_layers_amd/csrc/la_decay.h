@@ -99,7 +99,7 @@ __global__ __launch_bounds__(NT) void k_dseg_state(const T* __restrict__ K, cons
   __shared__ Planes<P::FV, CH, M> vt;
   __shared__ alignas(16) float sF[CH];  // exp(lam_last - lam_j)
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NT) void k_dfwd(const T* __restrict__ Q, const T* _
   __shared__ alignas(16) float slam[CH];
   __shared__ alignas(16) float sF[CH];
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(2 * NT) void k_dbq(const T* __restrict__ Q, const T
   __shared__ alignas(16) float slam[CH];
   __shared__ alignas(16) float sF[CH];
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const bool qrole = w < 4;
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(2 * NT) void k_dbkv(const T* __restrict__ Q, const 
   __shared__ alignas(16) float sC[CH];
   __shared__ alignas(16) float sX[CH];  // x_j of the chunk just processed
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const bool vrole = w < 4;  // dV wavefront, else dK
@@ -976,7 +976,7 @@ __global__ __launch_bounds__(2 * NT) void k_dbkv(const T* __restrict__ Q, const 
 // segment order).
 __global__ __launch_bounds__(NT) void k_dla_fix(float* __restrict__ dla, const float* __restrict__ xseg, int N,
                                                  int L, int nseg) {
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   if (seg == nseg - 1) return;
   float off = 0.f;
   for (int s = seg + 1; s < nseg; ++s) off += xseg[(size_t)bh * nseg + s];

@@ -38,6 +38,21 @@ namespace la {
 
 constexpr int CH = 64;  // forward chunk
 
+// Workgroup -> item = head * nseg + segment, for the kernels launched with
+// one workgroup per segment (grid = heads x nseg).  Workgroups go to the
+// eight XCDs round-robin (workgroup i to XCD i mod 8), each XCD with its own
+// L2.  When every XCD's share is a whole number of heads, the workgroups of
+// one XCD take whole heads: the segments of a head, which read one another's
+// aggregates and checkpoint entries kernel after kernel, then meet in one L2,
+// and within a head a lower segment keeps a lower workgroup index.  Otherwise
+// the items follow the workgroup index.
+__device__ __forceinline__ int seg_item(int nseg) {
+  constexpr int NX = 8;
+  const int nb = (int)gridDim.x, i = (int)blockIdx.x;
+  if (nb % NX != 0 || (nb / NX) % nseg != 0) return i;
+  return (i % NX) * (nb / NX) + i / NX;
+}
+
 // Planes per staged operand and per product for each storage type.
 // bf16 I/O: inputs V, dO are exact in one plane; computed operands use one
 // plane where the result only needs bf16 accuracy and two where a state
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(NT) void k_seg_state(const T* __restrict__ K, const
   __shared__ Planes<P::FKF, CH, D> kt;
   __shared__ Planes<P::FV, CH, M> vt;
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const T* __restrict__ Q, const T* __
   KPlanes& kt = *reinterpret_cast<KPlanes*>(kmem);
   float* const sbuf = CAUSAL ? reinterpret_cast<float*>(kmem) : sown;  // start state summed from the aggregates
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
@@ -547,7 +562,7 @@ __global__ __launch_bounds__(NT) void k_fwd_lb(const T* __restrict__ Q, const T*
   KPlanes& kt = *reinterpret_cast<KPlanes*>(kmem);
   float* const sbuf = reinterpret_cast<float*>(kmem);
 
-  const int item = blockIdx.x;
+  const int item = seg_item(nseg);
   const int seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
@@ -936,7 +951,7 @@ __global__ __launch_bounds__(NT) void k_nc_qr(const T* __restrict__ Q, const T* 
   __shared__ Planes<P::NS, D, M> sp;                 // S total, [d][m]
   __shared__ alignas(16) float sZ[D];                // Z total
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const int db = w % DB;
@@ -1079,7 +1094,7 @@ __global__ __launch_bounds__(NT) void k_nc_kv(const T* __restrict__ K, const T* 
   __shared__ alignas(16) float k32[CH][D + 4];
   __shared__ alignas(16) float sr[D];         // r total
 
-  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int item = seg_item(nseg), seg = item % nseg, bh = item / nseg;
   const int t0 = seg * L, t1 = min(N, t0 + L);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g = l >> 4;
   const T* Kh = K + (size_t)bh * N * D;
