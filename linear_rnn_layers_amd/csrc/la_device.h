@@ -35,7 +35,6 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <type_traits>
 
 namespace la {
 
@@ -69,15 +68,15 @@ __device__ __forceinline__ float phi(float x) {
   return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 // Its derivative is 1 for x > 0 and exp(x) otherwise, i.e. min(phi(x), 1).
-__device__ __forceinline__ float dphi_from_phi(float p) { return fminf(p, 1.f); }
 
 // Feature-map selection: every kernel takes a flag `fm`; fm = 0 applies eq. 7,
 // fm = 1 takes Q and K as feature vectors already (another feature map applied
 // by the caller, e.g. polynomial or positive random features): the identity,
 // with derivative 1.
 __device__ __forceinline__ float feat(float x, int fm) { return fm ? x : phi(x); }
-// As one median of three per value (the bound is uniform): the median of
-// (p, -inf, 1) is min(p, 1), that of (p, 1, 1) is 1.
+// The derivative from the staged p = feat(x): min(p, 1) for eq. 7, 1 for the
+// identity; as one median of three per value (the bound is uniform): the
+// median of (p, -inf, 1) is min(p, 1), that of (p, 1, 1) is 1.
 __device__ __forceinline__ float dfeat(float p, int fm) {
   return __builtin_amdgcn_fmed3f(p, fm ? 1.f : -__builtin_inff(), 1.f);
 }
