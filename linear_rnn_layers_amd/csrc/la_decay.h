@@ -45,10 +45,15 @@ struct DPrec;
 template <>
 struct DPrec<bf16_t> {
   static constexpr int Q = 2, K = 2, V = 1, DO = 1, S = 2, G = 2, R = 2, W = 2;
+  // the key pass's dV side: the weighted attention tile (phi(Q).phi(K), then
+  // as the operand of dO A) and phi(K) in R+^T phi(K) -- per-term products
+  // that cancel nothing -- take one plane (R+ keeps R)
+  static constexpr int Av = 1, Wv = 1, Kv = 1;
 };
 template <>
 struct DPrec<float> {
   static constexpr int Q = 3, K = 3, V = 3, DO = 3, S = 3, G = 2, R = 3, W = 3;
+  static constexpr int Av = 3, Wv = 3, Kv = 3;
 };
 
 __device__ __forceinline__ float exp_nat(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(2 * NT) void k_dbkv(const T* __restrict__ Q, const 
         if (ib >= rb) {
           if (vrole) {
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) mmaf<P::Q, P::K>(a, qt.template frag<P::Q>(16 * ib + r16, 32 * s, g), kf[s]);
+            for (int s = 0; s < D / 32; ++s) mmaf<P::Av, P::Av>(a, qt.template frag<P::Av>(16 * ib + r16, 32 * s, g), kf[s]);
           } else {
 #pragma unroll
             for (int s = 0; s < M / 32; ++s)
@@ -898,18 +903,27 @@ __global__ __launch_bounds__(2 * NT) void k_dbkv(const T* __restrict__ Q, const 
         tw[ib] = a;
       }
       Frag<P::W> wf[2];
+      if (vrole) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) wf[p] = acc2frag<P::W>(tw[2 * p], tw[2 * p + 1]);
+        for (int p = 0; p < 2; ++p) {
+          const Frag<P::Wv> f = acc2frag<P::Wv>(tw[2 * p], tw[2 * p + 1]);
+#pragma unroll
+          for (int q = 0; q < P::Wv; ++q) wf[p].p[q] = f.p[q];
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) wf[p] = acc2frag<P::W>(tw[2 * p], tw[2 * p + 1]);
+      }
       if (vrole) {
         // dV_j[m] = sum_i dO_i[m] aw[i][j] + f_j (R+^T phi(K_j))[m]
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           f32x4_t st = zero4(), acc = zero4();
 #pragma unroll
-          for (int s = 0; s < D / 32; ++s) mmaf<P::R, P::K>(st, rp.template tfrag<P::R>(32 * s, 16 * mb, g, r16), kf[s]);
+          for (int s = 0; s < D / 32; ++s) mmaf<P::R, P::Kv>(st, rp.template tfrag<P::R>(32 * s, 16 * mb, g, r16), kf[s]);
 #pragma unroll
           for (int p = 0; p < 2; ++p)
-            if (2 * p + 1 >= rb) mmaf<P::DO, P::W>(acc, ot.template tfrag_acc<P::DO>(32 * p, 16 * mb, g, r16), wf[p]);
+            if (2 * p + 1 >= rb) mmaf<P::DO, P::Wv>(acc, ot.template tfrag_acc<P::DO>(32 * p, 16 * mb, g, r16), wf[p]);
           if (row_ok) {
             float o[4];
 #pragma unroll
