@@ -47,14 +47,14 @@ CLOCK_GHZ = 2.4
 SIMDS = 256 * 4
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE = "long"
-NESTED = ("mnist", "cifar", "decode", "decode-dram", "mnist-rf256", "cifar-poly2")
+NESTED = ("mnist", "cifar", "decode", "decode-dram", "mnist-rf256", "cifar-poly2", "long-decay", "speech")
 DECODE_GRAPH = 64  # decode steps per captured graph
 THREADS = 16  # host threads for input generation (the GPU host's share of cores)
 
 # The kernel with the largest share of a step's GPU time (rocprofv3 kernel statistics in profiles/).
 DOMINANT = {"long": "bwd_kv", "mnist": "bwd_kv", "cifar": "bwd_kv", "mnist-rf": "bwd_kv", "mnist-rf256": "bwd_kv",
             "cifar-poly2": "bwd_kv",
-            "long-decay": "dbkv", "speech": "nc_qr", "decode": "decode", "decode-dram": "decode",
+            "long-decay": "dbq", "speech": "nc_qr", "decode": "decode", "decode-dram": "decode",
             "small": "fwd_causal"}
 
 
