@@ -263,7 +263,8 @@ class KernelTimer:
         if KernelTimer._hip is None:
             KernelTimer._hip = ctypes.CDLL("libamdhip64.so")
         hip = KernelTimer._hip
-        self._lib = hip  # kept on the instance: module globals may be gone when it is collected at exit
+        # kept on the instance: module globals (ctypes included) may be gone when it is collected at exit
+        self._lib, self._vp = hip, ctypes.c_void_p
         self.kernel = kernel.encode()
         self.pairs = int(pairs)
         self.events = (ctypes.c_void_p * (2 * self.pairs))()
@@ -306,12 +307,12 @@ class KernelTimer:
         return total, n
 
     def __del__(self):
-        hip = getattr(self, "_lib", None)
-        if hip is None:
+        hip, vp = getattr(self, "_lib", None), getattr(self, "_vp", None)
+        if hip is None or vp is None:
             return
         for e in range(2 * self.pairs):
             if self.events[e]:
-                hip.hipEventDestroy(ctypes.c_void_p(self.events[e]))
+                hip.hipEventDestroy(vp(self.events[e]))
 
 
 # --------------------------------------------------------- one-to-one calls
