@@ -51,9 +51,10 @@ NESTED = ("mnist", "cifar", "decode", "decode-dram", "mnist-rf256", "cifar-poly2
 DECODE_GRAPH = 64  # decode steps per captured graph
 THREADS = 16  # host threads for input generation (the GPU host's share of cores)
 
-# The kernel with the largest share of a step's GPU time (rocprofv3 kernel statistics in profiles/).
-DOMINANT = {"long": "bwd_kv", "mnist": "bwd_kv", "cifar": "bwd_kv", "mnist-rf": "bwd_kv", "mnist-rf256": "bwd_kv",
-            "cifar-poly2": "bwd_kv",
+# The kernel with the largest share of a step's GPU time in the rocprofv3 kernel statistics in profiles/
+# (dominant_kernel reads them; this table is what they showed, used when no statistics match the sources).
+DOMINANT = {"long": "bwd_query", "mnist": "bwd_query", "cifar": "bwd_query", "mnist-rf": "bwd_query",
+            "mnist-rf256": "bwd_query", "cifar-poly2": "bwd_query",
             "long-decay": "dbq", "speech": "nc_qr", "decode": "decode", "decode-dram": "decode",
             "small": "fwd_causal"}
 
@@ -146,6 +147,10 @@ class Step:
             specs = [("layer", i) for i in range(w.layers)]  # one independent input set per layer
         elif wl in ("mnist", "mnist-rf", "mnist-rf256"):
             specs = [("set", i) for i in range(6)]  # rotate batches so successive steps miss the 256 MB cache
+        elif wl in ("long", "long-decay"):
+            # 512 MB per set: one set already exceeds the cache, but the first chunks a step reads would still
+            # be there from the end of the step before
+            specs = [("set", i) for i in range(2)]
         else:
             specs = [("set", 0)]
         arrays = _parallel(lambda a: self._draw(*a), [(sp, t) for sp in specs for t in range(4)])
@@ -309,7 +314,8 @@ class Step:
             self._features_step(q, k, v, do)
             return
         if wl == "long-decay":
-            q, k, v, do = self.sets[0]
+            q, k, v, do = self.sets[self.i % len(self.sets)]
+            self.i += 1
             b.la_forward_causal(q, k, v, self.o, self.den, ckpt=self.ck, ws=self.ws_f, logA=self.log_a, opts=o)
             b.la_backward_causal(q, k, v, self.o, self.den, do, self.dq, self.dk, self.dv, ckpt=self.ck,
                                  ws=self.ws_b, logA=self.log_a, dlogA=self.dla, opts=o)
@@ -458,6 +464,15 @@ def _profile_json(name):
     with open(path) as f:
         rec = json.load(f)
     return rec if rec.get("source_hash") == source_hash() else None
+
+
+def dominant_kernel(wl):
+    """The kernel with the largest total time per step in the committed rocprofv3 statistics of this workload
+    (profiles/<workload>_kernels.json, when taken at the current kernel sources), else the DOMINANT table."""
+    ks = _profile_json(f"{wl}_kernels.json")
+    if ks and ks.get("kernels"):
+        return max(ks["kernels"], key=lambda k: ks["kernels"][k]["total_us"])
+    return DOMINANT[wl]
 
 
 def traffic_from_profiles(kernel, label):
@@ -956,7 +971,7 @@ def measure(wl, steps, warmup, args, headline=False, copy_gbs=None):
     bracketed by HIP events inside the timed region."""
     import torch
 
-    dominant = DOMINANT[wl]
+    dominant = dominant_kernel(wl)
     eager = wl.startswith("decode") and args.eager_decode
     per_step = {"cifar": 16, "speech": 9}.get(wl, 1)  # launches of the dominant kernel per step
     graphs_planned = wl.startswith("decode") and not eager  # replays are timed with events around each graph
