@@ -8,22 +8,26 @@ records with their own roofline, the MNIST-shaped layer (B=16 H=8 N=784
 D=M=32, float32: causal forward + backward + non-causal forward), the
 CIFAR-shaped 16-layer stack (B=4 H=8 N=3072 D=M=32 bf16, sigma 0.5), and the
 decode loop (4096 steps of B=256 H=16 D=M=64 after a 512-token prefill; HIP
-graphs of 64 steps and one launch per step), plus a decode run whose state
-(537 MB) exceeds the 256 MB last-level cache.  --workload X measures X alone
-(mnist, cifar, long, long-decay, mnist-rf, speech, decode, small).
+graphs of 64 steps and one launch per step), a decode run whose state (537 MB)
+exceeds the 256 MB last-level cache, the random-feature layer with C = 256
+(mnist-rf256), one CIFAR-shaped layer with the degree-2 polynomial map
+(cifar-poly2, C = 1088), the 2^16-token sequence with a data-dependent decay
+(long-decay) and the 9-layer bidirectional speech encoder (non-causal).
+--workload X measures X alone (also mnist-rf and small).
 
 Prints one JSON line.  `value` is whole-job throughput with the inputs
-resident in HBM; `roofline` is for the dominant kernel, its duration taken
-from HIP events that the library records on the launch stream around every
-launch of that kernel inside the timed region (la_options::timed_kernel with
-caller-created events), its bytes the survey's algorithmic bytes per
-token-head of the pass the kernel carries (forward (2D+2M)s+4, backward
-(4D+4M)s+4, s bytes per element) times the token-heads of one launch;
-`step_roofline` is the whole step's algorithmic bytes over the step time;
-`side_by_side` carries the HBM fraction, the executed-MFMA fraction and
-MFMA-busy (rocprofv3 counters in profiles/, when they were taken at the
-current kernel sources) and the useful-flop fraction.  `cpu_baseline` is the
-float64 oracle on the host cores on a bounded sample of the headline
+resident in HBM; `roofline` is for the dominant kernel (the largest share of
+the step in the committed kernel statistics), its duration taken from HIP
+events that the library records on the launch stream around every launch of
+that kernel inside the timed region (la_options::timed_kernel with
+caller-created events), its bytes the algorithmic bytes of one launch, the
+tensors that kernel must read or write over its token-heads (kernel_bytes);
+`step_roofline` is the whole step's algorithmic bytes per token-head of each
+pass (forward (2D+2M)s+4, backward (4D+4M)s+4, s bytes per element) over the
+step time; `side_by_side` carries the HBM fraction, the executed-MFMA
+fraction and MFMA-busy (rocprofv3 counters in profiles/, when they were taken
+at the current kernel sources) and the useful-flop fraction.  `cpu_baseline`
+is the float64 oracle on the host cores on a bounded sample of the headline
 workload.  The per-kernel breakdown comes from the rocprofv3 kernel
 statistics in profiles/ (per-launch events would inflate every kernel).
 """
@@ -363,7 +367,7 @@ class Step:
 
 # ---------------------------------------------------- algorithmic figures
 def pass_bytes(w, s):
-    """The survey's algorithmic bytes per token-head of each pass: forward (2D+2M)s+4 (read Q, K, V; write O,
+    """Algorithmic bytes per token-head of each pass: forward (2D+2M)s+4 (read Q, K, V; write O,
     den), backward (4D+4M)s+4 (read Q, K, V, O, dO, den; write dQ, dK, dV), non-causal forward (2D+2M)s (read
     Q, K, V; write O).  With random features the attention sees C-wide feature vectors in place of D."""
     D, M = w.features or w.D, w.M
@@ -403,7 +407,7 @@ def step_work(wl, w, s):
 def kernel_bytes(name, w, s):
     """Algorithmic HBM bytes per launch of a kernel: the bytes of the tensors it must read or write by its
     function (the split of the per-pass totals over the kernels that do the work).  Used for the traffic
-    tables; the roofline takes the survey's per-pass figure for the dominant kernel (dominant_bytes)."""
+    tables and, for the dominant kernel, the roofline (dominant_bytes)."""
     Din, M = w.D, w.M
     D = w.features or Din
     th = w.B * w.H * w.N
