@@ -1166,6 +1166,12 @@ def main():
                           "ms_per_step": (time.perf_counter() - t0) * 1e3 / (warmup + steps),
                           "source_hash": source_hash()}))
         return
+    from linear_rnn_layers_amd import build as _build
+
+    lib_stale = _build.stale()
+    if lib_stale:
+        print("bench: WARNING the HIP library is older than its sources; the figures are for the older build",
+              file=sys.stderr, flush=True)
     copy = copy_bandwidth()
     print(f"bench: {wl} ({steps} steps, {warmup} warm-up)", file=sys.stderr, flush=True)
     rec = measure(wl, steps, warmup, args, headline=True, copy_gbs=copy)
@@ -1192,7 +1198,7 @@ def main():
            "kernels_from_rocprof": rec["kernels_from_rocprof"], "parity": rec.get("parity"),
            "step_us": rec.get("step_us"), "memory": rec.get("memory"), "nested": nested or None,
            "copy_gbs": copy, "gpu": torch.cuda.get_device_name(0), "rocm": torch.version.hip,
-           "seeds": list(w.seeds), "source_hash": source_hash(),
+           "seeds": list(w.seeds), "source_hash": source_hash(), "library_older_than_sources": lib_stale,
            "kernel_events_in_timed_region": not args.no_kernel_events}
     if cpu and rec["unit"] == cpu["unit"]:
         out["gpu_over_cpu"] = rec["value"] / cpu["value"]
