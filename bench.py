@@ -421,8 +421,8 @@ def kernel_bytes(name, w, s):
         "nc_kv": (2 * D + 2 * M) * s,            # read K, V; write dK, dV
         "dseg_state": (D + M) * s + 4,           # read K, V, logA
         "dfwd": (2 * D + 2 * M) * s + 8,         # read Q, K, V, logA; write O, den
-        "dbq": (3 * D + 2 * M) * s + 12,         # read Q, K, V, dO, logA; write dQ, (1/den, c)
-        "dbkv": (3 * D + 3 * M) * s + 16,        # read Q, K, V, dO, logA, (1/den, c); write dK, dV, dlogA terms
+        "dbq": (3 * D + 2 * M) * s + 4,          # read Q, K, V, dO, logA; write dQ
+        "dbkv": (3 * D + 3 * M) * s + 8,         # read Q, K, V, dO, logA; write dK, dV, dlogA terms
         "dla_fix": 8,                            # read and write dlogA
         "feat_rf": (Din + D) * s,                # read X; write Phi
         "feat_rf_vjp": (2 * Din + D) * s,        # read X, dPhi; write dX
@@ -448,8 +448,9 @@ def kernel_bytes(name, w, s):
 
 def dominant_bytes(wl, name, w, s):
     """Algorithmic bytes per launch for the roofline of the dominant kernel: the tensors it must read or write by
-    its function (kernel_bytes); the per-token pair (1/den, O.dO) that the backward's query pass hands to its key
-    pass (8 bytes per token-head each way) is an intermediate of this implementation and is not counted."""
+    its function (kernel_bytes); the per-token pair (1/den, O.dO), or (1/den, c) with a decay, that the backward's
+    query pass hands to its key pass (8 bytes per token-head each way) is an intermediate of this implementation
+    and is not counted."""
     return kernel_bytes(name, w, s)
 
 
