@@ -62,25 +62,27 @@ __device__ __forceinline__ void put_neg_odo(Planes<NP, ROWS, COLS, PAD>& p, int 
 
 // [R | r]^T += [dO | -O.dO]^T q' over one 64-token chunk: tiles t = w + 4k
 // (t < the tile count) of the (M/16 + 1) x (D/16) tile grid, value block
-// t / DB (block M/16 holds the r rows M, M + 1), feature block t % DB.
+// t / DB (block M/16 holds the r rows M, M + 1), feature block t % DB.  DB
+// divides 4, so every tile of a wave has feature block w % DB and the q'
+// fragment is read once per step for all of them.
 template <typename T, int D, int M, int NTR, int NPO, int NPQ>
 __device__ __forceinline__ void rproduct64(f32x4_t* accR, const Planes<NPO, CH, M + 16>& ot,
                                            const Planes<NPQ, CH, D>& qt, int w, int g, int r16) {
   using P = Prec<T>;
   constexpr int DB = D / 16, NRT = (M / 16 + 1) * DB, NA = P::NDO < P::Rq ? P::NDO : P::Rq;
+  static_assert(4 % DB == 0, "a wave's tiles must share one feature block");
   f32x4_t acc[NTR];
 #pragma unroll
   for (int k = 0; k < NTR; ++k) acc[k] = accR[k];
 #pragma unroll
   for (int s = 0; s < CH / 32; ++s) {
     Frag<NA> oa[NTR];
-    Frag<P::Rq> qb[NTR];
 #pragma unroll
     for (int k = 0; k < NTR; ++k) {
       const int t = w + 4 * k < NRT ? w + 4 * k : w;  // past the grid (uneven split): a harmless repeat
       oa[k] = ot.template tfrag<NA>(32 * s, 16 * (t / DB), g, r16);
-      qb[k] = qt.template tfrag<P::Rq>(32 * s, 16 * (t % DB), g, r16);
     }
+    const Frag<P::Rq> qb = qt.template tfrag<P::Rq>(32 * s, 16 * (w % DB), g, r16);
     mmaf_tiles<NA, P::Rq>(acc, oa, qb);
   }
 #pragma unroll
