@@ -127,7 +127,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   const size_t offD = (size_t)bh * N * D, offM = (size_t)vh * N * M;
   const Frag<1> ones = ones_frag();
   ot.zero_cols(M + 2, M + 16);
-  auto sdb = [&](int k) { return (w + 4 * k) % DB; };
+  static_assert(4 % DB == 0, "a wave's S tiles must share one feature block");
+  auto sdb = [&](int) { return w % DB; };  // (w + 4k) mod DB: the same for all of the wave's tiles
   auto smb = [&](int k) { return (w + 4 * k) / DB; };
   const bool zw = w < DB;  // holds Z of feature block w
 
@@ -301,17 +302,15 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
     constexpr int NKB = P::Ka;
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
+      // phi(K)^T of the wave's feature block, read once for its S tiles and, where it holds Z, for Z
+      const Frag<NKB> kb = kt.template tfrag<NKB>(32 * s, 16 * sdb(0), g, r16);
       Frag<P::dS_a> va[NTS];
-      Frag<NKB> kb[NTS];
 #pragma unroll
-      for (int k = 0; k < NTS; ++k) {
-        va[k] = vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16);
-        kb[k] = kt.template tfrag<NKB>(32 * s, 16 * sdb(k), g, r16);
-      }
+      for (int k = 0; k < NTS; ++k) va[k] = vt.template tfrag<P::dS_a>(32 * s, 16 * smb(k), g, r16);
       mmaf_tiles<P::dS_a, P::Ka>(accS, va, kb);
-      if (zw) {
+      if (zw) {  // w < DB: its feature block is w
         f32x4_t dz = zero4();
-        mmaf<1, P::Ka>(dz, ones, kt.template tfrag<NKB>(32 * s, 16 * w, g, r16));
+        mmaf<1, P::Ka>(dz, ones, kb);
         zz += dz[0];
       }
     }
