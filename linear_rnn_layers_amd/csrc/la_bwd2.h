@@ -357,6 +357,7 @@ __global__ __launch_bounds__(NT) void k_bkv(const T* __restrict__ Q, const T* __
   constexpr int DB = D / 16, MB = M / 16, SV = D * M + D;
   constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
   __shared__ Planes<cmax(cmax(P::At, P::dK), P::Rq), CH, D> qt;  // q' = phi(Q) / den
+  static_assert(P::NK >= cmax(P::At, P::Vk), "pass B's phi(K) products need their planes staged");
   __shared__ Planes<P::NK, CH, D> kt;          // phi(K)
   __shared__ Planes<P::NV, CH, M> vt;          // V
   __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]

@@ -67,9 +67,11 @@ struct Prec<bf16_t> {
   // Z (the denominator is an output, and a 1-plane Z would leave it at bf16
   // accuracy; two planes keep it near float32)
   static constexpr int FQ = 1, FK = 1, FKF = 2, FV = 1, FS = 1, FA = 1, FZ = 2;
-  // backward staging (la_bwd2.h and the non-causal backward): phi(Q), phi(K),
-  // V, dO, [g | c], S, R
-  static constexpr int NQ = 2, NK = 2, NV = 1, NDO = 1, NG = 2, NS = 2, NR = 2;
+  // backward staging (la_bwd2.h and the non-causal backward): phi(Q), phi(K)
+  // in pass B (its products take one plane; the staged value also gives
+  // phi'(K) = min(phi, 1) to the bf16 dK, which one plane carries to bf16
+  // accuracy), V, dO, [g | c], S, R
+  static constexpr int NQ = 2, NK = 1, NV = 1, NDO = 1, NG = 2, NS = 2, NR = 2;
   // backward products: the non-causal backward's, and in the two-pass causal
   // backward V^T phi(K) (dS_a), dO.V (Bt, Wt), S dO (U1) and R V (KR)
   static constexpr int dS_a = 1, Bt = 1, U1_a = 2, U1_b = 1, dR = 2, Wt = 1, KR_a = 2, KR_b = 1, VR = 2;
@@ -86,7 +88,7 @@ struct Prec<bf16_t> {
 template <>
 struct Prec<float> {
   static constexpr int FQ = 2, FK = 2, FKF = 3, FV = 3, FS = 2, FA = 2, FZ = 2;
-  static constexpr int NQ = 3, NK = 3, NV = 3, NDO = 3, NG = 2, NS = 3, NR = 2;
+  static constexpr int NQ = 3, NK = 2, NV = 3, NDO = 3, NG = 2, NS = 3, NR = 2;
   // g_i.V_j - O_i.dO_i cancels where V_j = O_i, so dO.V and its product with
   // phi(Q) are taken at float32 level too (bf16 inputs make dO.V exact).
   static constexpr int dS_a = 3, Bt = 3, U1_a = 3, U1_b = 3, dR = 2, Wt = 3, KR_a = 2, KR_b = 2, VR = 2;
