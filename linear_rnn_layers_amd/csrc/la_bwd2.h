@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   constexpr int NTS = DB * MB / 4;        // S^T tiles per wave
   constexpr int NRT = (MB + 1) * DB, NTR = (NRT + 3) / 4;  // [R | r]^T tiles: all, per wave (the last maybe short)
   static_assert((DB * MB) % 4 == 0, "S tiles must divide over four waves");
-  __shared__ Planes<P::NQ, CH, D> qt;          // phi(Q), then q' = phi(Q) / den row by row
+  __shared__ Planes<P::NQ, CH, D> qt;          // q' = phi(Q) / den, written by the query rows' own lanes
   __shared__ Planes<P::Ka, CH, D> kt;          // phi(K)
   __shared__ Planes<P::NV, CH, M> vt;          // V
   __shared__ Planes<P::NDO, CH, M + 16> ot;    // [dO | -O.dO | 0]
@@ -144,11 +144,18 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
   }
 
   const int nchunk = (t1 - t0 + CH - 1) / CH;
-  RowBuf<T, CH, D> bq, bk;
+  // Q is needed only in the query rows' own lanes (row 16w + r16, features 16 d0 + 4g .. + 3, the layout of
+  // U and Z_i), so each lane reads its elements straight into registers: phi(Q) is formed there in float32
+  // and never staged (the q' rows written back below are all the LDS copy there is).
+  typename IO<T>::raw4 qraw[DB];
+  RowBuf<T, CH, D> bk;
   RowBuf<T, CH, M> bv, bd;
   auto fetch = [&](int c0) {
     const int nv = min(CH, t1 - c0);
-    bq.load(Q + offD + (size_t)c0 * D, nv);
+    const int il = 16 * w + r16;
+#pragma unroll
+    for (int d0 = 0; d0 < DB; ++d0)
+      qraw[d0] = il < nv ? IO<T>::load_raw4(Q + offD + (size_t)(c0 + il) * D + 16 * d0 + 4 * g) : IO<T>::zero_raw4();
     bk.load(K + offD + (size_t)c0 * D, nv);
     bv.load(V + offM + (size_t)c0 * M, nv);
     bd.load(dO + offM + (size_t)c0 * M, nv);
@@ -184,7 +191,13 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
       }
       if (zw && g == 0) sZ[16 * w + r16] = zz;
     }
-    bq.template stage_phi<P::NQ, CH, D, 8, 0>(qt, nv, nullptr, fm);
+    float qv[DB][4];  // phi(Q) of this lane's elements of its row (rows past the end: read as zero, unused)
+#pragma unroll
+    for (int d0 = 0; d0 < DB; ++d0) {
+      IO<T>::unpack4(qraw[d0], qv[d0]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qv[d0][r] = feat(qv[d0][r], fm);
+    }
     bk.template stage_phi<P::Ka, CH, D, 8, 0>(kt, nv, nullptr, fm);
     bv.stage_values(vt);
     bd.stage_values(ot);
@@ -248,11 +261,8 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         const float4 z4 = *reinterpret_cast<const float4*>(&sZ[16 * d0 + 4 * g]);
         ZC[d0] += f32x4_t{z4.x, z4.y, z4.z, z4.w};  // U: S_i dO_i [d][i], ZC: Z_i [d][i]
       }
-      float qv[DB][4];
       float invz = 0.f, odo = 0.f;
       if constexpr (MODE == kBqGiven) {
-#pragma unroll
-        for (int d0 = 0; d0 < DB; ++d0) qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
         const float2 pr = row_ok ? gc[(size_t)vh * N + c0 + il] : make_float2(0.f, 0.f);
         invz = pr.x;
         odo = pr.y;
@@ -260,7 +270,6 @@ __global__ __launch_bounds__(NT) void k_bq(const T* __restrict__ Q, const T* __r
         float pu = 0.f, pz = 0.f;
 #pragma unroll
         for (int d0 = 0; d0 < DB; ++d0) {
-          qt.get4(il, 16 * d0 + 4 * g, qv[d0]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             pu += qv[d0][r] * U[d0][r];

@@ -337,6 +337,13 @@ struct IO<float> {
     const float4 a = *reinterpret_cast<const float4*>(p);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   }
+  // four consecutive elements as loaded (kept in flight), then widened
+  using raw4 = float4;
+  __device__ static __forceinline__ raw4 load_raw4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static __forceinline__ raw4 zero_raw4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static __forceinline__ void unpack4(const raw4& a, float* x) {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  }
 };
 template <>
 struct IO<bf16_t> {
@@ -356,6 +363,12 @@ struct IO<bf16_t> {
   }
   __device__ static __forceinline__ void load4(const bf16_t* p, float* x) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
+    x[0] = lo2f(u.x); x[1] = hi2f(u.x); x[2] = lo2f(u.y); x[3] = hi2f(u.y);
+  }
+  using raw4 = uint2;
+  __device__ static __forceinline__ raw4 load_raw4(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static __forceinline__ raw4 zero_raw4() { return make_uint2(0u, 0u); }
+  __device__ static __forceinline__ void unpack4(const raw4& u, float* x) {
     x[0] = lo2f(u.x); x[1] = hi2f(u.x); x[2] = lo2f(u.y); x[3] = hi2f(u.y);
   }
 };
