@@ -57,7 +57,7 @@ THREADS = 16  # host threads for input generation (the GPU host's share of cores
 
 # The kernel with the largest share of a step's GPU time in the rocprofv3 kernel statistics in profiles/
 # (dominant_kernel reads them; this table is what they showed, used when no statistics match the sources).
-DOMINANT = {"long": "bwd_query", "mnist": "bwd_query", "cifar": "bwd_query", "mnist-rf": "bwd_query",
+DOMINANT = {"long": "bwd_kv", "mnist": "bwd_kv", "cifar": "bwd_kv", "mnist-rf": "bwd_query",
             "mnist-rf256": "bwd_query", "cifar-poly2": "bwd_query",
             "long-decay": "dbq", "speech": "nc_qr", "decode": "decode", "decode-dram": "decode",
             "small": "fwd_causal"}
